@@ -1,0 +1,47 @@
+"""Small shared helpers for the CPU and GPU tests: tiny configurations and
+their seeded inputs (drawn by the synthetic-input module)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from recurrent_decode_step_amd import synth
+from recurrent_decode_step_amd.configs import ModelConfig, DTYPE_FP32, TINY
+
+import oracle
+
+
+def tiny_cfg(**kw) -> ModelConfig:
+    return TINY.model.with_(**kw) if kw else TINY.model
+
+
+def oracle_kwargs(cfg: ModelConfig) -> dict:
+    return dict(d_model=cfg.d_model, n_heads=cfg.n_heads, n_layers=cfg.n_layers,
+                d_ffn=cfg.d_ffn, window=cfg.window, mem_groups=cfg.mem_groups,
+                vocab=cfg.vocab, rms_eps=cfg.rms_eps)
+
+
+def make_model(cfg: ModelConfig, params=None, precision="fp32", device="cpu"):
+    if params is None:
+        params = synth.model_params(cfg, device=device)
+    return oracle.Model(params=params, precision=precision, **oracle_kwargs(cfg)), params
+
+
+def inputs(cfg: ModelConfig, batch: int, steps: int, capacity=None, device="cpu"):
+    capacity = capacity or steps
+    e = synth.encoder_e(cfg, batch, steps, device=device)
+    mk, mv = synth.encoder_memory(cfg, batch, capacity, device=device)
+    return e, mk, mv
+
+
+def np64(t):
+    return t.detach().to("cpu").double().numpy() if hasattr(t, "detach") else np.asarray(t, np.float64)
+
+
+def gate_pinned(params: dict, value: float) -> dict:
+    """Copy of params with W_g = 0 and b_g = value: sigmoid is exactly 1 for
+    value = +100 and exactly 0 for value = -200 in fp32 and fp64."""
+    p = dict(params)
+    p["wg"] = torch.zeros_like(params["wg"])
+    p["bg"] = torch.full_like(params["bg"], value)
+    return p
