@@ -1,0 +1,231 @@
+/*
+ * rlt.h - C ABI of the Recurrent Looped Transformer decoder-step library
+ * (librlt.so, HIP, gfx950).
+ *
+ * The library computes the recurrent decoder state transition
+ *     H_{t-1} = (s_{t-1}, C_{t-1})  ->  H_t = (s_t, C_t),  logits_t = W_o RMSNorm_o(s_t)
+ * for a batch of independent sequences, each at its own position.
+ *
+ * Pages this follows (cited by title):
+ *   [Tutorial]  "Understanding and Applying the Recurrent Looped Transformer
+ *               Architecture": "How the Architecture Works" (H_t, H_0, the
+ *               state-transition equation, the next-token distribution),
+ *               "Three forms of context", "Basic Usage", "Prompt prefill",
+ *               "Autoregressive generation", "Advanced Implementation Tips".
+ *   [Princeton] "Princeton Researcher Proposes Recurrent Looped Transformer to
+ *               Carry Decoder State Across Tokens": architecture paragraph
+ *               (gated merge, block contents, memory groups, window), design
+ *               principles paragraph (batching independent sequences),
+ *               training/serving paragraph (prefix snapshot contents).
+ *   [Article]   "Recurrent Looped Transformer: A New Architecture for Infinite
+ *               Context Reasoning in Language Models": "The Recurrent Decoder
+ *               State", "The Critical Boundary", "Multi-Turn Serving".
+ *
+ * One step, per sequence consuming token t (t = 1 is BOS):
+ *   g   = sigmoid(W_g [e_t ; s_{t-1}] + b_g);  x = g*e_t + (1-g)*s_{t-1}
+ *   per layer l = 0..L-1 (pre-RMSNorm, residual adds):
+ *     x += W_O  SWA(W_Q a, W_K a, W_V a),  a = RMSNorm(x; g1[l])
+ *          window: positions max(1, t-W+1)..t, current token included
+ *     x += W_Oc Attn(W_Qc RMSNorm(x; g2[l]), memory group g(l), positions 1..t)
+ *     x += W_2 GELU(W_1 RMSNorm(x; g3[l]))
+ *   s_t = x;  logits = W_o RMSNorm(s_t; g_o)
+ * The gate formula, the pre-norm block layout, RMSNorm eps, the exact (erf)
+ * GELU, and "no positional encoding besides the window and memory bounds" are
+ * readings where the pages leave the step open.  Attention scale 1/sqrt(dh).
+ *
+ * Precision: dtype RLT_DTYPE_F32 computes and stores everything in fp32.
+ * RLT_DTYPE_BF16 stores weights, e_t, encoder memory, the decoder window cache,
+ * q/k/v, attention outputs, normalised GEMM inputs and the FFN hidden layer in
+ * bf16 (round to nearest even); accumulation, softmax, the residual stream,
+ * s_t and logits are fp32.
+ *
+ * Conventions for every function below:
+ *   - All device memory is owned by the caller.  The library only lays out
+ *     the buffers it is given (sizes from the *_bytes queries) and never
+ *     allocates device memory.  Handles hold host-side metadata only.
+ *   - Pointers named dev_* are device pointers; host_* are host pointers.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call that
+ *     takes a stream only enqueues work on it and returns; nothing
+ *     synchronises except rlt_state_import (see there).  Inputs must stay
+ *     valid until the stream has passed the enqueued work.
+ *   - Functions return rlt_status and never throw.  All validation happens on
+ *     the host before any device work, so a call that fails has no effect.
+ *     A detail message for the calling thread is in rlt_last_error().
+ *   - A model may be shared by several states and streams.  One state must be
+ *     used by one stream at a time; calls on one state that overlap race.
+ */
+#ifndef RLT_H
+#define RLT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RLT_ABI_VERSION 1
+
+typedef enum {
+  RLT_OK = 0,
+  RLT_ERR_INVALID_ARG = 1,   /* null pointer, bad count, duplicate or out-of-range slot */
+  RLT_ERR_SHAPE = 2,         /* buffer too small, dimension not supported by the layout */
+  RLT_ERR_RANGE = 3,         /* a position would pass the memory capacity or max_tokens */
+  RLT_ERR_STALE = 4,         /* state built for another model version: weights changed,
+                                caches are invalid [Article, "Multi-Turn Serving"] */
+  RLT_ERR_CONVENTION = 5,    /* snapshot of another shape / window / dtype / version */
+  RLT_ERR_UNSUPPORTED = 6,   /* configuration the kernels do not implement */
+  RLT_ERR_DEVICE = 7         /* a HIP call failed (also: an earlier asynchronous fault) */
+} rlt_status;
+
+enum { RLT_DTYPE_F32 = 0, RLT_DTYPE_BF16 = 1 };
+enum { RLT_LOGITS_ALL = 0, RLT_LOGITS_LAST = 1, RLT_LOGITS_NONE = 2 };
+
+/* Model dimensions.  head_dim must equal d_model / n_heads and be one of
+ * 16, 32, 64, 128, 256; d_model and d_ffn must be multiples of 32;
+ * mem_groups is 1 (one memory read by every layer) or n_layers (layer l reads
+ * group l) [Princeton, architecture paragraph].  window >= 1 counts the
+ * current token.  attn_chunk: positions per attention work item (0 = the
+ * library default 256); it fixes the order of the softmax sums and so is part
+ * of the model's numerics. */
+typedef struct {
+  int32_t vocab, d_model, n_heads, head_dim, n_layers, d_ffn, window, mem_groups, dtype;
+  float rms_eps;
+  int32_t attn_chunk;
+} rlt_config;
+
+/* Canonical parameters, device pointers, row-major, torch Linear convention
+ * W[out][in] (y = W x).  Matrices in the model dtype; vectors always fp32.
+ * Per-layer tensors are stacked on a leading [L] axis.  Read once by
+ * rlt_model_create (repacked into the model buffer); not retained. */
+typedef struct {
+  const void *s_star;           /* [d]       fp32: learned start state s*       */
+  const void *wg;               /* [d][2d]   gate weights, input order [e ; s]  */
+  const void *bg;               /* [d]       fp32 gate bias                     */
+  const void *g1, *g2, *g3;     /* [L][d]    fp32 RMSNorm gains (SWA, cross, FFN) */
+  const void *wq, *wk, *wv, *wo;/* [L][d][d] self-attention                     */
+  const void *wqc, *woc;        /* [L][d][d] cross-attention query / output     */
+  const void *w1;               /* [L][F][d] FFN up                             */
+  const void *w2;               /* [L][d][F] FFN down                           */
+  const void *go;               /* [d]       fp32 output RMSNorm gain           */
+  const void *wout;             /* [V][d]    output head                        */
+} rlt_params;
+
+/* Encoder memory M (read only, caller owned), already split per head:
+ * element (group g, sequence j, head h, position p (0-based), c) is at
+ * k[g*stride_group + j*stride_seq + h*stride_head + p*stride_pos + c]
+ * (strides in elements, head_dim contiguous, model dtype).  Sequence index
+ * j = state slot.  Entries 0..t-1 of a slot must be valid before the step that
+ * consumes its token t [Tutorial, "Three forms of context": memory is read only
+ * through the current position]. */
+typedef struct {
+  const void *k, *v;
+  int64_t stride_group, stride_seq, stride_head, stride_pos;
+  int32_t capacity;             /* positions available per sequence            */
+  int32_t n_seq;                /* sequences available (> every slot used)     */
+  int32_t n_groups;             /* groups available (>= mem_groups)            */
+} rlt_memory;
+
+typedef struct rlt_model rlt_model;
+typedef struct rlt_state rlt_state;
+
+int32_t     rlt_abi_version(void);
+const char *rlt_status_str(rlt_status s);
+const char *rlt_last_error(void);          /* thread-local; "" if none */
+
+/* ------------------------------------------------------------------ model */
+/* Bytes of device memory a model needs (0 if the config is invalid). */
+size_t rlt_model_bytes(const rlt_config *cfg);
+
+/* Validate cfg, repack `src` into dev_buf (>= rlt_model_bytes, 256-byte
+ * aligned) with kernels on `stream`, and return a host handle in *out.
+ * model_version tags every state made from this model. */
+rlt_status rlt_model_create(const rlt_config *cfg, const rlt_params *src,
+                            uint64_t model_version, void *dev_buf, size_t bytes,
+                            void *stream, rlt_model **out);
+void rlt_model_destroy(rlt_model *m);       /* frees the host handle only */
+
+/* ------------------------------------------------------------------ state */
+/* Bytes for a state of `batch` slots whose positions stay <= max_tokens:
+ * s [B][d] fp32, positions [B] int32, the window cache K,V [L][B][H][W][dh]
+ * in the model dtype (a ring: position p lives in entry (p-1) mod W), and the
+ * per-step scratch the kernels use. */
+size_t rlt_state_bytes(const rlt_config *cfg, int32_t batch, int32_t max_tokens);
+
+/* Lay out a state in dev_buf and set every slot to H_0 = (s*, empty cache),
+ * position 0 [Tutorial, "How the Architecture Works": initial state]. */
+rlt_status rlt_state_init(const rlt_model *m, int32_t batch, int32_t max_tokens,
+                          void *dev_buf, size_t bytes, void *stream, rlt_state **out);
+void rlt_state_destroy(rlt_state *st);
+
+/* Return the listed slots to H_0.  For a document boundary only: the prompt /
+ * response boundary is never a reset [Article, "The Critical Boundary"]. */
+rlt_status rlt_state_reset(const rlt_model *m, rlt_state *st, int32_t n,
+                           const int32_t *host_slots, void *stream);
+
+/* One decoder step for n listed slots (host_slots NULL = slots 0..n-1):
+ *   dev_e      [n][d] model dtype, row i = e_t of slot host_slots[i]
+ *   mem        encoder memory (sequence index = slot)
+ *   dev_logits [n][V] fp32 out (may be NULL: no logits; the state still advances)
+ * Each listed slot consumes exactly one token and its position advances by 1
+ * [Tutorial, "Autoregressive generation"].  Slots must be distinct.  Results
+ * for a slot do not depend on which other slots share the call. */
+rlt_status rlt_decoder_step(const rlt_model *m, rlt_state *st, int32_t n,
+                            const int32_t *host_slots, const void *dev_e,
+                            const rlt_memory *mem, float *dev_logits, void *stream);
+
+/* T steps for all B slots with no reset anywhere (prompt prefill and decode are
+ * the same transition) [Tutorial, "Prompt prefill"; Article, "The Critical
+ * Boundary"].  dev_e [B][T][d]; logits: RLT_LOGITS_ALL -> [B][T][V],
+ * RLT_LOGITS_LAST -> [B][V] of the last step, RLT_LOGITS_NONE -> none (NULL ok).
+ * Bitwise identical to T calls of rlt_decoder_step on all slots. */
+rlt_status rlt_run_sequence(const rlt_model *m, rlt_state *st, int32_t T,
+                            const void *dev_e, const rlt_memory *mem, float *dev_logits,
+                            int32_t logits_mode, void *stream);
+
+/* Host mirror of a slot's position (tokens consumed); -1 on a bad argument.
+ * Does not synchronise. */
+int32_t rlt_state_position(const rlt_state *st, int32_t slot);
+
+/* ------------------------------------------------------------- snapshots */
+/* Exact prefix snapshot of the decoder state [Article, "Multi-Turn Serving";
+ * Princeton, training/serving paragraph]: per slot one record of
+ * rlt_snapshot_bytes(cfg, 1) bytes, independent of the ring phase:
+ *   +0    header: uint32 magic 0x534C5452 ("RTLS"), uint32 format 1,
+ *         int32 d_model, n_heads, head_dim, n_layers, window, dtype, pos,
+ *         int32 0, uint64 model_version (48 bytes; 256 reserved)
+ *   +256  s: fp32 [d]
+ *   then  K: [L][H][W-1][dh] model dtype, logical order: entry e < n_hist =
+ *         min(pos, W-1) holds position pos - n_hist + 1 + e; later entries 0
+ *   then  V: same layout as K
+ * (each section starts at a 256-byte boundary). */
+size_t rlt_snapshot_bytes(const rlt_config *cfg, int32_t n);
+
+/* Write records of the listed slots to dev_snap (record i = host_slots[i]). */
+rlt_status rlt_state_export(const rlt_model *m, const rlt_state *st, int32_t n,
+                            const int32_t *host_slots, void *dev_snap, void *stream);
+
+/* Restore the listed slots from dev_snap.  Reads the n headers back to the host
+ * (synchronising `stream`) to check them: RLT_ERR_CONVENTION if a record's
+ * shape, window, dtype, magic or model_version differ from the model's, or
+ * its position exceeds the state's max_tokens; nothing is written then. */
+rlt_status rlt_state_import(const rlt_model *m, rlt_state *st, int32_t n,
+                            const int32_t *host_slots, const void *dev_snap, void *stream);
+
+/* ------------------------------------------------------------- profiling */
+/* Kernel classes for per-class timing. */
+enum { RLT_K_SETUP = 0, RLT_K_GEMM = 1, RLT_K_SWA = 2, RLT_K_CROSS = 3, RLT_K_NCLASSES = 4 };
+
+/* Start recording a HIP event pair around every launch of kernel class `kclass`
+ * on this state (up to max_launches), or stop with kclass = -1.  Recording
+ * adds host work per launch and is meant for measurement runs only. */
+rlt_status rlt_profile_begin(rlt_state *st, int32_t kclass, int32_t max_launches);
+/* Sum of the recorded launch durations (ms) and their count; waits for the
+ * recorded events.  Clears the record. */
+rlt_status rlt_profile_collect(rlt_state *st, double *total_ms, int32_t *launches,
+                               double *bytes_moved);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RLT_H */

@@ -1,0 +1,297 @@
+"""Thin Python binding of librlt.so (ctypes).  Argument marshalling only:
+torch supplies device memory and the current HIP stream; every step of the
+decoder runs in the library's HIP kernels.  The functions keep the C names
+(rlt_decoder_step, rlt_run_sequence, ...); the classes wrap the handles.
+
+Loading fails loudly when the library is missing: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+from .configs import ModelConfig, DTYPE_BF16, DTYPE_FP32
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librlt.so")
+
+RLT_OK, RLT_ERR_INVALID_ARG, RLT_ERR_SHAPE, RLT_ERR_RANGE, RLT_ERR_STALE, \
+    RLT_ERR_CONVENTION, RLT_ERR_UNSUPPORTED, RLT_ERR_DEVICE = range(8)
+RLT_LOGITS_ALL, RLT_LOGITS_LAST, RLT_LOGITS_NONE = 0, 1, 2
+RLT_K_SETUP, RLT_K_GEMM, RLT_K_SWA, RLT_K_CROSS = 0, 1, 2, 3
+
+EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_bytes",
+            "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",
+            "rlt_state_destroy", "rlt_state_reset", "rlt_decoder_step", "rlt_run_sequence",
+            "rlt_state_position", "rlt_snapshot_bytes", "rlt_state_export", "rlt_state_import",
+            "rlt_profile_begin", "rlt_profile_collect")
+
+
+class RLTError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class rlt_config(C.Structure):
+    _fields_ = [("vocab", C.c_int32), ("d_model", C.c_int32), ("n_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("n_layers", C.c_int32), ("d_ffn", C.c_int32),
+                ("window", C.c_int32), ("mem_groups", C.c_int32), ("dtype", C.c_int32),
+                ("rms_eps", C.c_float), ("attn_chunk", C.c_int32)]
+
+
+class rlt_params(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("s_star", "wg", "bg", "g1", "g2", "g3", "wq", "wk",
+                                          "wv", "wo", "wqc", "woc", "w1", "w2", "go", "wout")]
+
+
+class rlt_memory(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("stride_group", C.c_int64),
+                ("stride_seq", C.c_int64), ("stride_head", C.c_int64), ("stride_pos", C.c_int64),
+                ("capacity", C.c_int32), ("n_seq", C.c_int32), ("n_groups", C.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load librlt.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"librlt.so not found at {path}: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = C.CDLL(path)
+    vp, i32, u64, sz = C.c_void_p, C.c_int32, C.c_uint64, C.c_size_t
+    P = C.POINTER
+    sig = {
+        "rlt_abi_version": (i32, []),
+        "rlt_status_str": (C.c_char_p, [i32]),
+        "rlt_last_error": (C.c_char_p, []),
+        "rlt_model_bytes": (sz, [P(rlt_config)]),
+        "rlt_model_create": (i32, [P(rlt_config), P(rlt_params), u64, vp, sz, vp, P(vp)]),
+        "rlt_model_destroy": (None, [vp]),
+        "rlt_state_bytes": (sz, [P(rlt_config), i32, i32]),
+        "rlt_state_init": (i32, [vp, i32, i32, vp, sz, vp, P(vp)]),
+        "rlt_state_destroy": (None, [vp]),
+        "rlt_state_reset": (i32, [vp, vp, i32, P(i32), vp]),
+        "rlt_decoder_step": (i32, [vp, vp, i32, P(i32), vp, P(rlt_memory), vp, vp]),
+        "rlt_run_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, i32, vp]),
+        "rlt_state_position": (i32, [vp, i32]),
+        "rlt_snapshot_bytes": (sz, [P(rlt_config), i32]),
+        "rlt_state_export": (i32, [vp, vp, i32, P(i32), vp, vp]),
+        "rlt_state_import": (i32, [vp, vp, i32, P(i32), vp, vp]),
+        "rlt_profile_begin": (i32, [vp, i32, i32]),
+        "rlt_profile_collect": (i32, [vp, P(C.c_double), P(i32), P(C.c_double)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != RLT_OK:
+        lib = load_library()
+        raise RLTError(status, f"{lib.rlt_status_str(status).decode()}: "
+                               f"{lib.rlt_last_error().decode()}")
+
+
+def make_config(cfg: ModelConfig, attn_chunk: int = 0) -> rlt_config:
+    return rlt_config(cfg.vocab, cfg.d_model, cfg.n_heads, cfg.head_dim, cfg.n_layers, cfg.d_ffn,
+                      cfg.window, cfg.mem_groups, cfg.dtype, cfg.rms_eps, attn_chunk)
+
+
+def _stream(stream=None) -> C.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _slots_arg(slots):
+    if slots is None:
+        return None, None
+    arr = (C.c_int32 * len(slots))(*[int(s) for s in slots])
+    return arr, len(slots)
+
+
+def memory_view(k: torch.Tensor, v: torch.Tensor) -> rlt_memory:
+    """rlt_memory over K, V tensors shaped [G][S][H][T][dh] (dh contiguous)."""
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("K and V must have the same shape and strides")
+    if k.stride(-1) != 1:
+        raise ValueError("head_dim must be contiguous")
+    sg, ss, sh, sp, _ = k.stride()
+    return rlt_memory(k.data_ptr(), v.data_ptr(), sg, ss, sh, sp, k.shape[3], k.shape[1],
+                      k.shape[0])
+
+
+class Model:
+    """Packed weights on the device (rlt_model_create)."""
+
+    def __init__(self, cfg: ModelConfig, params: dict, version: int = 1, attn_chunk: int = 0,
+                 stream=None):
+        lib = load_library()
+        self.cfg = cfg
+        self.ccfg = make_config(cfg, attn_chunk)
+        self.version = version
+        nbytes = lib.rlt_model_bytes(C.byref(self.ccfg))
+        if nbytes == 0:
+            _check(RLT_ERR_INVALID_ARG)
+        dev = torch.device("cuda", torch.cuda.current_device())
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        keep = {}
+        sd = torch.bfloat16 if cfg.dtype == DTYPE_BF16 else torch.float32
+        for name in rlt_params._fields_:
+            key = name[0]
+            t = params[key]
+            want = torch.float32 if key in ("s_star", "bg", "g1", "g2", "g3", "go") else sd
+            keep[key] = t.to(device=dev, dtype=want).contiguous()
+        p = rlt_params(*[keep[n[0]].data_ptr() for n in rlt_params._fields_])
+        h = C.c_void_p()
+        _check(lib.rlt_model_create(C.byref(self.ccfg), C.byref(p), version, self.buf.data_ptr(),
+                                    nbytes, _stream(stream), C.byref(h)))
+        self.handle = h
+        # the canonical tensors are read by kernels already enqueued
+        torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+        del keep
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.rlt_model_destroy(self.handle)
+            self.handle = None
+
+
+class State:
+    """Decoder states of `batch` slots (rlt_state_init)."""
+
+    def __init__(self, model: Model, batch: int, max_tokens: int, stream=None):
+        lib = load_library()
+        self.model = model
+        self.batch = batch
+        self.max_tokens = max_tokens
+        nbytes = lib.rlt_state_bytes(C.byref(model.ccfg), batch, max_tokens)
+        if nbytes == 0:
+            _check(RLT_ERR_INVALID_ARG)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=model.buf.device)
+        h = C.c_void_p()
+        _check(lib.rlt_state_init(model.handle, batch, max_tokens, self.buf.data_ptr(), nbytes,
+                                  _stream(stream), C.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.rlt_state_destroy(self.handle)
+            self.handle = None
+
+    def position(self, slot: int) -> int:
+        return load_library().rlt_state_position(self.handle, slot)
+
+
+def rlt_decoder_step(model: Model, state: State, e: torch.Tensor, memory, logits=None,
+                     slots=None, want_logits=True, stream=None):
+    """One step for the rows of e ([n][d]); returns logits [n][V] fp32 (or None)."""
+    lib = load_library()
+    n = e.shape[0]
+    if e.stride(-1) != 1 or e.stride(0) != e.shape[1]:
+        e = e.contiguous()
+    if logits is None and want_logits:
+        logits = torch.empty((n, model.cfg.vocab), dtype=torch.float32, device=e.device)
+    arr, _ = _slots_arg(slots)
+    mem = memory if isinstance(memory, rlt_memory) else memory_view(*memory)
+    _check(lib.rlt_decoder_step(model.handle, state.handle, n, arr, e.data_ptr(), C.byref(mem),
+                                logits.data_ptr() if logits is not None else None,
+                                _stream(stream)))
+    return logits
+
+
+def rlt_run_sequence(model: Model, state: State, e: torch.Tensor, memory,
+                     logits_mode: int = RLT_LOGITS_ALL, logits=None, stream=None):
+    """T steps for all slots, e [B][T][d]; returns logits per logits_mode."""
+    lib = load_library()
+    B, T = e.shape[0], e.shape[1]
+    e = e.contiguous()
+    if logits is None and logits_mode != RLT_LOGITS_NONE:
+        shape = (B, T, model.cfg.vocab) if logits_mode == RLT_LOGITS_ALL else (B, model.cfg.vocab)
+        logits = torch.empty(shape, dtype=torch.float32, device=e.device)
+    mem = memory if isinstance(memory, rlt_memory) else memory_view(*memory)
+    _check(lib.rlt_run_sequence(model.handle, state.handle, T, e.data_ptr(), C.byref(mem),
+                                logits.data_ptr() if logits is not None else None, logits_mode,
+                                _stream(stream)))
+    return logits
+
+
+def rlt_state_reset(model: Model, state: State, slots, stream=None):
+    arr, n = _slots_arg(slots)
+    _check(load_library().rlt_state_reset(model.handle, state.handle, n, arr, _stream(stream)))
+
+
+def snapshot_bytes(model: Model, n: int) -> int:
+    return load_library().rlt_snapshot_bytes(C.byref(model.ccfg), n)
+
+
+def rlt_state_export(model: Model, state: State, slots, stream=None) -> torch.Tensor:
+    lib = load_library()
+    arr, n = _slots_arg(slots)
+    snap = torch.empty(snapshot_bytes(model, n), dtype=torch.uint8, device=model.buf.device)
+    _check(lib.rlt_state_export(model.handle, state.handle, n, arr, snap.data_ptr(),
+                                _stream(stream)))
+    return snap
+
+
+def rlt_state_import(model: Model, state: State, snap: torch.Tensor, slots, stream=None):
+    arr, n = _slots_arg(slots)
+    _check(load_library().rlt_state_import(model.handle, state.handle, n, arr, snap.data_ptr(),
+                                           _stream(stream)))
+
+
+def snapshot_layout(cfg: ModelConfig):
+    """(record bytes, offset of s, offset of K, offset of V) of one snapshot record."""
+    es = 2 if cfg.dtype == DTYPE_BF16 else 4
+    a256 = lambda x: (x + 255) // 256 * 256
+    hist = cfg.n_layers * cfg.n_heads * (cfg.window - 1) * cfg.head_dim * es
+    off_s = 256
+    off_k = off_s + a256(cfg.d_model * 4)
+    off_v = off_k + a256(hist)
+    return off_v + a256(hist), off_s, off_k, off_v
+
+
+def build_snapshot(cfg: ModelConfig, records, version: int, device) -> torch.Tensor:
+    """Write snapshot records (the library's documented format) from
+    {'pos', 's' [d], 'K'/'V' [L][H][n_hist][dh]} dicts."""
+    rec, off_s, off_k, off_v = snapshot_layout(cfg)
+    out = torch.zeros(rec * len(records), dtype=torch.uint8, device=device)
+    sd = torch.bfloat16 if cfg.dtype == DTYPE_BF16 else torch.float32
+    L, H, dh, Wm1 = cfg.n_layers, cfg.n_heads, cfg.head_dim, cfg.window - 1
+    for r, st in enumerate(records):
+        base = r * rec
+        hdr = torch.tensor([0x534C5452, 1], dtype=torch.int64).to(torch.int32)
+        ints = torch.tensor([cfg.d_model, H, dh, L, cfg.window, cfg.dtype, int(st["pos"]), 0],
+                            dtype=torch.int32)
+        head = torch.cat([hdr.view(torch.uint8), ints.view(torch.uint8),
+                          torch.tensor([version], dtype=torch.int64).view(torch.uint8)])
+        out[base:base + head.numel()] = head.to(device)
+        s = st["s"].to(device=device, dtype=torch.float32).contiguous()
+        out[base + off_s: base + off_s + s.numel() * 4] = s.view(torch.uint8)
+        n_hist = st["K"].shape[2]
+        if Wm1 > 0 and n_hist > 0:
+            for key, off in (("K", off_k), ("V", off_v)):
+                full = torch.zeros((L, H, Wm1, dh), dtype=sd, device=device)
+                full[:, :, :n_hist] = st[key].to(device=device, dtype=sd)
+                b = full.contiguous().view(torch.uint8).reshape(-1)
+                out[base + off: base + off + b.numel()] = b
+    return out
+
+
+def profile_begin(state: State, kclass: int, max_launches: int):
+    _check(load_library().rlt_profile_begin(state.handle, kclass, max_launches))
+
+
+def profile_collect(state: State):
+    tot, n, b = C.c_double(), C.c_int32(), C.c_double()
+    _check(load_library().rlt_profile_collect(state.handle, C.byref(tot), C.byref(n), C.byref(b)))
+    return tot.value, n.value, b.value

@@ -1,0 +1,988 @@
+// Host side of librlt.so: argument validation, buffer layouts, and the launch
+// sequence of one decoder step.  All validation runs before any device work.
+#include "rlt_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+using namespace rlt;
+
+namespace {
+
+thread_local std::string g_err;
+
+rlt_status fail(rlt_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+rlt_status ok() {
+  g_err.clear();
+  return RLT_OK;
+}
+
+rlt_status hip_fail(hipError_t e, const char *what) {
+  return fail(RLT_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Bump allocator over a caller buffer; with base == nullptr it only measures.
+struct Arena {
+  char *base;
+  size_t off = 0;
+  explicit Arena(void *b) : base(static_cast<char *>(b)) {}
+  template <typename P> P *take(size_t bytes) {
+    off = align256(off);
+    P *p = base ? reinterpret_cast<P *>(base + off) : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+int esize_of(int dtype) { return dtype == RLT_DTYPE_BF16 ? 2 : 4; }
+int kstep_of(int dtype) { return dtype == RLT_DTYPE_BF16 ? 32 : 16; }
+
+// ---- GEMM plan: the k-split depends only on (N, K, dtype) so that a row's
+// result never depends on how many rows share the launch.
+struct GemmPlan {
+  int N, K, Np, KT, n_blocks, splits, ks_per_split;
+};
+
+GemmPlan gemm_plan(int N, int K, int dtype) {
+  GemmPlan p;
+  p.N = N;
+  p.K = K;
+  p.Np = cdiv(N, kRowsPerBlock) * kRowsPerBlock;
+  p.KT = cdiv(K, kstep_of(dtype));
+  p.n_blocks = p.Np / kRowsPerBlock;
+  const int target_wgs = 512;
+  int s = std::max(1, target_wgs / p.n_blocks);
+  s = std::min(s, p.KT);
+  int per = cdiv(p.KT, s);
+  const int gran = std::min(8, p.KT);      // whole staged sub-chunks where possible
+  per = cdiv(per, gran) * gran;
+  p.ks_per_split = per;
+  p.splits = cdiv(p.KT, per);
+  return p;
+}
+
+// batch-column blocking of a launch over n rows
+struct ColPlan {
+  int ncb, groups;
+};
+ColPlan col_plan(int n) {
+  ColPlan c;
+  const int blocks16 = cdiv(n, 16);
+  if (blocks16 <= 1) c.ncb = 1;
+  else if (blocks16 <= 2) c.ncb = 2;
+  else if (blocks16 <= 4) c.ncb = 4;
+  else if (blocks16 <= 8) c.ncb = 8;
+  else c.ncb = 16;
+  c.groups = cdiv(n, c.ncb * 16);
+  return c;
+}
+
+size_t gemm_ws_bytes(const GemmPlan &g, int n) {
+  if (g.splits <= 1) return 0;
+  const ColPlan c = col_plan(n);
+  return (size_t)g.splits * g.n_blocks * c.groups * 4 * c.ncb * 64 * 16;
+}
+size_t gemm_counter_count(const GemmPlan &g, int n) {
+  return (size_t)g.n_blocks * col_plan(n).groups;
+}
+
+bool valid_dh(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128 || dh == 256; }
+
+rlt_status check_config(const rlt_config *c) {
+  if (!c) return fail(RLT_ERR_INVALID_ARG, "config is NULL");
+  if (c->vocab < 1 || c->d_model < 1 || c->n_heads < 1 || c->n_layers < 1 || c->d_ffn < 1 ||
+      c->window < 1)
+    return fail(RLT_ERR_INVALID_ARG, "config dimensions must be positive");
+  if (c->dtype != RLT_DTYPE_F32 && c->dtype != RLT_DTYPE_BF16)
+    return fail(RLT_ERR_INVALID_ARG, "dtype must be RLT_DTYPE_F32 or RLT_DTYPE_BF16");
+  if (c->head_dim * c->n_heads != c->d_model)
+    return fail(RLT_ERR_SHAPE, "head_dim * n_heads (%d * %d) != d_model (%d)", c->head_dim,
+                c->n_heads, c->d_model);
+  if (!valid_dh(c->head_dim))
+    return fail(RLT_ERR_UNSUPPORTED, "head_dim %d not in {16,32,64,128,256}", c->head_dim);
+  if (c->d_model % 32 || c->d_ffn % 32)
+    return fail(RLT_ERR_UNSUPPORTED, "d_model and d_ffn must be multiples of 32");
+  if (c->mem_groups != 1 && c->mem_groups != c->n_layers)
+    return fail(RLT_ERR_UNSUPPORTED, "mem_groups must be 1 or n_layers (got %d)", c->mem_groups);
+  if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps))
+    return fail(RLT_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (c->attn_chunk < 0) return fail(RLT_ERR_INVALID_ARG, "attn_chunk must be >= 0");
+  return RLT_OK;
+}
+
+int chunk_of(const rlt_config *c) {
+  const int cap = attn_chunk_max(c->dtype, c->head_dim);
+  const int want = c->attn_chunk > 0 ? c->attn_chunk : kDefaultChunk;
+  return std::min(want, cap);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ handles
+struct rlt_model {
+  rlt_config cfg;
+  uint64_t version;
+  int device;
+  int esize, chunk;
+  GemmPlan p_merge, p_qkv, p_o, p_ffn1, p_ffn2, p_head;
+  PackedMat wg, wout;
+  std::vector<PackedMat> wqkv, wo, wqc, woc, w1, w2;
+  float *s_star, *bg, *go, *g1, *g2, *g3;
+};
+
+struct ProfRec {
+  hipEvent_t a, b;
+  double bytes;
+};
+
+struct rlt_state {
+  rlt_config cfg;
+  uint64_t version;
+  int device;
+  int B, max_tokens;
+  size_t bytes;
+  float *s;
+  int *pos;
+  char *ring_k, *ring_v;
+  int *slots_dev;
+  int *rows_t, *rows_slot;
+  float *x, *sumsq;
+  char *qbuf, *obuf, *hbuf;
+  int2 *items_swa, *items_mem;
+  int *n_items;  // [2]
+  int *start_swa, *start_mem;
+  float *attn_part;
+  int *attn_cnt;
+  float *ws;
+  int *gemm_cnt;
+  size_t ws_bytes, gemm_cnt_n;
+  std::vector<int> host_pos;
+  std::vector<int> staged;   // slot list currently in slots_dev (empty: none)
+  // profiling
+  int prof_class = -1;
+  int prof_max = 0;
+  std::vector<ProfRec> prof;
+};
+
+namespace {
+
+void model_plans(rlt_model *m) {
+  const rlt_config &c = m->cfg;
+  const int d = c.d_model, F = c.d_ffn;
+  m->p_merge = gemm_plan(d, 2 * d, c.dtype);
+  m->p_qkv = gemm_plan(3 * d, d, c.dtype);
+  m->p_o = gemm_plan(d, d, c.dtype);
+  m->p_ffn1 = gemm_plan(F, d, c.dtype);
+  m->p_ffn2 = gemm_plan(d, F, c.dtype);
+  m->p_head = gemm_plan(c.vocab, d, c.dtype);
+}
+
+size_t packed_bytes(const GemmPlan &g, int esize, int dtype) {
+  return (size_t)g.Np * g.KT * kstep_of(dtype) * esize;
+}
+
+// model buffer layout (same walk for sizing and for carving)
+size_t model_layout(rlt_model *m, void *base) {
+  const rlt_config &c = m->cfg;
+  const int L = c.n_layers, d = c.d_model;
+  const int es = esize_of(c.dtype);
+  Arena ar(base);
+  auto mat = [&](const GemmPlan &g) {
+    PackedMat pm;
+    pm.N = g.N;
+    pm.K = g.K;
+    pm.Np = g.Np;
+    pm.KT = g.KT;
+    pm.p = ar.take<char>(packed_bytes(g, es, c.dtype));
+    return pm;
+  };
+  m->wg = mat(m->p_merge);
+  m->wqkv.resize(L);
+  m->wo.resize(L);
+  m->wqc.resize(L);
+  m->woc.resize(L);
+  m->w1.resize(L);
+  m->w2.resize(L);
+  for (int l = 0; l < L; ++l) {
+    m->wqkv[l] = mat(m->p_qkv);
+    m->wo[l] = mat(m->p_o);
+    m->wqc[l] = mat(m->p_o);
+    m->woc[l] = mat(m->p_o);
+    m->w1[l] = mat(m->p_ffn1);
+    m->w2[l] = mat(m->p_ffn2);
+  }
+  m->wout = mat(m->p_head);
+  m->s_star = ar.take<float>((size_t)d * 4);
+  m->bg = ar.take<float>((size_t)d * 4);
+  m->go = ar.take<float>((size_t)d * 4);
+  m->g1 = ar.take<float>((size_t)L * d * 4);
+  m->g2 = ar.take<float>((size_t)L * d * 4);
+  m->g3 = ar.take<float>((size_t)L * d * 4);
+  return align256(ar.off);
+}
+
+size_t state_layout(const rlt_model *mdl, const rlt_config &c, rlt_state *st, void *base, int B,
+                    int max_tokens) {
+  rlt_model tmp;
+  if (!mdl) {
+    tmp.cfg = c;
+    model_plans(&tmp);
+    mdl = &tmp;
+  }
+  const int L = c.n_layers, d = c.d_model, H = c.n_heads, dh = c.head_dim, W = c.window;
+  const int es = esize_of(c.dtype);
+  const int ch = chunk_of(&c);
+  Arena ar(base);
+  st->s = ar.take<float>((size_t)B * d * 4);
+  st->pos = ar.take<int>((size_t)B * 4);
+  st->ring_k = ar.take<char>((size_t)L * B * H * W * dh * es);
+  st->ring_v = ar.take<char>((size_t)L * B * H * W * dh * es);
+  st->slots_dev = ar.take<int>((size_t)B * 4);
+  st->rows_t = ar.take<int>((size_t)B * 4);
+  st->rows_slot = ar.take<int>((size_t)B * 4);
+  st->x = ar.take<float>((size_t)B * d * 4);
+  st->sumsq = ar.take<float>((size_t)cdiv(d, kRowsPerBlock) * B * 4);
+  st->qbuf = ar.take<char>((size_t)B * d * es);
+  st->obuf = ar.take<char>((size_t)B * d * es);
+  st->hbuf = ar.take<char>((size_t)B * c.d_ffn * es);
+  const size_t items_swa = (size_t)B * cdiv(std::min(max_tokens, W), ch);
+  const size_t items_mem = (size_t)B * cdiv(max_tokens, ch);
+  st->items_swa = ar.take<int2>(items_swa * 8);
+  st->items_mem = ar.take<int2>(items_mem * 8);
+  st->n_items = ar.take<int>(64);
+  st->start_swa = ar.take<int>((size_t)B * 4);
+  st->start_mem = ar.take<int>((size_t)B * 4);
+  st->attn_part = ar.take<float>(std::max(items_swa, items_mem) * H * (dh + 2) * 4);
+  st->attn_cnt = ar.take<int>((size_t)B * H * 4);
+  const GemmPlan *plans[] = {&mdl->p_merge, &mdl->p_qkv, &mdl->p_o,
+                             &mdl->p_ffn1,  &mdl->p_ffn2, &mdl->p_head};
+  size_t ws = 0, cnt = 0;
+  for (const GemmPlan *g : plans) {
+    ws = std::max(ws, gemm_ws_bytes(*g, B));
+    cnt = std::max(cnt, gemm_counter_count(*g, B));
+  }
+  st->ws_bytes = ws;
+  st->gemm_cnt_n = cnt;
+  st->ws = ar.take<float>(std::max<size_t>(ws, 16));
+  st->gemm_cnt = ar.take<int>(std::max<size_t>(cnt, 1) * 4);
+  return align256(ar.off);
+}
+
+rlt_status check_state(const rlt_model *m, const rlt_state *st) {
+  if (!m) return fail(RLT_ERR_INVALID_ARG, "model is NULL");
+  if (!st) return fail(RLT_ERR_INVALID_ARG, "state is NULL");
+  if (st->version != m->version)
+    return fail(RLT_ERR_STALE, "state built for model version %llu, model is version %llu",
+                (unsigned long long)st->version, (unsigned long long)m->version);
+  const rlt_config &a = st->cfg, &b = m->cfg;
+  if (a.d_model != b.d_model || a.n_layers != b.n_layers || a.n_heads != b.n_heads ||
+      a.window != b.window || a.dtype != b.dtype || a.d_ffn != b.d_ffn || a.vocab != b.vocab ||
+      a.mem_groups != b.mem_groups || a.attn_chunk != b.attn_chunk)
+    return fail(RLT_ERR_CONVENTION, "state and model configurations differ");
+  return RLT_OK;
+}
+
+rlt_status check_slots(const rlt_state *st, int n, const int32_t *slots) {
+  if (n < 1 || n > st->B) return fail(RLT_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, st->B);
+  if (!slots) return RLT_OK;
+  std::vector<char> seen(st->B, 0);
+  for (int i = 0; i < n; ++i) {
+    const int s = slots[i];
+    if (s < 0 || s >= st->B) return fail(RLT_ERR_INVALID_ARG, "slot %d out of range", s);
+    if (seen[s]) return fail(RLT_ERR_INVALID_ARG, "slot %d listed twice", s);
+    seen[s] = 1;
+  }
+  return RLT_OK;
+}
+
+rlt_status check_memory(const rlt_model *m, const rlt_memory *mem, int max_slot) {
+  if (!mem || !mem->k || !mem->v) return fail(RLT_ERR_INVALID_ARG, "memory K/V pointer is NULL");
+  if (mem->capacity < 1) return fail(RLT_ERR_INVALID_ARG, "memory capacity < 1");
+  if (mem->n_groups < m->cfg.mem_groups)
+    return fail(RLT_ERR_INVALID_ARG, "memory holds %d groups, model reads %d", mem->n_groups,
+                m->cfg.mem_groups);
+  if (mem->n_seq <= max_slot)
+    return fail(RLT_ERR_INVALID_ARG, "memory holds %d sequences, slot %d used", mem->n_seq, max_slot);
+  if (mem->stride_pos < m->cfg.head_dim || mem->stride_head < 0 || mem->stride_seq < 0 ||
+      mem->stride_group < 0)
+    return fail(RLT_ERR_INVALID_ARG, "bad memory strides");
+  const int es = esize_of(m->cfg.dtype);
+  const int64_t strides[4] = {mem->stride_group, mem->stride_seq, mem->stride_head, mem->stride_pos};
+  for (int64_t s : strides)
+    if ((s * es) % 16) return fail(RLT_ERR_SHAPE, "memory strides must be multiples of 16 bytes");
+  if (((uintptr_t)mem->k | (uintptr_t)mem->v) % 16)
+    return fail(RLT_ERR_SHAPE, "memory pointers must be 16-byte aligned");
+  return RLT_OK;
+}
+
+// Stage a slot list in device memory (only when it differs from the staged one).
+rlt_status stage_slots(rlt_state *st, int n, const int32_t *slots, hipStream_t s) {
+  if (st->staged.size() == (size_t)n && std::equal(slots, slots + n, st->staged.begin()))
+    return RLT_OK;
+  hipError_t e = hipMemcpyAsync(st->slots_dev, slots, (size_t)n * 4, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "staging slot list");
+  st->staged.assign(slots, slots + n);
+  return RLT_OK;
+}
+
+struct Prof {
+  rlt_state *st;
+  int cls;
+  hipStream_t s;
+  bool on;
+  hipEvent_t a = nullptr, b = nullptr;
+  Prof(rlt_state *st_, int cls_, hipStream_t s_)
+      : st(st_), cls(cls_), s(s_),
+        on(st_->prof_class == cls_ && (int)st_->prof.size() < st_->prof_max) {
+    if (on && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess)
+      (void)hipEventRecord(a, s);
+    else on = false;
+  }
+  void done(double bytes) {
+    if (!on) return;
+    (void)hipEventRecord(b, s);
+    st->prof.push_back({a, b, bytes});
+    on = false;
+  }
+};
+
+// Enqueue one decoder step for n rows.  e rows: e_base + i*ld_e (elements);
+// logits rows: logits + i*ld_logits (NULL: no head).  The slot list is already
+// staged (identity == true: rows are slots 0..n-1).
+rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
+                        const int32_t *host_slots, const void *e, int64_t ld_e,
+                        const rlt_memory *mem, float *logits, int64_t ld_logits, hipStream_t s) {
+  const rlt_config &c = m->cfg;
+  const int d = c.d_model, H = c.n_heads, dh = c.head_dim, W = c.window, L = c.n_layers;
+  const int F = c.d_ffn, B = st->B, es = m->esize;
+  const int ch = m->chunk;
+  hipError_t err;
+
+  // host mirror: positions of this step and attention work counts
+  int items_swa = 0, items_mem = 0;
+  double swa_len = 0, mem_len = 0;
+  for (int i = 0; i < n; ++i) {
+    const int slot = identity ? i : host_slots[i];
+    const int t = st->host_pos[slot] + 1;
+    items_swa += cdiv(std::min(t, W), ch);
+    items_mem += cdiv(t, ch);
+    swa_len += std::min(t, W);
+    mem_len += t;
+  }
+
+  {
+    SetupArgs sa;
+    sa.slots = identity ? nullptr : st->slots_dev;
+    sa.n = n;
+    sa.pos = st->pos;
+    sa.rows_t = st->rows_t;
+    sa.rows_slot = st->rows_slot;
+    sa.W = W;
+    sa.ch = ch;
+    sa.items_swa = st->items_swa;
+    sa.items_mem = st->items_mem;
+    sa.n_items_swa = st->n_items;
+    sa.n_items_mem = st->n_items + 1;
+    sa.start_swa = st->start_swa;
+    sa.start_mem = st->start_mem;
+    Prof p(st, RLT_K_SETUP, s);
+    if ((err = launch_setup(sa, s)) != hipSuccess) return hip_fail(err, "setup launch");
+    p.done(0);
+  }
+
+  const ColPlan cp = col_plan(n);
+  GemmArgs base;
+  memset(&base, 0, sizeof base);
+  base.n_rows = n;
+  base.x = st->x;
+  base.ld_x = d;
+  base.xio = st->x;
+  base.sumsq = st->sumsq;
+  base.sumsq_out = st->sumsq;
+  base.n_parts = cdiv(d, kRowsPerBlock);
+  base.part_ld = B;
+  base.eps = c.rms_eps;
+  base.s_state = st->s;
+  base.d = d;
+  base.rows_slot = st->rows_slot;
+  base.rows_t = st->rows_t;
+  base.H = H;
+  base.dh = dh;
+  base.W = W;
+  base.ws = st->ws;
+  base.counters = st->gemm_cnt;
+
+  auto gemm = [&](const GemmPlan &g, const PackedMat &w, int act, int epi, GemmArgs a,
+                  const char *what, double act_bytes_in, double out_bytes) -> rlt_status {
+    a.wp = w.p;
+    a.N = g.N;
+    a.K = g.K;
+    a.KT = g.KT;
+    a.ks_per_split = g.ks_per_split;
+    a.splits = g.splits;
+    Prof p(st, RLT_K_GEMM, s);
+    hipError_t e2 = launch_gemm_grid(c.dtype, cp.ncb, act, epi, a, g.n_blocks, g.splits,
+                                     cp.groups, s);
+    if (e2 != hipSuccess) return hip_fail(e2, what);
+    p.done((double)g.N * g.K * es + act_bytes_in + out_bytes);
+    return RLT_OK;
+  };
+  rlt_status rs;
+
+  // gated merge: x = g*e + (1-g)*s, g = sigmoid(W_g [e ; s] + b_g)
+  {
+    GemmArgs a = base;
+    a.act = e;
+    a.ld_act = ld_e;
+    a.bias = m->bg;
+    if ((rs = gemm(m->p_merge, m->wg, ACT_MERGE, EPI_MERGE, a, "merge gemm",
+                   (double)n * d * (es + 4), (double)n * d * 4)) != RLT_OK)
+      return rs;
+  }
+
+  const size_t ring_layer = (size_t)B * H * W * dh * es;
+  AttnArgs at;
+  memset(&at, 0, sizeof at);
+  at.rows_t = st->rows_t;
+  at.rows_slot = st->rows_slot;
+  at.part = st->attn_part;
+  at.counters = st->attn_cnt;
+  at.H = H;
+  at.d = d;
+  at.ch = ch;
+  at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
+
+  for (int l = 0; l < L; ++l) {
+    // (1) RMSNorm + Q,K,V; k,v appended to the window cache at entry (t-1) mod W
+    {
+      GemmArgs a = base;
+      a.gamma = m->g1 + (size_t)l * d;
+      a.out = st->qbuf;
+      a.ld_out = d;
+      a.ring_k = st->ring_k + l * ring_layer;
+      a.ring_v = st->ring_v + l * ring_layer;
+      if ((rs = gemm(m->p_qkv, m->wqkv[l], ACT_NORM, EPI_QKV, a, "qkv gemm", (double)n * d * 4,
+                     (double)n * 3 * d * es)) != RLT_OK)
+        return rs;
+    }
+    // (2) sliding-window self-attention over ring entries 0..min(t,W)-1
+    {
+      AttnArgs a = at;
+      a.q = st->qbuf;
+      a.out = st->obuf;
+      a.kb = st->ring_k + l * ring_layer;
+      a.vb = st->ring_v + l * ring_layer;
+      a.s_seq = (int64_t)H * W * dh;
+      a.s_head = (int64_t)W * dh;
+      a.s_pos = dh;
+      a.len_cap = W;
+      a.items = st->items_swa;
+      a.n_items = st->n_items;
+      a.row_item_start = st->start_swa;
+      Prof p(st, RLT_K_SWA, s);
+      if ((err = launch_attn(c.dtype, dh, a, items_swa, s)) != hipSuccess)
+        return hip_fail(err, "window attention launch");
+      p.done(swa_len * 2.0 * d * es + 2.0 * n * d * es);
+    }
+    // (3) x += W_O o
+    {
+      GemmArgs a = base;
+      a.act = st->obuf;
+      a.ld_act = d;
+      if ((rs = gemm(m->p_o, m->wo[l], ACT_PLAIN, EPI_RESID, a, "o gemm",
+                     (double)n * d * (es + 4), (double)n * d * 4)) != RLT_OK)
+        return rs;
+    }
+    // (4) RMSNorm + cross-attention query
+    {
+      GemmArgs a = base;
+      a.gamma = m->g2 + (size_t)l * d;
+      a.out = st->qbuf;
+      a.ld_out = d;
+      if ((rs = gemm(m->p_o, m->wqc[l], ACT_NORM, EPI_STORE, a, "qc gemm", (double)n * d * 4,
+                     (double)n * d * es)) != RLT_OK)
+        return rs;
+    }
+    // (5) cross-attention to memory positions 1..t of group g(l)
+    {
+      const int grp = c.mem_groups == 1 ? 0 : l;
+      AttnArgs a = at;
+      a.q = st->qbuf;
+      a.out = st->obuf;
+      a.kb = static_cast<const char *>(mem->k) + (size_t)grp * mem->stride_group * es;
+      a.vb = static_cast<const char *>(mem->v) + (size_t)grp * mem->stride_group * es;
+      a.s_seq = mem->stride_seq;
+      a.s_head = mem->stride_head;
+      a.s_pos = mem->stride_pos;
+      a.len_cap = 0x7fffffff;
+      a.items = st->items_mem;
+      a.n_items = st->n_items + 1;
+      a.row_item_start = st->start_mem;
+      Prof p(st, RLT_K_CROSS, s);
+      if ((err = launch_attn(c.dtype, dh, a, items_mem, s)) != hipSuccess)
+        return hip_fail(err, "cross attention launch");
+      p.done(mem_len * 2.0 * d * es + 2.0 * n * d * es);
+    }
+    // (6) x += W_Oc o_c
+    {
+      GemmArgs a = base;
+      a.act = st->obuf;
+      a.ld_act = d;
+      if ((rs = gemm(m->p_o, m->woc[l], ACT_PLAIN, EPI_RESID, a, "oc gemm",
+                     (double)n * d * (es + 4), (double)n * d * 4)) != RLT_OK)
+        return rs;
+    }
+    // (7) RMSNorm + FFN up + GELU
+    {
+      GemmArgs a = base;
+      a.gamma = m->g3 + (size_t)l * d;
+      a.out = st->hbuf;
+      a.ld_out = F;
+      if ((rs = gemm(m->p_ffn1, m->w1[l], ACT_NORM, EPI_GELU, a, "ffn1 gemm", (double)n * d * 4,
+                     (double)n * F * es)) != RLT_OK)
+        return rs;
+    }
+    // (8) x += W_2 h; the last layer also writes s_t
+    {
+      GemmArgs a = base;
+      a.act = st->hbuf;
+      a.ld_act = F;
+      if (l == L - 1) a.s_out = st->s;
+      if ((rs = gemm(m->p_ffn2, m->w2[l], ACT_PLAIN, EPI_RESID, a, "ffn2 gemm",
+                     (double)n * F * es + (double)n * d * 4, (double)n * d * 4)) != RLT_OK)
+        return rs;
+    }
+  }
+
+  // head: logits = W_o RMSNorm(s_t; g_o)
+  if (logits) {
+    GemmArgs a = base;
+    a.gamma = m->go;
+    a.out = logits;
+    a.ld_out = ld_logits;
+    if ((rs = gemm(m->p_head, m->wout, ACT_NORM, EPI_LOGITS, a, "head gemm", (double)n * d * 4,
+                   (double)n * c.vocab * 4)) != RLT_OK)
+      return rs;
+  }
+
+  for (int i = 0; i < n; ++i) st->host_pos[identity ? i : host_slots[i]] += 1;
+  return RLT_OK;
+}
+
+rlt_status check_positions(const rlt_state *st, const rlt_memory *mem, int n,
+                           const int32_t *slots, int steps) {
+  for (int i = 0; i < n; ++i) {
+    const int slot = slots ? slots[i] : i;
+    const long long last = (long long)st->host_pos[slot] + steps;
+    if (last > mem->capacity)
+      return fail(RLT_ERR_RANGE, "slot %d would reach position %lld > memory capacity %d", slot,
+                  last, mem->capacity);
+    if (last > st->max_tokens)
+      return fail(RLT_ERR_RANGE, "slot %d would reach position %lld > max_tokens %d", slot, last,
+                  st->max_tokens);
+  }
+  return RLT_OK;
+}
+
+rlt_status device_health() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "earlier device error");
+  return RLT_OK;
+}
+
+void snapshot_offsets(const rlt_config *c, size_t *off_s, size_t *off_k, size_t *off_v,
+                      size_t *rec) {
+  const int es = esize_of(c->dtype);
+  const size_t hist = (size_t)c->n_layers * c->n_heads * (c->window - 1) * c->head_dim * es;
+  *off_s = 256;
+  *off_k = *off_s + align256((size_t)c->d_model * 4);
+  *off_v = *off_k + align256(hist);
+  *rec = *off_v + align256(hist);
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+int32_t rlt_abi_version(void) { return RLT_ABI_VERSION; }
+
+const char *rlt_status_str(rlt_status s) {
+  switch (s) {
+    case RLT_OK: return "RLT_OK";
+    case RLT_ERR_INVALID_ARG: return "RLT_ERR_INVALID_ARG";
+    case RLT_ERR_SHAPE: return "RLT_ERR_SHAPE";
+    case RLT_ERR_RANGE: return "RLT_ERR_RANGE";
+    case RLT_ERR_STALE: return "RLT_ERR_STALE";
+    case RLT_ERR_CONVENTION: return "RLT_ERR_CONVENTION";
+    case RLT_ERR_UNSUPPORTED: return "RLT_ERR_UNSUPPORTED";
+    case RLT_ERR_DEVICE: return "RLT_ERR_DEVICE";
+  }
+  return "RLT_ERR_UNKNOWN";
+}
+
+const char *rlt_last_error(void) { return g_err.c_str(); }
+
+size_t rlt_model_bytes(const rlt_config *cfg) {
+  if (check_config(cfg) != RLT_OK) return 0;
+  rlt_model m;
+  m.cfg = *cfg;
+  model_plans(&m);
+  return model_layout(&m, nullptr);
+}
+
+rlt_status rlt_model_create(const rlt_config *cfg, const rlt_params *src, uint64_t model_version,
+                            void *dev_buf, size_t bytes, void *stream, rlt_model **out) {
+  rlt_status rs;
+  if (!out) return fail(RLT_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if ((rs = check_config(cfg)) != RLT_OK) return rs;
+  if (!src) return fail(RLT_ERR_INVALID_ARG, "params is NULL");
+  const void *need[] = {src->s_star, src->wg, src->bg, src->g1, src->g2, src->g3, src->wq,
+                        src->wk,     src->wv, src->wo, src->wqc, src->woc, src->w1, src->w2,
+                        src->go,     src->wout};
+  for (const void *p : need)
+    if (!p) return fail(RLT_ERR_INVALID_ARG, "a parameter pointer is NULL");
+  if (!dev_buf) return fail(RLT_ERR_INVALID_ARG, "dev_buf is NULL");
+  if ((uintptr_t)dev_buf % 256) return fail(RLT_ERR_SHAPE, "dev_buf must be 256-byte aligned");
+  const size_t need_bytes = rlt_model_bytes(cfg);
+  if (bytes < need_bytes)
+    return fail(RLT_ERR_SHAPE, "model buffer %zu bytes < %zu required", bytes, need_bytes);
+  if ((rs = device_health()) != RLT_OK) return rs;
+
+  rlt_model *m = new rlt_model();
+  m->cfg = *cfg;
+  m->version = model_version;
+  (void)hipGetDevice(&m->device);
+  m->esize = esize_of(cfg->dtype);
+  m->chunk = chunk_of(cfg);
+  model_plans(m);
+  model_layout(m, dev_buf);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int L = cfg->n_layers, d = cfg->d_model, F = cfg->d_ffn, es = m->esize;
+  const size_t dd = (size_t)d * d * es;
+  hipError_t e = hipSuccess;
+  auto pack = [&](const void *p, int rows, int K, int tile_begin, int tile_end,
+                  const PackedMat &dst) {
+    if (e == hipSuccess) e = launch_pack_tiles(p, rows, K, K, tile_begin, tile_end, dst, cfg->dtype, s);
+  };
+  auto tiles = [](const PackedMat &pm) { return pm.Np / 16; };
+  pack(src->wg, d, 2 * d, 0, tiles(m->wg), m->wg);
+  for (int l = 0; l < L; ++l) {
+    const char *wq = static_cast<const char *>(src->wq) + l * dd;
+    const char *wk = static_cast<const char *>(src->wk) + l * dd;
+    const char *wv = static_cast<const char *>(src->wv) + l * dd;
+    pack(wq, d, d, 0, d / 16, m->wqkv[l]);
+    pack(wk, d, d, d / 16, 2 * d / 16, m->wqkv[l]);
+    pack(wv, d, d, 2 * d / 16, tiles(m->wqkv[l]), m->wqkv[l]);
+    pack(static_cast<const char *>(src->wo) + l * dd, d, d, 0, tiles(m->wo[l]), m->wo[l]);
+    pack(static_cast<const char *>(src->wqc) + l * dd, d, d, 0, tiles(m->wqc[l]), m->wqc[l]);
+    pack(static_cast<const char *>(src->woc) + l * dd, d, d, 0, tiles(m->woc[l]), m->woc[l]);
+    pack(static_cast<const char *>(src->w1) + (size_t)l * F * d * es, F, d, 0, tiles(m->w1[l]),
+         m->w1[l]);
+    pack(static_cast<const char *>(src->w2) + (size_t)l * d * F * es, d, F, 0, tiles(m->w2[l]),
+         m->w2[l]);
+  }
+  pack(src->wout, cfg->vocab, d, 0, tiles(m->wout), m->wout);
+  if (e == hipSuccess) e = launch_copy(m->s_star, src->s_star, (size_t)d * 4, s);
+  if (e == hipSuccess) e = launch_copy(m->bg, src->bg, (size_t)d * 4, s);
+  if (e == hipSuccess) e = launch_copy(m->go, src->go, (size_t)d * 4, s);
+  if (e == hipSuccess) e = launch_copy(m->g1, src->g1, (size_t)L * d * 4, s);
+  if (e == hipSuccess) e = launch_copy(m->g2, src->g2, (size_t)L * d * 4, s);
+  if (e == hipSuccess) e = launch_copy(m->g3, src->g3, (size_t)L * d * 4, s);
+  if (e != hipSuccess) {
+    delete m;
+    return hip_fail(e, "packing weights");
+  }
+  *out = m;
+  return ok();
+}
+
+void rlt_model_destroy(rlt_model *m) { delete m; }
+
+size_t rlt_state_bytes(const rlt_config *cfg, int32_t batch, int32_t max_tokens) {
+  if (check_config(cfg) != RLT_OK || batch < 1 || max_tokens < 1) return 0;
+  rlt_state st;
+  st.cfg = *cfg;
+  return state_layout(nullptr, *cfg, &st, nullptr, batch, max_tokens);
+}
+
+rlt_status rlt_state_init(const rlt_model *m, int32_t batch, int32_t max_tokens, void *dev_buf,
+                          size_t bytes, void *stream, rlt_state **out) {
+  if (!out) return fail(RLT_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!m) return fail(RLT_ERR_INVALID_ARG, "model is NULL");
+  if (batch < 1) return fail(RLT_ERR_INVALID_ARG, "batch must be >= 1");
+  if (max_tokens < 1) return fail(RLT_ERR_INVALID_ARG, "max_tokens must be >= 1");
+  if (!dev_buf) return fail(RLT_ERR_INVALID_ARG, "dev_buf is NULL");
+  if ((uintptr_t)dev_buf % 256) return fail(RLT_ERR_SHAPE, "dev_buf must be 256-byte aligned");
+  const size_t need = rlt_state_bytes(&m->cfg, batch, max_tokens);
+  if (bytes < need) return fail(RLT_ERR_SHAPE, "state buffer %zu bytes < %zu required", bytes, need);
+  rlt_status rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  rlt_state *st = new rlt_state();
+  st->cfg = m->cfg;
+  st->version = m->version;
+  st->device = m->device;
+  st->B = batch;
+  st->max_tokens = max_tokens;
+  st->bytes = bytes;
+  state_layout(m, m->cfg, st, dev_buf, batch, max_tokens);
+  st->host_pos.assign(batch, 0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_state_init(st->s, st->pos, m->s_star, batch, m->cfg.d_model, nullptr,
+                                   batch, s);
+  if (e == hipSuccess) e = launch_zero(st->attn_cnt, (size_t)batch * m->cfg.n_heads * 4, s);
+  if (e == hipSuccess) e = launch_zero(st->gemm_cnt, std::max<size_t>(st->gemm_cnt_n, 1) * 4, s);
+  if (e != hipSuccess) {
+    delete st;
+    return hip_fail(e, "state init");
+  }
+  *out = st;
+  return ok();
+}
+
+void rlt_state_destroy(rlt_state *st) {
+  if (!st) return;
+  for (ProfRec &r : st->prof) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  delete st;
+}
+
+rlt_status rlt_state_reset(const rlt_model *m, rlt_state *st, int32_t n, const int32_t *host_slots,
+                           void *stream) {
+  rlt_status rs;
+  if ((rs = check_state(m, st)) != RLT_OK) return rs;
+  if (!host_slots) return fail(RLT_ERR_INVALID_ARG, "host_slots is NULL");
+  if ((rs = check_slots(st, n, host_slots)) != RLT_OK) return rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rs = stage_slots(st, n, host_slots, s)) != RLT_OK) return rs;
+  hipError_t e = launch_state_init(st->s, st->pos, m->s_star, st->B, m->cfg.d_model, st->slots_dev,
+                                   n, s);
+  if (e != hipSuccess) return hip_fail(e, "reset");
+  for (int i = 0; i < n; ++i) st->host_pos[host_slots[i]] = 0;
+  return ok();
+}
+
+rlt_status rlt_decoder_step(const rlt_model *m, rlt_state *st, int32_t n, const int32_t *host_slots,
+                            const void *dev_e, const rlt_memory *mem, float *dev_logits,
+                            void *stream) {
+  rlt_status rs;
+  if ((rs = check_state(m, st)) != RLT_OK) return rs;
+  if ((rs = check_slots(st, n, host_slots)) != RLT_OK) return rs;
+  if (!dev_e) return fail(RLT_ERR_INVALID_ARG, "dev_e is NULL");
+  int max_slot = n - 1;
+  if (host_slots) max_slot = *std::max_element(host_slots, host_slots + n);
+  if ((rs = check_memory(m, mem, max_slot)) != RLT_OK) return rs;
+  if ((rs = check_positions(st, mem, n, host_slots, 1)) != RLT_OK) return rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool identity = true;
+  if (host_slots)
+    for (int i = 0; i < n; ++i) identity = identity && host_slots[i] == i;
+  if (!identity && (rs = stage_slots(st, n, host_slots, s)) != RLT_OK) return rs;
+  if ((rs = enqueue_step(m, st, n, identity, host_slots, dev_e, m->cfg.d_model, mem, dev_logits,
+                         m->cfg.vocab, s)) != RLT_OK)
+    return rs;
+  return ok();
+}
+
+rlt_status rlt_run_sequence(const rlt_model *m, rlt_state *st, int32_t T, const void *dev_e,
+                            const rlt_memory *mem, float *dev_logits, int32_t logits_mode,
+                            void *stream) {
+  rlt_status rs;
+  if ((rs = check_state(m, st)) != RLT_OK) return rs;
+  if (T < 1) return fail(RLT_ERR_INVALID_ARG, "T must be >= 1");
+  if (!dev_e) return fail(RLT_ERR_INVALID_ARG, "dev_e is NULL");
+  if (logits_mode != RLT_LOGITS_ALL && logits_mode != RLT_LOGITS_LAST &&
+      logits_mode != RLT_LOGITS_NONE)
+    return fail(RLT_ERR_INVALID_ARG, "bad logits_mode");
+  if (logits_mode != RLT_LOGITS_NONE && !dev_logits)
+    return fail(RLT_ERR_INVALID_ARG, "dev_logits is NULL");
+  if ((rs = check_memory(m, mem, st->B - 1)) != RLT_OK) return rs;
+  if ((rs = check_positions(st, mem, st->B, nullptr, T)) != RLT_OK) return rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = m->cfg.d_model, V = m->cfg.vocab, es = m->esize;
+  for (int k = 0; k < T; ++k) {
+    const void *ek = static_cast<const char *>(dev_e) + (size_t)k * d * es;
+    float *lk = nullptr;
+    int64_t ld = V;
+    if (logits_mode == RLT_LOGITS_ALL) {
+      lk = dev_logits + (size_t)k * V;
+      ld = (int64_t)T * V;
+    } else if (logits_mode == RLT_LOGITS_LAST && k == T - 1) {
+      lk = dev_logits;
+    }
+    if ((rs = enqueue_step(m, st, st->B, true, nullptr, ek, (int64_t)T * d, mem, lk, ld, s)) !=
+        RLT_OK)
+      return rs;
+  }
+  return ok();
+}
+
+int32_t rlt_state_position(const rlt_state *st, int32_t slot) {
+  if (!st || slot < 0 || slot >= st->B) return -1;
+  return st->host_pos[slot];
+}
+
+size_t rlt_snapshot_bytes(const rlt_config *cfg, int32_t n) {
+  if (check_config(cfg) != RLT_OK || n < 1) return 0;
+  size_t a, b, c, rec;
+  snapshot_offsets(cfg, &a, &b, &c, &rec);
+  return rec * (size_t)n;
+}
+
+rlt_status rlt_state_export(const rlt_model *m, const rlt_state *st, int32_t n,
+                            const int32_t *host_slots, void *dev_snap, void *stream) {
+  rlt_status rs;
+  if ((rs = check_state(m, st)) != RLT_OK) return rs;
+  if (!host_slots) return fail(RLT_ERR_INVALID_ARG, "host_slots is NULL");
+  if ((rs = check_slots(st, n, host_slots)) != RLT_OK) return rs;
+  if (!dev_snap) return fail(RLT_ERR_INVALID_ARG, "dev_snap is NULL");
+  if ((uintptr_t)dev_snap % 256) return fail(RLT_ERR_SHAPE, "dev_snap must be 256-byte aligned");
+  if ((rs = device_health()) != RLT_OK) return rs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rlt_state *mst = const_cast<rlt_state *>(st);
+  if ((rs = stage_slots(mst, n, host_slots, s)) != RLT_OK) return rs;
+  SnapArgs a;
+  memset(&a, 0, sizeof a);
+  snapshot_offsets(&m->cfg, &a.off_s, &a.off_k, &a.off_v, &a.rec_bytes);
+  a.snap = dev_snap;
+  a.s = st->s;
+  a.pos = st->pos;
+  a.ring_k = st->ring_k;
+  a.ring_v = st->ring_v;
+  a.slots = st->slots_dev;
+  a.n = n;
+  a.B = st->B;
+  a.L = m->cfg.n_layers;
+  a.H = m->cfg.n_heads;
+  a.W = m->cfg.window;
+  a.dh = m->cfg.head_dim;
+  a.d = m->cfg.d_model;
+  a.dtype = m->cfg.dtype;
+  a.version = m->version;
+  hipError_t e = launch_export(a, s);
+  if (e != hipSuccess) return hip_fail(e, "export");
+  return ok();
+}
+
+rlt_status rlt_state_import(const rlt_model *m, rlt_state *st, int32_t n, const int32_t *host_slots,
+                            const void *dev_snap, void *stream) {
+  rlt_status rs;
+  if ((rs = check_state(m, st)) != RLT_OK) return rs;
+  if (!host_slots) return fail(RLT_ERR_INVALID_ARG, "host_slots is NULL");
+  if ((rs = check_slots(st, n, host_slots)) != RLT_OK) return rs;
+  if (!dev_snap) return fail(RLT_ERR_INVALID_ARG, "dev_snap is NULL");
+  if ((uintptr_t)dev_snap % 256) return fail(RLT_ERR_SHAPE, "dev_snap must be 256-byte aligned");
+  if ((rs = device_health()) != RLT_OK) return rs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SnapArgs a;
+  memset(&a, 0, sizeof a);
+  snapshot_offsets(&m->cfg, &a.off_s, &a.off_k, &a.off_v, &a.rec_bytes);
+  // read the headers back and check them before touching the state
+  std::vector<int> pos(n);
+  for (int i = 0; i < n; ++i) {
+    unsigned char hd[48];
+    hipError_t e = hipMemcpyAsync(hd, static_cast<const char *>(dev_snap) + (size_t)i * a.rec_bytes,
+                                  48, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "reading snapshot header");
+    uint32_t magic, fmt;
+    int32_t f[8];
+    uint64_t ver;
+    memcpy(&magic, hd, 4);
+    memcpy(&fmt, hd + 4, 4);
+    memcpy(f, hd + 8, 32);
+    memcpy(&ver, hd + 40, 8);
+    const rlt_config &c = m->cfg;
+    if (magic != 0x534C5452u || fmt != 1u)
+      return fail(RLT_ERR_CONVENTION, "record %d: not a snapshot record", i);
+    if (f[0] != c.d_model || f[1] != c.n_heads || f[2] != c.head_dim || f[3] != c.n_layers)
+      return fail(RLT_ERR_CONVENTION, "record %d: shape differs from the model", i);
+    if (f[4] != c.window) return fail(RLT_ERR_CONVENTION, "record %d: window %d != %d", i, f[4], c.window);
+    if (f[5] != c.dtype) return fail(RLT_ERR_CONVENTION, "record %d: dtype differs", i);
+    if (ver != m->version)
+      return fail(RLT_ERR_CONVENTION, "record %d: model version %llu != %llu", i,
+                  (unsigned long long)ver, (unsigned long long)m->version);
+    if (f[6] < 0 || f[6] > st->max_tokens)
+      return fail(RLT_ERR_CONVENTION, "record %d: position %d outside [0, max_tokens]", i, f[6]);
+    pos[i] = f[6];
+  }
+  if ((rs = stage_slots(st, n, host_slots, s)) != RLT_OK) return rs;
+  a.csnap = dev_snap;
+  a.s = st->s;
+  a.pos = st->pos;
+  a.ring_k = st->ring_k;
+  a.ring_v = st->ring_v;
+  a.slots = st->slots_dev;
+  a.n = n;
+  a.B = st->B;
+  a.L = m->cfg.n_layers;
+  a.H = m->cfg.n_heads;
+  a.W = m->cfg.window;
+  a.dh = m->cfg.head_dim;
+  a.d = m->cfg.d_model;
+  a.dtype = m->cfg.dtype;
+  a.version = m->version;
+  hipError_t e = launch_import(a, s);
+  if (e != hipSuccess) return hip_fail(e, "import");
+  for (int i = 0; i < n; ++i) st->host_pos[host_slots[i]] = pos[i];
+  return ok();
+}
+
+rlt_status rlt_profile_begin(rlt_state *st, int32_t kclass, int32_t max_launches) {
+  if (!st) return fail(RLT_ERR_INVALID_ARG, "state is NULL");
+  if (kclass < -1 || kclass >= RLT_K_NCLASSES) return fail(RLT_ERR_INVALID_ARG, "bad kernel class");
+  if (max_launches < 0) return fail(RLT_ERR_INVALID_ARG, "max_launches < 0");
+  st->prof_class = kclass;
+  st->prof_max = max_launches;
+  return ok();
+}
+
+rlt_status rlt_profile_collect(rlt_state *st, double *total_ms, int32_t *launches,
+                               double *bytes_moved) {
+  if (!st) return fail(RLT_ERR_INVALID_ARG, "state is NULL");
+  double tot = 0, bytes = 0;
+  int cnt = 0;
+  for (ProfRec &r : st->prof) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "profile events");
+    tot += ms;
+    bytes += r.bytes;
+    ++cnt;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  st->prof.clear();
+  if (total_ms) *total_ms = tot;
+  if (launches) *launches = cnt;
+  if (bytes_moved) *bytes_moved = bytes;
+  return ok();
+}
+
+}  // extern "C"

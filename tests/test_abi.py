@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every symbol include/rlt.h declares, and
+rejects bad arguments on the host before any device work (no GPU needed)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from recurrent_decode_step_amd import binding
+from recurrent_decode_step_amd.configs import TINY, SMALL, REFDEPTH, LARGEBATCH, LONGCTX
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("librlt.so is not built (run __graft_entry__.build())")
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "rlt.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlt_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = lib()
+    names = declared_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(binding.EXPORTED)
+    assert L.rlt_abi_version() == 1
+
+
+def test_status_strings():
+    L = lib()
+    for code in range(8):
+        assert L.rlt_status_str(code).decode().startswith("RLT_")
+
+
+def cfg_of(w, **kw):
+    c = binding.make_config(w.model)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_size_queries():
+    L = lib()
+    # model bytes cover the packed weights
+    for w in (TINY, SMALL, REFDEPTH, LONGCTX):
+        m = w.model
+        es = 2 if m.dtype == 1 else 4
+        params = (2 * m.d_model ** 2 + m.n_layers * (6 * m.d_model ** 2 + 2 * m.d_model * m.d_ffn)
+                  + m.vocab * m.d_model)
+        got = L.rlt_model_bytes(C.byref(cfg_of(w)))
+        assert params * es <= got <= params * es * 1.05 + (1 << 20), (w.name, got)
+    # state bytes cover s, positions and the window cache [L][B][H][W][dh] x 2
+    m = LARGEBATCH.model
+    ring = 2 * m.n_layers * 256 * m.n_heads * m.window * m.head_dim * 2
+    got = L.rlt_state_bytes(C.byref(cfg_of(LARGEBATCH)), 256, 8192)
+    assert ring < got < ring * 1.2
+    # snapshot record: header + s + 2 * [L][H][W-1][dh]
+    m = TINY.model
+    rec = L.rlt_snapshot_bytes(C.byref(cfg_of(TINY)), 1)
+    assert rec == binding.snapshot_layout(m)[0]
+    assert L.rlt_snapshot_bytes(C.byref(cfg_of(TINY)), 3) == 3 * rec
+
+
+@pytest.mark.parametrize("field,value", [
+    ("head_dim", 15), ("n_heads", 0), ("mem_groups", 3), ("dtype", 7), ("d_ffn", 100),
+    ("window", 0), ("attn_chunk", -1)])
+def test_bad_configs_are_rejected(field, value):
+    L = lib()
+    c = cfg_of(TINY, **{field: value})
+    assert L.rlt_model_bytes(C.byref(c)) == 0
+    out = C.c_void_p()
+    p = binding.rlt_params()
+    st = L.rlt_model_create(C.byref(c), C.byref(p), 1, None, 0, None, C.byref(out))
+    assert st in (binding.RLT_ERR_INVALID_ARG, binding.RLT_ERR_SHAPE, binding.RLT_ERR_UNSUPPORTED)
+    assert L.rlt_last_error().decode() != ""
+    assert not out.value
+
+
+def test_create_argument_checks_before_device_work():
+    L = lib()
+    c = cfg_of(TINY)
+    out = C.c_void_p()
+    p = binding.rlt_params()
+    # NULL parameter pointers
+    assert L.rlt_model_create(C.byref(c), C.byref(p), 1, None, 0, None,
+                              C.byref(out)) == binding.RLT_ERR_INVALID_ARG
+    # all pointers set but buffer misaligned / too small (fake addresses, never touched)
+    for name, _ in binding.rlt_params._fields_:
+        setattr(p, name, 0x1000)
+    assert L.rlt_model_create(C.byref(c), C.byref(p), 1, C.c_void_p(0x1008), 1 << 30, None,
+                              C.byref(out)) == binding.RLT_ERR_SHAPE
+    assert L.rlt_model_create(C.byref(c), C.byref(p), 1, C.c_void_p(0x1000), 10, None,
+                              C.byref(out)) == binding.RLT_ERR_SHAPE
+    assert "required" in L.rlt_last_error().decode()
+
+
+def test_null_handles():
+    L = lib()
+    out = C.c_void_p()
+    assert L.rlt_state_init(None, 4, 64, None, 0, None, C.byref(out)) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_decoder_step(None, None, 1, None, None, None, None, None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_run_sequence(None, None, 1, None, None, None, 0, None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_state_reset(None, None, 1, None, None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_state_export(None, None, 1, None, None, None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_state_import(None, None, 1, None, None, None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_state_position(None, 0) == -1
+    assert L.rlt_profile_begin(None, 0, 1) == binding.RLT_ERR_INVALID_ARG

@@ -1,0 +1,331 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Tolerances: fp32 models max |d logit| <= 1e-4; bf16 models relative L2 of the
+logits <= 2e-2 at every checked step.  Bitwise checks compare the library with
+itself (split, resume, batch composition, repeat)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _tiny import tiny_cfg, make_model, inputs
+from recurrent_decode_step_amd import binding, synth
+from recurrent_decode_step_amd.configs import ModelConfig, DTYPE_BF16, DTYPE_FP32
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def to_dev(params):
+    return {k: v.to(DEV) for k, v in params.items()}
+
+
+class Rig:
+    """Model + state + inputs of one case (inputs drawn on the CPU)."""
+
+    def __init__(self, cfg, B, T, attn_chunk=0, capacity=None, version=1, params=None):
+        self.cfg = cfg
+        self.B, self.T = B, T
+        self.params = params if params is not None else synth.model_params(cfg)
+        self.e, self.mk, self.mv = inputs(cfg, B, T, capacity or T)
+        self.model = binding.Model(cfg, to_dev(self.params), version=version, attn_chunk=attn_chunk)
+        self.mem = (self.mk.to(DEV), self.mv.to(DEV))
+        self.ed = self.e.to(DEV)
+        self.capacity = capacity or T
+
+    def state(self):
+        return binding.State(self.model, self.B, self.capacity)
+
+    def oracle_model(self, precision="fp32"):
+        m, _ = make_model(self.cfg, params=self.params, precision=precision)
+        return m
+
+    def oracle_run(self, precision="fp32", rows=None, steps=None):
+        m = self.oracle_model(precision)
+        rows = list(range(self.B)) if rows is None else rows
+        st = [oracle.initial_state(m) for _ in rows]
+        return oracle.run_sequence(m, st, self.e[rows], self.mk, self.mv, mem_index=rows,
+                                   steps=steps)
+
+
+F32_CASES = {
+    "tiny": (dict(), 0, 4, 40),
+    "tiny-chunk3": (dict(), 3, 4, 40),              # several attention chunks + combine
+    "window1": (dict(window=1), 0, 3, 20),
+    "window2-chunk1": (dict(window=2), 1, 3, 20),
+    "window-over-T": (dict(window=64), 5, 2, 30),
+    "L3-G3": (dict(n_layers=3, mem_groups=3), 4, 3, 24),
+    "H1-dh32": (dict(n_heads=1), 0, 2, 20),
+    "dh64": (dict(d_model=128, n_heads=2, d_ffn=256, vocab=40), 16, 5, 24),
+    "dh128-B20": (dict(d_model=256, n_heads=2, d_ffn=256, vocab=70), 32, 20, 12),
+    "dh256": (dict(d_model=256, n_heads=1, d_ffn=128, vocab=33, window=5), 0, 3, 12),
+}
+
+
+@pytest.mark.parametrize("name", list(F32_CASES))
+def test_f32_run_sequence_matches_oracle(name):
+    kw, chunk, B, T = F32_CASES[name]
+    cfg = tiny_cfg(**kw)
+    say(f"[f32 parity] case={name} cfg={kw} chunk={chunk} B={B} T={T}")
+    rig = Rig(cfg, B, T, attn_chunk=chunk)
+    st = rig.state()
+    got = binding.rlt_run_sequence(rig.model, st, rig.ed, rig.mem).cpu().numpy()
+    ref = rig.oracle_run()
+    err = float(np.max(np.abs(got - ref)))
+    say(f"  max|dlogit| = {err:.3e}")
+    assert err <= 1e-4
+    for b in range(B):
+        assert st.position(b) == T
+
+
+def test_f32_large_batch_columns():
+    """More than 256 rows: several 256-column groups per GEMM launch."""
+    cfg = tiny_cfg()
+    B, T = 300, 3
+    say(f"[f32 parity] B={B} T={T}")
+    rig = Rig(cfg, B, T)
+    got = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, rig.mem).cpu().numpy()
+    rows = [0, 17, 255, 256, 299]
+    ref = rig.oracle_run(rows=rows)
+    err = float(np.max(np.abs(got[rows] - ref)))
+    say(f"  max|dlogit| = {err:.3e}")
+    assert err <= 1e-4
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+BF16_SMALL = ModelConfig(vocab=4096, d_model=512, n_heads=8, n_layers=12, d_ffn=2048,
+                         window=128, mem_groups=12, dtype=DTYPE_BF16)
+
+
+def test_bf16_small_model_matches_oracle():
+    """The small bf16 model (d=512, 8 heads, 12 layers, G = 12, W = 128),
+    8 sequences over 150 steps (past the window)."""
+    cfg = BF16_SMALL
+    B, T = 8, 150
+    say(f"[bf16 parity] small model B={B} T={T}")
+    rig = Rig(cfg, B, T)
+    got = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, rig.mem).cpu().numpy()
+    rows = [0, 5]
+    ref32 = rig.oracle_run("fp32", rows=rows)
+    ref16 = rig.oracle_run("bf16", rows=rows)
+    worst32 = max(rel_l2(got[r, t], ref32[i, t]) for i, r in enumerate(rows) for t in range(T))
+    worst16 = max(rel_l2(got[r, t], ref16[i, t]) for i, r in enumerate(rows) for t in range(T))
+    say(f"  max over steps rel-L2: vs fp32 oracle {worst32:.3e}, vs bf16-emulation {worst16:.3e}")
+    assert worst32 <= 2e-2
+    assert worst16 <= 2e-2
+
+
+# ------------------------------------------------------------------ bitwise
+def test_split_and_chunking_are_bitwise_invisible():
+    """Proposition 3.1 on the GPU: run(T) == run(k) + (T-k) steps == run(k) + run(T-k)."""
+    cfg = tiny_cfg()
+    B, T = 3, 24
+    rig = Rig(cfg, B, T, attn_chunk=3)
+    full = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, rig.mem).cpu()
+    for k in (1, cfg.window - 1, cfg.window, cfg.window + 1, T // 2):
+        say(f"[split] k={k}")
+        st = rig.state()
+        a = binding.rlt_run_sequence(rig.model, st, rig.ed[:, :k], rig.mem).cpu()
+        rest = [binding.rlt_decoder_step(rig.model, st, rig.ed[:, j], rig.mem).cpu()
+                for j in range(k, T)]
+        assert torch.equal(torch.cat([a, torch.stack(rest, 1)], 1), full)
+        st = rig.state()
+        a = binding.rlt_run_sequence(rig.model, st, rig.ed[:, :k], rig.mem).cpu()
+        b = binding.rlt_run_sequence(rig.model, st, rig.ed[:, k:], rig.mem).cpu()
+        assert torch.equal(torch.cat([a, b], 1), full)
+
+
+def test_repeat_is_bitwise_identical_bf16():
+    cfg = BF16_SMALL.with_(n_layers=2, mem_groups=1)
+    rig = Rig(cfg, 4, 20)
+    say("[repeat] bf16 two runs")
+    a = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, rig.mem).cpu()
+    b = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, rig.mem).cpu()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", [DTYPE_FP32, DTYPE_BF16])
+def test_batch_composition_is_bitwise_invisible(dtype):
+    """A slot's logits do not depend on which slots share the step."""
+    cfg = tiny_cfg(dtype=dtype) if dtype == DTYPE_FP32 else BF16_SMALL.with_(n_layers=2, mem_groups=2)
+    B, T = 40, 10
+    rig = Rig(cfg, B, T, attn_chunk=4)
+    say(f"[batch invariance] dtype={dtype}")
+    full = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, rig.mem).cpu()
+    st = rig.state()
+    # step disjoint subsets in turn, each slot once per step
+    groups = [[7], [33, 2, 19], [i for i in range(B) if i not in (7, 33, 2, 19)][::-1]]
+    out = torch.empty_like(full)
+    for j in range(T):
+        for g in groups:
+            e = rig.ed[g, j]
+            lg = binding.rlt_decoder_step(rig.model, st, e, rig.mem, slots=g).cpu()
+            out[g, j] = lg
+    assert torch.equal(out, full)
+
+
+def test_memory_causality_bitwise():
+    """Memory positions after t never change logits_t; position t does."""
+    cfg = tiny_cfg()
+    B, T = 2, 12
+    rig = Rig(cfg, B, T)
+    base = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, rig.mem).cpu()
+    j = 7
+    mk2 = rig.mem[0].clone()
+    mk2[:, :, :, j - 1, :] += 0.25
+    say("[memory causality]")
+    out = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, (mk2, rig.mem[1])).cpu()
+    assert torch.equal(out[:, :j - 1], base[:, :j - 1])
+    assert not torch.equal(out[:, j - 1], base[:, j - 1])
+
+
+@pytest.mark.parametrize("dtype", [DTYPE_FP32, DTYPE_BF16])
+def test_export_import_resume(dtype):
+    """Snapshot at k, restore into a fresh state, continue: bitwise the same as
+    never stopping.  Restoring s with the window cache wiped is not."""
+    cfg = tiny_cfg(dtype=dtype)
+    B, T, k = 3, 26, 11
+    rig = Rig(cfg, B, T, attn_chunk=2)
+    full = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, rig.mem).cpu()
+    st = rig.state()
+    binding.rlt_run_sequence(rig.model, st, rig.ed[:, :k], rig.mem)
+    snap = binding.rlt_state_export(rig.model, st, [0, 1, 2])
+    say(f"[resume] dtype={dtype} k={k}")
+    st2 = rig.state()
+    binding.rlt_state_import(rig.model, st2, snap, [0, 1, 2])
+    assert [st2.position(b) for b in range(B)] == [k] * B
+    rest = binding.rlt_run_sequence(rig.model, st2, rig.ed[:, k:], rig.mem).cpu()
+    assert torch.equal(rest, full[:, k:])
+    # canonical record contents: s and history in logical order
+    rec, off_s, off_k, off_v = binding.snapshot_layout(cfg)
+    es = 4 if dtype == DTYPE_FP32 else 2
+    raw = snap.cpu()
+    hdr = raw[:48].view(torch.int32)
+    assert int(hdr[8]) == k and int(hdr[6]) == cfg.window
+    # wipe the history of every record: the continuation must change
+    bad = snap.clone()
+    for r in range(B):
+        bad[r * rec + off_k: r * rec + rec] = 0
+    st3 = rig.state()
+    binding.rlt_state_import(rig.model, st3, bad, [0, 1, 2])
+    wrong = binding.rlt_run_sequence(rig.model, st3, rig.ed[:, k:], rig.mem).cpu()
+    assert not torch.equal(wrong[:, 0], full[:, k])
+
+
+def test_snapshot_history_matches_oracle_cache():
+    """The exported window cache equals the oracle's retained entries."""
+    cfg = tiny_cfg()
+    B, T = 2, 13
+    rig = Rig(cfg, B, T)
+    st = rig.state()
+    binding.rlt_run_sequence(rig.model, st, rig.ed, rig.mem)
+    snap = binding.rlt_state_export(rig.model, st, [0, 1]).cpu()
+    m = rig.oracle_model()
+    ost = [oracle.initial_state(m) for _ in range(B)]
+    oracle.run_sequence(m, ost, rig.e, rig.mk, rig.mv)
+    rec, off_s, off_k, off_v = binding.snapshot_layout(cfg)
+    L, H, dh, Wm1 = cfg.n_layers, cfg.n_heads, cfg.head_dim, cfg.window - 1
+    for b in range(B):
+        r = snap[b * rec:(b + 1) * rec]
+        s = r[off_s:off_s + cfg.d_model * 4].view(torch.float32).numpy()
+        K = r[off_k:off_k + L * H * Wm1 * dh * 4].view(torch.float32).reshape(L, H, Wm1, dh).numpy()
+        assert np.max(np.abs(s - ost[b].s)) < 1e-4
+        for l in range(L):
+            np.testing.assert_allclose(K[l].transpose(1, 0, 2), ost[b].K[l], atol=2e-5)
+
+
+def test_ragged_imported_states_match_oracle():
+    """Slots at different positions (imported synthetic states) in one batch."""
+    cfg = tiny_cfg()
+    starts = [1, 4, 9, 21]            # token index t about to be consumed
+    B, steps = len(starts), 6
+    cap = max(starts) + steps
+    rig = Rig(cfg, B, cap, attn_chunk=3)
+    recs = []
+    for b, t in enumerate(starts):
+        s = synth.imported_state(cfg, t, index=b)
+        if t == 1:
+            s["s"] = rig.params["s_star"].clone()
+        recs.append(s)
+    snap = binding.build_snapshot(cfg, recs, version=1, device=DEV)
+    st = rig.state()
+    binding.rlt_state_import(rig.model, st, snap, list(range(B)))
+    m = rig.oracle_model()
+    ost = [oracle.state_from_arrays(m, r["pos"], r["s"], r["K"], r["V"]) for r in recs]
+    say("[ragged import] starts=" + str(starts))
+    for j in range(steps):
+        e_rows = torch.stack([rig.e[b, starts[b] - 1 + j] for b in range(B)])
+        got = binding.rlt_decoder_step(rig.model, st, e_rows.to(DEV), rig.mem).cpu().numpy()
+        ref = oracle.decoder_step(m, ost, e_rows, rig.mk, rig.mv)
+        err = float(np.max(np.abs(got - ref)))
+        assert err <= 1e-4, (j, err)
+
+
+def test_reset_returns_slot_to_initial_state():
+    cfg = tiny_cfg()
+    B, T = 3, 10
+    rig = Rig(cfg, B, T)
+    st = rig.state()
+    binding.rlt_run_sequence(rig.model, st, rig.ed[:, :5], rig.mem)
+    binding.rlt_state_reset(rig.model, st, [1])
+    assert st.position(1) == 0 and st.position(0) == 5
+    got = binding.rlt_decoder_step(rig.model, st, rig.ed[[1], 0], rig.mem, slots=[1]).cpu()
+    fresh = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed[:, :1], rig.mem).cpu()
+    assert torch.equal(got[0], fresh[1, 0])
+
+
+# ------------------------------------------------------------- error paths
+def test_stale_state_is_rejected():
+    cfg = tiny_cfg()
+    rig = Rig(cfg, 2, 4, version=1)
+    st = rig.state()
+    newer = binding.Model(cfg, to_dev(rig.params), version=2)
+    with pytest.raises(binding.RLTError) as ei:
+        binding.rlt_decoder_step(newer, st, rig.ed[:, 0], rig.mem)
+    assert ei.value.status == binding.RLT_ERR_STALE
+    assert st.position(0) == 0
+
+
+def test_snapshot_convention_mismatch_is_rejected():
+    cfg = tiny_cfg()
+    rig = Rig(cfg, 2, 6)
+    st = rig.state()
+    binding.rlt_run_sequence(rig.model, st, rig.ed[:, :3], rig.mem)
+    snap = binding.rlt_state_export(rig.model, st, [0])
+    other = binding.Model(cfg.with_(window=4), to_dev(rig.params), version=1)
+    st2 = binding.State(other, 2, 6)
+    with pytest.raises(binding.RLTError) as ei:
+        binding.rlt_state_import(other, st2, snap, [0])
+    assert ei.value.status == binding.RLT_ERR_CONVENTION
+    v2 = binding.Model(cfg, to_dev(rig.params), version=5)
+    st3 = binding.State(v2, 2, 6)
+    with pytest.raises(binding.RLTError) as ei:
+        binding.rlt_state_import(v2, st3, snap, [0])
+    assert ei.value.status == binding.RLT_ERR_CONVENTION
+
+
+def test_position_past_memory_is_rejected_without_side_effects():
+    cfg = tiny_cfg()
+    rig = Rig(cfg, 2, 4)
+    st = rig.state()
+    binding.rlt_run_sequence(rig.model, st, rig.ed[:, :4], rig.mem)
+    before = binding.rlt_state_export(rig.model, st, [0, 1]).clone()
+    with pytest.raises(binding.RLTError) as ei:
+        binding.rlt_decoder_step(rig.model, st, rig.ed[:, 0], rig.mem)
+    assert ei.value.status == binding.RLT_ERR_RANGE
+    with pytest.raises(binding.RLTError) as ei:
+        binding.rlt_decoder_step(rig.model, st, rig.ed[:, 0], rig.mem, slots=[1, 1])
+    assert ei.value.status == binding.RLT_ERR_INVALID_ARG
+    after = binding.rlt_state_export(rig.model, st, [0, 1])
+    assert torch.equal(before, after)
+    assert st.position(0) == 4
