@@ -216,14 +216,19 @@ rlt_status rlt_state_import(const rlt_model *m, rlt_state *st, int32_t n,
 /* Kernel classes for per-class timing. */
 enum { RLT_K_SETUP = 0, RLT_K_GEMM = 1, RLT_K_SWA = 2, RLT_K_CROSS = 3, RLT_K_NCLASSES = 4 };
 
-/* Start recording a HIP event pair around every launch of kernel class `kclass`
- * on this state (up to max_launches), or stop with kclass = -1.  Recording
- * adds host work per launch and is meant for measurement runs only. */
-rlt_status rlt_profile_begin(rlt_state *st, int32_t kclass, int32_t max_launches);
-/* Sum of the recorded launch durations (ms) and their count; waits for the
- * recorded events.  Clears the record. */
-rlt_status rlt_profile_collect(rlt_state *st, double *total_ms, int32_t *launches,
-                               double *bytes_moved);
+/* Start recording a HIP event pair around every launch of the kernel classes
+ * in class_mask (bit 1 << RLT_K_*) on this state, during every step_stride-th
+ * step (step_stride >= 1), up to max_launches pairs; class_mask = 0 stops.
+ * Events come from a pool kept by the state.  Meant for measurement runs: each
+ * recorded pair adds two event records to the stream. */
+rlt_status rlt_profile_begin(rlt_state *st, int32_t class_mask, int32_t max_launches,
+                             int32_t step_stride);
+/* For kernel class kclass: the sum of the recorded launch durations (ms), their
+ * count, and the algorithmic bytes those launches move (weights, window cache
+ * and memory entries read once, activations in and out, as stored).  Waits for
+ * the recorded events, then clears that class's records. */
+rlt_status rlt_profile_collect(rlt_state *st, int32_t kclass, double *total_ms,
+                               int32_t *launches, double *bytes_moved);
 
 #ifdef __cplusplus
 }

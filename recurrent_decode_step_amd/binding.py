@@ -84,8 +84,8 @@ def load_library(path: str = LIB_PATH):
         "rlt_snapshot_bytes": (sz, [P(rlt_config), i32]),
         "rlt_state_export": (i32, [vp, vp, i32, P(i32), vp, vp]),
         "rlt_state_import": (i32, [vp, vp, i32, P(i32), vp, vp]),
-        "rlt_profile_begin": (i32, [vp, i32, i32]),
-        "rlt_profile_collect": (i32, [vp, P(C.c_double), P(i32), P(C.c_double)]),
+        "rlt_profile_begin": (i32, [vp, i32, i32, i32]),
+        "rlt_profile_collect": (i32, [vp, i32, P(C.c_double), P(i32), P(C.c_double)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -287,11 +287,14 @@ def build_snapshot(cfg: ModelConfig, records, version: int, device) -> torch.Ten
     return out
 
 
-def profile_begin(state: State, kclass: int, max_launches: int):
-    _check(load_library().rlt_profile_begin(state.handle, kclass, max_launches))
+def profile_begin(state: State, class_mask: int, max_launches: int, step_stride: int = 1):
+    """Record launches of the kernel classes in class_mask (bit 1 << RLT_K_*)."""
+    _check(load_library().rlt_profile_begin(state.handle, class_mask, max_launches, step_stride))
 
 
-def profile_collect(state: State):
+def profile_collect(state: State, kclass: int):
+    """(total ms, launches, algorithmic bytes) recorded for one kernel class."""
     tot, n, b = C.c_double(), C.c_int32(), C.c_double()
-    _check(load_library().rlt_profile_collect(state.handle, C.byref(tot), C.byref(n), C.byref(b)))
+    _check(load_library().rlt_profile_collect(state.handle, kclass, C.byref(tot), C.byref(n),
+                                              C.byref(b)))
     return tot.value, n.value, b.value

@@ -55,53 +55,34 @@ struct Arena {
 int esize_of(int dtype) { return dtype == RLT_DTYPE_BF16 ? 2 : 4; }
 int kstep_of(int dtype) { return dtype == RLT_DTYPE_BF16 ? 32 : 16; }
 
-// ---- GEMM plan: the k-split depends only on (N, K, dtype) so that a row's
-// result never depends on how many rows share the launch.
+// ---- GEMM plan.  K is cut into `parts` consecutive parts (one wavefront
+// each, at most 16 k-steps per batch of loads); the cut depends on K only, so a
+// row's result never depends on how many rows share the launch.
 struct GemmPlan {
-  int N, K, Np, KT, n_blocks, splits, ks_per_split;
+  int N, K, Np, KT, tiles, parts;
 };
 
 GemmPlan gemm_plan(int N, int K, int dtype) {
   GemmPlan p;
   p.N = N;
   p.K = K;
-  p.Np = cdiv(N, kRowsPerBlock) * kRowsPerBlock;
+  p.Np = cdiv(N, 16) * 16;
+  p.tiles = p.Np / 16;
   p.KT = cdiv(K, kstep_of(dtype));
-  p.n_blocks = p.Np / kRowsPerBlock;
-  const int target_wgs = 512;
-  int s = std::max(1, target_wgs / p.n_blocks);
-  s = std::min(s, p.KT);
-  int per = cdiv(p.KT, s);
-  const int gran = std::min(8, p.KT);      // whole staged sub-chunks where possible
-  per = cdiv(per, gran) * gran;
-  p.ks_per_split = per;
-  p.splits = cdiv(p.KT, per);
+  p.parts = std::max(1, std::min(kMaxParts, cdiv(p.KT, 16)));
   return p;
 }
 
-// batch-column blocking of a launch over n rows
+// batch-column blocking of a launch over n rows: 16, 32 or 64 rows per group
 struct ColPlan {
   int ncb, groups;
 };
 ColPlan col_plan(int n) {
   ColPlan c;
   const int blocks16 = cdiv(n, 16);
-  if (blocks16 <= 1) c.ncb = 1;
-  else if (blocks16 <= 2) c.ncb = 2;
-  else if (blocks16 <= 4) c.ncb = 4;
-  else if (blocks16 <= 8) c.ncb = 8;
-  else c.ncb = 16;
+  c.ncb = blocks16 <= 1 ? 1 : (blocks16 <= 2 ? 2 : 4);
   c.groups = cdiv(n, c.ncb * 16);
   return c;
-}
-
-size_t gemm_ws_bytes(const GemmPlan &g, int n) {
-  if (g.splits <= 1) return 0;
-  const ColPlan c = col_plan(n);
-  return (size_t)g.splits * g.n_blocks * c.groups * 4 * c.ncb * 64 * 16;
-}
-size_t gemm_counter_count(const GemmPlan &g, int n) {
-  return (size_t)g.n_blocks * col_plan(n).groups;
 }
 
 bool valid_dh(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128 || dh == 256; }
@@ -130,8 +111,7 @@ rlt_status check_config(const rlt_config *c) {
 
 int chunk_of(const rlt_config *c) {
   const int cap = attn_chunk_max(c->dtype, c->head_dim);
-  const int want = c->attn_chunk > 0 ? c->attn_chunk : kDefaultChunk;
-  return std::min(want, cap);
+  return c->attn_chunk > 0 ? std::min(c->attn_chunk, cap) : cap;
 }
 
 }  // namespace
@@ -151,6 +131,7 @@ struct rlt_model {
 struct ProfRec {
   hipEvent_t a, b;
   double bytes;
+  int cls;
 };
 
 struct rlt_state {
@@ -163,23 +144,17 @@ struct rlt_state {
   int *pos;
   char *ring_k, *ring_v;
   int *slots_dev;
-  int *rows_t, *rows_slot;
   float *x, *sumsq;
-  char *qbuf, *obuf, *hbuf;
-  int2 *items_swa, *items_mem;
-  int *n_items;  // [2]
-  int *start_swa, *start_mem;
-  float *attn_part;
-  int *attn_cnt;
-  float *ws;
-  int *gemm_cnt;
-  size_t ws_bytes, gemm_cnt_n;
+  char *xg, *qbuf, *obuf, *hbuf;
   std::vector<int> host_pos;
   std::vector<int> staged;   // slot list currently in slots_dev (empty: none)
   // profiling
-  int prof_class = -1;
+  int prof_mask = 0;
   int prof_max = 0;
+  int prof_stride = 1;
+  long long step_counter = 0;
   std::vector<ProfRec> prof;
+  std::vector<hipEvent_t> event_pool;
 };
 
 namespace {
@@ -239,50 +214,21 @@ size_t model_layout(rlt_model *m, void *base) {
   return align256(ar.off);
 }
 
-size_t state_layout(const rlt_model *mdl, const rlt_config &c, rlt_state *st, void *base, int B,
-                    int max_tokens) {
-  rlt_model tmp;
-  if (!mdl) {
-    tmp.cfg = c;
-    model_plans(&tmp);
-    mdl = &tmp;
-  }
+size_t state_layout(const rlt_config &c, rlt_state *st, void *base, int B) {
   const int L = c.n_layers, d = c.d_model, H = c.n_heads, dh = c.head_dim, W = c.window;
   const int es = esize_of(c.dtype);
-  const int ch = chunk_of(&c);
   Arena ar(base);
   st->s = ar.take<float>((size_t)B * d * 4);
   st->pos = ar.take<int>((size_t)B * 4);
   st->ring_k = ar.take<char>((size_t)L * B * H * W * dh * es);
   st->ring_v = ar.take<char>((size_t)L * B * H * W * dh * es);
   st->slots_dev = ar.take<int>((size_t)B * 4);
-  st->rows_t = ar.take<int>((size_t)B * 4);
-  st->rows_slot = ar.take<int>((size_t)B * 4);
   st->x = ar.take<float>((size_t)B * d * 4);
-  st->sumsq = ar.take<float>((size_t)cdiv(d, kRowsPerBlock) * B * 4);
+  st->sumsq = ar.take<float>((size_t)cdiv(d, 16) * B * 4);
+  st->xg = ar.take<char>((size_t)B * d * es);
   st->qbuf = ar.take<char>((size_t)B * d * es);
   st->obuf = ar.take<char>((size_t)B * d * es);
   st->hbuf = ar.take<char>((size_t)B * c.d_ffn * es);
-  const size_t items_swa = (size_t)B * cdiv(std::min(max_tokens, W), ch);
-  const size_t items_mem = (size_t)B * cdiv(max_tokens, ch);
-  st->items_swa = ar.take<int2>(items_swa * 8);
-  st->items_mem = ar.take<int2>(items_mem * 8);
-  st->n_items = ar.take<int>(64);
-  st->start_swa = ar.take<int>((size_t)B * 4);
-  st->start_mem = ar.take<int>((size_t)B * 4);
-  st->attn_part = ar.take<float>(std::max(items_swa, items_mem) * H * (dh + 2) * 4);
-  st->attn_cnt = ar.take<int>((size_t)B * H * 4);
-  const GemmPlan *plans[] = {&mdl->p_merge, &mdl->p_qkv, &mdl->p_o,
-                             &mdl->p_ffn1,  &mdl->p_ffn2, &mdl->p_head};
-  size_t ws = 0, cnt = 0;
-  for (const GemmPlan *g : plans) {
-    ws = std::max(ws, gemm_ws_bytes(*g, B));
-    cnt = std::max(cnt, gemm_counter_count(*g, B));
-  }
-  st->ws_bytes = ws;
-  st->gemm_cnt_n = cnt;
-  st->ws = ar.take<float>(std::max<size_t>(ws, 16));
-  st->gemm_cnt = ar.take<int>(std::max<size_t>(cnt, 1) * 4);
   return align256(ar.off);
 }
 
@@ -343,6 +289,17 @@ rlt_status stage_slots(rlt_state *st, int n, const int32_t *slots, hipStream_t s
   return RLT_OK;
 }
 
+hipEvent_t pooled_event(rlt_state *st) {
+  hipEvent_t e = nullptr;
+  if (!st->event_pool.empty()) {
+    e = st->event_pool.back();
+    st->event_pool.pop_back();
+  } else if (hipEventCreate(&e) != hipSuccess) {
+    e = nullptr;
+  }
+  return e;
+}
+
 struct Prof {
   rlt_state *st;
   int cls;
@@ -351,15 +308,19 @@ struct Prof {
   hipEvent_t a = nullptr, b = nullptr;
   Prof(rlt_state *st_, int cls_, hipStream_t s_)
       : st(st_), cls(cls_), s(s_),
-        on(st_->prof_class == cls_ && (int)st_->prof.size() < st_->prof_max) {
-    if (on && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess)
-      (void)hipEventRecord(a, s);
-    else on = false;
+        on(((st_->prof_mask >> cls_) & 1) && (int)st_->prof.size() < st_->prof_max &&
+           st_->step_counter % st_->prof_stride == 0) {
+    if (on) {
+      a = pooled_event(st);
+      b = pooled_event(st);
+      on = a && b;
+    }
+    if (on) (void)hipEventRecord(a, s);
   }
   void done(double bytes) {
     if (!on) return;
     (void)hipEventRecord(b, s);
-    st->prof.push_back({a, b, bytes});
+    st->prof.push_back({a, b, bytes, cls});
     on = false;
   }
 };
@@ -373,79 +334,50 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
   const rlt_config &c = m->cfg;
   const int d = c.d_model, H = c.n_heads, dh = c.head_dim, W = c.window, L = c.n_layers;
   const int F = c.d_ffn, B = st->B, es = m->esize;
-  const int ch = m->chunk;
   hipError_t err;
 
-  // host mirror: positions of this step and attention work counts
-  int items_swa = 0, items_mem = 0;
+  // host mirror: algorithmic bytes of the two attentions (for profiling)
   double swa_len = 0, mem_len = 0;
   for (int i = 0; i < n; ++i) {
-    const int slot = identity ? i : host_slots[i];
-    const int t = st->host_pos[slot] + 1;
-    items_swa += cdiv(std::min(t, W), ch);
-    items_mem += cdiv(t, ch);
+    const int t = st->host_pos[identity ? i : host_slots[i]] + 1;
     swa_len += std::min(t, W);
     mem_len += t;
-  }
-
-  {
-    SetupArgs sa;
-    sa.slots = identity ? nullptr : st->slots_dev;
-    sa.n = n;
-    sa.pos = st->pos;
-    sa.rows_t = st->rows_t;
-    sa.rows_slot = st->rows_slot;
-    sa.W = W;
-    sa.ch = ch;
-    sa.items_swa = st->items_swa;
-    sa.items_mem = st->items_mem;
-    sa.n_items_swa = st->n_items;
-    sa.n_items_mem = st->n_items + 1;
-    sa.start_swa = st->start_swa;
-    sa.start_mem = st->start_mem;
-    Prof p(st, RLT_K_SETUP, s);
-    if ((err = launch_setup(sa, s)) != hipSuccess) return hip_fail(err, "setup launch");
-    p.done(0);
   }
 
   const ColPlan cp = col_plan(n);
   GemmArgs base;
   memset(&base, 0, sizeof base);
   base.n_rows = n;
-  base.x = st->x;
-  base.ld_x = d;
-  base.xio = st->x;
-  base.sumsq = st->sumsq;
-  base.sumsq_out = st->sumsq;
-  base.n_parts = cdiv(d, kRowsPerBlock);
-  base.part_ld = B;
-  base.eps = c.rms_eps;
+  base.slots = identity ? nullptr : st->slots_dev;
+  base.pos = st->pos;
   base.s_state = st->s;
   base.d = d;
-  base.rows_slot = st->rows_slot;
-  base.rows_t = st->rows_t;
+  base.sumsq = st->sumsq;
+  base.n_parts = cdiv(d, 16);
+  base.part_ld = B;
+  base.eps = c.rms_eps;
+  base.x = st->x;
+  base.xg = st->xg;
+  base.sumsq_out = st->sumsq;
   base.H = H;
   base.dh = dh;
   base.W = W;
-  base.ws = st->ws;
-  base.counters = st->gemm_cnt;
 
   auto gemm = [&](const GemmPlan &g, const PackedMat &w, int act, int epi, GemmArgs a,
-                  const char *what, double act_bytes_in, double out_bytes) -> rlt_status {
+                  const char *what, double act_bytes, double out_bytes) -> rlt_status {
     a.wp = w.p;
     a.N = g.N;
     a.K = g.K;
     a.KT = g.KT;
-    a.ks_per_split = g.ks_per_split;
-    a.splits = g.splits;
     Prof p(st, RLT_K_GEMM, s);
-    hipError_t e2 = launch_gemm_grid(c.dtype, cp.ncb, act, epi, a, g.n_blocks, g.splits,
-                                     cp.groups, s);
+    const hipError_t e2 = launch_gemm(c.dtype, cp.ncb, act, epi, a, g.tiles, cp.groups, g.parts, s);
     if (e2 != hipSuccess) return hip_fail(e2, what);
-    p.done((double)g.N * g.K * es + act_bytes_in + out_bytes);
+    p.done((double)g.N * g.K * es + act_bytes + out_bytes);
     return RLT_OK;
   };
   rlt_status rs;
+  const double row_in = (double)n * d * es;         // a normed / plain [n][d] activation
+  const double resid_out = (double)n * d * (8 + es); // x read + write, x*gamma out
 
   // gated merge: x = g*e + (1-g)*s, g = sigmoid(W_g [e ; s] + b_g)
   {
@@ -453,37 +385,38 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     a.act = e;
     a.ld_act = ld_e;
     a.bias = m->bg;
+    a.gamma_next = m->g1;
     if ((rs = gemm(m->p_merge, m->wg, ACT_MERGE, EPI_MERGE, a, "merge gemm",
-                   (double)n * d * (es + 4), (double)n * d * 4)) != RLT_OK)
+                   (double)n * d * (es + 4), (double)n * d * (4 + es))) != RLT_OK)
       return rs;
   }
 
   const size_t ring_layer = (size_t)B * H * W * dh * es;
   AttnArgs at;
   memset(&at, 0, sizeof at);
-  at.rows_t = st->rows_t;
-  at.rows_slot = st->rows_slot;
-  at.part = st->attn_part;
-  at.counters = st->attn_cnt;
+  at.slots = base.slots;
+  at.pos = st->pos;
   at.H = H;
   at.d = d;
-  at.ch = ch;
+  at.ch = m->chunk;
   at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
 
   for (int l = 0; l < L; ++l) {
-    // (1) RMSNorm + Q,K,V; k,v appended to the window cache at entry (t-1) mod W
+    const bool last = l == L - 1;
+    // (1) Q,K,V of RMSNorm(x; g1); k,v go to window entry (t-1) mod W
     {
       GemmArgs a = base;
-      a.gamma = m->g1 + (size_t)l * d;
+      a.act = st->xg;
+      a.ld_act = d;
       a.out = st->qbuf;
       a.ld_out = d;
       a.ring_k = st->ring_k + l * ring_layer;
       a.ring_v = st->ring_v + l * ring_layer;
-      if ((rs = gemm(m->p_qkv, m->wqkv[l], ACT_NORM, EPI_QKV, a, "qkv gemm", (double)n * d * 4,
+      if ((rs = gemm(m->p_qkv, m->wqkv[l], ACT_PLAIN, EPI_QKV, a, "qkv gemm", row_in,
                      (double)n * 3 * d * es)) != RLT_OK)
         return rs;
     }
-    // (2) sliding-window self-attention over ring entries 0..min(t,W)-1
+    // (2) sliding-window self-attention over window entries 0..min(t,W)-1
     {
       AttnArgs a = at;
       a.q = st->qbuf;
@@ -494,11 +427,8 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
       a.s_head = (int64_t)W * dh;
       a.s_pos = dh;
       a.len_cap = W;
-      a.items = st->items_swa;
-      a.n_items = st->n_items;
-      a.row_item_start = st->start_swa;
       Prof p(st, RLT_K_SWA, s);
-      if ((err = launch_attn(c.dtype, dh, a, items_swa, s)) != hipSuccess)
+      if ((err = launch_attn(c.dtype, dh, a, n, s)) != hipSuccess)
         return hip_fail(err, "window attention launch");
       p.done(swa_len * 2.0 * d * es + 2.0 * n * d * es);
     }
@@ -507,17 +437,19 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
       GemmArgs a = base;
       a.act = st->obuf;
       a.ld_act = d;
-      if ((rs = gemm(m->p_o, m->wo[l], ACT_PLAIN, EPI_RESID, a, "o gemm",
-                     (double)n * d * (es + 4), (double)n * d * 4)) != RLT_OK)
+      a.gamma_next = m->g2 + (size_t)l * d;
+      if ((rs = gemm(m->p_o, m->wo[l], ACT_PLAIN, EPI_RESID, a, "o gemm", row_in, resid_out)) !=
+          RLT_OK)
         return rs;
     }
-    // (4) RMSNorm + cross-attention query
+    // (4) cross-attention query of RMSNorm(x; g2)
     {
       GemmArgs a = base;
-      a.gamma = m->g2 + (size_t)l * d;
+      a.act = st->xg;
+      a.ld_act = d;
       a.out = st->qbuf;
       a.ld_out = d;
-      if ((rs = gemm(m->p_o, m->wqc[l], ACT_NORM, EPI_STORE, a, "qc gemm", (double)n * d * 4,
+      if ((rs = gemm(m->p_o, m->wqc[l], ACT_PLAIN, EPI_STORE, a, "qc gemm", row_in,
                      (double)n * d * es)) != RLT_OK)
         return rs;
     }
@@ -533,11 +465,8 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
       a.s_head = mem->stride_head;
       a.s_pos = mem->stride_pos;
       a.len_cap = 0x7fffffff;
-      a.items = st->items_mem;
-      a.n_items = st->n_items + 1;
-      a.row_item_start = st->start_mem;
       Prof p(st, RLT_K_CROSS, s);
-      if ((err = launch_attn(c.dtype, dh, a, items_mem, s)) != hipSuccess)
+      if ((err = launch_attn(c.dtype, dh, a, n, s)) != hipSuccess)
         return hip_fail(err, "cross attention launch");
       p.done(mem_len * 2.0 * d * es + 2.0 * n * d * es);
     }
@@ -546,17 +475,19 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
       GemmArgs a = base;
       a.act = st->obuf;
       a.ld_act = d;
-      if ((rs = gemm(m->p_o, m->woc[l], ACT_PLAIN, EPI_RESID, a, "oc gemm",
-                     (double)n * d * (es + 4), (double)n * d * 4)) != RLT_OK)
+      a.gamma_next = m->g3 + (size_t)l * d;
+      if ((rs = gemm(m->p_o, m->woc[l], ACT_PLAIN, EPI_RESID, a, "oc gemm", row_in, resid_out)) !=
+          RLT_OK)
         return rs;
     }
-    // (7) RMSNorm + FFN up + GELU
+    // (7) GELU(W_1 RMSNorm(x; g3))
     {
       GemmArgs a = base;
-      a.gamma = m->g3 + (size_t)l * d;
+      a.act = st->xg;
+      a.ld_act = d;
       a.out = st->hbuf;
       a.ld_out = F;
-      if ((rs = gemm(m->p_ffn1, m->w1[l], ACT_NORM, EPI_GELU, a, "ffn1 gemm", (double)n * d * 4,
+      if ((rs = gemm(m->p_ffn1, m->w1[l], ACT_PLAIN, EPI_GELU, a, "ffn1 gemm", row_in,
                      (double)n * F * es)) != RLT_OK)
         return rs;
     }
@@ -565,9 +496,13 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
       GemmArgs a = base;
       a.act = st->hbuf;
       a.ld_act = F;
-      if (l == L - 1) a.s_out = st->s;
+      a.gamma_next = last ? m->go : m->g1 + (size_t)(l + 1) * d;
+      if (last) {
+        a.s_out = st->s;
+        a.advance_pos = logits ? 0 : 1;
+      }
       if ((rs = gemm(m->p_ffn2, m->w2[l], ACT_PLAIN, EPI_RESID, a, "ffn2 gemm",
-                     (double)n * F * es + (double)n * d * 4, (double)n * d * 4)) != RLT_OK)
+                     (double)n * F * es, resid_out)) != RLT_OK)
         return rs;
     }
   }
@@ -575,15 +510,18 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
   // head: logits = W_o RMSNorm(s_t; g_o)
   if (logits) {
     GemmArgs a = base;
-    a.gamma = m->go;
+    a.act = st->xg;
+    a.ld_act = d;
     a.out = logits;
     a.ld_out = ld_logits;
-    if ((rs = gemm(m->p_head, m->wout, ACT_NORM, EPI_LOGITS, a, "head gemm", (double)n * d * 4,
+    a.advance_pos = 1;
+    if ((rs = gemm(m->p_head, m->wout, ACT_PLAIN, EPI_LOGITS, a, "head gemm", row_in,
                    (double)n * c.vocab * 4)) != RLT_OK)
       return rs;
   }
 
   for (int i = 0; i < n; ++i) st->host_pos[identity ? i : host_slots[i]] += 1;
+  st->step_counter += 1;
   return RLT_OK;
 }
 
@@ -722,7 +660,7 @@ size_t rlt_state_bytes(const rlt_config *cfg, int32_t batch, int32_t max_tokens)
   if (check_config(cfg) != RLT_OK || batch < 1 || max_tokens < 1) return 0;
   rlt_state st;
   st.cfg = *cfg;
-  return state_layout(nullptr, *cfg, &st, nullptr, batch, max_tokens);
+  return state_layout(*cfg, &st, nullptr, batch);
 }
 
 rlt_status rlt_state_init(const rlt_model *m, int32_t batch, int32_t max_tokens, void *dev_buf,
@@ -745,13 +683,11 @@ rlt_status rlt_state_init(const rlt_model *m, int32_t batch, int32_t max_tokens,
   st->B = batch;
   st->max_tokens = max_tokens;
   st->bytes = bytes;
-  state_layout(m, m->cfg, st, dev_buf, batch, max_tokens);
+  state_layout(m->cfg, st, dev_buf, batch);
   st->host_pos.assign(batch, 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_state_init(st->s, st->pos, m->s_star, batch, m->cfg.d_model, nullptr,
                                    batch, s);
-  if (e == hipSuccess) e = launch_zero(st->attn_cnt, (size_t)batch * m->cfg.n_heads * 4, s);
-  if (e == hipSuccess) e = launch_zero(st->gemm_cnt, std::max<size_t>(st->gemm_cnt_n, 1) * 4, s);
   if (e != hipSuccess) {
     delete st;
     return hip_fail(e, "state init");
@@ -766,6 +702,7 @@ void rlt_state_destroy(rlt_state *st) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
   }
+  for (hipEvent_t e : st->event_pool) (void)hipEventDestroy(e);
   delete st;
 }
 
@@ -953,21 +890,32 @@ rlt_status rlt_state_import(const rlt_model *m, rlt_state *st, int32_t n, const 
   return ok();
 }
 
-rlt_status rlt_profile_begin(rlt_state *st, int32_t kclass, int32_t max_launches) {
+rlt_status rlt_profile_begin(rlt_state *st, int32_t class_mask, int32_t max_launches,
+                             int32_t step_stride) {
   if (!st) return fail(RLT_ERR_INVALID_ARG, "state is NULL");
-  if (kclass < -1 || kclass >= RLT_K_NCLASSES) return fail(RLT_ERR_INVALID_ARG, "bad kernel class");
+  if (class_mask < 0 || class_mask >= (1 << RLT_K_NCLASSES))
+    return fail(RLT_ERR_INVALID_ARG, "bad kernel class mask");
   if (max_launches < 0) return fail(RLT_ERR_INVALID_ARG, "max_launches < 0");
-  st->prof_class = kclass;
+  if (step_stride < 1) return fail(RLT_ERR_INVALID_ARG, "step_stride < 1");
+  st->prof_mask = class_mask;
   st->prof_max = max_launches;
+  st->prof_stride = step_stride;
+  st->step_counter = 0;
   return ok();
 }
 
-rlt_status rlt_profile_collect(rlt_state *st, double *total_ms, int32_t *launches,
+rlt_status rlt_profile_collect(rlt_state *st, int32_t kclass, double *total_ms, int32_t *launches,
                                double *bytes_moved) {
   if (!st) return fail(RLT_ERR_INVALID_ARG, "state is NULL");
+  if (kclass < 0 || kclass >= RLT_K_NCLASSES) return fail(RLT_ERR_INVALID_ARG, "bad kernel class");
   double tot = 0, bytes = 0;
   int cnt = 0;
+  std::vector<ProfRec> keep;
   for (ProfRec &r : st->prof) {
+    if (r.cls != kclass) {
+      keep.push_back(r);
+      continue;
+    }
     float ms = 0.f;
     hipError_t e = hipEventSynchronize(r.b);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
@@ -975,10 +923,10 @@ rlt_status rlt_profile_collect(rlt_state *st, double *total_ms, int32_t *launche
     tot += ms;
     bytes += r.bytes;
     ++cnt;
-    (void)hipEventDestroy(r.a);
-    (void)hipEventDestroy(r.b);
+    st->event_pool.push_back(r.a);
+    st->event_pool.push_back(r.b);
   }
-  st->prof.clear();
+  st->prof.swap(keep);
   if (total_ms) *total_ms = tot;
   if (launches) *launches = cnt;
   if (bytes_moved) *bytes_moved = bytes;

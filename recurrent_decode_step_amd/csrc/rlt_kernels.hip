@@ -127,206 +127,216 @@ __global__ void k_pack(const T *__restrict__ src, int rows, int K, int64_t ld, i
 }
 
 // ---------------------------------------------------------------- GEMM
-// y[i][n] = sum_k W[n][k] act[i][k] for the n_rows batch rows, with fused
-// activation prologue and epilogue.  Workgroup = 4 wavefronts = 64 weight rows
-// (wave w: 16-row tile 4*blockIdx.x + w) x COLS batch rows (blockIdx.z picks the
-// column group) x one split of the k-steps (blockIdx.y).  The batch activation
-// of a k sub-chunk is staged in LDS once and shared by the 4 wavefronts; the
-// weights stream from HBM exactly once per launch.  Splits are summed by the
-// last-arriving workgroup of each row block in split order, so the result does
-// not depend on scheduling.
+// y[i][n] = sum_k W[n][k] a[i][k] for the batch rows i, fused epilogues.
+//
+// One workgroup per 16-row tile of W and per group of up to 64 batch rows.
+// K is cut into NP consecutive parts (NP depends on K only); wavefront w of the
+// workgroup runs part w as one MFMA chain in k order, and the NP partial tiles
+// are added in part order through LDS.  No workgroup ever waits for another,
+// and a row's result does not depend on how many rows share the launch.
+// Weights stream from HBM once per column group; activations (a few hundred
+// KiB) come from L2.
 template <typename T, int ACT>
-__device__ __forceinline__ u32x4 load_act(const GemmArgs &a, int i, bool valid, int k,
-                                          float rinv) {
+__device__ __forceinline__ u32x4 load_b(const GemmArgs &a, int i, int slot, int k) {
   constexpr int EPL = Num<T>::EPL;
-  if (!valid || k >= a.K) return u32x4{0u, 0u, 0u, 0u};
-  if constexpr (ACT == ACT_PLAIN) {
-    return *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.act) + (size_t)i * a.ld_act + k);
-  } else if constexpr (ACT == ACT_NORM) {
-    // RMSNorm: (x * rinv) * gamma, rounded to the storage type
-    const float *xp = a.x + (size_t)i * a.ld_x + k;
-    float v[EPL];
+  if constexpr (ACT == ACT_MERGE) {
+    // gate input [e_t ; s_{t-1}]: s is fp32 state, rounded to the storage type here
+    if (k >= a.d) {
+      const float *sp = a.s_state + (size_t)slot * a.d + (k - a.d);
+      float v[EPL];
 #pragma unroll
-    for (int j = 0; j < EPL; j += 4) {
-      const f32x4 xv = *reinterpret_cast<const f32x4 *>(xp + j);
-      const f32x4 gv = *reinterpret_cast<const f32x4 *>(a.gamma + k + j);
-      v[j + 0] = (xv.x * rinv) * gv.x;
-      v[j + 1] = (xv.y * rinv) * gv.y;
-      v[j + 2] = (xv.z * rinv) * gv.z;
-      v[j + 3] = (xv.w * rinv) * gv.w;
+      for (int j = 0; j < EPL; j += 4) {
+        const f32x4 sv = *reinterpret_cast<const f32x4 *>(sp + j);
+        v[j] = sv.x; v[j + 1] = sv.y; v[j + 2] = sv.z; v[j + 3] = sv.w;
+      }
+      return Num<T>::pack(v);
     }
-    return Num<T>::pack(v);
-  } else {
-    // gate input [e_t ; s_{t-1}] (s rounded to the storage type)
-    if (k < a.d)
-      return *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.act) + (size_t)i * a.ld_act + k);
-    const float *sp = a.s_state + (size_t)a.rows_slot[i] * a.d + (k - a.d);
-    float v[EPL];
-#pragma unroll
-    for (int j = 0; j < EPL; j += 4) {
-      const f32x4 sv = *reinterpret_cast<const f32x4 *>(sp + j);
-      v[j + 0] = sv.x; v[j + 1] = sv.y; v[j + 2] = sv.z; v[j + 3] = sv.w;
-    }
-    return Num<T>::pack(v);
   }
+  return *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.act) + (size_t)i * a.ld_act + k);
 }
 
-template <typename T, int NCB, int ACT, int EPI>
-__global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs a) {
+__device__ __forceinline__ int slot_of(const GemmArgs &a, int i) { return a.slots ? a.slots[i] : i; }
+
+template <typename T, int NCB, int ACT, int EPI, int MAXNW>
+__global__ __launch_bounds__(MAXNW * 64) void k_gemm(const GemmArgs a) {
   constexpr int EPL = Num<T>::EPL;
   constexpr int KSTEP = 4 * EPL;
-  constexpr int KCS = (NCB <= 4) ? 8 : 4;          // k-steps per staged sub-chunk
-  constexpr int KC = KCS * KSTEP;                  // elements per sub-chunk
-  constexpr int LDS_LD = KC + EPL;                 // padded LDS row
   constexpr int COLS = NCB * 16;
-  __shared__ __attribute__((aligned(16))) T s_act[COLS * LDS_LD];
+  // weight fragments in flight per wavefront, activation fragments prefetched;
+  // 16-wavefront workgroups have a quarter of the registers per lane
+  constexpr int WB = MAXNW <= 4 ? 16 : 8;
+  constexpr int PD = (MAXNW <= 4 && NCB <= 2) ? 4 : 2;
+  constexpr bool SCALED = EPI == EPI_QKV || EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_LOGITS;
+  extern __shared__ f32x4 s_acc[];                 // [parts][NCB][64] partial tiles
+  __shared__ float s_grp[8][COLS];
   __shared__ float s_rinv[COLS];
-  __shared__ float s_red[4][COLS];
-  __shared__ int s_flag;
 
+  const int NW = blockDim.x >> 6;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nb = blockIdx.x, split = blockIdx.y, cg = blockIdx.z;
-  const int col0 = cg * COLS;
+  const int tile = blockIdx.x;
+  const int col0 = blockIdx.y * COLS;
   const int ncols = min(COLS, a.n_rows - col0);
-  const int tile = nb * 4 + wave;
-  const int ks0 = split * a.ks_per_split;
-  const int ks1 = min(a.KT, ks0 + a.ks_per_split);
+  const int ks0 = (wave * a.KT) / NW;
+  const int nks = ((wave + 1) * a.KT) / NW - ks0;
 
-  if constexpr (ACT == ACT_NORM) {
-    // 1 / rms of each batch row from the producer's per-row-block partial sums,
-    // summed in block order
-    for (int c = tid; c < COLS; c += kGemmThreads) {
-      float r = 0.f;
+  int rowi[NCB], slot[NCB];
+  bool okc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int c = cb * 16 + (lane & 15);
+    okc[cb] = c < ncols;
+    rowi[cb] = col0 + (okc[cb] ? c : 0);
+    slot[cb] = (ACT == ACT_MERGE) ? slot_of(a, rowi[cb]) : 0;
+  }
+  const int kl = (lane >> 4) * EPL;
+  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+
+  // first batch of weights and activations, before anything else
+  const u32x4 *wp = static_cast<const u32x4 *>(a.wp) + ((size_t)tile * a.KT + ks0) * 64 + lane;
+  // fragment arrays start at zero: their loads are guarded by runtime counts
+  u32x4 wf[WB];
+  u32x4 ab[PD][NCB];
+#pragma unroll
+  for (int j = 0; j < WB; ++j) wf[j] = zero;
+#pragma unroll
+  for (int p = 0; p < PD; ++p)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) ab[p][cb] = zero;
+  const int nb0 = min(WB, nks);
+#pragma unroll
+  for (int j = 0; j < WB; ++j)
+    if (j < nb0) wf[j] = __builtin_nontemporal_load(wp + (size_t)j * 64);
+#pragma unroll
+  for (int p = 0; p < PD; ++p)
+    if (p < nb0) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        ab[p][cb] = okc[cb] ? load_b<T, ACT>(a, rowi[cb], slot[cb], (ks0 + p) * KSTEP + kl) : zero;
+    }
+
+  // 1/rms of every batch row from the producer's per-tile partial sums:
+  // 8 groups of consecutive parts, each summed in order, then the groups in order.
+  if constexpr (SCALED) {
+    const int P = a.n_parts;
+    const int per = (P + 7) / 8;
+    for (int q = tid; q < COLS * 8; q += blockDim.x) {
+      const int c = q % COLS, g = q / COLS;
+      float ss = 0.f;
       if (c < ncols) {
-        float ss = 0.f;
-        for (int p = 0; p < a.n_parts; ++p) ss += a.sumsq[(size_t)p * a.part_ld + col0 + c];
-        r = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+        const float *src = a.sumsq + col0 + c;
+        const int p1 = min(P, (g + 1) * per);
+        for (int p = g * per; p < p1; p += 16) {
+          float v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) v[u] = (p + u < p1) ? src[(size_t)(p + u) * a.part_ld] : 0.f;
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            if (p + u < p1) ss += v[u];
+        }
       }
-      s_rinv[c] = r;
+      s_grp[g][c] = ss;
+    }
+    __syncthreads();
+    for (int c = tid; c < COLS; c += blockDim.x) {
+      float ss = s_grp[0][c];
+#pragma unroll
+      for (int g = 1; g < 8; ++g) ss += s_grp[g][c];
+      s_rinv[c] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
     }
   }
 
+  // this wavefront's part of K: one MFMA chain
   f32x4 acc[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const u32x4 *wp = static_cast<const u32x4 *>(a.wp) + (size_t)tile * a.KT * 64 + lane;
-
-  for (int kc = ks0; kc < ks1; kc += KCS) {
-    const int nks = min(KCS, ks1 - kc);
-    u32x4 wf[KCS];
+  for (int b0 = 0; b0 < nks; b0 += WB) {
+    const int nb = min(WB, nks - b0);
+    if (b0 > 0) {
 #pragma unroll
-    for (int j = 0; j < KCS; ++j)
-      if (j < nks) wf[j] = __builtin_nontemporal_load(wp + (size_t)(kc + j) * 64);
-    __syncthreads();
-    const int kbase = kc * KSTEP;
-    const int fpc = nks * 4;                       // 16-byte fragments per column
-    for (int f = tid; f < COLS * fpc; f += kGemmThreads) {
-      const int c = f / fpc;
-      const int kk = (f - c * fpc) * EPL;
-      const u32x4 v = load_act<T, ACT>(a, col0 + c, c < ncols, kbase + kk,
-                                       ACT == ACT_NORM ? s_rinv[c] : 0.f);
-      *reinterpret_cast<u32x4 *>(&s_act[c * LDS_LD + kk]) = v;
+      for (int j = 0; j < WB; ++j)
+        if (j < nb) wf[j] = __builtin_nontemporal_load(wp + (size_t)(b0 + j) * 64);
+#pragma unroll
+      for (int p = 0; p < PD; ++p)
+        if (p < nb) {
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            ab[p][cb] = okc[cb] ? load_b<T, ACT>(a, rowi[cb], slot[cb], (ks0 + b0 + p) * KSTEP + kl)
+                                : zero;
+        }
     }
-    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < KCS; ++j) {
-      if (j < nks) {
+    for (int j = 0; j < WB; ++j) {
+      if (j < nb) {
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const u32x4 b = *reinterpret_cast<const u32x4 *>(
-              &s_act[(cb * 16 + (lane & 15)) * LDS_LD + j * KSTEP + (lane >> 4) * EPL]);
-          acc[cb] = mma_step(wf[j], b, acc[cb], T());
+        for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma_step(wf[j], ab[j % PD][cb], acc[cb], T());
+        if (j + PD < nb) {
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            ab[j % PD][cb] = okc[cb] ? load_b<T, ACT>(a, rowi[cb], slot[cb],
+                                                       (ks0 + b0 + j + PD) * KSTEP + kl)
+                                     : zero;
         }
       }
     }
   }
 
-  if (a.splits > 1) {
-    const size_t nbz = (size_t)cg * gridDim.x + nb;
-    const size_t per_split = (size_t)gridDim.x * gridDim.z * 4 * NCB * 64;
-    f32x4 *ws = reinterpret_cast<f32x4 *>(a.ws) + (size_t)split * per_split +
-                ((nbz * 4 + wave) * NCB) * 64 + lane;
+  // partial tiles summed in part order
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) ws[cb * 64] = acc[cb];
-    __syncthreads();
-    if (tid == 0) {
-      __threadfence();
-      const int prev = atomicAdd(&a.counters[nbz], 1);
-      s_flag = (prev == a.splits - 1);
-    }
-    __syncthreads();
-    if (!s_flag) return;
-    __threadfence();
-    const f32x4 *rd = reinterpret_cast<const f32x4 *>(a.ws) + ((nbz * 4 + wave) * NCB) * 64 + lane;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < a.splits; ++sp) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) acc[cb] += rd[(size_t)sp * per_split + cb * 64];
-    }
-    if (tid == 0) a.counters[nbz] = 0;
-  }
+  for (int cb = 0; cb < NCB; ++cb) s_acc[(wave * NCB + cb) * 64 + lane] = acc[cb];
+  __syncthreads();
 
   // ---- epilogue: lane holds features rbase..rbase+3 of batch column cb*16 + cl
   const int rbase = tile * 16 + (lane >> 4) * 4;
   const int cl = lane & 15;
-  if constexpr (EPI == EPI_RESID || EPI == EPI_MERGE) {
-    float ssq[NCB];
+  for (int cb = wave; cb < NCB; cb += NW) {
+    f32x4 yv = s_acc[cb * 64 + lane];
+    for (int w = 1; w < NW; ++w) yv += s_acc[(w * NCB + cb) * 64 + lane];
+    const int c = cb * 16 + cl;
+    const bool live = c < ncols && rbase < a.N;
+    const int i = col0 + c;
+    float y[4] = {yv[0], yv[1], yv[2], yv[3]};
+    if constexpr (SCALED) {
+      const float r = s_rinv[c];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const int c = cb * 16 + cl;
+      for (int q = 0; q < 4; ++q) y[q] *= r;
+    }
+    if constexpr (EPI == EPI_RESID || EPI == EPI_MERGE) {
       float ss = 0.f;
-      if (c < ncols && rbase < a.N) {
-        const int i = col0 + c;
-        float *xp = a.xio + (size_t)i * a.ld_x + rbase;
+      if (live) {
+        const int sl = slot_of(a, i);
+        float *xp = a.x + (size_t)i * a.d + rbase;
         float xv[4];
         if constexpr (EPI == EPI_RESID) {
           const f32x4 old = *reinterpret_cast<const f32x4 *>(xp);
-          xv[0] = old.x + acc[cb][0];
-          xv[1] = old.y + acc[cb][1];
-          xv[2] = old.z + acc[cb][2];
-          xv[3] = old.w + acc[cb][3];
+          xv[0] = old.x + y[0]; xv[1] = old.y + y[1]; xv[2] = old.z + y[2]; xv[3] = old.w + y[3];
         } else {
-          const int slot = a.rows_slot[i];
-          const float *sp = a.s_state + (size_t)slot * a.d + rbase;
+          // x = g * e + (1 - g) * s, g = sigmoid(W_g [e ; s] + b_g)
+          const float *sp = a.s_state + (size_t)sl * a.d + rbase;
           const T *ep = static_cast<const T *>(a.act) + (size_t)i * a.ld_act + rbase;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float z = acc[cb][r] + a.bias[rbase + r];
+          for (int q = 0; q < 4; ++q) {
+            const float z = y[q] + a.bias[rbase + q];
             const float g = 1.0f / (1.0f + __expf(-z));
             float ev;
-            if constexpr (sizeof(T) == 2) ev = bf2f(reinterpret_cast<const bf16_t *>(ep)[r]);
-            else ev = reinterpret_cast<const float *>(ep)[r];
-            xv[r] = g * ev + (1.0f - g) * sp[r];
+            if constexpr (sizeof(T) == 2) ev = bf2f(reinterpret_cast<const bf16_t *>(ep)[q]);
+            else ev = reinterpret_cast<const float *>(ep)[q];
+            xv[q] = g * ev + (1.0f - g) * sp[q];
           }
         }
         *reinterpret_cast<f32x4 *>(xp) = f32x4{xv[0], xv[1], xv[2], xv[3]};
-        if (a.s_out) {
-          float *so = a.s_out + (size_t)a.rows_slot[i] * a.d + rbase;
-          *reinterpret_cast<f32x4 *>(so) = f32x4{xv[0], xv[1], xv[2], xv[3]};
-        }
+        if (a.s_out)
+          *reinterpret_cast<f32x4 *>(a.s_out + (size_t)sl * a.d + rbase) =
+              f32x4{xv[0], xv[1], xv[2], xv[3]};
+        // input of the next RMSNorm'd GEMM: x * gamma_next in the storage type
+        const f32x4 gn = *reinterpret_cast<const f32x4 *>(a.gamma_next + rbase);
+        const float xg[4] = {xv[0] * gn.x, xv[1] * gn.y, xv[2] * gn.z, xv[3] * gn.w};
+        Num<T>::store4(static_cast<T *>(a.xg) + (size_t)i * a.d + rbase, xg);
         ss = ((xv[0] * xv[0] + xv[1] * xv[1]) + xv[2] * xv[2]) + xv[3] * xv[3];
       }
       ss += __shfl_xor(ss, 16);
       ss += __shfl_xor(ss, 32);
-      ssq[cb] = ss;
-    }
-    if (lane < 16) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) s_red[wave][cb * 16 + lane] = ssq[cb];
-    }
-    __syncthreads();
-    for (int c = tid; c < ncols; c += kGemmThreads)
-      a.sumsq_out[(size_t)nb * a.part_ld + col0 + c] =
-          ((s_red[0][c] + s_red[1][c]) + s_red[2][c]) + s_red[3][c];
-  } else {
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const int c = cb * 16 + cl;
-      if (c >= ncols || rbase >= a.N) continue;
-      const int i = col0 + c;
-      float y[4] = {acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]};
+      if (lane < 16 && c < ncols) a.sumsq_out[(size_t)tile * a.part_ld + i] = ss;
+    } else if (live) {
       if constexpr (EPI == EPI_QKV) {
         const int d = a.d;
         const int which = rbase / d;
@@ -335,67 +345,128 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm(const GemmArgs a) {
           Num<T>::store4(static_cast<T *>(a.out) + (size_t)i * a.ld_out + f, y);
         } else {
           const int h = f / a.dh, cc = f - h * a.dh;
-          const int slot = a.rows_slot[i];
-          const int w = (a.rows_t[i] - 1) % a.W;
+          const int sl = slot_of(a, i);
+          const int w = a.pos[sl] % a.W;          // entry of position t = pos + 1
           T *ring = static_cast<T *>(which == 1 ? a.ring_k : a.ring_v);
-          Num<T>::store4(ring + (((size_t)slot * a.H + h) * a.W + w) * a.dh + cc, y);
+          Num<T>::store4(ring + (((size_t)sl * a.H + h) * a.W + w) * a.dh + cc, y);
         }
       } else if constexpr (EPI == EPI_STORE) {
         Num<T>::store4(static_cast<T *>(a.out) + (size_t)i * a.ld_out + rbase, y);
       } else if constexpr (EPI == EPI_GELU) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = gelu_erf(y[r]);
+        for (int q = 0; q < 4; ++q) y[q] = gelu_erf(y[q]);
         Num<T>::store4(static_cast<T *>(a.out) + (size_t)i * a.ld_out + rbase, y);
       } else if constexpr (EPI == EPI_LOGITS) {
         float *lp = static_cast<float *>(a.out) + (size_t)i * a.ld_out + rbase;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (rbase + r < a.N) lp[r] = y[r];
+        for (int q = 0; q < 4; ++q)
+          if (rbase + q < a.N) lp[q] = y[q];
       }
     }
+  }
+
+  // the last kernel of a step advances the positions (no reader of pos runs in it)
+  if (a.advance_pos && blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int i = tid; i < a.n_rows; i += blockDim.x) a.pos[slot_of(a, i)] += 1;
   }
 }
 
 // ---------------------------------------------------------------- attention
-// One workgroup per (work item = (batch row, chunk of positions), head).
-// Positions of the chunk are spread over lane groups: LPR lanes hold one
-// position's dh values (16 bytes each).  K and V of the whole chunk are loaded
-// up front (U fragments per lane), scores go through LDS, softmax is taken
-// over the chunk in base 2, and the chunk's (max, sum, weighted values) are
-// either final (one chunk) or combined by the last-arriving workgroup of the
-// (row, head) in chunk order.
+// One workgroup per (batch row, head): softmax(q . K / sqrt(dh)) V over the
+// row's positions (the window ring entries 0..min(t,W)-1, or memory 1..t).
+// LPR lanes hold one position's dh values (16 bytes each); positions of a
+// chunk are interleaved over the 4 wavefronts, and every wavefront keeps its
+// own online softmax (running max, sum, weighted values) in base 2 with no
+// barrier until the end, where the 4 are combined in wavefront order.  K and V
+// of the next chunk are loaded while the current one is processed.
 template <typename T, int DH>
 struct AttnShape {
   static constexpr int EPL = Num<T>::EPL;
   static constexpr int LPR = DH / EPL;             // lanes per position
   static constexpr int RPW = 64 / LPR;             // positions per wavefront load
   static constexpr int RPB = 4 * RPW;              // positions per workgroup load
-  static constexpr int U = 16;                     // loads in flight per lane and tensor
-  static constexpr int CHMAX = U * RPB;
+  static constexpr int U = (RPW >= 16) ? 4 : 8;    // loads per lane and tensor per chunk
+  static constexpr int CH = U * RPB;               // positions per chunk
 };
+
+template <typename T, int DH>
+__device__ __forceinline__ void attn_load(const T *kp, const T *vp, int64_t s_pos, int base, int len,
+                                          int ch, int my, u32x4 *kr, u32x4 *vr) {
+  using S = AttnShape<T, DH>;
+#pragma unroll
+  for (int u = 0; u < S::U; ++u) {
+    const int pc = u * S::RPB + my;
+    const int p = base + pc;
+    if (pc < ch && p < len) {
+      kr[u] = *reinterpret_cast<const u32x4 *>(kp + (size_t)p * s_pos);
+      vr[u] = *reinterpret_cast<const u32x4 *>(vp + (size_t)p * s_pos);
+    }
+  }
+}
+
+template <typename T, int DH>
+__device__ __forceinline__ void attn_chunk(const float *qf, const u32x4 *kr, const u32x4 *vr,
+                                           int base, int len, int ch, int my, float &m, float &l,
+                                           float *o) {
+  using S = AttnShape<T, DH>;
+  constexpr int EPL = S::EPL, LPR = S::LPR, U = S::U;
+  float sc[U];
+  float cmax = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float kf[EPL];
+    Num<T>::unpack(kr[u], kf);
+    float dsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dsum = fmaf(qf[e], kf[e], dsum);
+#pragma unroll
+    for (int w = LPR / 2; w >= 1; w >>= 1) dsum += __shfl_xor(dsum, w);
+    const int pc = u * S::RPB + my;
+    const bool in = pc < ch && base + pc < len;
+    sc[u] = in ? dsum : -INFINITY;
+    cmax = fmaxf(cmax, sc[u]);
+  }
+  cmax = wave_max(cmax);
+  const float mnew = fmaxf(m, cmax);
+  const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mnew);   // o, l are still 0 then
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] *= alpha;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool in = sc[u] != -INFINITY;            // positions past the end weigh 0
+    const float pj = in ? exp2f(sc[u] - mnew) : 0.f;
+    psum += pj;
+    if (in) {
+      float vf[EPL];
+      Num<T>::unpack(vr[u], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(pj, vf[e], o[e]);
+    }
+  }
+  // each position's weight is held by its LPR lanes: sum over position rows only
+#pragma unroll
+  for (int w = LPR; w < 64; w <<= 1) psum += __shfl_xor(psum, w);
+  l = l * alpha + psum;
+  m = mnew;
+}
 
 template <typename T, int DH>
 __global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
   using S = AttnShape<T, DH>;
-  constexpr int EPL = S::EPL, LPR = S::LPR, RPW = S::RPW, RPB = S::RPB, U = S::U;
-  __shared__ float s_p[S::CHMAX];
+  constexpr int EPL = S::EPL, LPR = S::LPR, RPW = S::RPW, U = S::U;
   __shared__ float s_o[4][DH];
-  __shared__ float s_w[4];
-  __shared__ int s_flag;
+  __shared__ float s_ml[4][2];
 
-  const int item = blockIdx.x, h = blockIdx.y;
-  if (item >= *a.n_items) return;
-  const int2 it = a.items[item];
-  const int i = it.x, c = it.y;
-  const int t = a.rows_t[i], slot = a.rows_slot[i];
+  const int i = blockIdx.x, h = blockIdx.y;
+  const int slot = a.slots ? a.slots[i] : i;
+  const int t = a.pos[slot] + 1;
   const int len = min(t, a.len_cap);
-  const int nch = (len + a.ch - 1) / a.ch;
-  const int p0 = c * a.ch;
-  const int np = min(a.ch, len - p0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sub = lane % LPR, row = lane / LPR;
+  const int my = wave * RPW + row;                 // this lane's position within a load group
 
-  const size_t off = (size_t)slot * a.s_seq + (size_t)h * a.s_head + (size_t)p0 * a.s_pos + sub * EPL;
+  const size_t off = (size_t)slot * a.s_seq + (size_t)h * a.s_head + sub * EPL;
   const T *kp = static_cast<const T *>(a.kb) + off;
   const T *vp = static_cast<const T *>(a.vb) + off;
 
@@ -403,160 +474,55 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
   Num<T>::unpack(*reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.q) + (size_t)i * a.d +
                                                   h * DH + sub * EPL),
                  qf);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qf[e] *= a.scale_log2;
 
-  u32x4 kr[U], vr[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int p = u * RPB + wave * RPW + row;
-    if (p < np) kr[u] = *reinterpret_cast<const u32x4 *>(kp + (size_t)p * a.s_pos);
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int p = u * RPB + wave * RPW + row;
-    if (p < np) vr[u] = *reinterpret_cast<const u32x4 *>(vp + (size_t)p * a.s_pos);
-  }
-
-  // scores (pre-scaled by log2(e)/sqrt(dh))
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int p = u * RPB + wave * RPW + row;
-    float kf[EPL];
-    Num<T>::unpack(kr[u], kf);
-    float dsum = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) dsum = fmaf(qf[e], kf[e], dsum);
-#pragma unroll
-    for (int o = LPR / 2; o >= 1; o >>= 1) dsum += __shfl_xor(dsum, o);
-    if (sub == 0 && p < np) s_p[p] = dsum * a.scale_log2;
-  }
-  __syncthreads();
-  float m = -INFINITY;
-  for (int j = tid; j < np; j += kAttnThreads) m = fmaxf(m, s_p[j]);
-  m = wave_max(m);
-  if (lane == 0) s_w[wave] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(s_w[0], s_w[1]), fmaxf(s_w[2], s_w[3]));
-  __syncthreads();
-  float l = 0.f;
-  for (int j = tid; j < np; j += kAttnThreads) {
-    const float e = exp2f(s_p[j] - m);
-    s_p[j] = e;
-    l += e;
-  }
-  l = wave_sum(l);
-  if (lane == 0) s_w[wave] = l;
-  __syncthreads();
-  l = ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
-
-  float o[EPL];
+  float m = -INFINITY, l = 0.f, o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  const int ch = a.ch;                             // positions per chunk (<= CH)
+  u32x4 ka[U], va[U], kb2[U], vb2[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int p = u * RPB + wave * RPW + row;
-    if (p < np) {
-      const float pj = s_p[p];
-      float vf[EPL];
-      Num<T>::unpack(vr[u], vf);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = fmaf(pj, vf[e], o[e]);
-    }
+    ka[u] = u32x4{0u, 0u, 0u, 0u}; va[u] = ka[u]; kb2[u] = ka[u]; vb2[u] = ka[u];
   }
+  attn_load<T, DH>(kp, vp, a.s_pos, 0, len, ch, my, ka, va);
+  for (int c0 = 0; c0 < len; c0 += 2 * ch) {
+    if (c0 + ch < len) attn_load<T, DH>(kp, vp, a.s_pos, c0 + ch, len, ch, my, kb2, vb2);
+    attn_chunk<T, DH>(qf, ka, va, c0, len, ch, my, m, l, o);
+    if (c0 + ch >= len) break;
+    if (c0 + 2 * ch < len) attn_load<T, DH>(kp, vp, a.s_pos, c0 + 2 * ch, len, ch, my, ka, va);
+    attn_chunk<T, DH>(qf, kb2, vb2, c0 + ch, len, ch, my, m, l, o);
+  }
+
+  // rows of the wavefront, then the 4 wavefronts in order
 #pragma unroll
-  for (int sh = LPR; sh < 64; sh <<= 1) {
+  for (int w = LPR; w < 64; w <<= 1) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], sh);
+    for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], w);
   }
   if (row == 0) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) s_o[wave][sub * EPL + e] = o[e];
   }
+  if (lane == 0) {
+    s_ml[wave][0] = m;
+    s_ml[wave][1] = l;
+  }
   __syncthreads();
-
+  float M = fmaxf(fmaxf(s_ml[0][0], s_ml[1][0]), fmaxf(s_ml[2][0], s_ml[3][0]));
+  float sc[4], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    sc[w] = exp2f(s_ml[w][0] - M);               // a wavefront with no positions has m = -inf
+    L += s_ml[w][1] * sc[w];
+  }
   T *outp = static_cast<T *>(a.out) + (size_t)i * a.d + h * DH;
-  if (nch == 1) {
-    for (int j = tid; j < DH; j += kAttnThreads) {
-      const float v = ((s_o[0][j] + s_o[1][j]) + s_o[2][j]) + s_o[3][j];
-      Num<T>::store1(outp + j, v / l);
-    }
-    return;
-  }
-  const size_t pstride = (size_t)a.H * (DH + 2);
-  float *part = a.part + (size_t)(a.row_item_start[i] + c) * pstride + (size_t)h * (DH + 2);
-  for (int j = tid; j < DH; j += kAttnThreads)
-    part[2 + j] = ((s_o[0][j] + s_o[1][j]) + s_o[2][j]) + s_o[3][j];
-  if (tid == 0) {
-    part[0] = m;
-    part[1] = l;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const int prev = atomicAdd(&a.counters[i * a.H + h], 1);
-    s_flag = (prev == nch - 1);
-  }
-  __syncthreads();
-  if (!s_flag) return;
-  __threadfence();
-  const float *base = a.part + (size_t)a.row_item_start[i] * pstride + (size_t)h * (DH + 2);
-  float M = -INFINITY;
-  for (int cc = 0; cc < nch; ++cc) M = fmaxf(M, base[cc * pstride]);
-  float L = 0.f;
-  for (int cc = 0; cc < nch; ++cc) L += base[cc * pstride + 1] * exp2f(base[cc * pstride] - M);
   for (int j = tid; j < DH; j += kAttnThreads) {
-    float acc = 0.f;
-    for (int cc = 0; cc < nch; ++cc)
-      acc += base[cc * pstride + 2 + j] * exp2f(base[cc * pstride] - M);
-    Num<T>::store1(outp + j, acc / L);
-  }
-  if (tid == 0) a.counters[i * a.H + h] = 0;
-}
-
-// ---------------------------------------------------------------- setup
-// Per step: t_i = pos[slot_i] + 1 for every listed row, the position advance,
-// and the attention work lists (row, chunk) with per-row start offsets.
-__global__ __launch_bounds__(256) void k_setup(const SetupArgs a) {
-  __shared__ int s_cs[256], s_cm[256];
-  const int tid = threadIdx.x;
-  const int per = (a.n + 255) / 256;
-  const int r0 = min(a.n, tid * per), r1 = min(a.n, r0 + per);
-  int cs = 0, cm = 0;
-  for (int r = r0; r < r1; ++r) {
-    const int slot = a.slots ? a.slots[r] : r;
-    const int t = a.pos[slot] + 1;
-    a.rows_t[r] = t;
-    a.rows_slot[r] = slot;
-    a.pos[slot] = t;
-    cs += (min(t, a.W) + a.ch - 1) / a.ch;
-    cm += (t + a.ch - 1) / a.ch;
-  }
-  s_cs[tid] = cs;
-  s_cm[tid] = cm;
-  __syncthreads();
-  if (tid == 0) {
-    int os = 0, om = 0;
-    for (int j = 0; j < 256; ++j) {
-      const int xs = s_cs[j], xm = s_cm[j];
-      s_cs[j] = os;
-      s_cm[j] = om;
-      os += xs;
-      om += xm;
-    }
-    *a.n_items_swa = os;
-    *a.n_items_mem = om;
-  }
-  __syncthreads();
-  int os = s_cs[tid], om = s_cm[tid];
-  for (int r = r0; r < r1; ++r) {
-    const int t = a.rows_t[r];
-    const int ns = (min(t, a.W) + a.ch - 1) / a.ch;
-    const int nm = (t + a.ch - 1) / a.ch;
-    a.start_swa[r] = os;
-    a.start_mem[r] = om;
-    for (int c = 0; c < ns; ++c) a.items_swa[os + c] = make_int2(r, c);
-    for (int c = 0; c < nm; ++c) a.items_mem[om + c] = make_int2(r, c);
-    os += ns;
-    om += nm;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v += s_o[w][j] * sc[w];
+    Num<T>::store1(outp + j, v / L);
   }
 }
 
@@ -594,16 +560,25 @@ __global__ void k_export(const SnapArgs a) {
   const int n_hist = min(pos, Wm1);
   char *rec = static_cast<char *>(a.snap) + (size_t)r * a.rec_bytes;
   if (lh == 0) {
+    // header, s, and every padding byte of the record (records are canonical bytes)
+    uint32_t *w32 = reinterpret_cast<uint32_t *>(rec);
+    for (size_t j = threadIdx.x; j < a.off_s / 4; j += blockDim.x) w32[j] = 0u;
+    __syncthreads();
     if (threadIdx.x == 0) {
-      uint32_t *hd = reinterpret_cast<uint32_t *>(rec);
-      hd[0] = 0x534C5452u; hd[1] = 1u;
+      w32[0] = 0x534C5452u; w32[1] = 1u;
       int32_t *hi = reinterpret_cast<int32_t *>(rec + 8);
       hi[0] = a.d; hi[1] = a.H; hi[2] = a.dh; hi[3] = a.L; hi[4] = a.W; hi[5] = a.dtype;
       hi[6] = pos; hi[7] = 0;
       *reinterpret_cast<uint64_t *>(rec + 40) = a.version;
     }
     float *sd = reinterpret_cast<float *>(rec + a.off_s);
-    for (int c = threadIdx.x; c < a.d; c += blockDim.x) sd[c] = a.s[(size_t)slot * a.d + c];
+    for (size_t c = threadIdx.x; c < (a.off_k - a.off_s) / 4; c += blockDim.x)
+      sd[c] = c < (size_t)a.d ? a.s[(size_t)slot * a.d + c] : 0.f;
+    const size_t hist = (size_t)a.L * a.H * Wm1 * a.dh * sizeof(T);
+    for (size_t j = hist + threadIdx.x; j < a.off_v - a.off_k; j += blockDim.x) {
+      rec[a.off_k + j] = 0;
+      rec[a.off_v + j] = 0;
+    }
   }
   if (Wm1 == 0) return;
   const int l = lh / a.H, h = lh - (lh / a.H) * a.H;
@@ -668,45 +643,47 @@ hipError_t launch_pack_tiles(const void *src, int rows, int K, int64_t ld, int t
 }
 
 template <typename T, int NCB>
-static hipError_t gemm_dispatch_epi(int act, int epi, const GemmArgs &a, dim3 grid, hipStream_t s) {
+static hipError_t gemm_dispatch_epi(int act, int epi, const GemmArgs &a, dim3 grid, int threads,
+                                    hipStream_t s) {
+  const size_t lds = (size_t)(threads / 64) * NCB * 1024;
 #define RLT_G(A, E)                                                         \
   if (act == A && epi == E) {                                               \
-    k_gemm<T, NCB, A, E><<<grid, kGemmThreads, 0, s>>>(a);                  \
+    if (threads <= 256) k_gemm<T, NCB, A, E, 4><<<grid, threads, lds, s>>>(a);           \
+    else k_gemm<T, NCB, A, E, kMaxParts><<<grid, threads, lds, s>>>(a);                  \
     return hipGetLastError();                                               \
   }
-  RLT_G(ACT_NORM, EPI_QKV)
+  RLT_G(ACT_PLAIN, EPI_QKV)
   RLT_G(ACT_PLAIN, EPI_RESID)
-  RLT_G(ACT_NORM, EPI_STORE)
-  RLT_G(ACT_NORM, EPI_GELU)
+  RLT_G(ACT_PLAIN, EPI_STORE)
+  RLT_G(ACT_PLAIN, EPI_GELU)
   RLT_G(ACT_MERGE, EPI_MERGE)
-  RLT_G(ACT_NORM, EPI_LOGITS)
+  RLT_G(ACT_PLAIN, EPI_LOGITS)
 #undef RLT_G
   return hipErrorInvalidValue;
 }
 
 template <typename T>
 static hipError_t gemm_dispatch(int ncb, int act, int epi, const GemmArgs &a, dim3 grid,
-                                hipStream_t s) {
+                                int threads, hipStream_t s) {
   switch (ncb) {
-    case 1: return gemm_dispatch_epi<T, 1>(act, epi, a, grid, s);
-    case 2: return gemm_dispatch_epi<T, 2>(act, epi, a, grid, s);
-    case 4: return gemm_dispatch_epi<T, 4>(act, epi, a, grid, s);
-    case 8: return gemm_dispatch_epi<T, 8>(act, epi, a, grid, s);
-    case 16: return gemm_dispatch_epi<T, 16>(act, epi, a, grid, s);
+    case 1: return gemm_dispatch_epi<T, 1>(act, epi, a, grid, threads, s);
+    case 2: return gemm_dispatch_epi<T, 2>(act, epi, a, grid, threads, s);
+    case 4: return gemm_dispatch_epi<T, 4>(act, epi, a, grid, threads, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_grid(int dtype, int ncb, int act, int epi, const GemmArgs &a, int n_blocks,
-                            int splits, int col_groups, hipStream_t s) {
-  const dim3 grid((unsigned)n_blocks, (unsigned)splits, (unsigned)col_groups);
-  if (dtype == RLT_DTYPE_BF16) return gemm_dispatch<bf16_t>(ncb, act, epi, a, grid, s);
-  return gemm_dispatch<float>(ncb, act, epi, a, grid, s);
+hipError_t launch_gemm(int dtype, int ncb, int act, int epi, const GemmArgs &a, int tiles,
+                       int col_groups, int parts, hipStream_t s) {
+  const dim3 grid((unsigned)tiles, (unsigned)col_groups);
+  if (parts < 1 || parts > kMaxParts) return hipErrorInvalidValue;
+  if (dtype == RLT_DTYPE_BF16) return gemm_dispatch<bf16_t>(ncb, act, epi, a, grid, parts * 64, s);
+  return gemm_dispatch<float>(ncb, act, epi, a, grid, parts * 64, s);
 }
 
 template <typename T>
-static hipError_t attn_dispatch(int dh, const AttnArgs &a, int n_items, hipStream_t s) {
-  const dim3 grid((unsigned)n_items, (unsigned)a.H);
+static hipError_t attn_dispatch(int dh, const AttnArgs &a, int n_rows, hipStream_t s) {
+  const dim3 grid((unsigned)n_rows, (unsigned)a.H);
   switch (dh) {
     case 16: k_attn<T, 16><<<grid, kAttnThreads, 0, s>>>(a); break;
     case 32: k_attn<T, 32><<<grid, kAttnThreads, 0, s>>>(a); break;
@@ -718,36 +695,31 @@ static hipError_t attn_dispatch(int dh, const AttnArgs &a, int n_items, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_items, hipStream_t s) {
-  if (n_items <= 0) return hipSuccess;
-  if (dtype == RLT_DTYPE_BF16) return attn_dispatch<bf16_t>(dh, a, n_items, s);
-  return attn_dispatch<float>(dh, a, n_items, s);
-}
-
 int attn_chunk_max(int dtype, int dh) {
   if (dtype == RLT_DTYPE_BF16) {
     switch (dh) {
-      case 16: return AttnShape<bf16_t, 16>::CHMAX;
-      case 32: return AttnShape<bf16_t, 32>::CHMAX;
-      case 64: return AttnShape<bf16_t, 64>::CHMAX;
-      case 128: return AttnShape<bf16_t, 128>::CHMAX;
-      case 256: return AttnShape<bf16_t, 256>::CHMAX;
+      case 16: return AttnShape<bf16_t, 16>::CH;
+      case 32: return AttnShape<bf16_t, 32>::CH;
+      case 64: return AttnShape<bf16_t, 64>::CH;
+      case 128: return AttnShape<bf16_t, 128>::CH;
+      case 256: return AttnShape<bf16_t, 256>::CH;
     }
   } else {
     switch (dh) {
-      case 16: return AttnShape<float, 16>::CHMAX;
-      case 32: return AttnShape<float, 32>::CHMAX;
-      case 64: return AttnShape<float, 64>::CHMAX;
-      case 128: return AttnShape<float, 128>::CHMAX;
-      case 256: return AttnShape<float, 256>::CHMAX;
+      case 16: return AttnShape<float, 16>::CH;
+      case 32: return AttnShape<float, 32>::CH;
+      case 64: return AttnShape<float, 64>::CH;
+      case 128: return AttnShape<float, 128>::CH;
+      case 256: return AttnShape<float, 256>::CH;
     }
   }
   return 0;
 }
 
-hipError_t launch_setup(const SetupArgs &a, hipStream_t s) {
-  k_setup<<<1, 256, 0, s>>>(a);
-  return hipGetLastError();
+hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  if (dtype == RLT_DTYPE_BF16) return attn_dispatch<bf16_t>(dh, a, n_rows, s);
+  return attn_dispatch<float>(dh, a, n_rows, s);
 }
 
 hipError_t launch_state_init(float *s, int *pos, const float *s_star, int B, int d,

@@ -45,3 +45,23 @@ def gate_pinned(params: dict, value: float) -> dict:
     p["wg"] = torch.zeros_like(params["wg"])
     p["bg"] = torch.full_like(params["bg"], value)
     return p
+
+
+def oracle_state_from_snapshot(model, cfg, raw, record: int):
+    """Oracle state from one record of a library snapshot (raw uint8 tensor on
+    the CPU), following the record layout documented in include/rlt.h."""
+    from recurrent_decode_step_amd import binding
+    rec, off_s, off_k, off_v = binding.snapshot_layout(cfg)
+    r = raw[record * rec:(record + 1) * rec]
+    pos = int(r[:48].view(torch.int32)[8])
+    L, H, dh, Wm1 = cfg.n_layers, cfg.n_heads, cfg.head_dim, cfg.window - 1
+    n_hist = min(pos, Wm1)
+    es = 2 if cfg.dtype == 1 else 4
+    sdt = torch.bfloat16 if cfg.dtype == 1 else torch.float32
+    s = r[off_s:off_s + cfg.d_model * 4].view(torch.float32).clone()
+    if Wm1 > 0:
+        K = r[off_k:off_k + L * H * Wm1 * dh * es].view(sdt).reshape(L, H, Wm1, dh)[:, :, :n_hist]
+        V = r[off_v:off_v + L * H * Wm1 * dh * es].view(sdt).reshape(L, H, Wm1, dh)[:, :, :n_hist]
+    else:
+        K = V = torch.zeros((L, H, 0, dh), dtype=sdt)
+    return oracle.state_from_arrays(model, pos, s, K.float(), V.float())

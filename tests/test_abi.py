@@ -114,4 +114,5 @@ def test_null_handles():
     assert L.rlt_state_export(None, None, 1, None, None, None) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_state_import(None, None, 1, None, None, None) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_state_position(None, 0) == -1
-    assert L.rlt_profile_begin(None, 0, 1) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_profile_begin(None, 1, 1, 1) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_profile_collect(None, 0, None, None, None) == binding.RLT_ERR_INVALID_ARG
