@@ -59,17 +59,19 @@ int kstep_of(int dtype) { return dtype == RLT_DTYPE_BF16 ? 32 : 16; }
 // each, at most 16 k-steps per batch of loads); the cut depends on K only, so a
 // row's result never depends on how many rows share the launch.
 struct GemmPlan {
-  int N, K, Np, KT, tiles, parts;
+  int N, K, Np, KT, tiles, parts, tpw;
 };
 
 GemmPlan gemm_plan(int N, int K, int dtype) {
   GemmPlan p;
   p.N = N;
   p.K = K;
-  p.Np = cdiv(N, 16) * 16;
+  p.Np = cdiv(N, 32) * 32;                     // whole pairs of 16-row tiles
   p.tiles = p.Np / 16;
   p.KT = cdiv(K, kstep_of(dtype));
   p.parts = std::max(1, std::min(kMaxParts, cdiv(p.KT, 16)));
+  // two tiles per wavefront halve the activation reads; keep >= 128 workgroups
+  p.tpw = p.tiles >= 256 ? 2 : 1;
   return p;
 }
 
@@ -225,10 +227,11 @@ size_t state_layout(const rlt_config &c, rlt_state *st, void *base, int B) {
   st->slots_dev = ar.take<int>((size_t)B * 4);
   st->x = ar.take<float>((size_t)B * d * 4);
   st->sumsq = ar.take<float>((size_t)cdiv(d, 16) * B * 4);
-  st->xg = ar.take<char>((size_t)B * d * es);
+  const size_t rows16 = (size_t)cdiv(B, 16) * 16;   // packed activations: whole 16-row blocks
+  st->xg = ar.take<char>(rows16 * d * es);
   st->qbuf = ar.take<char>((size_t)B * d * es);
-  st->obuf = ar.take<char>((size_t)B * d * es);
-  st->hbuf = ar.take<char>((size_t)B * c.d_ffn * es);
+  st->obuf = ar.take<char>(rows16 * d * es);
+  st->hbuf = ar.take<char>(rows16 * c.d_ffn * es);
   return align256(ar.off);
 }
 
@@ -362,6 +365,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
   base.H = H;
   base.dh = dh;
   base.W = W;
+  base.kt_out = d / kstep_of(c.dtype);
 
   auto gemm = [&](const GemmPlan &g, const PackedMat &w, int act, int epi, GemmArgs a,
                   const char *what, double act_bytes, double out_bytes) -> rlt_status {
@@ -370,7 +374,9 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     a.K = g.K;
     a.KT = g.KT;
     Prof p(st, RLT_K_GEMM, s);
-    const hipError_t e2 = launch_gemm(c.dtype, cp.ncb, act, epi, a, g.tiles, cp.groups, g.parts, s);
+    const int tpw = cp.ncb <= 2 ? g.tpw : 1;    // registers: two tiles only up to 32 rows
+    const hipError_t e2 =
+        launch_gemm(c.dtype, cp.ncb, tpw, act, epi, a, g.tiles, cp.groups, g.parts, s);
     if (e2 != hipSuccess) return hip_fail(e2, what);
     p.done((double)g.N * g.K * es + act_bytes + out_bytes);
     return RLT_OK;
@@ -399,6 +405,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
   at.H = H;
   at.d = d;
   at.ch = m->chunk;
+  at.kt_out = d / kstep_of(c.dtype);
   at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
 
   for (int l = 0; l < L; ++l) {
@@ -487,6 +494,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
       a.ld_act = d;
       a.out = st->hbuf;
       a.ld_out = F;
+      a.kt_out = F / kstep_of(c.dtype);
       if ((rs = gemm(m->p_ffn1, m->w1[l], ACT_PLAIN, EPI_GELU, a, "ffn1 gemm", row_in,
                      (double)n * F * es)) != RLT_OK)
         return rs;

@@ -11,7 +11,7 @@ namespace rlt {
 typedef uint16_t bf16_t;
 
 constexpr int kAttnThreads = 256;
-constexpr int kMaxParts = 16;         // K parts (wavefronts) per GEMM workgroup
+constexpr int kMaxParts = 8;          // K parts (wavefronts) per GEMM workgroup
 constexpr int kColsPerGroup = 64;     // batch rows per GEMM workgroup (4 x 16-column blocks)
 
 // activation sources of a GEMM (the MFMA B operand)
@@ -31,11 +31,13 @@ struct PackedMat {
 
 struct GemmArgs {
   const void *wp;
-  int N, K, KT, n_rows;
+  int N, K, KT, n_rows;                     // the activation has the same KT
+  int kt_out;                               // KT of packed outputs (x*gamma, FFN hidden)
   const int *slots;                         // staged slot list, or null: row i is slot i
   int *pos;                                 // [B] tokens consumed per slot
   int advance_pos;                          // last kernel of a step: pos[slot] += 1
-  // activation (storage type, [n][ld_act]); MERGE: e rows, s from the state
+  // activation: fragment-packed [n/16][KT][64][16 B], storage type; MERGE: e
+  // rows [n][ld_act] and s [B][d] fp32 from the state, both row-major
   const void *act; int64_t ld_act;
   const float *s_state; int d;
   // 1/rms for scaled epilogues: partial sums [n_parts][part_ld]
@@ -43,7 +45,7 @@ struct GemmArgs {
   // epilogues
   void *out; int64_t ld_out;                // QKV (q part)/STORE/GELU: storage type; LOGITS: fp32
   float *x;                                 // RESID/MERGE: fp32 residual stream [n][d]
-  void *xg;                                 // RESID/MERGE: x * gamma_next, storage type [n][d]
+  void *xg;                                 // RESID/MERGE: x * gamma_next, storage type, packed
   const float *gamma_next;
   float *sumsq_out;                         // RESID/MERGE: [N/16][part_ld]
   float *s_out;                             // RESID (last layer): s [B][d]
@@ -53,7 +55,8 @@ struct GemmArgs {
 };
 
 struct AttnArgs {
-  const void *q; void *out;                 // [n][d]
+  const void *q; void *out;                 // q [n][d] row-major; out fragment-packed
+  int kt_out;                               // KT of the packed output (d / k-step)
   const void *kb; const void *vb;           // bases (group / layer applied)
   int64_t s_seq, s_head, s_pos;             // elements
   int len_cap;                              // window W, or INT32_MAX for memory
@@ -66,7 +69,7 @@ struct AttnArgs {
 // kernel launchers (rlt_kernels.hip)
 hipError_t launch_pack_tiles(const void *src, int rows, int K, int64_t ld, int tile_begin,
                              int tile_end, const PackedMat &dst, int dtype, hipStream_t s);
-hipError_t launch_gemm(int dtype, int ncb, int act, int epi, const GemmArgs &a, int tiles,
+hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const GemmArgs &a, int tiles,
                        int col_groups, int parts, hipStream_t s);
 hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStream_t s);
 int attn_chunk_max(int dtype, int dh);

@@ -129,20 +129,39 @@ __global__ void k_pack(const T *__restrict__ src, int rows, int K, int64_t ld, i
 // ---------------------------------------------------------------- GEMM
 // y[i][n] = sum_k W[n][k] a[i][k] for the batch rows i, fused epilogues.
 //
-// One workgroup per 16-row tile of W and per group of up to 64 batch rows.
-// K is cut into NP consecutive parts (NP depends on K only); wavefront w of the
-// workgroup runs part w as one MFMA chain in k order, and the NP partial tiles
-// are added in part order through LDS.  No workgroup ever waits for another,
-// and a row's result does not depend on how many rows share the launch.
-// Weights stream from HBM once per column group; activations (a few hundred
-// KiB) come from L2.
-template <typename T, int ACT>
-__device__ __forceinline__ u32x4 load_b(const GemmArgs &a, int i, int slot, int k) {
+// One workgroup per TPW 16-row tiles of W and per group of up to 64 batch
+// rows.  K is cut into NP consecutive parts (NP depends on K only); wavefront w
+// of the workgroup runs part w of every tile as one MFMA chain in k order, and
+// the NP partial tiles are added in part order through LDS.  No workgroup ever
+// waits for another, and a row's result does not depend on how many rows share
+// the launch or on TPW.
+//
+// Activations produced inside the step are stored fragment-packed: the
+// 16-byte B-operand fragment of batch row i, k-step ks, lane group g sits at
+// fragment index ((i/16) * KT + ks) * 64 + (i%16) + 16 g, so one wavefront
+// load per k-step and 16-row column block is one contiguous KiB.
+template <typename T>
+__device__ __forceinline__ size_t packed_off(int i, int k, int KT) {
   constexpr int EPL = Num<T>::EPL;
+  constexpr int KSTEP = 4 * EPL;
+  const int ks = k / KSTEP, r = k - ks * KSTEP;
+  const int lane = (i & 15) + 16 * (r / EPL);
+  return (((size_t)(i >> 4) * KT + ks) * 64 + lane) * EPL + (r % EPL);
+}
+
+__device__ __forceinline__ int slot_of(const GemmArgs &a, int i) { return a.slots ? a.slots[i] : i; }
+
+template <typename T, int ACT>
+__device__ __forceinline__ u32x4 load_b(const GemmArgs &a, int cbg, int irow, int slot, int ks,
+                                        int lane) {
+  constexpr int EPL = Num<T>::EPL;
+  constexpr int KSTEP = 4 * EPL;
   if constexpr (ACT == ACT_MERGE) {
-    // gate input [e_t ; s_{t-1}]: s is fp32 state, rounded to the storage type here
-    if (k >= a.d) {
-      const float *sp = a.s_state + (size_t)slot * a.d + (k - a.d);
+    // gate input [e_t ; s_{t-1}], both row-major: e in the storage type, s fp32
+    // state rounded to the storage type here
+    const int kl = (lane >> 4) * EPL;
+    if (ks * KSTEP >= a.d) {                        // uniform over the wavefront
+      const float *sp = a.s_state + (size_t)slot * a.d + (ks * KSTEP - a.d) + kl;
       float v[EPL];
 #pragma unroll
       for (int j = 0; j < EPL; j += 4) {
@@ -151,68 +170,60 @@ __device__ __forceinline__ u32x4 load_b(const GemmArgs &a, int i, int slot, int 
       }
       return Num<T>::pack(v);
     }
+    return *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.act) + (size_t)irow * a.ld_act +
+                                            ks * KSTEP + kl);
+  } else {
+    return static_cast<const u32x4 *>(a.act)[((size_t)cbg * a.KT + ks) * 64 + lane];
   }
-  return *reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.act) + (size_t)i * a.ld_act + k);
 }
 
-__device__ __forceinline__ int slot_of(const GemmArgs &a, int i) { return a.slots ? a.slots[i] : i; }
-
-template <typename T, int NCB, int ACT, int EPI, int MAXNW>
+template <typename T, int NCB, int ACT, int EPI, int MAXNW, int TPW>
 __global__ __launch_bounds__(MAXNW * 64) void k_gemm(const GemmArgs a) {
-  constexpr int EPL = Num<T>::EPL;
-  constexpr int KSTEP = 4 * EPL;
   constexpr int COLS = NCB * 16;
-  // weight fragments in flight per wavefront, activation fragments prefetched;
-  // 16-wavefront workgroups have a quarter of the registers per lane
-  constexpr int WB = MAXNW <= 4 ? 16 : 8;
-  constexpr int PD = (MAXNW <= 4 && NCB <= 2) ? 4 : 2;
+  constexpr int WB = 16;                           // k-steps per batch of weight loads
+  constexpr int AB = NCB == 1 ? 16 : (NCB == 2 ? 8 : 2);   // activation k-steps in registers
   constexpr bool SCALED = EPI == EPI_QKV || EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_LOGITS;
-  extern __shared__ f32x4 s_acc[];                 // [parts][NCB][64] partial tiles
+  extern __shared__ f32x4 s_acc[];                 // [parts][TPW][NCB][64] partial tiles
   __shared__ float s_grp[8][COLS];
   __shared__ float s_rinv[COLS];
 
   const int NW = blockDim.x >> 6;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int tile = blockIdx.x;
+  const int tile0 = blockIdx.x * TPW;
   const int col0 = blockIdx.y * COLS;
   const int ncols = min(COLS, a.n_rows - col0);
   const int ks0 = (wave * a.KT) / NW;
   const int nks = ((wave + 1) * a.KT) / NW - ks0;
 
-  int rowi[NCB], slot[NCB];
-  bool okc[NCB];
+  // Every load below is unconditional and in bounds: batch columns past the
+  // last row read the last row's data (their outputs are never stored), so no
+  // load needs a select and all of them stay in flight together.
+  int cbg[NCB], irow[NCB], slot[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    const int c = cb * 16 + (lane & 15);
-    okc[cb] = c < ncols;
-    rowi[cb] = col0 + (okc[cb] ? c : 0);
-    slot[cb] = (ACT == ACT_MERGE) ? slot_of(a, rowi[cb]) : 0;
+    cbg[cb] = min((int)blockIdx.y * NCB + cb, (a.n_rows - 1) >> 4);
+    irow[cb] = col0 + min(cb * 16 + (lane & 15), ncols - 1);
+    slot[cb] = (ACT == ACT_MERGE) ? slot_of(a, irow[cb]) : 0;
   }
-  const int kl = (lane >> 4) * EPL;
-  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+  const u32x4 *wp[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    wp[t] = static_cast<const u32x4 *>(a.wp) + ((size_t)(tile0 + t) * a.KT + ks0) * 64 + lane;
 
-  // first batch of weights and activations, before anything else
-  const u32x4 *wp = static_cast<const u32x4 *>(a.wp) + ((size_t)tile * a.KT + ks0) * 64 + lane;
-  // fragment arrays start at zero: their loads are guarded by runtime counts
-  u32x4 wf[WB];
-  u32x4 ab[PD][NCB];
+  u32x4 ab[AB][NCB];
+  u32x4 wf[TPW][WB];
+  auto issue_full = [&](int b0) {
 #pragma unroll
-  for (int j = 0; j < WB; ++j) wf[j] = zero;
-#pragma unroll
-  for (int p = 0; p < PD; ++p)
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) ab[p][cb] = zero;
-  const int nb0 = min(WB, nks);
-#pragma unroll
-  for (int j = 0; j < WB; ++j)
-    if (j < nb0) wf[j] = __builtin_nontemporal_load(wp + (size_t)j * 64);
-#pragma unroll
-  for (int p = 0; p < PD; ++p)
-    if (p < nb0) {
+    for (int p = 0; p < AB; ++p)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
-        ab[p][cb] = okc[cb] ? load_b<T, ACT>(a, rowi[cb], slot[cb], (ks0 + p) * KSTEP + kl) : zero;
-    }
+        ab[p][cb] = load_b<T, ACT>(a, cbg[cb], irow[cb], slot[cb], ks0 + b0 + p, lane);
+#pragma unroll
+    for (int j = 0; j < WB; ++j)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) wf[t][j] = __builtin_nontemporal_load(wp[t] + (size_t)(b0 + j) * 64);
+  };
+  if (nks >= WB) issue_full(0);                    // first batch before anything else
 
   // 1/rms of every batch row from the producer's per-tile partial sums:
   // 8 groups of consecutive parts, each summed in order, then the groups in order.
@@ -221,18 +232,15 @@ __global__ __launch_bounds__(MAXNW * 64) void k_gemm(const GemmArgs a) {
     const int per = (P + 7) / 8;
     for (int q = tid; q < COLS * 8; q += blockDim.x) {
       const int c = q % COLS, g = q / COLS;
+      const float *src = a.sumsq + col0 + min(c, ncols - 1);
+      const int p0 = g * per, p1 = min(P, p0 + per);
       float ss = 0.f;
-      if (c < ncols) {
-        const float *src = a.sumsq + col0 + c;
-        const int p1 = min(P, (g + 1) * per);
-        for (int p = g * per; p < p1; p += 16) {
-          float v[16];
+      for (int p = p0; p < p1; p += 16) {
+        float v[16];
 #pragma unroll
-          for (int u = 0; u < 16; ++u) v[u] = (p + u < p1) ? src[(size_t)(p + u) * a.part_ld] : 0.f;
+        for (int u = 0; u < 16; ++u) v[u] = src[(size_t)min(p + u, P - 1) * a.part_ld];
 #pragma unroll
-          for (int u = 0; u < 16; ++u)
-            if (p + u < p1) ss += v[u];
-        }
+        for (int u = 0; u < 16; ++u) ss += (p + u < p1) ? v[u] : 0.f;
       }
       s_grp[g][c] = ss;
     }
@@ -245,36 +253,55 @@ __global__ __launch_bounds__(MAXNW * 64) void k_gemm(const GemmArgs a) {
     }
   }
 
-  // this wavefront's part of K: one MFMA chain
-  f32x4 acc[NCB];
+  // this wavefront's part of K for each of its tiles: one MFMA chain in k order
+  f32x4 acc[TPW][NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[t][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int b0 = 0; b0 < nks; b0 += WB) {
     const int nb = min(WB, nks - b0);
-    if (b0 > 0) {
+    if (nb == WB) {
+      if (b0 > 0) issue_full(b0);
+#pragma unroll
+      for (int j = 0; j < WB; ++j) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) acc[t][cb] = mma_step(wf[t][j], ab[j % AB][cb], acc[t][cb], T());
+        if (AB < WB && j + AB < WB) {
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            ab[j % AB][cb] = load_b<T, ACT>(a, cbg[cb], irow[cb], slot[cb], ks0 + b0 + j + AB, lane);
+        }
+      }
+    } else {
+      // a ragged batch: loads clamped to the part, MFMAs guarded
+      const int last = ks0 + b0 + nb - 1;
+#pragma unroll
+      for (int p = 0; p < AB; ++p)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          ab[p][cb] = load_b<T, ACT>(a, cbg[cb], irow[cb], slot[cb], min(ks0 + b0 + p, last), lane);
 #pragma unroll
       for (int j = 0; j < WB; ++j)
-        if (j < nb) wf[j] = __builtin_nontemporal_load(wp + (size_t)(b0 + j) * 64);
 #pragma unroll
-      for (int p = 0; p < PD; ++p)
-        if (p < nb) {
+        for (int t = 0; t < TPW; ++t)
+          wf[t][j] = __builtin_nontemporal_load(wp[t] + (size_t)min(b0 + j, nks - 1) * 64);
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-            ab[p][cb] = okc[cb] ? load_b<T, ACT>(a, rowi[cb], slot[cb], (ks0 + b0 + p) * KSTEP + kl)
-                                : zero;
+      for (int j = 0; j < WB; ++j) {
+        if (j < nb) {
+#pragma unroll
+          for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              acc[t][cb] = mma_step(wf[t][j], ab[j % AB][cb], acc[t][cb], T());
         }
-    }
-#pragma unroll
-    for (int j = 0; j < WB; ++j) {
-      if (j < nb) {
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma_step(wf[j], ab[j % PD][cb], acc[cb], T());
-        if (j + PD < nb) {
+        if (AB < WB && j + AB < WB) {
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
-            ab[j % PD][cb] = okc[cb] ? load_b<T, ACT>(a, rowi[cb], slot[cb],
-                                                       (ks0 + b0 + j + PD) * KSTEP + kl)
-                                     : zero;
+            ab[j % AB][cb] =
+                load_b<T, ACT>(a, cbg[cb], irow[cb], slot[cb], min(ks0 + b0 + j + AB, last), lane);
         }
       }
     }
@@ -282,15 +309,19 @@ __global__ __launch_bounds__(MAXNW * 64) void k_gemm(const GemmArgs a) {
 
   // partial tiles summed in part order
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) s_acc[(wave * NCB + cb) * 64 + lane] = acc[cb];
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) s_acc[((wave * TPW + t) * NCB + cb) * 64 + lane] = acc[t][cb];
   __syncthreads();
 
   // ---- epilogue: lane holds features rbase..rbase+3 of batch column cb*16 + cl
-  const int rbase = tile * 16 + (lane >> 4) * 4;
   const int cl = lane & 15;
-  for (int cb = wave; cb < NCB; cb += NW) {
-    f32x4 yv = s_acc[cb * 64 + lane];
-    for (int w = 1; w < NW; ++w) yv += s_acc[(w * NCB + cb) * 64 + lane];
+  for (int q = wave; q < TPW * NCB; q += NW) {
+    const int t = q / NCB, cb = q - (q / NCB) * NCB;
+    f32x4 yv = s_acc[(t * NCB + cb) * 64 + lane];
+    for (int w = 1; w < NW; ++w) yv += s_acc[((w * TPW + t) * NCB + cb) * 64 + lane];
+    const int tile = tile0 + t;
+    const int rbase = tile * 16 + (lane >> 4) * 4;
     const int c = cb * 16 + cl;
     const bool live = c < ncols && rbase < a.N;
     const int i = col0 + c;
@@ -298,7 +329,7 @@ __global__ __launch_bounds__(MAXNW * 64) void k_gemm(const GemmArgs a) {
     if constexpr (SCALED) {
       const float r = s_rinv[c];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) y[q] *= r;
+      for (int u = 0; u < 4; ++u) y[u] *= r;
     }
     if constexpr (EPI == EPI_RESID || EPI == EPI_MERGE) {
       float ss = 0.f;
@@ -314,23 +345,23 @@ __global__ __launch_bounds__(MAXNW * 64) void k_gemm(const GemmArgs a) {
           const float *sp = a.s_state + (size_t)sl * a.d + rbase;
           const T *ep = static_cast<const T *>(a.act) + (size_t)i * a.ld_act + rbase;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float z = y[q] + a.bias[rbase + q];
+          for (int u = 0; u < 4; ++u) {
+            const float z = y[u] + a.bias[rbase + u];
             const float g = 1.0f / (1.0f + __expf(-z));
             float ev;
-            if constexpr (sizeof(T) == 2) ev = bf2f(reinterpret_cast<const bf16_t *>(ep)[q]);
-            else ev = reinterpret_cast<const float *>(ep)[q];
-            xv[q] = g * ev + (1.0f - g) * sp[q];
+            if constexpr (sizeof(T) == 2) ev = bf2f(reinterpret_cast<const bf16_t *>(ep)[u]);
+            else ev = reinterpret_cast<const float *>(ep)[u];
+            xv[u] = g * ev + (1.0f - g) * sp[u];
           }
         }
         *reinterpret_cast<f32x4 *>(xp) = f32x4{xv[0], xv[1], xv[2], xv[3]};
         if (a.s_out)
           *reinterpret_cast<f32x4 *>(a.s_out + (size_t)sl * a.d + rbase) =
               f32x4{xv[0], xv[1], xv[2], xv[3]};
-        // input of the next RMSNorm'd GEMM: x * gamma_next in the storage type
+        // input of the next RMSNorm'd GEMM: x * gamma_next, storage type, packed
         const f32x4 gn = *reinterpret_cast<const f32x4 *>(a.gamma_next + rbase);
         const float xg[4] = {xv[0] * gn.x, xv[1] * gn.y, xv[2] * gn.z, xv[3] * gn.w};
-        Num<T>::store4(static_cast<T *>(a.xg) + (size_t)i * a.d + rbase, xg);
+        Num<T>::store4(static_cast<T *>(a.xg) + packed_off<T>(i, rbase, a.kt_out), xg);
         ss = ((xv[0] * xv[0] + xv[1] * xv[1]) + xv[2] * xv[2]) + xv[3] * xv[3];
       }
       ss += __shfl_xor(ss, 16);
@@ -354,13 +385,13 @@ __global__ __launch_bounds__(MAXNW * 64) void k_gemm(const GemmArgs a) {
         Num<T>::store4(static_cast<T *>(a.out) + (size_t)i * a.ld_out + rbase, y);
       } else if constexpr (EPI == EPI_GELU) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) y[q] = gelu_erf(y[q]);
-        Num<T>::store4(static_cast<T *>(a.out) + (size_t)i * a.ld_out + rbase, y);
+        for (int u = 0; u < 4; ++u) y[u] = gelu_erf(y[u]);
+        Num<T>::store4(static_cast<T *>(a.out) + packed_off<T>(i, rbase, a.kt_out), y);
       } else if constexpr (EPI == EPI_LOGITS) {
         float *lp = static_cast<float *>(a.out) + (size_t)i * a.ld_out + rbase;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (rbase + q < a.N) lp[q] = y[q];
+        for (int u = 0; u < 4; ++u)
+          if (rbase + u < a.N) lp[u] = y[u];
       }
     }
   }
@@ -392,15 +423,15 @@ struct AttnShape {
 template <typename T, int DH>
 __device__ __forceinline__ void attn_load(const T *kp, const T *vp, int64_t s_pos, int base, int len,
                                           int ch, int my, u32x4 *kr, u32x4 *vr) {
+  // unconditional loads: positions past the chunk or the end re-read the last
+  // valid one and are masked out of the scores
   using S = AttnShape<T, DH>;
 #pragma unroll
   for (int u = 0; u < S::U; ++u) {
-    const int pc = u * S::RPB + my;
-    const int p = base + pc;
-    if (pc < ch && p < len) {
-      kr[u] = *reinterpret_cast<const u32x4 *>(kp + (size_t)p * s_pos);
-      vr[u] = *reinterpret_cast<const u32x4 *>(vp + (size_t)p * s_pos);
-    }
+    const int pc = min(u * S::RPB + my, ch - 1);
+    const int p = min(base + pc, len - 1);
+    kr[u] = *reinterpret_cast<const u32x4 *>(kp + (size_t)p * s_pos);
+    vr[u] = *reinterpret_cast<const u32x4 *>(vp + (size_t)p * s_pos);
   }
 }
 
@@ -470,6 +501,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
   const T *kp = static_cast<const T *>(a.kb) + off;
   const T *vp = static_cast<const T *>(a.vb) + off;
 
+  const int ch = a.ch;                             // positions per chunk (<= CH)
+  u32x4 ka[U], va[U], kb2[U], vb2[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    ka[u] = u32x4{0u, 0u, 0u, 0u}; va[u] = ka[u]; kb2[u] = ka[u]; vb2[u] = ka[u];
+  }
+  attn_load<T, DH>(kp, vp, a.s_pos, 0, len, ch, my, ka, va);   // first chunk in flight first
+
   float qf[EPL];
   Num<T>::unpack(*reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.q) + (size_t)i * a.d +
                                                   h * DH + sub * EPL),
@@ -480,13 +519,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
   float m = -INFINITY, l = 0.f, o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  const int ch = a.ch;                             // positions per chunk (<= CH)
-  u32x4 ka[U], va[U], kb2[U], vb2[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    ka[u] = u32x4{0u, 0u, 0u, 0u}; va[u] = ka[u]; kb2[u] = ka[u]; vb2[u] = ka[u];
-  }
-  attn_load<T, DH>(kp, vp, a.s_pos, 0, len, ch, my, ka, va);
   for (int c0 = 0; c0 < len; c0 += 2 * ch) {
     if (c0 + ch < len) attn_load<T, DH>(kp, vp, a.s_pos, c0 + ch, len, ch, my, kb2, vb2);
     attn_chunk<T, DH>(qf, ka, va, c0, len, ch, my, m, l, o);
@@ -517,12 +549,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
     sc[w] = exp2f(s_ml[w][0] - M);               // a wavefront with no positions has m = -inf
     L += s_ml[w][1] * sc[w];
   }
-  T *outp = static_cast<T *>(a.out) + (size_t)i * a.d + h * DH;
-  for (int j = tid; j < DH; j += kAttnThreads) {
-    float v = 0.f;
+  // output fragment-packed (the input layout of the next GEMM): one 16-byte
+  // fragment of EPL consecutive values per thread
+  for (int f = tid; f < DH / EPL; f += kAttnThreads) {
+    float v[EPL];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) v += s_o[w][j] * sc[w];
-    Num<T>::store1(outp + j, v / L);
+    for (int e = 0; e < EPL; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += s_o[w][f * EPL + e] * sc[w];
+      v[e] = acc / L;
+    }
+    *reinterpret_cast<u32x4 *>(static_cast<T *>(a.out) + packed_off<T>(i, h * DH + f * EPL, a.kt_out)) =
+        Num<T>::pack(v);
   }
 }
 
@@ -642,15 +681,15 @@ hipError_t launch_pack_tiles(const void *src, int rows, int K, int64_t ld, int t
   return hipGetLastError();
 }
 
-template <typename T, int NCB>
+template <typename T, int NCB, int TPW>
 static hipError_t gemm_dispatch_epi(int act, int epi, const GemmArgs &a, dim3 grid, int threads,
                                     hipStream_t s) {
-  const size_t lds = (size_t)(threads / 64) * NCB * 1024;
-#define RLT_G(A, E)                                                         \
-  if (act == A && epi == E) {                                               \
-    if (threads <= 256) k_gemm<T, NCB, A, E, 4><<<grid, threads, lds, s>>>(a);           \
-    else k_gemm<T, NCB, A, E, kMaxParts><<<grid, threads, lds, s>>>(a);                  \
-    return hipGetLastError();                                               \
+  const size_t lds = (size_t)(threads / 64) * TPW * NCB * 1024;
+#define RLT_G(A, E)                                                                    \
+  if (act == A && epi == E) {                                                          \
+    if (threads <= 256) k_gemm<T, NCB, A, E, 4, TPW><<<grid, threads, lds, s>>>(a);    \
+    else k_gemm<T, NCB, A, E, kMaxParts, TPW><<<grid, threads, lds, s>>>(a);           \
+    return hipGetLastError();                                                          \
   }
   RLT_G(ACT_PLAIN, EPI_QKV)
   RLT_G(ACT_PLAIN, EPI_RESID)
@@ -663,22 +702,31 @@ static hipError_t gemm_dispatch_epi(int act, int epi, const GemmArgs &a, dim3 gr
 }
 
 template <typename T>
-static hipError_t gemm_dispatch(int ncb, int act, int epi, const GemmArgs &a, dim3 grid,
+static hipError_t gemm_dispatch(int ncb, int tpw, int act, int epi, const GemmArgs &a, dim3 grid,
                                 int threads, hipStream_t s) {
-  switch (ncb) {
-    case 1: return gemm_dispatch_epi<T, 1>(act, epi, a, grid, threads, s);
-    case 2: return gemm_dispatch_epi<T, 2>(act, epi, a, grid, threads, s);
-    case 4: return gemm_dispatch_epi<T, 4>(act, epi, a, grid, threads, s);
+  if (tpw == 2) {
+    switch (ncb) {
+      case 1: return gemm_dispatch_epi<T, 1, 2>(act, epi, a, grid, threads, s);
+      case 2: return gemm_dispatch_epi<T, 2, 2>(act, epi, a, grid, threads, s);
+      case 4: return gemm_dispatch_epi<T, 4, 2>(act, epi, a, grid, threads, s);
+    }
+  } else {
+    switch (ncb) {
+      case 1: return gemm_dispatch_epi<T, 1, 1>(act, epi, a, grid, threads, s);
+      case 2: return gemm_dispatch_epi<T, 2, 1>(act, epi, a, grid, threads, s);
+      case 4: return gemm_dispatch_epi<T, 4, 1>(act, epi, a, grid, threads, s);
+    }
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(int dtype, int ncb, int act, int epi, const GemmArgs &a, int tiles,
+hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const GemmArgs &a, int tiles,
                        int col_groups, int parts, hipStream_t s) {
-  const dim3 grid((unsigned)tiles, (unsigned)col_groups);
-  if (parts < 1 || parts > kMaxParts) return hipErrorInvalidValue;
-  if (dtype == RLT_DTYPE_BF16) return gemm_dispatch<bf16_t>(ncb, act, epi, a, grid, parts * 64, s);
-  return gemm_dispatch<float>(ncb, act, epi, a, grid, parts * 64, s);
+  if (parts < 1 || parts > kMaxParts || (tpw != 1 && tpw != 2) || tiles % tpw)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(tiles / tpw), (unsigned)col_groups);
+  if (dtype == RLT_DTYPE_BF16) return gemm_dispatch<bf16_t>(ncb, tpw, act, epi, a, grid, parts * 64, s);
+  return gemm_dispatch<float>(ncb, tpw, act, epi, a, grid, parts * 64, s);
 }
 
 template <typename T>
