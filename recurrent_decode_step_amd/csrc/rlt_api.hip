@@ -69,9 +69,10 @@ GemmPlan gemm_plan(int N, int K, int dtype) {
   p.Np = cdiv(N, 32) * 32;                     // whole pairs of 16-row tiles
   p.tiles = p.Np / 16;
   p.KT = cdiv(K, kstep_of(dtype));
-  p.parts = std::max(1, std::min(kMaxParts, cdiv(p.KT, 16)));
+  // K parts of 8+ k-steps (one wavefront each), at most 8; the cut depends on K only
+  p.parts = std::max(1, std::min(kMaxParts, p.KT / 8));
   // two tiles per wavefront halve the activation reads; keep >= 128 workgroups
-  p.tpw = p.tiles >= 256 ? 2 : 1;
+  p.tpw = (p.tiles >= 256 && dtype == RLT_DTYPE_BF16) ? 2 : 1;
   return p;
 }
 

@@ -177,11 +177,22 @@ __device__ __forceinline__ u32x4 load_b(const GemmArgs &a, int cbg, int irow, in
   }
 }
 
-template <typename T, int NCB, int ACT, int EPI, int MAXNW, int TPW>
-__global__ __launch_bounds__(MAXNW * 64) void k_gemm(const GemmArgs a) {
+// Activation k-steps held in registers next to TPW x KSW weight fragments
+// (about 216 VGPRs of loads in flight per lane; the rest is refilled along the chain).
+template <int KSW, int TPW, int NCB>
+struct GemmRegs {
+  // single-tile 16-k-step variants keep a second weight batch in flight
+  static constexpr bool DB = TPW == 1 && KSW == 16;
+  static constexpr int budget = 216 - (DB ? 2 : 1) * TPW * KSW * 4 - 4 * TPW * NCB;
+  static constexpr int raw = budget / (4 * NCB);
+  static constexpr int AB = raw >= KSW ? KSW : (raw >= 16 ? 16 : (raw >= 8 ? 8 : (raw >= 4 ? 4 : 2)));
+};
+
+template <typename T, int NCB, int ACT, int EPI, int KSW, int TPW>
+__global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
   constexpr int COLS = NCB * 16;
-  constexpr int WB = 16;                           // k-steps per batch of weight loads
-  constexpr int AB = NCB == 1 ? 16 : (NCB == 2 ? 8 : 2);   // activation k-steps in registers
+  constexpr int WB = KSW;                          // k-steps per batch of weight loads
+  constexpr int AB = GemmRegs<KSW, TPW, NCB>::AB;  // activation k-steps in registers
   constexpr bool SCALED = EPI == EPI_QKV || EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_LOGITS;
   extern __shared__ f32x4 s_acc[];                 // [parts][TPW][NCB][64] partial tiles
   __shared__ float s_grp[8][COLS];
@@ -259,7 +270,40 @@ __global__ __launch_bounds__(MAXNW * 64) void k_gemm(const GemmArgs a) {
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[t][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int b0 = 0; b0 < nks; b0 += WB) {
+  bool done = false;
+  if constexpr (GemmRegs<KSW, TPW, NCB>::DB) {
+    if (nks == 2 * WB) {
+      // two full batches: the second batch's weights are in flight while the
+      // first is multiplied
+      u32x4 wf2[WB];
+#pragma unroll
+      for (int j = 0; j < WB; ++j) wf2[j] = __builtin_nontemporal_load(wp[0] + (size_t)(WB + j) * 64);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        if (h2 == 1) {
+#pragma unroll
+          for (int p = 0; p < AB; ++p)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              ab[p][cb] = load_b<T, ACT>(a, cbg[cb], irow[cb], slot[cb], ks0 + WB + p, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < WB; ++j) {
+          const u32x4 w = h2 == 0 ? wf[0][j] : wf2[j];
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) acc[0][cb] = mma_step(w, ab[j % AB][cb], acc[0][cb], T());
+          if (AB < WB && j + AB < WB) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              ab[j % AB][cb] =
+                  load_b<T, ACT>(a, cbg[cb], irow[cb], slot[cb], ks0 + h2 * WB + j + AB, lane);
+          }
+        }
+      }
+      done = true;
+    }
+  }
+  for (int b0 = 0; b0 < nks && !done; b0 += WB) {
     const int nb = min(WB, nks - b0);
     if (nb == WB) {
       if (b0 > 0) issue_full(b0);
@@ -410,22 +454,23 @@ __global__ __launch_bounds__(MAXNW * 64) void k_gemm(const GemmArgs a) {
 // own online softmax (running max, sum, weighted values) in base 2 with no
 // barrier until the end, where the 4 are combined in wavefront order.  K and V
 // of the next chunk are loaded while the current one is processed.
-template <typename T, int DH>
+template <typename T, int DH, int UU = 0>
 struct AttnShape {
   static constexpr int EPL = Num<T>::EPL;
   static constexpr int LPR = DH / EPL;             // lanes per position
   static constexpr int RPW = 64 / LPR;             // positions per wavefront load
   static constexpr int RPB = 4 * RPW;              // positions per workgroup load
-  static constexpr int U = (RPW >= 16) ? 4 : 8;    // loads per lane and tensor per chunk
+  // loads per lane and tensor per chunk
+  static constexpr int U = UU > 0 ? UU : ((RPW >= 16) ? 4 : 8);
   static constexpr int CH = U * RPB;               // positions per chunk
 };
 
-template <typename T, int DH>
+template <typename T, int DH, int UU>
 __device__ __forceinline__ void attn_load(const T *kp, const T *vp, int64_t s_pos, int base, int len,
                                           int ch, int my, u32x4 *kr, u32x4 *vr) {
   // unconditional loads: positions past the chunk or the end re-read the last
   // valid one and are masked out of the scores
-  using S = AttnShape<T, DH>;
+  using S = AttnShape<T, DH, UU>;
 #pragma unroll
   for (int u = 0; u < S::U; ++u) {
     const int pc = min(u * S::RPB + my, ch - 1);
@@ -435,11 +480,11 @@ __device__ __forceinline__ void attn_load(const T *kp, const T *vp, int64_t s_po
   }
 }
 
-template <typename T, int DH>
+template <typename T, int DH, int UU>
 __device__ __forceinline__ void attn_chunk(const float *qf, const u32x4 *kr, const u32x4 *vr,
                                            int base, int len, int ch, int my, float &m, float &l,
                                            float *o) {
-  using S = AttnShape<T, DH>;
+  using S = AttnShape<T, DH, UU>;
   constexpr int EPL = S::EPL, LPR = S::LPR, U = S::U;
   float sc[U];
   float cmax = -INFINITY;
@@ -482,9 +527,9 @@ __device__ __forceinline__ void attn_chunk(const float *qf, const u32x4 *kr, con
   m = mnew;
 }
 
-template <typename T, int DH>
+template <typename T, int DH, int UU = 0>
 __global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
-  using S = AttnShape<T, DH>;
+  using S = AttnShape<T, DH, UU>;
   constexpr int EPL = S::EPL, LPR = S::LPR, RPW = S::RPW, U = S::U;
   __shared__ float s_o[4][DH];
   __shared__ float s_ml[4][2];
@@ -507,7 +552,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
   for (int u = 0; u < U; ++u) {
     ka[u] = u32x4{0u, 0u, 0u, 0u}; va[u] = ka[u]; kb2[u] = ka[u]; vb2[u] = ka[u];
   }
-  attn_load<T, DH>(kp, vp, a.s_pos, 0, len, ch, my, ka, va);   // first chunk in flight first
+  attn_load<T, DH, UU>(kp, vp, a.s_pos, 0, len, ch, my, ka, va);   // first chunk in flight first
 
   float qf[EPL];
   Num<T>::unpack(*reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.q) + (size_t)i * a.d +
@@ -520,11 +565,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
   for (int c0 = 0; c0 < len; c0 += 2 * ch) {
-    if (c0 + ch < len) attn_load<T, DH>(kp, vp, a.s_pos, c0 + ch, len, ch, my, kb2, vb2);
-    attn_chunk<T, DH>(qf, ka, va, c0, len, ch, my, m, l, o);
+    if (c0 + ch < len) attn_load<T, DH, UU>(kp, vp, a.s_pos, c0 + ch, len, ch, my, kb2, vb2);
+    attn_chunk<T, DH, UU>(qf, ka, va, c0, len, ch, my, m, l, o);
     if (c0 + ch >= len) break;
-    if (c0 + 2 * ch < len) attn_load<T, DH>(kp, vp, a.s_pos, c0 + 2 * ch, len, ch, my, ka, va);
-    attn_chunk<T, DH>(qf, kb2, vb2, c0 + ch, len, ch, my, m, l, o);
+    if (c0 + 2 * ch < len) attn_load<T, DH, UU>(kp, vp, a.s_pos, c0 + 2 * ch, len, ch, my, ka, va);
+    attn_chunk<T, DH, UU>(qf, kb2, vb2, c0 + ch, len, ch, my, m, l, o);
   }
 
   // rows of the wavefront, then the 4 wavefronts in order
@@ -681,15 +726,14 @@ hipError_t launch_pack_tiles(const void *src, int rows, int K, int64_t ld, int t
   return hipGetLastError();
 }
 
-template <typename T, int NCB, int TPW>
+template <typename T, int NCB, int KSW, int TPW>
 static hipError_t gemm_dispatch_epi(int act, int epi, const GemmArgs &a, dim3 grid, int threads,
                                     hipStream_t s) {
   const size_t lds = (size_t)(threads / 64) * TPW * NCB * 1024;
-#define RLT_G(A, E)                                                                    \
-  if (act == A && epi == E) {                                                          \
-    if (threads <= 256) k_gemm<T, NCB, A, E, 4, TPW><<<grid, threads, lds, s>>>(a);    \
-    else k_gemm<T, NCB, A, E, kMaxParts, TPW><<<grid, threads, lds, s>>>(a);           \
-    return hipGetLastError();                                                          \
+#define RLT_G(A, E)                                                                 \
+  if (act == A && epi == E) {                                                       \
+    k_gemm<T, NCB, A, E, KSW, TPW><<<grid, threads, lds, s>>>(a);                   \
+    return hipGetLastError();                                                       \
   }
   RLT_G(ACT_PLAIN, EPI_QKV)
   RLT_G(ACT_PLAIN, EPI_RESID)
@@ -701,23 +745,20 @@ static hipError_t gemm_dispatch_epi(int act, int epi, const GemmArgs &a, dim3 gr
   return hipErrorInvalidValue;
 }
 
-template <typename T>
-static hipError_t gemm_dispatch(int ncb, int tpw, int act, int epi, const GemmArgs &a, dim3 grid,
-                                int threads, hipStream_t s) {
-  if (tpw == 2) {
-    switch (ncb) {
-      case 1: return gemm_dispatch_epi<T, 1, 2>(act, epi, a, grid, threads, s);
-      case 2: return gemm_dispatch_epi<T, 2, 2>(act, epi, a, grid, threads, s);
-      case 4: return gemm_dispatch_epi<T, 4, 2>(act, epi, a, grid, threads, s);
-    }
-  } else {
-    switch (ncb) {
-      case 1: return gemm_dispatch_epi<T, 1, 1>(act, epi, a, grid, threads, s);
-      case 2: return gemm_dispatch_epi<T, 2, 1>(act, epi, a, grid, threads, s);
-      case 4: return gemm_dispatch_epi<T, 4, 1>(act, epi, a, grid, threads, s);
-    }
+template <typename T, int KSW, int TPW>
+static hipError_t gemm_dispatch_ncb(int ncb, int act, int epi, const GemmArgs &a, dim3 grid,
+                                    int threads, hipStream_t s) {
+  switch (ncb) {
+    case 1: return gemm_dispatch_epi<T, 1, KSW, TPW>(act, epi, a, grid, threads, s);
+    case 2: return gemm_dispatch_epi<T, 2, KSW, TPW>(act, epi, a, grid, threads, s);
+    case 4: return gemm_dispatch_epi<T, 4, KSW, TPW>(act, epi, a, grid, threads, s);
   }
   return hipErrorInvalidValue;
+}
+
+int gemm_ksw(int dtype, int ks_per_part) {
+  if (dtype != RLT_DTYPE_BF16) return 8;
+  return ks_per_part >= 16 ? 16 : 8;
 }
 
 hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const GemmArgs &a, int tiles,
@@ -725,8 +766,18 @@ hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const Gemm
   if (parts < 1 || parts > kMaxParts || (tpw != 1 && tpw != 2) || tiles % tpw)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)(tiles / tpw), (unsigned)col_groups);
-  if (dtype == RLT_DTYPE_BF16) return gemm_dispatch<bf16_t>(ncb, tpw, act, epi, a, grid, parts * 64, s);
-  return gemm_dispatch<float>(ncb, tpw, act, epi, a, grid, parts * 64, s);
+  const int threads = parts * 64;
+  const int ksw = gemm_ksw(dtype, a.KT / parts);
+  if (dtype != RLT_DTYPE_BF16) {
+    if (tpw != 1) return hipErrorInvalidValue;
+    return gemm_dispatch_ncb<float, 8, 1>(ncb, act, epi, a, grid, threads, s);
+  }
+  if (tpw == 2) {
+    if (ksw == 16) return gemm_dispatch_ncb<bf16_t, 16, 2>(ncb, act, epi, a, grid, threads, s);
+    return gemm_dispatch_ncb<bf16_t, 8, 2>(ncb, act, epi, a, grid, threads, s);
+  }
+  if (ksw == 16) return gemm_dispatch_ncb<bf16_t, 16, 1>(ncb, act, epi, a, grid, threads, s);
+  return gemm_dispatch_ncb<bf16_t, 8, 1>(ncb, act, epi, a, grid, threads, s);
 }
 
 template <typename T>
