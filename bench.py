@@ -28,6 +28,43 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+KERNEL_SOURCE = os.path.join(ROOT, "recurrent_decode_step_amd", "csrc", "rlt_kernels.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_attn_cross_refdepth_b32_counters.md")
+
+
+def source_sha256(path=KERNEL_SOURCE):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(path=COUNTERS_FILE):
+    """HBM bytes per launch of the cross-attention kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy
+    calibration), or None when the summary is missing or was taken on another
+    version of the kernel source."""
+    try:
+        kv = {}
+        for line in open(path):
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                kv[k.strip().strip("`")] = v.strip().strip("`")
+        if kv.get("kernel_source_sha256") != source_sha256():
+            return None
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibration_copy(dev, mib=256):
+    """One plain streaming kernel of known size (reads and writes `mib` MiB),
+    so hardware byte counters can be scaled against it."""
+    import torch
+    a = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def algorithmic_bytes_per_step(cfg, positions, es):
@@ -119,6 +156,8 @@ def run_refdepth(args):
     logits_step = torch.empty((max(K - prompt, 1), B, cfg.vocab), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t_setup
+    if args.calibrate_copy:
+        calibration_copy(dev)
 
     # warmup: W steps from H_0, then every slot back to H_0 (untimed)
     if args.warmup > 0:
@@ -138,8 +177,12 @@ def run_refdepth(args):
     ev0.record(stream)
     binding.rlt_run_sequence(model, state, e[:, :n_pre], mem, logits_mode=binding.RLT_LOGITS_ALL,
                              logits=logits_pre)
+    if args.progress:
+        print(f"prompt of {n_pre} steps enqueued", file=sys.stderr, flush=True)
     for j in range(prompt, K):
         binding.rlt_decoder_step(model, state, e_by_step[j], mem, logits=logits_step[j - prompt])
+        if args.progress and (j + 1) % 128 == 0:
+            print(f"step {j + 1} enqueued", file=sys.stderr, flush=True)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
@@ -155,6 +198,7 @@ def run_refdepth(args):
     value = B * K / (ms / 1e3)
     cross_avg_ms = cross_ms / max(cross_n, 1)
     achieved = cross_bytes / max(cross_n, 1) / (cross_avg_ms / 1e3) / 1e9
+    traffic = measured_traffic() if K == T_total else None
     out = {
         "metric": "decoder token-steps/sec at 1 GPU (48-layer, B=32/256); % HBM/MFMA roofline",
         "value": round(value, 2),
@@ -171,9 +215,11 @@ def run_refdepth(args):
         "config": {"workload": wl.name, "batch": B, "prompt": min(prompt, K),
                    "decode_steps": max(K - prompt, 0), "positions": f"1..{K}",
                    "logits": "every step, fp32"},
-        "roofline": {"bound": "hbm", "kernel": "k_attn<bf16,128> (cross-attention, encoder memory)",
+        "roofline": {"bound": "hbm", "kernel": "k_attn<bf16,128,1> (cross-attention, encoder memory)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "algorithmic_bytes_per_launch": round(cross_bytes / max(cross_n, 1)),
                      "launches_timed": cross_n, "avg_launch_us": round(cross_avg_ms * 1e3, 2)},
         "step_roofline": {"bound": "hbm", "algorithmic_GB_per_step": round(bytes_run / K / 1e9, 3),
                           "achieved": round(bytes_run / (ms / 1e3) / 1e9, 1),
@@ -203,6 +249,10 @@ def main():
     ap.add_argument("--workload", default="refdepth", choices=["refdepth"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--progress", action="store_true",
+                    help="print enqueue progress to stderr (long profiled runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 256 MiB streaming kernel before warmup (counter scaling)")
     ap.add_argument("--breakdown", action="store_true",
                     help="time every kernel class on the sampled steps (adds event records)")
     args = ap.parse_args()

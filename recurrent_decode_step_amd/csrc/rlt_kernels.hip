@@ -527,7 +527,9 @@ __device__ __forceinline__ void attn_chunk(const float *qf, const u32x4 *kr, con
   m = mnew;
 }
 
-template <typename T, int DH, int UU = 0>
+// KIND 0: sliding window over the decoder cache; 1: encoder memory (the same
+// code, two symbols so profiles keep them apart)
+template <typename T, int DH, int KIND, int UU = 0>
 __global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
   using S = AttnShape<T, DH, UU>;
   constexpr int EPL = S::EPL, LPR = S::LPR, RPW = S::RPW, U = S::U;
@@ -780,15 +782,15 @@ hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const Gemm
   return gemm_dispatch_ncb<bf16_t, 8, 1>(ncb, act, epi, a, grid, threads, s);
 }
 
-template <typename T>
+template <typename T, int KIND>
 static hipError_t attn_dispatch(int dh, const AttnArgs &a, int n_rows, hipStream_t s) {
   const dim3 grid((unsigned)n_rows, (unsigned)a.H);
   switch (dh) {
-    case 16: k_attn<T, 16><<<grid, kAttnThreads, 0, s>>>(a); break;
-    case 32: k_attn<T, 32><<<grid, kAttnThreads, 0, s>>>(a); break;
-    case 64: k_attn<T, 64><<<grid, kAttnThreads, 0, s>>>(a); break;
-    case 128: k_attn<T, 128><<<grid, kAttnThreads, 0, s>>>(a); break;
-    case 256: k_attn<T, 256><<<grid, kAttnThreads, 0, s>>>(a); break;
+    case 16: k_attn<T, 16, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
+    case 32: k_attn<T, 32, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
+    case 64: k_attn<T, 64, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
+    case 128: k_attn<T, 128, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
+    case 256: k_attn<T, 256, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -817,8 +819,10 @@ int attn_chunk_max(int dtype, int dh) {
 
 hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  if (dtype == RLT_DTYPE_BF16) return attn_dispatch<bf16_t>(dh, a, n_rows, s);
-  return attn_dispatch<float>(dh, a, n_rows, s);
+  const bool mem = a.len_cap == 0x7fffffff;
+  if (dtype == RLT_DTYPE_BF16)
+    return mem ? attn_dispatch<bf16_t, 1>(dh, a, n_rows, s) : attn_dispatch<bf16_t, 0>(dh, a, n_rows, s);
+  return mem ? attn_dispatch<float, 1>(dh, a, n_rows, s) : attn_dispatch<float, 0>(dh, a, n_rows, s);
 }
 
 hipError_t launch_state_init(float *s, int *pos, const float *s_star, int B, int d,
