@@ -14,6 +14,17 @@ Printed: one JSON line with the throughput, the roofline figure of the
 dominant kernel (cross-attention over the encoder memory), measured with HIP
 events inside the timed region on the launch stream, and the CPU oracle timed
 on a bounded sample of the same workload on the host cores.
+
+Other measurements (each prints its own JSON line; not the default):
+  --workload largebatch   256 sequences at ragged positions t ~ U{1..8192},
+                          W = 1024: K consecutive batched steps from imported
+                          states, MFMA utilisation of the GEMM kernels
+  --workload longctx      d = 4096, 8 sequences, T = 32768: 64-step windows
+                          from imported states at six start positions, per-step
+                          time fitted as a + b min(t, W) + c t and summed
+  --counters-sample       reference-depth model, all sequences at the run's
+                          mean sampled position: a few steps for hardware
+                          counter passes (with --calibrate-copy)
 """
 from __future__ import annotations
 
@@ -38,11 +49,12 @@ def source_sha256(path=KERNEL_SOURCE):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(path=COUNTERS_FILE):
+def measured_traffic(algorithmic_per_launch, path=COUNTERS_FILE):
     """HBM bytes per launch of the cross-attention kernel from the committed
     rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy
-    calibration), or None when the summary is missing or was taken on another
-    version of the kernel source."""
+    calibration), taken on a sample of launches at the run's mean position and
+    scaled by the ratio of algorithmic bytes per launch (run / sample); None
+    when the summary is missing or was taken on another kernel source."""
     try:
         kv = {}
         for line in open(path):
@@ -51,7 +63,8 @@ def measured_traffic(path=COUNTERS_FILE):
                 kv[k.strip().strip("`")] = v.strip().strip("`")
         if kv.get("kernel_source_sha256") != source_sha256():
             return None
-        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+        sample = float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+        return sample * algorithmic_per_launch / float(kv["sample_algorithmic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -65,6 +78,30 @@ def calibration_copy(dev, mib=256):
     torch.neg(a, out=b)
     torch.cuda.synchronize()
     del a, b
+
+
+def synthetic_record(cfg, params, t, dev, index):
+    """Decoder state about to consume token t: s and min(t-1, W-1) history
+    entries per layer drawn N(0, 1); t = 1 is H_0 (s = s*, empty history)."""
+    from recurrent_decode_step_amd import synth
+    r = synth.imported_state(cfg, int(t), device=dev, index=index)
+    if int(t) == 1:
+        r["s"] = params["s_star"].clone()
+    return r
+
+
+def import_positions(model, state, cfg, params, positions, dev, chunk=8):
+    """Import synthetic states so slot b is about to consume token positions[b]."""
+    import torch
+    from recurrent_decode_step_amd import binding
+    B = len(positions)
+    for b0 in range(0, B, chunk):
+        idx = list(range(b0, min(B, b0 + chunk)))
+        recs = [synthetic_record(cfg, params, positions[b], dev, b) for b in idx]
+        snap = binding.build_snapshot(cfg, recs, version=model.version, device=dev)
+        binding.rlt_state_import(model, state, snap, idx)
+        del snap, recs
+    torch.cuda.synchronize()
 
 
 def algorithmic_bytes_per_step(cfg, positions, es):
@@ -96,37 +133,45 @@ def openblas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(cfg, params_gpu, e_gpu, mk_gpu, mv_gpu, budget_s=15.0, max_steps=64):
-    """The oracle (fp32 NumPy, as it stands) on the host: the first steps of the
-    same run, all sequences batched, until the time budget is spent."""
+def cpu_baseline(cfg, params_gpu, e_gpu, mk_gpu, mv_gpu, t0, budget_s=15.0, max_steps=16):
+    """The oracle (fp32 NumPy, as it stands) on the host: all sequences of the
+    workload batched, consuming tokens t0, t0+1, ... from synthetic states
+    imported at t0 (the run's mean position), until the time budget is spent."""
     import torch
     import oracle
     t_prep = time.time()
+    dev = e_gpu.device
     params = {k: v.float().cpu() for k, v in params_gpu.items()}
     B = e_gpu.shape[0]
     om = oracle.Model(params=params, precision="fp32", d_model=cfg.d_model, n_heads=cfg.n_heads,
                       n_layers=cfg.n_layers, d_ffn=cfg.d_ffn, window=cfg.window,
                       mem_groups=cfg.mem_groups, vocab=cfg.vocab, rms_eps=cfg.rms_eps)
     del params
-    steps_cap = max_steps
-    e = e_gpu[:, :steps_cap].float().cpu()
-    mk = mk_gpu[:, :, :, :steps_cap].float().cpu()
-    mv = mv_gpu[:, :, :, :steps_cap].float().cpu()
+    n_cap = min(max_steps, e_gpu.shape[1] - t0 + 1)
+    states = []
+    for b in range(B):
+        r = synthetic_record(cfg, params_gpu, t0, dev, b)
+        states.append(oracle.state_from_arrays(om, r["pos"], r["s"].float().cpu(),
+                                               r["K"].float().cpu(), r["V"].float().cpu()))
+        del r
+    e = e_gpu[:, t0 - 1:t0 - 1 + n_cap].float().cpu()
+    mk = mk_gpu[:, :, :, :t0 - 1 + n_cap].float().cpu()
+    mv = mv_gpu[:, :, :, :t0 - 1 + n_cap].float().cpu()
     prep = time.time() - t_prep
-    states = [oracle.initial_state(om) for _ in range(B)]
-    t0 = time.time()
+    t_start = time.time()
     done = 0
-    while done < steps_cap:
+    while done < n_cap:
         oracle.decoder_step(om, states, e[:, done], mk, mv)
         done += 1
-        if time.time() - t0 >= budget_s and done >= 2:
+        if time.time() - t_start >= budget_s:
             break
-    el = time.time() - t0
+    el = time.time() - t_start
     return {"value": B * done / el, "unit": "token-steps/s", "cores": openblas_threads(),
             "kind": "oracle",
-            "sample": f"{B} sequences x the first {done} steps (t = 1..{done}) of the same run, "
-                      f"NumPy fp32 oracle, weights read once per step for the batch "
-                      f"({el:.1f} s timed, {prep:.1f} s input transfer untimed)"}
+            "sample": f"{B} sequences x {done} steps (t = {t0}..{t0 + done - 1}, the run's mean "
+                      f"position) from synthetic states imported at t = {t0}, NumPy fp32 oracle, "
+                      f"weights read once per step for the batch ({el:.1f} s timed, "
+                      f"{prep:.1f} s state and input preparation untimed)"}
 
 
 def run_refdepth(args):
@@ -198,7 +243,7 @@ def run_refdepth(args):
     value = B * K / (ms / 1e3)
     cross_avg_ms = cross_ms / max(cross_n, 1)
     achieved = cross_bytes / max(cross_n, 1) / (cross_avg_ms / 1e3) / 1e9
-    traffic = measured_traffic() if K == T_total else None
+    traffic = measured_traffic(cross_bytes / max(cross_n, 1)) if K == T_total else None
     out = {
         "metric": "decoder token-steps/sec at 1 GPU (48-layer, B=32/256); % HBM/MFMA roofline",
         "value": round(value, 2),
@@ -237,8 +282,199 @@ def run_refdepth(args):
             names[c]: round(prof[c][2] / (prof[c][0] / 1e3) / 1e9, 1) if prof[c][0] else None
             for c in classes}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, params, e, mk, mv, budget_s=args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(cfg, params, e, mk, mv, t0=(K + 1) // 2,
+                                           budget_s=args.cpu_budget)
     return out
+
+
+def run_counters_sample(args):
+    """Reference-depth model, all 32 sequences at the mean position of the
+    steps bench.py samples for the roofline (t = 1, 41, ..., 2521: mean 1261),
+    a few decoder steps, for rocprofv3 counter passes."""
+    import torch
+    from recurrent_decode_step_amd import binding, synth
+    from recurrent_decode_step_amd.configs import REFDEPTH
+    wl = REFDEPTH
+    cfg, B, T = wl.model, wl.batch, wl.steps
+    n = args.sample_steps
+    stride = max(1, T // 64)
+    t_mean = sum(range(1, T + 1, stride)) / len(range(1, T + 1, stride))
+    t0 = int(round(t_mean - (n - 1) / 2))
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    params = synth.model_params(cfg, device=dev)
+    model = binding.Model(cfg, params, version=1)
+    e = synth.encoder_e(cfg, B, T, device=dev)
+    mk, mv = synth.encoder_memory(cfg, B, T, device=dev)
+    mem = binding.memory_view(mk, mv)
+    state = binding.State(model, B, T)
+    import_positions(model, state, cfg, params, [t0] * B, dev)
+    print(f"counters sample: states imported at t = {t0}", file=sys.stderr, flush=True)
+    if args.calibrate_copy:
+        calibration_copy(dev)
+    binding.profile_begin(state, 1 << binding.RLT_K_CROSS, 1 << 16, step_stride=1)
+    logits = torch.empty((B, cfg.vocab), dtype=torch.float32, device=dev)
+    for j in range(n):
+        binding.rlt_decoder_step(model, state, e[:, t0 - 1 + j].contiguous(), mem, logits=logits)
+    torch.cuda.synchronize()
+    ms, launches, nbytes = binding.profile_collect(state, binding.RLT_K_CROSS)
+    return {"mode": "counters-sample", "workload": wl.name, "positions": f"{t0}..{t0 + n - 1}",
+            "cross_launches": launches, "cross_algorithmic_bytes_per_launch": round(nbytes / launches),
+            "cross_avg_launch_us": round(ms / launches * 1e3, 2),
+            "calibration_copy_bytes": (256 << 20) if args.calibrate_copy else 0}
+
+
+def run_largebatch(args):
+    """256 sequences at ragged positions t_b ~ U{1..8192} (W = 1024): states
+    imported at t_b, one untimed step, then K batched steps timed with HIP
+    events around the whole pass, then K more with every launch timed per
+    kernel class (the GEMM time gives the MFMA utilisation).  Each pass moves
+    every sequence on by K positions (K << mean t, so the per-step work is
+    the same to within K / 4096)."""
+    import numpy as np
+    import torch
+    from recurrent_decode_step_amd import binding, synth
+    from recurrent_decode_step_amd.configs import LARGEBATCH
+    wl = LARGEBATCH
+    cfg, B = wl.model, wl.batch
+    K = args.steps or 5
+    n_steps = 2 * K + 1
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t_setup = time.time()
+    pos = synth.ragged_positions(B, wl.t_max)
+    cap = wl.t_max + n_steps
+    params = synth.model_params(cfg, device=dev)
+    model = binding.Model(cfg, params, version=1)
+    # e rows of the consumed positions only: stream (sequence b, start t_b)
+    e = torch.stack([synth.normal((n_steps, cfg.d_model), device=dev, seed=synth.SEED_E,
+                                  index=b, layer=int(pos[b]), round_bf16=True,
+                                  out_dtype=torch.bfloat16) for b in range(B)])
+    e_by_step = e.transpose(0, 1).contiguous()       # [step][B][d]
+    del e
+    mk, mv = synth.encoder_memory(cfg, B, cap, device=dev)
+    mem = binding.memory_view(mk, mv)
+    state = binding.State(model, B, cap)
+    import_positions(model, state, cfg, params, pos, dev)
+    print(f"largebatch: {B} states imported ({time.time() - t_setup:.0f} s)", file=sys.stderr,
+          flush=True)
+    logits = torch.empty((B, cfg.vocab), dtype=torch.float32, device=dev)
+    binding.rlt_decoder_step(model, state, e_by_step[0], mem, logits=logits)   # untimed
+    torch.cuda.synchronize()
+    classes = (binding.RLT_K_GEMM, binding.RLT_K_SWA, binding.RLT_K_CROSS)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    ev0.record(stream)
+    for j in range(1, K + 1):
+        binding.rlt_decoder_step(model, state, e_by_step[j], mem, logits=logits)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    binding.profile_begin(state, sum(1 << c for c in classes), 1 << 20, step_stride=1)
+    for j in range(K + 1, 2 * K + 1):
+        binding.rlt_decoder_step(model, state, e_by_step[j], mem, logits=logits)
+    torch.cuda.synchronize()
+    prof = {c: binding.profile_collect(state, c) for c in classes}
+    binding.profile_begin(state, 0, 0)
+    if not torch.isfinite(logits).all():
+        raise RuntimeError("non-finite logits")
+    gemm_ms = prof[binding.RLT_K_GEMM][0] / K
+    flops = gemm_flops_per_step(cfg, B)
+    bytes_step = sum(algorithmic_bytes_per_step(cfg, [int(t) + j for t in pos], 2)
+                     for j in range(1, K + 1)) / K
+    names = {binding.RLT_K_GEMM: "gemm", binding.RLT_K_SWA: "window_attention",
+             binding.RLT_K_CROSS: "cross_attention"}
+    return {
+        "metric": "decoder token-steps/sec at 1 GPU (48-layer, B=256); MFMA utilisation of the "
+                  "GEMM kernels",
+        "value": round(B * K / (ms / 1e3), 2), "unit": "token-steps/s", "n_gpus": 1, "steps": K,
+        "ms_per_step": round(ms / K, 4), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B,
+                   "positions": f"t_b ~ U{{1..{wl.t_max}}} (seed 3); timed steps consume "
+                                f"t_b+1..t_b+{K}, profiled steps t_b+{K + 1}..t_b+{2 * K}",
+                   "mean_t_b": round(float(np.mean(pos)), 1), "state": "imported synthetic"},
+        "mfma": {"bound": "mfma", "gemm_flops_per_step": flops,
+                 "gemm_ms_per_step": round(gemm_ms, 4),
+                 "achieved": round(flops / (gemm_ms / 1e3) / 1e12, 1),
+                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(flops / (gemm_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "step_roofline": {"bound": "hbm", "algorithmic_GB_per_step": round(bytes_step / 1e9, 3),
+                          "achieved": round(bytes_step / (ms / K / 1e3) / 1e9, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(bytes_step / (ms / K / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "breakdown_ms_per_step": {names[c]: round(prof[c][0] / K, 4) for c in classes},
+        "breakdown_GBps": {names[c]: round(prof[c][2] / (prof[c][0] / 1e3) / 1e9, 1)
+                           for c in classes},
+    }
+
+
+def run_longctx(args):
+    """d = 4096, B = 8, T = 32768.  The full run is estimated from 64-step
+    windows starting at imported states at t0 in {1, 4097, 8193, 16385, 24577,
+    32705}: per-step time tau(t) = a + b min(t, W) + c t is fitted to the
+    windows' per-step times (bytes per step are exactly affine in min(t, W)
+    and t) and summed over t = 1..32768."""
+    import numpy as np
+    import torch
+    from recurrent_decode_step_amd import binding, synth
+    from recurrent_decode_step_amd.configs import LONGCTX
+    wl = LONGCTX
+    cfg, B, T = wl.model, wl.batch, wl.steps
+    W = cfg.window
+    n = args.steps or 64
+    starts = [1, 4097, 8193, 16385, 24577, T - n + 1]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    params = synth.model_params(cfg, device=dev)
+    model = binding.Model(cfg, params, version=1)
+    mk, mv = synth.encoder_memory(cfg, B, T, device=dev)
+    mem = binding.memory_view(mk, mv)
+    state = binding.State(model, B, T)
+    rows = []
+    stream = torch.cuda.current_stream()
+    for t0 in starts:
+        import_positions(model, state, cfg, params, [t0] * B, dev, chunk=2)
+        e = torch.stack([synth.normal((n, cfg.d_model), device=dev, seed=synth.SEED_E, index=b,
+                                      layer=t0, round_bf16=True, out_dtype=torch.bfloat16)
+                         for b in range(B)])
+        if t0 == starts[0]:
+            binding.rlt_decoder_step(model, state, e[:, 0].contiguous(), mem)   # warm, untimed
+            import_positions(model, state, cfg, params, [t0] * B, dev, chunk=2)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        binding.rlt_run_sequence(model, state, e, mem, logits_mode=binding.RLT_LOGITS_LAST)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1)
+        t_mid = t0 + (n - 1) / 2
+        rows.append((t0, ms / n, float(np.mean([min(t, W) for t in range(t0, t0 + n)])), t_mid))
+        print(f"longctx: window t0={t0}: {ms / n:.3f} ms/step", file=sys.stderr, flush=True)
+    A = np.array([[1.0, r[2], r[3]] for r in rows])
+    y = np.array([r[1] for r in rows])
+    coef, *_ = np.linalg.lstsq(A, y, rcond=None)
+    ts = np.arange(1, T + 1, dtype=np.float64)
+    total_ms = float(np.sum(coef[0] + coef[1] * np.minimum(ts, W) + coef[2] * ts))
+    bytes_total = sum(algorithmic_bytes_per_step(cfg, [t] * B, 2) for t in range(1, T + 1, 64)) * 64
+    return {
+        "metric": "decoder token-steps/sec at 1 GPU (48-layer, d=4096, B=8, T=32768)",
+        "value": round(B * T / (total_ms / 1e3), 2), "unit": "token-steps/s", "n_gpus": 1,
+        "steps": T, "ms_per_step": round(total_ms / T, 4), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "method":
+                   f"{n}-step windows from imported states at t0 = {starts}; "
+                   "tau(t) = a + b min(t,W) + c t least-squares fit, summed over t = 1..32768"},
+        "windows_ms_per_step": {str(r[0]): round(r[1], 4) for r in rows},
+        "fit_ms": {"a": float(coef[0]), "b_per_window_pos": float(coef[1]),
+                   "c_per_memory_pos": float(coef[2])},
+        "step_roofline": {"bound": "hbm",
+                          "algorithmic_GB_per_step": round(bytes_total / T / 1e9, 3),
+                          "achieved": round(bytes_total / (total_ms / 1e3) / 1e9, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(bytes_total / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
 
 
 def main():
@@ -246,7 +482,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--workload", default="refdepth", choices=["refdepth"])
+    ap.add_argument("--workload", default="refdepth", choices=["refdepth", "largebatch", "longctx"])
+    ap.add_argument("--counters-sample", action="store_true",
+                    help="a few reference-depth steps at the sampled mean position (counter passes)")
+    ap.add_argument("--sample-steps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--progress", action="store_true",
@@ -261,7 +500,14 @@ def main():
               "communication, so N GPUs run N independent copies; run it with --gpus 1.",
               file=sys.stderr)
         raise SystemExit(2)
-    out = run_refdepth(args)
+    if args.counters_sample:
+        out = run_counters_sample(args)
+    elif args.workload == "largebatch":
+        out = run_largebatch(args)
+    elif args.workload == "longctx":
+        out = run_longctx(args)
+    else:
+        out = run_refdepth(args)
     print(json.dumps(out), flush=True)
 
 

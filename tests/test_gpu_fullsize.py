@@ -1,0 +1,109 @@
+"""Parity at the full sizes of the 48-layer workloads, on sampled sequences.
+
+Each case builds the full model and a full batch on the GPU, imports synthetic
+decoder states at ragged positions (so the window is full and the memory long
+without running thousands of steps), and runs ONE batched rlt_decoder_step over
+every slot: the kernels and launch shapes the benchmark times.  The oracle
+(bf16 emulation, fp32 arithmetic, one layer's weights converted at a time)
+then computes the same step for a few sampled sequences from the same states,
+and each sampled row must agree within relative L2 <= 2e-2 (the bf16 gate; the
+comparison starts from identical states, so it measures one step's kernels)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from recurrent_decode_step_amd import binding, synth
+from recurrent_decode_step_amd.configs import REFDEPTH, LARGEBATCH, LONGCTX
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+LAYER_KEYS = ("g1", "g2", "g3", "wq", "wk", "wv", "wo", "wqc", "woc", "w1", "w2")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def record(cfg, params, t, index):
+    r = synth.imported_state(cfg, int(t), device=DEV, index=index)
+    if int(t) == 1:
+        r["s"] = params["s_star"].clone()
+    return r
+
+
+def run_case(wl, positions, sample, chunk=8):
+    cfg = wl.model
+    B = len(positions)
+    cap = int(max(positions))
+    say(f"[fullsize] {wl.name}: B={B} positions min/max {min(positions)}/{max(positions)} "
+        f"sampled rows {sample}")
+    params = synth.model_params(cfg, device=DEV)
+    model = binding.Model(cfg, params, version=1)
+    mk, mv = synth.encoder_memory(cfg, B, cap, device=DEV)
+    state = binding.State(model, B, cap)
+    kept = {}
+    for b0 in range(0, B, chunk):
+        idx = list(range(b0, min(B, b0 + chunk)))
+        recs = [record(cfg, params, positions[b], b) for b in idx]
+        for b, r in zip(idx, recs):
+            if b in sample:
+                kept[b] = {"pos": r["pos"], "s": r["s"].float().cpu(), "K": r["K"].float().cpu(),
+                           "V": r["V"].float().cpu()}
+        snap = binding.build_snapshot(cfg, recs, version=1, device=DEV)
+        binding.rlt_state_import(model, state, snap, idx)
+        del snap, recs
+    e = torch.stack([synth.normal((cfg.d_model,), device=DEV, seed=synth.SEED_E, index=b,
+                                  layer=int(positions[b]), round_bf16=True,
+                                  out_dtype=torch.bfloat16) for b in range(B)])
+    got = binding.rlt_decoder_step(model, state, e, (mk, mv)).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.isfinite(got).all()
+    for b in range(B):
+        assert state.position(b) == positions[b]
+
+    # oracle for the sampled rows, one layer of fp32 weights at a time
+    small = {k: params[k].float().cpu() for k in ("s_star", "wg", "bg", "go", "wout")}
+    om = oracle.Model(params=small, precision="bf16", d_model=cfg.d_model, n_heads=cfg.n_heads,
+                      n_layers=cfg.n_layers, d_ffn=cfg.d_ffn, window=cfg.window,
+                      mem_groups=cfg.mem_groups, vocab=cfg.vocab, rms_eps=cfg.rms_eps,
+                      layer_source=lambda l: {k: params[k][l].float().cpu() for k in LAYER_KEYS})
+    states = [oracle.state_from_arrays(om, kept[b]["pos"], kept[b]["s"], kept[b]["K"],
+                                       kept[b]["V"]) for b in sample]
+    rows_mk = mk[:, sample].float().cpu()
+    rows_mv = mv[:, sample].float().cpu()
+    ref = oracle.decoder_step(om, states, e[sample].float().cpu(), rows_mk, rows_mv)
+    for j, b in enumerate(sample):
+        rel = float(np.linalg.norm(got[b] - ref[j]) / np.linalg.norm(ref[j]))
+        say(f"[fullsize] row {b} t={positions[b]} rel-L2 {rel:.2e}")
+        assert rel <= 2e-2, (b, positions[b], rel)
+
+
+def test_refdepth_full_batch_sampled_rows():
+    """48 layers, d = 2048, W = 512, B = 32: window not yet full, exactly full,
+    wrapped many times; memory from 1 to 2560 positions."""
+    wl = REFDEPTH
+    rng = np.random.default_rng([7, 0])
+    pos = [int(t) for t in rng.integers(1, wl.steps + 1, size=wl.batch)]
+    pos[0], pos[1], pos[2], pos[3] = 1, 512, 513, wl.steps
+    run_case(wl, pos, sample=[0, 1, 2, 3])
+
+
+def test_largebatch_full_batch_sampled_rows():
+    """B = 256 at t ~ U{1..8192} (the large-batch positions), W = 1024: four
+    column groups of 64 rows in every GEMM."""
+    wl = LARGEBATCH
+    pos = [int(t) for t in synth.ragged_positions(wl.batch, wl.t_max)]
+    order = np.argsort(pos)
+    sample = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1]), 255})
+    run_case(wl, pos, sample=sample)
+
+
+def test_longctx_full_batch_sampled_rows():
+    """d = 4096, 32 heads, F = 16384, W = 4096, B = 8, memory up to 32768."""
+    wl = LONGCTX
+    pos = [1, 4096, 4097, 300, 9000, 20000, 32768, 5000]
+    run_case(wl, pos, sample=[2, 6], chunk=2)
