@@ -77,6 +77,8 @@ GemmPlan gemm_plan(int N, int K, int dtype) {
 }
 
 // batch-column blocking of a launch over n rows: 16, 32 or 64 rows per group
+constexpr int kFillWorkgroups = 256;   // compute units of the part
+
 struct ColPlan {
   int ncb, groups;
 };
@@ -375,9 +377,22 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     a.K = g.K;
     a.KT = g.KT;
     Prof p(st, RLT_K_GEMM, s);
-    const int tpw = cp.ncb <= 2 ? g.tpw : 1;    // registers: two tiles only up to 32 rows
-    const hipError_t e2 =
-        launch_gemm(c.dtype, cp.ncb, tpw, act, epi, a, g.tiles, cp.groups, g.parts, s);
+    // narrower column groups until the launch has a workgroup per CU (results
+    // per row do not depend on the grouping)
+    ColPlan gc = cp;
+    int tpw = gc.ncb <= 2 ? g.tpw : 1;           // registers: two tiles only up to 32 rows
+    while (g.tpw == 1 && gc.ncb > 1 && (g.tiles / tpw) * gc.groups < kFillWorkgroups) {
+      gc.ncb /= 2;
+      gc.groups = cdiv(n, gc.ncb * 16);
+      tpw = gc.ncb <= 2 ? g.tpw : 1;
+    }
+    // large batches: the persistent kernel (same arithmetic, activations in
+    // registers, many tiles per workgroup)
+    hipError_t e2 = hipErrorInvalidValue;
+    if (c.dtype == RLT_DTYPE_BF16 && act == ACT_PLAIN && n > 64)
+      e2 = launch_gemm_persistent(c.dtype, epi, a, g.tiles, cdiv(n, 32), g.parts, s);
+    if (e2 == hipErrorInvalidValue)
+      e2 = launch_gemm(c.dtype, gc.ncb, tpw, act, epi, a, g.tiles, gc.groups, g.parts, s);
     if (e2 != hipSuccess) return hip_fail(e2, what);
     p.done((double)g.N * g.K * es + act_bytes + out_bytes);
     return RLT_OK;

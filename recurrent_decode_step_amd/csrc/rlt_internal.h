@@ -52,6 +52,9 @@ struct GemmArgs {
   const float *bias;                        // MERGE: b_g
   void *ring_k; void *ring_v;               // QKV: this layer's window cache [B][H][W][dh]
   int H, dh, W;
+  // workgroup -> (tile group, column group): tile_groups x col_groups
+  // workgroups on a 1-D grid; xcd_sets > 0 places them XCD-aware (see k_gemm)
+  int tile_groups, col_groups, xcd_sets;
 };
 
 struct AttnArgs {
@@ -71,6 +74,11 @@ hipError_t launch_pack_tiles(const void *src, int rows, int K, int64_t ld, int t
                              int tile_end, const PackedMat &dst, int dtype, hipStream_t s);
 hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const GemmArgs &a, int tiles,
                        int col_groups, int parts, hipStream_t s);
+// Large batches (bf16, plain activations, 32-row column groups): persistent
+// GEMM with the same arithmetic as launch_gemm; returns hipErrorInvalidValue
+// when the shape is not one it takes (the caller then uses launch_gemm).
+hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int tiles, int col_groups,
+                                  int parts, hipStream_t s);
 hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStream_t s);
 int attn_chunk_max(int dtype, int dh);
 hipError_t launch_state_init(float *s, int *pos, const float *s_star, int B, int d,

@@ -14,6 +14,7 @@
 #include "rlt_internal.h"
 
 #include <math.h>
+#include <algorithm>
 
 namespace rlt {
 
@@ -140,6 +141,15 @@ __global__ void k_pack(const T *__restrict__ src, int rows, int K, int64_t ld, i
 // 16-byte B-operand fragment of batch row i, k-step ks, lane group g sits at
 // fragment index ((i/16) * KT + ks) * 64 + (i%16) + 16 g, so one wavefront
 // load per k-step and 16-row column block is one contiguous KiB.
+// Weight fragment load: non-temporal when each weight tile is read once, so
+// the streamed weights do not push the activations out of L2; temporal when
+// several column groups read the tile from that L2.
+template <bool SHARED>
+__device__ __forceinline__ u32x4 wload_frag(const u32x4 *p) {
+  if constexpr (SHARED) return *p;
+  else return __builtin_nontemporal_load(p);
+}
+
 template <typename T>
 __device__ __forceinline__ size_t packed_off(int i, int k, int KT) {
   constexpr int EPL = Num<T>::EPL;
@@ -188,6 +198,89 @@ struct GemmRegs {
   static constexpr int AB = raw >= KSW ? KSW : (raw >= 16 ? 16 : (raw >= 8 ? 8 : (raw >= 4 ? 4 : 2)));
 };
 
+// Epilogue of one 16-row weight tile and one 16-column batch block: yv is the
+// reduced tile; lane holds features rbase..rbase+3 of batch column c (within
+// the column group starting at col0).  Called by a whole wavefront.
+// have_pre: x_pre / g_pre hold x and gamma_next of this lane (RESID).
+template <typename T, int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x4 yv, int tile, int c, int col0,
+                                              int ncols, float rinv, bool have_pre, f32x4 x_pre,
+                                              f32x4 g_pre, int lane) {
+  constexpr bool SCALED = EPI == EPI_QKV || EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_LOGITS;
+  const int rbase = tile * 16 + (lane >> 4) * 4;
+  const bool live = c < ncols && rbase < a.N;
+  const int i = col0 + c;
+  float y[4] = {yv[0], yv[1], yv[2], yv[3]};
+  if constexpr (SCALED) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) y[u] *= rinv;
+  }
+  if constexpr (EPI == EPI_RESID || EPI == EPI_MERGE) {
+    float ss = 0.f;
+    if (live) {
+      const int sl = slot_of(a, i);
+      float *xp = a.x + (size_t)i * a.d + rbase;
+      float xv[4];
+      if constexpr (EPI == EPI_RESID) {
+        const f32x4 old = have_pre ? x_pre : *reinterpret_cast<const f32x4 *>(xp);
+        xv[0] = old.x + y[0]; xv[1] = old.y + y[1]; xv[2] = old.z + y[2]; xv[3] = old.w + y[3];
+      } else {
+        // x = g * e + (1 - g) * s, g = sigmoid(W_g [e ; s] + b_g)
+        const float *sp = a.s_state + (size_t)sl * a.d + rbase;
+        const T *ep = static_cast<const T *>(a.act) + (size_t)i * a.ld_act + rbase;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float z = y[u] + a.bias[rbase + u];
+          const float g = 1.0f / (1.0f + __expf(-z));
+          float ev;
+          if constexpr (sizeof(T) == 2) ev = bf2f(reinterpret_cast<const bf16_t *>(ep)[u]);
+          else ev = reinterpret_cast<const float *>(ep)[u];
+          xv[u] = g * ev + (1.0f - g) * sp[u];
+        }
+      }
+      *reinterpret_cast<f32x4 *>(xp) = f32x4{xv[0], xv[1], xv[2], xv[3]};
+      if (a.s_out)
+        *reinterpret_cast<f32x4 *>(a.s_out + (size_t)sl * a.d + rbase) =
+            f32x4{xv[0], xv[1], xv[2], xv[3]};
+      // input of the next RMSNorm'd GEMM: x * gamma_next, storage type, packed
+      const f32x4 gn = (EPI == EPI_RESID && have_pre)
+                           ? g_pre : *reinterpret_cast<const f32x4 *>(a.gamma_next + rbase);
+      const float xg[4] = {xv[0] * gn.x, xv[1] * gn.y, xv[2] * gn.z, xv[3] * gn.w};
+      Num<T>::store4(static_cast<T *>(a.xg) + packed_off<T>(i, rbase, a.kt_out), xg);
+      ss = ((xv[0] * xv[0] + xv[1] * xv[1]) + xv[2] * xv[2]) + xv[3] * xv[3];
+    }
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if (lane < 16 && c < ncols) a.sumsq_out[(size_t)tile * a.part_ld + i] = ss;
+  } else if (live) {
+    if constexpr (EPI == EPI_QKV) {
+      const int d = a.d;
+      const int which = rbase / d;
+      const int f = rbase - which * d;
+      if (which == 0) {
+        Num<T>::store4(static_cast<T *>(a.out) + (size_t)i * a.ld_out + f, y);
+      } else {
+        const int h = f / a.dh, cc = f - h * a.dh;
+        const int sl = slot_of(a, i);
+        const int w = a.pos[sl] % a.W;          // entry of position t = pos + 1
+        T *ring = static_cast<T *>(which == 1 ? a.ring_k : a.ring_v);
+        Num<T>::store4(ring + (((size_t)sl * a.H + h) * a.W + w) * a.dh + cc, y);
+      }
+    } else if constexpr (EPI == EPI_STORE) {
+      Num<T>::store4(static_cast<T *>(a.out) + (size_t)i * a.ld_out + rbase, y);
+    } else if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) y[u] = gelu_erf(y[u]);
+      Num<T>::store4(static_cast<T *>(a.out) + packed_off<T>(i, rbase, a.kt_out), y);
+    } else if constexpr (EPI == EPI_LOGITS) {
+      float *lp = static_cast<float *>(a.out) + (size_t)i * a.ld_out + rbase;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (rbase + u < a.N) lp[u] = y[u];
+    }
+  }
+}
+
 template <typename T, int NCB, int ACT, int EPI, int KSW, int TPW>
 __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
   constexpr int COLS = NCB * 16;
@@ -200,8 +293,29 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
 
   const int NW = blockDim.x >> 6;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int tile0 = blockIdx.x * TPW;
-  const int col0 = blockIdx.y * COLS;
+  // Workgroup L runs on XCD L mod 8.  XCD-aware placement: the XCDs form
+  // xcd_sets sets, set s serving column groups s*gx .. s*gx+gx-1 and each
+  // XCD of a set a share of the tile groups; within an XCD the column groups
+  // of a tile group are consecutive, so the tile's weights are read from HBM
+  // once per set and the set's activations stay in that XCD's L2.
+  int tg, cg;
+  {
+    const int L = blockIdx.x;
+    if (a.xcd_sets > 0) {
+      const int NS = a.xcd_sets, xcd = L & 7, k = L >> 3;
+      const int gx = a.col_groups / NS, tgx = (a.tile_groups * NS) >> 3;
+      cg = (xcd % NS) * gx + k % gx;
+      tg = (xcd / NS) * tgx + k / gx;
+    } else {
+      tg = L % a.tile_groups;
+      cg = L / a.tile_groups;
+    }
+  }
+  const int tile0 = tg * TPW;
+  const int col0 = cg * COLS;
+  // 16-row column groups are used to split a batch over two or more groups
+  // (the host narrows the groups to fill the CUs): those share weight tiles
+  constexpr bool WSH = NCB == 1;
   const int ncols = min(COLS, a.n_rows - col0);
   const int ks0 = (wave * a.KT) / NW;
   const int nks = ((wave + 1) * a.KT) / NW - ks0;
@@ -212,7 +326,7 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
   int cbg[NCB], irow[NCB], slot[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
-    cbg[cb] = min((int)blockIdx.y * NCB + cb, (a.n_rows - 1) >> 4);
+    cbg[cb] = min(cg * NCB + cb, (a.n_rows - 1) >> 4);
     irow[cb] = col0 + min(cb * 16 + (lane & 15), ncols - 1);
     slot[cb] = (ACT == ACT_MERGE) ? slot_of(a, irow[cb]) : 0;
   }
@@ -232,9 +346,21 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < WB; ++j)
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) wf[t][j] = __builtin_nontemporal_load(wp[t] + (size_t)(b0 + j) * 64);
+      for (int t = 0; t < TPW; ++t) wf[t][j] = wload_frag<WSH>(wp[t] + (size_t)(b0 + j) * 64);
   };
   if (nks >= WB) issue_full(0);                    // first batch before anything else
+
+  // residual epilogue operands of this wavefront's first (tile, column block),
+  // loaded now so they are not waited for after the reduction
+  f32x4 x_pre = f32x4{0.f, 0.f, 0.f, 0.f}, g_pre = x_pre;
+  if constexpr (EPI == EPI_RESID) {
+    if (wave < TPW * NCB) {
+      const int rb = (tile0 + wave / NCB) * 16 + (lane >> 4) * 4;   // < N = d
+      const int c = min((wave % NCB) * 16 + (lane & 15), ncols - 1);
+      x_pre = *reinterpret_cast<const f32x4 *>(a.x + (size_t)(col0 + c) * a.d + rb);
+      g_pre = *reinterpret_cast<const f32x4 *>(a.gamma_next + rb);
+    }
+  }
 
   // 1/rms of every batch row from the producer's per-tile partial sums:
   // 8 groups of consecutive parts, each summed in order, then the groups in order.
@@ -277,7 +403,7 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
       // first is multiplied
       u32x4 wf2[WB];
 #pragma unroll
-      for (int j = 0; j < WB; ++j) wf2[j] = __builtin_nontemporal_load(wp[0] + (size_t)(WB + j) * 64);
+      for (int j = 0; j < WB; ++j) wf2[j] = wload_frag<WSH>(wp[0] + (size_t)(WB + j) * 64);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         if (h2 == 1) {
@@ -331,7 +457,7 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
       for (int j = 0; j < WB; ++j)
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
-          wf[t][j] = __builtin_nontemporal_load(wp[t] + (size_t)min(b0 + j, nks - 1) * 64);
+          wf[t][j] = wload_frag<WSH>(wp[t] + (size_t)min(b0 + j, nks - 1) * 64);
 #pragma unroll
       for (int j = 0; j < WB; ++j) {
         if (j < nb) {
@@ -358,90 +484,201 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
     for (int cb = 0; cb < NCB; ++cb) s_acc[((wave * TPW + t) * NCB + cb) * 64 + lane] = acc[t][cb];
   __syncthreads();
 
-  // ---- epilogue: lane holds features rbase..rbase+3 of batch column cb*16 + cl
-  const int cl = lane & 15;
+  // ---- epilogue, one (tile, column block) per wavefront
   for (int q = wave; q < TPW * NCB; q += NW) {
     const int t = q / NCB, cb = q - (q / NCB) * NCB;
     f32x4 yv = s_acc[(t * NCB + cb) * 64 + lane];
     for (int w = 1; w < NW; ++w) yv += s_acc[((w * TPW + t) * NCB + cb) * 64 + lane];
-    const int tile = tile0 + t;
-    const int rbase = tile * 16 + (lane >> 4) * 4;
-    const int c = cb * 16 + cl;
-    const bool live = c < ncols && rbase < a.N;
-    const int i = col0 + c;
-    float y[4] = {yv[0], yv[1], yv[2], yv[3]};
-    if constexpr (SCALED) {
-      const float r = s_rinv[c];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) y[u] *= r;
-    }
-    if constexpr (EPI == EPI_RESID || EPI == EPI_MERGE) {
-      float ss = 0.f;
-      if (live) {
-        const int sl = slot_of(a, i);
-        float *xp = a.x + (size_t)i * a.d + rbase;
-        float xv[4];
-        if constexpr (EPI == EPI_RESID) {
-          const f32x4 old = *reinterpret_cast<const f32x4 *>(xp);
-          xv[0] = old.x + y[0]; xv[1] = old.y + y[1]; xv[2] = old.z + y[2]; xv[3] = old.w + y[3];
-        } else {
-          // x = g * e + (1 - g) * s, g = sigmoid(W_g [e ; s] + b_g)
-          const float *sp = a.s_state + (size_t)sl * a.d + rbase;
-          const T *ep = static_cast<const T *>(a.act) + (size_t)i * a.ld_act + rbase;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float z = y[u] + a.bias[rbase + u];
-            const float g = 1.0f / (1.0f + __expf(-z));
-            float ev;
-            if constexpr (sizeof(T) == 2) ev = bf2f(reinterpret_cast<const bf16_t *>(ep)[u]);
-            else ev = reinterpret_cast<const float *>(ep)[u];
-            xv[u] = g * ev + (1.0f - g) * sp[u];
-          }
-        }
-        *reinterpret_cast<f32x4 *>(xp) = f32x4{xv[0], xv[1], xv[2], xv[3]};
-        if (a.s_out)
-          *reinterpret_cast<f32x4 *>(a.s_out + (size_t)sl * a.d + rbase) =
-              f32x4{xv[0], xv[1], xv[2], xv[3]};
-        // input of the next RMSNorm'd GEMM: x * gamma_next, storage type, packed
-        const f32x4 gn = *reinterpret_cast<const f32x4 *>(a.gamma_next + rbase);
-        const float xg[4] = {xv[0] * gn.x, xv[1] * gn.y, xv[2] * gn.z, xv[3] * gn.w};
-        Num<T>::store4(static_cast<T *>(a.xg) + packed_off<T>(i, rbase, a.kt_out), xg);
-        ss = ((xv[0] * xv[0] + xv[1] * xv[1]) + xv[2] * xv[2]) + xv[3] * xv[3];
-      }
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      if (lane < 16 && c < ncols) a.sumsq_out[(size_t)tile * a.part_ld + i] = ss;
-    } else if (live) {
-      if constexpr (EPI == EPI_QKV) {
-        const int d = a.d;
-        const int which = rbase / d;
-        const int f = rbase - which * d;
-        if (which == 0) {
-          Num<T>::store4(static_cast<T *>(a.out) + (size_t)i * a.ld_out + f, y);
-        } else {
-          const int h = f / a.dh, cc = f - h * a.dh;
-          const int sl = slot_of(a, i);
-          const int w = a.pos[sl] % a.W;          // entry of position t = pos + 1
-          T *ring = static_cast<T *>(which == 1 ? a.ring_k : a.ring_v);
-          Num<T>::store4(ring + (((size_t)sl * a.H + h) * a.W + w) * a.dh + cc, y);
-        }
-      } else if constexpr (EPI == EPI_STORE) {
-        Num<T>::store4(static_cast<T *>(a.out) + (size_t)i * a.ld_out + rbase, y);
-      } else if constexpr (EPI == EPI_GELU) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) y[u] = gelu_erf(y[u]);
-        Num<T>::store4(static_cast<T *>(a.out) + packed_off<T>(i, rbase, a.kt_out), y);
-      } else if constexpr (EPI == EPI_LOGITS) {
-        float *lp = static_cast<float *>(a.out) + (size_t)i * a.ld_out + rbase;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (rbase + u < a.N) lp[u] = y[u];
-      }
-    }
+    const int c = cb * 16 + (lane & 15);
+    gemm_epilogue<T, EPI>(a, yv, tile0 + t, c, col0, ncols, SCALED ? s_rinv[c] : 1.f, q == wave,
+                          x_pre, g_pre, lane);
   }
 
   // the last kernel of a step advances the positions (no reader of pos runs in it)
-  if (a.advance_pos && blockIdx.x == 0 && blockIdx.y == 0) {
+  if (a.advance_pos && tg == 0 && cg == 0) {
+    for (int i = tid; i < a.n_rows; i += blockDim.x) a.pos[slot_of(a, i)] += 1;
+  }
+}
+
+// Large batches: a persistent form of k_gemm for 32-row column groups with
+// the same arithmetic (the same K parts, one wavefront each, each an MFMA
+// chain in k order from zero, partial tiles added in part order), so a row's
+// result does not depend on which of the two kernels ran.  A workgroup keeps
+// activations in registers and runs several weight tiles:
+//  - parts of at most SC k-steps: the wavefront loads its activation
+//    fragments once and then only streams weights, the next tile's in flight
+//    while the current one is multiplied;
+//  - longer parts: SC-k-step activation chunks, each used by two tiles whose
+//    accumulators stay live across the chunks.
+// Placement: workgroup w runs on XCD x = w mod 8 and serves the tiles
+// t = x (mod 8); the workgroups of one XCD cover every column group of the
+// same tiles in step, so a tile's weights come from HBM once and from the
+// XCD's L2 for the other column groups.
+template <typename T, int NCB, int EPI, bool SHORT>
+__global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
+  constexpr int SC = 8;
+  constexpr int COLS = NCB * 16;
+  constexpr bool SCALED = EPI == EPI_QKV || EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_LOGITS;
+  __shared__ f32x4 s_acc[2][kMaxParts][NCB][64];
+  __shared__ float s_grp[8][COLS];
+  __shared__ float s_rinv[COLS];
+
+  const int NW = blockDim.x >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = a.col_groups;
+  const int wg = blockIdx.x, x = wg & 7, m = wg >> 3;
+  const int cg = m % G, l = m / G, L8 = ((int)gridDim.x >> 3) / G;
+  const int nx = a.tile_groups > x ? (a.tile_groups - x + 7) / 8 : 0;   // tiles = x (mod 8)
+  const int nt = nx > l ? (nx - l + L8 - 1) / L8 : 0;                     // this workgroup's
+  auto tile_of = [&](int i) { return x + 8 * (l + L8 * i); };
+  const int col0 = cg * COLS;
+  const int ncols = min(COLS, a.n_rows - col0);
+  const int ks0 = (wave * a.KT) / NW;
+  const int nks = ((wave + 1) * a.KT) / NW - ks0;
+
+  int cbg[NCB], irow[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    cbg[cb] = min(cg * NCB + cb, (a.n_rows - 1) >> 4);
+    irow[cb] = col0 + min(cb * 16 + (lane & 15), ncols - 1);
+  }
+  auto wload = [&](u32x4 *dst, int tile, int c0, int nc) {
+    const u32x4 *wp = static_cast<const u32x4 *>(a.wp) + ((size_t)tile * a.KT + ks0 + c0) * 64 + lane;
+#pragma unroll
+    for (int j = 0; j < SC; ++j) dst[j] = wp[(size_t)min(j, nc - 1) * 64];   // shared via L2
+  };
+  u32x4 av[SC][NCB];
+  auto aload = [&](int c0, int nc) {
+#pragma unroll
+    for (int j = 0; j < SC; ++j)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        av[j][cb] = load_b<T, ACT_PLAIN>(a, cbg[cb], irow[cb], 0, ks0 + c0 + min(j, nc - 1), lane);
+  };
+  auto chain = [&](f32x4 *acc, const u32x4 *w, int nc) {
+#pragma unroll
+    for (int j = 0; j < SC; ++j)
+      if (j < nc) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma_step(w[j], av[j][cb], acc[cb], T());
+      }
+  };
+  u32x4 wa[SC], wb[SC], wc[SC];
+  if (nt > 0) {
+    aload(0, min(SC, nks));
+    wload(wa, tile_of(0), 0, min(SC, nks));
+  }
+
+  if constexpr (SCALED) {
+    const int P = a.n_parts;
+    const int per = (P + 7) / 8;
+    for (int q = tid; q < COLS * 8; q += blockDim.x) {
+      const int c = q % COLS, g = q / COLS;
+      const float *src = a.sumsq + col0 + min(c, ncols - 1);
+      const int p0 = g * per, p1 = min(P, p0 + per);
+      float ss = 0.f;
+      for (int p = p0; p < p1; p += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = src[(size_t)min(p + u, P - 1) * a.part_ld];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) ss += (p + u < p1) ? v[u] : 0.f;
+      }
+      s_grp[g][c] = ss;
+    }
+    __syncthreads();
+    for (int c = tid; c < COLS; c += blockDim.x) {
+      float ss = s_grp[0][c];
+#pragma unroll
+      for (int g = 1; g < 8; ++g) ss += s_grp[g][c];
+      s_rinv[c] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+    }
+    __syncthreads();
+  }
+
+  // partial tiles of all parts through LDS (buffer `buf`, alternating from
+  // tile to tile), added in part order; column block cb is finished by
+  // wavefront cb mod NW (one wavefront: both blocks).  A buffer is rewritten
+  // two tiles later, after every wavefront has passed the next tile's barrier.
+  static_assert(NCB <= 2, "column blocks per wavefront");
+  auto reduce_store = [&](int buf, const f32x4 *acc, int tile, bool pre, f32x4 xp, f32x4 gp) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) s_acc[buf][wave][cb][lane] = acc[cb];
+    __syncthreads();
+    if (wave < NCB) {
+      f32x4 y = s_acc[buf][0][wave][lane];
+      for (int w = 1; w < NW; ++w) y += s_acc[buf][w][wave][lane];
+      const int c = wave * 16 + (lane & 15);
+      gemm_epilogue<T, EPI>(a, y, tile, c, col0, ncols, SCALED ? s_rinv[c] : 1.f, pre, xp, gp, lane);
+    }
+    if (wave + NW < NCB) {
+      f32x4 y = s_acc[buf][0][wave + NW][lane];
+      for (int w = 1; w < NW; ++w) y += s_acc[buf][w][wave + NW][lane];
+      const int c = (wave + NW) * 16 + (lane & 15);
+      gemm_epilogue<T, EPI>(a, y, tile, c, col0, ncols, SCALED ? s_rinv[c] : 1.f, false, xp, gp, lane);
+    }
+  };
+  auto prefetch_x = [&](int tile, f32x4 &xp, f32x4 &gp) {
+    if constexpr (EPI == EPI_RESID) {
+      if (wave < NCB) {
+        const int rb = tile * 16 + (lane >> 4) * 4;
+        const int c = min(wave * 16 + (lane & 15), ncols - 1);
+        xp = *reinterpret_cast<const f32x4 *>(a.x + (size_t)(col0 + c) * a.d + rb);
+        gp = *reinterpret_cast<const f32x4 *>(a.gamma_next + rb);
+      }
+    }
+  };
+
+  if constexpr (SHORT) {
+    // parts of at most SC k-steps (the launcher checks): one tile after
+    // another, the activations stay in registers
+    // three weight buffers: tile i multiplies while tiles i+1 and i+2 load
+    auto one = [&](int i, u32x4 *wcur, u32x4 *wnext2) {
+      const int tile = tile_of(i);
+      if (i + 2 < nt) wload(wnext2, tile_of(i + 2), 0, nks);
+      f32x4 xp = f32x4{0.f, 0.f, 0.f, 0.f}, gp = xp;
+      prefetch_x(tile, xp, gp);
+      f32x4 acc[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      chain(acc, wcur, nks);
+      reduce_store(i & 1, acc, tile, true, xp, gp);
+    };
+    if (nt > 1) wload(wb, tile_of(1), 0, nks);
+    for (int i = 0; i < nt; i += 3) {
+      one(i, wa, wc);
+      if (i + 1 < nt) one(i + 1, wb, wa);
+      if (i + 2 < nt) one(i + 2, wc, wb);
+    }
+  } else {
+    // chunks of SC k-steps outer, two tiles inner (wa: first tile, wb: second)
+    const int nch = (nks + SC - 1) / SC;
+    for (int i0 = 0; i0 < nt; i0 += 2) {
+      const bool two = i0 + 1 < nt;
+      f32x4 acc0[NCB], acc1[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc0[cb] = acc1[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (i0 > 0) {
+        aload(0, min(SC, nks));
+        wload(wa, tile_of(i0), 0, min(SC, nks));
+      }
+      for (int ch = 0; ch < nch; ++ch) {
+        const int c0 = ch * SC, nc = min(SC, nks - c0);
+        if (ch > 0) aload(c0, nc);
+        if (two) wload(wb, tile_of(i0 + 1), c0, nc);
+        chain(acc0, wa, nc);
+        if (ch + 1 < nch) wload(wa, tile_of(i0), c0 + SC, min(SC, nks - c0 - SC));
+        if (two) chain(acc1, wb, nc);
+      }
+      const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+      reduce_store(0, acc0, tile_of(i0), false, z, z);
+      if (two) reduce_store(1, acc1, tile_of(i0 + 1), false, z, z);
+      __syncthreads();   // both buffers free before the next pair
+    }
+  }
+
+  if (a.advance_pos && wg == 0) {
+    __syncthreads();
     for (int i = tid; i < a.n_rows; i += blockDim.x) a.pos[slot_of(a, i)] += 1;
   }
 }
@@ -765,21 +1002,33 @@ int gemm_ksw(int dtype, int ks_per_part) {
 
 hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const GemmArgs &a, int tiles,
                        int col_groups, int parts, hipStream_t s) {
-  if (parts < 1 || parts > kMaxParts || (tpw != 1 && tpw != 2) || tiles % tpw)
+  if (parts < 1 || parts > kMaxParts || (tpw != 1 && tpw != 2) || tiles % tpw || col_groups < 1)
     return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(tiles / tpw), (unsigned)col_groups);
+  GemmArgs b = a;
+  b.tile_groups = tiles / tpw;
+  b.col_groups = col_groups;
+  // XCD sets: as few as keep each XCD's column groups' activations within
+  // half an L2 (2 MiB); used when the grid splits evenly over the 8 XCDs
+  const size_t act_group = (size_t)ncb * 16 * a.K * (dtype == RLT_DTYPE_BF16 ? 2 : 4);
+  int ns = 1;
+  while (ns < 8 && col_groups % (2 * ns) == 0 && (size_t)(col_groups / ns) * act_group > ((size_t)2 << 20))
+    ns *= 2;
+  const bool even = ((size_t)b.tile_groups * col_groups) % 8 == 0 && col_groups % ns == 0 &&
+                    (b.tile_groups * ns) % 8 == 0;
+  b.xcd_sets = even ? ns : 0;
+  const dim3 grid((unsigned)(b.tile_groups * col_groups));
   const int threads = parts * 64;
   const int ksw = gemm_ksw(dtype, a.KT / parts);
   if (dtype != RLT_DTYPE_BF16) {
     if (tpw != 1) return hipErrorInvalidValue;
-    return gemm_dispatch_ncb<float, 8, 1>(ncb, act, epi, a, grid, threads, s);
+    return gemm_dispatch_ncb<float, 8, 1>(ncb, act, epi, b, grid, threads, s);
   }
   if (tpw == 2) {
-    if (ksw == 16) return gemm_dispatch_ncb<bf16_t, 16, 2>(ncb, act, epi, a, grid, threads, s);
-    return gemm_dispatch_ncb<bf16_t, 8, 2>(ncb, act, epi, a, grid, threads, s);
+    if (ksw == 16) return gemm_dispatch_ncb<bf16_t, 16, 2>(ncb, act, epi, b, grid, threads, s);
+    return gemm_dispatch_ncb<bf16_t, 8, 2>(ncb, act, epi, b, grid, threads, s);
   }
-  if (ksw == 16) return gemm_dispatch_ncb<bf16_t, 16, 1>(ncb, act, epi, a, grid, threads, s);
-  return gemm_dispatch_ncb<bf16_t, 8, 1>(ncb, act, epi, a, grid, threads, s);
+  if (ksw == 16) return gemm_dispatch_ncb<bf16_t, 16, 1>(ncb, act, epi, b, grid, threads, s);
+  return gemm_dispatch_ncb<bf16_t, 8, 1>(ncb, act, epi, b, grid, threads, s);
 }
 
 template <typename T, int KIND>
@@ -793,6 +1042,38 @@ static hipError_t attn_dispatch(int dh, const AttnArgs &a, int n_rows, hipStream
     case 256: k_attn<T, 256, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int tiles, int col_groups,
+                                  int parts, hipStream_t s) {
+  constexpr int kWorkgroups = 256;               // one per CU
+  if (dtype != RLT_DTYPE_BF16 || parts < 1 || parts > kMaxParts || col_groups < 1 ||
+      8 * col_groups > kWorkgroups || tiles < 1)
+    return hipErrorInvalidValue;
+  GemmArgs b = a;
+  b.tile_groups = tiles;
+  b.col_groups = col_groups;
+  b.xcd_sets = 0;
+  const int per_xcd = (tiles + 7) / 8;
+  const int l8 = std::max(1, std::min(kWorkgroups / (8 * col_groups), per_xcd));
+  const dim3 grid((unsigned)(8 * col_groups * l8));
+  const int threads = parts * 64;
+  const bool short_k = (a.KT + parts - 1) / parts <= 8;
+#define RLT_GP(E)                                                             \
+  case E:                                                                     \
+    if (short_k) k_gemm_p<bf16_t, 2, E, true><<<grid, threads, 0, s>>>(b);     \
+    else k_gemm_p<bf16_t, 2, E, false><<<grid, threads, 0, s>>>(b);           \
+    break;
+  switch (epi) {
+    RLT_GP(EPI_QKV)
+    RLT_GP(EPI_STORE)
+    RLT_GP(EPI_RESID)
+    RLT_GP(EPI_GELU)
+    RLT_GP(EPI_LOGITS)
+    default: return hipErrorInvalidValue;
+  }
+#undef RLT_GP
   return hipGetLastError();
 }
 

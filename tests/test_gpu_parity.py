@@ -239,6 +239,30 @@ def test_batch_composition_is_bitwise_invisible(dtype):
     assert torch.equal(out, full)
 
 
+@pytest.mark.parametrize("shape", [dict(n_layers=2, mem_groups=2),
+                                   dict(d_model=256, n_heads=2, d_ffn=4096, vocab=300, n_layers=2,
+                                        mem_groups=1)])
+def test_large_batch_kernels_match_small_batch_bitwise(shape):
+    """Steps over more than 64 rows run the persistent GEMM (activations held
+    in registers, many tiles per workgroup; d_ffn = 4096 also takes its
+    chunked long-K form); the same slots stepped in groups of at most 64 rows
+    run the per-tile GEMM.  The arithmetic is the same, so the logits are
+    bitwise equal."""
+    cfg = BF16_SMALL.with_(**shape)
+    B, T = 100, 4
+    rig = Rig(cfg, B, T, attn_chunk=4)
+    say(f"[large batch] shape={shape} B={B}")
+    full = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, rig.mem).cpu()
+    assert torch.isfinite(full).all()
+    st = rig.state()
+    groups = [list(range(0, 64)), list(range(64, 100))]
+    out = torch.empty_like(full)
+    for j in range(T):
+        for g in groups:
+            out[g, j] = binding.rlt_decoder_step(rig.model, st, rig.ed[g, j], rig.mem, slots=g).cpu()
+    assert torch.equal(out, full)
+
+
 def test_memory_causality_bitwise():
     """Memory positions after t never change logits_t; position t does."""
     cfg = tiny_cfg()
