@@ -702,27 +702,66 @@ struct AttnShape {
   static constexpr int CH = U * RPB;               // positions per chunk
 };
 
-template <typename T, int DH, int UU>
+// Reduction over lane-index bits [LO, HI) of a wavefront (sum, or max) of a
+// value that is already the same on all lanes differing only in bits below
+// LO: within 16-lane rows by DPP lane permutations (quad swaps, then the
+// half-row and row mirrors, each pairing lanes that differ in the next bit
+// once the lower bits are uniform), across rows by lane shuffles.  Each step
+// is v op partner, so the lanes of a group end with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int LO, int HI, bool MAX>
+__device__ __forceinline__ float lane_reduce(float v) {
+  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+  if constexpr (LO <= 0 && HI > 0) v = op(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  if constexpr (LO <= 1 && HI > 1) v = op(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  if constexpr (LO <= 2 && HI > 2) v = op(v, dpp_f<0x141>(v));   // row_half_mirror
+  if constexpr (LO <= 3 && HI > 3) v = op(v, dpp_f<0x140>(v));   // row_mirror
+  if constexpr (LO <= 4 && HI > 4) v = op(v, __shfl_xor(v, 16));
+  if constexpr (LO <= 5 && HI > 5) v = op(v, __shfl_xor(v, 32));
+  return v;
+}
+template <int N> struct Log2 { static constexpr int v = 1 + Log2<N / 2>::v; };
+template <> struct Log2<1> { static constexpr int v = 0; };
+
+// FULL: the chunk lies inside [0, len) and has CH positions, so no load is
+// clamped and no score masked; otherwise loads past the chunk or the end
+// re-read the last valid position and are masked out of the scores (every
+// load is unconditional either way).
+template <typename T, int DH, int UU, bool FULL>
 __device__ __forceinline__ void attn_load(const T *kp, const T *vp, int64_t s_pos, int base, int len,
                                           int ch, int my, u32x4 *kr, u32x4 *vr) {
-  // unconditional loads: positions past the chunk or the end re-read the last
-  // valid one and are masked out of the scores
   using S = AttnShape<T, DH, UU>;
+  if constexpr (FULL) {
+    const size_t step = (size_t)S::RPB * s_pos;
+    const T *kq = kp + (size_t)(base + my) * s_pos;
+    const T *vq = vp + (size_t)(base + my) * s_pos;
 #pragma unroll
-  for (int u = 0; u < S::U; ++u) {
-    const int pc = min(u * S::RPB + my, ch - 1);
-    const int p = min(base + pc, len - 1);
-    kr[u] = *reinterpret_cast<const u32x4 *>(kp + (size_t)p * s_pos);
-    vr[u] = *reinterpret_cast<const u32x4 *>(vp + (size_t)p * s_pos);
+    for (int u = 0; u < S::U; ++u) {
+      kr[u] = *reinterpret_cast<const u32x4 *>(kq);
+      vr[u] = *reinterpret_cast<const u32x4 *>(vq);
+      kq += step;
+      vq += step;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+      const int pc = min(u * S::RPB + my, ch - 1);
+      const int p = min(base + pc, len - 1);
+      kr[u] = *reinterpret_cast<const u32x4 *>(kp + (size_t)p * s_pos);
+      vr[u] = *reinterpret_cast<const u32x4 *>(vp + (size_t)p * s_pos);
+    }
   }
 }
 
-template <typename T, int DH, int UU>
+template <typename T, int DH, int UU, bool FULL>
 __device__ __forceinline__ void attn_chunk(const float *qf, const u32x4 *kr, const u32x4 *vr,
                                            int base, int len, int ch, int my, float &m, float &l,
                                            float *o) {
   using S = AttnShape<T, DH, UU>;
-  constexpr int EPL = S::EPL, LPR = S::LPR, U = S::U;
+  constexpr int EPL = S::EPL, LB = Log2<S::LPR>::v, U = S::U;
   float sc[U];
   float cmax = -INFINITY;
 #pragma unroll
@@ -732,23 +771,25 @@ __device__ __forceinline__ void attn_chunk(const float *qf, const u32x4 *kr, con
     float dsum = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) dsum = fmaf(qf[e], kf[e], dsum);
-#pragma unroll
-    for (int w = LPR / 2; w >= 1; w >>= 1) dsum += __shfl_xor(dsum, w);
-    const int pc = u * S::RPB + my;
-    const bool in = pc < ch && base + pc < len;
-    sc[u] = in ? dsum : -INFINITY;
+    dsum = lane_reduce<0, LB, false>(dsum);        // over the position's LPR lanes
+    if constexpr (FULL) {
+      sc[u] = dsum;
+    } else {
+      const int pc = u * S::RPB + my;
+      sc[u] = (pc < ch && base + pc < len) ? dsum : -INFINITY;
+    }
     cmax = fmaxf(cmax, sc[u]);
   }
-  cmax = wave_max(cmax);
+  cmax = lane_reduce<0, 6, true>(cmax);
   const float mnew = fmaxf(m, cmax);
-  const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mnew);   // o, l are still 0 then
+  const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew);   // o, l are 0 then
   float psum = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] *= alpha;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const bool in = sc[u] != -INFINITY;            // positions past the end weigh 0
-    const float pj = in ? exp2f(sc[u] - mnew) : 0.f;
+    const bool in = FULL || sc[u] != -INFINITY;    // positions past the end weigh 0
+    const float pj = in ? __builtin_amdgcn_exp2f(sc[u] - mnew) : 0.f;
     psum += pj;
     if (in) {
       float vf[EPL];
@@ -758,8 +799,7 @@ __device__ __forceinline__ void attn_chunk(const float *qf, const u32x4 *kr, con
     }
   }
   // each position's weight is held by its LPR lanes: sum over position rows only
-#pragma unroll
-  for (int w = LPR; w < 64; w <<= 1) psum += __shfl_xor(psum, w);
+  psum = lane_reduce<LB, 6, false>(psum);
   l = l * alpha + psum;
   m = mnew;
 }
@@ -767,7 +807,8 @@ __device__ __forceinline__ void attn_chunk(const float *qf, const u32x4 *kr, con
 // KIND 0: sliding window over the decoder cache; 1: encoder memory (the same
 // code, two symbols so profiles keep them apart)
 template <typename T, int DH, int KIND, int UU = 0>
-__global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void k_attn(const AttnArgs a) {
   using S = AttnShape<T, DH, UU>;
   constexpr int EPL = S::EPL, LPR = S::LPR, RPW = S::RPW, U = S::U;
   __shared__ float s_o[4][DH];
@@ -791,7 +832,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
   for (int u = 0; u < U; ++u) {
     ka[u] = u32x4{0u, 0u, 0u, 0u}; va[u] = ka[u]; kb2[u] = ka[u]; vb2[u] = ka[u];
   }
-  attn_load<T, DH, UU>(kp, vp, a.s_pos, 0, len, ch, my, ka, va);   // first chunk in flight first
+  attn_load<T, DH, UU, false>(kp, vp, a.s_pos, 0, len, ch, my, ka, va);   // first chunk in flight first
 
   float qf[EPL];
   Num<T>::unpack(*reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.q) + (size_t)i * a.d +
@@ -803,15 +844,28 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(const AttnArgs a) {
   float m = -INFINITY, l = 0.f, o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  for (int c0 = 0; c0 < len; c0 += 2 * ch) {
-    if (c0 + ch < len) attn_load<T, DH, UU>(kp, vp, a.s_pos, c0 + ch, len, ch, my, kb2, vb2);
-    attn_chunk<T, DH, UU>(qf, ka, va, c0, len, ch, my, m, l, o);
+  // chunk j covers positions [j ch, (j+1) ch), double-buffered (even: ka/va,
+  // odd: kb2/vb2).  While the chunks loaded and processed are whole and inside
+  // [0, len) they take the unclamped form; the last few take the general one.
+  const int nfull = ch == S::CH ? len / ch : 0;
+  int j = 0;
+  for (; j + 2 < nfull; j += 2) {
+    attn_load<T, DH, UU, true>(kp, vp, a.s_pos, (j + 1) * ch, len, ch, my, kb2, vb2);
+    attn_chunk<T, DH, UU, true>(qf, ka, va, j * ch, len, ch, my, m, l, o);
+    attn_load<T, DH, UU, true>(kp, vp, a.s_pos, (j + 2) * ch, len, ch, my, ka, va);
+    attn_chunk<T, DH, UU, true>(qf, kb2, vb2, (j + 1) * ch, len, ch, my, m, l, o);
+  }
+  for (int c0 = j * ch; c0 < len; c0 += 2 * ch) {
+    if (c0 + ch < len) attn_load<T, DH, UU, false>(kp, vp, a.s_pos, c0 + ch, len, ch, my, kb2, vb2);
+    attn_chunk<T, DH, UU, false>(qf, ka, va, c0, len, ch, my, m, l, o);
     if (c0 + ch >= len) break;
-    if (c0 + 2 * ch < len) attn_load<T, DH, UU>(kp, vp, a.s_pos, c0 + 2 * ch, len, ch, my, ka, va);
-    attn_chunk<T, DH, UU>(qf, kb2, vb2, c0 + ch, len, ch, my, m, l, o);
+    if (c0 + 2 * ch < len) attn_load<T, DH, UU, false>(kp, vp, a.s_pos, c0 + 2 * ch, len, ch, my, ka, va);
+    attn_chunk<T, DH, UU, false>(qf, kb2, vb2, c0 + ch, len, ch, my, m, l, o);
   }
 
   // rows of the wavefront, then the 4 wavefronts in order
+  // (lanes of one row hold different dims here: plain xor shuffles, which keep
+  // the low lane bits, not the mirror permutations of lane_reduce)
 #pragma unroll
   for (int w = LPR; w < 64; w <<= 1) {
 #pragma unroll
