@@ -85,9 +85,12 @@ enum { RLT_LOGITS_ALL = 0, RLT_LOGITS_LAST = 1, RLT_LOGITS_NONE = 2 };
  * 16, 32, 64, 128, 256; d_model and d_ffn must be multiples of 32;
  * mem_groups is 1 (one memory read by every layer) or n_layers (layer l reads
  * group l) [Princeton, architecture paragraph].  window >= 1 counts the
- * current token.  attn_chunk: positions per attention work item (0 = the
- * library default 256); it fixes the order of the softmax sums and so is part
- * of the model's numerics. */
+ * current token.  attn_chunk: positions an attention workgroup loads per step
+ * of its double-buffered loop, spread over its 4 wavefronts, each of which
+ * keeps its own running softmax (0 = the largest the kernel takes for the
+ * head size: 128 positions for bf16 with head_dim 128; larger values are cut
+ * to that).  It fixes the order of the softmax sums and so is part of the
+ * model's numerics: a state and its model must agree on it. */
 typedef struct {
   int32_t vocab, d_model, n_heads, head_dim, n_layers, d_ffn, window, mem_groups, dtype;
   float rms_eps;
@@ -146,10 +149,12 @@ rlt_status rlt_model_create(const rlt_config *cfg, const rlt_params *src,
 void rlt_model_destroy(rlt_model *m);       /* frees the host handle only */
 
 /* ------------------------------------------------------------------ state */
-/* Bytes for a state of `batch` slots whose positions stay <= max_tokens:
- * s [B][d] fp32, positions [B] int32, the window cache K,V [L][B][H][W][dh]
- * in the model dtype (a ring: position p lives in entry (p-1) mod W), and the
- * per-step scratch the kernels use. */
+/* Bytes for a state of `batch` slots whose positions stay <= max_tokens
+ * (max_tokens is checked by the calls, it does not change the size): s [B][d]
+ * fp32, positions [B] int32, the window cache K,V [L][B][H][W][dh] in the
+ * model dtype (a ring: position p lives in entry (p-1) mod W), and the
+ * per-step scratch the kernels use (residual stream, normalised GEMM inputs,
+ * attention outputs, FFN hidden layer, sum-of-squares partials). */
 size_t rlt_state_bytes(const rlt_config *cfg, int32_t batch, int32_t max_tokens);
 
 /* Lay out a state in dev_buf and set every slot to H_0 = (s*, empty cache),
