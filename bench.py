@@ -22,6 +22,8 @@ Other measurements (each prints its own JSON line; not the default):
   --workload longctx      d = 4096, 8 sequences, T = 32768: 64-step windows
                           from imported states at six start positions, per-step
                           time fitted as a + b min(t, W) + c t and summed
+  --score                 replay scoring at the reference depth: every next
+                          token's log-probability, read before it is consumed
   --counters-sample       reference-depth model, all sequences at the run's
                           mean sampled position: a few steps for hardware
                           counter passes (with --calibrate-copy)
@@ -324,6 +326,55 @@ def run_counters_sample(args):
             "calibration_copy_bytes": (256 << 20) if args.calibrate_copy else 0}
 
 
+def run_score(args):
+    """Replay scoring at the reference depth: all 32 sequences rebuilt from H_0
+    over 2560 recorded tokens (realized tokens uniform in the vocabulary), the
+    log-probability of every next token read from each step's logits before
+    it is consumed; one rlt_score_sequence call, timed with HIP events."""
+    import numpy as np
+    import torch
+    from recurrent_decode_step_amd import binding, synth
+    from recurrent_decode_step_amd.configs import REFDEPTH
+    wl = REFDEPTH
+    cfg, B, T_total = wl.model, wl.batch, wl.steps
+    K = T_total if args.steps is None else args.steps
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    params = synth.model_params(cfg, device=dev)
+    model = binding.Model(cfg, params, version=1)
+    e = synth.encoder_e(cfg, B, T_total, device=dev)
+    mk, mv = synth.encoder_memory(cfg, B, T_total, device=dev)
+    mem = binding.memory_view(mk, mv)
+    rng = np.random.default_rng([synth.SEED_POS, 1, 0, 0])
+    tokens = torch.from_numpy(rng.integers(0, cfg.vocab, size=(B, K)).astype(np.int32)).to(dev)
+    out = torch.empty((B, K), dtype=torch.float32, device=dev)
+    state = binding.State(model, B, T_total)
+    if args.warmup > 0:
+        binding.rlt_score_sequence(model, state, e[:, :args.warmup], mem, tokens[:, :args.warmup])
+        binding.rlt_state_reset(model, state, list(range(B)))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    binding.rlt_score_sequence(model, state, e[:, :K], mem, tokens, out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    if not torch.isfinite(out).all():
+        raise RuntimeError("non-finite scores")
+    return {
+        "metric": "replay-scored decoder token-steps/sec at 1 GPU (48-layer, B=32)",
+        "value": round(B * K / (ms / 1e3), 2), "unit": "token-steps/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms / K, 4), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + ", replay scoring", "batch": B, "positions": f"1..{K}",
+                   "tokens": "uniform in the vocabulary (seed 3)",
+                   "output": "log-probability of each realized next token, fp32"},
+        "mean_logprob": round(float(out.double().mean()), 4),
+    }
+
+
 def run_largebatch(args):
     """256 sequences at ragged positions t_b ~ U{1..8192} (W = 1024): states
     imported at t_b, one untimed step, then K batched steps timed with HIP
@@ -483,6 +534,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default="refdepth", choices=["refdepth", "largebatch", "longctx"])
+    ap.add_argument("--score", action="store_true",
+                    help="replay scoring at the reference depth (log-probability of each next token)")
     ap.add_argument("--counters-sample", action="store_true",
                     help="a few reference-depth steps at the sampled mean position (counter passes)")
     ap.add_argument("--sample-steps", type=int, default=4)
@@ -502,6 +555,8 @@ def main():
         raise SystemExit(2)
     if args.counters_sample:
         out = run_counters_sample(args)
+    elif args.score:
+        out = run_score(args)
     elif args.workload == "largebatch":
         out = run_largebatch(args)
     elif args.workload == "longctx":

@@ -188,6 +188,23 @@ rlt_status rlt_run_sequence(const rlt_model *m, rlt_state *st, int32_t T,
                             const void *dev_e, const rlt_memory *mem, float *dev_logits,
                             int32_t logits_mode, void *stream);
 
+/* Replay scoring [Tutorial, "Current-Policy Reinforcement Learning Replay":
+ * rebuild the states from the sequence start under the current weights,
+ * evaluate each action from the preceding state, then consume it once].
+ * T steps for all B slots exactly as rlt_run_sequence (no reset; the state
+ * ends bitwise where rlt_run_sequence would leave it), and for each step t
+ * the log-probability of the realized next token under that step's logits:
+ *   dev_logprob[b][t] = log softmax(logits of slot b after consuming e_t)[dev_tokens[b][t]]
+ * dev_e       [B][T][d] model dtype
+ * dev_tokens  [B][T] int32: the token slot b consumes at step t + 1; a token
+ *             < 0 is not scored (0 written), a token >= vocab gives NaN
+ * dev_logprob [B][T] fp32 out
+ * The logits are formed in the state's scratch and not returned; the log
+ * softmax is taken in fp32 with the maximum taken out first. */
+rlt_status rlt_score_sequence(const rlt_model *m, rlt_state *st, int32_t T, const void *dev_e,
+                              const rlt_memory *mem, const int32_t *dev_tokens,
+                              float *dev_logprob, void *stream);
+
 /* Host mirror of a slot's position (tokens consumed); -1 on a bad argument.
  * Does not synchronise. */
 int32_t rlt_state_position(const rlt_state *st, int32_t slot);

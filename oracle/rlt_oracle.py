@@ -286,3 +286,33 @@ def run_sequence(model: Model, states, e, mem_k, mem_v, mem_index=None, steps=No
     for j in range(steps):
         out[:, j] = decoder_step(model, states, e[:, j], mem_k, mem_v, mem_index, trace)
     return out
+
+
+def token_log_prob(logits, token):
+    """log p(token) under softmax(logits), in float64: logits[token] minus the
+    log of the sum of exp(logits), the maximum taken out first.  A token < 0
+    is not scored (0.0)."""
+    if token < 0:
+        return 0.0
+    z = np.asarray(logits, dtype=np.float64)
+    zmax = float(np.max(z))
+    return float(z[token] - zmax - math.log(float(np.sum(np.exp(z - zmax)))))
+
+
+def score_sequence(model: Model, states, e, mem_k, mem_v, tokens, mem_index=None):
+    """Replay scoring of a recorded sequence under the model as it stands:
+    step t consumes token t, and the log-probability of the realized next
+    token tokens[i][t] is read from that step's logits, before the token is
+    consumed by step t + 1 [Tutorial, "Current-Policy Reinforcement Learning
+    Replay": rebuild the states from the start, evaluate an action from the
+    preceding state, then consume it once].  e [n][T][d], tokens [n][T] int
+    (< 0: not scored) -> log-probabilities [n][T] float64."""
+    e = np.asarray(e) if not hasattr(e, "detach") else e
+    tok = np.asarray(tokens)
+    n, T = tok.shape
+    out = np.zeros((n, T), dtype=np.float64)
+    for j in range(T):
+        lg = decoder_step(model, states, e[:, j], mem_k, mem_v, mem_index)
+        for i in range(n):
+            out[i, j] = token_log_prob(lg[i], int(tok[i, j]))
+    return out

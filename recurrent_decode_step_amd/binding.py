@@ -25,6 +25,7 @@ RLT_K_SETUP, RLT_K_GEMM, RLT_K_SWA, RLT_K_CROSS = 0, 1, 2, 3
 EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_bytes",
             "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",
             "rlt_state_destroy", "rlt_state_reset", "rlt_decoder_step", "rlt_run_sequence",
+            "rlt_score_sequence",
             "rlt_state_position", "rlt_snapshot_bytes", "rlt_state_export", "rlt_state_import",
             "rlt_profile_begin", "rlt_profile_collect")
 
@@ -80,6 +81,7 @@ def load_library(path: str = LIB_PATH):
         "rlt_state_reset": (i32, [vp, vp, i32, P(i32), vp]),
         "rlt_decoder_step": (i32, [vp, vp, i32, P(i32), vp, P(rlt_memory), vp, vp]),
         "rlt_run_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, i32, vp]),
+        "rlt_score_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, vp, vp]),
         "rlt_state_position": (i32, [vp, i32]),
         "rlt_snapshot_bytes": (sz, [P(rlt_config), i32]),
         "rlt_state_export": (i32, [vp, vp, i32, P(i32), vp, vp]),
@@ -223,6 +225,25 @@ def rlt_run_sequence(model: Model, state: State, e: torch.Tensor, memory,
                                 logits.data_ptr() if logits is not None else None, logits_mode,
                                 _stream(stream)))
     return logits
+
+
+def rlt_score_sequence(model: Model, state: State, e: torch.Tensor, memory, tokens: torch.Tensor,
+                       out=None, stream=None) -> torch.Tensor:
+    """Replay scoring over T steps of all B slots: e [B][T][d], tokens [B][T]
+    int32 (the token consumed at step t + 1; < 0: not scored) -> log-probs
+    [B][T] fp32."""
+    lib = load_library()
+    B, T = e.shape[0], e.shape[1]
+    e = e.contiguous()
+    tokens = tokens.to(dtype=torch.int32).contiguous()
+    if tokens.shape != (B, T):
+        raise ValueError("tokens must be [B][T]")
+    if out is None:
+        out = torch.empty((B, T), dtype=torch.float32, device=e.device)
+    mem = memory if isinstance(memory, rlt_memory) else memory_view(*memory)
+    _check(lib.rlt_score_sequence(model.handle, state.handle, T, e.data_ptr(), C.byref(mem),
+                                  tokens.data_ptr(), out.data_ptr(), _stream(stream)))
+    return out
 
 
 def rlt_state_reset(model: Model, state: State, slots, stream=None):

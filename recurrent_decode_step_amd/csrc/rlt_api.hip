@@ -151,6 +151,7 @@ struct rlt_state {
   int *slots_dev;
   float *x, *sumsq;
   char *xg, *qbuf, *obuf, *hbuf;
+  float *lscratch;           // [B][V] fp32 logits of a scored step
   std::vector<int> host_pos;
   std::vector<int> staged;   // slot list currently in slots_dev (empty: none)
   // profiling
@@ -235,6 +236,7 @@ size_t state_layout(const rlt_config &c, rlt_state *st, void *base, int B) {
   st->qbuf = ar.take<char>((size_t)B * d * es);
   st->obuf = ar.take<char>(rows16 * d * es);
   st->hbuf = ar.take<char>(rows16 * c.d_ffn * es);
+  st->lscratch = ar.take<float>((size_t)B * c.vocab * 4);
   return align256(ar.off);
 }
 
@@ -799,6 +801,41 @@ rlt_status rlt_run_sequence(const rlt_model *m, rlt_state *st, int32_t T, const 
     if ((rs = enqueue_step(m, st, st->B, true, nullptr, ek, (int64_t)T * d, mem, lk, ld, s)) !=
         RLT_OK)
       return rs;
+  }
+  return ok();
+}
+
+rlt_status rlt_score_sequence(const rlt_model *m, rlt_state *st, int32_t T, const void *dev_e,
+                              const rlt_memory *mem, const int32_t *dev_tokens, float *dev_logprob,
+                              void *stream) {
+  rlt_status rs;
+  if ((rs = check_state(m, st)) != RLT_OK) return rs;
+  if (T < 1) return fail(RLT_ERR_INVALID_ARG, "T must be >= 1");
+  if (!dev_e) return fail(RLT_ERR_INVALID_ARG, "dev_e is NULL");
+  if (!dev_tokens) return fail(RLT_ERR_INVALID_ARG, "dev_tokens is NULL");
+  if (!dev_logprob) return fail(RLT_ERR_INVALID_ARG, "dev_logprob is NULL");
+  if ((rs = check_memory(m, mem, st->B - 1)) != RLT_OK) return rs;
+  if ((rs = check_positions(st, mem, st->B, nullptr, T)) != RLT_OK) return rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = m->cfg.d_model, V = m->cfg.vocab, es = m->esize;
+  for (int k = 0; k < T; ++k) {
+    // the step's logits go to the state's scratch; the score of the token
+    // that step k+1 will consume is read from them before it is consumed
+    const void *ek = static_cast<const char *>(dev_e) + (size_t)k * d * es;
+    if ((rs = enqueue_step(m, st, st->B, true, nullptr, ek, (int64_t)T * d, mem, st->lscratch, V,
+                           s)) != RLT_OK)
+      return rs;
+    ScoreArgs sa;
+    sa.logits = st->lscratch;
+    sa.ld = V;
+    sa.tokens = dev_tokens + k;
+    sa.ld_tok = T;
+    sa.out = dev_logprob + k;
+    sa.ld_out = T;
+    sa.V = V;
+    const hipError_t e = launch_score(sa, st->B, s);
+    if (e != hipSuccess) return hip_fail(e, "score launch");
   }
   return ok();
 }

@@ -57,6 +57,13 @@ struct GemmArgs {
   int tile_groups, col_groups, xcd_sets;
 };
 
+struct ScoreArgs {
+  const float *logits; int64_t ld;          // [n][ld] fp32 logits of the step
+  const int32_t *tokens; int64_t ld_tok;    // realized next token of row i at tokens[i * ld_tok]
+  float *out; int64_t ld_out;               // log-probability of row i at out[i * ld_out]
+  int V;
+};
+
 struct AttnArgs {
   const void *q; void *out;                 // q [n][d] row-major; out fragment-packed
   int kt_out;                               // KT of the packed output (d / k-step)
@@ -79,6 +86,8 @@ hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const Gemm
 // when the shape is not one it takes (the caller then uses launch_gemm).
 hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int tiles, int col_groups,
                                   int parts, hipStream_t s);
+// log softmax of each row's logits at its realized token (one workgroup per row)
+hipError_t launch_score(const ScoreArgs &a, int n_rows, hipStream_t s);
 hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStream_t s);
 int attn_chunk_max(int dtype, int dh);
 hipError_t launch_state_init(float *s, int *pos, const float *s_star, int B, int d,

@@ -903,6 +903,65 @@ void k_attn(const AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- scoring
+// Log-probability of the realized next token under a step's logits, for
+// replay scoring: z[tok] - max(z) - log(sum exp(z - max(z))).  One workgroup
+// per row; every thread takes a fixed strided subset of the vocabulary, the
+// wavefronts combine by a lane tree and then in wavefront order, so the
+// result does not depend on anything but the row's logits.  A token < 0 is
+// not scored (0), one >= V gives NaN.
+constexpr int kScoreThreads = 1024;
+__global__ __launch_bounds__(kScoreThreads) void k_score(const ScoreArgs a) {
+  constexpr int NWV = kScoreThreads / 64;
+  __shared__ float s_red[NWV];
+  const int i = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float *z = a.logits + (size_t)i * a.ld;
+  // 16-byte loads when rows allow it; each thread's elements in a fixed order
+  const bool vec = (a.V & 3) == 0 && (a.ld & 3) == 0;
+  const f32x4 *z4 = reinterpret_cast<const f32x4 *>(z);
+  const int V4 = a.V >> 2;
+  float mx = -INFINITY;
+  if (vec) {
+#pragma unroll 4
+    for (int j = tid; j < V4; j += kScoreThreads) {
+      const f32x4 q = z4[j];
+      mx = fmaxf(mx, fmaxf(fmaxf(q.x, q.y), fmaxf(q.z, q.w)));
+    }
+  } else {
+    for (int v = tid; v < a.V; v += kScoreThreads) mx = fmaxf(mx, z[v]);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  mx = s_red[0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) mx = fmaxf(mx, s_red[w]);
+  __syncthreads();
+  float sum = 0.f;
+  if (vec) {
+#pragma unroll 4
+    for (int j = tid; j < V4; j += kScoreThreads) {
+      const f32x4 q = z4[j];
+      sum += ((expf(q.x - mx) + expf(q.y - mx)) + expf(q.z - mx)) + expf(q.w - mx);
+    }
+  } else {
+    for (int v = tid; v < a.V; v += kScoreThreads) sum += expf(z[v] - mx);
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) s_red[wave] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    float tot = s_red[0];
+    for (int w = 1; w < NWV; ++w) tot += s_red[w];
+    const int tok = a.tokens[(size_t)i * a.ld_tok];
+    float lp;
+    if (tok < 0) lp = 0.f;
+    else if (tok >= a.V) lp = __int_as_float(0x7fc00000);
+    else lp = (z[tok] - mx) - logf(tot);
+    a.out[(size_t)i * a.ld_out] = lp;
+  }
+}
+
 // ---------------------------------------------------------------- state
 __global__ void k_state_init(float *s, int *pos, const float *s_star, int d, const int *slots,
                              int n) {
@@ -1128,6 +1187,12 @@ hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int til
     default: return hipErrorInvalidValue;
   }
 #undef RLT_GP
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const ScoreArgs &a, int n_rows, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  k_score<<<dim3((unsigned)n_rows), kScoreThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

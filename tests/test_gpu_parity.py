@@ -418,3 +418,56 @@ def test_position_past_memory_is_rejected_without_side_effects():
     after = binding.rlt_state_export(rig.model, st, [0, 1])
     assert torch.equal(before, after)
     assert st.position(0) == 4
+
+
+# ------------------------------------------------------------ replay scoring
+def test_score_sequence_f32_matches_oracle():
+    """Replay scores (log-probability of the realized next token, read before
+    it is consumed) against the oracle's, fp32.  Bound: |d logprob| <= 2e-4,
+    twice the logits gate (the token's logit and the log-sum-exp each carry at
+    most the logits' error)."""
+    cfg = tiny_cfg()
+    B, T = 4, 20
+    rig = Rig(cfg, B, T, attn_chunk=3)
+    tokens = torch.from_numpy(np.random.default_rng(11).integers(0, cfg.vocab, size=(B, T))).int()
+    tokens[:, ::5] = -1
+    say("[score f32]")
+    got = binding.rlt_score_sequence(rig.model, rig.state(), rig.ed, rig.mem, tokens.to(DEV)).cpu().numpy()
+    m = rig.oracle_model()
+    ref = oracle.score_sequence(m, [oracle.initial_state(m) for _ in range(B)], rig.e, rig.mk, rig.mv,
+                                tokens.numpy())
+    err = float(np.max(np.abs(got - ref)))
+    say(f"  max|d logprob| = {err:.3e}")
+    assert err <= 2e-4
+    assert np.all(got[:, ::5] == 0.0)
+
+
+def test_score_sequence_reads_its_own_logits_and_leaves_the_run_state():
+    """bf16: the scores equal the float64 log softmax of the logits the same
+    steps produce through rlt_run_sequence (bitwise the same head), a token
+    >= vocab scores NaN, and the state after scoring continues bitwise like
+    the state after rlt_run_sequence."""
+    cfg = BF16_SMALL.with_(n_layers=2, mem_groups=2)
+    B, T = 8, 6
+    rig = Rig(cfg, B, T + 1)
+    tokens = torch.from_numpy(np.random.default_rng(12).integers(0, cfg.vocab, size=(B, T))).int()
+    tokens[0, 2] = -1
+    tokens[1, 3] = cfg.vocab
+    say("[score bf16]")
+    st_a, st_b = rig.state(), rig.state()
+    logits = binding.rlt_run_sequence(rig.model, st_a, rig.ed[:, :T], rig.mem).cpu().double()
+    got = binding.rlt_score_sequence(rig.model, st_b, rig.ed[:, :T], rig.mem,
+                                     tokens.to(DEV)).cpu().double()
+    lsm = torch.log_softmax(logits, dim=-1)
+    for b in range(B):
+        for t in range(T):
+            tk = int(tokens[b, t])
+            if tk < 0:
+                assert got[b, t] == 0.0
+            elif tk >= cfg.vocab:
+                assert torch.isnan(got[b, t])
+            else:
+                assert abs(float(got[b, t]) - float(lsm[b, t, tk])) <= 1e-5, (b, t)
+    nxt_a = binding.rlt_decoder_step(rig.model, st_a, rig.ed[:, T], rig.mem).cpu()
+    nxt_b = binding.rlt_decoder_step(rig.model, st_b, rig.ed[:, T], rig.mem).cpu()
+    assert torch.equal(nxt_a, nxt_b)

@@ -473,3 +473,58 @@ def test_bf16_emulation_is_close_to_exact():
     b, _ = run_oracle(mbf, e, mk, mv)
     rel = np.linalg.norm(b - a) / np.linalg.norm(a)
     assert 1e-5 < rel < 3e-2, rel
+
+
+# ------------------------------------------------- replay scoring (next row)
+def test_token_log_prob_closed_forms():
+    """log softmax at the token: two logits 0 and ln 3 give ln(1/4) and ln(3/4);
+    V equal logits give -ln V; a shift of every logit by 1000 changes nothing
+    (the maximum is taken out before exp); a negative token is not scored."""
+    z = np.array([0.0, math.log(3.0)])
+    assert abs(oracle.token_log_prob(z, 0) - math.log(0.25)) < 1e-15
+    assert abs(oracle.token_log_prob(z, 1) - math.log(0.75)) < 1e-15
+    assert abs(oracle.token_log_prob(np.full(37, 2.5), 11) + math.log(37.0)) < 1e-14
+    rng = np.random.default_rng(5)
+    w = rng.normal(size=50)
+    assert abs(oracle.token_log_prob(w + 1000.0, 7) - oracle.token_log_prob(w, 7)) < 1e-9
+    assert oracle.token_log_prob(w, -1) == 0.0
+
+
+def test_token_log_probs_normalise():
+    """exp of the log-probabilities of every token sums to one."""
+    rng = np.random.default_rng(6)
+    z = rng.normal(scale=3.0, size=200)
+    total = sum(math.exp(oracle.token_log_prob(z, v)) for v in range(200))
+    assert abs(total - 1.0) < 1e-12
+
+
+def test_score_uses_the_logits_before_the_token_is_consumed():
+    """Column t of the replay score is read from the logits of step t (after
+    consuming token t, before token t+1) [Tutorial, "Current-Policy
+    Reinforcement Learning Replay"]: it equals log softmax of run_sequence's
+    logits at column t, and not at t-1 or t+1.  Unscored tokens (< 0) leave
+    the other columns unchanged."""
+    cfg = tiny_cfg()
+    model, _ = make_model(cfg)
+    B, T = 3, 10
+    e, mk, mv = inputs(cfg, B, T)
+    tokens = np.random.default_rng(7).integers(0, cfg.vocab, size=(B, T))
+    logits, _ = run_oracle(model, e, mk, mv)
+    got = oracle.score_sequence(model, [oracle.initial_state(model) for _ in range(B)],
+                                e, mk, mv, tokens)
+    for i in range(B):
+        for t in range(T):
+            z = logits[i, t].astype(np.float64)
+            ref = z[tokens[i, t]] - z.max() - math.log(np.exp(z - z.max()).sum())
+            assert abs(got[i, t] - ref) < 1e-12
+    shifted = np.array([[oracle.token_log_prob(logits[i, t - 1], tokens[i, t]) for t in range(1, T)]
+                        for i in range(B)])
+    assert np.max(np.abs(shifted - got[:, 1:])) > 1e-3
+    masked = tokens.copy()
+    masked[:, ::3] = -1
+    got2 = oracle.score_sequence(model, [oracle.initial_state(model) for _ in range(B)],
+                                 e, mk, mv, masked)
+    assert np.all(got2[:, ::3] == 0.0)
+    keep = np.ones(T, bool)
+    keep[::3] = False
+    assert np.array_equal(got2[:, keep], got[:, keep])
