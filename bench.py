@@ -19,6 +19,8 @@ Other measurements (each prints its own JSON line; not the default):
   --workload largebatch   256 sequences at ragged positions t ~ U{1..8192},
                           W = 1024: K consecutive batched steps from imported
                           states, MFMA utilisation of the GEMM kernels
+  --workload tiny|small   the tiny fp32 and small bf16 configs, whole runs
+                          (launch-bound; reported, not targeted)
   --workload longctx      d = 4096, 8 sequences, T = 32768: 64-step windows
                           from imported states at six start positions, per-step
                           time fitted as a + b min(t, W) + c t and summed
@@ -135,7 +137,8 @@ def openblas_threads():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(cfg, params_gpu, e_gpu, mk_gpu, mv_gpu, t0, budget_s=15.0, max_steps=16):
+def cpu_baseline(cfg, params_gpu, e_gpu, mk_gpu, mv_gpu, t0, budget_s=15.0, max_steps=16,
+                 where="the run's mean position"):
     """The oracle (fp32 NumPy, as it stands) on the host: all sequences of the
     workload batched, consuming tokens t0, t0+1, ... from synthetic states
     imported at t0 (the run's mean position), until the time budget is spent."""
@@ -170,8 +173,8 @@ def cpu_baseline(cfg, params_gpu, e_gpu, mk_gpu, mv_gpu, t0, budget_s=15.0, max_
     el = time.time() - t_start
     return {"value": B * done / el, "unit": "token-steps/s", "cores": openblas_threads(),
             "kind": "oracle",
-            "sample": f"{B} sequences x {done} steps (t = {t0}..{t0 + done - 1}, the run's mean "
-                      f"position) from synthetic states imported at t = {t0}, NumPy fp32 oracle, "
+            "sample": f"{B} sequences x {done} steps (t = {t0}..{t0 + done - 1}, {where}) "
+                      f"from synthetic states imported at t = {t0}, NumPy fp32 oracle, "
                       f"weights read once per step for the batch ({el:.1f} s timed, "
                       f"{prep:.1f} s state and input preparation untimed)"}
 
@@ -375,6 +378,59 @@ def run_score(args):
     }
 
 
+def run_full_sequence(args, wl):
+    """A whole-run workload (tiny fp32 or small bf16): all sequences from H_0
+    through T steps in one rlt_run_sequence call, logits of every step, timed
+    with HIP events; the median of 5 repeats (state reset in between); the
+    CPU oracle on the first steps of the same run beside it."""
+    import statistics
+    import torch
+    from recurrent_decode_step_amd import binding, synth
+    cfg, B, T = wl.model, wl.batch, wl.steps
+    es = 2 if cfg.dtype == 1 else 4
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    params = synth.model_params(cfg, device=dev)
+    model = binding.Model(cfg, params, version=1)
+    e = synth.encoder_e(cfg, B, T, device=dev)
+    mk, mv = synth.encoder_memory(cfg, B, T, device=dev)
+    mem = binding.memory_view(mk, mv)
+    state = binding.State(model, B, T)
+    logits = torch.empty((B, T, cfg.vocab), dtype=torch.float32, device=dev)
+    binding.rlt_run_sequence(model, state, e[:, :min(4, T)], mem)       # warm-up
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(5):
+        binding.rlt_state_reset(model, state, list(range(B)))
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        binding.rlt_run_sequence(model, state, e, mem, logits=logits)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1))
+    ms = statistics.median(times)
+    bytes_run = sum(algorithmic_bytes_per_step(cfg, [k + 1] * B, es) for k in range(T))
+    out = {
+        "metric": f"decoder token-steps/sec at 1 GPU ({wl.name.split(' ')[0]})",
+        "value": round(B * T / (ms / 1e3), 2), "unit": "token-steps/s", "n_gpus": 1, "steps": T,
+        "ms_per_step": round(ms / T, 4), "higher_is_better": True,
+        "dtype": "f32" if es == 4 else "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "positions": f"1..{T}",
+                   "repeats": "median of 5 full runs", "logits": "every step, fp32"},
+        "step_roofline": {"bound": "hbm", "algorithmic_GB_per_step": round(bytes_run / T / 1e9, 5),
+                          "achieved": round(bytes_run / (ms / 1e3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s",
+                          "frac": round(bytes_run / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "note": "launch-bound at this size; reported, not targeted"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, params, e, mk, mv, t0=1, budget_s=args.cpu_budget,
+                                           max_steps=T, where="from the start of the same run")
+    return out
+
+
 def run_largebatch(args):
     """256 sequences at ragged positions t_b ~ U{1..8192} (W = 1024): states
     imported at t_b, one untimed step, then K batched steps timed with HIP
@@ -533,7 +589,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--workload", default="refdepth", choices=["refdepth", "largebatch", "longctx"])
+    ap.add_argument("--workload", default="refdepth",
+                    choices=["refdepth", "largebatch", "longctx", "tiny", "small"])
     ap.add_argument("--score", action="store_true",
                     help="replay scoring at the reference depth (log-probability of each next token)")
     ap.add_argument("--counters-sample", action="store_true",
@@ -561,6 +618,9 @@ def main():
         out = run_largebatch(args)
     elif args.workload == "longctx":
         out = run_longctx(args)
+    elif args.workload in ("tiny", "small"):
+        from recurrent_decode_step_amd.configs import TINY, SMALL
+        out = run_full_sequence(args, TINY if args.workload == "tiny" else SMALL)
     else:
         out = run_refdepth(args)
     print(json.dumps(out), flush=True)
