@@ -24,6 +24,8 @@ Other measurements (each prints its own JSON line; not the default):
   --workload longctx      d = 4096, 8 sequences, T = 32768: 64-step windows
                           from imported states at six start positions, per-step
                           time fitted as a + b min(t, W) + c t and summed
+  --generate              generation at the reference depth: 512 tokens sampled
+                          (temperature 1, top-k 50) after the 2048-token prompt
   --score                 replay scoring at the reference depth: every next
                           token's log-probability, read before it is consumed
   --counters-sample       reference-depth model, all sequences at the run's
@@ -431,6 +433,55 @@ def run_full_sequence(args, wl):
     return out
 
 
+def run_generate(args):
+    """Generation at the reference depth: the 2048-token prompt of all 32
+    sequences through rlt_run_sequence (last logits only, untimed), then 512
+    tokens generated by rlt_generate (temperature 1, top-k 50; stand-in
+    encoder tables write the memory entries of the generated positions),
+    timed with HIP events around the generation."""
+    import torch
+    from recurrent_decode_step_amd import binding, synth
+    from recurrent_decode_step_amd.configs import REFDEPTH
+    wl = REFDEPTH
+    cfg, B, T, P = wl.model, wl.batch, wl.steps, wl.prompt
+    n = T - P if args.steps is None else min(args.steps, T - P)
+    temperature, top_k = 1.0, 50
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    params = synth.model_params(cfg, device=dev)
+    model = binding.Model(cfg, params, version=1)
+    e = synth.encoder_e(cfg, B, P, device=dev)
+    mk, mv = synth.encoder_memory(cfg, B, T, device=dev)
+    te, tk, tv = synth.encoder_tables(cfg, device=dev)
+    u = synth.uniforms((B, n), device=dev)
+    state = binding.State(model, B, T)
+    logits0 = binding.rlt_run_sequence(model, state, e, (mk, mv), logits_mode=binding.RLT_LOGITS_LAST)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    tok, lp, _ = binding.rlt_generate(model, state, logits0, te, tk, tv, (mk, mv), temperature,
+                                      top_k, u)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    if not torch.isfinite(lp).all():
+        raise RuntimeError("non-finite log-probabilities")
+    return {
+        "metric": "generated token-steps/sec at 1 GPU (48-layer, B=32, after a 2048-token prompt)",
+        "value": round(B * n / (ms / 1e3), 2), "unit": "token-steps/s", "n_gpus": 1, "steps": n,
+        "ms_per_step": round(ms / n, 4), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name + ", generation", "batch": B,
+                   "positions": f"{P + 1}..{P + n}",
+                   "sampling": f"temperature {temperature}, top-k {top_k}, uniforms seed 5",
+                   "encoder": "stand-in tables (e and memory rows of the sampled token)"},
+        "mean_behaviour_logprob": round(float(lp.double().mean()), 4),
+        "distinct_tokens": int(torch.unique(tok).numel()),
+    }
+
+
 def run_largebatch(args):
     """256 sequences at ragged positions t_b ~ U{1..8192} (W = 1024): states
     imported at t_b, one untimed step, then K batched steps timed with HIP
@@ -591,6 +642,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default="refdepth",
                     choices=["refdepth", "largebatch", "longctx", "tiny", "small"])
+    ap.add_argument("--generate", action="store_true",
+                    help="generation at the reference depth after the 2048-token prompt")
     ap.add_argument("--score", action="store_true",
                     help="replay scoring at the reference depth (log-probability of each next token)")
     ap.add_argument("--counters-sample", action="store_true",
@@ -614,6 +667,8 @@ def main():
         out = run_counters_sample(args)
     elif args.score:
         out = run_score(args)
+    elif args.generate:
+        out = run_generate(args)
     elif args.workload == "largebatch":
         out = run_largebatch(args)
     elif args.workload == "longctx":

@@ -205,6 +205,49 @@ rlt_status rlt_score_sequence(const rlt_model *m, rlt_state *st, int32_t T, cons
                               const rlt_memory *mem, const int32_t *dev_tokens,
                               float *dev_logprob, void *stream);
 
+/* --------------------------------------------------------- generation */
+/* Stand-in incremental encoder for generation: lookup tables of the token.
+ * The causal encoder itself is not part of this library; a generated token's
+ * e_t and memory entry come from these tables (device pointers, model dtype):
+ *   e  [V][d]            e_t of token v
+ *   k, v [G][V][H][dh]   memory K / V entry of token v in group g */
+typedef struct {
+  const void *e, *k, *v;
+} rlt_encoder_table;
+
+/* Sampling distribution: p(v) proportional to exp(logit_v / temperature)
+ * over the kept tokens, those whose logit is >= the top_k-th largest logit
+ * (top_k >= vocab keeps all).  temperature > 0, top_k >= 1. */
+typedef struct {
+  float temperature;
+  int32_t top_k;
+} rlt_sampling;
+
+/* Autoregressive generation of n_steps tokens for all B slots [Tutorial,
+ * "Autoregressive generation": use the preceding state's distribution,
+ * sample, encode the sampled token, consume it through the decoder exactly
+ * once].  For j = 0 .. n_steps-1 and every slot b:
+ *   1. sample x from the preceding state's logits (j = 0: dev_logits0 [B][V],
+ *      e.g. the last logits of the prompt from rlt_run_sequence; later: the
+ *      previous step's) with u = dev_u[b][j] in [0, 1): the first token v in
+ *      token order whose cumulative weight exceeds u times the total;
+ *   2. record dev_tokens[b][j] = x and dev_logprob[b][j] = its log-probability
+ *      under that distribution (the behaviour log-probability);
+ *   3. encode x with the stand-in tables: e_t = enc->e[x], and memory entry
+ *      pos (0-based; pos = the slot's position before the step) of every
+ *      group set to enc->k[g][x], enc->v[g][x] -- this call WRITES those
+ *      entries of the caller's memory buffers mem->k, mem->v;
+ *   4. consume x: one decoder step of all slots.
+ * dev_logits_last [B][V] fp32 (may be NULL) receives the last step's logits.
+ * Each slot's position advances by n_steps; RLT_ERR_RANGE if that would pass
+ * the memory capacity or max_tokens.  The state, scores and memory entries
+ * are bitwise those of rlt_run_sequence over the same tokens' table rows. */
+rlt_status rlt_generate(const rlt_model *m, rlt_state *st, int32_t n_steps,
+                        const float *dev_logits0, const rlt_encoder_table *enc,
+                        const rlt_memory *mem, const rlt_sampling *smp, const float *dev_u,
+                        int32_t *dev_tokens, float *dev_logprob, float *dev_logits_last,
+                        void *stream);
+
 /* Host mirror of a slot's position (tokens consumed); -1 on a bad argument.
  * Does not synchronise. */
 int32_t rlt_state_position(const rlt_state *st, int32_t slot);

@@ -316,3 +316,63 @@ def score_sequence(model: Model, states, e, mem_k, mem_v, tokens, mem_index=None
         for i in range(n):
             out[i, j] = token_log_prob(lg[i], int(tok[i, j]))
     return out
+
+
+def sampling_weights(logits, temperature, top_k):
+    """Weights of the sampling distribution, float64: exp((z - max z) / T) on
+    the kept tokens -- those whose logit is at least the top_k-th largest
+    (all when top_k >= V) -- and 0 elsewhere."""
+    z = np.asarray(logits, dtype=np.float64)
+    V = z.size
+    keep = np.ones(V, dtype=bool) if top_k >= V else z >= np.sort(z)[::-1][top_k - 1]
+    return np.where(keep, np.exp((z - z.max()) / temperature), 0.0), keep
+
+
+def sample_token(logits, temperature, top_k, u):
+    """Token drawn with uniform u by the inverse CDF in token order: the first
+    v whose cumulative weight exceeds u times the total.  Returns (token,
+    log-probability of it under the sampling distribution)
+    [Tutorial, "Autoregressive generation": sample from the distribution;
+    Princeton, design principles: record each action's behaviour
+    log-probability under the temperature and truncation actually used]."""
+    w, keep = sampling_weights(logits, temperature, top_k)
+    c = np.cumsum(w)
+    total = float(c[-1])
+    tok = int(np.searchsorted(c, u * total, side="right"))
+    tok = min(tok, int(np.nonzero(keep)[0][-1]))
+    z = np.asarray(logits, dtype=np.float64)
+    return tok, float((z[tok] - z.max()) / temperature - math.log(total))
+
+
+def generate(model: Model, states, logits0, table_e, table_k, table_v, mem_k, mem_v, temperature,
+             top_k, u, follow=None):
+    """Autoregressive generation [Tutorial, "Autoregressive generation"]: for
+    every step, sample from the preceding state's logits, record the token and
+    its log-probability, encode it with the stand-in tables (e = table_e[x];
+    memory entry t of each group = table_k/v[g][x], written into mem_k/mem_v,
+    numpy arrays [G][S][H][T][dh]) and consume it once.  follow [n][steps]:
+    tokens to take instead of the sampled ones (replaying another
+    implementation's choices); the log-probability is then that of the
+    followed token.  Returns (tokens, log-probs, logits of the last step)."""
+    n = len(states)
+    steps = np.asarray(u).shape[1]
+    toks = np.zeros((n, steps), dtype=np.int64)
+    lps = np.zeros((n, steps), dtype=np.float64)
+    logits = np.asarray(logits0, dtype=np.float64)
+    te, tk, tv = np.asarray(table_e), np.asarray(table_k), np.asarray(table_v)
+    for j in range(steps):
+        for i in range(n):
+            tok, lp = sample_token(logits[i], temperature, top_k, float(u[i][j]))
+            if follow is not None:
+                tok = int(follow[i][j])
+                z = logits[i]
+                w, _ = sampling_weights(z, temperature, top_k)
+                lp = float((z[tok] - z.max()) / temperature - math.log(w.sum()))
+            toks[i, j], lps[i, j] = tok, lp
+        e_rows = te[toks[:, j]]
+        for i, st in enumerate(states):
+            for g in range(mem_k.shape[0]):
+                mem_k[g, i, :, st.pos, :] = tk[g, toks[i, j]]
+                mem_v[g, i, :, st.pos, :] = tv[g, toks[i, j]]
+        logits = decoder_step(model, states, e_rows, mem_k, mem_v).astype(np.float64)
+    return toks, lps, logits

@@ -25,7 +25,7 @@ RLT_K_SETUP, RLT_K_GEMM, RLT_K_SWA, RLT_K_CROSS = 0, 1, 2, 3
 EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_bytes",
             "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",
             "rlt_state_destroy", "rlt_state_reset", "rlt_decoder_step", "rlt_run_sequence",
-            "rlt_score_sequence",
+            "rlt_score_sequence", "rlt_generate",
             "rlt_state_position", "rlt_snapshot_bytes", "rlt_state_export", "rlt_state_import",
             "rlt_profile_begin", "rlt_profile_collect")
 
@@ -52,6 +52,14 @@ class rlt_memory(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("stride_group", C.c_int64),
                 ("stride_seq", C.c_int64), ("stride_head", C.c_int64), ("stride_pos", C.c_int64),
                 ("capacity", C.c_int32), ("n_seq", C.c_int32), ("n_groups", C.c_int32)]
+
+
+class rlt_encoder_table(C.Structure):
+    _fields_ = [("e", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p)]
+
+
+class rlt_sampling(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("top_k", C.c_int32)]
 
 
 _lib = None
@@ -82,6 +90,8 @@ def load_library(path: str = LIB_PATH):
         "rlt_decoder_step": (i32, [vp, vp, i32, P(i32), vp, P(rlt_memory), vp, vp]),
         "rlt_run_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, i32, vp]),
         "rlt_score_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, vp, vp]),
+        "rlt_generate": (i32, [vp, vp, i32, vp, P(rlt_encoder_table), P(rlt_memory), P(rlt_sampling),
+                               vp, vp, vp, vp, vp]),
         "rlt_state_position": (i32, [vp, i32]),
         "rlt_snapshot_bytes": (sz, [P(rlt_config), i32]),
         "rlt_state_export": (i32, [vp, vp, i32, P(i32), vp, vp]),
@@ -244,6 +254,31 @@ def rlt_score_sequence(model: Model, state: State, e: torch.Tensor, memory, toke
     _check(lib.rlt_score_sequence(model.handle, state.handle, T, e.data_ptr(), C.byref(mem),
                                   tokens.data_ptr(), out.data_ptr(), _stream(stream)))
     return out
+
+
+def rlt_generate(model: Model, state: State, logits0: torch.Tensor, table_e: torch.Tensor,
+                 table_k: torch.Tensor, table_v: torch.Tensor, memory, temperature: float,
+                 top_k: int, u: torch.Tensor, stream=None):
+    """Generate u.shape[1] tokens for all B slots from the preceding logits
+    logits0 [B][V]; stand-in encoder tables e [V][d], k/v [G][V][H][dh];
+    memory (K, V) [G][B][H][T][dh] tensors whose entries at the generated
+    positions are written.  Returns (tokens [B][n] int32, log-probs [B][n]
+    fp32, logits of the last step [B][V] fp32)."""
+    lib = load_library()
+    B, n = u.shape
+    u = u.to(dtype=torch.float32).contiguous()
+    logits0 = logits0.to(dtype=torch.float32).contiguous()
+    dev = u.device
+    tokens = torch.empty((B, n), dtype=torch.int32, device=dev)
+    lp = torch.empty((B, n), dtype=torch.float32, device=dev)
+    last = torch.empty((B, model.cfg.vocab), dtype=torch.float32, device=dev)
+    enc = rlt_encoder_table(table_e.data_ptr(), table_k.data_ptr(), table_v.data_ptr())
+    mem = memory if isinstance(memory, rlt_memory) else memory_view(*memory)
+    smp = rlt_sampling(float(temperature), int(top_k))
+    _check(lib.rlt_generate(model.handle, state.handle, n, logits0.data_ptr(), C.byref(enc),
+                            C.byref(mem), C.byref(smp), u.data_ptr(), tokens.data_ptr(),
+                            lp.data_ptr(), last.data_ptr(), _stream(stream)))
+    return tokens, lp, last
 
 
 def rlt_state_reset(model: Model, state: State, slots, stream=None):

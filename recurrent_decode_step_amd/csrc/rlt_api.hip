@@ -151,7 +151,8 @@ struct rlt_state {
   int *slots_dev;
   float *x, *sumsq;
   char *xg, *qbuf, *obuf, *hbuf;
-  float *lscratch;           // [B][V] fp32 logits of a scored step
+  float *lscratch;           // [B][V] fp32 logits of a scored or generated step
+  char *escratch;            // [B][d] e rows of generated tokens
   std::vector<int> host_pos;
   std::vector<int> staged;   // slot list currently in slots_dev (empty: none)
   // profiling
@@ -237,6 +238,7 @@ size_t state_layout(const rlt_config &c, rlt_state *st, void *base, int B) {
   st->obuf = ar.take<char>(rows16 * d * es);
   st->hbuf = ar.take<char>(rows16 * c.d_ffn * es);
   st->lscratch = ar.take<float>((size_t)B * c.vocab * 4);
+  st->escratch = ar.take<char>((size_t)B * d * es);
   return align256(ar.off);
 }
 
@@ -836,6 +838,73 @@ rlt_status rlt_score_sequence(const rlt_model *m, rlt_state *st, int32_t T, cons
     sa.V = V;
     const hipError_t e = launch_score(sa, st->B, s);
     if (e != hipSuccess) return hip_fail(e, "score launch");
+  }
+  return ok();
+}
+
+rlt_status rlt_generate(const rlt_model *m, rlt_state *st, int32_t n_steps,
+                        const float *dev_logits0, const rlt_encoder_table *enc,
+                        const rlt_memory *mem, const rlt_sampling *smp, const float *dev_u,
+                        int32_t *dev_tokens, float *dev_logprob, float *dev_logits_last,
+                        void *stream) {
+  rlt_status rs;
+  if ((rs = check_state(m, st)) != RLT_OK) return rs;
+  if (n_steps < 1) return fail(RLT_ERR_INVALID_ARG, "n_steps must be >= 1");
+  if (!dev_logits0 || !enc || !enc->e || !enc->k || !enc->v || !smp || !dev_u || !dev_tokens ||
+      !dev_logprob)
+    return fail(RLT_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!(smp->temperature > 0.f) || smp->top_k < 1)
+    return fail(RLT_ERR_INVALID_ARG, "temperature must be > 0 and top_k >= 1");
+  if ((rs = check_memory(m, mem, st->B - 1)) != RLT_OK) return rs;
+  if ((rs = check_positions(st, mem, st->B, nullptr, n_steps)) != RLT_OK) return rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const rlt_config &c = m->cfg;
+  const int B = st->B, V = c.vocab, d = c.d_model;
+  for (int j = 0; j < n_steps; ++j) {
+    // 1-2: sample from the preceding state's logits, record token and log-prob
+    SampleArgs sa;
+    sa.logits = j == 0 ? dev_logits0 : st->lscratch;
+    sa.ld = V;
+    sa.u = dev_u + j;
+    sa.ld_u = n_steps;
+    sa.tokens = dev_tokens + j;
+    sa.ld_tok = n_steps;
+    sa.logprob = dev_logprob + j;
+    sa.ld_lp = n_steps;
+    sa.V = V;
+    sa.top_k = std::min(smp->top_k, V);
+    sa.inv_temp = 1.0f / smp->temperature;
+    hipError_t e = launch_sample(sa, B, s);
+    if (e != hipSuccess) return hip_fail(e, "sample launch");
+    // 3: stand-in encoder: e row and memory entry pos of every group
+    EncodeArgs ea;
+    ea.tokens = dev_tokens + j;
+    ea.ld_tok = n_steps;
+    ea.tab_e = enc->e;
+    ea.tab_k = enc->k;
+    ea.tab_v = enc->v;
+    ea.e_out = st->escratch;
+    ea.mem_k = const_cast<void *>(mem->k);
+    ea.mem_v = const_cast<void *>(mem->v);
+    ea.s_group = mem->stride_group;
+    ea.s_seq = mem->stride_seq;
+    ea.s_head = mem->stride_head;
+    ea.s_pos = mem->stride_pos;
+    ea.slots = nullptr;
+    ea.pos = st->pos;
+    ea.d = d;
+    ea.H = c.n_heads;
+    ea.dh = c.head_dim;
+    ea.V = V;
+    ea.G = c.mem_groups;
+    e = launch_encode(c.dtype, ea, B, s);
+    if (e != hipSuccess) return hip_fail(e, "encode launch");
+    // 4: consume it once; the logits of the new state go to the scratch (and
+    // to dev_logits_last on the last step)
+    float *lg = (j == n_steps - 1 && dev_logits_last) ? dev_logits_last : st->lscratch;
+    if ((rs = enqueue_step(m, st, B, true, nullptr, st->escratch, d, mem, lg, V, s)) != RLT_OK)
+      return rs;
   }
   return ok();
 }

@@ -64,6 +64,25 @@ struct ScoreArgs {
   int V;
 };
 
+struct SampleArgs {
+  const float *logits; int64_t ld;          // [n][ld] fp32 logits of the preceding state
+  const float *u; int64_t ld_u;             // uniform in [0, 1) of row i at u[i * ld_u]
+  int32_t *tokens; int64_t ld_tok;          // sampled token of row i at tokens[i * ld_tok]
+  float *logprob; int64_t ld_lp;            // its log-probability under the sampling distribution
+  int V; int top_k; float inv_temp;
+};
+
+struct EncodeArgs {
+  const int32_t *tokens; int64_t ld_tok;    // token of row i
+  const void *tab_e;                        // [V][d] storage type
+  const void *tab_k, *tab_v;                // [G][V][H][dh] storage type
+  void *e_out;                              // [n][d] storage type
+  void *mem_k, *mem_v;                      // caller memory (group / sequence / head / position strides)
+  int64_t s_group, s_seq, s_head, s_pos;
+  const int *slots; const int *pos;         // row i is slot slots[i] (null: i); entry index pos[slot]
+  int d, H, dh, V, G;
+};
+
 struct AttnArgs {
   const void *q; void *out;                 // q [n][d] row-major; out fragment-packed
   int kt_out;                               // KT of the packed output (d / k-step)
@@ -88,6 +107,10 @@ hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int til
                                   int parts, hipStream_t s);
 // log softmax of each row's logits at its realized token (one workgroup per row)
 hipError_t launch_score(const ScoreArgs &a, int n_rows, hipStream_t s);
+// sampling from each row's logits (temperature, top-k truncation, inverse CDF in token order)
+hipError_t launch_sample(const SampleArgs &a, int n_rows, hipStream_t s);
+// stand-in incremental encoder: e rows and memory entries of the sampled tokens
+hipError_t launch_encode(int dtype, const EncodeArgs &a, int n_rows, hipStream_t s);
 hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStream_t s);
 int attn_chunk_max(int dtype, int dh);
 hipError_t launch_state_init(float *s, int *pos, const float *s_star, int B, int d,

@@ -962,6 +962,160 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(const ScoreArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- generation
+// Sampling one token per row from p(v) proportional to exp(z_v / temperature)
+// over the kept tokens, the tokens whose logit is at least the top_k-th largest
+// logit (all of them when top_k >= V): the k-th largest is found exactly by a
+// radix selection on the order-preserving integer image of the fp32 logits
+// (four 8-bit digits, most significant first).  The token is the first v in
+// token order whose running sum of weights exceeds u * total; each thread owns
+// a contiguous block of tokens, blocks are summed in order and their prefixes
+// taken in thread order, so the decision depends only on the row.  Rounding
+// can only move the choice between tokens whose cumulative weights lie within
+// fp32 rounding of u * total.  The recorded log-probability is
+// (z_tok - zmax) / temperature - log(total) with zmax the largest logit.
+constexpr int kSampleThreads = 1024;
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__global__ __launch_bounds__(kSampleThreads) void k_sample(const SampleArgs a) {
+  constexpr int NWV = kSampleThreads / 64;
+  __shared__ uint32_t s_hist[256];
+  __shared__ uint32_t s_sel[2];
+  __shared__ float s_red[NWV];
+  __shared__ float s_wpre[NWV + 1];
+  __shared__ int s_tok;
+  const int i = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float *z = a.logits + (size_t)i * a.ld;
+  const int V = a.V;
+
+  // k-th largest key (kept: key >= kth); prefix/mask select the candidates
+  uint32_t kth = 0u;
+  if (a.top_k < V) {
+    uint32_t prefix = 0u, mask = 0u;
+    int need = a.top_k;                            // rank still to find among candidates
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int b = tid; b < 256; b += kSampleThreads) s_hist[b] = 0u;
+      __syncthreads();
+      for (int v = tid; v < V; v += kSampleThreads) {
+        const uint32_t k = order_key(z[v]);
+        if ((k & mask) == prefix) atomicAdd(&s_hist[(k >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int acc = 0, b = 255;
+        for (; b > 0; --b) {                      // from the largest digit down
+          if (acc + (int)s_hist[b] >= need) break;
+          acc += (int)s_hist[b];
+        }
+        s_sel[0] = (uint32_t)b;
+        s_sel[1] = (uint32_t)(need - acc);
+      }
+      __syncthreads();
+      prefix |= s_sel[0] << shift;
+      mask |= 255u << shift;
+      need = (int)s_sel[1];
+      __syncthreads();
+    }
+    kth = prefix;
+  }
+
+  // largest logit
+  float mx = -INFINITY;
+  for (int v = tid; v < V; v += kSampleThreads) mx = fmaxf(mx, z[v]);
+  mx = wave_max(mx);
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  mx = s_red[0];
+  for (int w = 1; w < NWV; ++w) mx = fmaxf(mx, s_red[w]);
+  __syncthreads();                                 // s_red is reused below
+
+  // this thread's contiguous block of tokens and its weight sum (in order)
+  const int per = (V + kSampleThreads - 1) / kSampleThreads;
+  const int v0 = min(V, tid * per), v1 = min(V, v0 + per);
+  float part = 0.f;
+  for (int v = v0; v < v1; ++v) {
+    const float zv = z[v];
+    if (order_key(zv) >= kth) part += expf((zv - mx) * a.inv_temp);
+  }
+  // block prefixes: a lane scan in each wavefront, wavefront totals in order;
+  // block t owns [lo_t, hi_t) with hi_t = lo_{t+1} exactly, so the blocks
+  // partition [0, total) whatever the rounding
+  float incl = part;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  float ex = __shfl_up(incl, 1);
+  if (lane == 0) ex = 0.f;
+  if (lane == 63) s_red[wave] = incl;
+  if (tid == 0) s_tok = -1;
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.f;
+    for (int w = 0; w < NWV; ++w) {
+      s_wpre[w] = acc;
+      acc += s_red[w];
+    }
+    s_wpre[NWV] = acc;
+  }
+  __syncthreads();
+  const float lo = s_wpre[wave] + ex;
+  float hi = __shfl_down(lo, 1);
+  if (lane == 63) hi = s_wpre[wave + 1];
+  const float tot = s_wpre[NWV];
+  const float target = a.u[(size_t)i * a.ld_u] * tot;
+  if (lo <= target && target < hi) {
+    float run = lo;
+    int pick = -1, last = -1;
+    for (int v = v0; v < v1; ++v) {
+      const float zv = z[v];
+      if (order_key(zv) < kth) continue;
+      last = v;
+      run += expf((zv - mx) * a.inv_temp);
+      if (run > target) { pick = v; break; }
+    }
+    s_tok = pick >= 0 ? pick : last;               // one block owns the target
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int tok = s_tok;
+    if (tok < 0) {
+      // target at or past the rounded total: the last kept token
+      for (int v = V - 1; v >= 0; --v)
+        if (order_key(z[v]) >= kth) { tok = v; break; }
+    }
+    a.tokens[(size_t)i * a.ld_tok] = tok;
+    a.logprob[(size_t)i * a.ld_lp] = (z[tok] - mx) * a.inv_temp - logf(tot);
+  }
+}
+
+// e row and memory entries of each row's token (one workgroup per row)
+template <typename T>
+__global__ __launch_bounds__(256) void k_encode(const EncodeArgs a) {
+  const int i = blockIdx.x;
+  const int slot = a.slots ? a.slots[i] : i;
+  const int tok = a.tokens[(size_t)i * a.ld_tok];
+  const T *src_e = static_cast<const T *>(a.tab_e) + (size_t)tok * a.d;
+  T *dst_e = static_cast<T *>(a.e_out) + (size_t)i * a.d;
+  for (int c = threadIdx.x; c < a.d; c += blockDim.x) dst_e[c] = src_e[c];
+  const int p = a.pos[slot];                       // entry of position t = pos + 1
+  const int hd = a.H * a.dh;
+  for (int g = 0; g < a.G; ++g) {
+    const T *sk = static_cast<const T *>(a.tab_k) + ((size_t)g * a.V + tok) * hd;
+    const T *sv = static_cast<const T *>(a.tab_v) + ((size_t)g * a.V + tok) * hd;
+    for (int c = threadIdx.x; c < hd; c += blockDim.x) {
+      const int h = c / a.dh, x = c - h * a.dh;
+      const size_t off = (size_t)g * a.s_group + (size_t)slot * a.s_seq + (size_t)h * a.s_head +
+                         (size_t)p * a.s_pos + x;
+      static_cast<T *>(a.mem_k)[off] = sk[c];
+      static_cast<T *>(a.mem_v)[off] = sv[c];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- state
 __global__ void k_state_init(float *s, int *pos, const float *s_star, int d, const int *slots,
                              int n) {
@@ -1103,7 +1257,10 @@ static hipError_t gemm_dispatch_ncb(int ncb, int act, int epi, const GemmArgs &a
   switch (ncb) {
     case 1: return gemm_dispatch_epi<T, 1, KSW, TPW>(act, epi, a, grid, threads, s);
     case 2: return gemm_dispatch_epi<T, 2, KSW, TPW>(act, epi, a, grid, threads, s);
-    case 4: return gemm_dispatch_epi<T, 4, KSW, TPW>(act, epi, a, grid, threads, s);
+    case 4:
+      // four column blocks hold registers for one tile per wavefront only
+      if constexpr (TPW == 1) return gemm_dispatch_epi<T, 4, KSW, TPW>(act, epi, a, grid, threads, s);
+      break;
   }
   return hipErrorInvalidValue;
 }
@@ -1193,6 +1350,19 @@ hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int til
 hipError_t launch_score(const ScoreArgs &a, int n_rows, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
   k_score<<<dim3((unsigned)n_rows), kScoreThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample(const SampleArgs &a, int n_rows, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  k_sample<<<dim3((unsigned)n_rows), kSampleThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(int dtype, const EncodeArgs &a, int n_rows, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  if (dtype == RLT_DTYPE_BF16) k_encode<bf16_t><<<dim3((unsigned)n_rows), 256, 0, s>>>(a);
+  else k_encode<float><<<dim3((unsigned)n_rows), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

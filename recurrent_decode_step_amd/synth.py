@@ -149,3 +149,26 @@ def imported_state(cfg: ModelConfig, t: int, device="cpu", seed=SEED_STATE, inde
         V[l] = normal((H, n_hist, dh), device=device, seed=seed, kind=2, layer=l, index=index,
                       round_bf16=bf, out_dtype=sd)
     return {"pos": t - 1, "s": s, "K": K, "V": V}
+
+
+SEED_TABLES = 5
+
+
+def encoder_tables(cfg: ModelConfig, device="cpu", seed=SEED_TABLES):
+    """Stand-in incremental encoder for generation: e [V][d] and memory K, V
+    [G][V][H][dh] rows per token, ~ N(0, 1), in the storage dtype."""
+    bf = cfg.dtype == DTYPE_BF16
+    sd = storage_dtype(cfg)
+    V, d, G, H, dh = cfg.vocab, cfg.d_model, cfg.mem_groups, cfg.n_heads, cfg.head_dim
+    e = normal((V, d), device=device, seed=seed, kind=0, round_bf16=bf, out_dtype=sd)
+    k = torch.stack([normal((V, H, dh), device=device, seed=seed, kind=1, layer=g, round_bf16=bf,
+                            out_dtype=sd) for g in range(G)])
+    v = torch.stack([normal((V, H, dh), device=device, seed=seed, kind=2, layer=g, round_bf16=bf,
+                            out_dtype=sd) for g in range(G)])
+    return e, k, v
+
+
+def uniforms(shape, device="cpu", seed=SEED_TABLES, index=0) -> torch.Tensor:
+    """Uniform numbers in [0, 1) for sampling, from the (seed, 3, 0, index) stream."""
+    g = _generator(device, seed, 3, 0, index)
+    return torch.rand(tuple(shape), generator=g, device=device, dtype=torch.float32)

@@ -111,6 +111,8 @@ def test_null_handles():
     assert L.rlt_decoder_step(None, None, 1, None, None, None, None, None) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_run_sequence(None, None, 1, None, None, None, 0, None) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_score_sequence(None, None, 1, None, None, None, None, None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_generate(None, None, 1, None, None, None, None, None, None, None, None,
+                          None) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_state_reset(None, None, 1, None, None) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_state_export(None, None, 1, None, None, None) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_state_import(None, None, 1, None, None, None) == binding.RLT_ERR_INVALID_ARG

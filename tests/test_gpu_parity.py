@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from _tiny import tiny_cfg, make_model, inputs, oracle_state_from_snapshot
+from _tiny import tiny_cfg, make_model, inputs, np64, oracle_state_from_snapshot
 from recurrent_decode_step_amd import binding, synth
 from recurrent_decode_step_amd.configs import ModelConfig, DTYPE_BF16, DTYPE_FP32
 
@@ -470,4 +470,115 @@ def test_score_sequence_reads_its_own_logits_and_leaves_the_run_state():
                 assert abs(float(got[b, t]) - float(lsm[b, t, tk])) <= 1e-5, (b, t)
     nxt_a = binding.rlt_decoder_step(rig.model, st_a, rig.ed[:, T], rig.mem).cpu()
     nxt_b = binding.rlt_decoder_step(rig.model, st_b, rig.ed[:, T], rig.mem).cpu()
+    assert torch.equal(nxt_a, nxt_b)
+
+
+# ---------------------------------------------------------------- generation
+def _cdf_valid(z, temperature, top_k, u, tok, rel=1e-4):
+    """tok is a valid draw for u: its weight is positive and u * total lies in
+    [cum(tok - 1), cum(tok)] up to rel * total (fp32 accumulation)."""
+    w, _ = oracle.sampling_weights(z, temperature, top_k)
+    c = np.cumsum(w)
+    tot = c[-1]
+    tgt = u * tot
+    lo = c[tok - 1] if tok > 0 else 0.0
+    return w[tok] > 0 and lo - rel * tot <= tgt <= c[tok] + rel * tot
+
+
+@pytest.mark.parametrize("vocab,settings", [
+    (1000, [(1.0, 1000), (0.7, 50), (1.3, 1), (1.0, 7)]),
+    (32768, [(1.0, 32768), (0.9, 50)]),
+])
+def test_sampler_draws_from_the_exact_distribution(vocab, settings):
+    """One generation step from given logits: each sampled token is a valid
+    inverse-CDF draw for its u under the float64 distribution (temperature,
+    top-k), equals the oracle's draw wherever u is not within rounding of a
+    CDF step, and its recorded log-probability matches (<= 1e-4)."""
+    cfg = tiny_cfg(vocab=vocab)
+    B = 32
+    rig = Rig(cfg, B, len(settings) + 1)
+    te, tk, tv = (t.to(DEV) for t in synth.encoder_tables(cfg, device="cpu"))
+    st = rig.state()
+    rng = np.random.default_rng(13)
+    say(f"[sampler] V={vocab} settings={settings}")
+    for j, (temp, topk) in enumerate(settings):
+        z = (rng.normal(size=(B, vocab)) * 3.0).astype(np.float32)
+        u = synth.uniforms((B, 1), index=j)
+        tok, lp, _ = binding.rlt_generate(rig.model, st, torch.from_numpy(z).to(DEV), te, tk, tv,
+                                          rig.mem, temp, topk, u.to(DEV))
+        tok, lp = tok.cpu().numpy()[:, 0], lp.cpu().numpy()[:, 0]
+        for b in range(B):
+            ub = float(u[b, 0])
+            assert _cdf_valid(z[b], temp, topk, ub, int(tok[b])), (j, b)
+            ref_tok, _ = oracle.sample_token(z[b], temp, topk, ub)
+            if ref_tok != tok[b]:
+                assert _cdf_valid(z[b], temp, topk, ub, ref_tok), (j, b)
+            w, _ = oracle.sampling_weights(z[b], temp, topk)
+            zz = z[b].astype(np.float64)
+            ref_lp = (zz[tok[b]] - zz.max()) / temp - np.log(w.sum())
+            assert abs(lp[b] - ref_lp) <= 1e-4, (j, b, lp[b], ref_lp)
+        if topk == 1:
+            assert np.array_equal(tok, z.argmax(axis=1))
+
+
+def test_generate_matches_oracle_f32():
+    """Prompt through rlt_run_sequence, then 12 generated tokens: every GPU
+    token is a valid draw under the oracle's logits (replayed by the oracle),
+    log-probabilities agree within 2e-4 / temperature, the last logits within
+    1e-4, and the memory entries written are the table rows of the tokens."""
+    cfg = tiny_cfg()
+    B, P, n, temp, topk = 4, 6, 12, 0.9, 8
+    rig = Rig(cfg, B, P + n)
+    te, tk, tv = synth.encoder_tables(cfg, device="cpu")
+    u = synth.uniforms((B, n))
+    st = rig.state()
+    say("[generate f32]")
+    pre = binding.rlt_run_sequence(rig.model, st, rig.ed[:, :P], rig.mem,
+                                   logits_mode=binding.RLT_LOGITS_LAST)
+    mk, mv = rig.mem
+    tok, lp, last = binding.rlt_generate(rig.model, st, pre, te.to(DEV), tk.to(DEV), tv.to(DEV),
+                                         (mk, mv), temp, topk, u.to(DEV))
+    tok, lp, last = tok.cpu().numpy(), lp.cpu().numpy(), last.cpu().numpy()
+    m = rig.oracle_model()
+    states = [oracle.initial_state(m) for _ in range(B)]
+    mk1, mv1 = np64(rig.mk).copy(), np64(rig.mv).copy()
+    opre = oracle.run_sequence(m, states, rig.e[:, :P], mk1, mv1)
+    # validity of each GPU choice under the oracle's logits, step by step
+    logits = opre[:, -1].astype(np.float64)
+    st_o = [oracle.copy_state(s) for s in states]
+    for j in range(n):
+        for b in range(B):
+            assert _cdf_valid(logits[b], temp, topk, float(u[b, j]), int(tok[b, j]), rel=1e-3), (j, b)
+        oracle_toks, olp, logits = oracle.generate(m, st_o, logits, te, tk, tv, mk1, mv1, temp, topk,
+                                                   u[:, j:j + 1].numpy(), follow=tok[:, j:j + 1])
+        assert np.max(np.abs(olp[:, 0] - lp[:, j])) <= 2e-4 / temp
+    assert np.max(np.abs(logits - last)) <= 1e-4
+    mk_g = rig.mem[0].cpu().numpy()
+    for b in range(B):
+        for j in range(n):
+            np.testing.assert_array_equal(mk_g[0, b, :, P + j], tk.numpy()[0, tok[b, j]])
+
+
+def test_generate_equals_run_sequence_over_its_tokens_bitwise():
+    """bf16: generating n tokens leaves the state, logits and memory exactly
+    where rlt_run_sequence over those tokens' table rows (with the memory the
+    generation wrote) leaves them: each token is consumed once."""
+    cfg = BF16_SMALL.with_(n_layers=2, mem_groups=2)
+    B, P, n = 8, 4, 6
+    rig = Rig(cfg, B, P + n + 1)
+    te, tk, tv = (t.to(DEV) for t in synth.encoder_tables(cfg, device="cpu"))
+    u = synth.uniforms((B, n), index=1).to(DEV)
+    say("[generate bf16 bitwise]")
+    st_a = rig.state()
+    pre = binding.rlt_run_sequence(rig.model, st_a, rig.ed[:, :P], rig.mem,
+                                   logits_mode=binding.RLT_LOGITS_LAST)
+    tok, lp, last = binding.rlt_generate(rig.model, st_a, pre, te, tk, tv, rig.mem, 1.0, 40, u)
+    assert torch.isfinite(lp).all()
+    st_b = rig.state()
+    binding.rlt_run_sequence(rig.model, st_b, rig.ed[:, :P], rig.mem, logits_mode=binding.RLT_LOGITS_NONE)
+    e_gen = te[tok.long()].contiguous()                       # [B][n][d]
+    rep = binding.rlt_run_sequence(rig.model, st_b, e_gen, rig.mem)
+    assert torch.equal(rep[:, -1].cpu(), last.cpu())
+    nxt_a = binding.rlt_decoder_step(rig.model, st_a, rig.ed[:, P + n], rig.mem).cpu()
+    nxt_b = binding.rlt_decoder_step(rig.model, st_b, rig.ed[:, P + n], rig.mem).cpu()
     assert torch.equal(nxt_a, nxt_b)

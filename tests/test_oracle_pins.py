@@ -528,3 +528,77 @@ def test_score_uses_the_logits_before_the_token_is_consumed():
     keep = np.ones(T, bool)
     keep[::3] = False
     assert np.array_equal(got2[:, keep], got[:, keep])
+
+
+# ------------------------------------------------------ generation (next row)
+def test_sample_token_inverse_cdf_closed_forms():
+    """Logits 0, ln 2, ln 3 give p = 1/6, 2/6, 3/6: u = 0.1, 0.2, 0.6 pick tokens
+    0, 1, 2 (first token whose cumulative probability exceeds u) with
+    log-probabilities ln p; top_k = 2 keeps tokens 1, 2 (p = 2/5, 3/5);
+    top_k = 1 is the argmax for every u; temperature 2 takes square roots of
+    the weights."""
+    z = np.array([0.0, math.log(2.0), math.log(3.0)])
+    for u, tok, p in ((0.1, 0, 1 / 6), (0.2, 1, 2 / 6), (0.6, 2, 3 / 6)):
+        t, lp = oracle.sample_token(z, 1.0, 3, u)
+        assert t == tok and abs(lp - math.log(p)) < 1e-12
+    t, lp = oracle.sample_token(z, 1.0, 2, 0.3)
+    assert t == 1 and abs(lp - math.log(0.4)) < 1e-12
+    t, lp = oracle.sample_token(z, 1.0, 2, 0.5)
+    assert t == 2 and abs(lp - math.log(0.6)) < 1e-12
+    for u in (0.0, 0.3, 0.999):
+        assert oracle.sample_token(z, 1.0, 1, u)[0] == 2
+    w = np.sqrt(np.array([1.0, 2.0, 3.0]))
+    t, lp = oracle.sample_token(z, 2.0, 3, 0.99)
+    assert t == 2 and abs(lp - math.log(w[2] / w.sum())) < 1e-12
+
+
+def test_sample_token_frequencies_and_ties():
+    """Over a fine grid of u the share of each token is its probability (to
+    the grid step); top_k keeps every token tied with the k-th largest logit."""
+    rng = np.random.default_rng(8)
+    z = rng.normal(size=12)
+    w, _ = oracle.sampling_weights(z, 0.7, 5)
+    p = w / w.sum()
+    N = 20000
+    counts = np.zeros(12)
+    for j in range(N):
+        counts[oracle.sample_token(z, 0.7, 5, (j + 0.5) / N)[0]] += 1
+    assert np.max(np.abs(counts / N - p)) <= 1.0 / N + 1e-12
+    assert np.count_nonzero(counts) == 5
+    tie = np.array([1.0, 5.0, 5.0, 2.0])
+    _, keep = oracle.sampling_weights(tie, 1.0, 1)
+    assert keep.tolist() == [False, True, True, False]
+
+
+def test_generate_consumes_each_token_once():
+    """Generation with the stand-in encoder equals running the decoder over the
+    table rows of the generated tokens, with the memory entries those tokens
+    wrote: the sampled token is encoded and consumed exactly once per step
+    [Tutorial, "Autoregressive generation"]."""
+    cfg = tiny_cfg()
+    model, _ = make_model(cfg)
+    B, P, n = 3, 5, 7
+    e, mk, mv = inputs(cfg, B, P + n)
+    te, tk, tv = synth.encoder_tables(cfg)
+    u = synth.uniforms((B, n))
+    mk1, mv1 = np64(mk).copy(), np64(mv).copy()
+    states = [oracle.initial_state(model) for _ in range(B)]
+    pre = oracle.run_sequence(model, states, e[:, :P], mk1, mv1)
+    toks, lps, last = oracle.generate(model, states, pre[:, -1], te, tk, tv, mk1, mv1, 0.8, 6, u)
+    # replay: the same prompt, then the table rows of the generated tokens
+    st2 = [oracle.initial_state(model) for _ in range(B)]
+    oracle.run_sequence(model, st2, e[:, :P], mk1, mv1)
+    e_gen = np64(te)[toks]                                 # [B][n][d]
+    rep = oracle.run_sequence(model, st2, e_gen, mk1, mv1)
+    np.testing.assert_array_equal(rep[:, -1], last.astype(rep.dtype))
+    for i in range(B):
+        for j in range(n):
+            np.testing.assert_array_equal(mk1[0, i, :, P + j], np64(tk)[0, toks[i, j]])
+        assert states[i].pos == P + n
+    # log-probabilities are those of the sampling distribution at each step
+    logits_steps = np.concatenate([pre[:, -1:], rep[:, :-1]], axis=1)
+    for i in range(B):
+        for j in range(n):
+            w, _ = oracle.sampling_weights(logits_steps[i, j], 0.8, 6)
+            z = logits_steps[i, j].astype(np.float64)
+            assert abs(lps[i, j] - ((z[toks[i, j]] - z.max()) / 0.8 - math.log(w.sum()))) < 1e-9
