@@ -1,9 +1,13 @@
 // HIP kernels of the recurrent decoder step, written for gfx950 (CDNA4).
 //
-// Step structure (one launch each, on the caller's stream):
-//   setup  : per-row position t = pos+1, position advance, attention work lists
-//   GEMM   : merge (gate), then per layer QKV, O, Qc, Oc, FFN-up, FFN-down, then head
-//   attn   : sliding-window self-attention and causal cross-attention (flash-decode)
+// Step structure (one launch each, on the caller's stream; no workgroup ever
+// waits for another, a launch boundary is the only global synchronisation):
+//   GEMM   : merge (gate), then per layer QKV (+ window append), O, Qc, Oc,
+//            FFN-up, FFN-down, then the head, which advances the positions
+//   attn   : sliding-window self-attention and causal cross-attention
+//            (flash-decode, one workgroup per row and head)
+//   extras : replay scoring (log softmax at a token), sampling and the
+//            stand-in encoder of generation, state init / export / import
 //
 // The decoder math follows the Recurrent Looped Transformer pages (titles in
 // include/rlt.h): the gated merge and block contents of the architecture
