@@ -219,7 +219,7 @@ def run_refdepth(args):
     torch.cuda.synchronize()
 
     stride = max(1, K // 64)
-    classes = (binding.RLT_K_SETUP, binding.RLT_K_GEMM, binding.RLT_K_SWA, binding.RLT_K_CROSS)
+    classes = (binding.RLT_K_EXTRA, binding.RLT_K_GEMM, binding.RLT_K_SWA, binding.RLT_K_CROSS)
     mask = (1 << binding.RLT_K_CROSS) if not args.breakdown else sum(1 << c for c in classes)
     binding.profile_begin(state, mask, 1 << 22, step_stride=stride)
     stream = torch.cuda.current_stream()
@@ -280,7 +280,7 @@ def run_refdepth(args):
         "setup_s": round(setup_s, 1),
     }
     if args.breakdown:
-        names = {binding.RLT_K_SETUP: "setup", binding.RLT_K_GEMM: "gemm",
+        names = {binding.RLT_K_EXTRA: "extra", binding.RLT_K_GEMM: "gemm",
                  binding.RLT_K_SWA: "window_attention", binding.RLT_K_CROSS: "cross_attention"}
         n_prof_steps = len(range(0, K, stride))
         out["breakdown_ms_per_step"] = {
@@ -482,6 +482,55 @@ def run_generate(args):
     }
 
 
+def run_longctx_full(args):
+    """The long-context workload run whole: 8 sequences from H_0 through all
+    32768 steps (rlt_run_sequence in chunks of 1024 steps, no reset, logits of
+    the last step of each chunk), timed with HIP events around the whole run."""
+    import torch
+    from recurrent_decode_step_amd import binding, synth
+    from recurrent_decode_step_amd.configs import LONGCTX
+    wl = LONGCTX
+    cfg, B, T = wl.model, wl.batch, wl.steps
+    chunk = 1024
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    params = synth.model_params(cfg, device=dev)
+    model = binding.Model(cfg, params, version=1)
+    e = synth.encoder_e(cfg, B, T, device=dev)
+    mk, mv = synth.encoder_memory(cfg, B, T, device=dev)
+    mem = binding.memory_view(mk, mv)
+    state = binding.State(model, B, T)
+    binding.rlt_run_sequence(model, state, e[:, :4], mem, logits_mode=binding.RLT_LOGITS_LAST)
+    binding.rlt_state_reset(model, state, list(range(B)))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(T // chunk + 1)]
+    ev[0].record(stream)
+    for c in range(T // chunk):
+        lg = binding.rlt_run_sequence(model, state, e[:, c * chunk:(c + 1) * chunk], mem,
+                                      logits_mode=binding.RLT_LOGITS_LAST)
+        ev[c + 1].record(stream)
+        ev[c + 1].synchronize()
+        print(f"longctx full run: {(c + 1) * chunk} of {T} steps, "
+              f"{ev[c].elapsed_time(ev[c + 1]) / chunk:.3f} ms/step", file=sys.stderr, flush=True)
+    ms = ev[0].elapsed_time(ev[-1])
+    if not torch.isfinite(lg).all():
+        raise RuntimeError("non-finite logits")
+    bytes_total = sum(algorithmic_bytes_per_step(cfg, [t] * B, 2) for t in range(1, T + 1, 64)) * 64
+    return {
+        "metric": "decoder token-steps/sec at 1 GPU (48-layer, d=4096, B=8, T=32768)",
+        "value": round(B * T / (ms / 1e3), 2), "unit": "token-steps/s", "n_gpus": 1, "steps": T,
+        "ms_per_step": round(ms / T, 4), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "method": "one full run of 32768 steps from H_0",
+                   "logits": "last step of every 1024-step chunk"},
+        "step_roofline": {"bound": "hbm", "algorithmic_GB_per_step": round(bytes_total / T / 1e9, 3),
+                          "achieved": round(bytes_total / (ms / 1e3) / 1e9, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(bytes_total / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+
 def run_largebatch(args):
     """256 sequences at ragged positions t_b ~ U{1..8192} (W = 1024): states
     imported at t_b, one untimed step, then K batched steps timed with HIP
@@ -642,6 +691,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default="refdepth",
                     choices=["refdepth", "largebatch", "longctx", "tiny", "small"])
+    ap.add_argument("--full", action="store_true",
+                    help="longctx: one full 32768-step run instead of the window fit")
     ap.add_argument("--generate", action="store_true",
                     help="generation at the reference depth after the 2048-token prompt")
     ap.add_argument("--score", action="store_true",
@@ -672,7 +723,7 @@ def main():
     elif args.workload == "largebatch":
         out = run_largebatch(args)
     elif args.workload == "longctx":
-        out = run_longctx(args)
+        out = run_longctx_full(args) if args.full else run_longctx(args)
     elif args.workload in ("tiny", "small"):
         from recurrent_decode_step_amd.configs import TINY, SMALL
         out = run_full_sequence(args, TINY if args.workload == "tiny" else SMALL)

@@ -278,8 +278,10 @@ rlt_status rlt_state_import(const rlt_model *m, rlt_state *st, int32_t n,
                             const int32_t *host_slots, const void *dev_snap, void *stream);
 
 /* ------------------------------------------------------------- profiling */
-/* Kernel classes for per-class timing. */
-enum { RLT_K_SETUP = 0, RLT_K_GEMM = 1, RLT_K_SWA = 2, RLT_K_CROSS = 3, RLT_K_NCLASSES = 4 };
+/* Kernel classes for per-class timing: RLT_K_EXTRA = the replay-scoring,
+ * sampling and stand-in encoder kernels; GEMM = every projection and the head;
+ * SWA = window attention; CROSS = memory attention. */
+enum { RLT_K_EXTRA = 0, RLT_K_GEMM = 1, RLT_K_SWA = 2, RLT_K_CROSS = 3, RLT_K_NCLASSES = 4 };
 
 /* Start recording a HIP event pair around every launch of the kernel classes
  * in class_mask (bit 1 << RLT_K_*) on this state, during every step_stride-th

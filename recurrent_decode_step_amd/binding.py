@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "librlt.so")
 RLT_OK, RLT_ERR_INVALID_ARG, RLT_ERR_SHAPE, RLT_ERR_RANGE, RLT_ERR_STALE, \
     RLT_ERR_CONVENTION, RLT_ERR_UNSUPPORTED, RLT_ERR_DEVICE = range(8)
 RLT_LOGITS_ALL, RLT_LOGITS_LAST, RLT_LOGITS_NONE = 0, 1, 2
-RLT_K_SETUP, RLT_K_GEMM, RLT_K_SWA, RLT_K_CROSS = 0, 1, 2, 3
+RLT_K_EXTRA, RLT_K_GEMM, RLT_K_SWA, RLT_K_CROSS = 0, 1, 2, 3
 
 EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_bytes",
             "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",

@@ -392,11 +392,10 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     }
     // large batches: the persistent kernel (same arithmetic, activations in
     // registers, many tiles per workgroup)
-    hipError_t e2 = hipErrorInvalidValue;
-    if (c.dtype == RLT_DTYPE_BF16 && act == ACT_PLAIN && n > 64)
-      e2 = launch_gemm_persistent(c.dtype, epi, a, g.tiles, cdiv(n, 32), g.parts, s);
-    if (e2 == hipErrorInvalidValue)
-      e2 = launch_gemm(c.dtype, gc.ncb, tpw, act, epi, a, g.tiles, gc.groups, g.parts, s);
+    const hipError_t e2 =
+        gemm_persistent_applies(c.dtype, act, epi, n, g.KT, g.parts)
+            ? launch_gemm_persistent(c.dtype, epi, a, g.tiles, n, g.parts, s)
+            : launch_gemm(c.dtype, gc.ncb, tpw, act, epi, a, g.tiles, gc.groups, g.parts, s);
     if (e2 != hipSuccess) return hip_fail(e2, what);
     p.done((double)g.N * g.K * es + act_bytes + out_bytes);
     return RLT_OK;
@@ -836,8 +835,10 @@ rlt_status rlt_score_sequence(const rlt_model *m, rlt_state *st, int32_t T, cons
     sa.out = dev_logprob + k;
     sa.ld_out = T;
     sa.V = V;
+    Prof p(st, RLT_K_EXTRA, s);
     const hipError_t e = launch_score(sa, st->B, s);
     if (e != hipSuccess) return hip_fail(e, "score launch");
+    p.done((double)st->B * V * 4 * 2);
   }
   return ok();
 }
@@ -875,8 +876,10 @@ rlt_status rlt_generate(const rlt_model *m, rlt_state *st, int32_t n_steps,
     sa.V = V;
     sa.top_k = std::min(smp->top_k, V);
     sa.inv_temp = 1.0f / smp->temperature;
+    Prof ps(st, RLT_K_EXTRA, s);
     hipError_t e = launch_sample(sa, B, s);
     if (e != hipSuccess) return hip_fail(e, "sample launch");
+    ps.done((double)B * V * 4 * 2);
     // 3: stand-in encoder: e row and memory entry pos of every group
     EncodeArgs ea;
     ea.tokens = dev_tokens + j;
@@ -898,8 +901,10 @@ rlt_status rlt_generate(const rlt_model *m, rlt_state *st, int32_t n_steps,
     ea.dh = c.head_dim;
     ea.V = V;
     ea.G = c.mem_groups;
+    Prof pe(st, RLT_K_EXTRA, s);
     e = launch_encode(c.dtype, ea, B, s);
     if (e != hipSuccess) return hip_fail(e, "encode launch");
+    pe.done((double)B * (d + 2.0 * c.mem_groups * d) * m->esize * 2);
     // 4: consume it once; the logits of the new state go to the scratch (and
     // to dev_logits_last on the last step)
     float *lg = (j == n_steps - 1 && dev_logits_last) ? dev_logits_last : st->lscratch;

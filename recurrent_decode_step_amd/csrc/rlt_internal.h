@@ -100,10 +100,11 @@ hipError_t launch_pack_tiles(const void *src, int rows, int K, int64_t ld, int t
                              int tile_end, const PackedMat &dst, int dtype, hipStream_t s);
 hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const GemmArgs &a, int tiles,
                        int col_groups, int parts, hipStream_t s);
-// Large batches (bf16, plain activations, 32-row column groups): persistent
-// GEMM with the same arithmetic as launch_gemm; returns hipErrorInvalidValue
-// when the shape is not one it takes (the caller then uses launch_gemm).
-hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int tiles, int col_groups,
+// Large batches (bf16, plain activations, more than 64 rows): persistent
+// GEMM with the same arithmetic as launch_gemm.  gemm_persistent_applies
+// says whether it takes a shape; launch_gemm_persistent reports real errors.
+bool gemm_persistent_applies(int dtype, int act, int epi, int n_rows, int KT, int parts);
+hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int tiles, int n_rows,
                                   int parts, hipStream_t s);
 // log softmax of each row's logits at its realized token (one workgroup per row)
 hipError_t launch_score(const ScoreArgs &a, int n_rows, hipStream_t s);

@@ -567,7 +567,7 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
         for (int cb = 0; cb < NCB; ++cb) acc[cb] = mma_step(w[j], av[j][cb], acc[cb], T());
       }
   };
-  u32x4 wa[SC], wb[SC], wc[SC];
+  u32x4 wa[SC], wb[SC], wc[NCB >= 4 ? 1 : SC];
   if (nt > 0) {
     aload(0, min(SC, nks));
     wload(wa, tile_of(0), 0, min(SC, nks));
@@ -602,44 +602,43 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
 
   // partial tiles of all parts through LDS (buffer `buf`, alternating from
   // tile to tile), added in part order; column block cb is finished by
-  // wavefront cb mod NW (one wavefront: both blocks).  A buffer is rewritten
-  // two tiles later, after every wavefront has passed the next tile's barrier.
-  static_assert(NCB <= 2, "column blocks per wavefront");
+  // wavefront cb mod NW.  A buffer is rewritten two tiles later, after every
+  // wavefront has passed the next tile's barrier.
   auto reduce_store = [&](int buf, const f32x4 *acc, int tile, bool pre, f32x4 xp, f32x4 gp) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) s_acc[buf][wave][cb][lane] = acc[cb];
     __syncthreads();
-    if (wave < NCB) {
-      f32x4 y = s_acc[buf][0][wave][lane];
-      for (int w = 1; w < NW; ++w) y += s_acc[buf][w][wave][lane];
-      const int c = wave * 16 + (lane & 15);
-      gemm_epilogue<T, EPI>(a, y, tile, c, col0, ncols, SCALED ? s_rinv[c] : 1.f, pre, xp, gp, lane);
-    }
-    if (wave + NW < NCB) {
-      f32x4 y = s_acc[buf][0][wave + NW][lane];
-      for (int w = 1; w < NW; ++w) y += s_acc[buf][w][wave + NW][lane];
-      const int c = (wave + NW) * 16 + (lane & 15);
-      gemm_epilogue<T, EPI>(a, y, tile, c, col0, ncols, SCALED ? s_rinv[c] : 1.f, false, xp, gp, lane);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      if (cb % NW == wave) {
+        f32x4 y = s_acc[buf][0][cb][lane];
+        for (int w = 1; w < NW; ++w) y += s_acc[buf][w][cb][lane];
+        const int c = cb * 16 + (lane & 15);
+        gemm_epilogue<T, EPI>(a, y, tile, c, col0, ncols, SCALED ? s_rinv[c] : 1.f,
+                              pre && cb == wave, xp, gp, lane);
+      }
     }
   };
   auto prefetch_x = [&](int tile, f32x4 &xp, f32x4 &gp) {
     if constexpr (EPI == EPI_RESID) {
-      if (wave < NCB) {
-        const int rb = tile * 16 + (lane >> 4) * 4;
-        const int c = min(wave * 16 + (lane & 15), ncols - 1);
-        xp = *reinterpret_cast<const f32x4 *>(a.x + (size_t)(col0 + c) * a.d + rb);
-        gp = *reinterpret_cast<const f32x4 *>(a.gamma_next + rb);
-      }
+      // every wavefront loads (clamped column block), only cb < NCB uses it
+      const int rb = tile * 16 + (lane >> 4) * 4;
+      const int c = min(min(wave, NCB - 1) * 16 + (lane & 15), ncols - 1);
+      xp = *reinterpret_cast<const f32x4 *>(a.x + (size_t)(col0 + c) * a.d + rb);
+      gp = *reinterpret_cast<const f32x4 *>(a.gamma_next + rb);
     }
   };
 
   if constexpr (SHORT) {
     // parts of at most SC k-steps (the launcher checks): one tile after
     // another, the activations stay in registers
-    // three weight buffers: tile i multiplies while tiles i+1 and i+2 load
-    auto one = [&](int i, u32x4 *wcur, u32x4 *wnext2) {
+    // weight buffers: with two column blocks three (tile i multiplies while
+    // tiles i+1 and i+2 load), with four two (the activations take the room)
+    auto one = [&](int i, u32x4 *wcur, u32x4 *wnext) {
       const int tile = tile_of(i);
-      if (i + 2 < nt) wload(wnext2, tile_of(i + 2), 0, nks);
+      // unconditional (clamped) so every wavefront issues the same loads in
+      // every iteration and the waits stay counted, not drained
+      wload(wnext, tile_of(min(i + (NCB >= 4 ? 1 : 2), nt - 1)), 0, nks);
       f32x4 xp = f32x4{0.f, 0.f, 0.f, 0.f}, gp = xp;
       prefetch_x(tile, xp, gp);
       f32x4 acc[NCB];
@@ -648,11 +647,18 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
       chain(acc, wcur, nks);
       reduce_store(i & 1, acc, tile, true, xp, gp);
     };
-    if (nt > 1) wload(wb, tile_of(1), 0, nks);
-    for (int i = 0; i < nt; i += 3) {
-      one(i, wa, wc);
-      if (i + 1 < nt) one(i + 1, wb, wa);
-      if (i + 2 < nt) one(i + 2, wc, wb);
+    if constexpr (NCB >= 4) {
+      for (int i = 0; i < nt; i += 2) {
+        one(i, wa, wb);
+        if (i + 1 < nt) one(i + 1, wb, wa);
+      }
+    } else {
+      wload(wb, tile_of(min(1, nt - 1)), 0, nks);
+      for (int i = 0; i < nt; i += 3) {
+        one(i, wa, wc);
+        if (i + 1 < nt) one(i + 1, wb, wa);
+        if (i + 2 < nt) one(i + 2, wc, wb);
+      }
     }
   } else {
     // chunks of SC k-steps outer, two tiles inner (wa: first tile, wb: second)
@@ -1319,12 +1325,31 @@ static hipError_t attn_dispatch(int dh, const AttnArgs &a, int n_rows, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int tiles, int col_groups,
+constexpr int kPersistentWorkgroups = 256;   // one per CU
+
+// parts of at most 8 k-steps keep the activations in registers, 64-row
+// column groups (32 for the residual epilogue, whose registers it needs);
+// longer parts stream them in chunks, 32-row groups
+static bool persistent_short(int KT, int parts) { return (KT + parts - 1) / parts <= 8; }
+static int persistent_ncb(int epi, int KT, int parts) {
+  return persistent_short(KT, parts) && epi != EPI_RESID ? 4 : 2;
+}
+
+bool gemm_persistent_applies(int dtype, int act, int epi, int n_rows, int KT, int parts) {
+  if (dtype != RLT_DTYPE_BF16 || act != ACT_PLAIN || n_rows <= 64 || parts < 1 || parts > kMaxParts)
+    return false;
+  const int ncb = persistent_ncb(epi, KT, parts);
+  return 8 * ((n_rows + 16 * ncb - 1) / (16 * ncb)) <= kPersistentWorkgroups;
+}
+
+hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int tiles, int n_rows,
                                   int parts, hipStream_t s) {
-  constexpr int kWorkgroups = 256;               // one per CU
-  if (dtype != RLT_DTYPE_BF16 || parts < 1 || parts > kMaxParts || col_groups < 1 ||
-      8 * col_groups > kWorkgroups || tiles < 1)
+  constexpr int kWorkgroups = kPersistentWorkgroups;
+  if (!gemm_persistent_applies(dtype, ACT_PLAIN, epi, n_rows, a.KT, parts) || tiles < 1)
     return hipErrorInvalidValue;
+  const bool short_k = persistent_short(a.KT, parts);
+  const int ncb = persistent_ncb(epi, a.KT, parts);
+  const int col_groups = (n_rows + 16 * ncb - 1) / (16 * ncb);
   GemmArgs b = a;
   b.tile_groups = tiles;
   b.col_groups = col_groups;
@@ -1333,18 +1358,17 @@ hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int til
   const int l8 = std::max(1, std::min(kWorkgroups / (8 * col_groups), per_xcd));
   const dim3 grid((unsigned)(8 * col_groups * l8));
   const int threads = parts * 64;
-  const bool short_k = (a.KT + parts - 1) / parts <= 8;
-#define RLT_GP(E)                                                             \
+#define RLT_GP(E, NC)                                                         \
   case E:                                                                     \
-    if (short_k) k_gemm_p<bf16_t, 2, E, true><<<grid, threads, 0, s>>>(b);     \
+    if (short_k) k_gemm_p<bf16_t, NC, E, true><<<grid, threads, 0, s>>>(b);    \
     else k_gemm_p<bf16_t, 2, E, false><<<grid, threads, 0, s>>>(b);           \
     break;
   switch (epi) {
-    RLT_GP(EPI_QKV)
-    RLT_GP(EPI_STORE)
-    RLT_GP(EPI_RESID)
-    RLT_GP(EPI_GELU)
-    RLT_GP(EPI_LOGITS)
+    RLT_GP(EPI_QKV, 4)
+    RLT_GP(EPI_STORE, 4)
+    RLT_GP(EPI_RESID, 2)
+    RLT_GP(EPI_GELU, 4)
+    RLT_GP(EPI_LOGITS, 4)
     default: return hipErrorInvalidValue;
   }
 #undef RLT_GP

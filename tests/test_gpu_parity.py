@@ -261,6 +261,16 @@ def test_large_batch_kernels_match_small_batch_bitwise(shape):
         for g in groups:
             out[g, j] = binding.rlt_decoder_step(rig.model, st, rig.ed[g, j], rig.mem, slots=g).cpu()
     assert torch.equal(out, full)
+    # more than 64 rows through an explicit, permuted slot list (persistent GEMM
+    # with slots), the remaining rows in a second call
+    st2 = rig.state()
+    perm = [int(x) for x in np.random.default_rng(9).permutation(B)]
+    big, rest = perm[:80], perm[80:]
+    out2 = torch.empty_like(full)
+    for j in range(T):
+        for g in (big, rest):
+            out2[g, j] = binding.rlt_decoder_step(rig.model, st2, rig.ed[g, j], rig.mem, slots=g).cpu()
+    assert torch.equal(out2, full)
 
 
 def test_memory_causality_bitwise():
@@ -417,6 +427,23 @@ def test_position_past_memory_is_rejected_without_side_effects():
     assert ei.value.status == binding.RLT_ERR_INVALID_ARG
     after = binding.rlt_state_export(rig.model, st, [0, 1])
     assert torch.equal(before, after)
+    assert st.position(0) == 4
+    # replay scoring and generation check the same bounds before any work
+    with pytest.raises(binding.RLTError) as ei:
+        binding.rlt_score_sequence(rig.model, st, rig.ed[:, :1], rig.mem,
+                                   torch.zeros((2, 1), dtype=torch.int32, device=DEV))
+    assert ei.value.status == binding.RLT_ERR_RANGE
+    te, tk, tv = (t.to(DEV) for t in synth.encoder_tables(cfg, device="cpu"))
+    logits0 = torch.zeros((2, cfg.vocab), device=DEV)
+    with pytest.raises(binding.RLTError) as ei:
+        binding.rlt_generate(rig.model, st, logits0, te, tk, tv, rig.mem, 1.0, 4,
+                             torch.zeros((2, 1), device=DEV))
+    assert ei.value.status == binding.RLT_ERR_RANGE
+    with pytest.raises(binding.RLTError) as ei:
+        binding.rlt_generate(rig.model, st, logits0, te, tk, tv, rig.mem, 0.0, 4,
+                             torch.zeros((2, 1), device=DEV))
+    assert ei.value.status == binding.RLT_ERR_INVALID_ARG
+    assert torch.equal(before, binding.rlt_state_export(rig.model, st, [0, 1]))
     assert st.position(0) == 4
 
 
