@@ -1,4 +1,5 @@
-"""CPU oracle of the recurrent decoder step (test infrastructure only).
+"""CPU oracle of the recurrent decoder step and the causal encoder (test
+infrastructure only).
 
 Only the test suite, the smoke check of the package entry file and the
 benchmark's CPU-baseline leg may import anything from this package.  The HIP
@@ -8,10 +9,11 @@ from .rlt_oracle import (Model, SeqState, round_bf16, initial_state, state_from_
                          copy_state, decoder_step, run_sequence, token_log_prob, score_sequence,
                          sampling_weights, sample_token, generate)
 from .brute import brute_force_run
+from .encoder import Encoder, encode, prefill
 from .parallel import parallel_swa_pass
 
 __all__ = ["Model", "SeqState", "round_bf16", "initial_state", "state_from_arrays",
            "copy_state", "decoder_step", "run_sequence", "token_log_prob", "score_sequence",
            "sampling_weights", "sample_token", "generate",
-           "brute_force_run",
+           "brute_force_run", "Encoder", "encode", "prefill",
            "parallel_swa_pass"]

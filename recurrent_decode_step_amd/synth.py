@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for the recurrent decoder step.
 
-This module only draws random numbers: decoder weights, encoder outputs e_t,
-encoder memory K/V, ragged positions and imported decoder states.  It holds no
+This module only draws random numbers: decoder and encoder weights, token ids,
+encoder outputs e_t, encoder memory K/V, ragged positions and imported decoder
+states.  It holds no
 part of the decoder's arithmetic and is shared by the tests, the benchmark and
 the oracle's callers; neither the oracle nor the HIP library imports it.
 
@@ -10,7 +11,8 @@ Recipe (the same for every workload):
 * every tensor comes from its own torch generator whose seed is derived from
   (seed, kind, layer, index) by numpy's SeedSequence, so any single tensor can
   be regenerated alone;
-* seeds: weights 0, e_t 1, memory 2, positions 3, imported states 4;
+* seeds: weights 0, e_t 1, memory 2, positions 3, imported states 4, stand-in
+  encoder tables and uniforms 5, encoder parameters 6, token ids 7;
 * weight matrices, s*, b_g ~ N(0, 0.02); RMSNorm gains = 1 + N(0, 0.02);
   e_t, memory K/V and imported states ~ N(0, 1);
 * bf16 models round every drawn value to bf16 (round to nearest even) before
@@ -172,3 +174,32 @@ def uniforms(shape, device="cpu", seed=SEED_TABLES, index=0) -> torch.Tensor:
     """Uniform numbers in [0, 1) for sampling, from the (seed, 3, 0, index) stream."""
     g = _generator(device, seed, 3, 0, index)
     return torch.rand(tuple(shape), generator=g, device=device, dtype=torch.float32)
+
+
+SEED_ENCODER, SEED_TOKENS = 6, 7
+K_EMB, K_GE, K_WKM, K_WVM = 1, 2, 3, 4
+
+
+def encoder_params(cfg: ModelConfig, device="cpu", seed=SEED_ENCODER) -> dict:
+    """Encoder-only parameters (the encoder's blocks reuse the decoder's
+    weights): token embedding emb [V][d] ~ N(0, 1) and memory projections
+    wkm, wvm [G][d][d] ~ N(0, 0.02) in the storage dtype; the final RMSNorm
+    gain ge [d] = 1 + N(0, 0.02) as fp32 holding storage-dtype values."""
+    bf = cfg.dtype == DTYPE_BF16
+    sd = storage_dtype(cfg)
+    V, d, G = cfg.vocab, cfg.d_model, cfg.mem_groups
+    kw = dict(device=device, seed=seed, round_bf16=bf)
+    return {
+        "emb": normal((V, d), kind=K_EMB, out_dtype=sd, **kw),
+        "ge": normal((d,), mean=1.0, std=0.02, kind=K_GE, **kw),
+        "wkm": torch.stack([normal((d, d), std=0.02, kind=K_WKM, layer=g, out_dtype=sd, **kw)
+                            for g in range(G)]),
+        "wvm": torch.stack([normal((d, d), std=0.02, kind=K_WVM, layer=g, out_dtype=sd, **kw)
+                            for g in range(G)]),
+    }
+
+
+def token_ids(batch: int, steps: int, vocab: int, seed=SEED_TOKENS, index: int = 0) -> np.ndarray:
+    """Token ids [batch][steps] ~ U{0..vocab-1} (int32)."""
+    rng = np.random.default_rng([seed, index, 0, 0])
+    return rng.integers(0, vocab, size=(batch, steps)).astype(np.int32)

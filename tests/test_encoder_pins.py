@@ -1,0 +1,208 @@
+"""Pins of the CPU oracle's causal encoder and memory projection (no GPU).
+
+Titles of the pages cited:
+  [Article]   Recurrent Looped Transformer: A New Architecture for Infinite Context
+              Reasoning in Language Models
+  [Tutorial]  Understanding and Applying the Recurrent Looped Transformer Architecture
+  [Princeton] Princeton Researcher Proposes Recurrent Looped Transformer to Carry
+              Decoder State Across Tokens
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from _tiny import tiny_cfg, make_model, np64
+from recurrent_decode_step_amd import synth
+
+
+def enc_model(cfg, precision="fp64", params=None, eparams=None):
+    model, params = make_model(cfg, params=params, precision=precision)
+    eparams = eparams if eparams is not None else synth.encoder_params(cfg)
+    return oracle.Encoder(model, eparams), params, eparams
+
+
+def torch_encoder(cfg, params, eparams, tokens):
+    """The same network from torch library routines in float64: embedding,
+    rms_norm, linear, scaled_dot_product_attention under its causal mask, exact
+    GELU.  Returns e [T][d], mem_k, mem_v [G][H][T][dh]."""
+    d, H, dh, L = cfg.d_model, cfg.n_heads, cfg.head_dim, cfg.n_layers
+    P = {k: v.double() for k, v in params.items()}
+    E = {k: v.double() for k, v in eparams.items()}
+    tok = torch.as_tensor(np.asarray(tokens), dtype=torch.long)
+    T = tok.numel()
+    x = F.embedding(tok, E["emb"])
+    for l in range(L):
+        a = F.rms_norm(x, (d,), weight=P["g1"][l], eps=cfg.rms_eps)
+        q = F.linear(a, P["wq"][l]).reshape(T, H, dh).transpose(0, 1)
+        k = F.linear(a, P["wk"][l]).reshape(T, H, dh).transpose(0, 1)
+        v = F.linear(a, P["wv"][l]).reshape(T, H, dh).transpose(0, 1)
+        o = F.scaled_dot_product_attention(q[None], k[None], v[None], is_causal=True)[0]
+        x = x + F.linear(o.transpose(0, 1).reshape(T, d), P["wo"][l])
+        f = F.rms_norm(x, (d,), weight=P["g3"][l], eps=cfg.rms_eps)
+        x = x + F.linear(F.gelu(F.linear(f, P["w1"][l]), approximate="none"), P["w2"][l])
+    e = F.rms_norm(x, (d,), weight=E["ge"], eps=cfg.rms_eps)
+    mk = torch.stack([F.linear(e, E["wkm"][g]).reshape(T, H, dh).transpose(0, 1)
+                      for g in range(cfg.mem_groups)])
+    mv = torch.stack([F.linear(e, E["wvm"][g]).reshape(T, H, dh).transpose(0, 1)
+                      for g in range(cfg.mem_groups)])
+    return e.numpy(), mk.numpy(), mv.numpy()
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_encoder_matches_torch_library(G):
+    """Causal transformer under a causal mask with the decoder's layer weights,
+    memory projected from e_t per group [Article, "Encoder-Decoder Pairing with
+    Shared Weights"; Princeton, architecture paragraph]: the oracle against the
+    same network assembled from torch's own routines (causal SDPA, rms_norm,
+    linear, erf GELU), float64."""
+    cfg = tiny_cfg(mem_groups=G)
+    enc, params, eparams = enc_model(cfg)
+    tokens = synth.token_ids(1, 13, cfg.vocab, index=G)[0]
+    r = oracle.encode(enc, tokens)
+    e, mk, mv = torch_encoder(cfg, params, eparams, tokens)
+    np.testing.assert_allclose(r["e"], e, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["mem_k"], mk, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["mem_v"], mv, rtol=0, atol=1e-12)
+
+
+def test_encoder_is_causal():
+    """Each position sees only itself and earlier tokens [Article, "Encoder-Decoder
+    Pairing with Shared Weights": causal mask]: changing token j leaves every
+    output row before j bitwise unchanged and changes row j."""
+    cfg = tiny_cfg()
+    enc, _, _ = enc_model(cfg, precision="fp32")
+    x = synth.token_ids(1, 12, cfg.vocab, index=3)[0]
+    for j in (0, 5, 11):
+        y = x.copy()
+        y[j] = (y[j] + 1) % cfg.vocab
+        a, b = oracle.encode(enc, x), oracle.encode(enc, y)
+        np.testing.assert_array_equal(a["e"][:j], b["e"][:j])
+        np.testing.assert_array_equal(a["cache_k"][:, :j], b["cache_k"][:, :j])
+        np.testing.assert_array_equal(a["mem_k"][:, :, :j], b["mem_k"][:, :, :j])
+        assert not np.array_equal(a["e"][j], b["e"][j])
+        # a prefix encodes to the prefix of the rows (up to the fp32 rounding
+        # of the matrix library, whose blocking depends on the row count)
+        p = oracle.encode(enc, x[:j + 1])
+        np.testing.assert_allclose(p["e"], a["e"][:j + 1], rtol=0, atol=1e-6)
+
+
+def test_encoder_uniform_scores_give_prefix_mean():
+    """With W_Q = 0 every score is equal, so position i's attention output is the
+    plain mean of the values at positions 1..i (closed form; pins the causal
+    range, its inclusion of i itself and the softmax normalisation)."""
+    cfg = tiny_cfg()
+    _, params = make_model(cfg, precision="fp64")
+    p = dict(params)
+    p["wq"] = torch.zeros_like(params["wq"])
+    enc, _, _ = enc_model(cfg, params=p)
+    tr = {}
+    oracle.encode(enc, synth.token_ids(1, 9, cfg.vocab, index=4)[0], trace=tr)
+    for l in range(cfg.n_layers):
+        v, o = tr["v"][l], tr["o"][l]
+        want = np.cumsum(v, axis=0) / np.arange(1, v.shape[0] + 1)[:, None, None]
+        np.testing.assert_allclose(o, want, rtol=0, atol=1e-13)
+
+
+def test_single_token_ignores_query_and_key_weights():
+    """Softmax over a single position is 1: a one-token prompt's output does not
+    depend on W_Q or W_K; a two-token prompt's does."""
+    cfg = tiny_cfg()
+    _, params = make_model(cfg, precision="fp64")
+    p = dict(params)
+    p["wq"] = params["wq"] * 3.0
+    p["wk"] = -params["wk"]
+    a, _, ep = enc_model(cfg)
+    b, _, _ = enc_model(cfg, params=p, eparams=ep)
+    tok = synth.token_ids(1, 2, cfg.vocab, index=5)[0]
+    np.testing.assert_allclose(oracle.encode(a, tok[:1])["e"], oracle.encode(b, tok[:1])["e"],
+                               rtol=0, atol=1e-14)
+    assert np.abs(oracle.encode(a, tok)["e"][1] - oracle.encode(b, tok)["e"][1]).max() > 1e-6
+
+
+def test_encoder_reads_only_the_tied_weights():
+    """Weight tying [Article, "Encoder-Decoder Pairing with Shared Weights"]: the
+    encoder reuses decoder layer l's attention and FFN weights; the decoder-only
+    cross-attention, gate, start state and head play no part."""
+    cfg = tiny_cfg()
+    _, params = make_model(cfg, precision="fp64")
+    tok = synth.token_ids(1, 7, cfg.vocab, index=6)[0]
+    base, _, ep = enc_model(cfg, params=params)
+    ref = oracle.encode(base, tok)
+    for key in ("g2", "wqc", "woc", "wg", "bg", "s_star", "go", "wout"):
+        p = dict(params)
+        p[key] = params[key] * 1.5 + 0.25
+        got = oracle.encode(enc_model(cfg, params=p, eparams=ep)[0], tok)
+        np.testing.assert_array_equal(got["e"], ref["e"])
+    for key in ("g1", "wq", "wk", "wv", "wo", "g3", "w1", "w2"):
+        p = dict(params)
+        p[key] = params[key].clone()
+        p[key][cfg.n_layers - 1] = p[key][cfg.n_layers - 1] * 1.5
+        got = oracle.encode(enc_model(cfg, params=p, eparams=ep)[0], tok)
+        assert np.abs(got["e"] - ref["e"]).max() > 1e-9, key
+
+
+def test_memory_projection_identity_splits_heads():
+    """With W_Km = I and W_Vm = -(g+1) I the memory is e_t itself split into
+    heads: K[g][h][t][c] = e_t[h*dh + c] (pins the head split and the [G][H][T][dh]
+    layout the decoder reads); groups are independent projections of one e_t
+    [Princeton, architecture paragraph: G = 1 or G = L]."""
+    cfg = tiny_cfg(mem_groups=2)
+    d, H, dh, G = cfg.d_model, cfg.n_heads, cfg.head_dim, 2
+    ep = synth.encoder_params(cfg)
+    ep = dict(ep)
+    eye = torch.eye(d)
+    ep["wkm"] = torch.stack([eye] * G)
+    ep["wvm"] = torch.stack([-(g + 1) * eye for g in range(G)])
+    enc, _, _ = enc_model(cfg, eparams=ep)
+    r = oracle.encode(enc, synth.token_ids(1, 5, cfg.vocab, index=7)[0])
+    e = r["e"]
+    for g in range(G):
+        for h in range(H):
+            np.testing.assert_array_equal(r["mem_k"][g, h], e[:, h * dh:(h + 1) * dh])
+            np.testing.assert_array_equal(r["mem_v"][g, h], -(g + 1) * e[:, h * dh:(h + 1) * dh])
+
+
+def test_bf16_encoder_stores_bf16_values():
+    """A bf16 model stores e_t, the memory entries and the encoder's k, v in bf16:
+    every such value of the bf16 emulation is a bf16 number, and the fp32
+    emulation stays within bf16 rounding of it."""
+    cfg = tiny_cfg(dtype=1)
+    enc, params, ep = enc_model(cfg, precision="bf16")
+    tok = synth.token_ids(1, 10, cfg.vocab, index=8)[0]
+    r = oracle.encode(enc, tok)
+    for key in ("e", "mem_k", "mem_v", "cache_k", "cache_v"):
+        np.testing.assert_array_equal(oracle.round_bf16(r[key]), r[key])
+    r32 = oracle.encode(enc_model(cfg, precision="fp32", params=params, eparams=ep)[0], tok)
+    rel = np.linalg.norm(r["e"] - r32["e"]) / np.linalg.norm(r32["e"])
+    assert rel < 2e-2
+
+
+def test_encoder_rejects_out_of_vocabulary_tokens():
+    cfg = tiny_cfg()
+    enc, _, _ = enc_model(cfg, precision="fp32")
+    with pytest.raises(ValueError):
+        oracle.encode(enc, [0, cfg.vocab])
+    with pytest.raises(ValueError):
+        oracle.encode(enc, [-1])
+
+
+def test_prefill_runs_decoder_over_every_prompt_token():
+    """Prompt prefill is the encoder over the prompt and then the decoder
+    recurrence over every prompt token [Tutorial, "Prompt prefill"]: the
+    decoder states end at position T, and their logits are those of decoding
+    the encoder's e rows with its memory."""
+    cfg = tiny_cfg()
+    enc, _, _ = enc_model(cfg, precision="fp64")
+    tok = synth.token_ids(2, 6, cfg.vocab, index=9)
+    st = [oracle.initial_state(enc.m) for _ in range(2)]
+    logits, e, mk, mv = oracle.prefill(enc, st, tok)
+    assert all(s.pos == 6 for s in st)
+    st2 = [oracle.initial_state(enc.m) for _ in range(2)]
+    np.testing.assert_array_equal(oracle.run_sequence(enc.m, st2, e, mk, mv), logits)
+    for i in range(2):
+        r = oracle.encode(enc, tok[i])
+        np.testing.assert_array_equal(r["mem_k"], mk[:, i])
