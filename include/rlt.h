@@ -207,8 +207,9 @@ rlt_status rlt_score_sequence(const rlt_model *m, rlt_state *st, int32_t T, cons
 
 /* --------------------------------------------------------- generation */
 /* Stand-in incremental encoder for generation: lookup tables of the token.
- * The causal encoder itself is not part of this library; a generated token's
- * e_t and memory entry come from these tables (device pointers, model dtype):
+ * A generated token's e_t and memory entry come from these tables (device
+ * pointers, model dtype); the causal encoder (rlt_encode) is not run inside
+ * this loop:
  *   e  [V][d]            e_t of token v
  *   k, v [G][V][H][dh]   memory K / V entry of token v in group g */
 typedef struct {
@@ -247,6 +248,103 @@ rlt_status rlt_generate(const rlt_model *m, rlt_state *st, int32_t n_steps,
                         const rlt_memory *mem, const rlt_sampling *smp, const float *dev_u,
                         int32_t *dev_tokens, float *dev_logprob, float *dev_logits_last,
                         void *stream);
+
+/* ------------------------------------------------------------ encoder */
+/* The causal encoder [Article, "Encoder-Decoder Pairing with Shared Weights"
+ * and "Principle 2: Co-Design Between Model and Hardware"; Princeton,
+ * architecture paragraph; Tutorial, "Prompt prefill"]: all known tokens of a
+ * sequence at once under a causal mask, as many layers as the decoder, layer l
+ * using decoder layer l's attention and feed-forward weights; the memory
+ * M_<=t is projected from e_t once per memory group.  For token x at encoder
+ * position p (0-based) of its sequence:
+ *   x = emb[x]
+ *   per layer l = 0..L-1:
+ *     x += W_O[l] CausalAttn(W_Q[l] a, W_K[l] a, W_V[l] a),  a = RMSNorm(x; g1[l])
+ *          over positions 0..p of the sequence (itself included; keys and
+ *          values of earlier calls come from the encoder cache)
+ *     x += W_2[l] GELU(W_1[l] RMSNorm(x; g3[l]))
+ *   e = RMSNorm(x; g_e)
+ *   memory entry p of group g: K = W_Km[g] e, V = W_Vm[g] e, split into heads
+ * Readings where the pages leave the step open: a learned token embedding, no
+ * positional encoding, the tied weights include the two RMSNorm gains, the
+ * encoder's own final gain g_e, memory projections without bias.  Precision as
+ * for the decoder; e and the memory entries are stored in the model dtype (the
+ * bf16 attention also rounds its softmax weights to bf16 for the P V product). */
+typedef struct {
+  const void *emb;              /* [V][d]    token embedding, model dtype         */
+  const void *ge;               /* [d]       fp32 final RMSNorm gain g_e           */
+  const void *wkm, *wvm;        /* [G][d][d] memory K / V projections, model dtype */
+} rlt_encoder_params;
+
+typedef struct rlt_encoder rlt_encoder;
+typedef struct rlt_encoder_state rlt_encoder_state;
+
+/* Bytes of device memory the encoder-only weights need; 0 if the model is
+ * NULL or its configuration is outside the encoder kernels (bf16 needs
+ * head_dim >= 32). */
+size_t rlt_encoder_bytes(const rlt_model *m);
+
+/* Copy and repack `src` into dev_buf (>= rlt_encoder_bytes, 256-byte aligned)
+ * with kernels on `stream`; src is not retained.  The encoder reads the tied
+ * layer weights from m's buffer: m must outlive it. */
+rlt_status rlt_encoder_create(const rlt_model *m, const rlt_encoder_params *src, void *dev_buf,
+                              size_t bytes, void *stream, rlt_encoder **out);
+void rlt_encoder_destroy(rlt_encoder *enc);   /* frees the host handle only */
+
+/* Bytes for an encoder state of `batch` slots: the encoder cache K, V
+ * [L][B][H][max_tokens][dh] (model dtype; position p of slot b, layer l, head h
+ * at ((l*B + b)*H + h)*max_tokens + p), a slot table, and scratch for up to
+ * max_rows tokens per rlt_encode call (fp32 residual stream [rows][d];
+ * normalised inputs, q, attention output and e rows [rows][d] and the FFN
+ * hidden layer [rows][F] in the model dtype).  0 on a bad argument. */
+size_t rlt_encoder_state_bytes(const rlt_config *cfg, int32_t batch, int32_t max_tokens,
+                               int32_t max_rows);
+
+/* Lay out an encoder state in dev_buf with every slot at position 0 (no
+ * tokens encoded).  No device work. */
+rlt_status rlt_encoder_state_init(const rlt_encoder *enc, int32_t batch, int32_t max_tokens,
+                                  int32_t max_rows, void *dev_buf, size_t bytes,
+                                  rlt_encoder_state **out);
+void rlt_encoder_state_destroy(rlt_encoder_state *es);
+
+/* Set the listed slots back to position 0 (a new document).  Host only. */
+rlt_status rlt_encoder_state_reset(rlt_encoder_state *es, int32_t n, const int32_t *host_slots);
+
+/* Tokens encoded so far in a slot; -1 on a bad argument. */
+int32_t rlt_encoder_position(const rlt_encoder_state *es, int32_t slot);
+
+/* Encode the next T tokens of each of n listed slots (host_slots NULL = slots
+ * 0..n-1; slots distinct):
+ *   dev_tokens [n][T] int32: row i holds the next T tokens of slot host_slots[i];
+ *              a token outside 0..V-1 makes its sequence's outputs NaN from that
+ *              token on (earlier tokens of that sequence in the same call may be
+ *              NaN too); other sequences are not affected
+ *   dev_e      [n][T][d] model dtype out, 16-byte aligned (NULL: e is kept in
+ *              the state's scratch only)
+ *   mem        caller memory, WRITTEN: for sequence index = slot, positions
+ *              p0..p0+T-1 of every group, p0 = the slot's position before the call
+ * Token j of slot s is encoder position p0_s + j and attends to positions
+ * 0..p0_s + j, so a prompt encoded in one call or in several chunks gives the
+ * same values up to the summation order of the softmax.  Each slot's position
+ * advances by T.  RLT_ERR_SHAPE if n*T > max_rows; RLT_ERR_RANGE if a position
+ * would pass max_tokens or the memory capacity.  A prompt's prefill is this
+ * call followed by rlt_run_sequence over dev_e (the decoder recurrence over
+ * every prompt token [Tutorial, "Prompt prefill"]). */
+rlt_status rlt_encode(const rlt_encoder *enc, rlt_encoder_state *es, int32_t n,
+                      const int32_t *host_slots, int32_t T, const int32_t *dev_tokens,
+                      void *dev_e, const rlt_memory *mem, void *stream);
+
+/* Encoder kernel timing, as rlt_profile_begin with every call one step:
+ * RLT_E_GEMM = the token-parallel GEMMs, RLT_E_ATTN = causal attention,
+ * RLT_E_OTHER = embedding and RMSNorm.  Collect returns the recorded launch
+ * durations (ms), their count, their algorithmic FLOPs (2 per multiply-add of
+ * the GEMMs, 4 * d per attended position of attention; 0 for OTHER) and bytes
+ * (weights, activations in and out, cache positions read once per sequence). */
+enum { RLT_E_GEMM = 0, RLT_E_ATTN = 1, RLT_E_OTHER = 2, RLT_E_NCLASSES = 3 };
+rlt_status rlt_encoder_profile_begin(rlt_encoder_state *es, int32_t class_mask,
+                                     int32_t max_launches);
+rlt_status rlt_encoder_profile_collect(rlt_encoder_state *es, int32_t kclass, double *total_ms,
+                                       int32_t *launches, double *flops, double *bytes_moved);
 
 /* Host mirror of a slot's position (tokens consumed); -1 on a bad argument.
  * Does not synchronise. */

@@ -1,6 +1,6 @@
 """Thin Python binding of librlt.so (ctypes).  Argument marshalling only:
 torch supplies device memory and the current HIP stream; every step of the
-decoder runs in the library's HIP kernels.  The functions keep the C names
+decoder and the encoder runs in the library's HIP kernels.  The functions keep the C names
 (rlt_decoder_step, rlt_run_sequence, ...); the classes wrap the handles.
 
 Loading fails loudly when the library is missing: there is no fallback.
@@ -21,13 +21,18 @@ RLT_OK, RLT_ERR_INVALID_ARG, RLT_ERR_SHAPE, RLT_ERR_RANGE, RLT_ERR_STALE, \
     RLT_ERR_CONVENTION, RLT_ERR_UNSUPPORTED, RLT_ERR_DEVICE = range(8)
 RLT_LOGITS_ALL, RLT_LOGITS_LAST, RLT_LOGITS_NONE = 0, 1, 2
 RLT_K_EXTRA, RLT_K_GEMM, RLT_K_SWA, RLT_K_CROSS = 0, 1, 2, 3
+RLT_E_GEMM, RLT_E_ATTN, RLT_E_OTHER = 0, 1, 2
 
 EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_bytes",
             "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",
             "rlt_state_destroy", "rlt_state_reset", "rlt_decoder_step", "rlt_run_sequence",
             "rlt_score_sequence", "rlt_generate",
             "rlt_state_position", "rlt_snapshot_bytes", "rlt_state_export", "rlt_state_import",
-            "rlt_profile_begin", "rlt_profile_collect")
+            "rlt_profile_begin", "rlt_profile_collect",
+            "rlt_encoder_bytes", "rlt_encoder_create", "rlt_encoder_destroy",
+            "rlt_encoder_state_bytes", "rlt_encoder_state_init", "rlt_encoder_state_destroy",
+            "rlt_encoder_state_reset", "rlt_encoder_position", "rlt_encode",
+            "rlt_encoder_profile_begin", "rlt_encoder_profile_collect")
 
 
 class RLTError(RuntimeError):
@@ -60,6 +65,10 @@ class rlt_encoder_table(C.Structure):
 
 class rlt_sampling(C.Structure):
     _fields_ = [("temperature", C.c_float), ("top_k", C.c_int32)]
+
+
+class rlt_encoder_params(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("emb", "ge", "wkm", "wvm")]
 
 
 _lib = None
@@ -98,6 +107,18 @@ def load_library(path: str = LIB_PATH):
         "rlt_state_import": (i32, [vp, vp, i32, P(i32), vp, vp]),
         "rlt_profile_begin": (i32, [vp, i32, i32, i32]),
         "rlt_profile_collect": (i32, [vp, i32, P(C.c_double), P(i32), P(C.c_double)]),
+        "rlt_encoder_bytes": (sz, [vp]),
+        "rlt_encoder_create": (i32, [vp, P(rlt_encoder_params), vp, sz, vp, P(vp)]),
+        "rlt_encoder_destroy": (None, [vp]),
+        "rlt_encoder_state_bytes": (sz, [P(rlt_config), i32, i32, i32]),
+        "rlt_encoder_state_init": (i32, [vp, i32, i32, i32, vp, sz, P(vp)]),
+        "rlt_encoder_state_destroy": (None, [vp]),
+        "rlt_encoder_state_reset": (i32, [vp, i32, P(i32)]),
+        "rlt_encoder_position": (i32, [vp, i32]),
+        "rlt_encode": (i32, [vp, vp, i32, P(i32), i32, vp, vp, P(rlt_memory), vp]),
+        "rlt_encoder_profile_begin": (i32, [vp, i32, i32]),
+        "rlt_encoder_profile_collect": (i32, [vp, i32, P(C.c_double), P(i32), P(C.c_double),
+                                              P(C.c_double)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -354,3 +375,116 @@ def profile_collect(state: State, kclass: int):
     _check(load_library().rlt_profile_collect(state.handle, kclass, C.byref(tot), C.byref(n),
                                               C.byref(b)))
     return tot.value, n.value, b.value
+
+
+# ---------------------------------------------------------------- encoder
+class Encoder:
+    """Encoder-only weights on the device (rlt_encoder_create); the layer
+    weights are the model's (tied)."""
+
+    def __init__(self, model: Model, params: dict, stream=None):
+        lib = load_library()
+        self.model = model
+        cfg = model.cfg
+        nbytes = lib.rlt_encoder_bytes(model.handle)
+        if nbytes == 0:
+            _check(RLT_ERR_UNSUPPORTED)
+        dev = model.buf.device
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        sd = torch.bfloat16 if cfg.dtype == DTYPE_BF16 else torch.float32
+        keep = {k: params[k].to(device=dev, dtype=torch.float32 if k == "ge" else sd).contiguous()
+                for k in ("emb", "ge", "wkm", "wvm")}
+        p = rlt_encoder_params(*[keep[n[0]].data_ptr() for n in rlt_encoder_params._fields_])
+        h = C.c_void_p()
+        _check(lib.rlt_encoder_create(model.handle, C.byref(p), self.buf.data_ptr(), nbytes,
+                                      _stream(stream), C.byref(h)))
+        self.handle = h
+        torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+        del keep
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.rlt_encoder_destroy(self.handle)
+            self.handle = None
+
+
+class EncoderState:
+    """Encoder cache and scratch of `batch` slots (rlt_encoder_state_init)."""
+
+    def __init__(self, encoder: Encoder, batch: int, max_tokens: int, max_rows: int):
+        lib = load_library()
+        self.encoder = encoder
+        self.batch = batch
+        self.max_tokens = max_tokens
+        self.max_rows = max_rows
+        nbytes = lib.rlt_encoder_state_bytes(C.byref(encoder.model.ccfg), batch, max_tokens,
+                                             max_rows)
+        if nbytes == 0:
+            _check(RLT_ERR_INVALID_ARG)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=encoder.buf.device)
+        h = C.c_void_p()
+        _check(lib.rlt_encoder_state_init(encoder.handle, batch, max_tokens, max_rows,
+                                          self.buf.data_ptr(), nbytes, C.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.rlt_encoder_state_destroy(self.handle)
+            self.handle = None
+
+    def position(self, slot: int) -> int:
+        return load_library().rlt_encoder_position(self.handle, slot)
+
+    def cache(self):
+        """Views (K, V) of the encoder cache, [L][B][H][max_tokens][dh]."""
+        cfg = self.encoder.model.cfg
+        sd = torch.bfloat16 if cfg.dtype == DTYPE_BF16 else torch.float32
+        shape = (cfg.n_layers, self.batch, cfg.n_heads, self.max_tokens, cfg.head_dim)
+        n = 1
+        for v in shape:
+            n *= v
+        flat = self.buf.view(sd)
+        return flat[:n].view(shape), flat[_align_elems(n, sd):][:n].view(shape)
+
+
+def _align_elems(n: int, dtype) -> int:
+    es = 2 if dtype == torch.bfloat16 else 4
+    return ((n * es + 255) // 256 * 256) // es
+
+
+def rlt_encoder_state_reset(es: EncoderState, slots):
+    arr, n = _slots_arg(slots)
+    _check(load_library().rlt_encoder_state_reset(es.handle, n, arr))
+
+
+def rlt_encode(encoder: Encoder, es: EncoderState, tokens: torch.Tensor, memory, slots=None,
+               e_out=None, want_e=True, stream=None):
+    """Encode the next T tokens of each listed slot: tokens [n][T] int32 on the
+    device; memory (K, V) [G][S][H][cap][dh] tensors (entries written).
+    Returns e [n][T][d] in the model dtype (None with want_e=False)."""
+    lib = load_library()
+    cfg = encoder.model.cfg
+    tokens = tokens.to(dtype=torch.int32).contiguous()
+    n, T = tokens.shape
+    if e_out is None and want_e:
+        sd = torch.bfloat16 if cfg.dtype == DTYPE_BF16 else torch.float32
+        e_out = torch.empty((n, T, cfg.d_model), dtype=sd, device=tokens.device)
+    arr, _ = _slots_arg(slots)
+    mem = memory if isinstance(memory, rlt_memory) else memory_view(*memory)
+    _check(lib.rlt_encode(encoder.handle, es.handle, n, arr, T, tokens.data_ptr(),
+                          e_out.data_ptr() if e_out is not None else None, C.byref(mem),
+                          _stream(stream)))
+    return e_out
+
+
+def encoder_profile_begin(es: EncoderState, class_mask: int, max_launches: int):
+    """Record launches of the encoder kernel classes in class_mask (bit 1 << RLT_E_*)."""
+    _check(load_library().rlt_encoder_profile_begin(es.handle, class_mask, max_launches))
+
+
+def encoder_profile_collect(es: EncoderState, kclass: int):
+    """(total ms, launches, algorithmic FLOPs, algorithmic bytes) of one encoder kernel class."""
+    tot, n, fl, b = C.c_double(), C.c_int32(), C.c_double(), C.c_double()
+    _check(load_library().rlt_encoder_profile_collect(es.handle, kclass, C.byref(tot), C.byref(n),
+                                                      C.byref(fl), C.byref(b)))
+    return tot.value, n.value, fl.value, b.value

@@ -135,8 +135,18 @@ struct rlt_model {
 
 struct ProfRec {
   hipEvent_t a, b;
-  double bytes;
+  double bytes, flops;
   int cls;
+};
+
+// HIP event pairs recorded around the launches of selected kernel classes.
+struct ProfLog {
+  int mask = 0;
+  int max = 0;
+  int stride = 1;
+  long long step_counter = 0;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
 };
 
 struct rlt_state {
@@ -155,13 +165,7 @@ struct rlt_state {
   char *escratch;            // [B][d] e rows of generated tokens
   std::vector<int> host_pos;
   std::vector<int> staged;   // slot list currently in slots_dev (empty: none)
-  // profiling
-  int prof_mask = 0;
-  int prof_max = 0;
-  int prof_stride = 1;
-  long long step_counter = 0;
-  std::vector<ProfRec> prof;
-  std::vector<hipEvent_t> event_pool;
+  ProfLog plog;
 };
 
 namespace {
@@ -299,38 +303,89 @@ rlt_status stage_slots(rlt_state *st, int n, const int32_t *slots, hipStream_t s
   return RLT_OK;
 }
 
-hipEvent_t pooled_event(rlt_state *st) {
+hipEvent_t pooled_event(ProfLog &pl) {
   hipEvent_t e = nullptr;
-  if (!st->event_pool.empty()) {
-    e = st->event_pool.back();
-    st->event_pool.pop_back();
+  if (!pl.pool.empty()) {
+    e = pl.pool.back();
+    pl.pool.pop_back();
   } else if (hipEventCreate(&e) != hipSuccess) {
     e = nullptr;
   }
   return e;
 }
 
+void prof_release(ProfLog &pl) {
+  for (ProfRec &r : pl.recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (hipEvent_t e : pl.pool) (void)hipEventDestroy(e);
+  pl.recs.clear();
+  pl.pool.clear();
+}
+
+rlt_status prof_begin(ProfLog &pl, int class_mask, int nclasses, int max_launches, int step_stride) {
+  if (class_mask < 0 || class_mask >= (1 << nclasses))
+    return fail(RLT_ERR_INVALID_ARG, "bad kernel class mask");
+  if (max_launches < 0) return fail(RLT_ERR_INVALID_ARG, "max_launches < 0");
+  if (step_stride < 1) return fail(RLT_ERR_INVALID_ARG, "step_stride < 1");
+  pl.mask = class_mask;
+  pl.max = max_launches;
+  pl.stride = step_stride;
+  pl.step_counter = 0;
+  return ok();
+}
+
+rlt_status prof_collect(ProfLog &pl, int kclass, double *total_ms, int32_t *launches,
+                        double *bytes_moved, double *flops) {
+  double tot = 0, bytes = 0, fl = 0;
+  int cnt = 0;
+  std::vector<ProfRec> keep;
+  for (ProfRec &r : pl.recs) {
+    if (r.cls != kclass) {
+      keep.push_back(r);
+      continue;
+    }
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "profile events");
+    tot += ms;
+    bytes += r.bytes;
+    fl += r.flops;
+    ++cnt;
+    pl.pool.push_back(r.a);
+    pl.pool.push_back(r.b);
+  }
+  pl.recs.swap(keep);
+  if (total_ms) *total_ms = tot;
+  if (launches) *launches = cnt;
+  if (bytes_moved) *bytes_moved = bytes;
+  if (flops) *flops = fl;
+  return ok();
+}
+
 struct Prof {
-  rlt_state *st;
+  ProfLog &pl;
   int cls;
   hipStream_t s;
   bool on;
   hipEvent_t a = nullptr, b = nullptr;
-  Prof(rlt_state *st_, int cls_, hipStream_t s_)
-      : st(st_), cls(cls_), s(s_),
-        on(((st_->prof_mask >> cls_) & 1) && (int)st_->prof.size() < st_->prof_max &&
-           st_->step_counter % st_->prof_stride == 0) {
+  Prof(ProfLog &pl_, int cls_, hipStream_t s_)
+      : pl(pl_), cls(cls_), s(s_),
+        on(((pl_.mask >> cls_) & 1) && (int)pl_.recs.size() < pl_.max &&
+           pl_.step_counter % pl_.stride == 0) {
     if (on) {
-      a = pooled_event(st);
-      b = pooled_event(st);
+      a = pooled_event(pl);
+      b = pooled_event(pl);
       on = a && b;
     }
     if (on) (void)hipEventRecord(a, s);
   }
-  void done(double bytes) {
+  void done(double bytes, double flops = 0.0) {
     if (!on) return;
     (void)hipEventRecord(b, s);
-    st->prof.push_back({a, b, bytes, cls});
+    pl.recs.push_back({a, b, bytes, flops, cls});
     on = false;
   }
 };
@@ -380,7 +435,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     a.N = g.N;
     a.K = g.K;
     a.KT = g.KT;
-    Prof p(st, RLT_K_GEMM, s);
+    Prof p(st->plog, RLT_K_GEMM, s);
     // narrower column groups until the launch has a workgroup per CU (results
     // per row do not depend on the grouping)
     ColPlan gc = cp;
@@ -453,7 +508,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
       a.s_head = (int64_t)W * dh;
       a.s_pos = dh;
       a.len_cap = W;
-      Prof p(st, RLT_K_SWA, s);
+      Prof p(st->plog, RLT_K_SWA, s);
       if ((err = launch_attn(c.dtype, dh, a, n, s)) != hipSuccess)
         return hip_fail(err, "window attention launch");
       p.done(swa_len * 2.0 * d * es + 2.0 * n * d * es);
@@ -491,7 +546,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
       a.s_head = mem->stride_head;
       a.s_pos = mem->stride_pos;
       a.len_cap = 0x7fffffff;
-      Prof p(st, RLT_K_CROSS, s);
+      Prof p(st->plog, RLT_K_CROSS, s);
       if ((err = launch_attn(c.dtype, dh, a, n, s)) != hipSuccess)
         return hip_fail(err, "cross attention launch");
       p.done(mem_len * 2.0 * d * es + 2.0 * n * d * es);
@@ -548,7 +603,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
   }
 
   for (int i = 0; i < n; ++i) st->host_pos[identity ? i : host_slots[i]] += 1;
-  st->step_counter += 1;
+  st->plog.step_counter += 1;
   return RLT_OK;
 }
 
@@ -725,11 +780,7 @@ rlt_status rlt_state_init(const rlt_model *m, int32_t batch, int32_t max_tokens,
 
 void rlt_state_destroy(rlt_state *st) {
   if (!st) return;
-  for (ProfRec &r : st->prof) {
-    (void)hipEventDestroy(r.a);
-    (void)hipEventDestroy(r.b);
-  }
-  for (hipEvent_t e : st->event_pool) (void)hipEventDestroy(e);
+  prof_release(st->plog);
   delete st;
 }
 
@@ -835,7 +886,7 @@ rlt_status rlt_score_sequence(const rlt_model *m, rlt_state *st, int32_t T, cons
     sa.out = dev_logprob + k;
     sa.ld_out = T;
     sa.V = V;
-    Prof p(st, RLT_K_EXTRA, s);
+    Prof p(st->plog, RLT_K_EXTRA, s);
     const hipError_t e = launch_score(sa, st->B, s);
     if (e != hipSuccess) return hip_fail(e, "score launch");
     p.done((double)st->B * V * 4 * 2);
@@ -876,7 +927,7 @@ rlt_status rlt_generate(const rlt_model *m, rlt_state *st, int32_t n_steps,
     sa.V = V;
     sa.top_k = std::min(smp->top_k, V);
     sa.inv_temp = 1.0f / smp->temperature;
-    Prof ps(st, RLT_K_EXTRA, s);
+    Prof ps(st->plog, RLT_K_EXTRA, s);
     hipError_t e = launch_sample(sa, B, s);
     if (e != hipSuccess) return hip_fail(e, "sample launch");
     ps.done((double)B * V * 4 * 2);
@@ -901,7 +952,7 @@ rlt_status rlt_generate(const rlt_model *m, rlt_state *st, int32_t n_steps,
     ea.dh = c.head_dim;
     ea.V = V;
     ea.G = c.mem_groups;
-    Prof pe(st, RLT_K_EXTRA, s);
+    Prof pe(st->plog, RLT_K_EXTRA, s);
     e = launch_encode(c.dtype, ea, B, s);
     if (e != hipSuccess) return hip_fail(e, "encode launch");
     pe.done((double)B * (d + 2.0 * c.mem_groups * d) * m->esize * 2);
@@ -1028,44 +1079,375 @@ rlt_status rlt_state_import(const rlt_model *m, rlt_state *st, int32_t n, const 
 rlt_status rlt_profile_begin(rlt_state *st, int32_t class_mask, int32_t max_launches,
                              int32_t step_stride) {
   if (!st) return fail(RLT_ERR_INVALID_ARG, "state is NULL");
-  if (class_mask < 0 || class_mask >= (1 << RLT_K_NCLASSES))
-    return fail(RLT_ERR_INVALID_ARG, "bad kernel class mask");
-  if (max_launches < 0) return fail(RLT_ERR_INVALID_ARG, "max_launches < 0");
-  if (step_stride < 1) return fail(RLT_ERR_INVALID_ARG, "step_stride < 1");
-  st->prof_mask = class_mask;
-  st->prof_max = max_launches;
-  st->prof_stride = step_stride;
-  st->step_counter = 0;
-  return ok();
+  return prof_begin(st->plog, class_mask, RLT_K_NCLASSES, max_launches, step_stride);
 }
 
 rlt_status rlt_profile_collect(rlt_state *st, int32_t kclass, double *total_ms, int32_t *launches,
                                double *bytes_moved) {
   if (!st) return fail(RLT_ERR_INVALID_ARG, "state is NULL");
   if (kclass < 0 || kclass >= RLT_K_NCLASSES) return fail(RLT_ERR_INVALID_ARG, "bad kernel class");
-  double tot = 0, bytes = 0;
-  int cnt = 0;
-  std::vector<ProfRec> keep;
-  for (ProfRec &r : st->prof) {
-    if (r.cls != kclass) {
-      keep.push_back(r);
-      continue;
-    }
-    float ms = 0.f;
-    hipError_t e = hipEventSynchronize(r.b);
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
-    if (e != hipSuccess) return hip_fail(e, "profile events");
-    tot += ms;
-    bytes += r.bytes;
-    ++cnt;
-    st->event_pool.push_back(r.a);
-    st->event_pool.push_back(r.b);
+  return prof_collect(st->plog, kclass, total_ms, launches, bytes_moved, nullptr);
+}
+
+}  // extern "C"
+
+// ================================================================== encoder
+// Host side of the token-parallel causal encoder: its own weights (embedding,
+// final gain, memory projections), references to the decoder's tied layer
+// weights, the encoder cache, and the launch sequence of one rlt_encode call.
+
+struct rlt_encoder {
+  const rlt_model *m;
+  int device;
+  char *emb;                       // [V][d] model dtype
+  float *ge;                       // [d]
+  std::vector<PackedMat> wkvm;     // per group: N = 2d (K rows, then V rows), K = d
+};
+
+struct rlt_encoder_state {
+  rlt_config cfg;
+  uint64_t version;
+  int device;
+  int B, max_tokens, max_rows;
+  char *cache_k, *cache_v;         // [L][B][H][max_tokens][dh] model dtype
+  int *slots_dev, *p0_dev;         // [B] slot and first position of each listed sequence
+  float *x;                        // [R][d] residual stream
+  char *abuf, *qbuf, *obuf, *hbuf, *ebuf;   // [R][d] / [R][F] model dtype
+  std::vector<int> host_pos;
+  std::vector<int> tbl;            // host copy of the staged slot / position table
+  ProfLog plog;
+};
+
+namespace {
+
+bool encoder_supported(const rlt_config &c) {
+  return !(c.dtype == RLT_DTYPE_BF16 && c.head_dim < 32);
+}
+
+size_t encoder_layout(const rlt_config &c, rlt_encoder *enc, void *base) {
+  const int d = c.d_model, es = esize_of(c.dtype);
+  Arena ar(base);
+  enc->emb = ar.take<char>((size_t)c.vocab * d * es);
+  enc->ge = ar.take<float>((size_t)d * 4);
+  const GemmPlan g = gemm_plan(2 * d, d, c.dtype);
+  enc->wkvm.resize(c.mem_groups);
+  for (PackedMat &pm : enc->wkvm) {
+    pm.N = g.N;
+    pm.K = g.K;
+    pm.Np = g.Np;
+    pm.KT = g.KT;
+    pm.p = ar.take<char>(packed_bytes(g, es, c.dtype));
   }
-  st->prof.swap(keep);
-  if (total_ms) *total_ms = tot;
-  if (launches) *launches = cnt;
-  if (bytes_moved) *bytes_moved = bytes;
+  return align256(ar.off);
+}
+
+size_t encoder_state_layout(const rlt_config &c, rlt_encoder_state *es, void *base, int B, int cap,
+                            int R) {
+  const int L = c.n_layers, d = c.d_model, H = c.n_heads, dh = c.head_dim;
+  const int e = esize_of(c.dtype);
+  Arena ar(base);
+  es->cache_k = ar.take<char>((size_t)L * B * H * cap * dh * e);
+  es->cache_v = ar.take<char>((size_t)L * B * H * cap * dh * e);
+  es->slots_dev = ar.take<int>((size_t)B * 4);
+  es->p0_dev = ar.take<int>((size_t)B * 4);
+  es->x = ar.take<float>((size_t)R * d * 4);
+  es->abuf = ar.take<char>((size_t)R * d * e);
+  es->qbuf = ar.take<char>((size_t)R * d * e);
+  es->obuf = ar.take<char>((size_t)R * d * e);
+  es->hbuf = ar.take<char>((size_t)R * c.d_ffn * e);
+  es->ebuf = ar.take<char>((size_t)R * d * e);
+  return align256(ar.off);
+}
+
+PGemmArgs pgemm_args(const PackedMat &w, const void *act, int64_t lda, const EncRows &rows) {
+  PGemmArgs a{};
+  a.a = act;
+  a.lda = lda;
+  a.wp = w.p;
+  a.N = w.N;
+  a.Np = w.Np;
+  a.K = w.K;
+  a.KT = w.KT;
+  a.rows = rows;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rlt_encoder_bytes(const rlt_model *m) {
+  if (!m || !encoder_supported(m->cfg)) return 0;
+  rlt_encoder enc;
+  return encoder_layout(m->cfg, &enc, nullptr);
+}
+
+rlt_status rlt_encoder_create(const rlt_model *m, const rlt_encoder_params *src, void *dev_buf,
+                              size_t bytes, void *stream, rlt_encoder **out) {
+  if (!out) return fail(RLT_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!m) return fail(RLT_ERR_INVALID_ARG, "model is NULL");
+  if (!src || !src->emb || !src->ge || !src->wkm || !src->wvm)
+    return fail(RLT_ERR_INVALID_ARG, "an encoder parameter pointer is NULL");
+  const rlt_config &c = m->cfg;
+  if (!encoder_supported(c))
+    return fail(RLT_ERR_UNSUPPORTED, "the bf16 encoder kernels need head_dim >= 32 (got %d)",
+                c.head_dim);
+  if (!dev_buf) return fail(RLT_ERR_INVALID_ARG, "dev_buf is NULL");
+  if ((uintptr_t)dev_buf % 256) return fail(RLT_ERR_SHAPE, "dev_buf must be 256-byte aligned");
+  const size_t need = rlt_encoder_bytes(m);
+  if (bytes < need) return fail(RLT_ERR_SHAPE, "encoder buffer %zu bytes < %zu required", bytes, need);
+  rlt_status rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  rlt_encoder *enc = new rlt_encoder();
+  enc->m = m;
+  enc->device = m->device;
+  encoder_layout(c, enc, dev_buf);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = c.d_model, es = esize_of(c.dtype);
+  const size_t dd = (size_t)d * d * es;
+  hipError_t e = launch_copy(enc->emb, src->emb, (size_t)c.vocab * d * es, s);
+  if (e == hipSuccess) e = launch_copy(enc->ge, src->ge, (size_t)d * 4, s);
+  for (int g = 0; g < c.mem_groups && e == hipSuccess; ++g) {
+    const PackedMat &pm = enc->wkvm[g];
+    e = launch_pack_tiles(static_cast<const char *>(src->wkm) + g * dd, d, d, d, 0, d / 16, pm,
+                          c.dtype, s);
+    if (e == hipSuccess)
+      e = launch_pack_tiles(static_cast<const char *>(src->wvm) + g * dd, d, d, d, d / 16,
+                            pm.Np / 16, pm, c.dtype, s);
+  }
+  if (e != hipSuccess) {
+    delete enc;
+    return hip_fail(e, "packing encoder weights");
+  }
+  *out = enc;
   return ok();
+}
+
+void rlt_encoder_destroy(rlt_encoder *enc) { delete enc; }
+
+size_t rlt_encoder_state_bytes(const rlt_config *cfg, int32_t batch, int32_t max_tokens,
+                               int32_t max_rows) {
+  if (check_config(cfg) != RLT_OK || !encoder_supported(*cfg) || batch < 1 || max_tokens < 1 ||
+      max_rows < 1)
+    return 0;
+  rlt_encoder_state es;
+  return encoder_state_layout(*cfg, &es, nullptr, batch, max_tokens, max_rows);
+}
+
+rlt_status rlt_encoder_state_init(const rlt_encoder *enc, int32_t batch, int32_t max_tokens,
+                                  int32_t max_rows, void *dev_buf, size_t bytes,
+                                  rlt_encoder_state **out) {
+  if (!out) return fail(RLT_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!enc) return fail(RLT_ERR_INVALID_ARG, "encoder is NULL");
+  if (batch < 1 || max_tokens < 1 || max_rows < 1)
+    return fail(RLT_ERR_INVALID_ARG, "batch, max_tokens and max_rows must be >= 1");
+  if (!dev_buf) return fail(RLT_ERR_INVALID_ARG, "dev_buf is NULL");
+  if ((uintptr_t)dev_buf % 256) return fail(RLT_ERR_SHAPE, "dev_buf must be 256-byte aligned");
+  const rlt_config &c = enc->m->cfg;
+  const size_t need = rlt_encoder_state_bytes(&c, batch, max_tokens, max_rows);
+  if (bytes < need)
+    return fail(RLT_ERR_SHAPE, "encoder state buffer %zu bytes < %zu required", bytes, need);
+  rlt_encoder_state *es = new rlt_encoder_state();
+  es->cfg = c;
+  es->version = enc->m->version;
+  es->device = enc->device;
+  es->B = batch;
+  es->max_tokens = max_tokens;
+  es->max_rows = max_rows;
+  encoder_state_layout(c, es, dev_buf, batch, max_tokens, max_rows);
+  es->host_pos.assign(batch, 0);
+  *out = es;
+  return ok();
+}
+
+void rlt_encoder_state_destroy(rlt_encoder_state *es) {
+  if (!es) return;
+  prof_release(es->plog);
+  delete es;
+}
+
+rlt_status rlt_encoder_state_reset(rlt_encoder_state *es, int32_t n, const int32_t *host_slots) {
+  if (!es) return fail(RLT_ERR_INVALID_ARG, "encoder state is NULL");
+  if (!host_slots) return fail(RLT_ERR_INVALID_ARG, "host_slots is NULL");
+  if (n < 1 || n > es->B) return fail(RLT_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, es->B);
+  for (int i = 0; i < n; ++i)
+    if (host_slots[i] < 0 || host_slots[i] >= es->B)
+      return fail(RLT_ERR_INVALID_ARG, "slot %d out of range", host_slots[i]);
+  for (int i = 0; i < n; ++i) es->host_pos[host_slots[i]] = 0;
+  return ok();
+}
+
+int32_t rlt_encoder_position(const rlt_encoder_state *es, int32_t slot) {
+  if (!es || slot < 0 || slot >= es->B) return -1;
+  return es->host_pos[slot];
+}
+
+rlt_status rlt_encode(const rlt_encoder *enc, rlt_encoder_state *es, int32_t n,
+                      const int32_t *host_slots, int32_t T, const int32_t *dev_tokens, void *dev_e,
+                      const rlt_memory *mem, void *stream) {
+  if (!enc) return fail(RLT_ERR_INVALID_ARG, "encoder is NULL");
+  if (!es) return fail(RLT_ERR_INVALID_ARG, "encoder state is NULL");
+  const rlt_model *m = enc->m;
+  const rlt_config &c = m->cfg;
+  if (es->version != m->version)
+    return fail(RLT_ERR_STALE, "encoder state built for model version %llu, model is version %llu",
+                (unsigned long long)es->version, (unsigned long long)m->version);
+  if (n < 1 || n > es->B) return fail(RLT_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, es->B);
+  if (T < 1) return fail(RLT_ERR_INVALID_ARG, "T must be >= 1");
+  if ((long long)n * T > es->max_rows)
+    return fail(RLT_ERR_SHAPE, "n * T = %lld rows > max_rows %d", (long long)n * T, es->max_rows);
+  if (!dev_tokens) return fail(RLT_ERR_INVALID_ARG, "dev_tokens is NULL");
+  std::vector<int> slots(n);
+  std::vector<char> seen(es->B, 0);
+  int max_slot = 0;
+  for (int i = 0; i < n; ++i) {
+    const int sl = host_slots ? host_slots[i] : i;
+    if (sl < 0 || sl >= es->B) return fail(RLT_ERR_INVALID_ARG, "slot %d out of range", sl);
+    if (seen[sl]) return fail(RLT_ERR_INVALID_ARG, "slot %d listed twice", sl);
+    seen[sl] = 1;
+    slots[i] = sl;
+    max_slot = std::max(max_slot, sl);
+  }
+  rlt_status rs;
+  if ((rs = check_memory(m, mem, max_slot)) != RLT_OK) return rs;
+  for (int i = 0; i < n; ++i) {
+    const long long last = (long long)es->host_pos[slots[i]] + T;
+    if (last > mem->capacity)
+      return fail(RLT_ERR_RANGE, "slot %d would reach position %lld > memory capacity %d",
+                  slots[i], last, mem->capacity);
+    if (last > es->max_tokens)
+      return fail(RLT_ERR_RANGE, "slot %d would reach position %lld > max_tokens %d", slots[i],
+                  last, es->max_tokens);
+  }
+  if ((uintptr_t)dev_e % 16) return fail(RLT_ERR_SHAPE, "dev_e must be 16-byte aligned");
+  if ((rs = device_health()) != RLT_OK) return rs;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int L = c.n_layers, d = c.d_model, F = c.d_ffn, H = c.n_heads, dh = c.head_dim;
+  const int esz = esize_of(c.dtype);
+  const int R = n * T;
+  // slot / first-position table of this call (host copy kept until the next call)
+  es->tbl.resize(2 * (size_t)n);
+  double attn_pairs = 0.0;     // sum over rows of the attended positions
+  double kv_positions = 0.0;   // cache positions each sequence's attention reads
+  for (int i = 0; i < n; ++i) {
+    es->tbl[i] = slots[i];
+    es->tbl[n + i] = es->host_pos[slots[i]];
+    attn_pairs += (double)T * es->tbl[n + i] + 0.5 * (double)T * (T + 1);
+    kv_positions += (double)es->tbl[n + i] + T;
+  }
+  hipError_t e = hipMemcpyAsync(es->slots_dev, es->tbl.data(), (size_t)n * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(es->p0_dev, es->tbl.data() + n, (size_t)n * 4, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "staging the slot table");
+  const EncRows rows{es->slots_dev, es->p0_dev, T, R};
+
+  auto gemm = [&](const PGemmArgs &a, int epi, const char *what) -> rlt_status {
+    Prof p(es->plog, RLT_E_GEMM, s);
+    const hipError_t err = launch_pgemm(c.dtype, epi, a, s);
+    const double flops = 2.0 * R * a.N * a.K;
+    const double out_bytes = epi == PEPI_RESID ? (double)R * a.N * 8 : (double)R * a.N * esz;
+    p.done((double)a.N * a.K * esz + (double)R * a.K * esz + out_bytes, flops);
+    return err == hipSuccess ? RLT_OK : hip_fail(err, what);
+  };
+  auto other = [&](hipError_t err, const char *what) -> rlt_status {
+    return err == hipSuccess ? RLT_OK : hip_fail(err, what);
+  };
+  const size_t layer_cache = (size_t)es->B * H * es->max_tokens * dh * esz;
+  const int64_t s_seq = (int64_t)H * es->max_tokens * dh, s_head = (int64_t)es->max_tokens * dh;
+
+  {
+    Prof p(es->plog, RLT_E_OTHER, s);
+    e = launch_enc_embed(c.dtype, dev_tokens, R, enc->emb, c.vocab, d, es->x, s);
+    p.done((double)R * 4 + (double)R * d * (esz + 4));
+    if ((rs = other(e, "embedding")) != RLT_OK) return rs;
+  }
+  auto norm = [&](const float *gamma, void *out) -> rlt_status {
+    Prof p(es->plog, RLT_E_OTHER, s);
+    const hipError_t err = launch_enc_norm(c.dtype, es->x, d, gamma, c.rms_eps, out, d, R, d, s);
+    p.done((double)R * d * (4 + esz) + (double)d * 4);
+    return other(err, "rmsnorm");
+  };
+  for (int l = 0; l < L; ++l) {
+    char *ck = es->cache_k + l * layer_cache, *cv = es->cache_v + l * layer_cache;
+    if ((rs = norm(m->g1 + (size_t)l * d, es->abuf)) != RLT_OK) return rs;
+    PGemmArgs a = pgemm_args(m->wqkv[l], es->abuf, d, rows);
+    a.out = es->qbuf;
+    a.ld_out = d;
+    a.kb = ck;
+    a.vb = cv;
+    a.s_seq = s_seq;
+    a.s_head = s_head;
+    a.s_pos = dh;
+    a.d = d;
+    a.H = H;
+    a.dh = dh;
+    if ((rs = gemm(a, PEPI_QKV, "qkv gemm")) != RLT_OK) return rs;
+    {
+      FAttnArgs fa{};
+      fa.q = es->qbuf;
+      fa.ldq = d;
+      fa.out = es->obuf;
+      fa.ldo = d;
+      fa.kb = ck;
+      fa.vb = cv;
+      fa.s_seq = s_seq;
+      fa.s_head = s_head;
+      fa.s_pos = dh;
+      fa.rows = rows;
+      fa.H = H;
+      fa.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
+      Prof p(es->plog, RLT_E_ATTN, s);
+      e = launch_fattn(c.dtype, dh, fa, s);
+      p.done(2.0 * R * d * esz + 2.0 * kv_positions * d * esz, 4.0 * attn_pairs * d);
+      if ((rs = other(e, "causal attention")) != RLT_OK) return rs;
+    }
+    a = pgemm_args(m->wo[l], es->obuf, d, rows);
+    a.x = es->x;
+    a.ld_x = d;
+    if ((rs = gemm(a, PEPI_RESID, "o gemm")) != RLT_OK) return rs;
+    if ((rs = norm(m->g3 + (size_t)l * d, es->abuf)) != RLT_OK) return rs;
+    a = pgemm_args(m->w1[l], es->abuf, d, rows);
+    a.out = es->hbuf;
+    a.ld_out = F;
+    if ((rs = gemm(a, PEPI_GELU, "ffn-up gemm")) != RLT_OK) return rs;
+    a = pgemm_args(m->w2[l], es->hbuf, F, rows);
+    a.x = es->x;
+    a.ld_x = d;
+    if ((rs = gemm(a, PEPI_RESID, "ffn-down gemm")) != RLT_OK) return rs;
+  }
+  void *e_out = dev_e ? dev_e : es->ebuf;
+  if ((rs = norm(enc->ge, e_out)) != RLT_OK) return rs;
+  for (int g = 0; g < c.mem_groups; ++g) {
+    PGemmArgs a = pgemm_args(enc->wkvm[g], e_out, d, rows);
+    a.kb = static_cast<char *>(const_cast<void *>(mem->k)) + (size_t)g * mem->stride_group * esz;
+    a.vb = static_cast<char *>(const_cast<void *>(mem->v)) + (size_t)g * mem->stride_group * esz;
+    a.s_seq = mem->stride_seq;
+    a.s_head = mem->stride_head;
+    a.s_pos = mem->stride_pos;
+    a.d = d;
+    a.H = H;
+    a.dh = dh;
+    if ((rs = gemm(a, PEPI_MEM, "memory projection gemm")) != RLT_OK) return rs;
+  }
+  for (int i = 0; i < n; ++i) es->host_pos[slots[i]] += T;
+  es->plog.step_counter += 1;
+  return ok();
+}
+
+rlt_status rlt_encoder_profile_begin(rlt_encoder_state *es, int32_t class_mask,
+                                     int32_t max_launches) {
+  if (!es) return fail(RLT_ERR_INVALID_ARG, "encoder state is NULL");
+  return prof_begin(es->plog, class_mask, RLT_E_NCLASSES, max_launches, 1);
+}
+
+rlt_status rlt_encoder_profile_collect(rlt_encoder_state *es, int32_t kclass, double *total_ms,
+                                       int32_t *launches, double *flops, double *bytes_moved) {
+  if (!es) return fail(RLT_ERR_INVALID_ARG, "encoder state is NULL");
+  if (kclass < 0 || kclass >= RLT_E_NCLASSES) return fail(RLT_ERR_INVALID_ARG, "bad kernel class");
+  return prof_collect(es->plog, kclass, total_ms, launches, bytes_moved, flops);
 }
 
 }  // extern "C"

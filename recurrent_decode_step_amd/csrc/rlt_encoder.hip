@@ -1,0 +1,511 @@
+// HIP kernels of the token-parallel causal encoder, written for gfx950 (CDNA4).
+//
+// The encoder runs all known tokens of a sequence at once under a causal mask
+// and produces e_t; its layers reuse the attention and feed-forward weights of
+// the decoder layers, and the memory M_<=t is projected from e_t once per
+// memory group ("Recurrent Looped Transformer: A New Architecture for Infinite
+// Context Reasoning in Language Models", "Encoder-Decoder Pairing with Shared
+// Weights" and "Principle 2: Co-Design Between Model and Hardware"; "Princeton
+// Researcher Proposes Recurrent Looped Transformer to Carry Decoder State
+// Across Tokens", architecture paragraph).
+//
+// Kernels (one launch each on the caller's stream):
+//   k_enc_embed  token embedding rows into the fp32 residual stream
+//   k_enc_norm   RMSNorm of rows into the storage type
+//   k_pgemm      token-parallel GEMM on MFMA: 128 tokens x 128 features per
+//                workgroup, both operands staged through LDS in fragment order,
+//                fused epilogues (q + encoder-cache append, residual add,
+//                GELU, memory K/V append)
+//   k_fattn      causal flash attention over the encoder cache: 64 queries of
+//                one (sequence, head) per workgroup, MFMA for Q K^T and P V
+#include "rlt_device.h"
+
+#include <algorithm>
+
+namespace rlt {
+
+// ---------------------------------------------------------------- embedding
+// x[r] = emb[tokens[r]] in fp32; a token outside 0..V-1 gives a NaN row.
+template <typename T>
+__global__ void k_enc_embed(const int32_t *__restrict__ tokens, int n_rows,
+                            const T *__restrict__ emb, int V, int d, float *__restrict__ x) {
+  const int q = d / 4;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)n_rows * q) return;
+  const int r = (int)(idx / q), c = (int)(idx % q) * 4;
+  const int tok = tokens[r];
+  f32x4 v;
+  if (tok >= 0 && tok < V) {
+    const T *p = emb + (size_t)tok * d + c;
+    if constexpr (sizeof(T) == 2) {
+      const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
+      v = f32x4{bf2f(w.x & 0xffffu), bf2f(w.x >> 16), bf2f(w.y & 0xffffu), bf2f(w.y >> 16)};
+    } else {
+      v = *reinterpret_cast<const f32x4 *>(p);
+    }
+  } else {
+    const float nan = __builtin_nanf("");
+    v = f32x4{nan, nan, nan, nan};
+  }
+  *reinterpret_cast<f32x4 *>(x + (size_t)r * d + c) = v;
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// out[r] = round((x[r] * (mean(x[r]^2) + eps)^(-1/2)) * gamma); one wavefront
+// per row, four rows per workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void k_enc_norm(const float *__restrict__ x, int64_t ldx,
+                                                  const float *__restrict__ gamma, float eps,
+                                                  T *__restrict__ out, int64_t ldo, int n_rows,
+                                                  int d) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n_rows) return;                       // uniform over the wavefront
+  const float *xr = x + (size_t)r * ldx;
+  float ss = 0.f;
+  for (int c = lane * 4; c < d; c += 256) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  const float rinv = 1.0f / sqrtf(ss / (float)d + eps);
+  T *o = out + (size_t)r * ldo;
+  for (int c = lane * 4; c < d; c += 256) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + c);
+    const f32x4 g = *reinterpret_cast<const f32x4 *>(gamma + c);
+    const float y[4] = {(v.x * rinv) * g.x, (v.y * rinv) * g.y, (v.z * rinv) * g.z,
+                        (v.w * rinv) * g.w};
+    Num<T>::store4(o + c, y);
+  }
+}
+
+// ---------------------------------------------------------------- GEMM
+// y[r][n] = sum_k W[n][k] a[r][k] over the call's token rows r.
+//
+// Workgroup tile: 128 token rows x 8 weight tiles (128 features), 4 wavefronts
+// in a 2 x 2 grid, each 64 features x 64 rows = 4 x 4 MFMA blocks.  The weight
+// tile is the A operand (feature rows), the token rows the B operand, so each
+// lane's accumulator holds 4 consecutive features of one token row.  K goes in
+// stages of 2 k-steps: every stage's fragments of both operands are loaded to
+// registers while the previous stage is multiplied out of LDS, then written to
+// the other LDS buffer in fragment order (each MFMA operand read is one
+// contiguous KiB).  The launch order puts each XCD on a contiguous run of
+// groups of 4 row tiles x all feature tiles, so the 4 row tiles stay in that
+// XCD's L2 while the weight tiles stream past them.
+constexpr int kPgRows = 128;   // token rows per workgroup
+constexpr int kPgTiles = 8;    // 16-feature weight tiles per workgroup
+constexpr int kPgKs = 2;       // k-steps per stage
+constexpr int kPgGroup = 4;    // row tiles per group of the launch order
+
+__device__ __forceinline__ void enc_row(const EncRows &R, int r, int &slot, int &pos) {
+  const int i = r / R.T;
+  slot = R.slots[i];
+  pos = R.p0[i] + (r - i * R.T);
+}
+
+// Epilogue of 4 consecutive features n..n+3 of token row r.
+template <typename T, int EPI>
+__device__ __forceinline__ void pgemm_store(const PGemmArgs &a, int r, int n, f32x4 acc) {
+  float y[4] = {acc[0], acc[1], acc[2], acc[3]};
+  if constexpr (EPI == PEPI_RESID) {
+    f32x4 *xp = reinterpret_cast<f32x4 *>(a.x + (size_t)r * a.ld_x + n);
+    const f32x4 o = *xp;
+    *xp = f32x4{o.x + y[0], o.y + y[1], o.z + y[2], o.w + y[3]};
+  } else if constexpr (EPI == PEPI_GELU) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) y[u] = gelu_erf(y[u]);
+    Num<T>::store4(static_cast<T *>(a.out) + (size_t)r * a.ld_out + n, y);
+  } else {
+    // QKV: parts q, k, v of width d; MEM: parts k, v.  A lane's 4 features
+    // never straddle a part or a head (d and dh are multiples of 16).
+    const int part = n / a.d;
+    const int c = n - part * a.d;
+    if (EPI == PEPI_QKV && part == 0) {
+      Num<T>::store4(static_cast<T *>(a.out) + (size_t)r * a.ld_out + c, y);
+      return;
+    }
+    const bool is_k = EPI == PEPI_QKV ? part == 1 : part == 0;
+    int slot, pos;
+    enc_row(a.rows, r, slot, pos);
+    const int h = c / a.dh, cc = c - h * a.dh;
+    T *dst = static_cast<T *>(is_k ? a.kb : a.vb) + (size_t)slot * a.s_seq +
+             (size_t)h * a.s_head + (size_t)pos * a.s_pos + cc;
+    Num<T>::store4(dst, y);
+  }
+}
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(256, 2) void k_pgemm(PGemmArgs a, int mt, int nt) {
+  constexpr int EPL = Num<T>::EPL;
+  constexpr int KSTEP = 4 * EPL;
+  constexpr int FR = kPgTiles * kPgKs * 64;     // fragments of one operand per stage
+  __shared__ u32x4 sW[2][FR];
+  __shared__ u32x4 sA[2][FR];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // workgroup -> (row tile, feature tile group)
+  const int total = mt * nt;
+  const int id = blockIdx.x;
+  const int v = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;
+  const int grp = v / (kPgGroup * nt);
+  const int m0 = grp * kPgGroup;
+  const int gm = min(kPgGroup, mt - m0);
+  const int w = v - grp * kPgGroup * nt;
+  const int tm = m0 + w % gm, tn = w / gm;
+  const int row0 = tm * kPgRows, tile0 = tn * kPgTiles;
+  const int ntiles = a.Np >> 4;
+  const int n_rows = a.rows.n_rows;
+  const u32x4 *wp = static_cast<const u32x4 *>(a.wp);
+  const T *ap = static_cast<const T *>(a.a);
+
+  // staging: wavefront w moves row blocks / weight tiles 2w and 2w+1, k-steps 0 and 1
+  u32x4 ra[4], rw[4];
+  auto load = [&](int st) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int blk = 2 * wave + (f >> 1), ks = f & 1;
+      const int kt = st * kPgKs + ks;
+      const bool kok = kt < a.KT;
+      const int row = row0 + blk * 16 + (lane & 15);
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      ra[f] = (kok && row < n_rows)
+                  ? *reinterpret_cast<const u32x4 *>(ap + (size_t)row * a.lda + kt * KSTEP +
+                                                     (lane >> 4) * EPL)
+                  : zero;
+      const int tile = tile0 + blk;
+      rw[f] = (kok && tile < ntiles) ? wp[((size_t)tile * a.KT + kt) * 64 + lane] : zero;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int blk = 2 * wave + (f >> 1), ks = f & 1;
+      sA[buf][(blk * kPgKs + ks) * 64 + lane] = ra[f];
+      sW[buf][(blk * kPgKs + ks) * 64 + lane] = rw[f];
+    }
+  };
+
+  const int wn = wave & 1, wm = wave >> 1;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int S = (a.KT + kPgKs - 1) / kPgKs;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int st = 0; st < S; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < S) load(st + 1);
+#pragma unroll
+    for (int ks = 0; ks < kPgKs; ++ks) {
+      u32x4 wf[4], af[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) wf[t] = sW[buf][((wn * 4 + t) * kPgKs + ks) * 64 + lane];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) af[b] = sA[buf][((wm * 4 + b) * kPgKs + ks) * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[t][b] = mma_step(wf[t], af[b], acc[t][b], T());
+    }
+    if (st + 1 < S) store(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int n = (tile0 + wn * 4 + t) * 16 + (lane >> 4) * 4;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int r = row0 + (wm * 4 + b) * 16 + (lane & 15);
+      if (r < n_rows && n < a.N) pgemm_store<T, EPI>(a, r, n, acc[t][b]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- attention
+// Causal attention of the call's token rows over the encoder cache of their
+// sequence: the query at position p sees cache positions 0..p (the rows of
+// this call were appended by the QKV epilogue before this launch).
+//
+// Workgroup: 64 consecutive queries of one (sequence, head), 16 per wavefront.
+// Per tile of KVT positions: S^T = K Q^T on MFMA (K fragments from LDS, the
+// wavefront's Q fragments held in registers), masking and a base-2 online
+// softmax per query column, then O^T += V^T P^T on MFMA with P^T taken straight
+// from the S^T accumulators and V staged transposed in LDS.  The next tile's
+// loads are in flight while a tile is multiplied out.
+template <typename T, int DH>
+struct FAttnShape {
+  static constexpr int EPL = Num<T>::EPL;
+  static constexpr int KSTEP = 4 * EPL;
+  static constexpr int KVT_RAW = 16384 / (DH * (int)sizeof(T));
+  static constexpr int KVT = KVT_RAW > 64 ? 64 : KVT_RAW;   // positions per tile
+  static constexpr int PB = KVT / 16;                       // 16-position blocks of S^T
+  static constexpr int KS = DH / KSTEP;                     // k-steps of Q K^T
+  static constexpr int PKS = KVT / KSTEP;                   // k-steps of P V
+  static constexpr int CB = DH / 16;                        // 16-channel blocks of O^T
+  static constexpr int VROW = KVT + 4;                      // padded row of V^T in LDS
+  static constexpr int NF = PB * KS;                        // K fragments per tile
+  static constexpr int PAIR = sizeof(T) == 2 ? 2 : 1;       // positions per V staging task
+  static constexpr int NVT = (KVT / PAIR) * (DH / EPL);     // V staging tasks per tile
+  static constexpr int VPT = (NVT + 255) / 256;
+  static_assert(KS >= 1 && PKS >= 1 && NF % 4 == 0, "unsupported head size");
+};
+
+template <typename T, int DH>
+__global__ __launch_bounds__(256, 2) void k_fattn(FAttnArgs a, int qblocks, int n_seq) {
+  using Sh = FAttnShape<T, DH>;
+  constexpr int EPL = Sh::EPL, KSTEP = Sh::KSTEP, KVT = Sh::KVT, PB = Sh::PB, KS = Sh::KS;
+  constexpr int PKS = Sh::PKS, CB = Sh::CB, VROW = Sh::VROW, NF = Sh::NF, PAIR = Sh::PAIR;
+  constexpr int NVT = Sh::NVT, VPT = Sh::VPT, KPW = NF / 4;
+  __shared__ u32x4 sK[NF * 64];
+  __shared__ T sVt[DH * VROW];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.x % a.H;
+  const int rest = blockIdx.x / a.H;
+  const int i = rest % n_seq;
+  const int qb = qblocks - 1 - rest / n_seq;     // longest query blocks first
+  const int Tn = a.rows.T;
+  const int slot = a.rows.slots[i], p0 = a.rows.p0[i];
+  const int j0 = qb * 64;
+  const int jlast = min(j0 + 63, Tn - 1);
+  const int kv_end = p0 + jlast + 1;             // cache positions 0 .. kv_end-1
+  const int ntile = (kv_end + KVT - 1) / KVT;
+  const int jraw = j0 + wave * 16 + (lane & 15);
+  const int jq = min(jraw, Tn - 1);              // rows past the call's tokens repeat the last
+  const int qpos = p0 + jq;
+  const int rq = i * Tn + jq;
+  const T *kbase = static_cast<const T *>(a.kb) + (size_t)slot * a.s_seq + (size_t)h * a.s_head;
+  const T *vbase = static_cast<const T *>(a.vb) + (size_t)slot * a.s_seq + (size_t)h * a.s_head;
+
+  // B operand of S^T: query (lane & 15), channels ks * KSTEP + (lane >> 4) * EPL
+  u32x4 qf[KS];
+  const T *qrow = static_cast<const T *>(a.q) + (size_t)rq * a.ldq + h * DH + (lane >> 4) * EPL;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const u32x4 *>(qrow + ks * KSTEP);
+
+  u32x4 kr[KPW];
+  u32x4 vr[VPT][PAIR];
+  auto load = [&](int tile) {
+    const int pbase = tile * KVT;
+#pragma unroll
+    for (int u = 0; u < KPW; ++u) {
+      const int f = u * 4 + wave;
+      const int pb = f / KS, ks = f - (f / KS) * KS;
+      const int p = min(pbase + pb * 16 + (lane & 15), kv_end - 1);
+      kr[u] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)p * a.s_pos + ks * KSTEP +
+                                               (lane >> 4) * EPL);
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int t = u * 256 + (int)threadIdx.x;
+      if (t < NVT) {
+        const int q = t % (KVT / PAIR), ch = t / (KVT / PAIR);
+#pragma unroll
+        for (int e = 0; e < PAIR; ++e) {
+          const int p = min(pbase + q * PAIR + e, kv_end - 1);
+          vr[u][e] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)p * a.s_pos + ch * EPL);
+        }
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < KPW; ++u) sK[(u * 4 + wave) * 64 + lane] = kr[u];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int t = u * 256 + (int)threadIdx.x;
+      if (t < NVT) {
+        const int q = t % (KVT / PAIR), ch = t / (KVT / PAIR);
+        uint32_t *vt = reinterpret_cast<uint32_t *>(sVt);
+        if constexpr (PAIR == 2) {
+          // positions 2q, 2q+1 of channels 8ch .. 8ch+7 -> one dword per channel
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = vr[u][0][e], hi = vr[u][1][e];
+            const int c = ch * 8 + 2 * e;
+            vt[(c * VROW + 2 * q) >> 1] = (lo & 0xffffu) | (hi << 16);
+            vt[((c + 1) * VROW + 2 * q) >> 1] = (lo >> 16) | (hi & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vt[(ch * 4 + e) * VROW + q] = vr[u][0][e];
+        }
+      }
+    }
+  };
+
+  f32x4 o[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+
+  load(0);
+  store();
+  __syncthreads();
+  for (int tile = 0; tile < ntile; ++tile) {
+    if (tile + 1 < ntile) load(tile + 1);
+    // S^T: lane holds positions tile*KVT + pb*16 + (lane>>4)*4 + e of query (lane & 15)
+    f32x4 s[PB];
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+      s[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[pb] = mma_step(sK[(pb * KS + ks) * 64 + lane], qf[ks], s[pb], T());
+    }
+    const int pos0 = tile * KVT + (lane >> 4) * 4;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sv = (pos0 + pb * 16 + e <= qpos) ? s[pb][e] * a.scale_log2 : -INFINITY;
+        s[pb][e] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // tile 0 holds position 0 <= qpos, so mn is finite from the first tile on
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2f(m - mn);
+    m = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pv = exp2f(s[pb][e] - mn);
+        s[pb][e] = pv;
+        lsum += pv;
+      }
+    // O^T += V^T P^T: k-slot e of lane group g is position ks*KSTEP + g*4 + e
+    // (bf16: e >= 4 -> +16 - 4), the same in both operands
+#pragma unroll
+    for (int ks = 0; ks < PKS; ++ks) {
+      u32x4 pf;
+      if constexpr (PAIR == 2) {
+        const f32x4 a0 = s[2 * ks], a1 = s[2 * ks + 1];
+        pf = u32x4{f2bf(a0[0]) | (f2bf(a0[1]) << 16), f2bf(a0[2]) | (f2bf(a0[3]) << 16),
+                   f2bf(a1[0]) | (f2bf(a1[1]) << 16), f2bf(a1[2]) | (f2bf(a1[3]) << 16)};
+      } else {
+        pf = u32x4{__float_as_uint(s[ks][0]), __float_as_uint(s[ks][1]),
+                   __float_as_uint(s[ks][2]), __float_as_uint(s[ks][3])};
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int c = cb * 16 + (lane & 15);
+        u32x4 vf;
+        if constexpr (PAIR == 2) {
+          const T *vp = sVt + c * VROW + ks * KSTEP + (lane >> 4) * 4;
+          const u32x2 lo = *reinterpret_cast<const u32x2 *>(vp);
+          const u32x2 hi = *reinterpret_cast<const u32x2 *>(vp + 16);
+          vf = u32x4{lo.x, lo.y, hi.x, hi.y};
+        } else {
+          vf = *reinterpret_cast<const u32x4 *>(sVt + c * VROW + ks * KSTEP + (lane >> 4) * 4);
+        }
+        o[cb] = mma_step(vf, pf, o[cb], T());
+      }
+    }
+    __syncthreads();
+    if (tile + 1 < ntile) {
+      store();
+      __syncthreads();
+    }
+  }
+
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (jraw < Tn) {
+    const float inv = 1.0f / lsum;
+    T *orow = static_cast<T *>(a.out) + (size_t)rq * a.ldo + h * DH + (lane >> 4) * 4;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const float y[4] = {o[cb][0] * inv, o[cb][1] * inv, o[cb][2] * inv, o[cb][3] * inv};
+      Num<T>::store4(orow + cb * 16, y);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_enc_embed(int dtype, const int32_t *tokens, int n_rows, const void *emb, int V,
+                            int d, float *x, hipStream_t s) {
+  const size_t n = (size_t)n_rows * (d / 4);
+  const int blocks = (int)((n + 255) / 256);
+  if (dtype == RLT_DTYPE_BF16)
+    hipLaunchKernelGGL(k_enc_embed<bf16_t>, dim3(blocks), dim3(256), 0, s, tokens, n_rows,
+                       static_cast<const bf16_t *>(emb), V, d, x);
+  else
+    hipLaunchKernelGGL(k_enc_embed<float>, dim3(blocks), dim3(256), 0, s, tokens, n_rows,
+                       static_cast<const float *>(emb), V, d, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_enc_norm(int dtype, const float *x, int64_t ldx, const float *gamma, float eps,
+                           void *out, int64_t ldo, int n_rows, int d, hipStream_t s) {
+  const int blocks = (n_rows + 3) / 4;
+  if (dtype == RLT_DTYPE_BF16)
+    hipLaunchKernelGGL(k_enc_norm<bf16_t>, dim3(blocks), dim3(256), 0, s, x, ldx, gamma, eps,
+                       static_cast<bf16_t *>(out), ldo, n_rows, d);
+  else
+    hipLaunchKernelGGL(k_enc_norm<float>, dim3(blocks), dim3(256), 0, s, x, ldx, gamma, eps,
+                       static_cast<float *>(out), ldo, n_rows, d);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t pgemm_epi(int epi, const PGemmArgs &a, hipStream_t s) {
+  const int mt = (a.rows.n_rows + kPgRows - 1) / kPgRows;
+  const int nt = ((a.Np >> 4) + kPgTiles - 1) / kPgTiles;
+  const dim3 grid(mt * nt), block(256);
+  switch (epi) {
+    case PEPI_QKV: hipLaunchKernelGGL((k_pgemm<T, PEPI_QKV>), grid, block, 0, s, a, mt, nt); break;
+    case PEPI_RESID: hipLaunchKernelGGL((k_pgemm<T, PEPI_RESID>), grid, block, 0, s, a, mt, nt); break;
+    case PEPI_GELU: hipLaunchKernelGGL((k_pgemm<T, PEPI_GELU>), grid, block, 0, s, a, mt, nt); break;
+    case PEPI_MEM: hipLaunchKernelGGL((k_pgemm<T, PEPI_MEM>), grid, block, 0, s, a, mt, nt); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pgemm(int dtype, int epi, const PGemmArgs &a, hipStream_t s) {
+  if (a.rows.n_rows < 1) return hipSuccess;
+  return dtype == RLT_DTYPE_BF16 ? pgemm_epi<bf16_t>(epi, a, s) : pgemm_epi<float>(epi, a, s);
+}
+
+template <typename T, int DH>
+hipError_t fattn_go(const FAttnArgs &a, hipStream_t s) {
+  const int qblocks = (a.rows.T + 63) / 64;
+  const int n_seq = a.rows.n_rows / a.rows.T;
+  hipLaunchKernelGGL((k_fattn<T, DH>), dim3(n_seq * qblocks * a.H), dim3(256), 0, s, a, qblocks,
+                     n_seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_fattn(int dtype, int dh, const FAttnArgs &a, hipStream_t s) {
+  if (a.rows.n_rows < 1) return hipSuccess;
+  if (dtype == RLT_DTYPE_BF16) {
+    switch (dh) {
+      case 32: return fattn_go<bf16_t, 32>(a, s);
+      case 64: return fattn_go<bf16_t, 64>(a, s);
+      case 128: return fattn_go<bf16_t, 128>(a, s);
+      case 256: return fattn_go<bf16_t, 256>(a, s);
+    }
+  } else {
+    switch (dh) {
+      case 16: return fattn_go<float, 16>(a, s);
+      case 32: return fattn_go<float, 32>(a, s);
+      case 64: return fattn_go<float, 64>(a, s);
+      case 128: return fattn_go<float, 128>(a, s);
+      case 256: return fattn_go<float, 256>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rlt

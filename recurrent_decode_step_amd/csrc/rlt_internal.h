@@ -132,4 +132,47 @@ struct SnapArgs {
 hipError_t launch_export(const SnapArgs &a, hipStream_t s);
 hipError_t launch_import(const SnapArgs &a, hipStream_t s);
 
+// ---------------------------------------------------------------- encoder
+// Rows of an encoder call: row r = token j of listed sequence i, r = i * T + j;
+// sequence i is slot slots[i] and its token j sits at encoder position
+// p0[i] + j (0-based).
+struct EncRows {
+  const int *slots;
+  const int *p0;
+  int T;
+  int n_rows;
+};
+
+// epilogues of the token-parallel GEMM
+enum PEpiKind { PEPI_QKV = 0, PEPI_RESID = 1, PEPI_GELU = 2, PEPI_MEM = 3 };
+
+struct PGemmArgs {
+  const void *a; int64_t lda;               // activations [n_rows][K], storage type, row-major
+  const void *wp; int N, Np, K, KT;         // packed weights (see k_pack)
+  EncRows rows;
+  void *out; int64_t ld_out;                // QKV: q part; GELU: hidden [n_rows][ld_out]
+  float *x; int64_t ld_x;                   // RESID: fp32 residual stream
+  void *kb, *vb;                            // QKV: this layer's encoder cache; MEM: this group's memory
+  int64_t s_seq, s_head, s_pos;             // elements
+  int d, H, dh;                             // QKV: N = 3d (q, k, v); MEM: N = 2d (k, v)
+};
+
+struct FAttnArgs {
+  const void *q; int64_t ldq;               // [n_rows][d]
+  void *out; int64_t ldo;                   // [n_rows][d]
+  const void *kb, *vb;                      // this layer's encoder cache
+  int64_t s_seq, s_head, s_pos;             // elements
+  EncRows rows;
+  int H;
+  float scale_log2;                         // log2(e) / sqrt(dh)
+};
+
+// kernel launchers (rlt_encoder.hip)
+hipError_t launch_enc_embed(int dtype, const int32_t *tokens, int n_rows, const void *emb, int V,
+                            int d, float *x, hipStream_t s);
+hipError_t launch_enc_norm(int dtype, const float *x, int64_t ldx, const float *gamma, float eps,
+                           void *out, int64_t ldo, int n_rows, int d, hipStream_t s);
+hipError_t launch_pgemm(int dtype, int epi, const PGemmArgs &a, hipStream_t s);
+hipError_t launch_fattn(int dtype, int dh, const FAttnArgs &a, hipStream_t s);
+
 }  // namespace rlt

@@ -119,3 +119,30 @@ def test_null_handles():
     assert L.rlt_state_position(None, 0) == -1
     assert L.rlt_profile_begin(None, 1, 1, 1) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_profile_collect(None, 0, None, None, None) == binding.RLT_ERR_INVALID_ARG
+
+
+def test_encoder_null_handles_and_sizes():
+    L = lib()
+    out = C.c_void_p()
+    assert L.rlt_encoder_bytes(None) == 0
+    p = binding.rlt_encoder_params()
+    assert L.rlt_encoder_create(None, C.byref(p), None, 0, None, C.byref(out)) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_encoder_state_init(None, 2, 16, 8, None, 0, C.byref(out)) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_encode(None, None, 1, None, 1, None, None, None, None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_encoder_state_reset(None, 1, None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_encoder_position(None, 0) == -1
+    assert L.rlt_encoder_profile_begin(None, 1, 1) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_encoder_profile_collect(None, 0, None, None, None, None) == binding.RLT_ERR_INVALID_ARG
+    # the encoder state holds the cache [L][B][H][cap][dh] twice plus per-row scratch
+    for w in (TINY, SMALL, REFDEPTH):
+        m = w.model
+        es = 2 if m.dtype == 1 else 4
+        B, cap, R = 4, 96, 40
+        cache = 2 * m.n_layers * B * m.d_model * cap * es
+        scratch = R * m.d_model * (4 + 4 * es) + R * m.d_ffn * es
+        got = L.rlt_encoder_state_bytes(C.byref(cfg_of(w)), B, cap, R)
+        assert cache + scratch <= got <= cache + scratch + 16 * 256
+    assert L.rlt_encoder_state_bytes(C.byref(cfg_of(TINY)), 0, 16, 8) == 0
+    assert L.rlt_encoder_state_bytes(C.byref(cfg_of(TINY)), 2, 16, 0) == 0
+    # bf16 with head_dim 16 is outside the encoder kernels
+    assert L.rlt_encoder_state_bytes(C.byref(cfg_of(SMALL, n_heads=32, head_dim=16)), 2, 16, 8) == 0

@@ -1,0 +1,271 @@
+"""GPU parity of the causal encoder (rlt_encode) against the CPU oracle.
+
+Pages (by title): the encoder runs all known tokens at once under a causal
+mask with the decoder layers' weights and projects the memory from e_t
+[Recurrent Looped Transformer: A New Architecture for Infinite Context
+Reasoning in Language Models, "Encoder-Decoder Pairing with Shared Weights";
+Princeton Researcher Proposes Recurrent Looped Transformer to Carry Decoder
+State Across Tokens, architecture paragraph]; prefill is the encoder followed
+by the decoder recurrence over every prompt token [Understanding and Applying
+the Recurrent Looped Transformer Architecture, "Prompt prefill"].
+
+Gates: fp32 max |delta| <= 1e-4 on e, memory and encoder cache (values of
+order 1) and on logits after prefill; bf16 relative L2 <= 2e-2.  Chunking
+and batch composition do not change any value (bitwise): every kernel's result
+for a token depends only on that token's own row and the cache positions it
+attends to, in a fixed order."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _tiny import oracle_kwargs
+from recurrent_decode_step_amd import binding, synth
+from recurrent_decode_step_amd.configs import ModelConfig, REFDEPTH
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def setup(cfg, B, cap, max_rows, seed_index=0):
+    params = synth.model_params(cfg, device=DEV)
+    eparams = synth.encoder_params(cfg, device=DEV)
+    model = binding.Model(cfg, params, version=1)
+    enc = binding.Encoder(model, eparams)
+    es = binding.EncoderState(enc, B, cap, max_rows)
+    sd = torch.bfloat16 if cfg.dtype == 1 else torch.float32
+    shape = (cfg.mem_groups, B, cfg.n_heads, cap, cfg.head_dim)
+    mk = torch.zeros(shape, dtype=sd, device=DEV)
+    mv = torch.zeros(shape, dtype=sd, device=DEV)
+    return params, eparams, model, enc, es, mk, mv
+
+
+def oracle_encoder(cfg, params, eparams, precision):
+    om = oracle.Model(params={k: v.float().cpu() for k, v in params.items()}, precision=precision,
+                      **oracle_kwargs(cfg))
+    return oracle.Encoder(om, {k: v.float().cpu() for k, v in eparams.items()})
+
+
+def f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+CONFIGS_F32 = [
+    # (d, H, L, F, V, G): dh = 32, 16 and 128, one and per-layer memory groups
+    (64, 2, 2, 256, 100, 1),
+    (128, 8, 2, 192, 77, 2),
+    (256, 2, 1, 512, 300, 1),
+]
+
+
+@pytest.mark.parametrize("dims", CONFIGS_F32, ids=lambda d: "d%d_H%d_L%d_G%d" % (d[0], d[1], d[2], d[5]))
+def test_encode_fp32_matches_oracle(dims):
+    """3 sequences x 150 tokens = 450 rows: four 128-row tiles with a ragged
+    tail, three 64-query blocks per sequence with a ragged last one."""
+    d, H, L, F, V, G = dims
+    cfg = ModelConfig(vocab=V, d_model=d, n_heads=H, n_layers=L, d_ffn=F, window=8,
+                      mem_groups=G, dtype=0)
+    B, T = 3, 150
+    say(f"[encoder f32] {dims} B={B} T={T}")
+    params, eparams, model, enc, es, mk, mv = setup(cfg, B, 160, B * T)
+    tok = synth.token_ids(B, T, V, index=1)
+    e = binding.rlt_encode(enc, es, torch.from_numpy(tok).to(DEV), (mk, mv))
+    torch.cuda.synchronize()
+    ck, cv = es.cache()
+    ref_enc = oracle_encoder(cfg, params, eparams, "fp32")
+    worst = 0.0
+    for b in range(B):
+        r = oracle.encode(ref_enc, tok[b])
+        checks = [(f64(e[b]), r["e"]), (f64(mk[:, b, :, :T]), r["mem_k"]),
+                  (f64(mv[:, b, :, :T]), r["mem_v"]),
+                  (f64(ck[:, b, :, :T].transpose(1, 2)), r["cache_k"]),
+                  (f64(cv[:, b, :, :T].transpose(1, 2)), r["cache_v"])]
+        for got, want in checks:
+            assert got.shape == want.shape
+            worst = max(worst, float(np.abs(got - want).max()))
+    say(f"[encoder f32] max |delta| {worst:.2e}")
+    assert worst <= 1e-4
+    for b in range(B):
+        assert es.position(b) == T
+
+
+def test_encode_chunks_and_batches_are_bitwise_invariant():
+    """A prompt encoded in one call, in uneven chunks, or alone gives bitwise
+    the same e, memory and cache (positions continue across calls)."""
+    cfg = ModelConfig(vocab=120, d_model=128, n_heads=4, n_layers=2, d_ffn=256, window=8,
+                      mem_groups=2, dtype=1)
+    B, T = 4, 200
+    tok = torch.from_numpy(synth.token_ids(B, T, cfg.vocab, index=2)).to(DEV)
+    params, eparams, model, enc, es, mk, mv = setup(cfg, B, 256, B * T)
+    e_all = binding.rlt_encode(enc, es, tok, (mk, mv))
+    # same model, second state: chunks 1 + 63 + 136, sequences in another order / alone
+    es2 = binding.EncoderState(enc, B, 256, B * T)
+    mk2, mv2 = torch.zeros_like(mk), torch.zeros_like(mv)
+    parts = []
+    for lo, hi in ((0, 1), (1, 64), (64, 200)):
+        parts.append(binding.rlt_encode(enc, es2, tok[[2, 0, 3, 1], lo:hi].contiguous(), (mk2, mv2),
+                                        slots=[2, 0, 3, 1]))
+    e_chunk = torch.cat(parts, dim=1)[[1, 3, 0, 2]]
+    torch.cuda.synchronize()
+    assert torch.equal(e_all, e_chunk)
+    assert torch.equal(mk, mk2) and torch.equal(mv, mv2)
+    k1, v1 = es.cache()
+    k2, v2 = es2.cache()
+    assert torch.equal(k1[:, :, :, :T], k2[:, :, :, :T]) and torch.equal(v1[:, :, :, :T], v2[:, :, :, :T])
+    # one sequence alone in a fresh state
+    es3 = binding.EncoderState(enc, B, 256, T)
+    mk3, mv3 = torch.zeros_like(mk), torch.zeros_like(mv)
+    e_one = binding.rlt_encode(enc, es3, tok[3:4], (mk3, mv3), slots=[3])
+    torch.cuda.synchronize()
+    assert torch.equal(e_one[0], e_all[3])
+    assert torch.equal(mk3[:, 3, :, :T], mk[:, 3, :, :T])
+
+
+def test_encode_bf16_matches_oracle():
+    """bf16 storage (the bf16-emulating oracle): dh = 128 and dh = 64, two groups."""
+    for d, H, G in ((256, 2, 1), (256, 4, 2)):
+        cfg = ModelConfig(vocab=500, d_model=d, n_heads=H, n_layers=2, d_ffn=512, window=8,
+                          mem_groups=G, dtype=1)
+        B, T = 2, 130
+        say(f"[encoder bf16] d={d} H={H} G={G}")
+        params, eparams, model, enc, es, mk, mv = setup(cfg, B, T, B * T)
+        tok = synth.token_ids(B, T, cfg.vocab, index=3)
+        e = binding.rlt_encode(enc, es, torch.from_numpy(tok).to(DEV), (mk, mv))
+        torch.cuda.synchronize()
+        ref_enc = oracle_encoder(cfg, params, eparams, "bf16")
+        for b in range(B):
+            r = oracle.encode(ref_enc, tok[b])
+            for name, got, want in (("e", f64(e[b]), r["e"]), ("mem_k", f64(mk[:, b]), r["mem_k"]),
+                                    ("mem_v", f64(mv[:, b]), r["mem_v"])):
+                rel = rel_l2(got, want)
+                say(f"[encoder bf16] seq {b} {name} rel-L2 {rel:.2e}")
+                assert rel <= 2e-2, (name, rel)
+
+
+def test_prefill_encoder_then_decoder_matches_oracle():
+    """Prefill = rlt_encode over the prompt, then rlt_run_sequence over every
+    prompt token with the encoder's e and memory; logits against the oracle's
+    prefill (fp32, max |delta logit| <= 1e-4)."""
+    cfg = ModelConfig(vocab=64, d_model=64, n_heads=2, n_layers=2, d_ffn=128, window=8,
+                      mem_groups=2, dtype=0)
+    B, T = 3, 40
+    params, eparams, model, enc, es, mk, mv = setup(cfg, B, T, B * T)
+    tok = synth.token_ids(B, T, cfg.vocab, index=4)
+    e = binding.rlt_encode(enc, es, torch.from_numpy(tok).to(DEV), (mk, mv))
+    st = binding.State(model, B, T)
+    logits = binding.rlt_run_sequence(model, st, e, (mk, mv))
+    torch.cuda.synchronize()
+    ref_enc = oracle_encoder(cfg, params, eparams, "fp32")
+    states = [oracle.initial_state(ref_enc.m) for _ in range(B)]
+    ref, _, _, _ = oracle.prefill(ref_enc, states, tok)
+    err = float(np.abs(f64(logits) - ref).max())
+    say(f"[prefill f32] max |delta logit| {err:.2e}")
+    assert err <= 1e-4
+    for b in range(B):
+        assert st.position(b) == T and es.position(b) == T
+
+
+def test_encode_argument_and_range_errors():
+    cfg = ModelConfig(vocab=50, d_model=64, n_heads=2, n_layers=1, d_ffn=128, window=4,
+                      mem_groups=1, dtype=0)
+    params, eparams, model, enc, es, mk, mv = setup(cfg, 2, 16, 20)
+    tok = torch.zeros((2, 10), dtype=torch.int32, device=DEV)
+    with pytest.raises(binding.RLTError) as ex:
+        binding.rlt_encode(enc, es, torch.zeros((2, 11), dtype=torch.int32, device=DEV), (mk, mv))
+    assert ex.value.status == binding.RLT_ERR_SHAPE
+    with pytest.raises(binding.RLTError) as ex:
+        binding.rlt_encode(enc, es, tok, (mk, mv), slots=[1, 1])
+    assert ex.value.status == binding.RLT_ERR_INVALID_ARG
+    binding.rlt_encode(enc, es, tok, (mk, mv))
+    with pytest.raises(binding.RLTError) as ex:          # 20 > max_tokens 16
+        binding.rlt_encode(enc, es, tok, (mk, mv))
+    assert ex.value.status == binding.RLT_ERR_RANGE
+    assert es.position(0) == 10 and es.position(1) == 10
+    binding.rlt_encoder_state_reset(es, [0])
+    assert es.position(0) == 0
+    small = torch.zeros((1, 2, 2, 12, 32), dtype=torch.float32, device=DEV)
+    with pytest.raises(binding.RLTError) as ex:          # memory capacity 12 < 10 + 10
+        binding.rlt_encode(enc, es, tok[1:], (small, small.clone()), slots=[1])
+    assert ex.value.status == binding.RLT_ERR_RANGE
+    # a bf16 model with head_dim 16 is outside the encoder kernels
+    cfg16 = ModelConfig(vocab=50, d_model=64, n_heads=4, n_layers=1, d_ffn=128, window=4,
+                        mem_groups=1, dtype=1)
+    m16 = binding.Model(cfg16, synth.model_params(cfg16, device=DEV))
+    with pytest.raises(binding.RLTError) as ex:
+        binding.Encoder(m16, synth.encoder_params(cfg16, device=DEV))
+    assert ex.value.status == binding.RLT_ERR_UNSUPPORTED
+
+
+def test_out_of_vocabulary_token_poisons_only_its_sequence():
+    """A token outside 0..V-1 gives NaN at its position and, through causal
+    attention, at every later position of its sequence; the other sequences of
+    the call are bitwise untouched (no out-of-range read)."""
+    cfg = ModelConfig(vocab=40, d_model=64, n_heads=2, n_layers=1, d_ffn=128, window=4,
+                      mem_groups=1, dtype=0)
+    params, eparams, model, enc, es, mk, mv = setup(cfg, 2, 12, 24)
+    tok = torch.from_numpy(synth.token_ids(2, 12, cfg.vocab, index=5)).to(DEV)
+    ref = binding.rlt_encode(enc, es, tok, (mk, mv))
+    es2 = binding.EncoderState(enc, 2, 12, 24)
+    bad = tok.clone()
+    bad[1, 5] = cfg.vocab
+    got = binding.rlt_encode(enc, es2, bad, (torch.zeros_like(mk), torch.zeros_like(mv)))
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], ref[0])
+    assert torch.isnan(got[1, 5:]).all()
+
+
+def test_refdepth_full_prompt_sampled_rows():
+    """The reference-depth model (48 layers, d = 2048, H = 16, F = 8192, bf16)
+    over the full 2048-token prompt of 32 sequences in one call (the launches
+    the benchmark times).  Causality lets the oracle check the first 48
+    positions of two sampled sequences exactly as computed in that launch; the
+    last positions are checked by chunk invariance (the same sequence encoded
+    alone in two calls gives bitwise the same rows)."""
+    wl = REFDEPTH
+    cfg = wl.model
+    B, T = wl.batch, wl.prompt
+    say(f"[encoder full] {wl.name}: B={B} T={T}")
+    params, eparams, model, enc, es, mk, mv = setup(cfg, B, T, B * T)
+    tok = torch.from_numpy(synth.token_ids(B, T, cfg.vocab, index=6)).to(DEV)
+    e = binding.rlt_encode(enc, es, tok, (mk, mv))
+    torch.cuda.synchronize()
+    assert torch.isfinite(e).all()
+    say("[encoder full] launch done")
+    # chunk invariance of the tail: sequence 31 alone, 2000 + 48 tokens
+    es2 = binding.EncoderState(enc, B, T, T)
+    mk2 = torch.zeros((cfg.mem_groups, B, cfg.n_heads, T, cfg.head_dim), dtype=mk.dtype, device=DEV)
+    mv2 = torch.zeros_like(mk2)
+    a = binding.rlt_encode(enc, es2, tok[31:32, :2000].contiguous(), (mk2, mv2), slots=[31])
+    b = binding.rlt_encode(enc, es2, tok[31:32, 2000:].contiguous(), (mk2, mv2), slots=[31])
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([a, b], dim=1)[0], e[31])
+    assert torch.equal(mk2[:, 31], mk[:, 31])
+    say("[encoder full] chunk invariance ok")
+    del es2, mk2, mv2
+    # oracle on the first P positions of two sequences
+    P = 48
+    LAYER_KEYS = ("g1", "g2", "g3", "wq", "wk", "wv", "wo", "wqc", "woc", "w1", "w2")
+    small = {k: params[k].float().cpu() for k in ("s_star", "wg", "bg", "go", "wout")}
+    om = oracle.Model(params=small, precision="bf16", **oracle_kwargs(cfg),
+                      layer_source=lambda l: {k: params[k][l].float().cpu() for k in LAYER_KEYS})
+    oe = oracle.Encoder(om, {k: v.float().cpu() for k, v in eparams.items()})
+    tok_np = tok.cpu().numpy()
+    for bsel in (0, 17):
+        r = oracle.encode(oe, tok_np[bsel, :P])
+        for name, got, want in (("e", f64(e[bsel, :P]), r["e"]),
+                                ("mem_k", f64(mk[:, bsel, :, :P]), r["mem_k"]),
+                                ("mem_v", f64(mv[:, bsel, :, :P]), r["mem_v"])):
+            rel = rel_l2(got, want)
+            say(f"[encoder full] seq {bsel} {name}[:{P}] rel-L2 {rel:.2e}")
+            assert rel <= 2e-2, (bsel, name, rel)
