@@ -684,6 +684,120 @@ def run_longctx(args):
     }
 
 
+def run_encode(args):
+    """The token-parallel causal encoder over the reference-depth prompt: 32
+    sequences x 2048 tokens in one rlt_encode call (e rows, the encoder cache
+    of every layer and the memory entries of all 2048 positions), repeated
+    `steps` times from position 0.  Each kernel class is timed with HIP events
+    on the launch stream; the GEMMs are the dominant, MFMA-bound kernels."""
+    import numpy as np
+    import torch
+    from recurrent_decode_step_amd import binding, synth
+    from recurrent_decode_step_amd.configs import REFDEPTH
+    wl = REFDEPTH
+    cfg, B, T = wl.model, wl.batch, wl.prompt
+    K = 3 if args.steps is None else args.steps
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t_setup = time.time()
+    params = synth.model_params(cfg, device=dev)
+    eparams = synth.encoder_params(cfg, device=dev)
+    model = binding.Model(cfg, params, version=1)
+    enc = binding.Encoder(model, eparams)
+    es = binding.EncoderState(enc, B, T, B * T)
+    sd = torch.bfloat16
+    mk = torch.zeros((cfg.mem_groups, B, cfg.n_heads, T, cfg.head_dim), dtype=sd, device=dev)
+    mv = torch.zeros_like(mk)
+    mem = binding.memory_view(mk, mv)
+    tok_np = synth.token_ids(B, T, cfg.vocab, index=0)
+    tok = torch.from_numpy(tok_np).to(dev)
+    e = torch.empty((B, T, cfg.d_model), dtype=sd, device=dev)
+    slots = list(range(B))
+    setup_s = time.time() - t_setup
+    if args.calibrate_copy:
+        calibration_copy(dev)
+    for _ in range(max(args.warmup, 0)):
+        binding.rlt_encode(enc, es, tok, mem, e_out=e)
+        binding.rlt_encoder_state_reset(es, slots)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(K):
+        binding.rlt_encode(enc, es, tok, mem, e_out=e)
+        binding.rlt_encoder_state_reset(es, slots)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / K
+    if not torch.isfinite(e).all():
+        raise RuntimeError("non-finite encoder output")
+    # per-class kernel times of one more call, HIP events around every launch
+    binding.encoder_profile_begin(es, 0b111, 100000)
+    binding.rlt_encode(enc, es, tok, mem, e_out=e)
+    binding.rlt_encoder_state_reset(es, slots)
+    cls = {}
+    for name, c in (("gemm", binding.RLT_E_GEMM), ("attention", binding.RLT_E_ATTN),
+                    ("embed_norm", binding.RLT_E_OTHER)):
+        tot, n, fl, by = binding.encoder_profile_collect(es, c)
+        cls[name] = {"ms": tot, "launches": n, "flops": fl, "bytes": by}
+    binding.encoder_profile_begin(es, 0, 0)
+    g = cls["gemm"]
+    a = cls["attention"]
+    flops_total = g["flops"] + a["flops"]
+    out = {
+        "metric": "encoder prompt tokens/sec at 1 GPU (48-layer, B=32 x 2048-token prompt)",
+        "value": round(B * T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + ", causal encoder over the prompt", "batch": B,
+                   "prompt": T, "tokens": "uniform in the vocabulary (seed 7)",
+                   "outputs": "e rows, encoder cache of 48 layers, memory K/V of 2048 positions"},
+        "roofline": {"bound": "mfma", "kernel": "k_pgemm (token-parallel GEMMs)",
+                     "achieved": round(g["flops"] / (g["ms"] / 1e3) / 1e12, 1), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(g["flops"] / (g["ms"] / 1e3) / 2.5e15, 4),
+                     "traffic": None, "flops_per_call": g["flops"], "launches": g["launches"],
+                     "avg_launch_us": round(1e3 * g["ms"] / max(g["launches"], 1), 2)},
+        "call_mfma": {"flops": flops_total, "achieved": round(flops_total / (ms / 1e3) / 1e12, 1),
+                      "frac": round(flops_total / (ms / 1e3) / 2.5e15, 4)},
+        "breakdown_ms": {k: round(v["ms"], 3) for k, v in cls.items()},
+        "attention_TFLOPs": round(a["flops"] / (a["ms"] / 1e3) / 1e12, 1),
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_encoder_baseline(cfg, params, eparams, tok_np[0], args.cpu_budget)
+    return out
+
+
+def cpu_encoder_baseline(cfg, params_gpu, eparams_gpu, tokens, budget_s=15.0):
+    """The oracle's encoder (fp32 NumPy, as it stands) over growing prefixes of
+    one sequence until the time budget is spent; tokens/s of the longest."""
+    import oracle
+    t_prep = time.time()
+    LAYER_KEYS = ("g1", "g2", "g3", "wq", "wk", "wv", "wo", "wqc", "woc", "w1", "w2")
+    small = {k: params_gpu[k].float().cpu() for k in ("s_star", "wg", "bg", "go", "wout")}
+    layers = [{k: params_gpu[k][l].float().cpu() for k in LAYER_KEYS} for l in range(cfg.n_layers)]
+    om = oracle.Model(params=small, precision="fp32", d_model=cfg.d_model, n_heads=cfg.n_heads,
+                      n_layers=cfg.n_layers, d_ffn=cfg.d_ffn, window=cfg.window,
+                      mem_groups=cfg.mem_groups, vocab=cfg.vocab, rms_eps=cfg.rms_eps,
+                      layer_source=lambda l: layers[l])
+    oe = oracle.Encoder(om, {k: v.float().cpu() for k, v in eparams_gpu.items()})
+    prep = time.time() - t_prep
+    n, rate, el = 16, 0.0, 0.0
+    spent = 0.0
+    while spent < budget_s and n <= len(tokens):
+        t0 = time.time()
+        oracle.encode(oe, tokens[:n])
+        el = time.time() - t0
+        spent += el
+        rate, done = n / el, n
+        n *= 2
+    return {"value": rate, "unit": "tokens/s", "cores": openblas_threads(), "kind": "oracle",
+            "sample": f"1 sequence, its first {done} tokens in one oracle encode call "
+                      f"(NumPy fp32, 48 layers; {el:.1f} s timed, {spent:.1f} s over the doubling "
+                      f"prefixes, {prep:.1f} s weight conversion untimed)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -695,6 +809,8 @@ def main():
                     help="longctx: one full 32768-step run instead of the window fit")
     ap.add_argument("--generate", action="store_true",
                     help="generation at the reference depth after the 2048-token prompt")
+    ap.add_argument("--encode", action="store_true",
+                    help="the causal encoder over the reference-depth prompt (B = 32 x 2048 tokens)")
     ap.add_argument("--score", action="store_true",
                     help="replay scoring at the reference depth (log-probability of each next token)")
     ap.add_argument("--counters-sample", action="store_true",
@@ -716,6 +832,8 @@ def main():
         raise SystemExit(2)
     if args.counters_sample:
         out = run_counters_sample(args)
+    elif args.encode:
+        out = run_encode(args)
     elif args.score:
         out = run_score(args)
     elif args.generate:

@@ -12,8 +12,9 @@
 // Kernels (one launch each on the caller's stream):
 //   k_enc_embed  token embedding rows into the fp32 residual stream
 //   k_enc_norm   RMSNorm of rows into the storage type
-//   k_pgemm      token-parallel GEMM on MFMA: 128 tokens x 128 features per
-//                workgroup, both operands staged through LDS in fragment order,
+//   k_pgemm32    token-parallel GEMM (bf16) on the 32x32x16 MFMA: 128 tokens x
+//                256 features per workgroup, both operands staged through LDS
+//                in fragment order (k_pgemm: the fp32 form on 16x16x4),
 //                fused epilogues (q + encoder-cache append, residual add,
 //                GELU, memory K/V append)
 //   k_fattn      causal flash attention over the encoder cache: 64 queries of
@@ -82,20 +83,33 @@ __global__ __launch_bounds__(256) void k_enc_norm(const float *__restrict__ x, i
 // ---------------------------------------------------------------- GEMM
 // y[r][n] = sum_k W[n][k] a[r][k] over the call's token rows r.
 //
-// Workgroup tile: 128 token rows x 8 weight tiles (128 features), 4 wavefronts
-// in a 2 x 2 grid, each 64 features x 64 rows = 4 x 4 MFMA blocks.  The weight
-// tile is the A operand (feature rows), the token rows the B operand, so each
-// lane's accumulator holds 4 consecutive features of one token row.  K goes in
-// stages of 2 k-steps: every stage's fragments of both operands are loaded to
-// registers while the previous stage is multiplied out of LDS, then written to
-// the other LDS buffer in fragment order (each MFMA operand read is one
-// contiguous KiB).  The launch order puts each XCD on a contiguous run of
-// groups of 4 row tiles x all feature tiles, so the 4 row tiles stay in that
-// XCD's L2 while the weight tiles stream past them.
-constexpr int kPgRows = 128;   // token rows per workgroup
-constexpr int kPgTiles = 8;    // 16-feature weight tiles per workgroup
-constexpr int kPgKs = 2;       // k-steps per stage
-constexpr int kPgGroup = 4;    // row tiles per group of the launch order
+// Workgroup tile: RB 16-row blocks of tokens x TB 16-feature weight tiles, WM x
+// WN wavefronts, each (RB/WM) row blocks x (TB/WN) tiles of MFMA blocks (the
+// configuration is a template argument, see PgCfg).  The
+// weight tile is the A operand (feature rows), the token rows the B operand,
+// so each lane's accumulator holds 4 consecutive features of one token row.
+// K goes in stages of KS k-steps: each stage's fragments of both operands are
+// loaded to registers while the previous stage is multiplied out of LDS, then
+// written to the other LDS buffer in fragment order (every MFMA operand read is
+// one contiguous KiB, conflict-free).  The launch order gives each XCD a
+// contiguous run of groups of GROUP row tiles x all feature tiles, so a
+// group's activation rows stay in that XCD's L2 while the weight tiles stream
+// past them.
+// Tile configuration: RB token row blocks x TB weight tiles per workgroup,
+// WM x WN wavefronts, KS k-steps per stage, NBUF LDS buffers (2: the next
+// stage is written while this one is read; 1: written after a barrier), WPE
+// wavefronts per SIMD the register budget is sized for, GROUP row tiles per
+// group of the launch order (0: plain row-major order, no XCD placement).
+template <int RB_, int TB_, int WM_, int WN_, int KS_, int NBUF_, int WPE_, int GROUP_ = 4>
+struct PgCfg {
+  static constexpr int RB = RB_, TB = TB_, WM = WM_, WN = WN_, KS = KS_, NBUF = NBUF_, WPE = WPE_;
+  static constexpr int GROUP = GROUP_;
+  static constexpr int THREADS = 64 * WM * WN;
+  static constexpr int LDS = NBUF * (RB + TB) * KS * 64 * 16;   // bytes
+};
+// 128 tokens x 256 features, one k-step per stage, double-buffered, two
+// workgroups per CU
+using PgDefault = PgCfg<8, 16, 2, 2, 1, 2, 2>;
 
 __device__ __forceinline__ void enc_row(const EncRows &R, int r, int &slot, int &pos) {
   const int i = r / R.T;
@@ -134,94 +148,328 @@ __device__ __forceinline__ void pgemm_store(const PGemmArgs &a, int r, int n, f3
   }
 }
 
-template <typename T, int EPI>
-__global__ __launch_bounds__(256, 2) void k_pgemm(PGemmArgs a, int mt, int nt) {
+template <typename T, int EPI, class C>
+__global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm(PGemmArgs a, int mt, int nt) {
   constexpr int EPL = Num<T>::EPL;
   constexpr int KSTEP = 4 * EPL;
-  constexpr int FR = kPgTiles * kPgKs * 64;     // fragments of one operand per stage
-  __shared__ u32x4 sW[2][FR];
-  __shared__ u32x4 sA[2][FR];
+  constexpr int kPgKs = C::KS;
+  constexpr int NW = C::WM * C::WN;
+  constexpr int FA = C::RB * kPgKs, FW = C::TB * kPgKs;    // fragments per stage
+  constexpr int FPW = (FA + FW) / NW;                      // fragments each wavefront stages
+  constexpr int WRB = C::RB / C::WM, WTB = C::TB / C::WN;  // wavefront tile
+  static_assert((FA + FW) % NW == 0 && FA % NW == 0, "staging split");
+  extern __shared__ u32x4 smem[];
+  u32x4 *sA = smem;                    // [NBUF][FA * 64]
+  u32x4 *sW = smem + C::NBUF * FA * 64;  // [NBUF][FW * 64]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // workgroup -> (row tile, feature tile group)
   const int total = mt * nt;
   const int id = blockIdx.x;
-  const int v = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;
-  const int grp = v / (kPgGroup * nt);
-  const int m0 = grp * kPgGroup;
-  const int gm = min(kPgGroup, mt - m0);
-  const int w = v - grp * kPgGroup * nt;
-  const int tm = m0 + w % gm, tn = w / gm;
-  const int row0 = tm * kPgRows, tile0 = tn * kPgTiles;
+  int tm, tn;
+  if constexpr (C::GROUP > 0) {
+    const int v = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;
+    const int grp = v / (C::GROUP * nt);
+    const int m0 = grp * C::GROUP;
+    const int gm = min(C::GROUP, mt - m0);
+    const int w = v - grp * C::GROUP * nt;
+    tm = m0 + w % gm;
+    tn = w / gm;
+  } else {
+    tm = id / nt;
+    tn = id - tm * nt;
+  }
+  const int row0 = tm * C::RB * 16, tile0 = tn * C::TB;
   const int ntiles = a.Np >> 4;
   const int n_rows = a.rows.n_rows;
   const u32x4 *wp = static_cast<const u32x4 *>(a.wp);
   const T *ap = static_cast<const T *>(a.a);
 
-  // staging: wavefront w moves row blocks / weight tiles 2w and 2w+1, k-steps 0 and 1
-  u32x4 ra[4], rw[4];
+  // staging: fragment f = wave + NW * u; u < FA / NW are activation fragments
+  // (row block f / KS), the rest weight fragments.  Every load is issued
+  // unconditionally from a clamped address and zeroed where out of range only
+  // when written to LDS, so no branch sits between the loads in flight.
+  u32x4 rg[FPW];
+  bool rok[FPW];
   auto load = [&](int st) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int blk = 2 * wave + (f >> 1), ks = f & 1;
-      const int kt = st * kPgKs + ks;
-      const bool kok = kt < a.KT;
-      const int row = row0 + blk * 16 + (lane & 15);
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      ra[f] = (kok && row < n_rows)
-                  ? *reinterpret_cast<const u32x4 *>(ap + (size_t)row * a.lda + kt * KSTEP +
-                                                     (lane >> 4) * EPL)
-                  : zero;
-      const int tile = tile0 + blk;
-      rw[f] = (kok && tile < ntiles) ? wp[((size_t)tile * a.KT + kt) * 64 + lane] : zero;
+    for (int u = 0; u < FPW; ++u) {
+      const int f = wave + NW * u;
+      if (u < FA / NW) {
+        const int blk = f / kPgKs, kt = st * kPgKs + f % kPgKs;
+        const int row = row0 + blk * 16 + (lane & 15);
+        rok[u] = kt < a.KT && row < n_rows;
+        rg[u] = *reinterpret_cast<const u32x4 *>(ap + (size_t)min(row, n_rows - 1) * a.lda +
+                                                 min(kt, a.KT - 1) * KSTEP + (lane >> 4) * EPL);
+      } else {
+        const int g = f - FA;
+        const int tile = tile0 + g / kPgKs, kt = st * kPgKs + g % kPgKs;
+        rok[u] = kt < a.KT && tile < ntiles;
+        rg[u] = wp[((size_t)min(tile, ntiles - 1) * a.KT + min(kt, a.KT - 1)) * 64 + lane];
+      }
     }
   };
   auto store = [&](int buf) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int blk = 2 * wave + (f >> 1), ks = f & 1;
-      sA[buf][(blk * kPgKs + ks) * 64 + lane] = ra[f];
-      sW[buf][(blk * kPgKs + ks) * 64 + lane] = rw[f];
+    for (int u = 0; u < FPW; ++u) {
+      const int f = wave + NW * u;
+      const u32x4 v = rok[u] ? rg[u] : zero;
+      if (u < FA / NW) sA[(buf * FA + f) * 64 + lane] = v;
+      else sW[(buf * FW + f - FA) * 64 + lane] = v;
     }
   };
 
-  const int wn = wave & 1, wm = wave >> 1;
-  f32x4 acc[4][4];
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  f32x4 acc[WTB][WRB];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < WTB; ++t)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < WRB; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // operand fragments of one k-step, two register sets: the next k-step's
+  // LDS reads are in flight while the current one is multiplied out
+  u32x4 wf[2][WTB], af[2][WRB];
+  auto frags = [&](int buf, int ks, int set) {
+#pragma unroll
+    for (int t = 0; t < WTB; ++t) wf[set][t] = sW[(buf * FW + (wn * WTB + t) * kPgKs + ks) * 64 + lane];
+#pragma unroll
+    for (int b = 0; b < WRB; ++b) af[set][b] = sA[(buf * FA + (wm * WRB + b) * kPgKs + ks) * 64 + lane];
+  };
 
   const int S = (a.KT + kPgKs - 1) / kPgKs;
   load(0);
   store(0);
   __syncthreads();
   for (int st = 0; st < S; ++st) {
-    const int buf = st & 1;
+    const int buf = C::NBUF == 2 ? (st & 1) : 0;
     if (st + 1 < S) load(st + 1);
+    frags(buf, 0, 0);
 #pragma unroll
     for (int ks = 0; ks < kPgKs; ++ks) {
-      u32x4 wf[4], af[4];
+      if (ks + 1 < kPgKs) frags(buf, ks + 1, (ks + 1) & 1);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) wf[t] = sW[buf][((wn * 4 + t) * kPgKs + ks) * 64 + lane];
+      for (int t = 0; t < WTB; ++t)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) af[b] = sA[buf][((wm * 4 + b) * kPgKs + ks) * 64 + lane];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[t][b] = mma_step(wf[t], af[b], acc[t][b], T());
+        for (int b = 0; b < WRB; ++b)
+          acc[t][b] = mma_step(wf[ks & 1][t], af[ks & 1][b], acc[t][b], T());
     }
-    if (st + 1 < S) store(buf ^ 1);
-    __syncthreads();
+    if constexpr (C::NBUF == 2) {
+      if (st + 1 < S) store(buf ^ 1);
+      __syncthreads();
+    } else {
+      __syncthreads();               // every wavefront is done reading the buffer
+      if (st + 1 < S) {
+        store(0);
+        __syncthreads();
+      }
+    }
   }
 
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int n = (tile0 + wn * 4 + t) * 16 + (lane >> 4) * 4;
+  for (int t = 0; t < WTB; ++t) {
+    const int n = (tile0 + wn * WTB + t) * 16 + (lane >> 4) * 4;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int r = row0 + (wm * 4 + b) * 16 + (lane & 15);
+    for (int b = 0; b < WRB; ++b) {
+      const int r = row0 + (wm * WRB + b) * 16 + (lane & 15);
       if (r < n_rows && n < a.N) pgemm_store<T, EPI>(a, r, n, acc[t][b]);
+    }
+  }
+}
+
+// bf16 form on the 32x32x16 MFMA, which does twice the work of the 16x16x32 one
+// per instruction at about the same issue cost on gfx950.  Fragments are
+// 32 rows x 16 k: lane l holds row l % 32, k = 8 (l / 32) .. +7; the product's
+// register r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+// A stage is one packed k-step (32 k = two MFMA k-steps).  Weight fragments
+// keep their packed 16-row layout in memory and are moved to the 32-row layout
+// when written to LDS: piece (16-row tile t, lane r16 + 16 g) goes to 32-row
+// block t / 2, k-half g / 2, lane (t % 2) * 16 + r16 + 32 (g % 2).
+template <int RB_, int FB_, int WM_, int WN_, int NBUF_, int WPE_, int GROUP_ = 4, int PD_ = 1>
+struct Pg32Cfg {
+  static constexpr int RB = RB_, FB = FB_, WM = WM_, WN = WN_, NBUF = NBUF_, WPE = WPE_;
+  static constexpr int GROUP = GROUP_;
+  static constexpr int PD = PD_;       // stages in flight ahead of the one multiplied out
+  static constexpr int THREADS = 64 * WM * WN;
+  static constexpr int LDS = NBUF * (RB + FB) * 2 * 64 * 16;   // bytes
+  static_assert(LDS >= WM * WN * 32 * 36 * 4, "epilogue scratch fits in the staging buffers");
+};
+// 128 tokens x 256 features, double-buffered, two stages in flight, two
+// workgroups per CU
+using Pg32Default = Pg32Cfg<4, 8, 2, 2, 2, 2, 8, 2>;
+
+template <int EPI, class C>
+__global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32(PGemmArgs a, int mt, int nt) {
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  constexpr int NW = C::WM * C::WN;
+  constexpr int FA = 2 * C::RB, FW = 2 * C::FB;             // 1-KiB fragments per stage
+  constexpr int FPW = (FA + FW) / NW;
+  constexpr int WRB = C::RB / C::WM, WFB = C::FB / C::WN;   // wavefront tile (32-blocks)
+  static_assert((FA + FW) % NW == 0 && FA % NW == 0, "staging split");
+  extern __shared__ u32x4 smem[];
+  u32x4 *sA = smem;                      // [NBUF][FA * 64]
+  u32x4 *sW = smem + C::NBUF * FA * 64;  // [NBUF][FW * 64]
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int total = mt * nt;
+  const int id = blockIdx.x;
+  int tm, tn;
+  if constexpr (C::GROUP > 0) {
+    const int v = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;
+    const int grp = v / (C::GROUP * nt);
+    const int m0 = grp * C::GROUP;
+    const int gm = min(C::GROUP, mt - m0);
+    const int w = v - grp * C::GROUP * nt;
+    tm = m0 + w % gm;
+    tn = w / gm;
+  } else {
+    tm = id / nt;
+    tn = id - tm * nt;
+  }
+  const int row0 = tm * C::RB * 32, tile0 = tn * C::FB * 2;   // first 16-row weight tile
+  const int ntiles = a.Np >> 4;
+  const int n_rows = a.rows.n_rows;
+  const u32x4 *wp = static_cast<const u32x4 *>(a.wp);
+  const bf16_t *ap = static_cast<const bf16_t *>(a.a);
+
+  // staging: fragment f = wave + NW * u; u < FA / NW: activations (32-row
+  // block f / 2, k-half f % 2); otherwise weight tile f - FA (packed layout).
+  // C::PD register sets: stage k's fragments live in set k % PD.
+  u32x4 rg[C::PD][FPW];
+  bool rok[C::PD][FPW];
+  auto load = [&](int st, int set) {
+#pragma unroll
+    for (int u = 0; u < FPW; ++u) {
+      const int f = wave + NW * u;
+      if (u < FA / NW) {
+        const int row = row0 + (f >> 1) * 32 + (lane & 31);
+        rok[set][u] = row < n_rows;
+        rg[set][u] = *reinterpret_cast<const u32x4 *>(ap + (size_t)min(row, n_rows - 1) * a.lda +
+                                                      st * 32 + (f & 1) * 16 + (lane >> 5) * 8);
+      } else {
+        const int tile = tile0 + f - FA;
+        rok[set][u] = tile < ntiles;
+        rg[set][u] = wp[((size_t)min(tile, ntiles - 1) * a.KT + st) * 64 + lane];
+      }
+    }
+  };
+  auto store = [&](int set, int buf) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < FPW; ++u) {
+      const int f = wave + NW * u;
+      const u32x4 v = rok[set][u] ? rg[set][u] : zero;
+      if (u < FA / NW) {
+        sA[(buf * FA + f) * 64 + lane] = v;
+      } else {
+        const int t = f - FA, g = lane >> 4;
+        const int dst = ((t >> 1) * 2 + (g >> 1)) * 64 + (t & 1) * 16 + (lane & 15) + 32 * (g & 1);
+        sW[buf * FW * 64 + dst] = v;
+      }
+    }
+  };
+
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  f32x16 acc[WFB][WRB];
+#pragma unroll
+  for (int f = 0; f < WFB; ++f)
+#pragma unroll
+    for (int r = 0; r < WRB; ++r)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[f][r][e] = 0.f;
+
+  u32x4 wf[2][WFB], af[2][WRB];
+  auto frags = [&](int buf, int j, int set) {
+#pragma unroll
+    for (int f = 0; f < WFB; ++f) wf[set][f] = sW[(buf * FW + (wn * WFB + f) * 2 + j) * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < WRB; ++r) af[set][r] = sA[(buf * FA + (wm * WRB + r) * 2 + j) * 64 + lane];
+  };
+
+  auto mult = [&](int buf) {
+    frags(buf, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j == 0) frags(buf, 1, 1);
+#pragma unroll
+      for (int f = 0; f < WFB; ++f)
+#pragma unroll
+        for (int r = 0; r < WRB; ++r)
+          acc[f][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, wf[j][f]), __builtin_bit_cast(bf16x8, af[j][r]),
+              acc[f][r], 0, 0, 0);
+    }
+  };
+
+  const int S = a.KT;
+  if constexpr (C::PD == 1) {
+    load(0, 0);
+    store(0, 0);
+    __syncthreads();
+    for (int st = 0; st < S; ++st) {
+      const int buf = C::NBUF == 2 ? (st & 1) : 0;
+      if (st + 1 < S) load(st + 1, 0);
+      mult(buf);
+      if constexpr (C::NBUF == 2) {
+        if (st + 1 < S) store(0, buf ^ 1);
+        __syncthreads();
+      } else {
+        __syncthreads();
+        if (st + 1 < S) {
+          store(0, 0);
+          __syncthreads();
+        }
+      }
+    }
+  } else {
+    // two stages in flight: stage st+2 is loaded into set st % 2 while stage st
+    // is multiplied out and stage st+1 (set (st+1) % 2) is written to LDS
+    static_assert(C::PD == 2 && C::NBUF == 2, "prefetch distance 2 needs two LDS buffers");
+    load(0, 0);
+    if (S > 1) load(1, 1);
+    store(0, 0);
+    __syncthreads();
+    auto step = [&](int st, int par) {
+      if (st + 2 < S) load(st + 2, par);
+      mult(par);
+      if (st + 1 < S) store(par ^ 1, par ^ 1);
+      __syncthreads();
+    };
+    for (int st = 0; st < S; st += 2) {
+      step(st, 0);
+      if (st + 1 < S) step(st + 1, 1);
+    }
+  }
+
+  // Epilogue through LDS (the staging buffers are free after the last
+  // barrier): each wavefront writes one 32 x 32 block at a time to its own
+  // padded scratch [token][feature] and reads it back by rows, so a store
+  // instruction covers 8 token rows x 32 consecutive features.
+  constexpr int EROW = 36;                           // padded row, floats
+  float *scr = reinterpret_cast<float *>(smem) + wave * 32 * EROW;
+#pragma unroll
+  for (int f = 0; f < WFB; ++f) {
+    const int fblk = (tile0 / 2 + wn * WFB + f) * 32;
+#pragma unroll
+    for (int r = 0; r < WRB; ++r) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4 *>(scr + (lane & 31) * EROW + 8 * q + 4 * (lane >> 5)) =
+            f32x4{acc[f][r][4 * q], acc[f][r][4 * q + 1], acc[f][r][4 * q + 2], acc[f][r][4 * q + 3]};
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int tblk = row0 + (wm * WRB + r) * 32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(scr + tr * EROW + fc);
+        const int row = tblk + tr, n = fblk + fc;
+        if (row < n_rows && n < a.N) pgemm_store<bf16_t, EPI>(a, row, n, v);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 }
@@ -458,24 +706,63 @@ hipError_t launch_enc_norm(int dtype, const float *x, int64_t ldx, const float *
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t pgemm_epi(int epi, const PGemmArgs &a, hipStream_t s) {
-  const int mt = (a.rows.n_rows + kPgRows - 1) / kPgRows;
-  const int nt = ((a.Np >> 4) + kPgTiles - 1) / kPgTiles;
-  const dim3 grid(mt * nt), block(256);
-  switch (epi) {
-    case PEPI_QKV: hipLaunchKernelGGL((k_pgemm<T, PEPI_QKV>), grid, block, 0, s, a, mt, nt); break;
-    case PEPI_RESID: hipLaunchKernelGGL((k_pgemm<T, PEPI_RESID>), grid, block, 0, s, a, mt, nt); break;
-    case PEPI_GELU: hipLaunchKernelGGL((k_pgemm<T, PEPI_GELU>), grid, block, 0, s, a, mt, nt); break;
-    case PEPI_MEM: hipLaunchKernelGGL((k_pgemm<T, PEPI_MEM>), grid, block, 0, s, a, mt, nt); break;
-    default: return hipErrorInvalidValue;
+template <typename T, int EPI, class C>
+hipError_t pgemm_go(const PGemmArgs &a, hipStream_t s) {
+  const int mt = (a.rows.n_rows + C::RB * 16 - 1) / (C::RB * 16);
+  const int nt = ((a.Np >> 4) + C::TB - 1) / C::TB;
+  if (C::LDS > 65536) {
+    // more LDS than the static limit: allow it once per instantiation
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_pgemm<T, EPI, C>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (attr != hipSuccess) return attr;
   }
+  hipLaunchKernelGGL((k_pgemm<T, EPI, C>), dim3(mt * nt), dim3(C::THREADS), C::LDS, s, a, mt, nt);
   return hipGetLastError();
+}
+
+template <typename T, class C>
+hipError_t pgemm_epi(int epi, const PGemmArgs &a, hipStream_t s) {
+  switch (epi) {
+    case PEPI_QKV: return pgemm_go<T, PEPI_QKV, C>(a, s);
+    case PEPI_RESID: return pgemm_go<T, PEPI_RESID, C>(a, s);
+    case PEPI_GELU: return pgemm_go<T, PEPI_GELU, C>(a, s);
+    case PEPI_MEM: return pgemm_go<T, PEPI_MEM, C>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int EPI, class C>
+hipError_t pgemm32_go(const PGemmArgs &a, hipStream_t s) {
+  const int mt = (a.rows.n_rows + C::RB * 32 - 1) / (C::RB * 32);
+  const int nt = ((a.Np >> 5) + C::FB - 1) / C::FB;
+  if (C::LDS > 65536) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_pgemm32<EPI, C>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL((k_pgemm32<EPI, C>), dim3(mt * nt), dim3(C::THREADS), C::LDS, s, a, mt, nt);
+  return hipGetLastError();
+}
+
+template <class C>
+hipError_t pgemm32_epi(int epi, const PGemmArgs &a, hipStream_t s) {
+  switch (epi) {
+    case PEPI_QKV: return pgemm32_go<PEPI_QKV, C>(a, s);
+    case PEPI_RESID: return pgemm32_go<PEPI_RESID, C>(a, s);
+    case PEPI_GELU: return pgemm32_go<PEPI_GELU, C>(a, s);
+    case PEPI_MEM: return pgemm32_go<PEPI_MEM, C>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_pgemm(int dtype, int epi, const PGemmArgs &a, hipStream_t s) {
   if (a.rows.n_rows < 1) return hipSuccess;
-  return dtype == RLT_DTYPE_BF16 ? pgemm_epi<bf16_t>(epi, a, s) : pgemm_epi<float>(epi, a, s);
+  // packed weights have whole 32-row pairs of tiles (Np % 32 == 0)
+  if (a.Np % 32) return hipErrorInvalidValue;
+  return dtype == RLT_DTYPE_BF16 ? pgemm32_epi<Pg32Default>(epi, a, s)
+                                 : pgemm_epi<float, PgDefault>(epi, a, s);
 }
 
 template <typename T, int DH>
