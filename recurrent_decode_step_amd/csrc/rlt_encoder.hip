@@ -17,8 +17,9 @@
 //                in fragment order (k_pgemm: the fp32 form on 16x16x4),
 //                fused epilogues (q + encoder-cache append, residual add,
 //                GELU, memory K/V append)
-//   k_fattn      causal flash attention over the encoder cache: 64 queries of
-//                one (sequence, head) per workgroup, MFMA for Q K^T and P V
+//   k_fattn32    causal flash attention over the encoder cache (bf16): 128
+//                queries of one (sequence, head) per workgroup, 32x32x16 MFMA
+//                for Q K^T and P V (k_fattn: the fp32 form, 64 queries, 16x16x4)
 #include "rlt_device.h"
 
 #include <algorithm>
@@ -680,6 +681,186 @@ __global__ __launch_bounds__(256, 2) void k_fattn(FAttnArgs a, int qblocks, int 
   }
 }
 
+// bf16 form on the 32x32x16 MFMA: 32 queries per wavefront, 128 per
+// workgroup, KV tiles of 64 positions.  S^T = K Q^T gives lane l query l % 32
+// and, in register r of position block pb, position pb*32 + 8 (r/4) + 4 (l/32)
+// + r % 4; P V takes its P^T fragment of k-step kk straight from registers
+// 8 (kk % 2) .. +7 of block kk / 2, and V^T reads the same positions from the
+// transposed tile.  A wavefront skips the products of tiles that lie wholly
+// after its last query (it still helps stage them).
+template <int DH>
+__global__ __launch_bounds__(256, 2) void k_fattn32(FAttnArgs a, int qblocks, int n_seq) {
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  constexpr int KVT = 64;                  // positions per tile
+  constexpr int KS = DH / 16;              // k-steps of Q K^T
+  constexpr int CB = DH / 32;              // 32-channel blocks of O^T
+  constexpr int VROW = KVT + 4;            // padded row of V^T (bf16)
+  constexpr int NF = 2 * KS;               // K fragments per tile
+  constexpr int KPT = NF / 4;              // per wavefront
+  constexpr int NVT = (KVT / 2) * (DH / 8);// V staging tasks (2 positions x 8 channels)
+  constexpr int VPT = (NVT + 255) / 256;
+  static_assert(NF % 4 == 0, "head size");
+  __shared__ u32x4 sK[NF * 64];
+  __shared__ bf16_t sVt[DH * VROW];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.x % a.H;
+  const int rest = blockIdx.x / a.H;
+  const int i = rest % n_seq;
+  const int qb = qblocks - 1 - rest / n_seq;
+  const int Tn = a.rows.T;
+  const int slot = a.rows.slots[i], p0 = a.rows.p0[i];
+  const int j0 = qb * 128;
+  const int jlast = min(j0 + 127, Tn - 1);
+  const int kv_end = p0 + jlast + 1;
+  const int ntile = (kv_end + KVT - 1) / KVT;
+  const int jraw = j0 + wave * 32 + (lane & 31);
+  const int jq = min(jraw, Tn - 1);
+  const int qpos = p0 + jq;
+  const int wave_last = p0 + min(j0 + wave * 32 + 31, Tn - 1);   // last query position of the wavefront
+  const int rq = i * Tn + jq;
+  const int hh = lane >> 5;
+  const bf16_t *kbase = static_cast<const bf16_t *>(a.kb) + (size_t)slot * a.s_seq + (size_t)h * a.s_head;
+  const bf16_t *vbase = static_cast<const bf16_t *>(a.vb) + (size_t)slot * a.s_seq + (size_t)h * a.s_head;
+
+  u32x4 qf[KS];
+  const bf16_t *qrow = static_cast<const bf16_t *>(a.q) + (size_t)rq * a.ldq + h * DH + hh * 8;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const u32x4 *>(qrow + ks * 16);
+
+  u32x4 kr[KPT], vr[VPT][2];
+  auto load = [&](int tile) {
+    const int pbase = tile * KVT;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int f = u * 4 + wave;
+      const int pb = f / KS, ks = f - (f / KS) * KS;
+      const int p = min(pbase + pb * 32 + (lane & 31), kv_end - 1);
+      kr[u] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)p * a.s_pos + ks * 16 + hh * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int t = u * 256 + (int)threadIdx.x;
+      if (NVT % 256 == 0 || t < NVT) {
+        const int q = t % (KVT / 2), ch = t / (KVT / 2);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int p = min(pbase + q * 2 + e, kv_end - 1);
+          vr[u][e] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)p * a.s_pos + ch * 8);
+        }
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) sK[(u * 4 + wave) * 64 + lane] = kr[u];
+    uint32_t *vt = reinterpret_cast<uint32_t *>(sVt);
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int t = u * 256 + (int)threadIdx.x;
+      if (NVT % 256 == 0 || t < NVT) {
+        const int q = t % (KVT / 2), ch = t / (KVT / 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = vr[u][0][e], hi = vr[u][1][e];
+          const int c = ch * 8 + 2 * e;
+          vt[(c * VROW + 2 * q) >> 1] = (lo & 0xffffu) | (hi << 16);
+          vt[((c + 1) * VROW + 2 * q) >> 1] = (lo >> 16) | (hi & 0xffff0000u);
+        }
+      }
+    }
+  };
+
+  f32x16 o[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
+
+  load(0);
+  store();
+  __syncthreads();
+  for (int tile = 0; tile < ntile; ++tile) {
+    if (tile + 1 < ntile) load(tile + 1);
+    if (tile * KVT <= wave_last) {                 // uniform over the wavefront
+      f32x16 s[2];
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[pb][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          s[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, sK[(pb * KS + ks) * 64 + lane]),
+              __builtin_bit_cast(bf16x8, qf[ks]), s[pb], 0, 0, 0);
+      }
+      const int pos0 = tile * KVT + 4 * hh;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int p = pos0 + pb * 32 + 8 * (r >> 2) + (r & 3);
+          const float sv = p <= qpos ? s[pb][r] * a.scale_log2 : -INFINITY;
+          s[pb][r] = sv;
+          mx = fmaxf(mx, sv);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float alpha = exp2f(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = exp2f(s[pb][r] - mn);
+          s[pb][r] = pv;
+          lsum += pv;
+        }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int pb = kk >> 1, r0 = 8 * (kk & 1);
+        const u32x4 pf = u32x4{f2bf(s[pb][r0]) | (f2bf(s[pb][r0 + 1]) << 16),
+                               f2bf(s[pb][r0 + 2]) | (f2bf(s[pb][r0 + 3]) << 16),
+                               f2bf(s[pb][r0 + 4]) | (f2bf(s[pb][r0 + 5]) << 16),
+                               f2bf(s[pb][r0 + 6]) | (f2bf(s[pb][r0 + 7]) << 16)};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const bf16_t *vp = sVt + (cb * 32 + (lane & 31)) * VROW + kk * 16 + 4 * hh;
+          const u32x2 lo = *reinterpret_cast<const u32x2 *>(vp);
+          const u32x2 hi = *reinterpret_cast<const u32x2 *>(vp + 8);
+          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}),
+              __builtin_bit_cast(bf16x8, pf), o[cb], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+    if (tile + 1 < ntile) {
+      store();
+      __syncthreads();
+    }
+  }
+
+  lsum += __shfl_xor(lsum, 32);
+  if (jraw < Tn) {
+    const float inv = 1.0f / lsum;
+    bf16_t *orow = static_cast<bf16_t *>(a.out) + (size_t)rq * a.ldo + h * DH + 4 * hh;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float y[4] = {o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv, o[cb][4 * q + 2] * inv,
+                            o[cb][4 * q + 3] * inv};
+        Num<bf16_t>::store4(orow + cb * 32 + 8 * q, y);
+      }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_enc_embed(int dtype, const int32_t *tokens, int n_rows, const void *emb, int V,
                             int d, float *x, hipStream_t s) {
@@ -774,14 +955,22 @@ hipError_t fattn_go(const FAttnArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DH>
+hipError_t fattn32_go(const FAttnArgs &a, hipStream_t s) {
+  const int qblocks = (a.rows.T + 127) / 128;
+  const int n_seq = a.rows.n_rows / a.rows.T;
+  hipLaunchKernelGGL((k_fattn32<DH>), dim3(n_seq * qblocks * a.H), dim3(256), 0, s, a, qblocks, n_seq);
+  return hipGetLastError();
+}
+
 hipError_t launch_fattn(int dtype, int dh, const FAttnArgs &a, hipStream_t s) {
   if (a.rows.n_rows < 1) return hipSuccess;
   if (dtype == RLT_DTYPE_BF16) {
     switch (dh) {
-      case 32: return fattn_go<bf16_t, 32>(a, s);
-      case 64: return fattn_go<bf16_t, 64>(a, s);
-      case 128: return fattn_go<bf16_t, 128>(a, s);
-      case 256: return fattn_go<bf16_t, 256>(a, s);
+      case 32: return fattn32_go<32>(a, s);
+      case 64: return fattn32_go<64>(a, s);
+      case 128: return fattn32_go<128>(a, s);
+      case 256: return fattn_go<bf16_t, 256>(a, s);   // the 32x32 form would spill at dh 256
     }
   } else {
     switch (dh) {

@@ -133,8 +133,8 @@ def test_encode_chunks_and_batches_are_bitwise_invariant():
 
 
 def test_encode_bf16_matches_oracle():
-    """bf16 storage (the bf16-emulating oracle): dh = 128 and dh = 64, two groups."""
-    for d, H, G in ((256, 2, 1), (256, 4, 2)):
+    """bf16 storage (the bf16-emulating oracle): dh = 128, 64 and 256, two groups."""
+    for d, H, G in ((256, 2, 1), (256, 4, 2), (512, 2, 1)):
         cfg = ModelConfig(vocab=500, d_model=d, n_heads=H, n_layers=2, d_ffn=512, window=8,
                           mem_groups=G, dtype=1)
         B, T = 2, 130
