@@ -45,14 +45,19 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
-KERNEL_SOURCE = os.path.join(ROOT, "recurrent_decode_step_amd", "csrc", "rlt_kernels.hip")
+KERNEL_SOURCE = (os.path.join(ROOT, "recurrent_decode_step_amd", "csrc", "rlt_kernels.hip"),
+                 os.path.join(ROOT, "recurrent_decode_step_amd", "csrc", "rlt_device.h"))
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_attn_cross_refdepth_b32_counters.md")
 
 
-def source_sha256(path=KERNEL_SOURCE):
+def source_sha256(paths=KERNEL_SOURCE):
+    """sha256 over the decoder kernel sources (the kernels and their device helpers)."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(algorithmic_per_launch, path=COUNTERS_FILE):
