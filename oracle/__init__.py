@@ -10,10 +10,11 @@ from .rlt_oracle import (Model, SeqState, round_bf16, initial_state, state_from_
                          sampling_weights, sample_token, generate)
 from .brute import brute_force_run
 from .encoder import Encoder, encode, prefill
+from . import bptt
 from .parallel import parallel_swa_pass
 
 __all__ = ["Model", "SeqState", "round_bf16", "initial_state", "state_from_arrays",
            "copy_state", "decoder_step", "run_sequence", "token_log_prob", "score_sequence",
            "sampling_weights", "sample_token", "generate",
-           "brute_force_run", "Encoder", "encode", "prefill",
+           "brute_force_run", "Encoder", "encode", "prefill", "bptt",
            "parallel_swa_pass"]
