@@ -375,6 +375,47 @@ rlt_status rlt_state_export(const rlt_model *m, const rlt_state *st, int32_t n,
 rlt_status rlt_state_import(const rlt_model *m, rlt_state *st, int32_t n,
                             const int32_t *host_slots, const void *dev_snap, void *stream);
 
+/* ------------------------------------------------------------- training */
+/* Backpropagation through time [Article, "Training Methodology"; Tutorial,
+ * "Pretraining and supervised fine-tuning"; Forget, its note on truncated
+ * BPTT].  B sequences run from H_0 over T steps (the step of this header, fp32,
+ * on the canonical parameters: the decode path's packed model is not used),
+ * with the loss
+ *   loss = sum over b, t with dev_targets[b][t] >= 0 of -log softmax(logits_{b,t})[dev_targets[b][t]]
+ * (a target < 0 removes the loss term only: the step still updates the state,
+ * and gradients from later losses flow through it; a target >= vocab makes the
+ * loss NaN), then the exact gradient of that loss w.r.t. every parameter, the
+ * e rows and the memory.  Gradients flow through s_t and through every window
+ * cache entry to each later step that reads it (the cross terms of the
+ * state-to-state Jacobian).  Truncation names what it cuts: with opts->chunk = k
+ * > 0, at each boundary between steps k*j and k*j + 1 the parts of H listed in
+ * opts->detach are detached, RLT_DETACH_S (s) and/or RLT_DETACH_KV (every cache
+ * entry carried across the boundary); the forward values never change.
+ * opts NULL or chunk 0 = full BPTT. */
+enum { RLT_DETACH_S = 1, RLT_DETACH_KV = 2 };
+typedef struct {
+  int32_t chunk;                /* truncation length in steps; 0 = none */
+  int32_t detach;               /* RLT_DETACH_* bits cut at each chunk boundary */
+} rlt_bptt_opts;
+
+/* Workspace bytes for rlt_bptt (every intermediate of the T steps is kept:
+ * about (22 d + 3 F) * L + 7 d + V floats per sequence and step); 0 if the
+ * config is invalid, not fp32, or T exceeds 4096. */
+size_t rlt_bptt_workspace_bytes(const rlt_config *cfg, int32_t batch, int32_t T);
+
+/* params: fp32 canonical device tensors as for rlt_model_create (read only).
+ * grads:  buffers of the same shapes, OVERWRITTEN with d loss / d param.
+ * dev_e [B][T][d] fp32; mem: fp32 memory, sequence index = b, capacity >= T.
+ * dev_de [B][T][d] (written) or NULL; dmem: memory gradients with mem's
+ * strides (ACCUMULATED into: zero them first) or NULL; dev_loss [1] (written).
+ * dev_workspace: >= rlt_bptt_workspace_bytes, 256-byte aligned, caller owned.
+ * RLT_ERR_UNSUPPORTED for a bf16 config. */
+rlt_status rlt_bptt(const rlt_config *cfg, const rlt_params *params, int32_t batch, int32_t T,
+                    const float *dev_e, const rlt_memory *mem, const int32_t *dev_targets,
+                    const rlt_bptt_opts *opts, const rlt_params *grads, float *dev_de,
+                    const rlt_memory *dmem, float *dev_loss, void *dev_workspace,
+                    size_t workspace_bytes, void *stream);
+
 /* ------------------------------------------------------------- profiling */
 /* Kernel classes for per-class timing: RLT_K_EXTRA = the replay-scoring,
  * sampling and stand-in encoder kernels; GEMM = every projection and the head;

@@ -22,6 +22,7 @@ RLT_OK, RLT_ERR_INVALID_ARG, RLT_ERR_SHAPE, RLT_ERR_RANGE, RLT_ERR_STALE, \
 RLT_LOGITS_ALL, RLT_LOGITS_LAST, RLT_LOGITS_NONE = 0, 1, 2
 RLT_K_EXTRA, RLT_K_GEMM, RLT_K_SWA, RLT_K_CROSS = 0, 1, 2, 3
 RLT_E_GEMM, RLT_E_ATTN, RLT_E_OTHER = 0, 1, 2
+RLT_DETACH_S, RLT_DETACH_KV = 1, 2
 
 EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_bytes",
             "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",
@@ -32,7 +33,8 @@ EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_by
             "rlt_encoder_bytes", "rlt_encoder_create", "rlt_encoder_destroy",
             "rlt_encoder_state_bytes", "rlt_encoder_state_init", "rlt_encoder_state_destroy",
             "rlt_encoder_state_reset", "rlt_encoder_position", "rlt_encode",
-            "rlt_encoder_profile_begin", "rlt_encoder_profile_collect")
+            "rlt_encoder_profile_begin", "rlt_encoder_profile_collect",
+            "rlt_bptt_workspace_bytes", "rlt_bptt")
 
 
 class RLTError(RuntimeError):
@@ -65,6 +67,10 @@ class rlt_encoder_table(C.Structure):
 
 class rlt_sampling(C.Structure):
     _fields_ = [("temperature", C.c_float), ("top_k", C.c_int32)]
+
+
+class rlt_bptt_opts(C.Structure):
+    _fields_ = [("chunk", C.c_int32), ("detach", C.c_int32)]
 
 
 class rlt_encoder_params(C.Structure):
@@ -119,6 +125,9 @@ def load_library(path: str = LIB_PATH):
         "rlt_encoder_profile_begin": (i32, [vp, i32, i32]),
         "rlt_encoder_profile_collect": (i32, [vp, i32, P(C.c_double), P(i32), P(C.c_double),
                                               P(C.c_double)]),
+        "rlt_bptt_workspace_bytes": (sz, [P(rlt_config), i32, i32]),
+        "rlt_bptt": (i32, [P(rlt_config), P(rlt_params), i32, i32, vp, P(rlt_memory), vp,
+                           P(rlt_bptt_opts), P(rlt_params), vp, P(rlt_memory), vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -488,3 +497,47 @@ def encoder_profile_collect(es: EncoderState, kclass: int):
     _check(load_library().rlt_encoder_profile_collect(es.handle, kclass, C.byref(tot), C.byref(n),
                                                       C.byref(fl), C.byref(b)))
     return tot.value, n.value, fl.value, b.value
+
+
+# ---------------------------------------------------------------- training
+PARAM_NAMES = tuple(n for n, _ in rlt_params._fields_)
+
+
+def rlt_bptt(cfg: ModelConfig, params: dict, e: torch.Tensor, memory, targets: torch.Tensor,
+             chunk: int = 0, detach: int = 0, want_de: bool = True, want_dmem: bool = True,
+             workspace=None, stream=None):
+    """Backpropagation through time over e [B][T][d] (fp32 model): returns
+    (loss tensor [1], {name: gradient}, de [B][T][d] or None, (dmk, dmv) or None).
+    params: canonical fp32 tensors; memory: (K, V) [G][B][H][cap][dh] fp32."""
+    lib = load_library()
+    if cfg.dtype != DTYPE_FP32:
+        _check(RLT_ERR_UNSUPPORTED)
+    ccfg = make_config(cfg)
+    B, T = e.shape[0], e.shape[1]
+    dev = e.device
+    e = e.to(torch.float32).contiguous()
+    tg = targets.to(device=dev, dtype=torch.int32).contiguous()
+    P = {k: params[k].to(device=dev, dtype=torch.float32).contiguous() for k in PARAM_NAMES}
+    grads = {k: torch.empty_like(P[k]) for k in PARAM_NAMES}
+    cp = rlt_params(*[P[k].data_ptr() for k in PARAM_NAMES])
+    cg = rlt_params(*[grads[k].data_ptr() for k in PARAM_NAMES])
+    mk, mv = memory
+    mem = memory_view(mk, mv)
+    dmem = None
+    dm = None
+    if want_dmem:
+        dm = (torch.zeros_like(mk), torch.zeros_like(mv))
+        dmem = memory_view(*dm)
+    de = torch.empty_like(e) if want_de else None
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    nbytes = lib.rlt_bptt_workspace_bytes(C.byref(ccfg), B, T)
+    if nbytes == 0:
+        _check(RLT_ERR_INVALID_ARG)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    opts = rlt_bptt_opts(int(chunk), int(detach))
+    _check(lib.rlt_bptt(C.byref(ccfg), C.byref(cp), B, T, e.data_ptr(), C.byref(mem), tg.data_ptr(),
+                        C.byref(opts), C.byref(cg), de.data_ptr() if de is not None else None,
+                        C.byref(dmem) if dmem is not None else None, loss.data_ptr(),
+                        workspace.data_ptr(), nbytes, _stream(stream)))
+    return loss, grads, de, dm

@@ -10,7 +10,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/rlt_api.hip", "csrc/rlt_kernels.hip", "csrc/rlt_encoder.hip"]
+SOURCES = ["csrc/rlt_api.hip", "csrc/rlt_kernels.hip", "csrc/rlt_encoder.hip", "csrc/rlt_train.hip"]
 OUT = os.path.join(HERE, "librlt.so")
 
 FLAGS = [

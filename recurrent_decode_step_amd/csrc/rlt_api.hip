@@ -273,24 +273,28 @@ rlt_status check_slots(const rlt_state *st, int n, const int32_t *slots) {
   return RLT_OK;
 }
 
-rlt_status check_memory(const rlt_model *m, const rlt_memory *mem, int max_slot) {
+rlt_status check_memory_cfg(const rlt_config &c, const rlt_memory *mem, int max_slot) {
   if (!mem || !mem->k || !mem->v) return fail(RLT_ERR_INVALID_ARG, "memory K/V pointer is NULL");
   if (mem->capacity < 1) return fail(RLT_ERR_INVALID_ARG, "memory capacity < 1");
-  if (mem->n_groups < m->cfg.mem_groups)
+  if (mem->n_groups < c.mem_groups)
     return fail(RLT_ERR_INVALID_ARG, "memory holds %d groups, model reads %d", mem->n_groups,
-                m->cfg.mem_groups);
+                c.mem_groups);
   if (mem->n_seq <= max_slot)
     return fail(RLT_ERR_INVALID_ARG, "memory holds %d sequences, slot %d used", mem->n_seq, max_slot);
-  if (mem->stride_pos < m->cfg.head_dim || mem->stride_head < 0 || mem->stride_seq < 0 ||
+  if (mem->stride_pos < c.head_dim || mem->stride_head < 0 || mem->stride_seq < 0 ||
       mem->stride_group < 0)
     return fail(RLT_ERR_INVALID_ARG, "bad memory strides");
-  const int es = esize_of(m->cfg.dtype);
+  const int es = esize_of(c.dtype);
   const int64_t strides[4] = {mem->stride_group, mem->stride_seq, mem->stride_head, mem->stride_pos};
   for (int64_t s : strides)
     if ((s * es) % 16) return fail(RLT_ERR_SHAPE, "memory strides must be multiples of 16 bytes");
   if (((uintptr_t)mem->k | (uintptr_t)mem->v) % 16)
     return fail(RLT_ERR_SHAPE, "memory pointers must be 16-byte aligned");
   return RLT_OK;
+}
+
+rlt_status check_memory(const rlt_model *m, const rlt_memory *mem, int max_slot) {
+  return check_memory_cfg(m->cfg, mem, max_slot);
 }
 
 // Stage a slot list in device memory (only when it differs from the staged one).
@@ -1448,6 +1452,87 @@ rlt_status rlt_encoder_profile_collect(rlt_encoder_state *es, int32_t kclass, do
   if (!es) return fail(RLT_ERR_INVALID_ARG, "encoder state is NULL");
   if (kclass < 0 || kclass >= RLT_E_NCLASSES) return fail(RLT_ERR_INVALID_ARG, "bad kernel class");
   return prof_collect(es->plog, kclass, total_ms, launches, bytes_moved, flops);
+}
+
+}  // extern "C"
+
+// ================================================================== training
+extern "C" {
+
+size_t rlt_bptt_workspace_bytes(const rlt_config *cfg, int32_t batch, int32_t T) {
+  if (check_config(cfg) != RLT_OK || cfg->dtype != RLT_DTYPE_F32 || batch < 1 || T < 1 ||
+      T > kTrainMaxPos)
+    return 0;
+  return train_workspace_bytes(*cfg, batch, T);
+}
+
+rlt_status rlt_bptt(const rlt_config *cfg, const rlt_params *params, int32_t batch, int32_t T,
+                    const float *dev_e, const rlt_memory *mem, const int32_t *dev_targets,
+                    const rlt_bptt_opts *opts, const rlt_params *grads, float *dev_de,
+                    const rlt_memory *dmem, float *dev_loss, void *dev_workspace,
+                    size_t workspace_bytes, void *stream) {
+  rlt_status rs;
+  if ((rs = check_config(cfg)) != RLT_OK) return rs;
+  if (cfg->dtype != RLT_DTYPE_F32)
+    return fail(RLT_ERR_UNSUPPORTED, "backpropagation through time is implemented for fp32 models");
+  if (!params || !grads) return fail(RLT_ERR_INVALID_ARG, "params or grads is NULL");
+  const void *need[] = {params->s_star, params->wg, params->bg, params->g1, params->g2, params->g3,
+                        params->wq, params->wk, params->wv, params->wo, params->wqc, params->woc,
+                        params->w1, params->w2, params->go, params->wout,
+                        grads->s_star, grads->wg, grads->bg, grads->g1, grads->g2, grads->g3,
+                        grads->wq, grads->wk, grads->wv, grads->wo, grads->wqc, grads->woc,
+                        grads->w1, grads->w2, grads->go, grads->wout};
+  for (const void *p : need)
+    if (!p) return fail(RLT_ERR_INVALID_ARG, "a parameter or gradient pointer is NULL");
+  if (batch < 1 || T < 1) return fail(RLT_ERR_INVALID_ARG, "batch and T must be >= 1");
+  if (T > kTrainMaxPos)
+    return fail(RLT_ERR_UNSUPPORTED, "T = %d > %d positions per attention row", T, kTrainMaxPos);
+  if (!dev_e || !dev_targets || !dev_loss) return fail(RLT_ERR_INVALID_ARG, "e, targets or loss is NULL");
+  if ((rs = check_memory_cfg(*cfg, mem, batch - 1)) != RLT_OK) return rs;
+  if (mem->capacity < T)
+    return fail(RLT_ERR_RANGE, "memory capacity %d < T = %d", mem->capacity, T);
+  if (dmem) {
+    if (!dmem->k || !dmem->v) return fail(RLT_ERR_INVALID_ARG, "memory gradient pointer is NULL");
+    if (dmem->stride_group != mem->stride_group || dmem->stride_seq != mem->stride_seq ||
+        dmem->stride_head != mem->stride_head || dmem->stride_pos != mem->stride_pos)
+      return fail(RLT_ERR_SHAPE, "memory gradients must have the memory's strides");
+  }
+  int chunk = 0, detach = 0;
+  if (opts) {
+    chunk = opts->chunk;
+    detach = opts->detach;
+  }
+  if (chunk < 0) return fail(RLT_ERR_INVALID_ARG, "chunk must be >= 0");
+  if (detach & ~(RLT_DETACH_S | RLT_DETACH_KV)) return fail(RLT_ERR_INVALID_ARG, "unknown detach bits");
+  const size_t need_ws = rlt_bptt_workspace_bytes(cfg, batch, T);
+  if (!dev_workspace) return fail(RLT_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)dev_workspace % 256) return fail(RLT_ERR_SHAPE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need_ws)
+    return fail(RLT_ERR_SHAPE, "workspace %zu bytes < %zu required", workspace_bytes, need_ws);
+  if ((rs = device_health()) != RLT_OK) return rs;
+  TrainArgs a{};
+  a.c = *cfg;
+  a.p = params;
+  a.gr = grads;
+  a.B = batch;
+  a.T = T;
+  a.e = dev_e;
+  a.mk = static_cast<const float *>(mem->k);
+  a.mv = static_cast<const float *>(mem->v);
+  a.m_group = mem->stride_group;
+  a.m_seq = mem->stride_seq;
+  a.m_head = mem->stride_head;
+  a.m_pos = mem->stride_pos;
+  a.dmk = dmem ? static_cast<float *>(const_cast<void *>(dmem->k)) : nullptr;
+  a.dmv = dmem ? static_cast<float *>(const_cast<void *>(dmem->v)) : nullptr;
+  a.tg = dev_targets;
+  a.chunk = chunk;
+  a.detach = detach;
+  a.de = dev_de;
+  a.loss = dev_loss;
+  const hipError_t e = launch_bptt(a, dev_workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bptt");
+  return ok();
 }
 
 }  // extern "C"

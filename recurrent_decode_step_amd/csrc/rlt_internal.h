@@ -175,4 +175,25 @@ hipError_t launch_enc_norm(int dtype, const float *x, int64_t ldx, const float *
 hipError_t launch_pgemm(int dtype, int epi, const PGemmArgs &a, hipStream_t s);
 hipError_t launch_fattn(int dtype, int dh, const FAttnArgs &a, hipStream_t s);
 
+// ---------------------------------------------------------------- training
+// Backpropagation through time, fp32 (rlt_train.hip).  Positions one row may
+// attend are limited to kTrainMaxPos (LDS score buffer of the attention kernels).
+constexpr int kTrainMaxPos = 4096;
+struct TrainArgs {
+  rlt_config c;
+  const rlt_params *p;       // canonical fp32 parameters (device)
+  const rlt_params *gr;      // gradient buffers, same shapes (device, overwritten)
+  int B, T;
+  const float *e;            // [B][T][d]
+  const float *mk, *mv;      // memory, element strides below
+  int64_t m_group, m_seq, m_head, m_pos;
+  float *dmk, *dmv;          // memory gradients with the same strides (+=), or null
+  const int32_t *tg;         // [B][T] targets
+  int chunk, detach;         // truncation length (0: none) and RLT_DETACH_* bits
+  float *de;                 // [B][T][d] or null
+  float *loss;               // [1]
+};
+size_t train_workspace_bytes(const rlt_config &c, int B, int T);
+hipError_t launch_bptt(const TrainArgs &a, void *ws, hipStream_t s);
+
 }  // namespace rlt

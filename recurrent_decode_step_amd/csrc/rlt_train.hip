@@ -1,0 +1,698 @@
+// Backpropagation through time of the recurrent decoder (fp32), for gfx950.
+//
+// The training path of the Recurrent Looped Transformer: full-sequence
+// next-token prediction with backpropagation through the recurrence, the loss
+// masked per target but never the state update, and truncation that names the
+// detached parts of the state ("Recurrent Looped Transformer: A New
+// Architecture for Infinite Context Reasoning in Language Models", "Training
+// Methodology"; "Understanding and Applying the Recurrent Looped Transformer
+// Architecture", "Pretraining and supervised fine-tuning"; "What If a
+// Transformer Never Had to Forget? Meet the Recurrent Looped Transformer
+// (RLT)", its note on truncated BPTT: the state-to-state Jacobian has cross
+// terms through the decoder key-value cache).
+//
+// It works on the canonical row-major fp32 parameters, not on the decode
+// path's packed weights.  Forward: the decoder step of include/rlt.h for T
+// steps from H_0, every intermediate a backward step needs saved in the
+// workspace ([L][T][B][...] per layer).  Backward: steps in reverse order,
+// layers in reverse order; the keys and values of step t collect their
+// gradient from every later step whose window reads them (the cache cross
+// terms) in per-step gradient rows, complete by the time step t is reached.
+// Weight gradients are formed at the end as one GEMM per matrix over all T*B
+// rows.  Every reduction runs in a fixed order: results do not depend on the
+// launch shape.
+#include "rlt_internal.h"
+
+#include <math.h>
+
+#include <string>
+#include <vector>
+
+namespace rlt {
+namespace {
+
+// ---------------------------------------------------------------- kernels
+// C[m][n] = (ACC ? C[m][n] : 0) + sum_k A(m, k) B(k, n), k in order.
+// A(m, k) = TA ? A[k * lda + m] : A[m * lda + k]; B(k, n) = TB ? B[n * ldb + k] : B[k * ldb + n].
+// 64 x 64 outputs per workgroup, 4 x 4 per thread, K in chunks of 16 through LDS.
+template <bool TA, bool TB, bool ACC>
+__global__ __launch_bounds__(256) void k_t_gemm(const float *__restrict__ A, int64_t lda,
+                                                const float *__restrict__ B, int64_t ldb,
+                                                float *__restrict__ C, int64_t ldc, int M, int N,
+                                                int K) {
+  __shared__ float As[16][64 + 1];
+  __shared__ float Bs[16][64 + 1];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = threadIdx.x + 256 * u;   // 0..1023
+      // A tile: 64 (m) x 16 (k)
+      {
+        int mm, kk;
+        if (TA) { mm = idx & 63; kk = idx >> 6; } else { kk = idx & 15; mm = idx >> 4; }
+        const int m = m0 + mm, k = k0 + kk;
+        float v = 0.f;
+        if (m < M && k < K) v = TA ? A[(size_t)k * lda + m] : A[(size_t)m * lda + k];
+        As[kk][mm] = v;
+      }
+      // B tile: 16 (k) x 64 (n)
+      {
+        int kk, nn;
+        if (TB) { kk = idx & 15; nn = idx >> 4; } else { nn = idx & 63; kk = idx >> 6; }
+        const int k = k0 + kk, n = n0 + nn;
+        float v = 0.f;
+        if (n < N && k < K) v = TB ? B[(size_t)n * ldb + k] : B[(size_t)k * ldb + n];
+        Bs[kk][nn] = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      float *c = C + (size_t)m * ldc + n;
+      *c = ACC ? *c + acc[i][j] : acc[i][j];
+    }
+  }
+}
+
+__device__ __forceinline__ float t_wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ float t_wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// y = x * r * gamma, r = (mean(x^2) + eps)^(-1/2); one wavefront per row.
+__global__ void k_t_norm_fwd(const float *__restrict__ x, const float *__restrict__ gamma, float eps,
+                             float *__restrict__ y, float *__restrict__ r_out, int rows, int d) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float *xr = x + (size_t)row * d;
+  float ss = 0.f;
+  for (int c = lane; c < d; c += 64) ss = fmaf(xr[c], xr[c], ss);
+  ss = t_wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int c = lane; c < d; c += 64) y[(size_t)row * d + c] = xr[c] * r * gamma[c];
+  if (lane == 0) r_out[row] = r;
+}
+
+// dx (+)= r * (gamma * dy - xhat * mean(gamma * dy * xhat)), xhat = x * r.
+__global__ void k_t_norm_bwd(const float *__restrict__ x, const float *__restrict__ r_in,
+                             const float *__restrict__ gamma, const float *__restrict__ dy,
+                             float *__restrict__ dx, int rows, int d, int accumulate) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float r = r_in[row];
+  const float *xr = x + (size_t)row * d;
+  const float *g = dy + (size_t)row * d;
+  float dot = 0.f;
+  for (int c = lane; c < d; c += 64) dot = fmaf(gamma[c] * g[c], xr[c] * r, dot);
+  dot = t_wave_sum(dot) / (float)d;
+  for (int c = lane; c < d; c += 64) {
+    const float v = r * (gamma[c] * g[c] - xr[c] * r * dot);
+    float *o = dx + (size_t)row * d + c;
+    *o = accumulate ? *o + v : v;
+  }
+}
+
+// out[n] += sum_m a[m][n] (* b[m][n]) (* r[m]), m in order; one thread per column.
+__global__ void k_t_colsum(const float *__restrict__ a, const float *__restrict__ b,
+                           const float *__restrict__ r, float *__restrict__ out, int M, int N,
+                           int64_t ld) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.f;
+  for (int m = 0; m < M; ++m) {
+    float v = a[(size_t)m * ld + n];
+    if (b) v *= b[(size_t)m * ld + n];
+    if (r) v *= r[m];
+    s += v;
+  }
+  out[n] += s;
+}
+
+// Attention of query row b, head h over positions lo..hi of its sequence.
+// Forward writes o and the softmax statistics (max m, sum l) of the row.
+struct TAttn {
+  const float *q; int64_t ldq;          // [B][d]
+  const float *kb, *vb;                 // K/V bases
+  int64_t s_seq, s_head, s_pos;         // element strides of K/V (and of their gradients)
+  const int *lo, *hi;                   // per row (device), inclusive
+  float *o; int64_t ldo;                // forward out / backward: o (in)
+  float *m, *l;                         // [B][H]
+  // backward
+  const float *dout;                    // [B][d]
+  float *dq;                            // [B][d] (written)
+  float *dkb, *dvb;                     // gradient bases, same strides as K/V (+=)
+  int cut_lo;                           // positions below get no K/V gradient (detached)
+  int H, dh;
+  float scale;
+};
+
+constexpr int kTMaxPos = kTrainMaxPos;
+
+__global__ __launch_bounds__(64) void k_t_attn_fwd(TAttn a) {
+  __shared__ float sc[kTMaxPos];
+  const int b = blockIdx.x / a.H, h = blockIdx.x % a.H, lane = threadIdx.x;
+  const int lo = a.lo[b], hi = a.hi[b], n = hi - lo + 1;
+  const float *q = a.q + (size_t)b * a.ldq + h * a.dh;
+  const float *K = a.kb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
+  const float *V = a.vb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
+  float mx = -INFINITY;
+  for (int j = lane; j < n; j += 64) {
+    const float *k = K + (size_t)(lo + j) * a.s_pos;
+    float s = 0.f;
+    for (int c = 0; c < a.dh; ++c) s = fmaf(q[c], k[c], s);
+    s *= a.scale;
+    sc[j] = s;
+    mx = fmaxf(mx, s);
+  }
+  mx = t_wave_max(mx);
+  float sum = 0.f;
+  for (int j = lane; j < n; j += 64) {
+    const float p = expf(sc[j] - mx);
+    sc[j] = p;
+    sum += p;
+  }
+  sum = t_wave_sum(sum);
+  __syncthreads();
+  const float inv = 1.0f / sum;
+  for (int c = lane; c < a.dh; c += 64) {
+    float acc = 0.f;
+    for (int j = 0; j < n; ++j) acc = fmaf(sc[j], V[(size_t)(lo + j) * a.s_pos + c], acc);
+    a.o[(size_t)b * a.ldo + h * a.dh + c] = acc * inv;
+  }
+  if (lane == 0) {
+    a.m[b * a.H + h] = mx;
+    a.l[b * a.H + h] = sum;
+  }
+}
+
+// p_j = exp(s_j - m) / l; D = do . o; ds_j = p_j (do . v_j - D);
+// dq = scale sum_j ds_j k_j; dk_j += scale ds_j q; dv_j += p_j do.
+__global__ __launch_bounds__(64) void k_t_attn_bwd(TAttn a) {
+  __shared__ float sp[kTMaxPos];
+  __shared__ float sds[kTMaxPos];
+  const int b = blockIdx.x / a.H, h = blockIdx.x % a.H, lane = threadIdx.x;
+  const int lo = a.lo[b], hi = a.hi[b], n = hi - lo + 1;
+  const float *q = a.q + (size_t)b * a.ldq + h * a.dh;
+  const float *o = a.o + (size_t)b * a.ldo + h * a.dh;
+  const float *dout = a.dout + (size_t)b * a.ldo + h * a.dh;
+  const float *K = a.kb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
+  const float *V = a.vb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
+  const float mx = a.m[b * a.H + h], inv = 1.0f / a.l[b * a.H + h];
+  float D = 0.f;
+  for (int c = lane; c < a.dh; c += 64) D = fmaf(dout[c], o[c], D);
+  D = t_wave_sum(D);
+  for (int j = lane; j < n; j += 64) {
+    const float *k = K + (size_t)(lo + j) * a.s_pos;
+    const float *v = V + (size_t)(lo + j) * a.s_pos;
+    float s = 0.f, dp = 0.f;
+    for (int c = 0; c < a.dh; ++c) {
+      s = fmaf(q[c], k[c], s);
+      dp = fmaf(dout[c], v[c], dp);
+    }
+    const float p = expf(s * a.scale - mx) * inv;
+    sp[j] = p;
+    sds[j] = p * (dp - D);
+  }
+  __syncthreads();
+  for (int c = lane; c < a.dh; c += 64) {
+    float acc = 0.f;
+    for (int j = 0; j < n; ++j) acc = fmaf(sds[j], K[(size_t)(lo + j) * a.s_pos + c], acc);
+    a.dq[(size_t)b * a.ldq + h * a.dh + c] = acc * a.scale;
+  }
+  if (a.dkb) {
+    float *dK = a.dkb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
+    float *dV = a.dvb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
+    const int j0 = max(0, a.cut_lo - lo);
+    for (int j = j0; j < n; ++j) {
+      const float ds = sds[j] * a.scale, p = sp[j];
+      for (int c = lane; c < a.dh; c += 64) {
+        dK[(size_t)(lo + j) * a.s_pos + c] += ds * q[c];
+        dV[(size_t)(lo + j) * a.s_pos + c] += p * dout[c];
+      }
+    }
+  }
+}
+
+// Gate: z = W_g [e ; s] + b_g (z already holds the product), g = sigmoid(z),
+// u = g e + (1 - g) s.  es = [e ; s] rows [B][2d].
+__global__ void k_t_merge_fwd(const float *__restrict__ es, float *__restrict__ z,
+                              const float *__restrict__ bg, float *__restrict__ u, int B, int d) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * d) return;
+  const int b = i / d, c = i - b * d;
+  const float zz = z[i] + bg[c];
+  const float g = 1.0f / (1.0f + expf(-zz));
+  z[i] = g;                                   // keeps g for the backward
+  const float e = es[(size_t)b * 2 * d + c], s = es[(size_t)b * 2 * d + d + c];
+  u[i] = g * e + (1.0f - g) * s;
+}
+
+// du -> de = g du (written to des[:, :d]), ds = (1 - g) du (des[:, d:]),
+// dz = du (e - s) g (1 - g).
+__global__ void k_t_merge_bwd(const float *__restrict__ es, const float *__restrict__ g_in,
+                              const float *__restrict__ du, float *__restrict__ dz,
+                              float *__restrict__ des, int B, int d) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * d) return;
+  const int b = i / d, c = i - b * d;
+  const float g = g_in[i], e = es[(size_t)b * 2 * d + c], s = es[(size_t)b * 2 * d + d + c];
+  const float dd = du[i];
+  des[(size_t)b * 2 * d + c] = g * dd;
+  des[(size_t)b * 2 * d + d + c] = (1.0f - g) * dd;
+  dz[i] = dd * (e - s) * g * (1.0f - g);
+}
+
+__device__ __forceinline__ float t_gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float t_gelu_d(float x) {
+  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.3989422804014327f * expf(-0.5f * x * x);
+}
+
+__global__ void k_t_gelu_fwd(const float *__restrict__ pre, float *__restrict__ h, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) h[i] = t_gelu(pre[i]);
+}
+__global__ void k_t_gelu_bwd(const float *__restrict__ pre, float *__restrict__ dh, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dh[i] *= t_gelu_d(pre[i]);
+}
+
+// strided 2-D copy: dst[r][c] = src[r][c] for c < cols
+__global__ void k_t_copy2d(const float *src, int64_t lds, float *dst, int64_t ldd, int rows, int cols) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)rows * cols) return;
+  const int r = (int)(i / cols), c = (int)(i % cols);
+  dst[(size_t)r * ldd + c] = src[(size_t)r * lds + c];
+}
+
+// Loss and dlogits of one step, one wavefront per row:
+// loss_row = logsumexp(z) - z[y]; dz = softmax(z) - onehot(y); y < 0: 0 and 0.
+__global__ void k_t_ce(const float *__restrict__ logits, const int32_t *__restrict__ tg,
+                       int64_t ld_tg, float *__restrict__ dlogits, float *__restrict__ loss_row,
+                       int rows, int V) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float *z = logits + (size_t)row * V;
+  float *dz = dlogits + (size_t)row * V;
+  const int y = tg[(size_t)row * ld_tg];
+  if (y < 0 || y >= V) {
+    for (int c = lane; c < V; c += 64) dz[c] = 0.f;
+    if (lane == 0) loss_row[row] = (y < 0) ? 0.f : __builtin_nanf("");
+    return;
+  }
+  float mx = -INFINITY;
+  for (int c = lane; c < V; c += 64) mx = fmaxf(mx, z[c]);
+  mx = t_wave_max(mx);
+  float s = 0.f;
+  for (int c = lane; c < V; c += 64) s += expf(z[c] - mx);
+  s = t_wave_sum(s);
+  const float inv = 1.0f / s;
+  for (int c = lane; c < V; c += 64) dz[c] = expf(z[c] - mx) * inv - (c == y ? 1.0f : 0.0f);
+  if (lane == 0) loss_row[row] = logf(s) + mx - z[y];
+}
+
+// total = sum of n values in order (one thread)
+__global__ void k_t_sum(const float *v, size_t n, float *out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  float s = 0.f;
+  for (size_t i = 0; i < n; ++i) s += v[i];
+  *out = s;
+}
+
+__global__ void k_t_fill(float *p, size_t n, float v) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// per-row attention ranges of step t: window lo = max(0, t - W + 1), memory lo = 0; hi = t
+__global__ void k_t_ranges(int *lo_w, int *lo_m, int *hi, int B, int t, int W) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  lo_w[b] = max(0, t - W + 1);
+  lo_m[b] = 0;
+  hi[b] = t;
+}
+
+// ---------------------------------------------------------------- host helpers
+unsigned blocks_for(size_t n, unsigned per = 256) { return (unsigned)((n + per - 1) / per); }
+
+template <bool TA, bool TB, bool ACC>
+void t_gemm_go(const float *A, int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
+               int M, int N, int K, hipStream_t s) {
+  if (M <= 0 || N <= 0) return;
+  if (K <= 0) {
+    if (!ACC) {
+      for (int m = 0; m < M; ++m)
+        hipLaunchKernelGGL(k_t_fill, dim3(blocks_for(N)), dim3(256), 0, s, C + (size_t)m * ldc,
+                           (size_t)N, 0.f);
+    }
+    return;
+  }
+  hipLaunchKernelGGL((k_t_gemm<TA, TB, ACC>), dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s,
+                     A, lda, B, ldb, C, ldc, M, N, K);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- driver
+namespace {
+// Workspace arrays (fp32 unless noted), carved in this order.
+struct TrainWs {
+  // per layer [L][T][B][.]
+  float *xin, *r1, *a, *q, *kh, *vh, *m1, *l1, *o, *x1, *r2, *c, *qc, *m2, *l2, *oc, *x2, *r3, *f,
+      *hpre, *h;
+  float *dq, *dkh, *dvh, *dxo, *dqc, *dxoc, *dhp, *dxf, *da, *dc, *df;
+  // per step [T][B][.]
+  float *es, *g, *s, *ro, *sn, *dl, *lossr, *dz, *dsn;
+  // scratch [B][.]
+  float *u, *logits, *dx, *dx2, *dtmp, *dh, *des, *dscarry, *dsd;
+  int *lo_w, *lo_m, *hi;
+};
+
+size_t train_layout(const rlt_config &c, int B, int T, TrainWs *w, void *base) {
+  const size_t L = c.n_layers, d = c.d_model, F = c.d_ffn, H = c.n_heads, V = c.vocab;
+  const size_t TB = (size_t)T * B;
+  size_t off = 0;
+  char *p = static_cast<char *>(base);
+  auto take = [&](size_t elems) -> float * {
+    off = (off + 255) & ~(size_t)255;
+    float *r = base ? reinterpret_cast<float *>(p + off) : nullptr;
+    off += elems * 4;
+    return r;
+  };
+  const size_t LTB = L * TB;
+  w->xin = take(LTB * d); w->r1 = take(LTB); w->a = take(LTB * d); w->q = take(LTB * d);
+  w->kh = take(LTB * d); w->vh = take(LTB * d); w->m1 = take(LTB * H); w->l1 = take(LTB * H);
+  w->o = take(LTB * d); w->x1 = take(LTB * d); w->r2 = take(LTB); w->c = take(LTB * d);
+  w->qc = take(LTB * d); w->m2 = take(LTB * H); w->l2 = take(LTB * H); w->oc = take(LTB * d);
+  w->x2 = take(LTB * d); w->r3 = take(LTB); w->f = take(LTB * d); w->hpre = take(LTB * F);
+  w->h = take(LTB * F);
+  w->dq = take(LTB * d); w->dkh = take(LTB * d); w->dvh = take(LTB * d); w->dxo = take(LTB * d);
+  w->dqc = take(LTB * d); w->dxoc = take(LTB * d); w->dhp = take(LTB * F); w->dxf = take(LTB * d);
+  w->da = take(LTB * d); w->dc = take(LTB * d); w->df = take(LTB * d);
+  w->es = take(TB * 2 * d); w->g = take(TB * d); w->s = take(TB * d); w->ro = take(TB);
+  w->sn = take(TB * d); w->dl = take(TB * V); w->lossr = take(TB); w->dz = take(TB * d);
+  w->dsn = take(TB * d);
+  w->u = take((size_t)B * d); w->logits = take((size_t)B * V); w->dx = take((size_t)B * d);
+  w->dx2 = take((size_t)B * d); w->dtmp = take((size_t)B * d); w->dh = take((size_t)B * F);
+  w->des = take((size_t)B * 2 * d); w->dscarry = take((size_t)B * d); w->dsd = take((size_t)B * d);
+  w->lo_w = reinterpret_cast<int *>(take(B)); w->lo_m = reinterpret_cast<int *>(take(B));
+  w->hi = reinterpret_cast<int *>(take(B));
+  return (off + 255) & ~(size_t)255;
+}
+
+hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
+  const rlt_config &c = A.c;
+  const int B = A.B, T = A.T, L = c.n_layers, d = c.d_model, F = c.d_ffn, H = c.n_heads,
+            dh = c.head_dim, V = c.vocab, Wn = c.window, G = c.mem_groups;
+  const float eps = c.rms_eps, scale = 1.0f / sqrtf((float)dh);
+  const size_t TB = (size_t)T * B;
+  const float *P_wg = (const float *)A.p->wg, *P_bg = (const float *)A.p->bg;
+  auto LP = [&](const void *base, size_t per) { return [=](int l) { return (const float *)base + (size_t)l * per; }; };
+  auto g1 = LP(A.p->g1, d), g2 = LP(A.p->g2, d), g3 = LP(A.p->g3, d);
+  auto wq = LP(A.p->wq, (size_t)d * d), wk = LP(A.p->wk, (size_t)d * d), wv = LP(A.p->wv, (size_t)d * d),
+       wo = LP(A.p->wo, (size_t)d * d), wqc = LP(A.p->wqc, (size_t)d * d), woc = LP(A.p->woc, (size_t)d * d),
+       w1 = LP(A.p->w1, (size_t)F * d), w2 = LP(A.p->w2, (size_t)d * F);
+  auto GL = [&](const void *base, size_t per) { return [=](int l) { return (float *)base + (size_t)l * per; }; };
+  auto dg1 = GL(A.gr->g1, d), dg2 = GL(A.gr->g2, d), dg3 = GL(A.gr->g3, d);
+  auto dwq = GL(A.gr->wq, (size_t)d * d), dwk = GL(A.gr->wk, (size_t)d * d), dwv = GL(A.gr->wv, (size_t)d * d),
+       dwo = GL(A.gr->wo, (size_t)d * d), dwqc = GL(A.gr->wqc, (size_t)d * d), dwoc = GL(A.gr->woc, (size_t)d * d),
+       dw1 = GL(A.gr->w1, (size_t)F * d), dw2 = GL(A.gr->w2, (size_t)d * F);
+  // per-layer saved rows: layer l, step t, row b
+  auto at = [&](float *base, int l, int t, size_t width) { return base + (((size_t)l * T + t) * B) * width; };
+  auto st = [&](float *base, int t, size_t width) { return base + (size_t)t * B * width; };
+  auto norm_fwd = [&](const float *x, const float *gm, float *y, float *r) {
+    hipLaunchKernelGGL(k_t_norm_fwd, dim3((B + 3) / 4), dim3(256), 0, s, x, gm, eps, y, r, B, d);
+  };
+  auto norm_bwd = [&](const float *x, const float *r, const float *gm, const float *dy, float *dx, int acc) {
+    hipLaunchKernelGGL(k_t_norm_bwd, dim3((B + 3) / 4), dim3(256), 0, s, x, r, gm, dy, dx, B, d, acc);
+  };
+  auto mem_base = [&](const float *m, int grp) { return m + (size_t)grp * A.m_group; };
+
+  // ---- zero the gradient outputs and accumulators
+  // the gradient buffers are the caller's writable outputs (rlt_params holds const pointers)
+  auto zero = [&](const void *p, size_t n) {
+    if (p)
+      hipLaunchKernelGGL(k_t_fill, dim3(blocks_for(n)), dim3(256), 0, s,
+                         static_cast<float *>(const_cast<void *>(p)), n, 0.f);
+  };
+  zero(A.gr->s_star, d); zero(A.gr->wg, (size_t)d * 2 * d); zero(A.gr->bg, d); zero(A.gr->go, d);
+  zero(A.gr->wout, (size_t)V * d);
+  zero(A.gr->g1, (size_t)L * d); zero(A.gr->g2, (size_t)L * d); zero(A.gr->g3, (size_t)L * d);
+  zero(w.dkh, (size_t)L * TB * d); zero(w.dvh, (size_t)L * TB * d);
+  zero(w.dscarry, (size_t)B * d);
+  if (A.de) zero(A.de, TB * d);
+
+  // ---- forward
+  for (int t = 0; t < T; ++t) {
+    hipLaunchKernelGGL(k_t_ranges, dim3(blocks_for(B, 64)), dim3(64), 0, s, w.lo_w, w.lo_m, w.hi, B, t, Wn);
+    // es = [e_t ; s_{t-1}]
+    float *es = st(w.es, t, 2 * d);
+    hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s,
+                       A.e + (size_t)t * d, (int64_t)T * d, es, (int64_t)2 * d, B, d);
+    if (t == 0) {
+      for (int b = 0; b < B; ++b)
+        hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for(d)), dim3(256), 0, s,
+                           (const float *)A.p->s_star, (int64_t)d, es + (size_t)b * 2 * d + d,
+                           (int64_t)2 * d, 1, d);
+    } else {
+      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s,
+                         st(w.s, t - 1, d), (int64_t)d, es + d, (int64_t)2 * d, B, d);
+    }
+    float *gz = st(w.g, t, d);
+    t_gemm_go<false, true, false>(es, 2 * d, P_wg, 2 * d, gz, d, B, d, 2 * d, s);
+    hipLaunchKernelGGL(k_t_merge_fwd, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, es, gz, P_bg,
+                       w.u, B, d);
+    const float *x = w.u;
+    for (int l = 0; l < L; ++l) {
+      float *xin = at(w.xin, l, t, d);
+      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, x, (int64_t)d,
+                         xin, (int64_t)d, B, d);
+      float *a = at(w.a, l, t, d), *r1 = at(w.r1, l, t, 1);
+      norm_fwd(xin, g1(l), a, r1);
+      float *q = at(w.q, l, t, d), *kh = at(w.kh, l, t, d), *vh = at(w.vh, l, t, d);
+      t_gemm_go<false, true, false>(a, d, wq(l), d, q, d, B, d, d, s);
+      t_gemm_go<false, true, false>(a, d, wk(l), d, kh, d, B, d, d, s);
+      t_gemm_go<false, true, false>(a, d, wv(l), d, vh, d, B, d, d, s);
+      TAttn ta{};
+      ta.q = q; ta.ldq = d;
+      ta.kb = at(w.kh, l, 0, d); ta.vb = at(w.vh, l, 0, d);
+      ta.s_seq = d; ta.s_head = dh; ta.s_pos = (int64_t)B * d;
+      ta.lo = w.lo_w; ta.hi = w.hi;
+      ta.o = at(w.o, l, t, d); ta.ldo = d;
+      ta.m = at(w.m1, l, t, H); ta.l = at(w.l1, l, t, H);
+      ta.H = H; ta.dh = dh; ta.scale = scale;
+      hipLaunchKernelGGL(k_t_attn_fwd, dim3(B * H), dim3(64), 0, s, ta);
+      float *x1 = at(w.x1, l, t, d);
+      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, xin, (int64_t)d,
+                         x1, (int64_t)d, B, d);
+      t_gemm_go<false, true, true>(ta.o, d, wo(l), d, x1, d, B, d, d, s);
+      float *cc = at(w.c, l, t, d), *r2 = at(w.r2, l, t, 1);
+      norm_fwd(x1, g2(l), cc, r2);
+      float *qc = at(w.qc, l, t, d);
+      t_gemm_go<false, true, false>(cc, d, wqc(l), d, qc, d, B, d, d, s);
+      const int grp = G == 1 ? 0 : l;
+      TAttn tc{};
+      tc.q = qc; tc.ldq = d;
+      tc.kb = mem_base(A.mk, grp); tc.vb = mem_base(A.mv, grp);
+      tc.s_seq = A.m_seq; tc.s_head = A.m_head; tc.s_pos = A.m_pos;
+      tc.lo = w.lo_m; tc.hi = w.hi;
+      tc.o = at(w.oc, l, t, d); tc.ldo = d;
+      tc.m = at(w.m2, l, t, H); tc.l = at(w.l2, l, t, H);
+      tc.H = H; tc.dh = dh; tc.scale = scale;
+      hipLaunchKernelGGL(k_t_attn_fwd, dim3(B * H), dim3(64), 0, s, tc);
+      float *x2 = at(w.x2, l, t, d);
+      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, x1, (int64_t)d,
+                         x2, (int64_t)d, B, d);
+      t_gemm_go<false, true, true>(tc.o, d, woc(l), d, x2, d, B, d, d, s);
+      float *ff = at(w.f, l, t, d), *r3 = at(w.r3, l, t, 1);
+      norm_fwd(x2, g3(l), ff, r3);
+      float *hpre = at(w.hpre, l, t, F), *hh = at(w.h, l, t, F);
+      t_gemm_go<false, true, false>(ff, d, w1(l), d, hpre, F, B, F, d, s);
+      hipLaunchKernelGGL(k_t_gelu_fwd, dim3(blocks_for((size_t)B * F)), dim3(256), 0, s, hpre, hh,
+                         (size_t)B * F);
+      // x3 = x2 + W2 h, kept in u (the next layer's input)
+      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, x2, (int64_t)d,
+                         w.u, (int64_t)d, B, d);
+      t_gemm_go<false, true, true>(hh, F, w2(l), F, w.u, d, B, d, F, s);
+      x = w.u;
+    }
+    float *sv = st(w.s, t, d);
+    hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, x, (int64_t)d, sv,
+                       (int64_t)d, B, d);
+    float *sn = st(w.sn, t, d), *ro = st(w.ro, t, 1);
+    norm_fwd(sv, (const float *)A.p->go, sn, ro);
+    t_gemm_go<false, true, false>(sn, d, (const float *)A.p->wout, d, w.logits, V, B, V, d, s);
+    hipLaunchKernelGGL(k_t_ce, dim3((B + 3) / 4), dim3(256), 0, s, w.logits, A.tg + t, (int64_t)T,
+                       st(w.dl, t, V), st(w.lossr, t, 1), B, V);
+  }
+  hipLaunchKernelGGL(k_t_sum, dim3(1), dim3(64), 0, s, w.lossr, TB, A.loss);
+
+  // ---- backward, steps in reverse
+  const bool det_s = (A.detach & RLT_DETACH_S) != 0, det_kv = (A.detach & RLT_DETACH_KV) != 0;
+  for (int t = T - 1; t >= 0; --t) {
+    hipLaunchKernelGGL(k_t_ranges, dim3(blocks_for(B, 64)), dim3(64), 0, s, w.lo_w, w.lo_m, w.hi, B, t, Wn);
+    const int chunk_start = A.chunk > 0 ? (t / A.chunk) * A.chunk : 0;
+    // head: dsn = dlogits W_out; ds_t = carry + RMSNorm_o backward
+    float *dsn = st(w.dsn, t, d);
+    t_gemm_go<false, false, false>(st(w.dl, t, V), V, (const float *)A.p->wout, d, dsn, d, B, d, V, s);
+    hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dscarry,
+                       (int64_t)d, w.dx, (int64_t)d, B, d);
+    norm_bwd(st(w.s, t, d), st(w.ro, t, 1), (const float *)A.p->go, dsn, w.dx, 1);
+    for (int l = L - 1; l >= 0; --l) {
+      // FFN: x3 = x2 + W2 gelu(W1 f), f = norm3(x2)
+      float *dxf = at(w.dxf, l, t, d);
+      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dx, (int64_t)d,
+                         dxf, (int64_t)d, B, d);
+      float *dhp = at(w.dhp, l, t, F);
+      t_gemm_go<false, false, false>(w.dx, d, w2(l), F, dhp, F, B, F, d, s);
+      hipLaunchKernelGGL(k_t_gelu_bwd, dim3(blocks_for((size_t)B * F)), dim3(256), 0, s,
+                         at(w.hpre, l, t, F), dhp, (size_t)B * F);
+      float *df = at(w.df, l, t, d);
+      t_gemm_go<false, false, false>(dhp, F, w1(l), d, df, d, B, d, F, s);
+      norm_bwd(at(w.x2, l, t, d), at(w.r3, l, t, 1), g3(l), df, w.dx, 1);
+      // cross: x2 = x1 + W_Oc attn(W_Qc c, memory), c = norm2(x1)
+      float *dxoc = at(w.dxoc, l, t, d);
+      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dx, (int64_t)d,
+                         dxoc, (int64_t)d, B, d);
+      t_gemm_go<false, false, false>(w.dx, d, woc(l), d, w.dtmp, d, B, d, d, s);   // d oc
+      const int grp = G == 1 ? 0 : l;
+      TAttn tc{};
+      tc.q = at(w.qc, l, t, d); tc.ldq = d;
+      tc.kb = mem_base(A.mk, grp); tc.vb = mem_base(A.mv, grp);
+      tc.s_seq = A.m_seq; tc.s_head = A.m_head; tc.s_pos = A.m_pos;
+      tc.lo = w.lo_m; tc.hi = w.hi;
+      tc.o = at(w.oc, l, t, d); tc.ldo = d;
+      tc.m = at(w.m2, l, t, H); tc.l = at(w.l2, l, t, H);
+      tc.dout = w.dtmp;
+      float *dqc = at(w.dqc, l, t, d);
+      tc.dq = dqc;
+      tc.dkb = A.dmk ? A.dmk + (size_t)grp * A.m_group : nullptr;
+      tc.dvb = A.dmv ? A.dmv + (size_t)grp * A.m_group : nullptr;
+      tc.cut_lo = 0;
+      tc.H = H; tc.dh = dh; tc.scale = scale;
+      hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(64), 0, s, tc);
+      float *dcc = at(w.dc, l, t, d);
+      t_gemm_go<false, false, false>(dqc, d, wqc(l), d, dcc, d, B, d, d, s);
+      norm_bwd(at(w.x1, l, t, d), at(w.r2, l, t, 1), g2(l), dcc, w.dx, 1);
+      // window self-attention: x1 = xin + W_O attn(q, K, V), q,k,v = W a, a = norm1(xin)
+      float *dxo = at(w.dxo, l, t, d);
+      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dx, (int64_t)d,
+                         dxo, (int64_t)d, B, d);
+      t_gemm_go<false, false, false>(w.dx, d, wo(l), d, w.dtmp, d, B, d, d, s);    // d o
+      TAttn ta{};
+      ta.q = at(w.q, l, t, d); ta.ldq = d;
+      ta.kb = at(w.kh, l, 0, d); ta.vb = at(w.vh, l, 0, d);
+      ta.s_seq = d; ta.s_head = dh; ta.s_pos = (int64_t)B * d;
+      ta.lo = w.lo_w; ta.hi = w.hi;
+      ta.o = at(w.o, l, t, d); ta.ldo = d;
+      ta.m = at(w.m1, l, t, H); ta.l = at(w.l1, l, t, H);
+      ta.dout = w.dtmp;
+      float *dq = at(w.dq, l, t, d);
+      ta.dq = dq;
+      ta.dkb = at(w.dkh, l, 0, d); ta.dvb = at(w.dvh, l, 0, d);
+      ta.cut_lo = det_kv ? chunk_start : 0;
+      ta.H = H; ta.dh = dh; ta.scale = scale;
+      hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(64), 0, s, ta);
+      // da = dq Wq + dk_t Wk + dv_t Wv (dk_t, dv_t complete: every later reader is done)
+      float *daa = at(w.da, l, t, d);
+      t_gemm_go<false, false, false>(dq, d, wq(l), d, daa, d, B, d, d, s);
+      t_gemm_go<false, false, true>(at(w.dkh, l, t, d), d, wk(l), d, daa, d, B, d, d, s);
+      t_gemm_go<false, false, true>(at(w.dvh, l, t, d), d, wv(l), d, daa, d, B, d, d, s);
+      norm_bwd(at(w.xin, l, t, d), at(w.r1, l, t, 1), g1(l), daa, w.dx, 1);
+    }
+    // merge: u = g e + (1 - g) s_{t-1}, g = sigmoid(W_g [e ; s] + b_g)
+    float *dz = st(w.dz, t, d);
+    hipLaunchKernelGGL(k_t_merge_bwd, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, st(w.es, t, 2 * d),
+                       st(w.g, t, d), w.dx, dz, w.des, B, d);
+    t_gemm_go<false, false, true>(dz, d, P_wg, 2 * d, w.des, 2 * d, B, 2 * d, d, s);
+    if (A.de)
+      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.des,
+                         (int64_t)2 * d, A.de + (size_t)t * d, (int64_t)T * d, B, d);
+    // the gradient reaching s_{t-1}; cut at a chunk boundary when s is detached
+    const bool cut = det_s && A.chunk > 0 && t > 0 && t % A.chunk == 0;
+    if (t > 0) {
+      if (cut) {
+        hipLaunchKernelGGL(k_t_fill, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dscarry,
+                           (size_t)B * d, 0.f);
+      } else {
+        hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.des + d,
+                           (int64_t)2 * d, w.dscarry, (int64_t)d, B, d);
+      }
+    } else {
+      // s_0 = s* for every sequence
+      hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, w.des + d, nullptr, nullptr,
+                         (float *)A.gr->s_star, B, d, (int64_t)2 * d);
+    }
+  }
+
+  // ---- parameter gradients over all T*B rows
+  const int R = (int)TB;
+  for (int l = 0; l < L; ++l) {
+    auto X = [&](float *base, size_t width) { return at(base, l, 0, width); };
+    t_gemm_go<true, false, false>(X(w.dq, d), d, X(w.a, d), d, dwq(l), d, d, d, R, s);
+    t_gemm_go<true, false, false>(X(w.dkh, d), d, X(w.a, d), d, dwk(l), d, d, d, R, s);
+    t_gemm_go<true, false, false>(X(w.dvh, d), d, X(w.a, d), d, dwv(l), d, d, d, R, s);
+    t_gemm_go<true, false, false>(X(w.dxo, d), d, X(w.o, d), d, dwo(l), d, d, d, R, s);
+    t_gemm_go<true, false, false>(X(w.dqc, d), d, X(w.c, d), d, dwqc(l), d, d, d, R, s);
+    t_gemm_go<true, false, false>(X(w.dxoc, d), d, X(w.oc, d), d, dwoc(l), d, d, d, R, s);
+    t_gemm_go<true, false, false>(X(w.dhp, F), F, X(w.f, d), d, dw1(l), d, F, d, R, s);
+    t_gemm_go<true, false, false>(X(w.dxf, d), d, X(w.h, F), F, dw2(l), F, d, F, R, s);
+    // gains: dgamma[n] = sum_rows dy[n] * x[n] * r
+    hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, X(w.da, d), X(w.xin, d),
+                       at(w.r1, l, 0, 1), dg1(l), R, d, (int64_t)d);
+    hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, X(w.dc, d), X(w.x1, d),
+                       at(w.r2, l, 0, 1), dg2(l), R, d, (int64_t)d);
+    hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, X(w.df, d), X(w.x2, d),
+                       at(w.r3, l, 0, 1), dg3(l), R, d, (int64_t)d);
+  }
+  t_gemm_go<true, false, false>(w.dl, V, w.sn, d, (float *)A.gr->wout, d, V, d, R, s);
+  t_gemm_go<true, false, false>(w.dz, d, w.es, 2 * d, (float *)A.gr->wg, 2 * d, d, 2 * d, R, s);
+  hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, w.dz, nullptr, nullptr,
+                     (float *)A.gr->bg, R, d, (int64_t)d);
+  hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, w.dsn, w.s, w.ro,
+                     (float *)A.gr->go, R, d, (int64_t)d);
+  return hipGetLastError();
+}
+}  // namespace
+
+size_t train_workspace_bytes(const rlt_config &c, int B, int T) {
+  TrainWs w;
+  return train_layout(c, B, T, &w, nullptr);
+}
+
+hipError_t launch_bptt(const TrainArgs &a, void *ws, hipStream_t s) {
+  TrainWs w;
+  train_layout(a.c, a.B, a.T, &w, ws);
+  return run_bptt(a, w, s);
+}
+
+}  // namespace rlt
