@@ -803,6 +803,87 @@ def cpu_encoder_baseline(cfg, params_gpu, eparams_gpu, tokens, budget_s=15.0):
                       f"prefixes, {prep:.1f} s weight conversion untimed)"}
 
 
+def run_train(args):
+    """Backpropagation through time at the small configuration in fp32
+    (d = 512, H = 8, L = 12, F = 2048, W = 128, G = 12, V = 4096): 32 sequences
+    x 128 steps from H_0, loss on every next token, the full gradient of every
+    parameter, e and the memory (one rlt_bptt call), repeated `steps` times."""
+    import torch
+    from recurrent_decode_step_amd import binding, synth
+    from recurrent_decode_step_amd.configs import SMALL
+    cfg = SMALL.model.with_(dtype=0)
+    B, T = 32, 128
+    K = 3 if args.steps is None else args.steps
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    params = synth.model_params(cfg, device=dev)
+    e = synth.encoder_e(cfg, B, T, device=dev)
+    mk, mv = synth.encoder_memory(cfg, B, T, device=dev)
+    tg = torch.from_numpy(synth.token_ids(B, T, cfg.vocab, index=0)).to(dev)
+    ws = None
+    for _ in range(max(args.warmup, 1)):
+        loss, g, de, dm = binding.rlt_bptt(cfg, params, e, (mk, mv), tg)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(K):
+        loss, g, de, dm = binding.rlt_bptt(cfg, params, e, (mk, mv), tg)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / K
+    if not torch.isfinite(loss).all():
+        raise RuntimeError("non-finite loss")
+    d, L, F, V, W, H = cfg.d_model, cfg.n_layers, cfg.d_ffn, cfg.vocab, cfg.window, cfg.n_heads
+    # GEMM FLOPs: forward, input gradients and weight gradients (3 x the forward products)
+    fwd = 4 * d * d + L * (12 * d * d + 4 * d * F) + 2 * d * V
+    gemm_flops = 3.0 * B * T * fwd
+    # attention: 4 d per attended position forward, twice that backward
+    pos = sum(min(t + 1, W) + (t + 1) for t in range(T))
+    attn_flops = 3.0 * 4 * d * L * B * pos
+    total = gemm_flops + attn_flops
+    out = {
+        "metric": "BPTT training tokens/sec at 1 GPU (fp32, 12-layer d=512, B=32 x 128 steps)",
+        "value": round(B * T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": max(args.warmup, 1), "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": SMALL.name.replace("bf16", "f32") + ", BPTT over 128 steps",
+                   "batch": B, "steps_per_sequence": T, "loss": "next-token cross-entropy, all targets",
+                   "gradients": "every parameter, e and memory; full BPTT"},
+        "roofline": {"bound": "alu", "kernel": "whole rlt_bptt call (fp32 VALU GEMMs and attention)",
+                     "achieved": round(total / (ms / 1e3) / 1e12, 2), "peak": 157.3,
+                     "unit": "TFLOP/s", "frac": round(total / (ms / 1e3) / 157.3e12, 4),
+                     "traffic": None, "gemm_flops": gemm_flops, "attention_flops": attn_flops},
+        "loss_per_token": round(float(loss) / (B * T), 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_train_baseline(cfg, params, e, mk, mv, tg, args.cpu_budget)
+    return out
+
+
+def cpu_train_baseline(cfg, params, e, mk, mv, tg, budget_s=15.0):
+    """The oracle's BPTT (torch autograd, float64 as it stands) on the host,
+    one sequence over growing step counts until the budget is spent."""
+    import torch
+    from oracle import bptt
+    host = {k: v.float().cpu() for k, v in params.items()}
+    nthreads = torch.get_num_threads()
+    n, rate, el, spent, done = 2, 0.0, 0.0, 0.0, 0
+    while spent < budget_s and n <= e.shape[1]:
+        t0 = time.time()
+        bptt.gradients(host, e[:1, :n].cpu(), mk[:, :1, :, :n].cpu(), mv[:, :1, :, :n].cpu(),
+                       tg[:1, :n].cpu().numpy(), n_heads=cfg.n_heads, window=cfg.window,
+                       rms_eps=cfg.rms_eps)
+        el = time.time() - t0
+        spent += el
+        rate, done = n / el, n
+        n *= 2
+    return {"value": rate, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"1 sequence x {done} steps in one oracle BPTT call (torch autograd, float64, "
+                      f"12 layers; {el:.1f} s timed, {spent:.1f} s over the doubling lengths)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -814,6 +895,8 @@ def main():
                     help="longctx: one full 32768-step run instead of the window fit")
     ap.add_argument("--generate", action="store_true",
                     help="generation at the reference depth after the 2048-token prompt")
+    ap.add_argument("--train", action="store_true",
+                    help="backpropagation through time (fp32, small config, B = 32 x 128 steps)")
     ap.add_argument("--encode", action="store_true",
                     help="the causal encoder over the reference-depth prompt (B = 32 x 2048 tokens)")
     ap.add_argument("--score", action="store_true",
@@ -839,6 +922,8 @@ def main():
         out = run_counters_sample(args)
     elif args.encode:
         out = run_encode(args)
+    elif args.train:
+        out = run_train(args)
     elif args.score:
         out = run_score(args)
     elif args.generate:

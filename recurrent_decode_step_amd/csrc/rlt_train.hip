@@ -25,6 +25,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -35,17 +36,21 @@ namespace {
 // C[m][n] = (ACC ? C[m][n] : 0) + sum_k A(m, k) B(k, n), k in order.
 // A(m, k) = TA ? A[k * lda + m] : A[m * lda + k]; B(k, n) = TB ? B[n * ldb + k] : B[k * ldb + n].
 // 64 x 64 outputs per workgroup, 4 x 4 per thread, K in chunks of 16 through LDS.
+// Split-K form (blockIdx.z = part): part z covers k in [z * kpart, (z+1) * kpart)
+// and writes its sum to C + z * M * N (ldc = N); k_t_reduce adds the parts in order.
 template <bool TA, bool TB, bool ACC>
 __global__ __launch_bounds__(256) void k_t_gemm(const float *__restrict__ A, int64_t lda,
                                                 const float *__restrict__ B, int64_t ldb,
                                                 float *__restrict__ C, int64_t ldc, int M, int N,
-                                                int K) {
+                                                int K, int kpart) {
   __shared__ float As[16][64 + 1];
   __shared__ float Bs[16][64 + 1];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int kbeg = blockIdx.z * kpart, kend = min(K, kbeg + kpart);
+  C += (size_t)blockIdx.z * M * N;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
+  for (int k0 = kbeg; k0 < kend; k0 += 16) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int idx = threadIdx.x + 256 * u;   // 0..1023
@@ -55,7 +60,7 @@ __global__ __launch_bounds__(256) void k_t_gemm(const float *__restrict__ A, int
         if (TA) { mm = idx & 63; kk = idx >> 6; } else { kk = idx & 15; mm = idx >> 4; }
         const int m = m0 + mm, k = k0 + kk;
         float v = 0.f;
-        if (m < M && k < K) v = TA ? A[(size_t)k * lda + m] : A[(size_t)m * lda + k];
+        if (m < M && k < kend) v = TA ? A[(size_t)k * lda + m] : A[(size_t)m * lda + k];
         As[kk][mm] = v;
       }
       // B tile: 16 (k) x 64 (n)
@@ -64,7 +69,7 @@ __global__ __launch_bounds__(256) void k_t_gemm(const float *__restrict__ A, int
         if (TB) { kk = idx & 15; nn = idx >> 4; } else { nn = idx & 63; kk = idx >> 6; }
         const int k = k0 + kk, n = n0 + nn;
         float v = 0.f;
-        if (n < N && k < K) v = TB ? B[(size_t)n * ldb + k] : B[(size_t)k * ldb + n];
+        if (n < N && k < kend) v = TB ? B[(size_t)n * ldb + k] : B[(size_t)k * ldb + n];
         Bs[kk][nn] = v;
       }
     }
@@ -95,6 +100,19 @@ __global__ __launch_bounds__(256) void k_t_gemm(const float *__restrict__ A, int
       *c = ACC ? *c + acc[i][j] : acc[i][j];
     }
   }
+}
+
+// C[m][n] (+)= sum over parts z in order of P[z][m][n]
+template <bool ACC>
+__global__ void k_t_reduce(const float *__restrict__ P, int parts, float *__restrict__ C,
+                           int64_t ldc, int M, int N) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)M * N) return;
+  const int m = (int)(i / N), n = (int)(i % N);
+  float s = 0.f;
+  for (int z = 0; z < parts; ++z) s += P[(size_t)z * M * N + i];
+  float *c = C + (size_t)m * ldc + n;
+  *c = ACC ? *c + s : s;
 }
 
 __device__ __forceinline__ float t_wave_sum(float v) {
@@ -364,10 +382,30 @@ __global__ void k_t_ranges(int *lo_w, int *lo_m, int *hi, int B, int t, int W) {
 // ---------------------------------------------------------------- host helpers
 unsigned blocks_for(size_t n, unsigned per = 256) { return (unsigned)((n + per - 1) / per); }
 
+// Split-K scratch of the per-step products: parts * tiles <= kSplitTiles, each
+// tile 64 x 64, so the partial sums never exceed kSplitTiles * 4096 floats.
+constexpr int kSplitTiles = 256;
+thread_local float *g_split = nullptr;   // the calling thread's current workspace scratch
+
 template <bool TA, bool TB, bool ACC>
 void t_gemm_go(const float *A, int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
                int M, int N, int K, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
+  const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  int parts = 1;
+  if (g_split && tiles < kSplitTiles / 2 && K >= 256) {
+    parts = std::min(kSplitTiles / tiles, K / 128);
+    parts = std::max(parts, 1);
+  }
+  if (parts > 1) {
+    const int kpart = (((K + parts - 1) / parts) + 15) / 16 * 16;
+    parts = (K + kpart - 1) / kpart;
+    hipLaunchKernelGGL((k_t_gemm<TA, TB, false>), dim3((N + 63) / 64, (M + 63) / 64, parts),
+                       dim3(256), 0, s, A, lda, B, ldb, g_split, (int64_t)N, M, N, K, kpart);
+    hipLaunchKernelGGL((k_t_reduce<ACC>), dim3(blocks_for((size_t)M * N)), dim3(256), 0, s,
+                       (const float *)g_split, parts, C, ldc, M, N);
+    return;
+  }
   if (K <= 0) {
     if (!ACC) {
       for (int m = 0; m < M; ++m)
@@ -377,7 +415,7 @@ void t_gemm_go(const float *A, int64_t lda, const float *B, int64_t ldb, float *
     return;
   }
   hipLaunchKernelGGL((k_t_gemm<TA, TB, ACC>), dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s,
-                     A, lda, B, ldb, C, ldc, M, N, K);
+                     A, lda, B, ldb, C, ldc, M, N, K, K);
 }
 
 }  // namespace
@@ -395,6 +433,7 @@ struct TrainWs {
   // scratch [B][.]
   float *u, *logits, *dx, *dx2, *dtmp, *dh, *des, *dscarry, *dsd;
   int *lo_w, *lo_m, *hi;
+  float *split;              // split-K partial sums
 };
 
 size_t train_layout(const rlt_config &c, int B, int T, TrainWs *w, void *base) {
@@ -426,6 +465,7 @@ size_t train_layout(const rlt_config &c, int B, int T, TrainWs *w, void *base) {
   w->des = take((size_t)B * 2 * d); w->dscarry = take((size_t)B * d); w->dsd = take((size_t)B * d);
   w->lo_w = reinterpret_cast<int *>(take(B)); w->lo_m = reinterpret_cast<int *>(take(B));
   w->hi = reinterpret_cast<int *>(take(B));
+  w->split = take((size_t)kSplitTiles * 64 * 64);
   return (off + 255) & ~(size_t)255;
 }
 
@@ -692,7 +732,10 @@ size_t train_workspace_bytes(const rlt_config &c, int B, int T) {
 hipError_t launch_bptt(const TrainArgs &a, void *ws, hipStream_t s) {
   TrainWs w;
   train_layout(a.c, a.B, a.T, &w, ws);
-  return run_bptt(a, w, s);
+  g_split = w.split;
+  const hipError_t e = run_bptt(a, w, s);
+  g_split = nullptr;
+  return e;
 }
 
 }  // namespace rlt
