@@ -146,3 +146,18 @@ def test_encoder_null_handles_and_sizes():
     assert L.rlt_encoder_state_bytes(C.byref(cfg_of(TINY)), 2, 16, 0) == 0
     # bf16 with head_dim 16 is outside the encoder kernels
     assert L.rlt_encoder_state_bytes(C.byref(cfg_of(SMALL, n_heads=32, head_dim=16)), 2, 16, 8) == 0
+
+
+def test_bptt_host_checks():
+    L = lib()
+    c = cfg_of(TINY)
+    # fp32 tiny config: a workspace size; bf16 or T beyond 4096: none
+    assert L.rlt_bptt_workspace_bytes(C.byref(c), 2, 16) > 0
+    assert L.rlt_bptt_workspace_bytes(C.byref(cfg_of(SMALL)), 2, 16) == 0
+    assert L.rlt_bptt_workspace_bytes(C.byref(c), 2, 5000) == 0
+    # NULL parameters and a bf16 config are rejected before any device work
+    p = binding.rlt_params()
+    assert L.rlt_bptt(C.byref(c), C.byref(p), 2, 4, None, None, None, None, C.byref(p), None, None,
+                      None, None, 0, None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_bptt(C.byref(cfg_of(SMALL)), C.byref(p), 2, 4, None, None, None, None, C.byref(p),
+                      None, None, None, None, 0, None) == binding.RLT_ERR_UNSUPPORTED
