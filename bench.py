@@ -805,14 +805,14 @@ def cpu_encoder_baseline(cfg, params_gpu, eparams_gpu, tokens, budget_s=15.0):
 
 def run_train(args):
     """Backpropagation through time at the small configuration in fp32
-    (d = 512, H = 8, L = 12, F = 2048, W = 128, G = 12, V = 4096): 32 sequences
-    x 128 steps from H_0, loss on every next token, the full gradient of every
+    (d = 512, H = 8, L = 12, F = 2048, W = 128, G = 12, V = 4096): B sequences
+    (default 128) x 128 steps from H_0, loss on every next token, the full gradient of every
     parameter, e and the memory (one rlt_bptt call), repeated `steps` times."""
     import torch
     from recurrent_decode_step_amd import binding, synth
     from recurrent_decode_step_amd.configs import SMALL
     cfg = SMALL.model.with_(dtype=0)
-    B, T = 32, 128
+    B, T = args.train_batch, 128
     K = 3 if args.steps is None else args.steps
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -844,7 +844,7 @@ def run_train(args):
     attn_flops = 3.0 * 4 * d * L * B * pos
     total = gemm_flops + attn_flops
     out = {
-        "metric": "BPTT training tokens/sec at 1 GPU (fp32, 12-layer d=512, B=32 x 128 steps)",
+        "metric": f"BPTT training tokens/sec at 1 GPU (fp32, 12-layer d=512, B={B} x 128 steps)",
         "value": round(B * T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": max(args.warmup, 1), "ms_per_step": round(ms, 3), "higher_is_better": True,
         "dtype": "f32", "data": "synthetic",
@@ -896,7 +896,9 @@ def main():
     ap.add_argument("--generate", action="store_true",
                     help="generation at the reference depth after the 2048-token prompt")
     ap.add_argument("--train", action="store_true",
-                    help="backpropagation through time (fp32, small config, B = 32 x 128 steps)")
+                    help="backpropagation through time (fp32, small config, B x 128 steps)")
+    ap.add_argument("--train-batch", type=int, default=128,
+                    help="sequences per BPTT call for --train")
     ap.add_argument("--encode", action="store_true",
                     help="the causal encoder over the reference-depth prompt (B = 32 x 2048 tokens)")
     ap.add_argument("--score", action="store_true",

@@ -195,15 +195,40 @@ struct TAttn {
 
 constexpr int kTMaxPos = kTrainMaxPos;
 
-__global__ __launch_bounds__(64) void k_t_attn_fwd(TAttn a) {
+__device__ __forceinline__ float t_block_max(float v, float *red) {
+  v = t_wave_max(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ float t_block_sum(float v, float *red) {
+  v = t_wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  const float r = ((red[0] + red[1]) + red[2]) + red[3];
+  __syncthreads();
+  return r;
+}
+
+// 4 wavefronts per (row, head): positions spread over all 256 threads for the
+// scores; each wavefront then sums a quarter of the positions per channel, and
+// the four partial sums are added in wavefront order.
+__global__ __launch_bounds__(256) void k_t_attn_fwd(TAttn a) {
   __shared__ float sc[kTMaxPos];
-  const int b = blockIdx.x / a.H, h = blockIdx.x % a.H, lane = threadIdx.x;
+  __shared__ float red[4];
+  __shared__ float part[4][256];
+  const int b = blockIdx.x / a.H, h = blockIdx.x % a.H, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int lo = a.lo[b], hi = a.hi[b], n = hi - lo + 1;
   const float *q = a.q + (size_t)b * a.ldq + h * a.dh;
   const float *K = a.kb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
   const float *V = a.vb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
   float mx = -INFINITY;
-  for (int j = lane; j < n; j += 64) {
+  for (int j = tid; j < n; j += 256) {
     const float *k = K + (size_t)(lo + j) * a.s_pos;
     float s = 0.f;
     for (int c = 0; c < a.dh; ++c) s = fmaf(q[c], k[c], s);
@@ -211,22 +236,29 @@ __global__ __launch_bounds__(64) void k_t_attn_fwd(TAttn a) {
     sc[j] = s;
     mx = fmaxf(mx, s);
   }
-  mx = t_wave_max(mx);
+  mx = t_block_max(mx, red);
   float sum = 0.f;
-  for (int j = lane; j < n; j += 64) {
+  for (int j = tid; j < n; j += 256) {
     const float p = expf(sc[j] - mx);
     sc[j] = p;
     sum += p;
   }
-  sum = t_wave_sum(sum);
-  __syncthreads();
+  sum = t_block_sum(sum, red);
   const float inv = 1.0f / sum;
-  for (int c = lane; c < a.dh; c += 64) {
+  const int q4 = (n + 3) / 4, j0 = wave * q4, j1 = min(n, j0 + q4);
+  for (int c0 = 0; c0 < a.dh; c0 += 64) {
+    const int c = c0 + lane;
     float acc = 0.f;
-    for (int j = 0; j < n; ++j) acc = fmaf(sc[j], V[(size_t)(lo + j) * a.s_pos + c], acc);
-    a.o[(size_t)b * a.ldo + h * a.dh + c] = acc * inv;
+    if (c < a.dh)
+      for (int j = j0; j < j1; ++j) acc = fmaf(sc[j], V[(size_t)(lo + j) * a.s_pos + c], acc);
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && c < a.dh)
+      a.o[(size_t)b * a.ldo + h * a.dh + c] =
+          (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) * inv;
+    __syncthreads();
   }
-  if (lane == 0) {
+  if (tid == 0) {
     a.m[b * a.H + h] = mx;
     a.l[b * a.H + h] = sum;
   }
@@ -234,10 +266,13 @@ __global__ __launch_bounds__(64) void k_t_attn_fwd(TAttn a) {
 
 // p_j = exp(s_j - m) / l; D = do . o; ds_j = p_j (do . v_j - D);
 // dq = scale sum_j ds_j k_j; dk_j += scale ds_j q; dv_j += p_j do.
-__global__ __launch_bounds__(64) void k_t_attn_bwd(TAttn a) {
+__global__ __launch_bounds__(256) void k_t_attn_bwd(TAttn a) {
   __shared__ float sp[kTMaxPos];
   __shared__ float sds[kTMaxPos];
-  const int b = blockIdx.x / a.H, h = blockIdx.x % a.H, lane = threadIdx.x;
+  __shared__ float red[4];
+  __shared__ float part[4][256];
+  const int b = blockIdx.x / a.H, h = blockIdx.x % a.H, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int lo = a.lo[b], hi = a.hi[b], n = hi - lo + 1;
   const float *q = a.q + (size_t)b * a.ldq + h * a.dh;
   const float *o = a.o + (size_t)b * a.ldo + h * a.dh;
@@ -246,9 +281,9 @@ __global__ __launch_bounds__(64) void k_t_attn_bwd(TAttn a) {
   const float *V = a.vb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
   const float mx = a.m[b * a.H + h], inv = 1.0f / a.l[b * a.H + h];
   float D = 0.f;
-  for (int c = lane; c < a.dh; c += 64) D = fmaf(dout[c], o[c], D);
-  D = t_wave_sum(D);
-  for (int j = lane; j < n; j += 64) {
+  for (int c = tid; c < a.dh; c += 256) D = fmaf(dout[c], o[c], D);
+  D = t_block_sum(D, red);
+  for (int j = tid; j < n; j += 256) {
     const float *k = K + (size_t)(lo + j) * a.s_pos;
     const float *v = V + (size_t)(lo + j) * a.s_pos;
     float s = 0.f, dp = 0.f;
@@ -261,16 +296,26 @@ __global__ __launch_bounds__(64) void k_t_attn_bwd(TAttn a) {
     sds[j] = p * (dp - D);
   }
   __syncthreads();
-  for (int c = lane; c < a.dh; c += 64) {
+  // dq: each wavefront sums a quarter of the positions, added in wavefront order
+  const int q4 = (n + 3) / 4, j0 = wave * q4, j1 = min(n, j0 + q4);
+  for (int c0 = 0; c0 < a.dh; c0 += 64) {
+    const int c = c0 + lane;
     float acc = 0.f;
-    for (int j = 0; j < n; ++j) acc = fmaf(sds[j], K[(size_t)(lo + j) * a.s_pos + c], acc);
-    a.dq[(size_t)b * a.ldq + h * a.dh + c] = acc * a.scale;
+    if (c < a.dh)
+      for (int j = j0; j < j1; ++j) acc = fmaf(sds[j], K[(size_t)(lo + j) * a.s_pos + c], acc);
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && c < a.dh)
+      a.dq[(size_t)b * a.ldq + h * a.dh + c] =
+          (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) * a.scale;
+    __syncthreads();
   }
   if (a.dkb) {
+    // every position's rows belong to this (row, head) alone: threads split positions
     float *dK = a.dkb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
     float *dV = a.dvb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
-    const int j0 = max(0, a.cut_lo - lo);
-    for (int j = j0; j < n; ++j) {
+    const int jc = max(0, a.cut_lo - lo);
+    for (int j = jc + wave; j < n; j += 4) {
       const float ds = sds[j] * a.scale, p = sp[j];
       for (int c = lane; c < a.dh; c += 64) {
         dK[(size_t)(lo + j) * a.s_pos + c] += ds * q[c];
@@ -393,8 +438,8 @@ void t_gemm_go(const float *A, int64_t lda, const float *B, int64_t ldb, float *
   if (M <= 0 || N <= 0) return;
   const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
   int parts = 1;
-  if (g_split && tiles < kSplitTiles / 2 && K >= 256) {
-    parts = std::min(kSplitTiles / tiles, K / 128);
+  if (g_split && tiles < kSplitTiles / 2 && K >= 64) {
+    parts = std::min(kSplitTiles / tiles, K / 32);
     parts = std::max(parts, 1);
   }
   if (parts > 1) {
@@ -550,7 +595,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       ta.o = at(w.o, l, t, d); ta.ldo = d;
       ta.m = at(w.m1, l, t, H); ta.l = at(w.l1, l, t, H);
       ta.H = H; ta.dh = dh; ta.scale = scale;
-      hipLaunchKernelGGL(k_t_attn_fwd, dim3(B * H), dim3(64), 0, s, ta);
+      hipLaunchKernelGGL(k_t_attn_fwd, dim3(B * H), dim3(256), 0, s, ta);
       float *x1 = at(w.x1, l, t, d);
       hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, xin, (int64_t)d,
                          x1, (int64_t)d, B, d);
@@ -568,7 +613,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       tc.o = at(w.oc, l, t, d); tc.ldo = d;
       tc.m = at(w.m2, l, t, H); tc.l = at(w.l2, l, t, H);
       tc.H = H; tc.dh = dh; tc.scale = scale;
-      hipLaunchKernelGGL(k_t_attn_fwd, dim3(B * H), dim3(64), 0, s, tc);
+      hipLaunchKernelGGL(k_t_attn_fwd, dim3(B * H), dim3(256), 0, s, tc);
       float *x2 = at(w.x2, l, t, d);
       hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, x1, (int64_t)d,
                          x2, (int64_t)d, B, d);
@@ -639,7 +684,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       tc.dvb = A.dmv ? A.dmv + (size_t)grp * A.m_group : nullptr;
       tc.cut_lo = 0;
       tc.H = H; tc.dh = dh; tc.scale = scale;
-      hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(64), 0, s, tc);
+      hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(256), 0, s, tc);
       float *dcc = at(w.dc, l, t, d);
       t_gemm_go<false, false, false>(dqc, d, wqc(l), d, dcc, d, B, d, d, s);
       norm_bwd(at(w.x1, l, t, d), at(w.r2, l, t, 1), g2(l), dcc, w.dx, 1);
@@ -661,7 +706,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       ta.dkb = at(w.dkh, l, 0, d); ta.dvb = at(w.dvh, l, 0, d);
       ta.cut_lo = det_kv ? chunk_start : 0;
       ta.H = H; ta.dh = dh; ta.scale = scale;
-      hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(64), 0, s, ta);
+      hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(256), 0, s, ta);
       // da = dq Wq + dk_t Wk + dv_t Wv (dk_t, dv_t complete: every later reader is done)
       float *daa = at(w.da, l, t, d);
       t_gemm_go<false, false, false>(dq, d, wq(l), d, daa, d, B, d, d, s);

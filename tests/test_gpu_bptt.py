@@ -80,6 +80,8 @@ CONFIGS = [
     ((32, 2, 2, 64, 11, 3, 1), 2, 6),
     ((32, 2, 2, 64, 11, 3, 2), 2, 6),
     ((128, 4, 2, 256, 200, 5, 1), 3, 20),
+    # 128 sequences: the per-step products take the 128 x 128 tiles with split K
+    ((128, 4, 1, 256, 200, 4, 1), 128, 4),
 ]
 
 
