@@ -159,19 +159,30 @@ __global__ void k_t_norm_bwd(const float *__restrict__ x, const float *__restric
   }
 }
 
-// out[n] += sum_m a[m][n] (* b[m][n]) (* r[m]), m in order; one thread per column.
+// out[n] += sum_m a[m][n] (* b[m][n]) (* r[m]) in two fixed-order stages: chunk
+// z (blockIdx.y) of `rows_per` rows sums its rows in order into part[z][n], then
+// k_t_colsum_fin adds the chunks in order.
 __global__ void k_t_colsum(const float *__restrict__ a, const float *__restrict__ b,
-                           const float *__restrict__ r, float *__restrict__ out, int M, int N,
-                           int64_t ld) {
+                           const float *__restrict__ r, float *__restrict__ part, int M,
+                           int64_t ld, int rows_per) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
+  const int m0 = blockIdx.y * rows_per, m1 = min(M, m0 + rows_per);
   float s = 0.f;
-  for (int m = 0; m < M; ++m) {
+  for (int m = m0; m < m1; ++m) {
     float v = a[(size_t)m * ld + n];
     if (b) v *= b[(size_t)m * ld + n];
     if (r) v *= r[m];
     s += v;
   }
+  part[(size_t)blockIdx.y * N + n] = s;
+}
+__global__ void k_t_colsum_fin(const float *__restrict__ part, int chunks, float *__restrict__ out,
+                               int N) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.f;
+  for (int z = 0; z < chunks; ++z) s += part[(size_t)z * N + n];
   out[n] += s;
 }
 
@@ -431,6 +442,19 @@ unsigned blocks_for(size_t n, unsigned per = 256) { return (unsigned)((n + per -
 // tile 64 x 64, so the partial sums never exceed kSplitTiles * 4096 floats.
 constexpr int kSplitTiles = 256;
 thread_local float *g_split = nullptr;   // the calling thread's current workspace scratch
+
+// column sums through the split scratch: up to 64 chunks of rows
+void t_colsum(const float *a, const float *b, const float *r, float *out, int M, int N, int64_t ld,
+              hipStream_t s) {
+  int chunks = std::max(1, std::min(64, M / 64));
+  while (chunks > 1 && (size_t)chunks * N > (size_t)kSplitTiles * 4096) --chunks;
+  const int rows_per = (M + chunks - 1) / chunks;
+  chunks = (M + rows_per - 1) / rows_per;
+  hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(N), chunks), dim3(256), 0, s, a, b, r, g_split, M, N,
+                     ld, rows_per);
+  hipLaunchKernelGGL(k_t_colsum_fin, dim3(blocks_for(N)), dim3(256), 0, s, (const float *)g_split,
+                     chunks, out, N);
+}
 
 template <bool TA, bool TB, bool ACC>
 void t_gemm_go(const float *A, int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
@@ -734,8 +758,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       }
     } else {
       // s_0 = s* for every sequence
-      hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, w.des + d, nullptr, nullptr,
-                         (float *)A.gr->s_star, B, d, (int64_t)2 * d);
+      t_colsum(w.des + d, nullptr, nullptr, (float *)A.gr->s_star, B, d, (int64_t)2 * d, s);
     }
   }
 
@@ -752,19 +775,14 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
     t_gemm_go<true, false, false>(X(w.dhp, F), F, X(w.f, d), d, dw1(l), d, F, d, R, s);
     t_gemm_go<true, false, false>(X(w.dxf, d), d, X(w.h, F), F, dw2(l), F, d, F, R, s);
     // gains: dgamma[n] = sum_rows dy[n] * x[n] * r
-    hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, X(w.da, d), X(w.xin, d),
-                       at(w.r1, l, 0, 1), dg1(l), R, d, (int64_t)d);
-    hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, X(w.dc, d), X(w.x1, d),
-                       at(w.r2, l, 0, 1), dg2(l), R, d, (int64_t)d);
-    hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, X(w.df, d), X(w.x2, d),
-                       at(w.r3, l, 0, 1), dg3(l), R, d, (int64_t)d);
+    t_colsum(X(w.da, d), X(w.xin, d), at(w.r1, l, 0, 1), dg1(l), R, d, (int64_t)d, s);
+    t_colsum(X(w.dc, d), X(w.x1, d), at(w.r2, l, 0, 1), dg2(l), R, d, (int64_t)d, s);
+    t_colsum(X(w.df, d), X(w.x2, d), at(w.r3, l, 0, 1), dg3(l), R, d, (int64_t)d, s);
   }
   t_gemm_go<true, false, false>(w.dl, V, w.sn, d, (float *)A.gr->wout, d, V, d, R, s);
   t_gemm_go<true, false, false>(w.dz, d, w.es, 2 * d, (float *)A.gr->wg, 2 * d, d, 2 * d, R, s);
-  hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, w.dz, nullptr, nullptr,
-                     (float *)A.gr->bg, R, d, (int64_t)d);
-  hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(d)), dim3(256), 0, s, w.dsn, w.s, w.ro,
-                     (float *)A.gr->go, R, d, (int64_t)d);
+  t_colsum(w.dz, nullptr, nullptr, (float *)A.gr->bg, R, d, (int64_t)d, s);
+  t_colsum(w.dsn, w.s, w.ro, (float *)A.gr->go, R, d, (int64_t)d, s);
   return hipGetLastError();
 }
 }  // namespace
