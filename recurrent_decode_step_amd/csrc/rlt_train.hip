@@ -163,7 +163,7 @@ __global__ void k_t_norm_bwd(const float *__restrict__ x, const float *__restric
 // z (blockIdx.y) of `rows_per` rows sums its rows in order into part[z][n], then
 // k_t_colsum_fin adds the chunks in order.
 __global__ void k_t_colsum(const float *__restrict__ a, const float *__restrict__ b,
-                           const float *__restrict__ r, float *__restrict__ part, int M,
+                           const float *__restrict__ r, float *__restrict__ part, int M, int N,
                            int64_t ld, int rows_per) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
