@@ -441,28 +441,27 @@ unsigned blocks_for(size_t n, unsigned per = 256) { return (unsigned)((n + per -
 // Split-K scratch of the per-step products: parts * tiles <= kSplitTiles, each
 // tile 64 x 64, so the partial sums never exceed kSplitTiles * 4096 floats.
 constexpr int kSplitTiles = 256;
-thread_local float *g_split = nullptr;   // the calling thread's current workspace scratch
 
 // column sums through the split scratch: up to 64 chunks of rows
 void t_colsum(const float *a, const float *b, const float *r, float *out, int M, int N, int64_t ld,
-              hipStream_t s) {
+              hipStream_t s, float *split) {
   int chunks = std::max(1, std::min(64, M / 64));
   while (chunks > 1 && (size_t)chunks * N > (size_t)kSplitTiles * 4096) --chunks;
   const int rows_per = (M + chunks - 1) / chunks;
   chunks = (M + rows_per - 1) / rows_per;
-  hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(N), chunks), dim3(256), 0, s, a, b, r, g_split, M, N,
+  hipLaunchKernelGGL(k_t_colsum, dim3(blocks_for(N), chunks), dim3(256), 0, s, a, b, r, split, M, N,
                      ld, rows_per);
-  hipLaunchKernelGGL(k_t_colsum_fin, dim3(blocks_for(N)), dim3(256), 0, s, (const float *)g_split,
+  hipLaunchKernelGGL(k_t_colsum_fin, dim3(blocks_for(N)), dim3(256), 0, s, (const float *)split,
                      chunks, out, N);
 }
 
 template <bool TA, bool TB, bool ACC>
 void t_gemm_go(const float *A, int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
-               int M, int N, int K, hipStream_t s) {
+               int M, int N, int K, hipStream_t s, float *split) {
   if (M <= 0 || N <= 0) return;
   const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
   int parts = 1;
-  if (g_split && tiles < kSplitTiles / 2 && K >= 64) {
+  if (split && tiles < kSplitTiles / 2 && K >= 64) {
     parts = std::min(kSplitTiles / tiles, K / 32);
     parts = std::max(parts, 1);
   }
@@ -470,9 +469,9 @@ void t_gemm_go(const float *A, int64_t lda, const float *B, int64_t ldb, float *
     const int kpart = (((K + parts - 1) / parts) + 15) / 16 * 16;
     parts = (K + kpart - 1) / kpart;
     hipLaunchKernelGGL((k_t_gemm<TA, TB, false>), dim3((N + 63) / 64, (M + 63) / 64, parts),
-                       dim3(256), 0, s, A, lda, B, ldb, g_split, (int64_t)N, M, N, K, kpart);
+                       dim3(256), 0, s, A, lda, B, ldb, split, (int64_t)N, M, N, K, kpart);
     hipLaunchKernelGGL((k_t_reduce<ACC>), dim3(blocks_for((size_t)M * N)), dim3(256), 0, s,
-                       (const float *)g_split, parts, C, ldc, M, N);
+                       (const float *)split, parts, C, ldc, M, N);
     return;
   }
   if (K <= 0) {
@@ -597,7 +596,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
                          st(w.s, t - 1, d), (int64_t)d, es + d, (int64_t)2 * d, B, d);
     }
     float *gz = st(w.g, t, d);
-    t_gemm_go<false, true, false>(es, 2 * d, P_wg, 2 * d, gz, d, B, d, 2 * d, s);
+    t_gemm_go<false, true, false>(es, 2 * d, P_wg, 2 * d, gz, d, B, d, 2 * d, s, w.split);
     hipLaunchKernelGGL(k_t_merge_fwd, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, es, gz, P_bg,
                        w.u, B, d);
     const float *x = w.u;
@@ -608,9 +607,9 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       float *a = at(w.a, l, t, d), *r1 = at(w.r1, l, t, 1);
       norm_fwd(xin, g1(l), a, r1);
       float *q = at(w.q, l, t, d), *kh = at(w.kh, l, t, d), *vh = at(w.vh, l, t, d);
-      t_gemm_go<false, true, false>(a, d, wq(l), d, q, d, B, d, d, s);
-      t_gemm_go<false, true, false>(a, d, wk(l), d, kh, d, B, d, d, s);
-      t_gemm_go<false, true, false>(a, d, wv(l), d, vh, d, B, d, d, s);
+      t_gemm_go<false, true, false>(a, d, wq(l), d, q, d, B, d, d, s, w.split);
+      t_gemm_go<false, true, false>(a, d, wk(l), d, kh, d, B, d, d, s, w.split);
+      t_gemm_go<false, true, false>(a, d, wv(l), d, vh, d, B, d, d, s, w.split);
       TAttn ta{};
       ta.q = q; ta.ldq = d;
       ta.kb = at(w.kh, l, 0, d); ta.vb = at(w.vh, l, 0, d);
@@ -623,11 +622,11 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       float *x1 = at(w.x1, l, t, d);
       hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, xin, (int64_t)d,
                          x1, (int64_t)d, B, d);
-      t_gemm_go<false, true, true>(ta.o, d, wo(l), d, x1, d, B, d, d, s);
+      t_gemm_go<false, true, true>(ta.o, d, wo(l), d, x1, d, B, d, d, s, w.split);
       float *cc = at(w.c, l, t, d), *r2 = at(w.r2, l, t, 1);
       norm_fwd(x1, g2(l), cc, r2);
       float *qc = at(w.qc, l, t, d);
-      t_gemm_go<false, true, false>(cc, d, wqc(l), d, qc, d, B, d, d, s);
+      t_gemm_go<false, true, false>(cc, d, wqc(l), d, qc, d, B, d, d, s, w.split);
       const int grp = G == 1 ? 0 : l;
       TAttn tc{};
       tc.q = qc; tc.ldq = d;
@@ -641,17 +640,17 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       float *x2 = at(w.x2, l, t, d);
       hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, x1, (int64_t)d,
                          x2, (int64_t)d, B, d);
-      t_gemm_go<false, true, true>(tc.o, d, woc(l), d, x2, d, B, d, d, s);
+      t_gemm_go<false, true, true>(tc.o, d, woc(l), d, x2, d, B, d, d, s, w.split);
       float *ff = at(w.f, l, t, d), *r3 = at(w.r3, l, t, 1);
       norm_fwd(x2, g3(l), ff, r3);
       float *hpre = at(w.hpre, l, t, F), *hh = at(w.h, l, t, F);
-      t_gemm_go<false, true, false>(ff, d, w1(l), d, hpre, F, B, F, d, s);
+      t_gemm_go<false, true, false>(ff, d, w1(l), d, hpre, F, B, F, d, s, w.split);
       hipLaunchKernelGGL(k_t_gelu_fwd, dim3(blocks_for((size_t)B * F)), dim3(256), 0, s, hpre, hh,
                          (size_t)B * F);
       // x3 = x2 + W2 h, kept in u (the next layer's input)
       hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, x2, (int64_t)d,
                          w.u, (int64_t)d, B, d);
-      t_gemm_go<false, true, true>(hh, F, w2(l), F, w.u, d, B, d, F, s);
+      t_gemm_go<false, true, true>(hh, F, w2(l), F, w.u, d, B, d, F, s, w.split);
       x = w.u;
     }
     float *sv = st(w.s, t, d);
@@ -659,7 +658,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
                        (int64_t)d, B, d);
     float *sn = st(w.sn, t, d), *ro = st(w.ro, t, 1);
     norm_fwd(sv, (const float *)A.p->go, sn, ro);
-    t_gemm_go<false, true, false>(sn, d, (const float *)A.p->wout, d, w.logits, V, B, V, d, s);
+    t_gemm_go<false, true, false>(sn, d, (const float *)A.p->wout, d, w.logits, V, B, V, d, s, w.split);
     hipLaunchKernelGGL(k_t_ce, dim3((B + 3) / 4), dim3(256), 0, s, w.logits, A.tg + t, (int64_t)T,
                        st(w.dl, t, V), st(w.lossr, t, 1), B, V);
   }
@@ -672,7 +671,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
     const int chunk_start = A.chunk > 0 ? (t / A.chunk) * A.chunk : 0;
     // head: dsn = dlogits W_out; ds_t = carry + RMSNorm_o backward
     float *dsn = st(w.dsn, t, d);
-    t_gemm_go<false, false, false>(st(w.dl, t, V), V, (const float *)A.p->wout, d, dsn, d, B, d, V, s);
+    t_gemm_go<false, false, false>(st(w.dl, t, V), V, (const float *)A.p->wout, d, dsn, d, B, d, V, s, w.split);
     hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dscarry,
                        (int64_t)d, w.dx, (int64_t)d, B, d);
     norm_bwd(st(w.s, t, d), st(w.ro, t, 1), (const float *)A.p->go, dsn, w.dx, 1);
@@ -682,17 +681,17 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dx, (int64_t)d,
                          dxf, (int64_t)d, B, d);
       float *dhp = at(w.dhp, l, t, F);
-      t_gemm_go<false, false, false>(w.dx, d, w2(l), F, dhp, F, B, F, d, s);
+      t_gemm_go<false, false, false>(w.dx, d, w2(l), F, dhp, F, B, F, d, s, w.split);
       hipLaunchKernelGGL(k_t_gelu_bwd, dim3(blocks_for((size_t)B * F)), dim3(256), 0, s,
                          at(w.hpre, l, t, F), dhp, (size_t)B * F);
       float *df = at(w.df, l, t, d);
-      t_gemm_go<false, false, false>(dhp, F, w1(l), d, df, d, B, d, F, s);
+      t_gemm_go<false, false, false>(dhp, F, w1(l), d, df, d, B, d, F, s, w.split);
       norm_bwd(at(w.x2, l, t, d), at(w.r3, l, t, 1), g3(l), df, w.dx, 1);
       // cross: x2 = x1 + W_Oc attn(W_Qc c, memory), c = norm2(x1)
       float *dxoc = at(w.dxoc, l, t, d);
       hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dx, (int64_t)d,
                          dxoc, (int64_t)d, B, d);
-      t_gemm_go<false, false, false>(w.dx, d, woc(l), d, w.dtmp, d, B, d, d, s);   // d oc
+      t_gemm_go<false, false, false>(w.dx, d, woc(l), d, w.dtmp, d, B, d, d, s, w.split);   // d oc
       const int grp = G == 1 ? 0 : l;
       TAttn tc{};
       tc.q = at(w.qc, l, t, d); tc.ldq = d;
@@ -710,13 +709,13 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       tc.H = H; tc.dh = dh; tc.scale = scale;
       hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(256), 0, s, tc);
       float *dcc = at(w.dc, l, t, d);
-      t_gemm_go<false, false, false>(dqc, d, wqc(l), d, dcc, d, B, d, d, s);
+      t_gemm_go<false, false, false>(dqc, d, wqc(l), d, dcc, d, B, d, d, s, w.split);
       norm_bwd(at(w.x1, l, t, d), at(w.r2, l, t, 1), g2(l), dcc, w.dx, 1);
       // window self-attention: x1 = xin + W_O attn(q, K, V), q,k,v = W a, a = norm1(xin)
       float *dxo = at(w.dxo, l, t, d);
       hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dx, (int64_t)d,
                          dxo, (int64_t)d, B, d);
-      t_gemm_go<false, false, false>(w.dx, d, wo(l), d, w.dtmp, d, B, d, d, s);    // d o
+      t_gemm_go<false, false, false>(w.dx, d, wo(l), d, w.dtmp, d, B, d, d, s, w.split);    // d o
       TAttn ta{};
       ta.q = at(w.q, l, t, d); ta.ldq = d;
       ta.kb = at(w.kh, l, 0, d); ta.vb = at(w.vh, l, 0, d);
@@ -733,16 +732,16 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(256), 0, s, ta);
       // da = dq Wq + dk_t Wk + dv_t Wv (dk_t, dv_t complete: every later reader is done)
       float *daa = at(w.da, l, t, d);
-      t_gemm_go<false, false, false>(dq, d, wq(l), d, daa, d, B, d, d, s);
-      t_gemm_go<false, false, true>(at(w.dkh, l, t, d), d, wk(l), d, daa, d, B, d, d, s);
-      t_gemm_go<false, false, true>(at(w.dvh, l, t, d), d, wv(l), d, daa, d, B, d, d, s);
+      t_gemm_go<false, false, false>(dq, d, wq(l), d, daa, d, B, d, d, s, w.split);
+      t_gemm_go<false, false, true>(at(w.dkh, l, t, d), d, wk(l), d, daa, d, B, d, d, s, w.split);
+      t_gemm_go<false, false, true>(at(w.dvh, l, t, d), d, wv(l), d, daa, d, B, d, d, s, w.split);
       norm_bwd(at(w.xin, l, t, d), at(w.r1, l, t, 1), g1(l), daa, w.dx, 1);
     }
     // merge: u = g e + (1 - g) s_{t-1}, g = sigmoid(W_g [e ; s] + b_g)
     float *dz = st(w.dz, t, d);
     hipLaunchKernelGGL(k_t_merge_bwd, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, st(w.es, t, 2 * d),
                        st(w.g, t, d), w.dx, dz, w.des, B, d);
-    t_gemm_go<false, false, true>(dz, d, P_wg, 2 * d, w.des, 2 * d, B, 2 * d, d, s);
+    t_gemm_go<false, false, true>(dz, d, P_wg, 2 * d, w.des, 2 * d, B, 2 * d, d, s, w.split);
     if (A.de)
       hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.des,
                          (int64_t)2 * d, A.de + (size_t)t * d, (int64_t)T * d, B, d);
@@ -758,7 +757,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       }
     } else {
       // s_0 = s* for every sequence
-      t_colsum(w.des + d, nullptr, nullptr, (float *)A.gr->s_star, B, d, (int64_t)2 * d, s);
+      t_colsum(w.des + d, nullptr, nullptr, (float *)A.gr->s_star, B, d, (int64_t)2 * d, s, w.split);
     }
   }
 
@@ -766,23 +765,23 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
   const int R = (int)TB;
   for (int l = 0; l < L; ++l) {
     auto X = [&](float *base, size_t width) { return at(base, l, 0, width); };
-    t_gemm_go<true, false, false>(X(w.dq, d), d, X(w.a, d), d, dwq(l), d, d, d, R, s);
-    t_gemm_go<true, false, false>(X(w.dkh, d), d, X(w.a, d), d, dwk(l), d, d, d, R, s);
-    t_gemm_go<true, false, false>(X(w.dvh, d), d, X(w.a, d), d, dwv(l), d, d, d, R, s);
-    t_gemm_go<true, false, false>(X(w.dxo, d), d, X(w.o, d), d, dwo(l), d, d, d, R, s);
-    t_gemm_go<true, false, false>(X(w.dqc, d), d, X(w.c, d), d, dwqc(l), d, d, d, R, s);
-    t_gemm_go<true, false, false>(X(w.dxoc, d), d, X(w.oc, d), d, dwoc(l), d, d, d, R, s);
-    t_gemm_go<true, false, false>(X(w.dhp, F), F, X(w.f, d), d, dw1(l), d, F, d, R, s);
-    t_gemm_go<true, false, false>(X(w.dxf, d), d, X(w.h, F), F, dw2(l), F, d, F, R, s);
+    t_gemm_go<true, false, false>(X(w.dq, d), d, X(w.a, d), d, dwq(l), d, d, d, R, s, w.split);
+    t_gemm_go<true, false, false>(X(w.dkh, d), d, X(w.a, d), d, dwk(l), d, d, d, R, s, w.split);
+    t_gemm_go<true, false, false>(X(w.dvh, d), d, X(w.a, d), d, dwv(l), d, d, d, R, s, w.split);
+    t_gemm_go<true, false, false>(X(w.dxo, d), d, X(w.o, d), d, dwo(l), d, d, d, R, s, w.split);
+    t_gemm_go<true, false, false>(X(w.dqc, d), d, X(w.c, d), d, dwqc(l), d, d, d, R, s, w.split);
+    t_gemm_go<true, false, false>(X(w.dxoc, d), d, X(w.oc, d), d, dwoc(l), d, d, d, R, s, w.split);
+    t_gemm_go<true, false, false>(X(w.dhp, F), F, X(w.f, d), d, dw1(l), d, F, d, R, s, w.split);
+    t_gemm_go<true, false, false>(X(w.dxf, d), d, X(w.h, F), F, dw2(l), F, d, F, R, s, w.split);
     // gains: dgamma[n] = sum_rows dy[n] * x[n] * r
-    t_colsum(X(w.da, d), X(w.xin, d), at(w.r1, l, 0, 1), dg1(l), R, d, (int64_t)d, s);
-    t_colsum(X(w.dc, d), X(w.x1, d), at(w.r2, l, 0, 1), dg2(l), R, d, (int64_t)d, s);
-    t_colsum(X(w.df, d), X(w.x2, d), at(w.r3, l, 0, 1), dg3(l), R, d, (int64_t)d, s);
+    t_colsum(X(w.da, d), X(w.xin, d), at(w.r1, l, 0, 1), dg1(l), R, d, (int64_t)d, s, w.split);
+    t_colsum(X(w.dc, d), X(w.x1, d), at(w.r2, l, 0, 1), dg2(l), R, d, (int64_t)d, s, w.split);
+    t_colsum(X(w.df, d), X(w.x2, d), at(w.r3, l, 0, 1), dg3(l), R, d, (int64_t)d, s, w.split);
   }
-  t_gemm_go<true, false, false>(w.dl, V, w.sn, d, (float *)A.gr->wout, d, V, d, R, s);
-  t_gemm_go<true, false, false>(w.dz, d, w.es, 2 * d, (float *)A.gr->wg, 2 * d, d, 2 * d, R, s);
-  t_colsum(w.dz, nullptr, nullptr, (float *)A.gr->bg, R, d, (int64_t)d, s);
-  t_colsum(w.dsn, w.s, w.ro, (float *)A.gr->go, R, d, (int64_t)d, s);
+  t_gemm_go<true, false, false>(w.dl, V, w.sn, d, (float *)A.gr->wout, d, V, d, R, s, w.split);
+  t_gemm_go<true, false, false>(w.dz, d, w.es, 2 * d, (float *)A.gr->wg, 2 * d, d, 2 * d, R, s, w.split);
+  t_colsum(w.dz, nullptr, nullptr, (float *)A.gr->bg, R, d, (int64_t)d, s, w.split);
+  t_colsum(w.dsn, w.s, w.ro, (float *)A.gr->go, R, d, (int64_t)d, s, w.split);
   return hipGetLastError();
 }
 }  // namespace
@@ -795,10 +794,7 @@ size_t train_workspace_bytes(const rlt_config &c, int B, int T) {
 hipError_t launch_bptt(const TrainArgs &a, void *ws, hipStream_t s) {
   TrainWs w;
   train_layout(a.c, a.B, a.T, &w, ws);
-  g_split = w.split;
-  const hipError_t e = run_bptt(a, w, s);
-  g_split = nullptr;
-  return e;
+  return run_bptt(a, w, s);
 }
 
 }  // namespace rlt
