@@ -12,9 +12,10 @@
 // Kernels (one launch each on the caller's stream):
 //   k_enc_embed  token embedding rows into the fp32 residual stream
 //   k_enc_norm   RMSNorm of rows into the storage type
-//   k_pgemm32    token-parallel GEMM (bf16) on the 32x32x16 MFMA: 128 tokens x
-//                256 features per workgroup, both operands staged through LDS
-//                in fragment order (k_pgemm: the fp32 form on 16x16x4),
+//   k_pgemm32d   token-parallel GEMM (bf16) on the 32x32x16 MFMA: 128 tokens x
+//                256 features per workgroup, both operands loaded straight
+//                into LDS in fragment order (k_pgemm32: the register-staged
+//                form; k_pgemm: the fp32 form on 16x16x4),
 //                fused epilogues (q + encoder-cache append, residual add,
 //                GELU, memory K/V append)
 //   k_fattn32    causal flash attention over the encoder cache (bf16): 128
@@ -286,18 +287,20 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm(PGemmArgs a, int m
 // keep their packed 16-row layout in memory and are moved to the 32-row layout
 // when written to LDS: piece (16-row tile t, lane r16 + 16 g) goes to 32-row
 // block t / 2, k-half g / 2, lane (t % 2) * 16 + r16 + 32 (g % 2).
-template <int RB_, int FB_, int WM_, int WN_, int NBUF_, int WPE_, int GROUP_ = 4, int PD_ = 1>
+template <int RB_, int FB_, int WM_, int WN_, int NBUF_, int WPE_, int GROUP_ = 4, int PD_ = 1,
+          bool DIRECT_ = false>
 struct Pg32Cfg {
   static constexpr int RB = RB_, FB = FB_, WM = WM_, WN = WN_, NBUF = NBUF_, WPE = WPE_;
   static constexpr int GROUP = GROUP_;
   static constexpr int PD = PD_;       // stages in flight ahead of the one multiplied out
+  static constexpr bool DIRECT = DIRECT_;   // direct-to-LDS loads (k_pgemm32d; NBUF = 3)
   static constexpr int THREADS = 64 * WM * WN;
   static constexpr int LDS = NBUF * (RB + FB) * 2 * 64 * 16;   // bytes
   static_assert(LDS >= WM * WN * 32 * 36 * 4, "epilogue scratch fits in the staging buffers");
 };
-// 128 tokens x 256 features, double-buffered, two stages in flight, two
-// workgroups per CU
-using Pg32Default = Pg32Cfg<4, 8, 2, 2, 2, 2, 8, 2>;
+// 128 tokens x 256 features, direct-to-LDS loads into three stages (two in
+// flight), two workgroups per CU
+using Pg32Default = Pg32Cfg<4, 8, 2, 2, 3, 2, 8, 2, true>;
 
 template <int EPI, class C>
 __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32(PGemmArgs a, int mt, int nt) {
@@ -447,6 +450,163 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32(PGemmArgs a, int
   // padded scratch [token][feature] and reads it back by rows, so a store
   // instruction covers 8 token rows x 32 consecutive features.
   constexpr int EROW = 36;                           // padded row, floats
+  float *scr = reinterpret_cast<float *>(smem) + wave * 32 * EROW;
+#pragma unroll
+  for (int f = 0; f < WFB; ++f) {
+    const int fblk = (tile0 / 2 + wn * WFB + f) * 32;
+#pragma unroll
+    for (int r = 0; r < WRB; ++r) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4 *>(scr + (lane & 31) * EROW + 8 * q + 4 * (lane >> 5)) =
+            f32x4{acc[f][r][4 * q], acc[f][r][4 * q + 1], acc[f][r][4 * q + 2], acc[f][r][4 * q + 3]};
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int tblk = row0 + (wm * WRB + r) * 32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(scr + tr * EROW + fc);
+        const int row = tblk + tr, n = fblk + fc;
+        if (row < n_rows && n < a.N) pgemm_store<bf16_t, EPI>(a, row, n, v);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
+// Direct-to-LDS form of k_pgemm32: every 16-byte piece is loaded by
+// global_load_lds straight into its final place of the 32-row fragment layout
+// (the weight pieces' move from the packed 16-row layout is done by each
+// lane's global address), three LDS stages, two in flight while the third is
+// multiplied out.  Waits are explicit: a stage is used after its wavefront's
+// loads have counted down (s_waitcnt vmcnt) and a barrier; a buffer is
+// refilled only after the barrier that ends its products.  Out-of-range rows
+// and weight tiles are read from clamped addresses; their products only reach
+// outputs that are never stored.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt: vmcnt low 4 bits and high 2 bits (15:14); expcnt and lgkmcnt left at no-wait
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070 | 0x0F00);
+#endif
+}
+
+template <int EPI, class C>
+__global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, int mt, int nt) {
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  constexpr int NW = C::WM * C::WN;
+  constexpr int FA = 2 * C::RB, FW = 2 * C::FB;
+  constexpr int FS = FA + FW;                               // fragments per stage
+  constexpr int FPW = FS / NW;
+  constexpr int WRB = C::RB / C::WM, WFB = C::FB / C::WN;
+  static_assert(FS % NW == 0 && FA % NW == 0, "staging split");
+  extern __shared__ u32x4 smem[];                           // [3][FS * 64]
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int total = mt * nt;
+  const int id = blockIdx.x;
+  int tm, tn;
+  if constexpr (C::GROUP > 0) {
+    const int v = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;
+    const int grp = v / (C::GROUP * nt);
+    const int m0 = grp * C::GROUP;
+    const int gm = min(C::GROUP, mt - m0);
+    const int w = v - grp * C::GROUP * nt;
+    tm = m0 + w % gm;
+    tn = w / gm;
+  } else {
+    tm = id / nt;
+    tn = id - tm * nt;
+  }
+  const int row0 = tm * C::RB * 32, tile0 = tn * C::FB * 2;
+  const int ntiles = a.Np >> 4;
+  const int n_rows = a.rows.n_rows;
+  const u32x4 *wp = static_cast<const u32x4 *>(a.wp);
+  const bf16_t *ap = static_cast<const bf16_t *>(a.a);
+
+  // per-lane global addresses of this wavefront's pieces, advanced by one k-step per stage
+  const u32x4 *src[FPW];
+  int64_t step[FPW];
+#pragma unroll
+  for (int u = 0; u < FPW; ++u) {
+    const int f = wave + NW * u;
+    if (u < FA / NW) {
+      const int row = min(row0 + (f >> 1) * 32 + (lane & 31), n_rows - 1);
+      src[u] = reinterpret_cast<const u32x4 *>(ap + (size_t)row * a.lda + (f & 1) * 16 + (lane >> 5) * 8);
+      step[u] = 32 * sizeof(bf16_t) / 16;                  // 32 k of bf16, in 16-byte units
+    } else {
+      const int g = f - FA, fb = g >> 1, j = g & 1;
+      const int tile = min(tile0 + 2 * fb + ((lane & 31) >> 4), ntiles - 1);
+      src[u] = wp + (size_t)tile * a.KT * 64 + (lane & 15) + 16 * (2 * j + (lane >> 5));
+      step[u] = 64;                                         // next packed k-step
+    }
+  }
+  auto issue = [&](int st, int buf) {
+#pragma unroll
+    for (int u = 0; u < FPW; ++u) {
+      const int f = wave + NW * u;
+#if __HIP_DEVICE_COMPILE__   // the host pass never runs kernel bodies
+      __builtin_amdgcn_global_load_lds(src[u] + st * step[u],
+                                       (lds_void *)&smem[(buf * FS + f) * 64], 16, 0, 0);
+#endif
+    }
+  };
+
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  f32x16 acc[WFB][WRB];
+#pragma unroll
+  for (int f = 0; f < WFB; ++f)
+#pragma unroll
+    for (int r = 0; r < WRB; ++r)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[f][r][e] = 0.f;
+
+  u32x4 wf[2][WFB], af[2][WRB];
+  auto frags = [&](int buf, int j, int set) {
+#pragma unroll
+    for (int f = 0; f < WFB; ++f) wf[set][f] = smem[(buf * FS + FA + (wn * WFB + f) * 2 + j) * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < WRB; ++r) af[set][r] = smem[(buf * FS + (wm * WRB + r) * 2 + j) * 64 + lane];
+  };
+  auto mult = [&](int buf) {
+    frags(buf, 0, 0);
+    frags(buf, 1, 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int f = 0; f < WFB; ++f)
+#pragma unroll
+        for (int r = 0; r < WRB; ++r)
+          acc[f][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, wf[j][f]), __builtin_bit_cast(bf16x8, af[j][r]),
+              acc[f][r], 0, 0, 0);
+  };
+
+  const int S = a.KT;
+  issue(0, 0);
+  if (S > 1) issue(1, 1);
+  for (int st = 0; st < S; ++st) {
+    const int buf = st % 3;
+    const bool more2 = st + 2 < S;
+    if (more2) issue(st + 2, (st + 2) % 3);
+    // loads issued after this stage's: stages st+1 and st+2 that exist
+    if (more2) wait_vmcnt<2 * FPW>();
+    else if (st + 1 < S) wait_vmcnt<FPW>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    mult(buf);
+    __builtin_amdgcn_s_barrier();
+  }
+
+  // epilogue through LDS, as in k_pgemm32 (every load has landed: the last wait was 0)
+  constexpr int EROW = 36;
   float *scr = reinterpret_cast<float *>(smem) + wave * 32 * EROW;
 #pragma unroll
   for (int f = 0; f < WFB; ++f) {
@@ -917,13 +1077,24 @@ template <int EPI, class C>
 hipError_t pgemm32_go(const PGemmArgs &a, hipStream_t s) {
   const int mt = (a.rows.n_rows + C::RB * 32 - 1) / (C::RB * 32);
   const int nt = ((a.Np >> 5) + C::FB - 1) / C::FB;
-  if (C::LDS > 65536) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&k_pgemm32<EPI, C>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (attr != hipSuccess) return attr;
+  if constexpr (C::DIRECT) {
+    if constexpr (C::LDS > 65536) {
+      // more LDS than the static limit: allow it once per instantiation
+      static const hipError_t attr = hipFuncSetAttribute(
+          reinterpret_cast<const void *>(&k_pgemm32d<EPI, C>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+      if (attr != hipSuccess) return attr;
+    }
+    hipLaunchKernelGGL((k_pgemm32d<EPI, C>), dim3(mt * nt), dim3(C::THREADS), C::LDS, s, a, mt, nt);
+  } else {
+    if constexpr (C::LDS > 65536) {
+      static const hipError_t attr = hipFuncSetAttribute(
+          reinterpret_cast<const void *>(&k_pgemm32<EPI, C>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+      if (attr != hipSuccess) return attr;
+    }
+    hipLaunchKernelGGL((k_pgemm32<EPI, C>), dim3(mt * nt), dim3(C::THREADS), C::LDS, s, a, mt, nt);
   }
-  hipLaunchKernelGGL((k_pgemm32<EPI, C>), dim3(mt * nt), dim3(C::THREADS), C::LDS, s, a, mt, nt);
   return hipGetLastError();
 }
 
