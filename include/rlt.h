@@ -88,7 +88,7 @@ enum { RLT_LOGITS_ALL = 0, RLT_LOGITS_LAST = 1, RLT_LOGITS_NONE = 2 };
  * current token.  attn_chunk: positions an attention workgroup loads per step
  * of its double-buffered loop, spread over its 4 wavefronts, each of which
  * keeps its own running softmax (0 = the largest the kernel takes for the
- * head size: 128 positions for bf16 with head_dim 128; larger values are cut
+ * head size: 64 positions for bf16 with head_dim 128; larger values are cut
  * to that).  It fixes the order of the softmax sums and so is part of the
  * model's numerics: a state and its model must agree on it. */
 typedef struct {

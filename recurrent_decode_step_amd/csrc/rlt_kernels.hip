@@ -617,6 +617,11 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
 // own online softmax (running max, sum, weighted values) in base 2 with no
 // barrier until the end, where the 4 are combined in wavefront order.  K and V
 // of the next chunk are loaded while the current one is processed.
+// Every wavefront load moves 1 KiB whatever dh is; four loads per tensor and
+// chunk (8 KiB per wavefront and buffer) keep enough bytes in flight and
+// measured faster at dh = 128 than eight.  K and V are read once per step, so
+// the loads are non-temporal (they do not displace the weights and
+// activations that the GEMMs reuse from L2), which measured 7-10% faster.
 template <typename T, int DH, int UU = 0>
 struct AttnShape {
   static constexpr int EPL = Num<T>::EPL;
@@ -624,7 +629,7 @@ struct AttnShape {
   static constexpr int RPW = 64 / LPR;             // positions per wavefront load
   static constexpr int RPB = 4 * RPW;              // positions per workgroup load
   // loads per lane and tensor per chunk
-  static constexpr int U = UU > 0 ? UU : ((RPW >= 16) ? 4 : 8);
+  static constexpr int U = UU > 0 ? UU : 4;
   static constexpr int CH = U * RPB;               // positions per chunk
 };
 
@@ -666,8 +671,8 @@ __device__ __forceinline__ void attn_load(const T *kp, const T *vp, int64_t s_po
     const T *vq = vp + (size_t)(base + my) * s_pos;
 #pragma unroll
     for (int u = 0; u < S::U; ++u) {
-      kr[u] = *reinterpret_cast<const u32x4 *>(kq);
-      vr[u] = *reinterpret_cast<const u32x4 *>(vq);
+      kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kq));
+      vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vq));
       kq += step;
       vq += step;
     }
@@ -676,8 +681,8 @@ __device__ __forceinline__ void attn_load(const T *kp, const T *vp, int64_t s_po
     for (int u = 0; u < S::U; ++u) {
       const int pc = min(u * S::RPB + my, ch - 1);
       const int p = min(base + pc, len - 1);
-      kr[u] = *reinterpret_cast<const u32x4 *>(kp + (size_t)p * s_pos);
-      vr[u] = *reinterpret_cast<const u32x4 *>(vp + (size_t)p * s_pos);
+      kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + (size_t)p * s_pos));
+      vr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + (size_t)p * s_pos));
     }
   }
 }
