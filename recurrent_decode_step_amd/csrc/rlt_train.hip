@@ -21,7 +21,7 @@
 // Weight gradients are formed at the end as one GEMM per matrix over all T*B
 // rows.  Every reduction runs in a fixed order: results do not depend on the
 // launch shape.
-#include "rlt_internal.h"
+#include "rlt_device.h"
 
 #include <math.h>
 
@@ -98,6 +98,160 @@ __global__ __launch_bounds__(256) void k_t_gemm(const float *__restrict__ A, int
       if (n >= N) continue;
       float *c = C + (size_t)m * ldc + n;
       *c = ACC ? *c + acc[i][j] : acc[i][j];
+    }
+  }
+}
+
+// Per-step products on the 16x16x4 fp32 MFMA, one launch and no split
+// scratch: C[m][n] (+)= sum_k A[m][k] B(k, n), A row-major [M][K],
+// B(k, n) = TB ? B[n * ldb + k] : B[k * ldb + n], K a multiple of 16.  A
+// workgroup of kSgWaves wavefronts computes a 16 x 32 tile; K is cut into
+// kSgWaves consecutive parts of 16-k chunks, one per wavefront, each an MFMA
+// chain over its chunks in order (lane l holds row / column l & 15 and
+// k = 4 (l >> 4) .. +3 of a chunk in both operands, so the four MFMAs of a
+// chunk pair the same k), and the partial tiles are added in wavefront order
+// through LDS.  Rows and columns past M, N read clamped addresses and are
+// never stored.
+constexpr int kSgWaves = 8;
+template <bool TB, bool ACC>
+__global__ __launch_bounds__(kSgWaves * 64) void k_t_sgemm(const float *__restrict__ A, int64_t lda,
+                                                           const float *__restrict__ B, int64_t ldb,
+                                                           float *__restrict__ C, int64_t ldc, int M,
+                                                           int N, int K) {
+  __shared__ f32x4 part[kSgWaves][2][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.y * 16, n0 = blockIdx.x * 32;
+  const int li = lane & 15, g = lane >> 4;
+  const int chunks = K >> 4;
+  const int c_beg = (wave * chunks) / kSgWaves, c_end = ((wave + 1) * chunks) / kSgWaves;
+  const float *ap = A + (size_t)min(m0 + li, M - 1) * lda + 4 * g;
+  const int nA = min(n0 + li, N - 1), nB = min(n0 + 16 + li, N - 1);
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  constexpr int PB = 8;                            // chunks whose loads are in flight together
+  for (int c0 = c_beg; c0 < c_end; c0 += PB) {
+    u32x4 av[PB], b0[PB], b1[PB];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int c = min(c0 + u, c_end - 1);
+      const int k = c * 16 + 4 * g;
+      av[u] = *reinterpret_cast<const u32x4 *>(ap + (size_t)c * 16);
+      if constexpr (TB) {
+        b0[u] = *reinterpret_cast<const u32x4 *>(B + (size_t)nA * ldb + k);
+        b1[u] = *reinterpret_cast<const u32x4 *>(B + (size_t)nB * ldb + k);
+      } else {
+        const float *bp = B + (size_t)k * ldb;
+        b0[u] = u32x4{__float_as_uint(bp[nA]), __float_as_uint(bp[ldb + nA]),
+                      __float_as_uint(bp[2 * ldb + nA]), __float_as_uint(bp[3 * ldb + nA])};
+        b1[u] = u32x4{__float_as_uint(bp[nB]), __float_as_uint(bp[ldb + nB]),
+                      __float_as_uint(bp[2 * ldb + nB]), __float_as_uint(bp[3 * ldb + nB])};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      if (c0 + u < c_end) {
+        acc0 = mma_step(av[u], b0[u], acc0, 0.f);
+        acc1 = mma_step(av[u], b1[u], acc1, 0.f);
+      }
+    }
+  }
+  part[wave][0][lane] = acc0;
+  part[wave][1][lane] = acc1;
+  __syncthreads();
+  if (wave < 2) {
+    f32x4 v = part[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < kSgWaves; ++w) v += part[w][wave][lane];
+    // lane l, element r: row 4 (l >> 4) + r, column l & 15 of the 16 x 16 half
+    const int n = n0 + wave * 16 + li, mb = m0 + 4 * g;
+    if (n < N) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (mb + r < M) {
+          float *c = C + (size_t)(mb + r) * ldc + n;
+          *c = ACC ? *c + v[r] : v[r];
+        }
+      }
+    }
+  }
+}
+
+// Weight gradients on the 16x16x4 fp32 MFMA: C[m][n] (+)= sum_k A[k][m] B[k][n]
+// over the rows k of a whole call (A [K][lda], B [K][ldb], row-major).  A
+// workgroup of kWgWaves wavefronts computes a 32 x 32 tile (2 x 2 MFMA tiles);
+// K is cut into kWgWaves consecutive parts of 16-k chunks, one per wavefront,
+// each an MFMA chain over its chunks in order (MFMA i of a chunk takes
+// k = 16 c + 4 (l >> 4) + i on lane l, whose row / column is l & 15), and the
+// partial tiles are added in wavefront order through LDS.  Rows k past K add
+// zero; rows and columns past M, N read clamped addresses and are not stored.
+constexpr int kWgWaves = 8;
+template <bool ACC>
+__global__ __launch_bounds__(kWgWaves * 64) void k_t_wgemm(const float *__restrict__ A, int64_t lda,
+                                                           const float *__restrict__ B, int64_t ldb,
+                                                           float *__restrict__ C, int64_t ldc, int M,
+                                                           int N, int K) {
+  __shared__ f32x4 part[kWgWaves][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  const int li = lane & 15, g = lane >> 4;
+  const int chunks = (K + 15) >> 4;
+  const int c_beg = (wave * chunks) / kWgWaves, c_end = ((wave + 1) * chunks) / kWgWaves;
+  const int ma = min(m0 + li, M - 1), mb = min(m0 + 16 + li, M - 1);
+  const int na = min(n0 + li, N - 1), nb = min(n0 + 16 + li, N - 1);
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int PB = 8;                            // chunks whose loads are in flight together
+  for (int c0 = c_beg; c0 < c_end; c0 += PB) {
+    float a0[PB][4], a1[PB][4], b0[PB][4], b1[PB][4];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int c = min(c0 + u, c_end - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = c * 16 + 4 * g + i;
+        const bool in = k < K;
+        const float *ar = A + (size_t)min(k, K - 1) * lda;
+        const float *br = B + (size_t)min(k, K - 1) * ldb;
+        a0[u][i] = in ? ar[ma] : 0.f;
+        a1[u][i] = in ? ar[mb] : 0.f;
+        b0[u][i] = in ? br[na] : 0.f;
+        b1[u][i] = in ? br[nb] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      if (c0 + u < c_end) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[u][i], b0[u][i], acc[0][0], 0, 0, 0);
+          acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[u][i], b1[u][i], acc[0][1], 0, 0, 0);
+          acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[u][i], b0[u][i], acc[1][0], 0, 0, 0);
+          acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[u][i], b1[u][i], acc[1][1], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) part[wave][2 * i + j][lane] = acc[i][j];
+  __syncthreads();
+  if (wave < 4) {
+    f32x4 v = part[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < kWgWaves; ++w) v += part[w][wave][lane];
+    // lane l, element r: row 4 (l >> 4) + r, column l & 15 of the 16 x 16 tile
+    const int mt = m0 + 16 * (wave >> 1) + 4 * g, n = n0 + 16 * (wave & 1) + li;
+    if (n < N) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (mt + r < M) {
+          float *c = C + (size_t)(mt + r) * ldc + n;
+          *c = ACC ? *c + v[r] : v[r];
+        }
+      }
     }
   }
 }
@@ -225,9 +379,22 @@ __device__ __forceinline__ float t_block_sum(float v, float *red) {
   return r;
 }
 
-// 4 wavefronts per (row, head): positions spread over all 256 threads for the
-// scores; each wavefront then sums a quarter of the positions per channel, and
-// the four partial sums are added in wavefront order.
+// Dot products of one position's dh channels with one or two vectors, on the
+// 16 lanes of a lane group: lane `sub` takes channels sub, sub + 16, ... in
+// order (coalesced 64-byte reads), then the 16 partial sums meet in a fixed
+// butterfly.  Every lane of the group ends with the sums.
+__device__ __forceinline__ float t_group_sum16(float v) {
+  v += __shfl_xor(v, 8);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 1);
+  return v;
+}
+
+// 4 wavefronts per (row, head): scores with 16 lanes per position (16
+// positions per pass of the workgroup); each wavefront then sums a quarter of
+// the positions per channel, and the four partial sums are added in
+// wavefront order.
 __global__ __launch_bounds__(256) void k_t_attn_fwd(TAttn a) {
   __shared__ float sc[kTMaxPos];
   __shared__ float red[4];
@@ -238,16 +405,23 @@ __global__ __launch_bounds__(256) void k_t_attn_fwd(TAttn a) {
   const float *q = a.q + (size_t)b * a.ldq + h * a.dh;
   const float *K = a.kb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
   const float *V = a.vb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
+  const int sub = lane & 15, grp = wave * 4 + (lane >> 4);
   float mx = -INFINITY;
-  for (int j = tid; j < n; j += 256) {
-    const float *k = K + (size_t)(lo + j) * a.s_pos;
+  for (int j0 = 0; j0 < n; j0 += 16) {
+    const int j = j0 + grp;
     float s = 0.f;
-    for (int c = 0; c < a.dh; ++c) s = fmaf(q[c], k[c], s);
-    s *= a.scale;
-    sc[j] = s;
-    mx = fmaxf(mx, s);
+    if (j < n) {
+      const float *k = K + (size_t)(lo + j) * a.s_pos;
+      for (int c = sub; c < a.dh; c += 16) s = fmaf(q[c], k[c], s);
+    }
+    s = t_group_sum16(s);
+    if (j < n) {
+      s *= a.scale;
+      if (sub == 0) sc[j] = s;
+      mx = fmaxf(mx, s);
+    }
   }
-  mx = t_block_max(mx, red);
+  mx = t_block_max(mx, red);     // also orders the score writes before their reads
   float sum = 0.f;
   for (int j = tid; j < n; j += 256) {
     const float p = expf(sc[j] - mx);
@@ -294,17 +468,26 @@ __global__ __launch_bounds__(256) void k_t_attn_bwd(TAttn a) {
   float D = 0.f;
   for (int c = tid; c < a.dh; c += 256) D = fmaf(dout[c], o[c], D);
   D = t_block_sum(D, red);
-  for (int j = tid; j < n; j += 256) {
-    const float *k = K + (size_t)(lo + j) * a.s_pos;
-    const float *v = V + (size_t)(lo + j) * a.s_pos;
+  // scores and dp = do . v_j with 16 lanes per position
+  const int sub = lane & 15, grp = wave * 4 + (lane >> 4);
+  for (int j0 = 0; j0 < n; j0 += 16) {
+    const int j = j0 + grp;
     float s = 0.f, dp = 0.f;
-    for (int c = 0; c < a.dh; ++c) {
-      s = fmaf(q[c], k[c], s);
-      dp = fmaf(dout[c], v[c], dp);
+    if (j < n) {
+      const float *k = K + (size_t)(lo + j) * a.s_pos;
+      const float *v = V + (size_t)(lo + j) * a.s_pos;
+      for (int c = sub; c < a.dh; c += 16) {
+        s = fmaf(q[c], k[c], s);
+        dp = fmaf(dout[c], v[c], dp);
+      }
     }
-    const float p = expf(s * a.scale - mx) * inv;
-    sp[j] = p;
-    sds[j] = p * (dp - D);
+    s = t_group_sum16(s);
+    dp = t_group_sum16(dp);
+    if (j < n && sub == 0) {
+      const float p = expf(s * a.scale - mx) * inv;
+      sp[j] = p;
+      sds[j] = p * (dp - D);
+    }
   }
   __syncthreads();
   // dq: each wavefront sums a quarter of the positions, added in wavefront order
@@ -455,10 +638,25 @@ void t_colsum(const float *a, const float *b, const float *r, float *out, int M,
                      chunks, out, N);
 }
 
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
 template <bool TA, bool TB, bool ACC>
 void t_gemm_go(const float *A, int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
                int M, int N, int K, hipStream_t s, float *split) {
   if (M <= 0 || N <= 0) return;
+  // per-step products (A not transposed) with 16-byte aligned rows: the MFMA form
+  if (!TA && K >= 16 && K % 16 == 0 && lda % 4 == 0 && aligned16(A) &&
+      (!TB || (ldb % 4 == 0 && aligned16(B)))) {
+    hipLaunchKernelGGL((k_t_sgemm<TB, ACC>), dim3((N + 31) / 32, (M + 15) / 16), dim3(kSgWaves * 64),
+                       0, s, A, lda, B, ldb, C, ldc, M, N, K);
+    return;
+  }
+  // weight gradients (sums over the rows of the call): the MFMA form
+  if (TA && !TB && K >= 1) {
+    hipLaunchKernelGGL((k_t_wgemm<ACC>), dim3((N + 31) / 32, (M + 31) / 32), dim3(kWgWaves * 64), 0,
+                       s, A, lda, B, ldb, C, ldc, M, N, K);
+    return;
+  }
   const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
   int parts = 1;
   if (split && tiles < kSplitTiles / 2 && K >= 64) {

@@ -132,6 +132,40 @@ def test_encode_chunks_and_batches_are_bitwise_invariant():
     assert torch.equal(mk3[:, 3, :, :T], mk[:, 3, :, :T])
 
 
+def test_large_call_matches_per_sequence_calls_bitwise():
+    """17100 token rows in one call (134 row tiles, the last one ragged; 384
+    QKV features, so a ragged feature tile too) against the same prompts
+    encoded one sequence at a time in two chunks: every e row, memory row and
+    cache entry agrees bitwise, and one sequence's first rows agree with the
+    bf16 oracle."""
+    cfg = ModelConfig(vocab=120, d_model=128, n_heads=4, n_layers=2, d_ffn=256, window=8,
+                      mem_groups=2, dtype=1)
+    B, T = 9, 1900
+    say(f"[encoder large call] B={B} T={T} rows={B * T}")
+    params, eparams, model, enc, es, mk, mv = setup(cfg, B, T, B * T)
+    tok = torch.from_numpy(synth.token_ids(B, T, cfg.vocab, index=8)).to(DEV)
+    e_all = binding.rlt_encode(enc, es, tok, (mk, mv))
+    es2 = binding.EncoderState(enc, B, T, T)
+    mk2, mv2 = torch.zeros_like(mk), torch.zeros_like(mv)
+    rows = []
+    for b in range(B):
+        a = binding.rlt_encode(enc, es2, tok[b:b + 1, :700].contiguous(), (mk2, mv2), slots=[b])
+        c = binding.rlt_encode(enc, es2, tok[b:b + 1, 700:].contiguous(), (mk2, mv2), slots=[b])
+        rows.append(torch.cat([a, c], dim=1))
+    torch.cuda.synchronize()
+    assert torch.isfinite(e_all).all()
+    assert torch.equal(torch.cat(rows, dim=0), e_all)
+    assert torch.equal(mk, mk2) and torch.equal(mv, mv2)
+    k1, v1 = es.cache()
+    k2, v2 = es2.cache()
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    P = 24
+    oe = oracle_encoder(cfg, params, eparams, "bf16")
+    r = oracle.encode(oe, tok.cpu().numpy()[5, :P])
+    rel = rel_l2(f64(e_all[5, :P]), r["e"])
+    say(f"[encoder large call] bitwise ok; seq 5 e[:{P}] rel-L2 {rel:.2e}")
+    assert rel <= 2e-2
+
 def test_encode_bf16_matches_oracle():
     """bf16 storage (the bf16-emulating oracle): dh = 128, 64 and 256, two groups."""
     for d, H, G in ((256, 2, 1), (256, 4, 2), (512, 2, 1)):
