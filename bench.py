@@ -851,7 +851,7 @@ def run_train(args):
         "config": {"workload": SMALL.name.replace("bf16", "f32") + ", BPTT over 128 steps",
                    "batch": B, "steps_per_sequence": T, "loss": "next-token cross-entropy, all targets",
                    "gradients": "every parameter, e and memory; full BPTT"},
-        "roofline": {"bound": "alu", "kernel": "whole rlt_bptt call (fp32 VALU GEMMs and attention)",
+        "roofline": {"bound": "mfma", "kernel": "whole rlt_bptt call (fp32 MFMA GEMMs, VALU attention)",
                      "achieved": round(total / (ms / 1e3) / 1e12, 2), "peak": 157.3,
                      "unit": "TFLOP/s", "frac": round(total / (ms / 1e3) / 157.3e12, 4),
                      "traffic": None, "gemm_flops": gemm_flops, "attention_flops": attn_flops},
