@@ -103,29 +103,41 @@ __global__ __launch_bounds__(256) void k_t_gemm(const float *__restrict__ A, int
 }
 
 // Per-step products on the 16x16x4 fp32 MFMA, one launch and no split
-// scratch: C[m][n] (+)= sum_k A[m][k] B(k, n), A row-major [M][K],
-// B(k, n) = TB ? B[n * ldb + k] : B[k * ldb + n], K a multiple of 16.  A
-// workgroup of kSgWaves wavefronts computes a 16 x 32 tile; K is cut into
-// kSgWaves consecutive parts of 16-k chunks, one per wavefront, each an MFMA
-// chain over its chunks in order (lane l holds row / column l & 15 and
-// k = 4 (l >> 4) .. +3 of a chunk in both operands, so the four MFMAs of a
-// chunk pair the same k), and the partial tiles are added in wavefront order
-// through LDS.  Rows and columns past M, N read clamped addresses and are
-// never stored.
+// scratch.  Output o = blockIdx.z:
+//   C_o[m][n] = (R ? R[m][n] : ACC ? C_o[m][n] : 0) + sum_s sum_k A_s[m][k] B_s(k, n)
+// over nseg segments s (each K long, K a multiple of 16), A_s row-major
+// [M][K] (lda), B_s(k, n) = TB ? B_s[n * ldb + k] : B_s[k * ldb + n].  With
+// several outputs there is one segment, A shared and B, C per output; with
+// several segments, one output.  A workgroup of kSgWaves wavefronts computes a
+// 16 x 32 tile; the nseg * K / 16 chunks (segments in order, k in order
+// within each) are cut into kSgWaves consecutive parts, one per wavefront,
+// each an MFMA chain over its chunks in order (lane l holds row / column
+// l & 15 and k = 4 (l >> 4) .. +3 of a chunk in both operands, so the four
+// MFMAs of a chunk pair the same k), and the partial tiles are added in
+// wavefront order through LDS.  Rows and columns past M, N read clamped
+// addresses and are never stored.
 constexpr int kSgWaves = 8;
+struct SgArgs {
+  const float *A[3];
+  const float *B[3];
+  float *C[3];
+  int nseg;
+  const float *R;                     // residual input added to the sum (or null)
+  int64_t lda, ldb, ldc, ldr;
+  int M, N, K;
+};
 template <bool TB, bool ACC>
-__global__ __launch_bounds__(kSgWaves * 64) void k_t_sgemm(const float *__restrict__ A, int64_t lda,
-                                                           const float *__restrict__ B, int64_t ldb,
-                                                           float *__restrict__ C, int64_t ldc, int M,
-                                                           int N, int K) {
+__global__ __launch_bounds__(kSgWaves * 64) void k_t_sgemm(const SgArgs a) {
   __shared__ f32x4 part[kSgWaves][2][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int o = blockIdx.z;
   const int m0 = blockIdx.y * 16, n0 = blockIdx.x * 32;
   const int li = lane & 15, g = lane >> 4;
-  const int chunks = K >> 4;
+  const int cps = a.K >> 4, chunks = cps * a.nseg;
   const int c_beg = (wave * chunks) / kSgWaves, c_end = ((wave + 1) * chunks) / kSgWaves;
-  const float *ap = A + (size_t)min(m0 + li, M - 1) * lda + 4 * g;
-  const int nA = min(n0 + li, N - 1), nB = min(n0 + 16 + li, N - 1);
+  const size_t arow = (size_t)min(m0 + li, a.M - 1) * a.lda + 4 * g;
+  const int nA = min(n0 + li, a.N - 1), nB = min(n0 + 16 + li, a.N - 1);
+  const int64_t ldb = a.ldb;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
   constexpr int PB = 8;                            // chunks whose loads are in flight together
   for (int c0 = c_beg; c0 < c_end; c0 += PB) {
@@ -133,13 +145,16 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_t_sgemm(const float *__restri
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
       const int c = min(c0 + u, c_end - 1);
-      const int k = c * 16 + 4 * g;
-      av[u] = *reinterpret_cast<const u32x4 *>(ap + (size_t)c * 16);
+      const int sg = c / cps, cl = c - sg * cps;
+      const float *As = a.A[a.nseg > 1 ? sg : 0];
+      const float *Bs = a.B[a.nseg > 1 ? sg : o];
+      const int k = cl * 16 + 4 * g;
+      av[u] = *reinterpret_cast<const u32x4 *>(As + arow + (size_t)cl * 16);
       if constexpr (TB) {
-        b0[u] = *reinterpret_cast<const u32x4 *>(B + (size_t)nA * ldb + k);
-        b1[u] = *reinterpret_cast<const u32x4 *>(B + (size_t)nB * ldb + k);
+        b0[u] = *reinterpret_cast<const u32x4 *>(Bs + (size_t)nA * ldb + k);
+        b1[u] = *reinterpret_cast<const u32x4 *>(Bs + (size_t)nB * ldb + k);
       } else {
-        const float *bp = B + (size_t)k * ldb;
+        const float *bp = Bs + (size_t)k * ldb;
         b0[u] = u32x4{__float_as_uint(bp[nA]), __float_as_uint(bp[ldb + nA]),
                       __float_as_uint(bp[2 * ldb + nA]), __float_as_uint(bp[3 * ldb + nA])};
         b1[u] = u32x4{__float_as_uint(bp[nB]), __float_as_uint(bp[ldb + nB]),
@@ -163,12 +178,14 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_t_sgemm(const float *__restri
     for (int w = 1; w < kSgWaves; ++w) v += part[w][wave][lane];
     // lane l, element r: row 4 (l >> 4) + r, column l & 15 of the 16 x 16 half
     const int n = n0 + wave * 16 + li, mb = m0 + 4 * g;
-    if (n < N) {
+    if (n < a.N) {
+      float *C = a.C[o];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (mb + r < M) {
-          float *c = C + (size_t)(mb + r) * ldc + n;
-          *c = ACC ? *c + v[r] : v[r];
+        if (mb + r < a.M) {
+          float *c = C + (size_t)(mb + r) * a.ldc + n;
+          const float base = a.R ? a.R[(size_t)(mb + r) * a.ldr + n] : ACC ? *c : 0.f;
+          *c = base + v[r];
         }
       }
     }
@@ -295,9 +312,12 @@ __global__ void k_t_norm_fwd(const float *__restrict__ x, const float *__restric
 }
 
 // dx (+)= r * (gamma * dy - xhat * mean(gamma * dy * xhat)), xhat = x * r.
+// dx = (base ? base : 0) + RMSNorm backward of dy, also written to dx2 when
+// given (base may be dx itself: each element is read before it is written, by
+// the same thread)
 __global__ void k_t_norm_bwd(const float *__restrict__ x, const float *__restrict__ r_in,
                              const float *__restrict__ gamma, const float *__restrict__ dy,
-                             float *__restrict__ dx, int rows, int d, int accumulate) {
+                             const float *base, float *dx, float *dx2, int rows, int d) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float r = r_in[row];
@@ -308,8 +328,10 @@ __global__ void k_t_norm_bwd(const float *__restrict__ x, const float *__restric
   dot = t_wave_sum(dot) / (float)d;
   for (int c = lane; c < d; c += 64) {
     const float v = r * (gamma[c] * g[c] - xr[c] * r * dot);
-    float *o = dx + (size_t)row * d + c;
-    *o = accumulate ? *o + v : v;
+    const size_t i = (size_t)row * d + c;
+    const float y = base ? base[i] + v : v;
+    dx[i] = y;
+    if (dx2) dx2[i] = y;
   }
 }
 
@@ -505,15 +527,31 @@ __global__ __launch_bounds__(256) void k_t_attn_bwd(TAttn a) {
     __syncthreads();
   }
   if (a.dkb) {
-    // every position's rows belong to this (row, head) alone: threads split positions
-    float *dK = a.dkb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
-    float *dV = a.dvb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
+    // every position's rows belong to this (row, head) alone: wavefront w takes
+    // positions w, w + 4, ...; eight positions' old values are loaded before
+    // any of them is written back, so the read-modify-writes overlap
+    float *__restrict__ dK = a.dkb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
+    float *__restrict__ dV = a.dvb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
     const int jc = max(0, a.cut_lo - lo);
-    for (int j = jc + wave; j < n; j += 4) {
-      const float ds = sds[j] * a.scale, p = sp[j];
-      for (int c = lane; c < a.dh; c += 64) {
-        dK[(size_t)(lo + j) * a.s_pos + c] += ds * q[c];
-        dV[(size_t)(lo + j) * a.s_pos + c] += p * dout[c];
+    constexpr int U = 8;
+    for (int c = lane; c < a.dh; c += 64) {
+      const float qc = q[c], dc = dout[c];
+      for (int j0 = jc + wave; j0 < n; j0 += 4 * U) {
+        float kv[U], vv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = min(j0 + 4 * u, n - 1);
+          kv[u] = dK[(size_t)(lo + j) * a.s_pos + c];
+          vv[u] = dV[(size_t)(lo + j) * a.s_pos + c];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + 4 * u;
+          if (j < n) {
+            dK[(size_t)(lo + j) * a.s_pos + c] = kv[u] + sds[j] * a.scale * qc;
+            dV[(size_t)(lo + j) * a.s_pos + c] = vv[u] + sp[j] * dc;
+          }
+        }
       }
     }
   }
@@ -640,15 +678,29 @@ void t_colsum(const float *a, const float *b, const float *r, float *out, int M,
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
+// whether the MFMA per-step form takes an operand pair: K a multiple of 16 and
+// 16-byte aligned rows of A (and of B when it is read along k)
+bool sgemm_ok(const float *A, int64_t lda, const float *B, int64_t ldb, bool tb, int K) {
+  return K >= 16 && K % 16 == 0 && lda % 4 == 0 && aligned16(A) &&
+         (!tb || (ldb % 4 == 0 && aligned16(B)));
+}
+
+template <bool TB, bool ACC>
+void sgemm_launch(const SgArgs &g, int nout, hipStream_t s) {
+  hipLaunchKernelGGL((k_t_sgemm<TB, ACC>), dim3((g.N + 31) / 32, (g.M + 15) / 16, nout),
+                     dim3(kSgWaves * 64), 0, s, g);
+}
+
 template <bool TA, bool TB, bool ACC>
 void t_gemm_go(const float *A, int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
                int M, int N, int K, hipStream_t s, float *split) {
   if (M <= 0 || N <= 0) return;
-  // per-step products (A not transposed) with 16-byte aligned rows: the MFMA form
-  if (!TA && K >= 16 && K % 16 == 0 && lda % 4 == 0 && aligned16(A) &&
-      (!TB || (ldb % 4 == 0 && aligned16(B)))) {
-    hipLaunchKernelGGL((k_t_sgemm<TB, ACC>), dim3((N + 31) / 32, (M + 15) / 16), dim3(kSgWaves * 64),
-                       0, s, A, lda, B, ldb, C, ldc, M, N, K);
+  // per-step products (A not transposed): the MFMA form
+  if (!TA && sgemm_ok(A, lda, B, ldb, TB, K)) {
+    SgArgs g{};
+    g.A[0] = A; g.B[0] = B; g.C[0] = C; g.nseg = 1;
+    g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.M = M; g.N = N; g.K = K;
+    sgemm_launch<TB, ACC>(g, 1, s);
     return;
   }
   // weight gradients (sums over the rows of the call): the MFMA form
@@ -684,6 +736,56 @@ void t_gemm_go(const float *A, int64_t lda, const float *B, int64_t ldb, float *
                      A, lda, B, ldb, C, ldc, M, N, K, K);
 }
 
+// C = R + A B^T (a forward product added to its residual input R != C)
+void t_gemm_res(const float *A, int64_t lda, const float *Bm, int64_t ldb, const float *R, int64_t ldr,
+                float *C, int64_t ldc, int M, int N, int K, hipStream_t s, float *split) {
+  if (M <= 0 || N <= 0) return;
+  if (sgemm_ok(A, lda, Bm, ldb, true, K)) {
+    SgArgs g{};
+    g.A[0] = A; g.B[0] = Bm; g.C[0] = C; g.nseg = 1; g.R = R; g.ldr = ldr;
+    g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.M = M; g.N = N; g.K = K;
+    sgemm_launch<true, false>(g, 1, s);
+    return;
+  }
+  hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)M * N)), dim3(256), 0, s, R, ldr, C, ldc, M, N);
+  t_gemm_go<false, true, true>(A, lda, Bm, ldb, C, ldc, M, N, K, s, split);
+}
+
+// C_o = A B_o^T for up to three outputs sharing A (one launch)
+void t_gemm_multi(const float *A, int64_t lda, const float *const *Bs, int64_t ldb, float *const *Cs,
+                  int64_t ldc, int nout, int M, int N, int K, hipStream_t s, float *split) {
+  if (M <= 0 || N <= 0) return;
+  bool ok = nout >= 1 && nout <= 3;
+  for (int o = 0; o < nout && ok; ++o) ok = sgemm_ok(A, lda, Bs[o], ldb, true, K);
+  if (ok) {
+    SgArgs g{};
+    g.A[0] = A;
+    for (int o = 0; o < nout; ++o) { g.B[o] = Bs[o]; g.C[o] = Cs[o]; }
+    g.nseg = 1; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.M = M; g.N = N; g.K = K;
+    sgemm_launch<true, false>(g, nout, s);
+    return;
+  }
+  for (int o = 0; o < nout; ++o) t_gemm_go<false, true, false>(A, lda, Bs[o], ldb, Cs[o], ldc, M, N, K, s, split);
+}
+
+// C = sum over segments s of A_s B_s, B_s read as [K][ldb] (one launch; the
+// segments' k-chunks in order)
+void t_gemm_sum(const float *const *As, int64_t lda, const float *const *Bs, int64_t ldb, int nseg,
+                float *C, int64_t ldc, int M, int N, int K, hipStream_t s, float *split) {
+  if (M <= 0 || N <= 0) return;
+  bool ok = nseg >= 1 && nseg <= 3;
+  for (int q = 0; q < nseg && ok; ++q) ok = sgemm_ok(As[q], lda, Bs[q], ldb, false, K);
+  if (ok) {
+    SgArgs g{};
+    for (int q = 0; q < nseg; ++q) { g.A[q] = As[q]; g.B[q] = Bs[q]; }
+    g.C[0] = C; g.nseg = nseg; g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.M = M; g.N = N; g.K = K;
+    sgemm_launch<false, false>(g, 1, s);
+    return;
+  }
+  t_gemm_go<false, false, false>(As[0], lda, Bs[0], ldb, C, ldc, M, N, K, s, split);
+  for (int q = 1; q < nseg; ++q) t_gemm_go<false, false, true>(As[q], lda, Bs[q], ldb, C, ldc, M, N, K, s, split);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- driver
@@ -697,7 +799,7 @@ struct TrainWs {
   // per step [T][B][.]
   float *es, *g, *s, *ro, *sn, *dl, *lossr, *dz, *dsn;
   // scratch [B][.]
-  float *u, *logits, *dx, *dx2, *dtmp, *dh, *des, *dscarry, *dsd;
+  float *logits, *dx, *dtmp, *des, *dscarry;
   int *lo_w, *lo_m, *hi;
   float *split;              // split-K partial sums
 };
@@ -726,9 +828,8 @@ size_t train_layout(const rlt_config &c, int B, int T, TrainWs *w, void *base) {
   w->es = take(TB * 2 * d); w->g = take(TB * d); w->s = take(TB * d); w->ro = take(TB);
   w->sn = take(TB * d); w->dl = take(TB * V); w->lossr = take(TB); w->dz = take(TB * d);
   w->dsn = take(TB * d);
-  w->u = take((size_t)B * d); w->logits = take((size_t)B * V); w->dx = take((size_t)B * d);
-  w->dx2 = take((size_t)B * d); w->dtmp = take((size_t)B * d); w->dh = take((size_t)B * F);
-  w->des = take((size_t)B * 2 * d); w->dscarry = take((size_t)B * d); w->dsd = take((size_t)B * d);
+  w->logits = take((size_t)B * V); w->dx = take((size_t)B * d); w->dtmp = take((size_t)B * d);
+  w->des = take((size_t)B * 2 * d); w->dscarry = take((size_t)B * d);
   w->lo_w = reinterpret_cast<int *>(take(B)); w->lo_m = reinterpret_cast<int *>(take(B));
   w->hi = reinterpret_cast<int *>(take(B));
   w->split = take((size_t)kSplitTiles * 64 * 64);
@@ -758,8 +859,9 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
   auto norm_fwd = [&](const float *x, const float *gm, float *y, float *r) {
     hipLaunchKernelGGL(k_t_norm_fwd, dim3((B + 3) / 4), dim3(256), 0, s, x, gm, eps, y, r, B, d);
   };
-  auto norm_bwd = [&](const float *x, const float *r, const float *gm, const float *dy, float *dx, int acc) {
-    hipLaunchKernelGGL(k_t_norm_bwd, dim3((B + 3) / 4), dim3(256), 0, s, x, r, gm, dy, dx, B, d, acc);
+  auto norm_bwd = [&](const float *x, const float *r, const float *gm, const float *dy, const float *base,
+                      float *dx, float *dx2) {
+    hipLaunchKernelGGL(k_t_norm_bwd, dim3((B + 3) / 4), dim3(256), 0, s, x, r, gm, dy, base, dx, dx2, B, d);
   };
   auto mem_base = [&](const float *m, int grp) { return m + (size_t)grp * A.m_group; };
 
@@ -795,19 +897,19 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
     }
     float *gz = st(w.g, t, d);
     t_gemm_go<false, true, false>(es, 2 * d, P_wg, 2 * d, gz, d, B, d, 2 * d, s, w.split);
+    // u, written straight into layer 0's saved input
     hipLaunchKernelGGL(k_t_merge_fwd, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, es, gz, P_bg,
-                       w.u, B, d);
-    const float *x = w.u;
+                       at(w.xin, 0, t, d), B, d);
     for (int l = 0; l < L; ++l) {
       float *xin = at(w.xin, l, t, d);
-      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, x, (int64_t)d,
-                         xin, (int64_t)d, B, d);
       float *a = at(w.a, l, t, d), *r1 = at(w.r1, l, t, 1);
       norm_fwd(xin, g1(l), a, r1);
       float *q = at(w.q, l, t, d), *kh = at(w.kh, l, t, d), *vh = at(w.vh, l, t, d);
-      t_gemm_go<false, true, false>(a, d, wq(l), d, q, d, B, d, d, s, w.split);
-      t_gemm_go<false, true, false>(a, d, wk(l), d, kh, d, B, d, d, s, w.split);
-      t_gemm_go<false, true, false>(a, d, wv(l), d, vh, d, B, d, d, s, w.split);
+      {
+        const float *wqkv[3] = {wq(l), wk(l), wv(l)};
+        float *qkv[3] = {q, kh, vh};
+        t_gemm_multi(a, d, wqkv, d, qkv, d, 3, B, d, d, s, w.split);
+      }
       TAttn ta{};
       ta.q = q; ta.ldq = d;
       ta.kb = at(w.kh, l, 0, d); ta.vb = at(w.vh, l, 0, d);
@@ -818,9 +920,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       ta.H = H; ta.dh = dh; ta.scale = scale;
       hipLaunchKernelGGL(k_t_attn_fwd, dim3(B * H), dim3(256), 0, s, ta);
       float *x1 = at(w.x1, l, t, d);
-      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, xin, (int64_t)d,
-                         x1, (int64_t)d, B, d);
-      t_gemm_go<false, true, true>(ta.o, d, wo(l), d, x1, d, B, d, d, s, w.split);
+      t_gemm_res(ta.o, d, wo(l), d, xin, d, x1, d, B, d, d, s, w.split);
       float *cc = at(w.c, l, t, d), *r2 = at(w.r2, l, t, 1);
       norm_fwd(x1, g2(l), cc, r2);
       float *qc = at(w.qc, l, t, d);
@@ -836,24 +936,18 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       tc.H = H; tc.dh = dh; tc.scale = scale;
       hipLaunchKernelGGL(k_t_attn_fwd, dim3(B * H), dim3(256), 0, s, tc);
       float *x2 = at(w.x2, l, t, d);
-      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, x1, (int64_t)d,
-                         x2, (int64_t)d, B, d);
-      t_gemm_go<false, true, true>(tc.o, d, woc(l), d, x2, d, B, d, d, s, w.split);
+      t_gemm_res(tc.o, d, woc(l), d, x1, d, x2, d, B, d, d, s, w.split);
       float *ff = at(w.f, l, t, d), *r3 = at(w.r3, l, t, 1);
       norm_fwd(x2, g3(l), ff, r3);
       float *hpre = at(w.hpre, l, t, F), *hh = at(w.h, l, t, F);
       t_gemm_go<false, true, false>(ff, d, w1(l), d, hpre, F, B, F, d, s, w.split);
       hipLaunchKernelGGL(k_t_gelu_fwd, dim3(blocks_for((size_t)B * F)), dim3(256), 0, s, hpre, hh,
                          (size_t)B * F);
-      // x3 = x2 + W2 h, kept in u (the next layer's input)
-      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, x2, (int64_t)d,
-                         w.u, (int64_t)d, B, d);
-      t_gemm_go<false, true, true>(hh, F, w2(l), F, w.u, d, B, d, F, s, w.split);
-      x = w.u;
+      // x3 = x2 + W2 h: the next layer's saved input, after the last layer s_t
+      float *x3 = l + 1 < L ? at(w.xin, l + 1, t, d) : st(w.s, t, d);
+      t_gemm_res(hh, F, w2(l), F, x2, d, x3, d, B, d, F, s, w.split);
     }
     float *sv = st(w.s, t, d);
-    hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, x, (int64_t)d, sv,
-                       (int64_t)d, B, d);
     float *sn = st(w.sn, t, d), *ro = st(w.ro, t, 1);
     norm_fwd(sv, (const float *)A.p->go, sn, ro);
     t_gemm_go<false, true, false>(sn, d, (const float *)A.p->wout, d, w.logits, V, B, V, d, s, w.split);
@@ -870,25 +964,20 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
     // head: dsn = dlogits W_out; ds_t = carry + RMSNorm_o backward
     float *dsn = st(w.dsn, t, d);
     t_gemm_go<false, false, false>(st(w.dl, t, V), V, (const float *)A.p->wout, d, dsn, d, B, d, V, s, w.split);
-    hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dscarry,
-                       (int64_t)d, w.dx, (int64_t)d, B, d);
-    norm_bwd(st(w.s, t, d), st(w.ro, t, 1), (const float *)A.p->go, dsn, w.dx, 1);
+    // dx = carry + RMSNorm_o backward, saved as the last layer's output gradient
+    norm_bwd(st(w.s, t, d), st(w.ro, t, 1), (const float *)A.p->go, dsn, w.dscarry, w.dx,
+             at(w.dxf, L - 1, t, d));
     for (int l = L - 1; l >= 0; --l) {
       // FFN: x3 = x2 + W2 gelu(W1 f), f = norm3(x2)
-      float *dxf = at(w.dxf, l, t, d);
-      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dx, (int64_t)d,
-                         dxf, (int64_t)d, B, d);
+      // w.dx (saved in dxf of this layer) is the gradient of the layer's output x3
       float *dhp = at(w.dhp, l, t, F);
       t_gemm_go<false, false, false>(w.dx, d, w2(l), F, dhp, F, B, F, d, s, w.split);
       hipLaunchKernelGGL(k_t_gelu_bwd, dim3(blocks_for((size_t)B * F)), dim3(256), 0, s,
                          at(w.hpre, l, t, F), dhp, (size_t)B * F);
       float *df = at(w.df, l, t, d);
       t_gemm_go<false, false, false>(dhp, F, w1(l), d, df, d, B, d, F, s, w.split);
-      norm_bwd(at(w.x2, l, t, d), at(w.r3, l, t, 1), g3(l), df, w.dx, 1);
-      // cross: x2 = x1 + W_Oc attn(W_Qc c, memory), c = norm2(x1)
-      float *dxoc = at(w.dxoc, l, t, d);
-      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dx, (int64_t)d,
-                         dxoc, (int64_t)d, B, d);
+      norm_bwd(at(w.x2, l, t, d), at(w.r3, l, t, 1), g3(l), df, w.dx, w.dx, at(w.dxoc, l, t, d));
+      // cross: x2 = x1 + W_Oc attn(W_Qc c, memory), c = norm2(x1); w.dx = d x2 (saved in dxoc)
       t_gemm_go<false, false, false>(w.dx, d, woc(l), d, w.dtmp, d, B, d, d, s, w.split);   // d oc
       const int grp = G == 1 ? 0 : l;
       TAttn tc{};
@@ -908,11 +997,9 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(256), 0, s, tc);
       float *dcc = at(w.dc, l, t, d);
       t_gemm_go<false, false, false>(dqc, d, wqc(l), d, dcc, d, B, d, d, s, w.split);
-      norm_bwd(at(w.x1, l, t, d), at(w.r2, l, t, 1), g2(l), dcc, w.dx, 1);
-      // window self-attention: x1 = xin + W_O attn(q, K, V), q,k,v = W a, a = norm1(xin)
-      float *dxo = at(w.dxo, l, t, d);
-      hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.dx, (int64_t)d,
-                         dxo, (int64_t)d, B, d);
+      norm_bwd(at(w.x1, l, t, d), at(w.r2, l, t, 1), g2(l), dcc, w.dx, w.dx, at(w.dxo, l, t, d));
+      // window self-attention: x1 = xin + W_O attn(q, K, V), q,k,v = W a, a = norm1(xin);
+      // w.dx = d x1 (saved in dxo)
       t_gemm_go<false, false, false>(w.dx, d, wo(l), d, w.dtmp, d, B, d, d, s, w.split);    // d o
       TAttn ta{};
       ta.q = at(w.q, l, t, d); ta.ldq = d;
@@ -930,10 +1017,14 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(256), 0, s, ta);
       // da = dq Wq + dk_t Wk + dv_t Wv (dk_t, dv_t complete: every later reader is done)
       float *daa = at(w.da, l, t, d);
-      t_gemm_go<false, false, false>(dq, d, wq(l), d, daa, d, B, d, d, s, w.split);
-      t_gemm_go<false, false, true>(at(w.dkh, l, t, d), d, wk(l), d, daa, d, B, d, d, s, w.split);
-      t_gemm_go<false, false, true>(at(w.dvh, l, t, d), d, wv(l), d, daa, d, B, d, d, s, w.split);
-      norm_bwd(at(w.xin, l, t, d), at(w.r1, l, t, 1), g1(l), daa, w.dx, 1);
+      {
+        const float *dqkv[3] = {dq, at(w.dkh, l, t, d), at(w.dvh, l, t, d)};
+        const float *wqkv[3] = {wq(l), wk(l), wv(l)};
+        t_gemm_sum(dqkv, d, wqkv, d, 3, daa, d, B, d, d, s, w.split);
+      }
+      // w.dx = d xin, the previous layer's output gradient (saved in its dxf)
+      norm_bwd(at(w.xin, l, t, d), at(w.r1, l, t, 1), g1(l), daa, w.dx, w.dx,
+               l > 0 ? at(w.dxf, l - 1, t, d) : nullptr);
     }
     // merge: u = g e + (1 - g) s_{t-1}, g = sigmoid(W_g [e ; s] + b_g)
     float *dz = st(w.dz, t, d);
