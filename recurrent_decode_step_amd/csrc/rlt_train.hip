@@ -129,12 +129,17 @@ struct SgArgs {
 template <bool TB, bool ACC>
 __global__ __launch_bounds__(kSgWaves * 64) void k_t_sgemm(const SgArgs a) {
   __shared__ f32x4 part[kSgWaves][2][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wavefront index is uniform: keep the chunk range and the operand
+  // pointers in scalar registers (no per-chunk loads of the argument arrays)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int o = blockIdx.z;
   const int m0 = blockIdx.y * 16, n0 = blockIdx.x * 32;
   const int li = lane & 15, g = lane >> 4;
   const int cps = a.K >> 4, chunks = cps * a.nseg;
   const int c_beg = (wave * chunks) / kSgWaves, c_end = ((wave + 1) * chunks) / kSgWaves;
+  const float *const A0 = a.A[0], *const A1 = a.A[1], *const A2 = a.A[2];
+  const float *const Bo = o == 0 ? a.B[0] : (o == 1 ? a.B[1] : a.B[2]);
+  const float *const B1 = a.B[1], *const B2 = a.B[2];
   const size_t arow = (size_t)min(m0 + li, a.M - 1) * a.lda + 4 * g;
   const int nA = min(n0 + li, a.N - 1), nB = min(n0 + 16 + li, a.N - 1);
   const int64_t ldb = a.ldb;
@@ -145,9 +150,9 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_t_sgemm(const SgArgs a) {
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
       const int c = min(c0 + u, c_end - 1);
-      const int sg = c / cps, cl = c - sg * cps;
-      const float *As = a.A[a.nseg > 1 ? sg : 0];
-      const float *Bs = a.B[a.nseg > 1 ? sg : o];
+      const int sg = c / cps, cl = c - sg * cps;  // segment (0 when there is one)
+      const float *As = sg == 0 ? A0 : (sg == 1 ? A1 : A2);
+      const float *Bs = sg == 0 ? Bo : (sg == 1 ? B1 : B2);
       const int k = cl * 16 + 4 * g;
       av[u] = *reinterpret_cast<const u32x4 *>(As + arow + (size_t)cl * 16);
       if constexpr (TB) {
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(kWgWaves * 64) void k_t_wgemm(const float *__restri
                                                            float *__restrict__ C, int64_t ldc, int M,
                                                            int N, int K) {
   __shared__ f32x4 part[kWgWaves][4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
   const int li = lane & 15, g = lane >> 4;
   const int chunks = (K + 15) >> 4;
