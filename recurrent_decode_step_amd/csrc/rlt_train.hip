@@ -108,15 +108,14 @@ __global__ __launch_bounds__(256) void k_t_gemm(const float *__restrict__ A, int
 // over nseg segments s (each K long, K a multiple of 16), A_s row-major
 // [M][K] (lda), B_s(k, n) = TB ? B_s[n * ldb + k] : B_s[k * ldb + n].  With
 // several outputs there is one segment, A shared and B, C per output; with
-// several segments, one output.  A workgroup of kSgWaves wavefronts computes a
-// 16 x 32 tile; the nseg * K / 16 chunks (segments in order, k in order
-// within each) are cut into kSgWaves consecutive parts, one per wavefront,
+// several segments, one output.  A workgroup of NW wavefronts computes a
+// 16 x 16 NT tile; the nseg * K / 16 chunks (segments in order, k in order
+// within each) are cut into NW consecutive parts, one per wavefront,
 // each an MFMA chain over its chunks in order (lane l holds row / column
 // l & 15 and k = 4 (l >> 4) .. +3 of a chunk in both operands, so the four
 // MFMAs of a chunk pair the same k), and the partial tiles are added in
 // wavefront order through LDS.  Rows and columns past M, N read clamped
 // addresses and are never stored.
-constexpr int kSgWaves = 8;
 struct SgArgs {
   const float *A[3];
   const float *B[3];
@@ -126,27 +125,31 @@ struct SgArgs {
   int64_t lda, ldb, ldc, ldr;
   int M, N, K;
 };
-template <bool TB, bool ACC>
-__global__ __launch_bounds__(kSgWaves * 64) void k_t_sgemm(const SgArgs a) {
-  __shared__ f32x4 part[kSgWaves][2][64];
+template <bool TB, bool ACC, int NW, int NT>
+__global__ __launch_bounds__(NW * 64) void k_t_sgemm(const SgArgs a) {
+  __shared__ f32x4 part[NW][NT][64];
   // the wavefront index is uniform: keep the chunk range and the operand
   // pointers in scalar registers (no per-chunk loads of the argument arrays)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int o = blockIdx.z;
-  const int m0 = blockIdx.y * 16, n0 = blockIdx.x * 32;
+  const int m0 = blockIdx.y * 16, n0 = blockIdx.x * (16 * NT);
   const int li = lane & 15, g = lane >> 4;
   const int cps = a.K >> 4, chunks = cps * a.nseg;
-  const int c_beg = (wave * chunks) / kSgWaves, c_end = ((wave + 1) * chunks) / kSgWaves;
+  const int c_beg = (wave * chunks) / NW, c_end = ((wave + 1) * chunks) / NW;
   const float *const A0 = a.A[0], *const A1 = a.A[1], *const A2 = a.A[2];
   const float *const Bo = o == 0 ? a.B[0] : (o == 1 ? a.B[1] : a.B[2]);
   const float *const B1 = a.B[1], *const B2 = a.B[2];
   const size_t arow = (size_t)min(m0 + li, a.M - 1) * a.lda + 4 * g;
-  const int nA = min(n0 + li, a.N - 1), nB = min(n0 + 16 + li, a.N - 1);
+  int nc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) nc[t] = min(n0 + 16 * t + li, a.N - 1);
   const int64_t ldb = a.ldb;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  constexpr int PB = 8;                            // chunks whose loads are in flight together
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int PB = NT > 2 ? 4 : 8;               // chunks whose loads are in flight together
   for (int c0 = c_beg; c0 < c_end; c0 += PB) {
-    u32x4 av[PB], b0[PB], b1[PB];
+    u32x4 av[PB], bv[PB][NT];
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
       const int c = min(c0 + u, c_end - 1);
@@ -155,34 +158,34 @@ __global__ __launch_bounds__(kSgWaves * 64) void k_t_sgemm(const SgArgs a) {
       const float *Bs = sg == 0 ? Bo : (sg == 1 ? B1 : B2);
       const int k = cl * 16 + 4 * g;
       av[u] = *reinterpret_cast<const u32x4 *>(As + arow + (size_t)cl * 16);
-      if constexpr (TB) {
-        b0[u] = *reinterpret_cast<const u32x4 *>(Bs + (size_t)nA * ldb + k);
-        b1[u] = *reinterpret_cast<const u32x4 *>(Bs + (size_t)nB * ldb + k);
-      } else {
-        const float *bp = Bs + (size_t)k * ldb;
-        b0[u] = u32x4{__float_as_uint(bp[nA]), __float_as_uint(bp[ldb + nA]),
-                      __float_as_uint(bp[2 * ldb + nA]), __float_as_uint(bp[3 * ldb + nA])};
-        b1[u] = u32x4{__float_as_uint(bp[nB]), __float_as_uint(bp[ldb + nB]),
-                      __float_as_uint(bp[2 * ldb + nB]), __float_as_uint(bp[3 * ldb + nB])};
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (TB) {
+          bv[u][t] = *reinterpret_cast<const u32x4 *>(Bs + (size_t)nc[t] * ldb + k);
+        } else {
+          const float *bp = Bs + (size_t)k * ldb + nc[t];
+          bv[u][t] = u32x4{__float_as_uint(bp[0]), __float_as_uint(bp[ldb]),
+                           __float_as_uint(bp[2 * ldb]), __float_as_uint(bp[3 * ldb])};
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
       if (c0 + u < c_end) {
-        acc0 = mma_step(av[u], b0[u], acc0, 0.f);
-        acc1 = mma_step(av[u], b1[u], acc1, 0.f);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mma_step(av[u], bv[u][t], acc[t], 0.f);
       }
     }
   }
-  part[wave][0][lane] = acc0;
-  part[wave][1][lane] = acc1;
-  __syncthreads();
-  if (wave < 2) {
-    f32x4 v = part[0][wave][lane];
 #pragma unroll
-    for (int w = 1; w < kSgWaves; ++w) v += part[w][wave][lane];
-    // lane l, element r: row 4 (l >> 4) + r, column l & 15 of the 16 x 16 half
-    const int n = n0 + wave * 16 + li, mb = m0 + 4 * g;
+  for (int t = 0; t < NT; ++t) part[wave][t][lane] = acc[t];
+  __syncthreads();
+  for (int t = wave; t < NT; t += NW) {
+    f32x4 v = part[0][t][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += part[w][t][lane];
+    // lane l, element r: row 4 (l >> 4) + r, column l & 15 of 16-column block t
+    const int n = n0 + t * 16 + li, mb = m0 + 4 * g;
     if (n < a.N) {
       float *C = a.C[o];
 #pragma unroll
@@ -690,10 +693,21 @@ bool sgemm_ok(const float *A, int64_t lda, const float *B, int64_t ldb, bool tb,
          (!tb || (ldb % 4 == 0 && aligned16(B)));
 }
 
+template <bool TB, bool ACC, int NW, int NT>
+void sgemm_go(const SgArgs &g, int nout, hipStream_t s) {
+  hipLaunchKernelGGL((k_t_sgemm<TB, ACC, NW, NT>), dim3((g.N + 16 * NT - 1) / (16 * NT), (g.M + 15) / 16, nout),
+                     dim3(NW * 64), 0, s, g);
+}
+
+// Shape choice (measured on the per-step products at 128 rows): 16 x 16 tiles
+// on 4 wavefronts, except wide outputs over a short K (FFN-up, the head and
+// their input gradients), which take 16 x 64 tiles on 8 wavefronts.  The
+// choice depends on N and K only, so a row's result does not depend on the
+// batch.
 template <bool TB, bool ACC>
 void sgemm_launch(const SgArgs &g, int nout, hipStream_t s) {
-  hipLaunchKernelGGL((k_t_sgemm<TB, ACC>), dim3((g.N + 31) / 32, (g.M + 15) / 16, nout),
-                     dim3(kSgWaves * 64), 0, s, g);
+  if (g.N >= 2048 && (int64_t)g.K * g.nseg <= 1024) sgemm_go<TB, ACC, 8, 4>(g, nout, s);
+  else sgemm_go<TB, ACC, 4, 1>(g, nout, s);
 }
 
 template <bool TA, bool TB, bool ACC>
