@@ -33,6 +33,8 @@ namespace rlt {
 namespace {
 
 // ---------------------------------------------------------------- kernels
+// VALU form, for the products the MFMA forms below do not take (K not a
+// multiple of 16 or rows not 16-byte aligned in a per-step product):
 // C[m][n] = (ACC ? C[m][n] : 0) + sum_k A(m, k) B(k, n), k in order.
 // A(m, k) = TA ? A[k * lda + m] : A[m * lda + k]; B(k, n) = TB ? B[n * ldb + k] : B[k * ldb + n].
 // 64 x 64 outputs per workgroup, 4 x 4 per thread, K in chunks of 16 through LDS.
