@@ -80,8 +80,11 @@ CONFIGS = [
     ((32, 2, 2, 64, 11, 3, 1), 2, 6),
     ((32, 2, 2, 64, 11, 3, 2), 2, 6),
     ((128, 4, 2, 256, 200, 5, 1), 3, 20),
-    # 128 sequences: the per-step products take the 128 x 128 tiles with split K
+    # 128 sequences: per-step products over 128 rows
     ((128, 4, 1, 256, 200, 4, 1), 128, 4),
+    # F = V = 2048: the wide per-step product form (16 x 64 tiles) and, with V a
+    # multiple of 16, the MFMA form of the head's input gradient
+    ((128, 4, 1, 2048, 2048, 6, 1), 16, 4),
 ]
 
 
