@@ -16,12 +16,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // ---------------------------------------------------------------- numerics
 __device__ __forceinline__ float bf2f(uint32_t h16) { return __uint_as_float(h16 << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet)
+// fp32 -> bf16, round to nearest even (NaN stays NaN), by the hardware
+// conversion (v_cvt_pk_bf16_f32, two values per instruction)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f);
+}
+// two values, lo in bits 0..15 and hi in bits 16..31
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> struct Num;
@@ -50,13 +54,11 @@ template <> struct Num<bf16_t> {
     f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
   }
   __device__ static u32x4 pack(const float *f) {
-    return u32x4{f2bf(f[0]) | (f2bf(f[1]) << 16), f2bf(f[2]) | (f2bf(f[3]) << 16),
-                 f2bf(f[4]) | (f2bf(f[5]) << 16), f2bf(f[6]) | (f2bf(f[7]) << 16)};
+    return u32x4{f2bf2(f[0], f[1]), f2bf2(f[2], f[3]), f2bf2(f[4], f[5]), f2bf2(f[6], f[7])};
   }
   __device__ static float round(float v) { return bf2f(f2bf(v)); }
   __device__ static void store4(bf16_t *p, const float *y) {
-    *reinterpret_cast<u32x2 *>(p) =
-        u32x2{f2bf(y[0]) | (f2bf(y[1]) << 16), f2bf(y[2]) | (f2bf(y[3]) << 16)};
+    *reinterpret_cast<u32x2 *>(p) = u32x2{f2bf2(y[0], y[1]), f2bf2(y[2], y[3])};
   }
   __device__ static void store1(bf16_t *p, float y) { *p = (bf16_t)f2bf(y); }
 };

@@ -800,8 +800,7 @@ __global__ __launch_bounds__(256, 2) void k_fattn(FAttnArgs a, int qblocks, int 
       u32x4 pf;
       if constexpr (PAIR == 2) {
         const f32x4 a0 = s[2 * ks], a1 = s[2 * ks + 1];
-        pf = u32x4{f2bf(a0[0]) | (f2bf(a0[1]) << 16), f2bf(a0[2]) | (f2bf(a0[3]) << 16),
-                   f2bf(a1[0]) | (f2bf(a1[1]) << 16), f2bf(a1[2]) | (f2bf(a1[3]) << 16)};
+        pf = u32x4{f2bf2(a0[0], a0[1]), f2bf2(a0[2], a0[3]), f2bf2(a1[0], a1[1]), f2bf2(a1[2], a1[3])};
       } else {
         pf = u32x4{__float_as_uint(s[ks][0]), __float_as_uint(s[ks][1]),
                    __float_as_uint(s[ks][2]), __float_as_uint(s[ks][3])};
@@ -984,10 +983,8 @@ __global__ __launch_bounds__(256, 2) void k_fattn32(FAttnArgs a, int qblocks, in
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int pb = kk >> 1, r0 = 8 * (kk & 1);
-        const u32x4 pf = u32x4{f2bf(s[pb][r0]) | (f2bf(s[pb][r0 + 1]) << 16),
-                               f2bf(s[pb][r0 + 2]) | (f2bf(s[pb][r0 + 3]) << 16),
-                               f2bf(s[pb][r0 + 4]) | (f2bf(s[pb][r0 + 5]) << 16),
-                               f2bf(s[pb][r0 + 6]) | (f2bf(s[pb][r0 + 7]) << 16)};
+        const u32x4 pf = u32x4{f2bf2(s[pb][r0], s[pb][r0 + 1]), f2bf2(s[pb][r0 + 2], s[pb][r0 + 3]),
+                               f2bf2(s[pb][r0 + 4], s[pb][r0 + 5]), f2bf2(s[pb][r0 + 6], s[pb][r0 + 7])};
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           const bf16_t *vp = sVt + (cb * 32 + (lane & 31)) * VROW + kk * 16 + 4 * hh;
