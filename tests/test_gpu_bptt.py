@@ -127,3 +127,6 @@ def test_bptt_rejects_bf16_and_bad_arguments():
     with pytest.raises(binding.RLTError) as ex:
         binding.rlt_bptt(cfg32, params, e, (mk, mv), tg, detach=4, chunk=2)
     assert ex.value.status == binding.RLT_ERR_INVALID_ARG
+    with pytest.raises(binding.RLTError) as ex:          # zero steps
+        binding.rlt_bptt(cfg32, params, e[:, :0], (mk, mv), tg[:, :0])
+    assert ex.value.status == binding.RLT_ERR_INVALID_ARG

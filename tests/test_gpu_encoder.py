@@ -221,6 +221,10 @@ def test_encode_argument_and_range_errors():
     with pytest.raises(binding.RLTError) as ex:
         binding.rlt_encode(enc, es, tok, (mk, mv), slots=[1, 1])
     assert ex.value.status == binding.RLT_ERR_INVALID_ARG
+    with pytest.raises(binding.RLTError) as ex:          # zero tokens: nothing to encode
+        binding.rlt_encode(enc, es, tok[:, :0], (mk, mv))
+    assert ex.value.status == binding.RLT_ERR_INVALID_ARG
+    assert es.position(0) == 0 and es.position(1) == 0
     binding.rlt_encode(enc, es, tok, (mk, mv))
     with pytest.raises(binding.RLTError) as ex:          # 20 > max_tokens 16
         binding.rlt_encode(enc, es, tok, (mk, mv))

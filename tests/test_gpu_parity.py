@@ -447,6 +447,30 @@ def test_position_past_memory_is_rejected_without_side_effects():
     assert st.position(0) == 4
 
 
+def test_empty_calls_are_rejected_without_side_effects():
+    """Every call consumes at least one token per listed slot: zero rows or
+    zero steps are invalid arguments, rejected before any work, and no
+    position or state entry moves."""
+    cfg = tiny_cfg()
+    rig = Rig(cfg, 2, 6)
+    st = rig.state()
+    binding.rlt_run_sequence(rig.model, st, rig.ed[:, :2], rig.mem)
+    before = binding.rlt_state_export(rig.model, st, [0, 1]).clone()
+    calls = {
+        "decoder_step n=0": lambda: binding.rlt_decoder_step(rig.model, st, rig.ed[:0, 0], rig.mem),
+        "run_sequence T=0": lambda: binding.rlt_run_sequence(rig.model, st, rig.ed[:, :0], rig.mem),
+        "score_sequence T=0": lambda: binding.rlt_score_sequence(
+            rig.model, st, rig.ed[:, :0], rig.mem, torch.zeros((2, 0), dtype=torch.int32, device=DEV)),
+    }
+    for name, f in calls.items():
+        with pytest.raises(binding.RLTError) as ei:
+            f()
+        assert ei.value.status == binding.RLT_ERR_INVALID_ARG, name
+    torch.cuda.synchronize()
+    assert torch.equal(before, binding.rlt_state_export(rig.model, st, [0, 1]))
+    assert st.position(0) == 2 and st.position(1) == 2
+
+
 # ------------------------------------------------------------ replay scoring
 def test_score_sequence_f32_matches_oracle():
     """Replay scores (log-probability of the realized next token, read before
