@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <climits>
 #include <string>
 #include <vector>
 
@@ -159,12 +160,14 @@ struct rlt_state {
   int *pos;
   char *ring_k, *ring_v;
   int *slots_dev;
+  int *order_dev;            // [B] attention launch order of a ragged step (longest first)
   float *x, *sumsq;
   char *xg, *qbuf, *obuf, *hbuf;
   float *lscratch;           // [B][V] fp32 logits of a scored or generated step
   char *escratch;            // [B][d] e rows of generated tokens
   std::vector<int> host_pos;
   std::vector<int> staged;   // slot list currently in slots_dev (empty: none)
+  std::vector<int> staged_order;   // row order currently in order_dev
   ProfLog plog;
 };
 
@@ -234,6 +237,7 @@ size_t state_layout(const rlt_config &c, rlt_state *st, void *base, int B) {
   st->ring_k = ar.take<char>((size_t)L * B * H * W * dh * es);
   st->ring_v = ar.take<char>((size_t)L * B * H * W * dh * es);
   st->slots_dev = ar.take<int>((size_t)B * 4);
+  st->order_dev = ar.take<int>((size_t)B * 4);
   st->x = ar.take<float>((size_t)B * d * 4);
   st->sumsq = ar.take<float>((size_t)cdiv(d, 16) * B * 4);
   const size_t rows16 = (size_t)cdiv(B, 16) * 16;   // packed activations: whole 16-row blocks
@@ -407,10 +411,33 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
 
   // host mirror: algorithmic bytes of the two attentions (for profiling)
   double swa_len = 0, mem_len = 0;
+  int tmin = INT_MAX, tmax = 0;
   for (int i = 0; i < n; ++i) {
     const int t = st->host_pos[identity ? i : host_slots[i]] + 1;
     swa_len += std::min(t, W);
     mem_len += t;
+    tmin = std::min(tmin, t);
+    tmax = std::max(tmax, t);
+  }
+  // Rows of different lengths (a ragged batch): the attention launches take
+  // the rows longest first, so that the long rows do not form the tail of the
+  // launch.  A row's result does not depend on the order.
+  const int *order_dev = nullptr;
+  if (tmax > tmin) {
+    std::vector<int> ord(n);
+    for (int i = 0; i < n; ++i) ord[i] = i;
+    auto t_of = [&](int i) { return st->host_pos[identity ? i : host_slots[i]]; };
+    std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return t_of(x) > t_of(y); });
+    if (ord != st->staged_order) {
+      st->staged_order = ord;
+      err = hipMemcpyAsync(st->order_dev, st->staged_order.data(), (size_t)n * 4,
+                           hipMemcpyHostToDevice, s);
+      if (err != hipSuccess) {
+        st->staged_order.clear();
+        return hip_fail(err, "staging the attention row order");
+      }
+    }
+    order_dev = st->order_dev;
   }
 
   const ColPlan cp = col_plan(n);
@@ -479,6 +506,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
   AttnArgs at;
   memset(&at, 0, sizeof at);
   at.slots = base.slots;
+  at.order = order_dev;
   at.pos = st->pos;
   at.H = H;
   at.d = d;

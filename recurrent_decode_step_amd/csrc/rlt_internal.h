@@ -91,6 +91,10 @@ struct AttnArgs {
   int len_cap;                              // window W, or INT32_MAX for memory
   int ch;                                   // positions per chunk (<= the kernel's maximum)
   const int *slots; const int *pos;
+  // rows in launch order, longest first (null: row i is workgroup column i);
+  // with an order the grid is (H, n) so every head of a row is launched
+  // before any head of the next row
+  const int *order;
   int H, d;
   float scale_log2;                         // log2(e) / sqrt(dh)
 };

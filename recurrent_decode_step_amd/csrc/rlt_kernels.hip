@@ -745,7 +745,8 @@ void k_attn(const AttnArgs a) {
   __shared__ float s_o[4][DH];
   __shared__ float s_ml[4][2];
 
-  const int i = blockIdx.x, h = blockIdx.y;
+  const int i = a.order ? a.order[blockIdx.y] : (int)blockIdx.x;
+  const int h = a.order ? (int)blockIdx.x : (int)blockIdx.y;
   const int slot = a.slots ? a.slots[i] : i;
   const int t = a.pos[slot] + 1;
   const int len = min(t, a.len_cap);
@@ -1234,7 +1235,7 @@ hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const Gemm
 
 template <typename T, int KIND>
 static hipError_t attn_dispatch(int dh, const AttnArgs &a, int n_rows, hipStream_t s) {
-  const dim3 grid((unsigned)n_rows, (unsigned)a.H);
+  const dim3 grid = a.order ? dim3((unsigned)a.H, (unsigned)n_rows) : dim3((unsigned)n_rows, (unsigned)a.H);
   switch (dh) {
     case 16: k_attn<T, 16, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
     case 32: k_attn<T, 32, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
