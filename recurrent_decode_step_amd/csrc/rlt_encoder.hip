@@ -55,8 +55,10 @@ __global__ void k_enc_embed(const int32_t *__restrict__ tokens, int n_rows,
 
 // ---------------------------------------------------------------- RMSNorm
 // out[r] = round((x[r] * (mean(x[r]^2) + eps)^(-1/2)) * gamma); one wavefront
-// per row, four rows per workgroup.
-template <typename T>
+// per row, four rows per workgroup.  NC > 0: d = 256 NC, and the row stays in
+// registers between the sum of squares and the output (x is read once); the
+// sums run in the same order either way.
+template <typename T, int NC>
 __global__ __launch_bounds__(256) void k_enc_norm(const float *__restrict__ x, int64_t ldx,
                                                   const float *__restrict__ gamma, float eps,
                                                   T *__restrict__ out, int64_t ldo, int n_rows,
@@ -65,20 +67,38 @@ __global__ __launch_bounds__(256) void k_enc_norm(const float *__restrict__ x, i
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n_rows) return;                       // uniform over the wavefront
   const float *xr = x + (size_t)r * ldx;
-  float ss = 0.f;
-  for (int c = lane * 4; c < d; c += 256) {
-    const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  const float rinv = 1.0f / sqrtf(ss / (float)d + eps);
   T *o = out + (size_t)r * ldo;
-  for (int c = lane * 4; c < d; c += 256) {
-    const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + c);
-    const f32x4 g = *reinterpret_cast<const f32x4 *>(gamma + c);
-    const float y[4] = {(v.x * rinv) * g.x, (v.y * rinv) * g.y, (v.z * rinv) * g.z,
-                        (v.w * rinv) * g.w};
-    Num<T>::store4(o + c, y);
+  float ss = 0.f;
+  if constexpr (NC > 0) {
+    f32x4 v[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) v[i] = *reinterpret_cast<const f32x4 *>(xr + lane * 4 + 256 * i);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    ss = wave_sum(ss);
+    const float rinv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane * 4 + 256 * i;
+      const f32x4 g = *reinterpret_cast<const f32x4 *>(gamma + c);
+      const float y[4] = {(v[i].x * rinv) * g.x, (v[i].y * rinv) * g.y, (v[i].z * rinv) * g.z,
+                          (v[i].w * rinv) * g.w};
+      Num<T>::store4(o + c, y);
+    }
+  } else {
+    for (int c = lane * 4; c < d; c += 256) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + c);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    const float rinv = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int c = lane * 4; c < d; c += 256) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + c);
+      const f32x4 g = *reinterpret_cast<const f32x4 *>(gamma + c);
+      const float y[4] = {(v.x * rinv) * g.x, (v.y * rinv) * g.y, (v.z * rinv) * g.z,
+                          (v.w * rinv) * g.w};
+      Num<T>::store4(o + c, y);
+    }
   }
 }
 
@@ -1032,15 +1052,29 @@ hipError_t launch_enc_embed(int dtype, const int32_t *tokens, int n_rows, const 
   return hipGetLastError();
 }
 
+template <typename T, int NC>
+void enc_norm_go(const float *x, int64_t ldx, const float *gamma, float eps, void *out, int64_t ldo,
+                 int n_rows, int d, hipStream_t s) {
+  hipLaunchKernelGGL((k_enc_norm<T, NC>), dim3((n_rows + 3) / 4), dim3(256), 0, s, x, ldx, gamma, eps,
+                     static_cast<T *>(out), ldo, n_rows, d);
+}
+
+template <typename T>
+void enc_norm_dispatch(const float *x, int64_t ldx, const float *gamma, float eps, void *out,
+                       int64_t ldo, int n_rows, int d, hipStream_t s) {
+  switch (d) {
+    case 512: return enc_norm_go<T, 2>(x, ldx, gamma, eps, out, ldo, n_rows, d, s);
+    case 1024: return enc_norm_go<T, 4>(x, ldx, gamma, eps, out, ldo, n_rows, d, s);
+    case 2048: return enc_norm_go<T, 8>(x, ldx, gamma, eps, out, ldo, n_rows, d, s);
+    case 4096: return enc_norm_go<T, 16>(x, ldx, gamma, eps, out, ldo, n_rows, d, s);
+    default: return enc_norm_go<T, 0>(x, ldx, gamma, eps, out, ldo, n_rows, d, s);
+  }
+}
+
 hipError_t launch_enc_norm(int dtype, const float *x, int64_t ldx, const float *gamma, float eps,
                            void *out, int64_t ldo, int n_rows, int d, hipStream_t s) {
-  const int blocks = (n_rows + 3) / 4;
-  if (dtype == RLT_DTYPE_BF16)
-    hipLaunchKernelGGL(k_enc_norm<bf16_t>, dim3(blocks), dim3(256), 0, s, x, ldx, gamma, eps,
-                       static_cast<bf16_t *>(out), ldo, n_rows, d);
-  else
-    hipLaunchKernelGGL(k_enc_norm<float>, dim3(blocks), dim3(256), 0, s, x, ldx, gamma, eps,
-                       static_cast<float *>(out), ldo, n_rows, d);
+  if (dtype == RLT_DTYPE_BF16) enc_norm_dispatch<bf16_t>(x, ldx, gamma, eps, out, ldo, n_rows, d, s);
+  else enc_norm_dispatch<float>(x, ldx, gamma, eps, out, ldo, n_rows, d, s);
   return hipGetLastError();
 }
 

@@ -66,6 +66,8 @@ CONFIGS_F32 = [
     (64, 2, 2, 256, 100, 1),
     (128, 8, 2, 192, 77, 2),
     (256, 2, 1, 512, 300, 1),
+    # d = 512: the RMSNorm form that keeps the row in registers
+    (512, 4, 1, 512, 64, 1),
 ]
 
 
