@@ -308,23 +308,40 @@ __device__ __forceinline__ float t_wave_max(float v) {
 }
 
 // y = x * r * gamma, r = (mean(x^2) + eps)^(-1/2); one wavefront per row.
+// NI > 0: d = 64 NI, every load of the row issued at once into registers (the
+// sums run in the same order as the loop form).
+template <int NI>
 __global__ void k_t_norm_fwd(const float *__restrict__ x, const float *__restrict__ gamma, float eps,
                              float *__restrict__ y, float *__restrict__ r_out, int rows, int d) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float *xr = x + (size_t)row * d;
   float ss = 0.f;
-  for (int c = lane; c < d; c += 64) ss = fmaf(xr[c], xr[c], ss);
-  ss = t_wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c = lane; c < d; c += 64) y[(size_t)row * d + c] = xr[c] * r * gamma[c];
-  if (lane == 0) r_out[row] = r;
+  if constexpr (NI > 0) {
+    float v[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) v[i] = xr[lane + 64 * i];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) ss = fmaf(v[i], v[i], ss);
+    ss = t_wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) y[(size_t)row * d + lane + 64 * i] = v[i] * r * gamma[lane + 64 * i];
+    if (lane == 0) r_out[row] = r;
+  } else {
+    for (int c = lane; c < d; c += 64) ss = fmaf(xr[c], xr[c], ss);
+    ss = t_wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int c = lane; c < d; c += 64) y[(size_t)row * d + c] = xr[c] * r * gamma[c];
+    if (lane == 0) r_out[row] = r;
+  }
 }
 
 // dx (+)= r * (gamma * dy - xhat * mean(gamma * dy * xhat)), xhat = x * r.
 // dx = (base ? base : 0) + RMSNorm backward of dy, also written to dx2 when
 // given (base may be dx itself: each element is read before it is written, by
-// the same thread)
+// the same thread).  NI as in k_t_norm_fwd.
+template <int NI>
 __global__ void k_t_norm_bwd(const float *__restrict__ x, const float *__restrict__ r_in,
                              const float *__restrict__ gamma, const float *__restrict__ dy,
                              const float *base, float *dx, float *dx2, int rows, int d) {
@@ -334,14 +351,36 @@ __global__ void k_t_norm_bwd(const float *__restrict__ x, const float *__restric
   const float *xr = x + (size_t)row * d;
   const float *g = dy + (size_t)row * d;
   float dot = 0.f;
-  for (int c = lane; c < d; c += 64) dot = fmaf(gamma[c] * g[c], xr[c] * r, dot);
-  dot = t_wave_sum(dot) / (float)d;
-  for (int c = lane; c < d; c += 64) {
-    const float v = r * (gamma[c] * g[c] - xr[c] * r * dot);
-    const size_t i = (size_t)row * d + c;
-    const float y = base ? base[i] + v : v;
-    dx[i] = y;
-    if (dx2) dx2[i] = y;
+  if constexpr (NI > 0) {
+    float gg[NI], xx[NI], bb[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = lane + 64 * i;
+      gg[i] = gamma[c] * g[c];
+      xx[i] = xr[c];
+      bb[i] = base ? base[(size_t)row * d + c] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dot = fmaf(gg[i], xx[i] * r, dot);
+    dot = t_wave_sum(dot) / (float)d;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float v = r * (gg[i] - xx[i] * r * dot);
+      const size_t k = (size_t)row * d + lane + 64 * i;
+      const float yv = base ? bb[i] + v : v;
+      dx[k] = yv;
+      if (dx2) dx2[k] = yv;
+    }
+  } else {
+    for (int c = lane; c < d; c += 64) dot = fmaf(gamma[c] * g[c], xr[c] * r, dot);
+    dot = t_wave_sum(dot) / (float)d;
+    for (int c = lane; c < d; c += 64) {
+      const float v = r * (gamma[c] * g[c] - xr[c] * r * dot);
+      const size_t i = (size_t)row * d + c;
+      const float yv = base ? base[i] + v : v;
+      dx[i] = yv;
+      if (dx2) dx2[i] = yv;
+    }
   }
 }
 
@@ -878,11 +917,23 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
   auto at = [&](float *base, int l, int t, size_t width) { return base + (((size_t)l * T + t) * B) * width; };
   auto st = [&](float *base, int t, size_t width) { return base + (size_t)t * B * width; };
   auto norm_fwd = [&](const float *x, const float *gm, float *y, float *r) {
-    hipLaunchKernelGGL(k_t_norm_fwd, dim3((B + 3) / 4), dim3(256), 0, s, x, gm, eps, y, r, B, d);
+    const dim3 g((B + 3) / 4), t(256);
+    switch (d) {
+      case 256: hipLaunchKernelGGL(k_t_norm_fwd<4>, g, t, 0, s, x, gm, eps, y, r, B, d); break;
+      case 512: hipLaunchKernelGGL(k_t_norm_fwd<8>, g, t, 0, s, x, gm, eps, y, r, B, d); break;
+      case 1024: hipLaunchKernelGGL(k_t_norm_fwd<16>, g, t, 0, s, x, gm, eps, y, r, B, d); break;
+      default: hipLaunchKernelGGL(k_t_norm_fwd<0>, g, t, 0, s, x, gm, eps, y, r, B, d); break;
+    }
   };
   auto norm_bwd = [&](const float *x, const float *r, const float *gm, const float *dy, const float *base,
                       float *dx, float *dx2) {
-    hipLaunchKernelGGL(k_t_norm_bwd, dim3((B + 3) / 4), dim3(256), 0, s, x, r, gm, dy, base, dx, dx2, B, d);
+    const dim3 g((B + 3) / 4), t(256);
+    switch (d) {
+      case 256: hipLaunchKernelGGL(k_t_norm_bwd<4>, g, t, 0, s, x, r, gm, dy, base, dx, dx2, B, d); break;
+      case 512: hipLaunchKernelGGL(k_t_norm_bwd<8>, g, t, 0, s, x, r, gm, dy, base, dx, dx2, B, d); break;
+      case 1024: hipLaunchKernelGGL(k_t_norm_bwd<16>, g, t, 0, s, x, r, gm, dy, base, dx, dx2, B, d); break;
+      default: hipLaunchKernelGGL(k_t_norm_bwd<0>, g, t, 0, s, x, r, gm, dy, base, dx, dx2, B, d); break;
+    }
   };
   auto mem_base = [&](const float *m, int grp) { return m + (size_t)grp * A.m_group; };
 

@@ -85,6 +85,8 @@ CONFIGS = [
     # F = V = 2048: the wide per-step product form (16 x 64 tiles) and, with V a
     # multiple of 16, the MFMA form of the head's input gradient
     ((128, 4, 1, 2048, 2048, 6, 1), 16, 4),
+    # d = 512 (the benchmark's width): the RMSNorm forms that load the row into registers
+    ((512, 8, 1, 512, 40, 3, 1), 3, 5),
 ]
 
 
