@@ -118,6 +118,14 @@ __global__ __launch_bounds__(256) void k_t_gemm(const float *__restrict__ A, int
 // MFMAs of a chunk pair the same k), and the partial tiles are added in
 // wavefront order through LDS.  Rows and columns past M, N read clamped
 // addresses and are never stored.
+// exact GELU and its derivative
+__device__ __forceinline__ float t_gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float t_gelu_d(float x) {
+  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.3989422804014327f * expf(-0.5f * x * x);
+}
+
+// epilogues of the per-step products
+enum SgEpi { SG_PLAIN = 0, SG_GELU = 1, SG_GELU_GRAD = 2 };
 struct SgArgs {
   const float *A[3];
   const float *B[3];
@@ -126,6 +134,11 @@ struct SgArgs {
   const float *R;                     // residual input added to the sum (or null)
   int64_t lda, ldb, ldc, ldr;
   int M, N, K;
+  // SG_GELU: C holds the pre-activation and C2 (ldc) its GELU; SG_GELU_GRAD:
+  // the sum is multiplied by GELU'(aux) (aux: the pre-activation, ldc)
+  int epi;
+  float *C2;
+  const float *aux;
 };
 template <bool TB, bool ACC, int NW, int NT>
 __global__ __launch_bounds__(NW * 64) void k_t_sgemm(const SgArgs a) {
@@ -193,9 +206,13 @@ __global__ __launch_bounds__(NW * 64) void k_t_sgemm(const SgArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (mb + r < a.M) {
-          float *c = C + (size_t)(mb + r) * a.ldc + n;
+          const size_t off = (size_t)(mb + r) * a.ldc + n;
+          float *c = C + off;
           const float base = a.R ? a.R[(size_t)(mb + r) * a.ldr + n] : ACC ? *c : 0.f;
-          *c = base + v[r];
+          float yv = base + v[r];
+          if (a.epi == SG_GELU_GRAD) yv *= t_gelu_d(a.aux[off]);
+          *c = yv;
+          if (a.epi == SG_GELU) a.C2[off] = t_gelu(yv);
         }
       }
     }
@@ -635,10 +652,6 @@ __global__ void k_t_merge_bwd(const float *__restrict__ es, const float *__restr
   dz[i] = dd * (e - s) * g * (1.0f - g);
 }
 
-__device__ __forceinline__ float t_gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
-__device__ __forceinline__ float t_gelu_d(float x) {
-  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.3989422804014327f * expf(-0.5f * x * x);
-}
 
 __global__ void k_t_gelu_fwd(const float *__restrict__ pre, float *__restrict__ h, size_t n) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -828,6 +841,38 @@ void t_gemm_multi(const float *A, int64_t lda, const float *const *Bs, int64_t l
   for (int o = 0; o < nout; ++o) t_gemm_go<false, true, false>(A, lda, Bs[o], ldb, Cs[o], ldc, M, N, K, s, split);
 }
 
+// H = A B^T and G = GELU(H) (FFN-up forward: pre-activation and hidden)
+void t_gemm_gelu(const float *A, int64_t lda, const float *Bm, int64_t ldb, float *Hpre, float *G,
+                 int64_t ldc, int M, int N, int K, hipStream_t s, float *split) {
+  if (M <= 0 || N <= 0) return;
+  if (sgemm_ok(A, lda, Bm, ldb, true, K)) {
+    SgArgs g{};
+    g.A[0] = A; g.B[0] = Bm; g.C[0] = Hpre; g.nseg = 1; g.epi = SG_GELU; g.C2 = G;
+    g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.M = M; g.N = N; g.K = K;
+    sgemm_launch<true, false>(g, 1, s);
+    return;
+  }
+  t_gemm_go<false, true, false>(A, lda, Bm, ldb, Hpre, ldc, M, N, K, s, split);
+  hipLaunchKernelGGL(k_t_gelu_fwd, dim3(blocks_for((size_t)M * N)), dim3(256), 0, s, Hpre, G,
+                     (size_t)M * N);
+}
+
+// D = (A B) * GELU'(Hpre), B read as [K][ldb] (FFN backward through the GELU)
+void t_gemm_gelu_grad(const float *A, int64_t lda, const float *Bm, int64_t ldb, const float *Hpre,
+                      float *D, int64_t ldc, int M, int N, int K, hipStream_t s, float *split) {
+  if (M <= 0 || N <= 0) return;
+  if (sgemm_ok(A, lda, Bm, ldb, false, K)) {
+    SgArgs g{};
+    g.A[0] = A; g.B[0] = Bm; g.C[0] = D; g.nseg = 1; g.epi = SG_GELU_GRAD; g.aux = Hpre;
+    g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.M = M; g.N = N; g.K = K;
+    sgemm_launch<false, false>(g, 1, s);
+    return;
+  }
+  t_gemm_go<false, false, false>(A, lda, Bm, ldb, D, ldc, M, N, K, s, split);
+  hipLaunchKernelGGL(k_t_gelu_bwd, dim3(blocks_for((size_t)M * N)), dim3(256), 0, s, Hpre, D,
+                     (size_t)M * N);
+}
+
 // C = sum over segments s of A_s B_s, B_s read as [K][ldb] (one launch; the
 // segments' k-chunks in order)
 void t_gemm_sum(const float *const *As, int64_t lda, const float *const *Bs, int64_t ldb, int nseg,
@@ -1012,9 +1057,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       float *ff = at(w.f, l, t, d), *r3 = at(w.r3, l, t, 1);
       norm_fwd(x2, g3(l), ff, r3);
       float *hpre = at(w.hpre, l, t, F), *hh = at(w.h, l, t, F);
-      t_gemm_go<false, true, false>(ff, d, w1(l), d, hpre, F, B, F, d, s, w.split);
-      hipLaunchKernelGGL(k_t_gelu_fwd, dim3(blocks_for((size_t)B * F)), dim3(256), 0, s, hpre, hh,
-                         (size_t)B * F);
+      t_gemm_gelu(ff, d, w1(l), d, hpre, hh, F, B, F, d, s, w.split);
       // x3 = x2 + W2 h: the next layer's saved input, after the last layer s_t
       float *x3 = l + 1 < L ? at(w.xin, l + 1, t, d) : st(w.s, t, d);
       t_gemm_res(hh, F, w2(l), F, x2, d, x3, d, B, d, F, s, w.split);
@@ -1043,9 +1086,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       // FFN: x3 = x2 + W2 gelu(W1 f), f = norm3(x2)
       // w.dx (saved in dxf of this layer) is the gradient of the layer's output x3
       float *dhp = at(w.dhp, l, t, F);
-      t_gemm_go<false, false, false>(w.dx, d, w2(l), F, dhp, F, B, F, d, s, w.split);
-      hipLaunchKernelGGL(k_t_gelu_bwd, dim3(blocks_for((size_t)B * F)), dim3(256), 0, s,
-                         at(w.hpre, l, t, F), dhp, (size_t)B * F);
+      t_gemm_gelu_grad(w.dx, d, w2(l), F, at(w.hpre, l, t, F), dhp, F, B, F, d, s, w.split);
       float *df = at(w.df, l, t, d);
       t_gemm_go<false, false, false>(dhp, F, w1(l), d, df, d, B, d, F, s, w.split);
       norm_bwd(at(w.x2, l, t, d), at(w.r3, l, t, 1), g3(l), df, w.dx, w.dx, at(w.dxoc, l, t, d));
