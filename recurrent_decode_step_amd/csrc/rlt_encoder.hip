@@ -313,7 +313,7 @@ struct Pg32Cfg {
   static constexpr int RB = RB_, FB = FB_, WM = WM_, WN = WN_, NBUF = NBUF_, WPE = WPE_;
   static constexpr int GROUP = GROUP_;
   static constexpr int PD = PD_;       // stages in flight ahead of the one multiplied out
-  static constexpr bool DIRECT = DIRECT_;   // direct-to-LDS loads (k_pgemm32d; NBUF = 3)
+  static constexpr bool DIRECT = DIRECT_;   // direct-to-LDS loads (k_pgemm32d; NBUF - 1 stages in flight)
   static constexpr int THREADS = 64 * WM * WN;
   static constexpr int LDS = NBUF * (RB + FB) * 2 * 64 * 16;   // bytes
   static_assert(LDS >= WM * WN * 32 * 36 * 4, "epilogue scratch fits in the staging buffers");
@@ -609,17 +609,28 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, in
               acc[f][r], 0, 0, 0);
   };
 
+  // NBUF buffers, NBUF - 1 stages in flight: stage st + NBUF - 1 is loaded
+  // into the buffer stage st - 1 used, which every wavefront has finished with
+  // (the barrier that ends iteration st - 1)
+  constexpr int PD = C::NBUF - 1;
   const int S = a.KT;
-  issue(0, 0);
-  if (S > 1) issue(1, 1);
+  for (int k = 0; k < PD && k < S; ++k) issue(k, k);
   for (int st = 0; st < S; ++st) {
-    const int buf = st % 3;
-    const bool more2 = st + 2 < S;
-    if (more2) issue(st + 2, (st + 2) % 3);
-    // loads issued after this stage's: stages st+1 and st+2 that exist
-    if (more2) wait_vmcnt<2 * FPW>();
-    else if (st + 1 < S) wait_vmcnt<FPW>();
-    else wait_vmcnt<0>();
+    const int buf = st % C::NBUF;
+    if (st + PD < S) issue(st + PD, (st + PD) % C::NBUF);
+    // loads issued after this stage's: the stages st+1 .. st+PD that exist
+    const int after = min(S - 1, st + PD) - st;
+    if constexpr (PD >= 3) {
+      if (PD >= 4 && after >= 4) wait_vmcnt<(PD >= 4 ? 4 : 3) * FPW>();
+      else if (after >= 3) wait_vmcnt<3 * FPW>();
+      else if (after == 2) wait_vmcnt<2 * FPW>();
+      else if (after == 1) wait_vmcnt<FPW>();
+      else wait_vmcnt<0>();
+    } else {
+      if (after >= 2) wait_vmcnt<2 * FPW>();
+      else if (after == 1) wait_vmcnt<FPW>();
+      else wait_vmcnt<0>();
+    }
     __builtin_amdgcn_s_barrier();
     mult(buf);
     __builtin_amdgcn_s_barrier();
