@@ -407,7 +407,8 @@ size_t rlt_bptt_workspace_bytes(const rlt_config *cfg, int32_t batch, int32_t T)
  * grads:  buffers of the same shapes, OVERWRITTEN with d loss / d param.
  * dev_e [B][T][d] fp32; mem: fp32 memory, sequence index = b, capacity >= T.
  * dev_de [B][T][d] (written) or NULL; dmem: memory gradients with mem's
- * strides (ACCUMULATED into: zero them first) or NULL; dev_loss [1] (written).
+ * strides and 16-byte aligned pointers (RLT_ERR_SHAPE otherwise; ACCUMULATED
+ * into: zero them first) or NULL; dev_loss [1] (written).
  * dev_workspace: >= rlt_bptt_workspace_bytes, 256-byte aligned, caller owned.
  * RLT_ERR_UNSUPPORTED for a bf16 config. */
 rlt_status rlt_bptt(const rlt_config *cfg, const rlt_params *params, int32_t batch, int32_t T,

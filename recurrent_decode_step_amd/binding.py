@@ -526,7 +526,9 @@ def rlt_bptt(cfg: ModelConfig, params: dict, e: torch.Tensor, memory, targets: t
     dmem = None
     dm = None
     if want_dmem:
-        dm = (torch.zeros_like(mk), torch.zeros_like(mv))
+        # the library takes the gradients with the memory's strides
+        dm = tuple(torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device).zero_()
+                   for t in (mk, mv))
         dmem = memory_view(*dm)
     de = torch.empty_like(e) if want_de else None
     loss = torch.empty(1, dtype=torch.float32, device=dev)

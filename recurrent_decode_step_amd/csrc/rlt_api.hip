@@ -1524,6 +1524,8 @@ rlt_status rlt_bptt(const rlt_config *cfg, const rlt_params *params, int32_t bat
     if (dmem->stride_group != mem->stride_group || dmem->stride_seq != mem->stride_seq ||
         dmem->stride_head != mem->stride_head || dmem->stride_pos != mem->stride_pos)
       return fail(RLT_ERR_SHAPE, "memory gradients must have the memory's strides");
+    if (((uintptr_t)dmem->k | (uintptr_t)dmem->v) % 16)
+      return fail(RLT_ERR_SHAPE, "memory gradient pointers must be 16-byte aligned");
   }
   int chunk = 0, detach = 0;
   if (opts) {

@@ -483,6 +483,9 @@ __device__ __forceinline__ float t_group_sum16(float v) {
 // positions per pass of the workgroup); each wavefront then sums a quarter of
 // the positions per channel, and the four partial sums are added in
 // wavefront order.
+// Rows are 16-byte aligned (the workspace is 256-byte aligned, d and dh are
+// multiples of 16, and the library takes memory strides in multiples of 16
+// bytes only): each lane of a position's group reads 4 consecutive channels.
 __global__ __launch_bounds__(256) void k_t_attn_fwd(TAttn a) {
   __shared__ float sc[kTMaxPos];
   __shared__ float red[4];
@@ -500,7 +503,14 @@ __global__ __launch_bounds__(256) void k_t_attn_fwd(TAttn a) {
     float s = 0.f;
     if (j < n) {
       const float *k = K + (size_t)(lo + j) * a.s_pos;
-      for (int c = sub; c < a.dh; c += 16) s = fmaf(q[c], k[c], s);
+      for (int c = 4 * sub; c < a.dh; c += 64) {
+        const f32x4 kv = *reinterpret_cast<const f32x4 *>(k + c);
+        const f32x4 qv = *reinterpret_cast<const f32x4 *>(q + c);
+        s = fmaf(qv.x, kv.x, s);
+        s = fmaf(qv.y, kv.y, s);
+        s = fmaf(qv.z, kv.z, s);
+        s = fmaf(qv.w, kv.w, s);
+      }
     }
     s = t_group_sum16(s);
     if (j < n) {
@@ -522,8 +532,17 @@ __global__ __launch_bounds__(256) void k_t_attn_fwd(TAttn a) {
   for (int c0 = 0; c0 < a.dh; c0 += 64) {
     const int c = c0 + lane;
     float acc = 0.f;
-    if (c < a.dh)
-      for (int j = j0; j < j1; ++j) acc = fmaf(sc[j], V[(size_t)(lo + j) * a.s_pos + c], acc);
+    if (c < a.dh) {
+      // eight positions' loads in flight at a time; the sum runs over j in order
+      for (int j = j0; j < j1; j += 8) {
+        float vv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) vv[u] = V[(size_t)(lo + min(j + u, j1 - 1)) * a.s_pos + c];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (j + u < j1) acc = fmaf(sc[j + u], vv[u], acc);
+      }
+    }
     part[wave][lane] = acc;
     __syncthreads();
     if (wave == 0 && c < a.dh)
@@ -564,9 +583,15 @@ __global__ __launch_bounds__(256) void k_t_attn_bwd(TAttn a) {
     if (j < n) {
       const float *k = K + (size_t)(lo + j) * a.s_pos;
       const float *v = V + (size_t)(lo + j) * a.s_pos;
-      for (int c = sub; c < a.dh; c += 16) {
-        s = fmaf(q[c], k[c], s);
-        dp = fmaf(dout[c], v[c], dp);
+      for (int c = 4 * sub; c < a.dh; c += 64) {
+        const f32x4 kv = *reinterpret_cast<const f32x4 *>(k + c);
+        const f32x4 vv = *reinterpret_cast<const f32x4 *>(v + c);
+        const f32x4 qv = *reinterpret_cast<const f32x4 *>(q + c);
+        const f32x4 dv = *reinterpret_cast<const f32x4 *>(dout + c);
+        s = fmaf(qv.x, kv.x, s); s = fmaf(qv.y, kv.y, s);
+        s = fmaf(qv.z, kv.z, s); s = fmaf(qv.w, kv.w, s);
+        dp = fmaf(dv.x, vv.x, dp); dp = fmaf(dv.y, vv.y, dp);
+        dp = fmaf(dv.z, vv.z, dp); dp = fmaf(dv.w, vv.w, dp);
       }
     }
     s = t_group_sum16(s);
@@ -583,8 +608,16 @@ __global__ __launch_bounds__(256) void k_t_attn_bwd(TAttn a) {
   for (int c0 = 0; c0 < a.dh; c0 += 64) {
     const int c = c0 + lane;
     float acc = 0.f;
-    if (c < a.dh)
-      for (int j = j0; j < j1; ++j) acc = fmaf(sds[j], K[(size_t)(lo + j) * a.s_pos + c], acc);
+    if (c < a.dh) {
+      for (int j = j0; j < j1; j += 8) {
+        float kk[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kk[u] = K[(size_t)(lo + min(j + u, j1 - 1)) * a.s_pos + c];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (j + u < j1) acc = fmaf(sds[j + u], kk[u], acc);
+      }
+    }
     part[wave][lane] = acc;
     __syncthreads();
     if (wave == 0 && c < a.dh)
@@ -739,6 +772,7 @@ void t_colsum(const float *a, const float *b, const float *r, float *out, int M,
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
 
 // whether the MFMA per-step form takes an operand pair: K a multiple of 16 and
 // 16-byte aligned rows of A (and of B when it is read along k)
@@ -942,6 +976,10 @@ size_t train_layout(const rlt_config &c, int B, int T, TrainWs *w, void *base) {
 }
 
 hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
+  // the attention kernels read 16-byte row pieces of the memory
+  if (A.m_seq % 4 || A.m_head % 4 || A.m_pos % 4 || A.m_group % 4 || !aligned16(A.mk) ||
+      !aligned16(A.mv) || (A.dmk && (!aligned16(A.dmk) || !aligned16(A.dmv))))
+    return hipErrorInvalidValue;
   const rlt_config &c = A.c;
   const int B = A.B, T = A.T, L = c.n_layers, d = c.d_model, F = c.d_ffn, H = c.n_heads,
             dh = c.head_dim, V = c.vocab, Wn = c.window, G = c.mem_groups;

@@ -114,6 +114,22 @@ def test_truncated_bptt_matches_oracle(detach):
         assert float(de[:, :3].abs().max()) > 0
 
 
+def test_memory_with_unaligned_rows_is_rejected():
+    """Memory rows must start on 16-byte boundaries (the attention kernels read
+    16-byte pieces): a position stride of dh + 1 elements is a shape error,
+    found before any work."""
+    cfg = ModelConfig(vocab=11, d_model=32, n_heads=2, n_layers=2, d_ffn=64, window=3,
+                      mem_groups=1, dtype=0)
+    params, e, mk, mv, tg = case(cfg, 2, 6)
+    G, B, H, cap, dh = mk.shape
+    padded = torch.zeros((G, B, H, cap, dh + 1), dtype=mk.dtype, device=DEV)
+    view = padded[..., :dh]
+    assert view.stride(-2) == dh + 1
+    with pytest.raises(binding.RLTError) as ex:
+        binding.rlt_bptt(cfg, params, e, (view, view), tg)
+    assert ex.value.status == binding.RLT_ERR_SHAPE
+
+
 def test_bptt_rejects_bf16_and_bad_arguments():
     cfg = ModelConfig(vocab=11, d_model=32, n_heads=2, n_layers=1, d_ffn=64, window=3,
                       mem_groups=1, dtype=1)
