@@ -848,7 +848,8 @@ def run_train(args):
         "value": round(B * T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": max(args.warmup, 1), "ms_per_step": round(ms, 3), "higher_is_better": True,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": SMALL.name.replace("bf16", "f32") + ", BPTT over 128 steps",
+        "config": {"workload": (f"small-f32 model (V={V},d={d},H={H},L={L},F={F},W={W},G={cfg.mem_groups}), "
+                                f"BPTT over B={B} sequences x T={T} steps"),
                    "batch": B, "steps_per_sequence": T, "loss": "next-token cross-entropy, all targets",
                    "gradients": "every parameter, e and memory; full BPTT"},
         "roofline": {"bound": "mfma", "kernel": "whole rlt_bptt call (fp32 MFMA GEMMs, VALU attention)",
