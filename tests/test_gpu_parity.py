@@ -370,6 +370,36 @@ def test_ragged_imported_states_match_oracle():
         assert err <= 1e-4, (j, err)
 
 
+@pytest.mark.parametrize("dtype", [DTYPE_FP32, DTYPE_BF16])
+def test_ragged_batch_is_bitwise_invisible(dtype):
+    """Slots at different positions in one step: the attention launches take
+    the rows longest first; each slot's logits equal those of the same slot
+    stepped alone (one row, no reordering), bit for bit."""
+    cfg = tiny_cfg(dtype=dtype) if dtype == DTYPE_FP32 else BF16_SMALL.with_(n_layers=2, mem_groups=2)
+    starts = [9, 1, 21, 4, 14]        # token index t about to be consumed
+    B, steps = len(starts), 5
+    cap = max(starts) + steps
+    rig = Rig(cfg, B, cap, attn_chunk=3 if dtype == DTYPE_FP32 else 4)
+    recs = []
+    for b, t in enumerate(starts):
+        s = synth.imported_state(cfg, t, index=b)
+        if t == 1:
+            s["s"] = rig.params["s_star"].clone()
+        recs.append(s)
+    snap = binding.build_snapshot(cfg, recs, version=1, device=DEV)
+    together, alone = rig.state(), rig.state()
+    binding.rlt_state_import(rig.model, together, snap, list(range(B)))
+    binding.rlt_state_import(rig.model, alone, snap, list(range(B)))
+    say(f"[ragged bitwise] dtype={dtype} starts={starts}")
+    for j in range(steps):
+        e_rows = torch.stack([rig.e[b, starts[b] - 1 + j] for b in range(B)]).to(DEV)
+        got = binding.rlt_decoder_step(rig.model, together, e_rows, rig.mem).cpu()
+        assert torch.isfinite(got).all()
+        for b in range(B):
+            one = binding.rlt_decoder_step(rig.model, alone, e_rows[b:b + 1], rig.mem, slots=[b]).cpu()
+            assert torch.equal(one[0], got[b]), (j, b)
+
+
 def test_reset_returns_slot_to_initial_state():
     cfg = tiny_cfg()
     B, T = 3, 10
