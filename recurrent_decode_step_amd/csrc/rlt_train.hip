@@ -116,8 +116,10 @@ __global__ __launch_bounds__(256) void k_t_gemm(const float *__restrict__ A, int
 // each an MFMA chain over its chunks in order (lane l holds row / column
 // l & 15 and k = 4 (l >> 4) .. +3 of a chunk in both operands, so the four
 // MFMAs of a chunk pair the same k), and the partial tiles are added in
-// wavefront order through LDS.  Rows and columns past M, N read clamped
-// addresses and are never stored.
+// wavefront order through LDS.  A wavefront loads its chunks in batches
+// into two register sets, the next batch in flight while the current one is
+// multiplied.  Rows and columns past M, N read clamped addresses and are
+// never stored.
 // exact GELU and its derivative
 __device__ __forceinline__ float t_gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 __device__ __forceinline__ float t_gelu_d(float x) {
@@ -162,36 +164,46 @@ __global__ __launch_bounds__(NW * 64) void k_t_sgemm(const SgArgs a) {
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int PB = NT > 2 ? 4 : 8;               // chunks whose loads are in flight together
-  for (int c0 = c_beg; c0 < c_end; c0 += PB) {
-    u32x4 av[PB], bv[PB][NT];
-#pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      const int c = min(c0 + u, c_end - 1);
-      const int sg = c / cps, cl = c - sg * cps;  // segment (0 when there is one)
-      const float *As = sg == 0 ? A0 : (sg == 1 ? A1 : A2);
-      const float *Bs = sg == 0 ? Bo : (sg == 1 ? B1 : B2);
-      const int k = cl * 16 + 4 * g;
-      av[u] = *reinterpret_cast<const u32x4 *>(As + arow + (size_t)cl * 16);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if constexpr (TB) {
-          bv[u][t] = *reinterpret_cast<const u32x4 *>(Bs + (size_t)nc[t] * ldb + k);
-        } else {
-          const float *bp = Bs + (size_t)k * ldb + nc[t];
-          bv[u][t] = u32x4{__float_as_uint(bp[0]), __float_as_uint(bp[ldb]),
-                           __float_as_uint(bp[2 * ldb]), __float_as_uint(bp[3 * ldb])};
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      if (c0 + u < c_end) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = mma_step(av[u], bv[u][t], acc[t], 0.f);
-      }
-    }
+  constexpr int PB = NT > 2 ? 4 : 8;               // chunks per batch of loads (two batches in flight)
+  // batch loads (clamped to the part's last chunk) and their MFMAs, chunks in order
+#define T_SG_LOAD(C0, AV, BV)                                                              \
+  _Pragma("unroll") for (int u = 0; u < PB; ++u) {                                       \
+    const int c = min((C0) + u, c_end - 1);                                               \
+    const int sg = c / cps, cl = c - sg * cps;                                            \
+    const float *As = sg == 0 ? A0 : (sg == 1 ? A1 : A2);                                 \
+    const float *Bs = sg == 0 ? Bo : (sg == 1 ? B1 : B2);                                 \
+    const int k = cl * 16 + 4 * g;                                                        \
+    AV[u] = *reinterpret_cast<const u32x4 *>(As + arow + (size_t)cl * 16);                \
+    _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                     \
+      if constexpr (TB) {                                                                 \
+        BV[u][t] = *reinterpret_cast<const u32x4 *>(Bs + (size_t)nc[t] * ldb + k);        \
+      } else {                                                                            \
+        const float *bp = Bs + (size_t)k * ldb + nc[t];                                   \
+        BV[u][t] = u32x4{__float_as_uint(bp[0]), __float_as_uint(bp[ldb]),                \
+                         __float_as_uint(bp[2 * ldb]), __float_as_uint(bp[3 * ldb])};     \
+      }                                                                                   \
+    }                                                                                     \
   }
+#define T_SG_MMA(C0, AV, BV)                                                               \
+  _Pragma("unroll") for (int u = 0; u < PB; ++u) {                                       \
+    if ((C0) + u < c_end) {                                                               \
+      _Pragma("unroll") for (int t = 0; t < NT; ++t) acc[t] = mma_step(AV[u], BV[u][t], acc[t], 0.f); \
+    }                                                                                     \
+  }
+  // two register sets: the next batch's loads are in flight while this one is
+  // multiplied (the MFMA order is the chunk order either way)
+  u32x4 a0[PB], b0[PB][NT], a1[PB], b1[PB][NT];
+  if (c_beg < c_end) { T_SG_LOAD(c_beg, a0, b0) }
+  for (int c0 = c_beg; c0 < c_end; c0 += 2 * PB) {
+    const int c1 = c0 + PB;
+    if (c1 < c_end) { T_SG_LOAD(c1, a1, b1) }
+    T_SG_MMA(c0, a0, b0)
+    if (c1 >= c_end) break;
+    if (c1 + PB < c_end) { T_SG_LOAD(c1 + PB, a0, b0) }
+    T_SG_MMA(c1, a1, b1)
+  }
+#undef T_SG_LOAD
+#undef T_SG_MMA
 #pragma unroll
   for (int t = 0; t < NT; ++t) part[wave][t][lane] = acc[t];
   __syncthreads();
