@@ -116,10 +116,10 @@ __global__ __launch_bounds__(256) void k_t_gemm(const float *__restrict__ A, int
 // each an MFMA chain over its chunks in order (lane l holds row / column
 // l & 15 and k = 4 (l >> 4) .. +3 of a chunk in both operands, so the four
 // MFMAs of a chunk pair the same k), and the partial tiles are added in
-// wavefront order through LDS.  A wavefront loads its chunks in batches
-// into two register sets, the next batch in flight while the current one is
-// multiplied.  Rows and columns past M, N read clamped addresses and are
-// never stored.
+// wavefront order through LDS.  A wavefront loads its chunks in batches;
+// with DB into two register sets, the next batch in flight while the current
+// one is multiplied (the same MFMAs in the same order, so the same result).
+// Rows and columns past M, N read clamped addresses and are never stored.
 // exact GELU and its derivative
 __device__ __forceinline__ float t_gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 __device__ __forceinline__ float t_gelu_d(float x) {
@@ -142,7 +142,7 @@ struct SgArgs {
   float *C2;
   const float *aux;
 };
-template <bool TB, bool ACC, int NW, int NT>
+template <bool TB, bool ACC, int NW, int NT, bool DB>
 __global__ __launch_bounds__(NW * 64) void k_t_sgemm(const SgArgs a) {
   __shared__ f32x4 part[NW][NT][64];
   // the wavefront index is uniform: keep the chunk range and the operand
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(NW * 64) void k_t_sgemm(const SgArgs a) {
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int PB = NT > 2 ? 4 : 8;               // chunks per batch of loads (two batches in flight)
+  constexpr int PB = NT > 2 ? 4 : 8;               // chunks per batch of loads
   // batch loads (clamped to the part's last chunk) and their MFMAs, chunks in order
 #define T_SG_LOAD(C0, AV, BV)                                                              \
   _Pragma("unroll") for (int u = 0; u < PB; ++u) {                                       \
@@ -190,17 +190,26 @@ __global__ __launch_bounds__(NW * 64) void k_t_sgemm(const SgArgs a) {
       _Pragma("unroll") for (int t = 0; t < NT; ++t) acc[t] = mma_step(AV[u], BV[u][t], acc[t], 0.f); \
     }                                                                                     \
   }
-  // two register sets: the next batch's loads are in flight while this one is
-  // multiplied (the MFMA order is the chunk order either way)
-  u32x4 a0[PB], b0[PB][NT], a1[PB], b1[PB][NT];
-  if (c_beg < c_end) { T_SG_LOAD(c_beg, a0, b0) }
-  for (int c0 = c_beg; c0 < c_end; c0 += 2 * PB) {
-    const int c1 = c0 + PB;
-    if (c1 < c_end) { T_SG_LOAD(c1, a1, b1) }
-    T_SG_MMA(c0, a0, b0)
-    if (c1 >= c_end) break;
-    if (c1 + PB < c_end) { T_SG_LOAD(c1 + PB, a0, b0) }
-    T_SG_MMA(c1, a1, b1)
+  if constexpr (DB) {
+    // two register sets: the next batch's loads are in flight while this one
+    // is multiplied (the MFMA order is the chunk order either way)
+    u32x4 a0[PB], b0[PB][NT], a1[PB], b1[PB][NT];
+    if (c_beg < c_end) { T_SG_LOAD(c_beg, a0, b0) }
+    for (int c0 = c_beg; c0 < c_end; c0 += 2 * PB) {
+      const int c1 = c0 + PB;
+      if (c1 < c_end) { T_SG_LOAD(c1, a1, b1) }
+      T_SG_MMA(c0, a0, b0)
+      if (c1 >= c_end) break;
+      if (c1 + PB < c_end) { T_SG_LOAD(c1 + PB, a0, b0) }
+      T_SG_MMA(c1, a1, b1)
+    }
+  } else {
+    // one register set (fewer registers, more wavefronts per SIMD)
+    for (int c0 = c_beg; c0 < c_end; c0 += PB) {
+      u32x4 a0[PB], b0[PB][NT];
+      T_SG_LOAD(c0, a0, b0)
+      T_SG_MMA(c0, a0, b0)
+    }
   }
 #undef T_SG_LOAD
 #undef T_SG_MMA
@@ -793,21 +802,30 @@ bool sgemm_ok(const float *A, int64_t lda, const float *B, int64_t ldb, bool tb,
          (!tb || (ldb % 4 == 0 && aligned16(B)));
 }
 
-template <bool TB, bool ACC, int NW, int NT>
+template <bool TB, bool ACC, int NW, int NT, bool DB>
 void sgemm_go(const SgArgs &g, int nout, hipStream_t s) {
-  hipLaunchKernelGGL((k_t_sgemm<TB, ACC, NW, NT>), dim3((g.N + 16 * NT - 1) / (16 * NT), (g.M + 15) / 16, nout),
+  hipLaunchKernelGGL((k_t_sgemm<TB, ACC, NW, NT, DB>), dim3((g.N + 16 * NT - 1) / (16 * NT), (g.M + 15) / 16, nout),
                      dim3(NW * 64), 0, s, g);
 }
 
 // Shape choice (measured on the per-step products at 128 rows): 16 x 16 tiles
 // on 4 wavefronts, except wide outputs over a short K (FFN-up, the head and
 // their input gradients), which take 16 x 64 tiles on 8 wavefronts.  The
-// choice depends on N and K only, so a row's result does not depend on the
-// batch.
+// shape depends on N and K only, so a row's result does not depend on the
+// batch.  Two register sets (the next batch of loads in flight) pay at up to
+// 128 rows, where a launch has few workgroups per CU (5% on the training call
+// at 128 sequences); at 256 and 512 sequences the single set's extra
+// wavefronts per SIMD win (1-2%).  Both forms give the same bits.
 template <bool TB, bool ACC>
 void sgemm_launch(const SgArgs &g, int nout, hipStream_t s) {
-  if (g.N >= 2048 && (int64_t)g.K * g.nseg <= 1024) sgemm_go<TB, ACC, 8, 4>(g, nout, s);
-  else sgemm_go<TB, ACC, 4, 1>(g, nout, s);
+  const bool db = g.M <= 128;
+  if (g.N >= 2048 && (int64_t)g.K * g.nseg <= 1024) {
+    if (db) sgemm_go<TB, ACC, 8, 4, true>(g, nout, s);
+    else sgemm_go<TB, ACC, 8, 4, false>(g, nout, s);
+  } else {
+    if (db) sgemm_go<TB, ACC, 4, 1, true>(g, nout, s);
+    else sgemm_go<TB, ACC, 4, 1, false>(g, nout, s);
+  }
 }
 
 template <bool TA, bool TB, bool ACC>

@@ -80,8 +80,10 @@ CONFIGS = [
     ((32, 2, 2, 64, 11, 3, 1), 2, 6),
     ((32, 2, 2, 64, 11, 3, 2), 2, 6),
     ((128, 4, 2, 256, 200, 5, 1), 3, 20),
-    # 128 sequences: per-step products over 128 rows
+    # 128 sequences: per-step products over 128 rows (two register sets of loads)
     ((128, 4, 1, 256, 200, 4, 1), 128, 4),
+    # 144 sequences: past 128 rows the per-step products keep one register set
+    ((128, 4, 1, 256, 200, 4, 1), 144, 3),
     # F = V = 2048: the wide per-step product form (16 x 64 tiles) and, with V a
     # multiple of 16, the MFMA form of the head's input gradient
     ((128, 4, 1, 2048, 2048, 6, 1), 16, 4),
@@ -90,7 +92,7 @@ CONFIGS = [
 ]
 
 
-@pytest.mark.parametrize("spec", CONFIGS, ids=lambda s: "d%d_L%d_W%d_G%d" % (s[0][0], s[0][2], s[0][5], s[0][6]))
+@pytest.mark.parametrize("spec", CONFIGS, ids=lambda s: "d%d_L%d_W%d_G%d_B%d" % (s[0][0], s[0][2], s[0][5], s[0][6], s[1]))
 def test_full_bptt_matches_oracle(spec):
     (d, H, L, F, V, W, G), B, T = spec
     cfg = ModelConfig(vocab=V, d_model=d, n_heads=H, n_layers=L, d_ffn=F, window=W, mem_groups=G,
