@@ -554,13 +554,13 @@ __global__ __launch_bounds__(256) void k_t_attn_fwd(TAttn a) {
     const int c = c0 + lane;
     float acc = 0.f;
     if (c < a.dh) {
-      // eight positions' loads in flight at a time; the sum runs over j in order
-      for (int j = j0; j < j1; j += 8) {
-        float vv[8];
+      // sixteen positions' loads in flight at a time; the sum runs over j in order
+      for (int j = j0; j < j1; j += 16) {
+        float vv[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) vv[u] = V[(size_t)(lo + min(j + u, j1 - 1)) * a.s_pos + c];
+        for (int u = 0; u < 16; ++u) vv[u] = V[(size_t)(lo + min(j + u, j1 - 1)) * a.s_pos + c];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
           if (j + u < j1) acc = fmaf(sc[j + u], vv[u], acc);
       }
     }
@@ -630,12 +630,12 @@ __global__ __launch_bounds__(256) void k_t_attn_bwd(TAttn a) {
     const int c = c0 + lane;
     float acc = 0.f;
     if (c < a.dh) {
-      for (int j = j0; j < j1; j += 8) {
-        float kk[8];
+      for (int j = j0; j < j1; j += 16) {
+        float kk[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) kk[u] = K[(size_t)(lo + min(j + u, j1 - 1)) * a.s_pos + c];
+        for (int u = 0; u < 16; ++u) kk[u] = K[(size_t)(lo + min(j + u, j1 - 1)) * a.s_pos + c];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
           if (j + u < j1) acc = fmaf(sds[j + u], kk[u], acc);
       }
     }
@@ -648,12 +648,12 @@ __global__ __launch_bounds__(256) void k_t_attn_bwd(TAttn a) {
   }
   if (a.dkb) {
     // every position's rows belong to this (row, head) alone: wavefront w takes
-    // positions w, w + 4, ...; eight positions' old values are loaded before
+    // positions w, w + 4, ...; sixteen positions' old values are loaded before
     // any of them is written back, so the read-modify-writes overlap
     float *__restrict__ dK = a.dkb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
     float *__restrict__ dV = a.dvb + (size_t)b * a.s_seq + (size_t)h * a.s_head;
     const int jc = max(0, a.cut_lo - lo);
-    constexpr int U = 8;
+    constexpr int U = 16;
     for (int c = lane; c < a.dh; c += 64) {
       const float qc = q[c], dc = dout[c];
       for (int j0 = jc + wave; j0 < n; j0 += 4 * U) {
