@@ -724,30 +724,32 @@ __global__ void k_t_copy2d(const float *src, int64_t lds, float *dst, int64_t ld
   dst[(size_t)r * ldd + c] = src[(size_t)r * lds + c];
 }
 
-// Loss and dlogits of one step, one wavefront per row:
+// Loss and dlogits of one step, one workgroup of 4 wavefronts per row (the
+// maximum and the sum over the vocabulary reduced across the workgroup):
 // loss_row = logsumexp(z) - z[y]; dz = softmax(z) - onehot(y); y < 0: 0 and 0.
-__global__ void k_t_ce(const float *__restrict__ logits, const int32_t *__restrict__ tg,
-                       int64_t ld_tg, float *__restrict__ dlogits, float *__restrict__ loss_row,
-                       int rows, int V) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (row >= rows) return;
+__global__ __launch_bounds__(256) void k_t_ce(const float *__restrict__ logits, const int32_t *__restrict__ tg,
+                                              int64_t ld_tg, float *__restrict__ dlogits,
+                                              float *__restrict__ loss_row, int rows, int V) {
+  __shared__ float red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  if (row >= rows) return;                       // uniform over the workgroup
   const float *z = logits + (size_t)row * V;
   float *dz = dlogits + (size_t)row * V;
   const int y = tg[(size_t)row * ld_tg];
-  if (y < 0 || y >= V) {
-    for (int c = lane; c < V; c += 64) dz[c] = 0.f;
-    if (lane == 0) loss_row[row] = (y < 0) ? 0.f : __builtin_nanf("");
+  if (y < 0 || y >= V) {                         // uniform over the workgroup
+    for (int c = tid; c < V; c += 256) dz[c] = 0.f;
+    if (tid == 0) loss_row[row] = (y < 0) ? 0.f : __builtin_nanf("");
     return;
   }
   float mx = -INFINITY;
-  for (int c = lane; c < V; c += 64) mx = fmaxf(mx, z[c]);
-  mx = t_wave_max(mx);
+  for (int c = tid; c < V; c += 256) mx = fmaxf(mx, z[c]);
+  mx = t_block_max(mx, red);
   float s = 0.f;
-  for (int c = lane; c < V; c += 64) s += expf(z[c] - mx);
-  s = t_wave_sum(s);
+  for (int c = tid; c < V; c += 256) s += expf(z[c] - mx);
+  s = t_block_sum(s, red);
   const float inv = 1.0f / s;
-  for (int c = lane; c < V; c += 64) dz[c] = expf(z[c] - mx) * inv - (c == y ? 1.0f : 0.0f);
-  if (lane == 0) loss_row[row] = logf(s) + mx - z[y];
+  for (int c = tid; c < V; c += 256) dz[c] = expf(z[c] - mx) * inv - (c == y ? 1.0f : 0.0f);
+  if (tid == 0) loss_row[row] = logf(s) + mx - z[y];
 }
 
 // total = sum of n values in order (one thread)
@@ -1134,7 +1136,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
     float *sn = st(w.sn, t, d), *ro = st(w.ro, t, 1);
     norm_fwd(sv, (const float *)A.p->go, sn, ro);
     t_gemm_go<false, true, false>(sn, d, (const float *)A.p->wout, d, w.logits, V, B, V, d, s, w.split);
-    hipLaunchKernelGGL(k_t_ce, dim3((B + 3) / 4), dim3(256), 0, s, w.logits, A.tg + t, (int64_t)T,
+    hipLaunchKernelGGL(k_t_ce, dim3(B), dim3(256), 0, s, w.logits, A.tg + t, (int64_t)T,
                        st(w.dl, t, V), st(w.lossr, t, 1), B, V);
   }
   hipLaunchKernelGGL(k_t_sum, dim3(1), dim3(64), 0, s, w.lossr, TB, A.loss);
