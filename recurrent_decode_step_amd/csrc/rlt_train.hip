@@ -432,6 +432,7 @@ __global__ void k_t_colsum(const float *__restrict__ a, const float *__restrict_
   if (n >= N) return;
   const int m0 = blockIdx.y * rows_per, m1 = min(M, m0 + rows_per);
   float s = 0.f;
+#pragma unroll 8
   for (int m = m0; m < m1; ++m) {
     float v = a[(size_t)m * ld + n];
     if (b) v *= b[(size_t)m * ld + n];
@@ -445,6 +446,7 @@ __global__ void k_t_colsum_fin(const float *__restrict__ part, int chunks, float
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
   float s = 0.f;
+#pragma unroll 8
   for (int z = 0; z < chunks; ++z) s += part[(size_t)z * N + n];
   out[n] += s;
 }
@@ -781,10 +783,10 @@ unsigned blocks_for(size_t n, unsigned per = 256) { return (unsigned)((n + per -
 // tile 64 x 64, so the partial sums never exceed kSplitTiles * 4096 floats.
 constexpr int kSplitTiles = 256;
 
-// column sums through the split scratch: up to 64 chunks of rows
+// column sums through the split scratch: up to 128 chunks of rows
 void t_colsum(const float *a, const float *b, const float *r, float *out, int M, int N, int64_t ld,
               hipStream_t s, float *split) {
-  int chunks = std::max(1, std::min(64, M / 64));
+  int chunks = std::max(1, std::min(128, M / 64));
   while (chunks > 1 && (size_t)chunks * N > (size_t)kSplitTiles * 4096) --chunks;
   const int rows_per = (M + chunks - 1) / chunks;
   chunks = (M + rows_per - 1) / rows_per;
