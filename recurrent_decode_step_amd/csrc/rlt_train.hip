@@ -351,7 +351,7 @@ __device__ __forceinline__ float t_wave_max(float v) {
 template <int NI>
 __global__ void k_t_norm_fwd(const float *__restrict__ x, const float *__restrict__ gamma, float eps,
                              float *__restrict__ y, float *__restrict__ r_out, int rows, int d) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float *xr = x + (size_t)row * d;
   float ss = 0.f;
@@ -383,7 +383,7 @@ template <int NI>
 __global__ void k_t_norm_bwd(const float *__restrict__ x, const float *__restrict__ r_in,
                              const float *__restrict__ gamma, const float *__restrict__ dy,
                              const float *base, float *dx, float *dx2, int rows, int d) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float r = r_in[row];
   const float *xr = x + (size_t)row * d;
@@ -1034,7 +1034,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
   auto at = [&](float *base, int l, int t, size_t width) { return base + (((size_t)l * T + t) * B) * width; };
   auto st = [&](float *base, int t, size_t width) { return base + (size_t)t * B * width; };
   auto norm_fwd = [&](const float *x, const float *gm, float *y, float *r) {
-    const dim3 g((B + 3) / 4), t(256);
+    const dim3 g(B), t(64);                      // one wavefront (row) per workgroup
     switch (d) {
       case 256: hipLaunchKernelGGL(k_t_norm_fwd<4>, g, t, 0, s, x, gm, eps, y, r, B, d); break;
       case 512: hipLaunchKernelGGL(k_t_norm_fwd<8>, g, t, 0, s, x, gm, eps, y, r, B, d); break;
@@ -1044,7 +1044,7 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
   };
   auto norm_bwd = [&](const float *x, const float *r, const float *gm, const float *dy, const float *base,
                       float *dx, float *dx2) {
-    const dim3 g((B + 3) / 4), t(256);
+    const dim3 g(B), t(64);                      // one wavefront (row) per workgroup
     switch (d) {
       case 256: hipLaunchKernelGGL(k_t_norm_bwd<4>, g, t, 0, s, x, r, gm, dy, base, dx, dx2, B, d); break;
       case 512: hipLaunchKernelGGL(k_t_norm_bwd<8>, g, t, 0, s, x, r, gm, dy, base, dx, dx2, B, d); break;
