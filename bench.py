@@ -6,9 +6,16 @@ Default workload: the reference-depth model (48 layers, d = 2048, 16 heads,
 FFN 8192, window 512, one shared memory group, V = 32768, bf16) on 32
 sequences: 2048 prompt tokens through rlt_run_sequence, then 512 single
 rlt_decoder_step calls on the same state (no reset at the split).  A "step" is
-one decoder step over the whole batch; --steps K times the first K steps of
-that run (default: all 2560).  Inputs are synthetic (seeded, drawn on the GPU)
-and resident in HBM before timing starts; logits of every step are written.
+one decoder step over the whole batch.  With no --steps the whole 2560-step
+run is timed.  --steps K < 2560 times K steps at positions stratified over the
+run instead: the run is cut into min(K, 20) equal strata of positions, a
+resident state of all 32 sequences is imported (synthetic history, the
+imported-state reading) at the middle of each stratum, and the K steps go
+round those states in order, each consuming that state's next token; the K
+steps are enqueued back to back and timed as one region, so their mean
+position is the run's (about 1280) and the per-step work is the run's mean.
+Inputs are synthetic (seeded, drawn on the GPU) and resident in HBM before
+timing starts; logits of every step are written.
 
 Printed: one JSON line with the throughput, the roofline figure of the
 dominant kernel (cross-attention over the encoder memory), measured with HIP
@@ -296,6 +303,207 @@ def run_refdepth(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, params, e, mk, mv, t0=(K + 1) // 2,
                                            budget_s=args.cpu_budget)
+    return out
+
+
+def stratified_positions(T_total, K, n_states):
+    """Strata of the positions 1..T_total: state j serves steps k = j, j + n,
+    j + 2n, ... of the K timed steps and consumes r_j consecutive tokens
+    from t_j, centred on the middle of stratum j."""
+    starts, counts = [], []
+    for j in range(n_states):
+        r = len(range(j, K, n_states))
+        mid = (j + 0.5) * T_total / n_states
+        t0 = int(round(mid - (r - 1) / 2))
+        t0 = max(1, min(t0, T_total - r + 1))
+        starts.append(t0)
+        counts.append(r)
+    return starts, counts
+
+
+def cpu_baseline_at(cfg, params_gpu, e_gpu, mk_gpu, mv_gpu, positions, budget_s=15.0):
+    """The oracle (fp32 NumPy, as it stands) on the host: one batched step of
+    all sequences at each sampled position, taken in pairs symmetric about the
+    mean of `positions` (so the sample's mean position is the run's), each
+    from synthetic states imported there, until the time budget is spent."""
+    import oracle
+    dev = e_gpu.device
+    params = {k: v.float().cpu() for k, v in params_gpu.items()}
+    B = e_gpu.shape[0]
+    om = oracle.Model(params=params, precision="fp32", d_model=cfg.d_model, n_heads=cfg.n_heads,
+                      n_layers=cfg.n_layers, d_ffn=cfg.d_ffn, window=cfg.window,
+                      mem_groups=cfg.mem_groups, vocab=cfg.vocab, rms_eps=cfg.rms_eps)
+    del params
+    ps = sorted(positions)
+    order = []
+    lo, hi = 0, len(ps) - 1
+    while lo <= hi:
+        order.append(ps[lo])
+        if hi != lo:
+            order.append(ps[hi])
+        lo, hi = lo + 1, hi - 1
+    t_max = max(ps)
+    mk = mk_gpu[:, :, :, :t_max].float().cpu().numpy()
+    mv = mv_gpu[:, :, :, :t_max].float().cpu().numpy()
+    spent, prep, done = 0.0, 0.0, []
+    for t in order:
+        t_prep = time.time()
+        states = []
+        for b in range(B):
+            r = synthetic_record(cfg, params_gpu, t, dev, b)
+            states.append(oracle.state_from_arrays(om, r["pos"], r["s"].float().cpu(),
+                                                   r["K"].float().cpu(), r["V"].float().cpu()))
+            del r
+        e = e_gpu[:, t - 1].float().cpu()
+        prep += time.time() - t_prep
+        t0 = time.time()
+        oracle.decoder_step(om, states, e, mk, mv)
+        spent += time.time() - t0
+        done.append(t)
+        del states
+        if spent >= budget_s and len(done) % 2 == 0:
+            break
+    return {"value": B * len(done) / spent, "unit": "token-steps/s", "cores": openblas_threads(),
+            "kind": "oracle",
+            "sample": f"{B} sequences x {len(done)} batched steps at t = "
+                      f"{', '.join(str(t) for t in done)} (pairs symmetric about the run's mean "
+                      f"position; mean t = {sum(done) / len(done):.0f}), each from synthetic "
+                      f"states imported there, NumPy fp32 oracle, weights read once per step for "
+                      f"the batch ({spent:.1f} s timed, {prep:.1f} s state preparation untimed)"}
+
+
+def run_refdepth_stratified(args):
+    """K timed steps of the reference-depth run at positions stratified over
+    1..2560 (see the module docstring)."""
+    import torch
+    from recurrent_decode_step_amd import binding, synth
+    from recurrent_decode_step_amd.configs import REFDEPTH
+
+    wl = REFDEPTH
+    cfg = wl.model
+    B, T_total = wl.batch, wl.steps
+    K = args.steps
+    n_states = min(K, 20)
+    starts, counts = stratified_positions(T_total, K, n_states)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    es = 2
+    t_setup = time.time()
+    params = synth.model_params(cfg, device=dev)
+    model = binding.Model(cfg, params, version=1)
+    e = synth.encoder_e(cfg, B, T_total, device=dev)
+    mk, mv = synth.encoder_memory(cfg, B, T_total, device=dev)
+    mem = binding.memory_view(mk, mv)
+    e_by_step = e.transpose(0, 1).contiguous()       # [T][B][d]: one contiguous block per step
+    states = []
+    for j in range(n_states):
+        st = binding.State(model, B, T_total)
+        import_positions(model, st, cfg, params, [starts[j]] * B, dev)
+        states.append(st)
+        if args.progress:
+            print(f"state {j} imported at t = {starts[j]}", file=sys.stderr, flush=True)
+    logits = torch.empty((n_states, B, cfg.vocab), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    if args.calibrate_copy:
+        calibration_copy(dev)
+
+    # warmup: W steps on a separate state at the run's mean position (untimed)
+    if args.warmup > 0:
+        t_mid = T_total // 2
+        ws = binding.State(model, B, T_total)
+        import_positions(model, ws, cfg, params, [t_mid] * B, dev)
+        for j in range(args.warmup):
+            binding.rlt_decoder_step(model, ws, e_by_step[min(t_mid - 1 + j, T_total - 1)], mem,
+                                     logits=logits[0])
+        torch.cuda.synchronize()
+        del ws
+    torch.cuda.synchronize()
+
+    classes = (binding.RLT_K_EXTRA, binding.RLT_K_GEMM, binding.RLT_K_SWA, binding.RLT_K_CROSS)
+    mask = (1 << binding.RLT_K_CROSS) if not args.breakdown else sum(1 << c for c in classes)
+    for st in states:
+        binding.profile_begin(st, mask, 1 << 16, step_stride=1)
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    next_t = list(starts)
+    positions = []
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for k in range(K):
+        j = k % n_states
+        t = next_t[j]
+        binding.rlt_decoder_step(model, states[j], e_by_step[t - 1], mem, logits=logits[j])
+        positions.append(t)
+        next_t[j] = t + 1
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    prof = {c: [0.0, 0, 0.0] for c in classes}
+    for st in states:
+        for c in classes:
+            a, n, b = binding.profile_collect(st, c)
+            prof[c][0] += a
+            prof[c][1] += n
+            prof[c][2] += b
+        binding.profile_begin(st, 0, 0)
+    for j, st in enumerate(states):
+        assert all(st.position(b) == starts[j] - 1 + counts[j] for b in range(B))
+    if not torch.isfinite(logits).all():
+        raise RuntimeError("non-finite logits")
+
+    bytes_run = sum(algorithmic_bytes_per_step(cfg, [t] * B, es) for t in positions)
+    cross_ms, cross_n, cross_bytes = prof[binding.RLT_K_CROSS]
+    cross_avg_ms = cross_ms / max(cross_n, 1)
+    achieved = cross_bytes / max(cross_n, 1) / (cross_avg_ms / 1e3) / 1e9
+    traffic = measured_traffic(cross_bytes / max(cross_n, 1))
+    mean_t = sum(positions) / len(positions)
+    out = {
+        "metric": "decoder token-steps/sec at 1 GPU (48-layer, B=32/256); % HBM/MFMA roofline",
+        "value": round(B * K / (ms / 1e3), 2),
+        "unit": "token-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B,
+                   "method": f"{K} steps at positions stratified over 1..{T_total}: {n_states} "
+                             f"resident states imported at the strata's middles, steps taken "
+                             f"round the states back to back in one timed region",
+                   "positions": f"{min(positions)}..{max(positions)} in {n_states} strata, "
+                                f"mean t = {mean_t:.1f}",
+                   "strata_starts": starts,
+                   "logits": "every step, fp32"},
+        "roofline": {"bound": "hbm", "kernel": "k_attn<bf16,128,1> (cross-attention, encoder memory)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "algorithmic_bytes_per_launch": round(cross_bytes / max(cross_n, 1)),
+                     "launches_timed": cross_n, "avg_launch_us": round(cross_avg_ms * 1e3, 2)},
+        "step_roofline": {"bound": "hbm", "algorithmic_GB_per_step": round(bytes_run / K / 1e9, 3),
+                          "achieved": round(bytes_run / (ms / 1e3) / 1e9, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(bytes_run / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "setup_s": round(setup_s, 1),
+    }
+    if args.breakdown:
+        names = {binding.RLT_K_EXTRA: "extra", binding.RLT_K_GEMM: "gemm",
+                 binding.RLT_K_SWA: "window_attention", binding.RLT_K_CROSS: "cross_attention"}
+        out["breakdown_ms_per_step"] = {names[c]: round(prof[c][0] / K, 4) for c in classes}
+        out["breakdown_GBps"] = {
+            names[c]: round(prof[c][2] / (prof[c][0] / 1e3) / 1e9, 1) if prof[c][0] else None
+            for c in classes}
+    del states
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_at(cfg, params, e, mk, mv, sorted(set(positions)),
+                                              budget_s=args.cpu_budget)
     return out
 
 
@@ -938,6 +1146,8 @@ def main():
     elif args.workload in ("tiny", "small"):
         from recurrent_decode_step_amd.configs import TINY, SMALL
         out = run_full_sequence(args, TINY if args.workload == "tiny" else SMALL)
+    elif args.steps is not None and args.steps < 2560:
+        out = run_refdepth_stratified(args)
     else:
         out = run_refdepth(args)
     print(json.dumps(out), flush=True)

@@ -128,8 +128,16 @@ class Model:
         return {k: _to_np(v, self.dt) for k, v in self._layer_source(l).items()}
 
     # --- elementwise pieces -------------------------------------------------
-    def R(self, x):
-        """Storage rounding point: bf16 in the bf16 emulation, identity otherwise."""
+    # The storage rounding points of a bf16 model (reading: every value a bf16
+    # model stores is a bf16 number; accumulation, softmax, the residual
+    # stream, s_t and the logits stay fp32).  Each call site of R names its
+    # point, so a test can trace every rounded value and drop one point.
+    ROUNDING_POINTS = ("gate_s", "norm1", "q", "k", "v", "swa_out", "norm2", "qc",
+                       "cross_out", "norm3", "ffn_hidden", "norm_out")
+
+    def R(self, x, point=None):
+        """Storage rounding point `point`: bf16 in the bf16 emulation, identity
+        otherwise."""
         return round_bf16(x) if self.bf16 else x
 
     def rms(self, x, gamma):
@@ -157,7 +165,7 @@ class Model:
         """Gated merge (reading): g = sigmoid(W_g [e ; s] + b_g),
         u = g * e + (1 - g) * s.  The gate input takes bf16(s) in the bf16
         emulation; the mix uses s itself."""
-        z = np.concatenate([e, self.R(s_prev)], axis=-1) @ self.wg.T + self.bg
+        z = np.concatenate([e, self.R(s_prev, "gate_s")], axis=-1) @ self.wg.T + self.bg
         g = _expit(z).astype(self.dt)
         return g * e + (self.dt(1.0) - g) * s_prev
 
@@ -230,10 +238,10 @@ def decoder_step(model: Model, states, e_rows, mem_k, mem_v, mem_index=None, tra
         P = m.layer(l)
         # (1) causal sliding-window self-attention, window = positions
         #     max(1, t-W+1) .. t, the current token's entry included
-        a = m.R(m.rms(x, P["g1"]))
-        q = m.R(a @ P["wq"].T).reshape(n, m.H, m.dh)
-        k = m.R(a @ P["wk"].T).reshape(n, m.H, m.dh)
-        v = m.R(a @ P["wv"].T).reshape(n, m.H, m.dh)
+        a = m.R(m.rms(x, P["g1"]), "norm1")
+        q = m.R(a @ P["wq"].T, "q").reshape(n, m.H, m.dh)
+        k = m.R(a @ P["wk"].T, "k").reshape(n, m.H, m.dh)
+        v = m.R(a @ P["wv"].T, "v").reshape(n, m.H, m.dh)
         o = np.empty((n, m.H, m.dh), dtype=dt)
         for i, st in enumerate(states):
             Kw = np.concatenate([st.K[l], k[i:i + 1]], axis=0)
@@ -245,20 +253,20 @@ def decoder_step(model: Model, states, e_rows, mem_k, mem_v, mem_index=None, tra
             first_kept = max(0, Kw.shape[0] - (m.W - 1))
             st.K[l] = Kw[first_kept:].copy()
             st.V[l] = Vw[first_kept:].copy()
-        x = x + m.R(o.reshape(n, m.d)) @ P["wo"].T
+        x = x + m.R(o.reshape(n, m.d), "swa_out") @ P["wo"].T
         # (2) cross-attention to encoder memory positions 1..t
-        c = m.R(m.rms(x, P["g2"]))
-        qc = m.R(c @ P["wqc"].T).reshape(n, m.H, m.dh)
+        c = m.R(m.rms(x, P["g2"]), "norm2")
+        qc = m.R(c @ P["wqc"].T, "qc").reshape(n, m.H, m.dh)
         grp = 0 if m.G == 1 else l
         oc = np.empty((n, m.H, m.dh), dtype=dt)
         for i in range(n):
             Km = _to_np(mem_k[grp, mem_index[i], :, :t[i], :], dt).transpose(1, 0, 2)
             Vm = _to_np(mem_v[grp, mem_index[i], :, :t[i], :], dt).transpose(1, 0, 2)
             oc[i] = m.attend(qc[i], Km, Vm)
-        x = x + m.R(oc.reshape(n, m.d)) @ P["woc"].T
+        x = x + m.R(oc.reshape(n, m.d), "cross_out") @ P["woc"].T
         # (3) feed-forward network
-        f = m.R(m.rms(x, P["g3"]))
-        h = m.R(m.gelu(f @ P["w1"].T))
+        f = m.R(m.rms(x, P["g3"]), "norm3")
+        h = m.R(m.gelu(f @ P["w1"].T), "ffn_hidden")
         x = x + h @ P["w2"].T
         if trace is not None:
             trace.setdefault("q", []).append(q.copy())
@@ -271,7 +279,7 @@ def decoder_step(model: Model, states, e_rows, mem_k, mem_v, mem_index=None, tra
         st.s = x[i].copy()
         st.pos += 1
     # next-token logits from s_t [Tutorial, "How the Architecture Works"]
-    return m.R(m.rms(x, m.go)) @ m.wout.T
+    return m.R(m.rms(x, m.go), "norm_out") @ m.wout.T
 
 
 def run_sequence(model: Model, states, e, mem_k, mem_v, mem_index=None, steps=None,

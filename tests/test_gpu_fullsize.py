@@ -73,8 +73,8 @@ def run_case(wl, positions, sample, chunk=8):
                       layer_source=lambda l: {k: params[k][l].float().cpu() for k in LAYER_KEYS})
     states = [oracle.state_from_arrays(om, kept[b]["pos"], kept[b]["s"], kept[b]["K"],
                                        kept[b]["V"]) for b in sample]
-    rows_mk = mk[:, sample].float().cpu()
-    rows_mv = mv[:, sample].float().cpu()
+    rows_mk = mk[:, sample].float().cpu().numpy()
+    rows_mv = mv[:, sample].float().cpu().numpy()
     ref = oracle.decoder_step(om, states, e[sample].float().cpu(), rows_mk, rows_mv)
     for j, b in enumerate(sample):
         rel = float(np.linalg.norm(got[b] - ref[j]) / np.linalg.norm(ref[j]))
@@ -107,3 +107,58 @@ def test_longctx_full_batch_sampled_rows():
     wl = LONGCTX
     pos = [1, 4096, 4097, 300, 9000, 20000, 32768, 5000]
     run_case(wl, pos, sample=[2, 6], chunk=2)
+
+
+def test_small_full_run_sampled_rows():
+    """The small bf16 workload at its own size and in its own launch shape:
+    64 sequences from H_0 through 1024 steps of rlt_run_sequence (G = 12
+    memory groups, W = 128).  At sampled steps the states of four sequences
+    are exported and the oracle, in its bf16 emulation and in fp32, takes
+    that step from the same state; rel-L2 of the logits <= 2e-2 each.  The
+    last step checked is the run's last (t = 1024, memory 1024 long, window
+    wrapped eight times)."""
+    from recurrent_decode_step_amd.configs import SMALL
+    from _tiny import oracle_state_from_snapshot
+    wl = SMALL
+    cfg = wl.model
+    B, T = wl.batch, wl.steps
+    rows = [0, 21, 42, 63]
+    check = [1, 2, 128, 129, 512, 1024]
+    say(f"[fullsize] {wl.name}: B={B} T={T} sampled rows {rows} at steps {check}")
+    params = synth.model_params(cfg, device=DEV)
+    model = binding.Model(cfg, params, version=1)
+    e = synth.encoder_e(cfg, B, T, device=DEV)
+    mk, mv = synth.encoder_memory(cfg, B, T, device=DEV)
+    mem = binding.memory_view(mk, mv)
+    state = binding.State(model, B, T)
+    snaps, got = {}, {}
+    done = 0
+    for t in check:
+        if t - 1 > done:
+            binding.rlt_run_sequence(model, state, e[:, done:t - 1], mem,
+                                     logits_mode=binding.RLT_LOGITS_NONE)
+        snaps[t] = binding.rlt_state_export(model, state, rows).cpu()
+        got[t] = binding.rlt_run_sequence(model, state, e[:, t - 1:t], mem)[:, 0].cpu().numpy()
+        done = t
+    torch.cuda.synchronize()
+    for b in range(B):
+        assert state.position(b) == T
+    cpu = {k: v.float().cpu() for k, v in params.items()}
+    e_rows = e[rows].float().cpu()
+    mk_rows = mk[:, rows].float().cpu().numpy()
+    mv_rows = mv[:, rows].float().cpu().numpy()
+    for prec in ("bf16", "fp32"):
+        om = oracle.Model(params=cpu, precision=prec, d_model=cfg.d_model, n_heads=cfg.n_heads,
+                          n_layers=cfg.n_layers, d_ffn=cfg.d_ffn, window=cfg.window,
+                          mem_groups=cfg.mem_groups, vocab=cfg.vocab, rms_eps=cfg.rms_eps)
+        worst = 0.0
+        for t in check:
+            for j, b in enumerate(rows):
+                ost = oracle_state_from_snapshot(om, cfg, snaps[t], j)
+                assert ost.pos == t - 1
+                ref = oracle.decoder_step(om, [ost], e_rows[[j], t - 1], mk_rows, mv_rows,
+                                          mem_index=[j])
+                rel = float(np.linalg.norm(got[t][b] - ref[0]) / np.linalg.norm(ref[0]))
+                worst = max(worst, rel)
+                assert rel <= 2e-2, (prec, t, b, rel)
+        say(f"[fullsize] small: worst per-step rel-L2 vs the {prec} oracle {worst:.2e}")

@@ -37,6 +37,7 @@ class Rig:
         self.e, self.mk, self.mv = inputs(cfg, B, T, capacity or T)
         self.model = binding.Model(cfg, to_dev(self.params), version=version, attn_chunk=attn_chunk)
         self.mem = (self.mk.to(DEV), self.mv.to(DEV))
+        self.mk_np, self.mv_np = self.mk.float().numpy(), self.mv.float().numpy()
         self.ed = self.e.to(DEV)
         self.capacity = capacity or T
 
@@ -51,12 +52,12 @@ class Rig:
         m = self.oracle_model(precision)
         rows = list(range(self.B)) if rows is None else rows
         st = [oracle.initial_state(m) for _ in rows]
-        return oracle.run_sequence(m, st, self.e[rows], self.mk, self.mv, mem_index=rows,
+        return oracle.run_sequence(m, st, self.e[rows], self.mk_np, self.mv_np, mem_index=rows,
                                    steps=steps)
 
 
 F32_CASES = {
-    "tiny": (dict(), 0, 4, 40),
+    "tiny": (dict(), 0, 4, 64),                     # the tiny fp32 workload: B = 4, T = 64
     "tiny-chunk3": (dict(), 3, 4, 40),              # several attention chunks + combine
     "window1": (dict(window=1), 0, 3, 20),
     "window2-chunk1": (dict(window=2), 1, 3, 20),
@@ -108,53 +109,78 @@ BF16_SMALL = ModelConfig(vocab=4096, d_model=512, n_heads=8, n_layers=12, d_ffn=
 
 
 def test_bf16_small_model_matches_oracle():
-    """The small bf16 model (d=512, 8 heads, 12 layers, G = 12, W = 128),
-    8 sequences over 150 steps (past the window).
+    """The small bf16 model (d=512, 8 heads, 12 layers, G = 12, W = 128), all
+    8 sequences over 150 steps (past the window), two bars:
 
-    The bar is per step: before each checked step the library's exact state is
-    exported and the oracle takes the same step from it; rel-L2 of the logits
-    <= 2e-2.  Free-running trajectories of this random-weight recurrence
-    amplify any rounding difference (the oracle's own bf16 emulation drifts from
-    its float64 run by a few 1e-2 over 150 steps), so the free-running gap is
-    printed, and checked only against that drift."""
+    Per step: before each checked step the library's exact state is exported
+    and the oracle (fp32, and its bf16 emulation) takes the same step from
+    it; rel-L2 of the logits <= 2e-2.
+
+    Free-running, every step t: the recurrence amplifies any rounding
+    difference (the oracle's perturbation probe: a 2^-9 jitter of the inputs
+    grows more than 10x over 150 steps), so the library's trajectory is
+    compared with the oracle's own bf16 drift D(t) = rel-L2(bf16 emulation,
+    float64) over the same 8 sequences:
+      rel-L2(library, bf16 emulation) <= C_DRIFT * D(t) at every step, and
+      <= 2e-2 at every step before D first reaches 2e-2.
+    C_DRIFT = 3: if the library's accumulated rounding error has the
+    emulation's size and is independent of it, their difference is about
+    sqrt(2) D(t); 3 allows the library's own error to be up to about twice
+    the emulation's (it rounds the normed activation at a different point
+    and sums in another order), while a dropped rounding, a wrong index or a
+    stale cache entry shows up as a gap many times D(t)."""
+    C_DRIFT = 3.0
     cfg = BF16_SMALL
     B, T = 8, 150
     say(f"[bf16 parity] small model B={B} T={T}")
     rig = Rig(cfg, B, T)
     st = rig.state()
-    rows = [0, 5]
+    rows = list(range(B))
     check = {1, 2, 3, 10, 64, 127, 128, 129, 150}
     snaps, got = {}, []
     for j in range(T):
         if j + 1 in check:
             snaps[j + 1] = binding.rlt_state_export(rig.model, st, rows).cpu()
         got.append(binding.rlt_decoder_step(rig.model, st, rig.ed[:, j], rig.mem).cpu().numpy())
-    got = np.stack(got, 1)
+    got = np.stack(got, 1).astype(np.float64)
     worst = {"fp32": 0.0, "bf16": 0.0}
     for prec in worst:
         m = rig.oracle_model(prec)
         for t in sorted(check):
-            for i, r in enumerate(rows):
-                ost = oracle_state_from_snapshot(m, cfg, snaps[t], i)
+            for r in rows:
+                ost = oracle_state_from_snapshot(m, cfg, snaps[t], r)
                 assert ost.pos == t - 1
-                ref = oracle.decoder_step(m, [ost], rig.e[[r], t - 1], rig.mk, rig.mv,
+                ref = oracle.decoder_step(m, [ost], rig.e[[r], t - 1], rig.mk_np, rig.mv_np,
                                           mem_index=[r])
                 worst[prec] = max(worst[prec], rel_l2(got[r, t - 1], ref[0]))
     say(f"  per-step rel-L2 from the same state: fp32 oracle {worst['fp32']:.3e}, "
         f"bf16 emulation {worst['bf16']:.3e}")
     assert worst["fp32"] <= 2e-2
     assert worst["bf16"] <= 2e-2
-    # free-running: report, and compare with the oracle's own bf16-vs-fp64 drift
-    ref32 = rig.oracle_run("fp32", rows=rows)
-    ref64 = rig.oracle_run("fp64", rows=rows)
-    ref16 = rig.oracle_run("bf16", rows=rows)
-    for i, r in enumerate(rows):
-        g = [rel_l2(got[r, t], ref32[i, t]) for t in range(T)]
-        o = [rel_l2(ref16[i, t], ref64[i, t]) for t in range(T)]
-        say(f"  row {r} free-running rel-L2 (t=1,10,50,100,150): gpu-vs-fp32 "
-            + ", ".join(f"{g[t]:.2e}" for t in (0, 9, 49, 99, 149))
-            + " | oracle bf16-vs-fp64 " + ", ".join(f"{o[t]:.2e}" for t in (0, 9, 49, 99, 149)))
-        assert g[0] <= 2e-2
+    # free-running, all rows, every step
+    ref64 = rig.oracle_run("fp64").astype(np.float64)
+    ref16 = rig.oracle_run("bf16").astype(np.float64)
+
+    def rel_rows(a, b):
+        return np.linalg.norm(a - b, axis=(0, 2)) / np.linalg.norm(b, axis=(0, 2))
+
+    drift = rel_rows(ref16, ref64)            # the oracle's own bf16 drift D(t)
+    gap = rel_rows(got, ref16)                # library vs bf16 emulation
+    gap64 = rel_rows(got, ref64)              # library vs float64
+    for t in (1, 2, 5, 10, 20, 50, 75, 100, 128, 150):
+        say(f"  t={t:3d}  library-vs-bf16emu {gap[t - 1]:.3e}  library-vs-fp64 "
+            f"{gap64[t - 1]:.3e}  oracle bf16-vs-fp64 D {drift[t - 1]:.3e}  "
+            f"ratio {gap[t - 1] / drift[t - 1]:.2f}")
+    worst_ratio = float(np.max(gap / drift))
+    say(f"  max over steps of gap / D = {worst_ratio:.2f} (bar {C_DRIFT})")
+    assert np.all(gap <= C_DRIFT * drift), worst_ratio
+    crossed = np.nonzero(drift >= 2e-2)[0]
+    early = int(crossed[0]) if crossed.size else T
+    say(f"  D first reaches 2e-2 at step {early + 1 if crossed.size else None}; "
+        f"max gap before it {float(gap[:early].max()):.3e}")
+    assert np.all(gap[:early] <= 2e-2)
+    for b in rows:
+        assert st.position(b) == T
 
 
 BF16_TINY_CASES = {
@@ -184,7 +210,7 @@ def test_bf16_small_dims_match_oracle_per_step(name):
         assert np.isfinite(got).all(), j
         for r in (0, B - 1):
             ost = oracle_state_from_snapshot(m, cfg, snap, r)
-            ref = oracle.decoder_step(m, [ost], rig.e[[r], j], rig.mk, rig.mv, mem_index=[r])
+            ref = oracle.decoder_step(m, [ost], rig.e[[r], j], rig.mk_np, rig.mv_np, mem_index=[r])
             worst = max(worst, rel_l2(got[r], ref[0]))
     say(f"  per-step rel-L2 vs fp32 oracle: {worst:.3e}")
     assert worst <= 2e-2
@@ -331,7 +357,7 @@ def test_snapshot_history_matches_oracle_cache():
     snap = binding.rlt_state_export(rig.model, st, [0, 1]).cpu()
     m = rig.oracle_model()
     ost = [oracle.initial_state(m) for _ in range(B)]
-    oracle.run_sequence(m, ost, rig.e, rig.mk, rig.mv)
+    oracle.run_sequence(m, ost, rig.e, rig.mk_np, rig.mv_np)
     rec, off_s, off_k, off_v = binding.snapshot_layout(cfg)
     L, H, dh, Wm1 = cfg.n_layers, cfg.n_heads, cfg.head_dim, cfg.window - 1
     for b in range(B):
@@ -365,7 +391,7 @@ def test_ragged_imported_states_match_oracle():
     for j in range(steps):
         e_rows = torch.stack([rig.e[b, starts[b] - 1 + j] for b in range(B)])
         got = binding.rlt_decoder_step(rig.model, st, e_rows.to(DEV), rig.mem).cpu().numpy()
-        ref = oracle.decoder_step(m, ost, e_rows, rig.mk, rig.mv)
+        ref = oracle.decoder_step(m, ost, e_rows, rig.mk_np, rig.mv_np)
         err = float(np.max(np.abs(got - ref)))
         assert err <= 1e-4, (j, err)
 
@@ -515,7 +541,7 @@ def test_score_sequence_f32_matches_oracle():
     say("[score f32]")
     got = binding.rlt_score_sequence(rig.model, rig.state(), rig.ed, rig.mem, tokens.to(DEV)).cpu().numpy()
     m = rig.oracle_model()
-    ref = oracle.score_sequence(m, [oracle.initial_state(m) for _ in range(B)], rig.e, rig.mk, rig.mv,
+    ref = oracle.score_sequence(m, [oracle.initial_state(m) for _ in range(B)], rig.e, rig.mk_np, rig.mv_np,
                                 tokens.numpy())
     err = float(np.max(np.abs(got - ref)))
     say(f"  max|d logprob| = {err:.3e}")
