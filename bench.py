@@ -58,13 +58,21 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "k_attn_cross_refdepth_b32_counte
 
 
 def source_sha256(paths=KERNEL_SOURCE):
-    """sha256 over the decoder kernel sources (the kernels and their device helpers)."""
+    """sha256 over the cross-attention kernel's own source: the device helpers
+    (rlt_device.h), the attention section of rlt_kernels.hip and its launcher
+    functions (attn_dispatch, launch_attn, attn_chunk_max).  Edits to the
+    GEMMs or other kernels leave it unchanged."""
     import hashlib
-    h = hashlib.sha256()
-    for path in paths:
-        with open(path, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+    import re
+    kernels, device = paths
+    text = open(kernels).read()
+    a = text.index("// ---------------------------------------------------------------- attention")
+    b = text.index("// ----------------------------------------------------------------", a + 10)
+    parts = [open(device).read(), text[a:b]]
+    for name in ("attn_dispatch", "launch_attn", "attn_chunk_max"):
+        m = re.search(r"\n[^\n]*\b" + name + r"\([^)]*\) \{.*?\n\}\n", text, re.S)
+        parts.append(m.group(0) if m else "")
+    return hashlib.sha256("\0".join(parts).encode()).hexdigest()
 
 
 def measured_traffic(algorithmic_per_launch, path=COUNTERS_FILE):
@@ -420,10 +428,14 @@ def run_refdepth_stratified(args):
         del ws
     torch.cuda.synchronize()
 
+    # the kernel figure: every launch of the chosen class in the states of
+    # the strata pairs (j, n-1-j) with j even, half the strata, symmetric about
+    # the run's mean position; the launch carries its own timing events
     classes = (binding.RLT_K_EXTRA, binding.RLT_K_GEMM, binding.RLT_K_SWA, binding.RLT_K_CROSS)
     mask = (1 << binding.RLT_K_CROSS) if not args.breakdown else sum(1 << c for c in classes)
-    for st in states:
-        binding.profile_begin(st, mask, 1 << 16, step_stride=1)
+    profiled = [j for j in range(n_states) if min(j, n_states - 1 - j) % 2 == 0]
+    for j in profiled:
+        binding.profile_begin(states[j], mask, 1 << 16, step_stride=1)
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -441,13 +453,14 @@ def run_refdepth_stratified(args):
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1)
     prof = {c: [0.0, 0, 0.0] for c in classes}
-    for st in states:
+    for j in profiled:
         for c in classes:
-            a, n, b = binding.profile_collect(st, c)
+            a, n, b = binding.profile_collect(states[j], c)
             prof[c][0] += a
             prof[c][1] += n
             prof[c][2] += b
-        binding.profile_begin(st, 0, 0)
+        binding.profile_begin(states[j], 0, 0)
+    prof_steps = sum(counts[j] for j in profiled)
     for j, st in enumerate(states):
         assert all(st.position(b) == starts[j] - 1 + counts[j] for b in range(B))
     if not torch.isfinite(logits).all():
@@ -485,7 +498,10 @@ def run_refdepth_stratified(args):
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic),
                      "algorithmic_bytes_per_launch": round(cross_bytes / max(cross_n, 1)),
-                     "launches_timed": cross_n, "avg_launch_us": round(cross_avg_ms * 1e3, 2)},
+                     "launches_timed": cross_n, "avg_launch_us": round(cross_avg_ms * 1e3, 2),
+                     "timing": f"events bound to each launch's own dispatch, every launch of the "
+                               f"{len(profiled)} strata {profiled} (pairs symmetric about the "
+                               f"mean position)"},
         "step_roofline": {"bound": "hbm", "algorithmic_GB_per_step": round(bytes_run / K / 1e9, 3),
                           "achieved": round(bytes_run / (ms / 1e3) / 1e9, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -495,7 +511,8 @@ def run_refdepth_stratified(args):
     if args.breakdown:
         names = {binding.RLT_K_EXTRA: "extra", binding.RLT_K_GEMM: "gemm",
                  binding.RLT_K_SWA: "window_attention", binding.RLT_K_CROSS: "cross_attention"}
-        out["breakdown_ms_per_step"] = {names[c]: round(prof[c][0] / K, 4) for c in classes}
+        out["breakdown_ms_per_step"] = {names[c]: round(prof[c][0] / prof_steps, 4)
+                                        for c in classes}
         out["breakdown_GBps"] = {
             names[c]: round(prof[c][2] / (prof[c][0] / 1e3) / 1e9, 1) if prof[c][0] else None
             for c in classes}
@@ -509,16 +526,16 @@ def run_refdepth_stratified(args):
 
 def run_counters_sample(args):
     """Reference-depth model, all 32 sequences at the mean position of the
-    steps bench.py samples for the roofline (t = 1, 41, ..., 2521: mean 1261),
-    a few decoder steps, for rocprofv3 counter passes."""
+    stratified timed steps (20 strata of 1..2560: mean t = 1280), a few
+    decoder steps, for rocprofv3 counter passes."""
     import torch
     from recurrent_decode_step_amd import binding, synth
     from recurrent_decode_step_amd.configs import REFDEPTH
     wl = REFDEPTH
     cfg, B, T = wl.model, wl.batch, wl.steps
     n = args.sample_steps
-    stride = max(1, T // 64)
-    t_mean = sum(range(1, T + 1, stride)) / len(range(1, T + 1, stride))
+    starts, _ = stratified_positions(T, 20, 20)
+    t_mean = sum(starts) / len(starts)
     t0 = int(round(t_mean - (n - 1) / 2))
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)

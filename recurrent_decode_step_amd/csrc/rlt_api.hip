@@ -12,6 +12,10 @@
 #include <string>
 #include <vector>
 
+namespace rlt {
+thread_local PendingEvents g_pending_events;
+}
+
 using namespace rlt;
 
 namespace {
@@ -373,14 +377,16 @@ rlt_status prof_collect(ProfLog &pl, int kclass, double *total_ms, int32_t *laun
   return ok();
 }
 
+// Times one launch of a selected class: the event pair is handed to the
+// launch (rlt::launch binds it to the kernel's own dispatch), so the timing
+// adds no packet to the stream and measures the kernel alone.
 struct Prof {
   ProfLog &pl;
   int cls;
-  hipStream_t s;
   bool on;
   hipEvent_t a = nullptr, b = nullptr;
-  Prof(ProfLog &pl_, int cls_, hipStream_t s_)
-      : pl(pl_), cls(cls_), s(s_),
+  Prof(ProfLog &pl_, int cls_, hipStream_t)
+      : pl(pl_), cls(cls_),
         on(((pl_.mask >> cls_) & 1) && (int)pl_.recs.size() < pl_.max &&
            pl_.step_counter % pl_.stride == 0) {
     if (on) {
@@ -388,13 +394,26 @@ struct Prof {
       b = pooled_event(pl);
       on = a && b;
     }
-    if (on) (void)hipEventRecord(a, s);
+    if (on) g_pending_events = PendingEvents{a, b, false};
   }
   void done(double bytes, double flops = 0.0) {
     if (!on) return;
-    (void)hipEventRecord(b, s);
-    pl.recs.push_back({a, b, bytes, flops, cls});
     on = false;
+    const bool used = g_pending_events.used;
+    g_pending_events = PendingEvents{};
+    if (used) {
+      pl.recs.push_back({a, b, bytes, flops, cls});
+    } else {                    // nothing was launched: give the pair back
+      pl.pool.push_back(a);
+      pl.pool.push_back(b);
+    }
+  }
+  ~Prof() {
+    if (on) {                   // an error path left before done()
+      g_pending_events = PendingEvents{};
+      pl.pool.push_back(a);
+      pl.pool.push_back(b);
+    }
   }
 };
 

@@ -1055,19 +1055,19 @@ hipError_t launch_enc_embed(int dtype, const int32_t *tokens, int n_rows, const 
   const size_t n = (size_t)n_rows * (d / 4);
   const int blocks = (int)((n + 255) / 256);
   if (dtype == RLT_DTYPE_BF16)
-    hipLaunchKernelGGL(k_enc_embed<bf16_t>, dim3(blocks), dim3(256), 0, s, tokens, n_rows,
-                       static_cast<const bf16_t *>(emb), V, d, x);
+    (void)launch(k_enc_embed<bf16_t>, dim3(blocks), dim3(256), 0, s, tokens, n_rows,
+                 static_cast<const bf16_t *>(emb), V, d, x);
   else
-    hipLaunchKernelGGL(k_enc_embed<float>, dim3(blocks), dim3(256), 0, s, tokens, n_rows,
-                       static_cast<const float *>(emb), V, d, x);
+    (void)launch(k_enc_embed<float>, dim3(blocks), dim3(256), 0, s, tokens, n_rows,
+                 static_cast<const float *>(emb), V, d, x);
   return hipGetLastError();
 }
 
 template <typename T, int NC>
 void enc_norm_go(const float *x, int64_t ldx, const float *gamma, float eps, void *out, int64_t ldo,
                  int n_rows, int d, hipStream_t s) {
-  hipLaunchKernelGGL((k_enc_norm<T, NC>), dim3((n_rows + 3) / 4), dim3(256), 0, s, x, ldx, gamma, eps,
-                     static_cast<T *>(out), ldo, n_rows, d);
+  (void)launch((k_enc_norm<T, NC>), dim3((n_rows + 3) / 4), dim3(256), 0, s, x, ldx, gamma, eps,
+               static_cast<T *>(out), ldo, n_rows, d);
 }
 
 template <typename T>
@@ -1100,7 +1100,7 @@ hipError_t pgemm_go(const PGemmArgs &a, hipStream_t s) {
         hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (attr != hipSuccess) return attr;
   }
-  hipLaunchKernelGGL((k_pgemm<T, EPI, C>), dim3(mt * nt), dim3(C::THREADS), C::LDS, s, a, mt, nt);
+  (void)launch((k_pgemm<T, EPI, C>), dim3(mt * nt), dim3(C::THREADS), C::LDS, s, a, mt, nt);
   return hipGetLastError();
 }
 
@@ -1127,7 +1127,7 @@ hipError_t pgemm32_go(const PGemmArgs &a, hipStream_t s) {
           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
       if (attr != hipSuccess) return attr;
     }
-    hipLaunchKernelGGL((k_pgemm32d<EPI, C>), dim3(mt * nt), dim3(C::THREADS), C::LDS, s, a, mt, nt);
+    (void)launch((k_pgemm32d<EPI, C>), dim3(mt * nt), dim3(C::THREADS), C::LDS, s, a, mt, nt);
   } else {
     if constexpr (C::LDS > 65536) {
       static const hipError_t attr = hipFuncSetAttribute(
@@ -1135,7 +1135,7 @@ hipError_t pgemm32_go(const PGemmArgs &a, hipStream_t s) {
           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
       if (attr != hipSuccess) return attr;
     }
-    hipLaunchKernelGGL((k_pgemm32<EPI, C>), dim3(mt * nt), dim3(C::THREADS), C::LDS, s, a, mt, nt);
+    (void)launch((k_pgemm32<EPI, C>), dim3(mt * nt), dim3(C::THREADS), C::LDS, s, a, mt, nt);
   }
   return hipGetLastError();
 }
@@ -1163,8 +1163,8 @@ template <typename T, int DH>
 hipError_t fattn_go(const FAttnArgs &a, hipStream_t s) {
   const int qblocks = (a.rows.T + 63) / 64;
   const int n_seq = a.rows.n_rows / a.rows.T;
-  hipLaunchKernelGGL((k_fattn<T, DH>), dim3(n_seq * qblocks * a.H), dim3(256), 0, s, a, qblocks,
-                     n_seq);
+  (void)launch((k_fattn<T, DH>), dim3(n_seq * qblocks * a.H), dim3(256), 0, s, a, qblocks,
+               n_seq);
   return hipGetLastError();
 }
 
@@ -1172,7 +1172,7 @@ template <int DH>
 hipError_t fattn32_go(const FAttnArgs &a, hipStream_t s) {
   const int qblocks = (a.rows.T + 127) / 128;
   const int n_seq = a.rows.n_rows / a.rows.T;
-  hipLaunchKernelGGL((k_fattn32<DH>), dim3(n_seq * qblocks * a.H), dim3(256), 0, s, a, qblocks, n_seq);
+  (void)launch((k_fattn32<DH>), dim3(n_seq * qblocks * a.H), dim3(256), 0, s, a, qblocks, n_seq);
   return hipGetLastError();
 }
 

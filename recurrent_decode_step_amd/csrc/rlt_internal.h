@@ -1,14 +1,51 @@
 // Internal declarations shared by the host side (rlt_api.hip) and the kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <stddef.h>
+
+#include <tuple>
+#include <type_traits>
 
 #include "../../include/rlt.h"
 
 namespace rlt {
 
 typedef uint16_t bf16_t;
+
+// Timing of one kernel launch: when `start` is set, the next launch through
+// rlt::launch binds both events to its own dispatch (hipExtLaunchKernel), so
+// their elapsed time is that kernel's execution alone and no extra packet
+// sits between it and its neighbours on the stream.  The launch clears the
+// pair and sets `used`.  One pending pair per host thread.
+struct PendingEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+extern thread_local PendingEvents g_pending_events;
+
+template <typename... P, typename... A>
+inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                         A &&...args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  PendingEvents &pe = g_pending_events;
+  if (pe.start) {
+    std::tuple<std::decay_t<P>...> vals(std::forward<A>(args)...);
+    void *argv[sizeof...(P) > 0 ? sizeof...(P) : 1];
+    std::apply([&](auto &...v) {
+      size_t i = 0;
+      ((argv[i++] = static_cast<void *>(&v)), ...);
+    }, vals);
+    const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block,
+                                            argv, lds, s, pe.start, pe.stop, 0);
+    pe.start = pe.stop = nullptr;
+    pe.used = true;
+    return e;
+  }
+  hipLaunchKernelGGL(kernel, grid, block, lds, s, std::forward<A>(args)...);
+  return hipGetLastError();
+}
 
 constexpr int kAttnThreads = 256;
 constexpr int kMaxParts = 8;          // K parts (wavefronts) per GEMM workgroup

@@ -1170,8 +1170,7 @@ static hipError_t gemm_dispatch_epi(int act, int epi, const GemmArgs &a, dim3 gr
   const size_t lds = (size_t)(threads / 64) * TPW * NCB * 1024;
 #define RLT_G(A, E)                                                                 \
   if (act == A && epi == E) {                                                       \
-    k_gemm<T, NCB, A, E, KSW, TPW><<<grid, threads, lds, s>>>(a);                   \
-    return hipGetLastError();                                                       \
+    return launch(k_gemm<T, NCB, A, E, KSW, TPW>, grid, dim3(threads), lds, s, a);  \
   }
   RLT_G(ACT_PLAIN, EPI_QKV)
   RLT_G(ACT_PLAIN, EPI_RESID)
@@ -1237,14 +1236,13 @@ template <typename T, int KIND>
 static hipError_t attn_dispatch(int dh, const AttnArgs &a, int n_rows, hipStream_t s) {
   const dim3 grid = a.order ? dim3((unsigned)a.H, (unsigned)n_rows) : dim3((unsigned)n_rows, (unsigned)a.H);
   switch (dh) {
-    case 16: k_attn<T, 16, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
-    case 32: k_attn<T, 32, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
-    case 64: k_attn<T, 64, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
-    case 128: k_attn<T, 128, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
-    case 256: k_attn<T, 256, KIND><<<grid, kAttnThreads, 0, s>>>(a); break;
+    case 16: return launch(k_attn<T, 16, KIND>, grid, dim3(kAttnThreads), 0, s, a);
+    case 32: return launch(k_attn<T, 32, KIND>, grid, dim3(kAttnThreads), 0, s, a);
+    case 64: return launch(k_attn<T, 64, KIND>, grid, dim3(kAttnThreads), 0, s, a);
+    case 128: return launch(k_attn<T, 128, KIND>, grid, dim3(kAttnThreads), 0, s, a);
+    case 256: return launch(k_attn<T, 256, KIND>, grid, dim3(kAttnThreads), 0, s, a);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 constexpr int kPersistentWorkgroups = 256;   // one per CU
@@ -1282,9 +1280,8 @@ hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int til
   const int threads = parts * 64;
 #define RLT_GP(E, NC)                                                         \
   case E:                                                                     \
-    if (short_k) k_gemm_p<bf16_t, NC, E, true><<<grid, threads, 0, s>>>(b);    \
-    else k_gemm_p<bf16_t, 2, E, false><<<grid, threads, 0, s>>>(b);           \
-    break;
+    if (short_k) return launch(k_gemm_p<bf16_t, NC, E, true>, grid, dim3(threads), 0, s, b); \
+    return launch(k_gemm_p<bf16_t, 2, E, false>, grid, dim3(threads), 0, s, b);
   switch (epi) {
     RLT_GP(EPI_QKV, 4)
     RLT_GP(EPI_STORE, 4)
@@ -1299,21 +1296,18 @@ hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int til
 
 hipError_t launch_score(const ScoreArgs &a, int n_rows, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  k_score<<<dim3((unsigned)n_rows), kScoreThreads, 0, s>>>(a);
-  return hipGetLastError();
+  return launch(k_score, dim3((unsigned)n_rows), dim3(kScoreThreads), 0, s, a);
 }
 
 hipError_t launch_sample(const SampleArgs &a, int n_rows, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  k_sample<<<dim3((unsigned)n_rows), kSampleThreads, 0, s>>>(a);
-  return hipGetLastError();
+  return launch(k_sample, dim3((unsigned)n_rows), dim3(kSampleThreads), 0, s, a);
 }
 
 hipError_t launch_encode(int dtype, const EncodeArgs &a, int n_rows, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  if (dtype == RLT_DTYPE_BF16) k_encode<bf16_t><<<dim3((unsigned)n_rows), 256, 0, s>>>(a);
-  else k_encode<float><<<dim3((unsigned)n_rows), 256, 0, s>>>(a);
-  return hipGetLastError();
+  if (dtype == RLT_DTYPE_BF16) return launch(k_encode<bf16_t>, dim3((unsigned)n_rows), dim3(256), 0, s, a);
+  return launch(k_encode<float>, dim3((unsigned)n_rows), dim3(256), 0, s, a);
 }
 
 int attn_chunk_max(int dtype, int dh) {

@@ -119,16 +119,25 @@ def test_bf16_small_model_matches_oracle():
     Free-running, every step t: the recurrence amplifies any rounding
     difference (the oracle's perturbation probe: a 2^-9 jitter of the inputs
     grows more than 10x over 150 steps), so the library's trajectory is
-    compared with the oracle's own bf16 drift D(t) = rel-L2(bf16 emulation,
+    judged against the oracle's own bf16 drift D(t) = rel-L2(bf16 emulation,
     float64) over the same 8 sequences:
-      rel-L2(library, bf16 emulation) <= C_DRIFT * D(t) at every step, and
-      <= 2e-2 at every step before D first reaches 2e-2.
-    C_DRIFT = 3: if the library's accumulated rounding error has the
-    emulation's size and is independent of it, their difference is about
-    sqrt(2) D(t); 3 allows the library's own error to be up to about twice
-    the emulation's (it rounds the normed activation at a different point
-    and sums in another order), while a dropped rounding, a wrong index or a
-    stale cache entry shows up as a gap many times D(t)."""
+      (i)   rel-L2(library, float64) <= 2 D(t): the library's accumulated
+            rounding error is at most twice the emulation's;
+      (ii)  rel-L2(library, bf16 emulation) <= C_DRIFT D(t), C_DRIFT = 3: two
+            independent errors of the emulation's size differ by about
+            sqrt(2) D(t); 3 leaves room for the library's own error to be up
+            to about twice the emulation's (it rounds the normed activation
+            at another point and sums in another order), while a dropped
+            rounding, a wrong index or a stale cache entry shows up as a gap
+            many times D(t);
+      (iii) both gaps <= 2e-2 at every step while D(t) <= 1e-2, half the bar:
+            there an implementation as accurate as the emulation meets the
+            2e-2 bar with the sqrt(2) of independent errors to spare.  Past
+            that point the bar measures the dynamics, not the kernels: the
+            emulation itself leaves 2e-2 of float64 at about the same step,
+            and a second implementation that is exactly as accurate differs
+            from it by about 1.4 D(t) (measured: 1.3 to 1.6).
+    """
     C_DRIFT = 3.0
     cfg = BF16_SMALL
     B, T = 8, 150
@@ -172,13 +181,18 @@ def test_bf16_small_model_matches_oracle():
             f"{gap64[t - 1]:.3e}  oracle bf16-vs-fp64 D {drift[t - 1]:.3e}  "
             f"ratio {gap[t - 1] / drift[t - 1]:.2f}")
     worst_ratio = float(np.max(gap / drift))
-    say(f"  max over steps of gap / D = {worst_ratio:.2f} (bar {C_DRIFT})")
+    worst_ratio64 = float(np.max(gap64 / drift))
+    say(f"  max over steps: gap-to-emulation / D = {worst_ratio:.2f} (bar {C_DRIFT}), "
+        f"gap-to-fp64 / D = {worst_ratio64:.2f} (bar 2)")
+    assert np.all(gap64 <= 2.0 * drift), worst_ratio64
     assert np.all(gap <= C_DRIFT * drift), worst_ratio
-    crossed = np.nonzero(drift >= 2e-2)[0]
-    early = int(crossed[0]) if crossed.size else T
-    say(f"  D first reaches 2e-2 at step {early + 1 if crossed.size else None}; "
-        f"max gap before it {float(gap[:early].max()):.3e}")
+    over = np.nonzero(drift > 1e-2)[0]
+    early = int(over[0]) if over.size else T
+    say(f"  D <= 1e-2 through step {early}; max gaps there: to the emulation "
+        f"{float(gap[:early].max()):.3e}, to fp64 {float(gap64[:early].max()):.3e} (bar 2e-2)")
+    assert early >= 20
     assert np.all(gap[:early] <= 2e-2)
+    assert np.all(gap64[:early] <= 2e-2)
     for b in rows:
         assert st.position(b) == T
 
