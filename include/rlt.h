@@ -179,6 +179,26 @@ rlt_status rlt_decoder_step(const rlt_model *m, rlt_state *st, int32_t n,
                             const int32_t *host_slots, const void *dev_e,
                             const rlt_memory *mem, float *dev_logits, void *stream);
 
+/* rlt_decoder_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, kernels and results (bitwise), but the per-step working
+ * memory -- residual stream, sum-of-squares partials, packed normed GEMM
+ * inputs, q, attention output, FFN hidden layer, staged slot list and row
+ * order -- lives in a static array of 16 MiB per device that the library holds
+ * until the process ends, instead of in the state's scratch region.  It calls
+ * no allocating routine.  Every call on one device shares that array: calls
+ * that overlap on one GPU (two streams, or two host threads) race and must
+ * not be issued; calls in stream order are safe, and nothing in the array
+ * needs to start at zero.  The model's device must be current on the first
+ * call on that device.  Errors: those of rlt_decoder_step, plus RLT_ERR_RANGE
+ * when the n rows need more than the 16 MiB, with no side effects.  The need
+ * is about n * (8 + 4.25 d + 3 es d + es F) bytes (es = 2 for bf16, 4 for
+ * fp32; packed buffers round n up to 16 rows): up to 448 rows at d = 2048,
+ * F = 8192 and 224 rows at d = 4096, F = 16384 in bf16. */
+rlt_status rlt_decoder_step_noalloc(const rlt_model *m, rlt_state *st, int32_t n,
+                                    const int32_t *host_slots, const void *dev_e,
+                                    const rlt_memory *mem, float *dev_logits, void *stream);
+
 /* T steps for all B slots with no reset anywhere (prompt prefill and decode are
  * the same transition) [Tutorial, "Prompt prefill"; Article, "The Critical
  * Boundary"].  dev_e [B][T][d]; logits: RLT_LOGITS_ALL -> [B][T][V],

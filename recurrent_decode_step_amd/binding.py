@@ -26,7 +26,8 @@ RLT_DETACH_S, RLT_DETACH_KV = 1, 2
 
 EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_bytes",
             "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",
-            "rlt_state_destroy", "rlt_state_reset", "rlt_decoder_step", "rlt_run_sequence",
+            "rlt_state_destroy", "rlt_state_reset", "rlt_decoder_step", "rlt_decoder_step_noalloc",
+            "rlt_run_sequence",
             "rlt_score_sequence", "rlt_generate",
             "rlt_state_position", "rlt_snapshot_bytes", "rlt_state_export", "rlt_state_import",
             "rlt_profile_begin", "rlt_profile_collect",
@@ -103,6 +104,7 @@ def load_library(path: str = LIB_PATH):
         "rlt_state_destroy": (None, [vp]),
         "rlt_state_reset": (i32, [vp, vp, i32, P(i32), vp]),
         "rlt_decoder_step": (i32, [vp, vp, i32, P(i32), vp, P(rlt_memory), vp, vp]),
+        "rlt_decoder_step_noalloc": (i32, [vp, vp, i32, P(i32), vp, P(rlt_memory), vp, vp]),
         "rlt_run_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, i32, vp]),
         "rlt_score_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, vp, vp]),
         "rlt_generate": (i32, [vp, vp, i32, vp, P(rlt_encoder_table), P(rlt_memory), P(rlt_sampling),
@@ -248,6 +250,25 @@ def rlt_decoder_step(model: Model, state: State, e: torch.Tensor, memory, logits
     _check(lib.rlt_decoder_step(model.handle, state.handle, n, arr, e.data_ptr(), C.byref(mem),
                                 logits.data_ptr() if logits is not None else None,
                                 _stream(stream)))
+    return logits
+
+
+def rlt_decoder_step_noalloc(model: Model, state: State, e: torch.Tensor, memory, logits,
+                             slots=None, stream=None):
+    """rlt_decoder_step with the per-step working memory in the library's
+    static per-device array: nothing is allocated here or in the library, so
+    the caller passes the logits buffer ([n][V] fp32, or None for no logits)
+    and e as a contiguous [n][d] tensor."""
+    lib = load_library()
+    n = e.shape[0]
+    if e.stride(-1) != 1 or e.stride(0) != e.shape[1]:
+        raise ValueError("e must be a contiguous [n][d] tensor")
+    arr, _ = _slots_arg(slots)
+    mem = memory if isinstance(memory, rlt_memory) else memory_view(*memory)
+    _check(lib.rlt_decoder_step_noalloc(model.handle, state.handle, n, arr, e.data_ptr(),
+                                        C.byref(mem),
+                                        logits.data_ptr() if logits is not None else None,
+                                        _stream(stream)))
     return logits
 
 

@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -124,6 +125,46 @@ int chunk_of(const rlt_config *c) {
   return c->attn_chunk > 0 ? std::min(c->attn_chunk, cap) : cap;
 }
 
+// ---------------------------------------------------------- static scratch
+// Working memory of rlt_decoder_step_noalloc, for callers that cannot
+// allocate: one array per device, held until the process ends.  Host code
+// never names the array itself (its host-side symbol is no device address):
+// the device address is looked up once per device with hipGetSymbolAddress,
+// with that device current, and only that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+rlt_status static_scratch(int device, void **out) {
+  *out = nullptr;
+  if (device < 0 || device >= kMaxDevices)
+    return fail(RLT_ERR_UNSUPPORTED, "device %d outside the static scratch table", device);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != device)
+      return fail(RLT_ERR_INVALID_ARG, "the model's device %d must be current (device %d is)",
+                  device, cur);
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "static scratch address");
+    if (!p) return fail(RLT_ERR_DEVICE, "static scratch address is NULL");
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return RLT_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ handles
@@ -172,6 +213,7 @@ struct rlt_state {
   std::vector<int> host_pos;
   std::vector<int> staged;   // slot list currently in slots_dev (empty: none)
   std::vector<int> staged_order;   // row order currently in order_dev
+  std::vector<int> static_slots, static_order;   // host copies staged into the static scratch
   ProfLog plog;
 };
 
@@ -251,6 +293,45 @@ size_t state_layout(const rlt_config &c, rlt_state *st, void *base, int B) {
   st->hbuf = ar.take<char>(rows16 * c.d_ffn * es);
   st->lscratch = ar.take<float>((size_t)B * c.vocab * 4);
   st->escratch = ar.take<char>((size_t)B * d * es);
+  return align256(ar.off);
+}
+
+// Per-step working memory of the decoder step: the residual stream, the
+// sum-of-squares partials, the packed normed GEMM inputs, q, the attention
+// output, the FFN hidden layer and the staged slot list / row order.  It
+// lives in the state (rlt_decoder_step) or in the library's static per-device
+// array (rlt_decoder_step_noalloc).
+struct StepScratch {
+  float *x, *sumsq;
+  char *xg, *qbuf, *obuf, *hbuf;
+  int *slots_dev, *order_dev;
+  int part_ld;               // leading dimension of the sum-of-squares partials
+  bool shared;               // static array: shared by every call, nothing cached
+  ProfLog *plog;             // null: no profiling
+};
+
+StepScratch state_scratch(rlt_state *st) {
+  return StepScratch{st->x, st->sumsq, st->xg, st->qbuf, st->obuf, st->hbuf, st->slots_dev,
+                     st->order_dev, st->B, false, &st->plog};
+}
+
+// The same buffers for n rows carved from `base` (nullptr: only measure).
+size_t step_scratch_layout(const rlt_config &c, int n, void *base, StepScratch *w) {
+  const int d = c.d_model;
+  const int es = esize_of(c.dtype);
+  const size_t rows16 = (size_t)cdiv(n, 16) * 16;
+  Arena ar(base);
+  w->slots_dev = ar.take<int>((size_t)n * 4);
+  w->order_dev = ar.take<int>((size_t)n * 4);
+  w->x = ar.take<float>((size_t)n * d * 4);
+  w->sumsq = ar.take<float>((size_t)cdiv(d, 16) * n * 4);
+  w->xg = ar.take<char>(rows16 * d * es);
+  w->qbuf = ar.take<char>((size_t)n * d * es);
+  w->obuf = ar.take<char>(rows16 * d * es);
+  w->hbuf = ar.take<char>(rows16 * c.d_ffn * es);
+  w->part_ld = n;
+  w->shared = true;
+  w->plog = nullptr;
   return align256(ar.off);
 }
 
@@ -420,13 +501,15 @@ struct Prof {
 // Enqueue one decoder step for n rows.  e rows: e_base + i*ld_e (elements);
 // logits rows: logits + i*ld_logits (NULL: no head).  The slot list is already
 // staged (identity == true: rows are slots 0..n-1).
-rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
-                        const int32_t *host_slots, const void *e, int64_t ld_e,
+rlt_status enqueue_step(const rlt_model *m, rlt_state *st, const StepScratch &w, int n,
+                        bool identity, const int32_t *host_slots, const void *e, int64_t ld_e,
                         const rlt_memory *mem, float *logits, int64_t ld_logits, hipStream_t s) {
   const rlt_config &c = m->cfg;
   const int d = c.d_model, H = c.n_heads, dh = c.head_dim, W = c.window, L = c.n_layers;
   const int F = c.d_ffn, B = st->B, es = m->esize;
   hipError_t err;
+  ProfLog no_prof;                                  // profiling off: mask 0
+  ProfLog *plog = w.plog ? w.plog : &no_prof;
 
   // host mirror: algorithmic bytes of the two attentions (for profiling)
   double swa_len = 0, mem_len = 0;
@@ -447,33 +530,39 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     for (int i = 0; i < n; ++i) ord[i] = i;
     auto t_of = [&](int i) { return st->host_pos[identity ? i : host_slots[i]]; };
     std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return t_of(x) > t_of(y); });
-    if (ord != st->staged_order) {
+    if (w.shared) {
+      // the static array is shared by every call: stage the order every time
+      st->static_order = ord;
+      err = hipMemcpyAsync(w.order_dev, st->static_order.data(), (size_t)n * 4,
+                           hipMemcpyHostToDevice, s);
+      if (err != hipSuccess) return hip_fail(err, "staging the attention row order");
+    } else if (ord != st->staged_order) {
       st->staged_order = ord;
-      err = hipMemcpyAsync(st->order_dev, st->staged_order.data(), (size_t)n * 4,
+      err = hipMemcpyAsync(w.order_dev, st->staged_order.data(), (size_t)n * 4,
                            hipMemcpyHostToDevice, s);
       if (err != hipSuccess) {
         st->staged_order.clear();
         return hip_fail(err, "staging the attention row order");
       }
     }
-    order_dev = st->order_dev;
+    order_dev = w.order_dev;
   }
 
   const ColPlan cp = col_plan(n);
   GemmArgs base;
   memset(&base, 0, sizeof base);
   base.n_rows = n;
-  base.slots = identity ? nullptr : st->slots_dev;
+  base.slots = identity ? nullptr : w.slots_dev;
   base.pos = st->pos;
   base.s_state = st->s;
   base.d = d;
-  base.sumsq = st->sumsq;
+  base.sumsq = w.sumsq;
   base.n_parts = cdiv(d, 16);
-  base.part_ld = B;
+  base.part_ld = w.part_ld;
   base.eps = c.rms_eps;
-  base.x = st->x;
-  base.xg = st->xg;
-  base.sumsq_out = st->sumsq;
+  base.x = w.x;
+  base.xg = w.xg;
+  base.sumsq_out = w.sumsq;
   base.H = H;
   base.dh = dh;
   base.W = W;
@@ -485,7 +574,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     a.N = g.N;
     a.K = g.K;
     a.KT = g.KT;
-    Prof p(st->plog, RLT_K_GEMM, s);
+    Prof p(*plog, RLT_K_GEMM, s);
     // narrower column groups until the launch has a workgroup per CU (results
     // per row do not depend on the grouping)
     ColPlan gc = cp;
@@ -538,9 +627,9 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     // (1) Q,K,V of RMSNorm(x; g1); k,v go to window entry (t-1) mod W
     {
       GemmArgs a = base;
-      a.act = st->xg;
+      a.act = w.xg;
       a.ld_act = d;
-      a.out = st->qbuf;
+      a.out = w.qbuf;
       a.ld_out = d;
       a.ring_k = st->ring_k + l * ring_layer;
       a.ring_v = st->ring_v + l * ring_layer;
@@ -551,15 +640,15 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     // (2) sliding-window self-attention over window entries 0..min(t,W)-1
     {
       AttnArgs a = at;
-      a.q = st->qbuf;
-      a.out = st->obuf;
+      a.q = w.qbuf;
+      a.out = w.obuf;
       a.kb = st->ring_k + l * ring_layer;
       a.vb = st->ring_v + l * ring_layer;
       a.s_seq = (int64_t)H * W * dh;
       a.s_head = (int64_t)W * dh;
       a.s_pos = dh;
       a.len_cap = W;
-      Prof p(st->plog, RLT_K_SWA, s);
+      Prof p(*plog, RLT_K_SWA, s);
       if ((err = launch_attn(c.dtype, dh, a, n, s)) != hipSuccess)
         return hip_fail(err, "window attention launch");
       p.done(swa_len * 2.0 * d * es + 2.0 * n * d * es);
@@ -567,7 +656,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     // (3) x += W_O o
     {
       GemmArgs a = base;
-      a.act = st->obuf;
+      a.act = w.obuf;
       a.ld_act = d;
       a.gamma_next = m->g2 + (size_t)l * d;
       if ((rs = gemm(m->p_o, m->wo[l], ACT_PLAIN, EPI_RESID, a, "o gemm", row_in, resid_out)) !=
@@ -577,9 +666,9 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     // (4) cross-attention query of RMSNorm(x; g2)
     {
       GemmArgs a = base;
-      a.act = st->xg;
+      a.act = w.xg;
       a.ld_act = d;
-      a.out = st->qbuf;
+      a.out = w.qbuf;
       a.ld_out = d;
       if ((rs = gemm(m->p_o, m->wqc[l], ACT_PLAIN, EPI_STORE, a, "qc gemm", row_in,
                      (double)n * d * es)) != RLT_OK)
@@ -589,15 +678,15 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     {
       const int grp = c.mem_groups == 1 ? 0 : l;
       AttnArgs a = at;
-      a.q = st->qbuf;
-      a.out = st->obuf;
+      a.q = w.qbuf;
+      a.out = w.obuf;
       a.kb = static_cast<const char *>(mem->k) + (size_t)grp * mem->stride_group * es;
       a.vb = static_cast<const char *>(mem->v) + (size_t)grp * mem->stride_group * es;
       a.s_seq = mem->stride_seq;
       a.s_head = mem->stride_head;
       a.s_pos = mem->stride_pos;
       a.len_cap = 0x7fffffff;
-      Prof p(st->plog, RLT_K_CROSS, s);
+      Prof p(*plog, RLT_K_CROSS, s);
       if ((err = launch_attn(c.dtype, dh, a, n, s)) != hipSuccess)
         return hip_fail(err, "cross attention launch");
       p.done(mem_len * 2.0 * d * es + 2.0 * n * d * es);
@@ -605,7 +694,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     // (6) x += W_Oc o_c
     {
       GemmArgs a = base;
-      a.act = st->obuf;
+      a.act = w.obuf;
       a.ld_act = d;
       a.gamma_next = m->g3 + (size_t)l * d;
       if ((rs = gemm(m->p_o, m->woc[l], ACT_PLAIN, EPI_RESID, a, "oc gemm", row_in, resid_out)) !=
@@ -615,9 +704,9 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     // (7) GELU(W_1 RMSNorm(x; g3))
     {
       GemmArgs a = base;
-      a.act = st->xg;
+      a.act = w.xg;
       a.ld_act = d;
-      a.out = st->hbuf;
+      a.out = w.hbuf;
       a.ld_out = F;
       a.kt_out = F / kstep_of(c.dtype);
       if ((rs = gemm(m->p_ffn1, m->w1[l], ACT_PLAIN, EPI_GELU, a, "ffn1 gemm", row_in,
@@ -627,7 +716,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
     // (8) x += W_2 h; the last layer also writes s_t
     {
       GemmArgs a = base;
-      a.act = st->hbuf;
+      a.act = w.hbuf;
       a.ld_act = F;
       a.gamma_next = last ? m->go : m->g1 + (size_t)(l + 1) * d;
       if (last) {
@@ -643,7 +732,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, int n, bool identity,
   // head: logits = W_o RMSNorm(s_t; g_o)
   if (logits) {
     GemmArgs a = base;
-    a.act = st->xg;
+    a.act = w.xg;
     a.ld_act = d;
     a.out = logits;
     a.ld_out = ld_logits;
@@ -868,8 +957,47 @@ rlt_status rlt_decoder_step(const rlt_model *m, rlt_state *st, int32_t n, const 
   if (host_slots)
     for (int i = 0; i < n; ++i) identity = identity && host_slots[i] == i;
   if (!identity && (rs = stage_slots(st, n, host_slots, s)) != RLT_OK) return rs;
-  if ((rs = enqueue_step(m, st, n, identity, host_slots, dev_e, m->cfg.d_model, mem, dev_logits,
-                         m->cfg.vocab, s)) != RLT_OK)
+  if ((rs = enqueue_step(m, st, state_scratch(st), n, identity, host_slots, dev_e,
+                         m->cfg.d_model, mem, dev_logits, m->cfg.vocab, s)) != RLT_OK)
+    return rs;
+  return ok();
+}
+
+rlt_status rlt_decoder_step_noalloc(const rlt_model *m, rlt_state *st, int32_t n,
+                                    const int32_t *host_slots, const void *dev_e,
+                                    const rlt_memory *mem, float *dev_logits, void *stream) {
+  rlt_status rs;
+  if ((rs = check_state(m, st)) != RLT_OK) return rs;
+  if ((rs = check_slots(st, n, host_slots)) != RLT_OK) return rs;
+  if (!dev_e) return fail(RLT_ERR_INVALID_ARG, "dev_e is NULL");
+  StepScratch w;
+  const size_t need = step_scratch_layout(m->cfg, n, nullptr, &w);
+  if (need > kStaticScratchBytes)
+    return fail(RLT_ERR_RANGE,
+                "a step of %d rows needs %zu bytes of working memory, more than the %zu bytes "
+                "of the static scratch; split the call or use rlt_decoder_step",
+                n, need, kStaticScratchBytes);
+  int max_slot = n - 1;
+  if (host_slots) max_slot = *std::max_element(host_slots, host_slots + n);
+  if ((rs = check_memory(m, mem, max_slot)) != RLT_OK) return rs;
+  if ((rs = check_positions(st, mem, n, host_slots, 1)) != RLT_OK) return rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  void *base = nullptr;
+  if ((rs = static_scratch(m->device, &base)) != RLT_OK) return rs;
+  step_scratch_layout(m->cfg, n, base, &w);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool identity = true;
+  if (host_slots)
+    for (int i = 0; i < n; ++i) identity = identity && host_slots[i] == i;
+  if (!identity) {
+    // staged into the shared array on every call
+    st->static_slots.assign(host_slots, host_slots + n);
+    const hipError_t e = hipMemcpyAsync(w.slots_dev, st->static_slots.data(), (size_t)n * 4,
+                                        hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "staging slot list");
+  }
+  if ((rs = enqueue_step(m, st, w, n, identity, host_slots, dev_e, m->cfg.d_model, mem,
+                         dev_logits, m->cfg.vocab, s)) != RLT_OK)
     return rs;
   return ok();
 }
@@ -901,7 +1029,8 @@ rlt_status rlt_run_sequence(const rlt_model *m, rlt_state *st, int32_t T, const 
     } else if (logits_mode == RLT_LOGITS_LAST && k == T - 1) {
       lk = dev_logits;
     }
-    if ((rs = enqueue_step(m, st, st->B, true, nullptr, ek, (int64_t)T * d, mem, lk, ld, s)) !=
+    if ((rs = enqueue_step(m, st, state_scratch(st), st->B, true, nullptr, ek, (int64_t)T * d,
+                           mem, lk, ld, s)) !=
         RLT_OK)
       return rs;
   }
@@ -926,7 +1055,8 @@ rlt_status rlt_score_sequence(const rlt_model *m, rlt_state *st, int32_t T, cons
     // the step's logits go to the state's scratch; the score of the token
     // that step k+1 will consume is read from them before it is consumed
     const void *ek = static_cast<const char *>(dev_e) + (size_t)k * d * es;
-    if ((rs = enqueue_step(m, st, st->B, true, nullptr, ek, (int64_t)T * d, mem, st->lscratch, V,
+    if ((rs = enqueue_step(m, st, state_scratch(st), st->B, true, nullptr, ek, (int64_t)T * d,
+                           mem, st->lscratch, V,
                            s)) != RLT_OK)
       return rs;
     ScoreArgs sa;
@@ -1010,7 +1140,8 @@ rlt_status rlt_generate(const rlt_model *m, rlt_state *st, int32_t n_steps,
     // 4: consume it once; the logits of the new state go to the scratch (and
     // to dev_logits_last on the last step)
     float *lg = (j == n_steps - 1 && dev_logits_last) ? dev_logits_last : st->lscratch;
-    if ((rs = enqueue_step(m, st, B, true, nullptr, st->escratch, d, mem, lg, V, s)) != RLT_OK)
+    if ((rs = enqueue_step(m, st, state_scratch(st), B, true, nullptr, st->escratch, d, mem, lg,
+                           V, s)) != RLT_OK)
       return rs;
   }
   return ok();
