@@ -870,6 +870,7 @@ def run_longctx(args):
     mem = binding.memory_view(mk, mv)
     state = binding.State(model, B, T)
     rows = []
+    cross = []                                  # per window: (ms, launches, bytes)
     stream = torch.cuda.current_stream()
     for t0 in starts:
         import_positions(model, state, cfg, params, [t0] * B, dev, chunk=2)
@@ -881,11 +882,14 @@ def run_longctx(args):
             import_positions(model, state, cfg, params, [t0] * B, dev, chunk=2)
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
+        binding.profile_begin(state, 1 << binding.RLT_K_CROSS, 1 << 16, step_stride=1)
         ev0.record(stream)
         binding.rlt_run_sequence(model, state, e, mem, logits_mode=binding.RLT_LOGITS_LAST)
         ev1.record(stream)
         torch.cuda.synchronize()
         ms = ev0.elapsed_time(ev1)
+        cross.append(binding.profile_collect(state, binding.RLT_K_CROSS))
+        binding.profile_begin(state, 0, 0)
         t_mid = t0 + (n - 1) / 2
         rows.append((t0, ms / n, float(np.mean([min(t, W) for t in range(t0, t0 + n)])), t_mid))
         print(f"longctx: window t0={t0}: {ms / n:.3f} ms/step", file=sys.stderr, flush=True)
@@ -895,7 +899,10 @@ def run_longctx(args):
     ts = np.arange(1, T + 1, dtype=np.float64)
     total_ms = float(np.sum(coef[0] + coef[1] * np.minimum(ts, W) + coef[2] * ts))
     bytes_total = sum(algorithmic_bytes_per_step(cfg, [t] * B, 2) for t in range(1, T + 1, 64)) * 64
-    return {
+    c_ms = sum(c[0] for c in cross)
+    c_n = sum(c[1] for c in cross)
+    c_bytes = sum(c[2] for c in cross)
+    out = {
         "metric": "decoder token-steps/sec at 1 GPU (48-layer, d=4096, B=8, T=32768)",
         "value": round(B * T / (total_ms / 1e3), 2), "unit": "token-steps/s", "n_gpus": 1,
         "steps": T, "ms_per_step": round(total_ms / T, 4), "higher_is_better": True,
@@ -911,7 +918,75 @@ def run_longctx(args):
                           "achieved": round(bytes_total / (total_ms / 1e3) / 1e9, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(bytes_total / (total_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "k_attn<bf16,128,1> (cross-attention, encoder memory)",
+                     "achieved": round(c_bytes / (c_ms / 1e3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(c_bytes / (c_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "launches_timed": c_n,
+                     "avg_launch_us": round(c_ms / max(c_n, 1) * 1e3, 2),
+                     "per_window_GBps": {str(t0): round(c[2] / (c[0] / 1e3) / 1e9, 1)
+                                         for t0, c in zip(starts, cross)},
+                     "timing": "events bound to each launch's own dispatch, every launch of the "
+                               "six windows"},
     }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_longctx(cfg, params, mk, mv, starts, W, T,
+                                                   budget_s=max(args.cpu_budget, 60.0))
+    return out
+
+
+def cpu_baseline_longctx(cfg, params_gpu, mk_gpu, mv_gpu, starts, W, T, budget_s=60.0, rows=2):
+    """The oracle (fp32 NumPy, as it stands) on the host for the long-context
+    workload: `rows` sequences take one batched step from synthetic states
+    imported at each window start (in the order 1, last, then inwards, until
+    the budget is spent and at least three starts are done), per-step time
+    fitted as a + b min(t, W) + c t (as on the GPU) and summed over the run.
+    The fp32 weights (42.6 GiB) are converted once, untimed."""
+    import numpy as np
+    import oracle
+    dev = mk_gpu.device
+    t_prep = time.time()
+    params = {k: v.float().cpu() for k, v in params_gpu.items()}
+    om = oracle.Model(params=params, precision="fp32", d_model=cfg.d_model, n_heads=cfg.n_heads,
+                      n_layers=cfg.n_layers, d_ffn=cfg.d_ffn, window=cfg.window,
+                      mem_groups=cfg.mem_groups, vocab=cfg.vocab, rms_eps=cfg.rms_eps)
+    del params
+    prep = time.time() - t_prep
+    order = [starts[0], starts[-1]] + [t for t in reversed(starts[1:-1])]
+    pts, spent = [], 0.0
+    for t in order:
+        t_prep = time.time()
+        st = []
+        for b in range(rows):
+            r = synthetic_record(cfg, params_gpu, t, dev, b)
+            st.append(oracle.state_from_arrays(om, r["pos"], r["s"].float().cpu(),
+                                               r["K"].float().cpu(), r["V"].float().cpu()))
+            del r
+        mk = mk_gpu[:, :rows, :, :t].float().cpu().numpy()
+        mv = mv_gpu[:, :rows, :, :t].float().cpu().numpy()
+        e = np.random.default_rng(t).standard_normal((rows, cfg.d_model)).astype(np.float32)
+        prep += time.time() - t_prep
+        t0 = time.time()
+        oracle.decoder_step(om, st, e, mk, mv)
+        el = time.time() - t0
+        spent += el
+        pts.append((t, el))
+        print(f"longctx cpu baseline: t = {t}: {el:.2f} s per step", file=sys.stderr, flush=True)
+        del st, mk, mv
+        if spent >= budget_s and len(pts) >= 3:
+            break
+    A = np.array([[1.0, min(t, W), t] for t, _ in pts])
+    y = np.array([el for _, el in pts])
+    coef, *_ = np.linalg.lstsq(A, y, rcond=None)
+    ts = np.arange(1, T + 1, dtype=np.float64)
+    total_s = float(np.sum(coef[0] + coef[1] * np.minimum(ts, W) + coef[2] * ts))
+    return {"value": rows * T / total_s, "unit": "token-steps/s", "cores": openblas_threads(),
+            "kind": "oracle",
+            "sample": f"{rows} sequences x one batched step at t = "
+                      f"{', '.join(str(t) for t, _ in pts)} (s per step "
+                      f"{', '.join(f'{el:.2f}' for _, el in pts)}), each from synthetic states "
+                      f"imported there, NumPy fp32 oracle; per-step time fitted as a + b min(t, W) "
+                      f"+ c t and summed over t = 1..{T} ({spent:.1f} s timed, {prep:.1f} s weight "
+                      f"conversion and state preparation untimed)"}
 
 
 def run_encode(args):
