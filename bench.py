@@ -441,12 +441,19 @@ def run_refdepth_stratified(args):
     ev1 = torch.cuda.Event(enable_timing=True)
     next_t = list(starts)
     positions = []
+    ws = binding.StepWorkspace(model, B) if args.persistent else None
+    if ws is not None:
+        profiled = []                           # the persistent step has no per-kernel events
     torch.cuda.synchronize()
     ev0.record(stream)
     for k in range(K):
         j = k % n_states
         t = next_t[j]
-        binding.rlt_decoder_step(model, states[j], e_by_step[t - 1], mem, logits=logits[j])
+        if ws is None:
+            binding.rlt_decoder_step(model, states[j], e_by_step[t - 1], mem, logits=logits[j])
+        else:
+            binding.rlt_run_sequence_persistent(model, states[j], e_by_step[t - 1].unsqueeze(1),
+                                                mem, ws, logits=logits[j].unsqueeze(1))
         positions.append(t)
         next_t[j] = t + 1
     ev1.record(stream)
@@ -466,11 +473,13 @@ def run_refdepth_stratified(args):
     if not torch.isfinite(logits).all():
         raise RuntimeError("non-finite logits")
 
+    if ws is not None:
+        binding.rlt_persistent_check(ws)
     bytes_run = sum(algorithmic_bytes_per_step(cfg, [t] * B, es) for t in positions)
     cross_ms, cross_n, cross_bytes = prof[binding.RLT_K_CROSS]
     cross_avg_ms = cross_ms / max(cross_n, 1)
-    achieved = cross_bytes / max(cross_n, 1) / (cross_avg_ms / 1e3) / 1e9
-    traffic = measured_traffic(cross_bytes / max(cross_n, 1))
+    achieved = cross_bytes / max(cross_n, 1) / (cross_avg_ms / 1e3) / 1e9 if cross_n else 0.0
+    traffic = measured_traffic(cross_bytes / max(cross_n, 1)) if cross_n else None
     mean_t = sum(positions) / len(positions)
     out = {
         "metric": "decoder token-steps/sec at 1 GPU (48-layer, B=32/256); % HBM/MFMA roofline",
@@ -492,7 +501,9 @@ def run_refdepth_stratified(args):
                    "positions": f"{min(positions)}..{max(positions)} in {n_states} strata, "
                                 f"mean t = {mean_t:.1f}",
                    "strata_starts": starts,
-                   "logits": "every step, fp32"},
+                   "logits": "every step, fp32",
+                   "step": "persistent (one cooperative launch per step)" if ws is not None
+                           else "launch chain (2 + 8L launches per step)"},
         "roofline": {"bound": "hbm", "kernel": "k_attn<bf16,128,1> (cross-attention, encoder memory)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -629,7 +640,14 @@ def run_full_sequence(args, wl):
     mem = binding.memory_view(mk, mv)
     state = binding.State(model, B, T)
     logits = torch.empty((B, T, cfg.vocab), dtype=torch.float32, device=dev)
-    binding.rlt_run_sequence(model, state, e[:, :min(4, T)], mem)       # warm-up
+    ws = binding.StepWorkspace(model, B) if args.persistent else None
+
+    def run(ee, lg=None):
+        if ws is not None:
+            return binding.rlt_run_sequence_persistent(model, state, ee, mem, ws, logits=lg)
+        return binding.rlt_run_sequence(model, state, ee, mem, logits=lg)
+
+    run(e[:, :min(4, T)])                                               # warm-up
     stream = torch.cuda.current_stream()
     times = []
     for _ in range(5):
@@ -638,7 +656,7 @@ def run_full_sequence(args, wl):
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        binding.rlt_run_sequence(model, state, e, mem, logits=logits)
+        run(e, logits)
         ev1.record(stream)
         torch.cuda.synchronize()
         times.append(ev0.elapsed_time(ev1))
@@ -650,7 +668,9 @@ def run_full_sequence(args, wl):
         "ms_per_step": round(ms / T, 4), "higher_is_better": True,
         "dtype": "f32" if es == 4 else "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "positions": f"1..{T}",
-                   "repeats": "median of 5 full runs", "logits": "every step, fp32"},
+                   "repeats": "median of 5 full runs", "logits": "every step, fp32",
+                   "step": "persistent (one cooperative launch per step)" if ws is not None
+                           else "launch chain (2 + 8L launches per step)"},
         "step_roofline": {"bound": "hbm", "algorithmic_GB_per_step": round(bytes_run / T / 1e9, 5),
                           "achieved": round(bytes_run / (ms / 1e3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s",
@@ -1213,6 +1233,8 @@ def main():
                     help="print enqueue progress to stderr (long profiled runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB streaming kernel before warmup (counter scaling)")
+    ap.add_argument("--persistent", action="store_true",
+                    help="tiny/small/refdepth --steps K: one persistent launch per decoder step")
     ap.add_argument("--breakdown", action="store_true",
                     help="time every kernel class on the sampled steps (adds event records)")
     args = ap.parse_args()

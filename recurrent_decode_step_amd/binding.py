@@ -27,7 +27,8 @@ RLT_DETACH_S, RLT_DETACH_KV = 1, 2
 EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_bytes",
             "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",
             "rlt_state_destroy", "rlt_state_reset", "rlt_decoder_step", "rlt_decoder_step_noalloc",
-            "rlt_run_sequence",
+            "rlt_run_sequence", "rlt_persistent_workspace_bytes", "rlt_run_sequence_persistent",
+            "rlt_persistent_check",
             "rlt_score_sequence", "rlt_generate",
             "rlt_state_position", "rlt_snapshot_bytes", "rlt_state_export", "rlt_state_import",
             "rlt_profile_begin", "rlt_profile_collect",
@@ -106,6 +107,9 @@ def load_library(path: str = LIB_PATH):
         "rlt_decoder_step": (i32, [vp, vp, i32, P(i32), vp, P(rlt_memory), vp, vp]),
         "rlt_decoder_step_noalloc": (i32, [vp, vp, i32, P(i32), vp, P(rlt_memory), vp, vp]),
         "rlt_run_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, i32, vp]),
+        "rlt_persistent_workspace_bytes": (sz, [P(rlt_config), i32]),
+        "rlt_run_sequence_persistent": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, i32, vp, sz, vp]),
+        "rlt_persistent_check": (i32, [vp, vp]),
         "rlt_score_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, vp, vp]),
         "rlt_generate": (i32, [vp, vp, i32, vp, P(rlt_encoder_table), P(rlt_memory), P(rlt_sampling),
                                vp, vp, vp, vp, vp]),
@@ -286,6 +290,40 @@ def rlt_run_sequence(model: Model, state: State, e: torch.Tensor, memory,
                                 logits.data_ptr() if logits is not None else None, logits_mode,
                                 _stream(stream)))
     return logits
+
+
+class StepWorkspace:
+    """Device workspace of rlt_run_sequence_persistent for a state of `batch` slots."""
+
+    def __init__(self, model: Model, batch: int):
+        lib = load_library()
+        nbytes = lib.rlt_persistent_workspace_bytes(C.byref(model.ccfg), batch)
+        if nbytes == 0:
+            _check(RLT_ERR_INVALID_ARG)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=model.buf.device)
+
+
+def rlt_run_sequence_persistent(model: Model, state: State, e: torch.Tensor, memory,
+                                workspace: StepWorkspace, logits_mode: int = RLT_LOGITS_ALL,
+                                logits=None, stream=None):
+    """rlt_run_sequence with one persistent launch per step; e [B][T][d]."""
+    lib = load_library()
+    B, T = e.shape[0], e.shape[1]
+    e = e.contiguous()
+    if logits is None and logits_mode != RLT_LOGITS_NONE:
+        shape = (B, T, model.cfg.vocab) if logits_mode == RLT_LOGITS_ALL else (B, model.cfg.vocab)
+        logits = torch.empty(shape, dtype=torch.float32, device=e.device)
+    mem = memory if isinstance(memory, rlt_memory) else memory_view(*memory)
+    _check(lib.rlt_run_sequence_persistent(
+        model.handle, state.handle, T, e.data_ptr(), C.byref(mem),
+        logits.data_ptr() if logits is not None else None, logits_mode,
+        workspace.buf.data_ptr(), workspace.buf.numel(), _stream(stream)))
+    return logits
+
+
+def rlt_persistent_check(workspace: StepWorkspace, stream=None):
+    """Raises RLTError(RLT_ERR_DEVICE) if a barrier wait of the last persistent call timed out."""
+    _check(load_library().rlt_persistent_check(workspace.buf.data_ptr(), _stream(stream)))
 
 
 def rlt_score_sequence(model: Model, state: State, e: torch.Tensor, memory, tokens: torch.Tensor,

@@ -214,6 +214,7 @@ struct rlt_state {
   std::vector<int> staged;   // slot list currently in slots_dev (empty: none)
   std::vector<int> staged_order;   // row order currently in order_dev
   std::vector<int> static_slots, static_order;   // host copies staged into the static scratch
+  std::vector<StepPhase> step_tab[2];  // persistent step: phase tables (no head, head) being uploaded
   ProfLog plog;
 };
 
@@ -561,6 +562,7 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, const StepScratch &w,
   base.part_ld = w.part_ld;
   base.eps = c.rms_eps;
   base.x = w.x;
+  base.x_in = w.x;
   base.xg = w.xg;
   base.sumsq_out = w.sumsq;
   base.H = H;
@@ -745,6 +747,235 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, const StepScratch &w,
   for (int i = 0; i < n; ++i) st->host_pos[identity ? i : host_slots[i]] += 1;
   st->plog.step_counter += 1;
   return RLT_OK;
+}
+
+// ------------------------------------------------------- persistent step
+// Workspace of rlt_run_sequence_persistent for n rows: barrier lines, the two
+// phase tables (a step without and with the head), and one output buffer per
+// producing phase, so no address is written twice within one launch.
+// Producer k of the residual stream is the merge (k = 0) and, in layer l, the
+// O, Oc and FFN-down products (k = 3l+1, 3l+2, 3l+3).
+constexpr int kStepMaxGrid = 1024;
+
+struct StepBufs {
+  unsigned *flags, *rel, *err;
+  StepPhase *tab[2];
+  std::vector<float *> x, sumsq;     // [3L+1]
+  std::vector<char *> xg;            // [3L+1]
+  std::vector<char *> q, o;          // [2L]: (q, q_c), (window, cross) attention outputs
+  std::vector<char *> h;             // [L]
+};
+
+int step_phases_max(const rlt_config &c) { return 2 + 8 * c.n_layers; }
+
+size_t step_layout(const rlt_config &c, int n, void *base, StepBufs *b) {
+  const int L = c.n_layers, d = c.d_model, F = c.d_ffn;
+  const int es = esize_of(c.dtype);
+  const size_t rows16 = (size_t)cdiv(n, 16) * 16;
+  Arena ar(base);
+  b->flags = ar.take<unsigned>((size_t)kStepMaxGrid * kStepFlagWords * 4);
+  b->rel = ar.take<unsigned>(256);
+  b->err = ar.take<unsigned>(256);
+  for (int t = 0; t < 2; ++t) b->tab[t] = ar.take<StepPhase>((size_t)step_phases_max(c) * sizeof(StepPhase));
+  b->x.resize(3 * L + 1);
+  b->sumsq.resize(3 * L + 1);
+  b->xg.resize(3 * L + 1);
+  for (int k = 0; k <= 3 * L; ++k) {
+    b->x[k] = ar.take<float>((size_t)n * d * 4);
+    b->sumsq[k] = ar.take<float>((size_t)cdiv(d, 16) * n * 4);
+    b->xg[k] = ar.take<char>(rows16 * d * es);
+  }
+  b->q.resize(2 * L);
+  b->o.resize(2 * L);
+  for (int k = 0; k < 2 * L; ++k) {
+    b->q[k] = ar.take<char>((size_t)n * d * es);
+    b->o[k] = ar.take<char>(rows16 * d * es);
+  }
+  b->h.resize(L);
+  for (int l = 0; l < L; ++l) b->h[l] = ar.take<char>(rows16 * F * es);
+  return align256(ar.off);
+}
+
+// The phases of one step over all n = B slots of the state (identity slot
+// list), in the launch chain's order and with its K parts; every GEMM phase
+// uses 16-row tiles and 16-row column groups (a placement choice, invisible
+// in the results).  with_head: the head phase is the last and advances the
+// positions, otherwise the last FFN-down does.
+void build_step_phases(const rlt_model *m, rlt_state *st, const rlt_memory *mem,
+                       const StepBufs &b, bool with_head, std::vector<StepPhase> &out) {
+  const rlt_config &c = m->cfg;
+  const int d = c.d_model, H = c.n_heads, dh = c.head_dim, W = c.window, L = c.n_layers;
+  const int F = c.d_ffn, n = st->B, es = m->esize;
+  const int col_groups = cdiv(n, 16);
+  out.clear();
+
+  GemmArgs base;
+  memset(&base, 0, sizeof base);
+  base.n_rows = n;
+  base.slots = nullptr;
+  base.pos = st->pos;
+  base.s_state = st->s;
+  base.d = d;
+  base.n_parts = cdiv(d, 16);
+  base.part_ld = n;
+  base.eps = c.rms_eps;
+  base.H = H;
+  base.dh = dh;
+  base.W = W;
+  base.kt_out = d / kstep_of(c.dtype);
+
+  auto gemm = [&](const GemmPlan &g, const PackedMat &w, int act, int epi, GemmArgs a) {
+    a.wp = w.p;
+    a.N = g.N;
+    a.K = g.K;
+    a.KT = g.KT;
+    gemm_grid(c.dtype, 1, 1, g.tiles, col_groups, &a);
+    StepPhase ph;
+    memset(&ph, 0, sizeof ph);
+    ph.kind = STEP_GEMM;
+    ph.act = act;
+    ph.epi = epi;
+    ph.nv = a.tile_groups * a.col_groups;
+    ph.parts = g.parts;
+    ph.g = a;
+    out.push_back(ph);
+  };
+  AttnArgs at;
+  memset(&at, 0, sizeof at);
+  at.slots = nullptr;
+  at.order = nullptr;
+  at.pos = st->pos;
+  at.H = H;
+  at.d = d;
+  at.ch = m->chunk;
+  at.kt_out = d / kstep_of(c.dtype);
+  at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
+  auto attn = [&](const AttnArgs &a) {
+    StepPhase ph;
+    memset(&ph, 0, sizeof ph);
+    ph.kind = STEP_ATTN;
+    ph.nv = n * H;
+    ph.n_rows = n;
+    ph.at = a;
+    out.push_back(ph);
+  };
+
+  // gated merge (its e rows come with each launch)
+  {
+    GemmArgs a = base;
+    a.bias = m->bg;
+    a.gamma_next = m->g1;
+    a.x = b.x[0];
+    a.x_in = b.x[0];
+    a.xg = b.xg[0];
+    a.sumsq_out = b.sumsq[0];
+    gemm(m->p_merge, m->wg, ACT_MERGE, EPI_MERGE, a);
+  }
+  const size_t ring_layer = (size_t)st->B * H * W * dh * es;
+  for (int l = 0; l < L; ++l) {
+    const bool last = l == L - 1;
+    const int k0 = 3 * l;
+    {  // Q, K, V of RMSNorm(x; g1); k, v to window entry (t-1) mod W
+      GemmArgs a = base;
+      a.act = b.xg[k0];
+      a.ld_act = d;
+      a.sumsq = b.sumsq[k0];
+      a.out = b.q[2 * l];
+      a.ld_out = d;
+      a.ring_k = st->ring_k + l * ring_layer;
+      a.ring_v = st->ring_v + l * ring_layer;
+      gemm(m->p_qkv, m->wqkv[l], ACT_PLAIN, EPI_QKV, a);
+    }
+    {  // window attention
+      AttnArgs a = at;
+      a.q = b.q[2 * l];
+      a.out = b.o[2 * l];
+      a.kb = st->ring_k + l * ring_layer;
+      a.vb = st->ring_v + l * ring_layer;
+      a.s_seq = (int64_t)H * W * dh;
+      a.s_head = (int64_t)W * dh;
+      a.s_pos = dh;
+      a.len_cap = W;
+      attn(a);
+    }
+    {  // x += W_O o
+      GemmArgs a = base;
+      a.act = b.o[2 * l];
+      a.ld_act = d;
+      a.x_in = b.x[k0];
+      a.x = b.x[k0 + 1];
+      a.xg = b.xg[k0 + 1];
+      a.sumsq_out = b.sumsq[k0 + 1];
+      a.gamma_next = m->g2 + (size_t)l * d;
+      gemm(m->p_o, m->wo[l], ACT_PLAIN, EPI_RESID, a);
+    }
+    {  // cross-attention query of RMSNorm(x; g2)
+      GemmArgs a = base;
+      a.act = b.xg[k0 + 1];
+      a.ld_act = d;
+      a.sumsq = b.sumsq[k0 + 1];
+      a.out = b.q[2 * l + 1];
+      a.ld_out = d;
+      gemm(m->p_o, m->wqc[l], ACT_PLAIN, EPI_STORE, a);
+    }
+    {  // cross-attention to memory positions 1..t of group g(l)
+      const int grp = c.mem_groups == 1 ? 0 : l;
+      AttnArgs a = at;
+      a.q = b.q[2 * l + 1];
+      a.out = b.o[2 * l + 1];
+      a.kb = static_cast<const char *>(mem->k) + (size_t)grp * mem->stride_group * es;
+      a.vb = static_cast<const char *>(mem->v) + (size_t)grp * mem->stride_group * es;
+      a.s_seq = mem->stride_seq;
+      a.s_head = mem->stride_head;
+      a.s_pos = mem->stride_pos;
+      a.len_cap = 0x7fffffff;
+      attn(a);
+    }
+    {  // x += W_Oc o_c
+      GemmArgs a = base;
+      a.act = b.o[2 * l + 1];
+      a.ld_act = d;
+      a.x_in = b.x[k0 + 1];
+      a.x = b.x[k0 + 2];
+      a.xg = b.xg[k0 + 2];
+      a.sumsq_out = b.sumsq[k0 + 2];
+      a.gamma_next = m->g3 + (size_t)l * d;
+      gemm(m->p_o, m->woc[l], ACT_PLAIN, EPI_RESID, a);
+    }
+    {  // GELU(W_1 RMSNorm(x; g3))
+      GemmArgs a = base;
+      a.act = b.xg[k0 + 2];
+      a.ld_act = d;
+      a.sumsq = b.sumsq[k0 + 2];
+      a.out = b.h[l];
+      a.ld_out = F;
+      a.kt_out = F / kstep_of(c.dtype);
+      gemm(m->p_ffn1, m->w1[l], ACT_PLAIN, EPI_GELU, a);
+    }
+    {  // x += W_2 h; the last layer also writes s_t
+      GemmArgs a = base;
+      a.act = b.h[l];
+      a.ld_act = F;
+      a.x_in = b.x[k0 + 2];
+      a.x = b.x[k0 + 3];
+      a.xg = b.xg[k0 + 3];
+      a.sumsq_out = b.sumsq[k0 + 3];
+      a.gamma_next = last ? m->go : m->g1 + (size_t)(l + 1) * d;
+      if (last) {
+        a.s_out = st->s;
+        a.advance_pos = with_head ? 0 : 1;
+      }
+      gemm(m->p_ffn2, m->w2[l], ACT_PLAIN, EPI_RESID, a);
+    }
+  }
+  if (with_head) {  // logits = W_o RMSNorm(s_t; g_o) (the output comes with each launch)
+    GemmArgs a = base;
+    a.act = b.xg[3 * L];
+    a.ld_act = d;
+    a.sumsq = b.sumsq[3 * L];
+    a.advance_pos = 1;
+    gemm(m->p_head, m->wout, ACT_PLAIN, EPI_LOGITS, a);
+  }
 }
 
 rlt_status check_positions(const rlt_state *st, const rlt_memory *mem, int n,
@@ -1034,6 +1265,97 @@ rlt_status rlt_run_sequence(const rlt_model *m, rlt_state *st, int32_t T, const 
         RLT_OK)
       return rs;
   }
+  return ok();
+}
+
+size_t rlt_persistent_workspace_bytes(const rlt_config *cfg, int32_t n) {
+  if (check_config(cfg) != RLT_OK || n < 1) return 0;
+  StepBufs b;
+  return step_layout(*cfg, n, nullptr, &b);
+}
+
+rlt_status rlt_run_sequence_persistent(const rlt_model *m, rlt_state *st, int32_t T,
+                                       const void *dev_e, const rlt_memory *mem,
+                                       float *dev_logits, int32_t logits_mode,
+                                       void *dev_workspace, size_t workspace_bytes,
+                                       void *stream) {
+  rlt_status rs;
+  if ((rs = check_state(m, st)) != RLT_OK) return rs;
+  if (T < 1) return fail(RLT_ERR_INVALID_ARG, "T must be >= 1");
+  if (!dev_e) return fail(RLT_ERR_INVALID_ARG, "dev_e is NULL");
+  if (logits_mode != RLT_LOGITS_ALL && logits_mode != RLT_LOGITS_LAST &&
+      logits_mode != RLT_LOGITS_NONE)
+    return fail(RLT_ERR_INVALID_ARG, "bad logits_mode");
+  if (logits_mode != RLT_LOGITS_NONE && !dev_logits)
+    return fail(RLT_ERR_INVALID_ARG, "dev_logits is NULL");
+  if (!dev_workspace) return fail(RLT_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)dev_workspace % 256) return fail(RLT_ERR_SHAPE, "workspace must be 256-byte aligned");
+  const rlt_config &c = m->cfg;
+  StepBufs b;
+  const size_t need = step_layout(c, st->B, nullptr, &b);
+  if (workspace_bytes < need)
+    return fail(RLT_ERR_SHAPE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  const int grid = step_grid(c.dtype, c.head_dim);
+  if (grid < 8 || grid > kStepMaxGrid)
+    return fail(RLT_ERR_UNSUPPORTED, "no persistent step for this dtype and head_dim %d",
+                c.head_dim);
+  const uint64_t epochs = (uint64_t)T * (uint64_t)step_phases_max(c);
+  if (epochs >= (1ull << 31)) return fail(RLT_ERR_RANGE, "T too large for one call");
+  if ((rs = check_memory(m, mem, st->B - 1)) != RLT_OK) return rs;
+  if ((rs = check_positions(st, mem, st->B, nullptr, T)) != RLT_OK) return rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  step_layout(c, st->B, dev_workspace, &b);
+  // phase tables for steps without and with the head
+  for (int t = 0; t < 2; ++t) {
+    build_step_phases(m, st, mem, b, t == 1, st->step_tab[t]);
+    hipError_t e = hipMemcpyAsync(b.tab[t], st->step_tab[t].data(),
+                                  st->step_tab[t].size() * sizeof(StepPhase),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "phase table upload");
+  }
+  // barrier lines, release and error words start at zero in every call
+  hipError_t e = launch_zero(b.flags, (size_t)((char *)b.tab[0] - (char *)b.flags), s);
+  if (e != hipSuccess) return hip_fail(e, "barrier reset");
+  const int d = c.d_model, V = c.vocab, es = m->esize;
+  for (int k = 0; k < T; ++k) {
+    StepRun r;
+    r.e = static_cast<const char *>(dev_e) + (size_t)k * d * es;
+    r.ld_e = (int64_t)T * d;
+    r.logits = nullptr;
+    r.ld_logits = V;
+    if (logits_mode == RLT_LOGITS_ALL) {
+      r.logits = dev_logits + (size_t)k * V;
+      r.ld_logits = (int64_t)T * V;
+    } else if (logits_mode == RLT_LOGITS_LAST && k == T - 1) {
+      r.logits = dev_logits;
+    }
+    const int t = r.logits ? 1 : 0;
+    r.ph = b.tab[t];
+    r.n_phases = (int)st->step_tab[t].size();
+    r.flags = b.flags;
+    r.rel = b.rel;
+    r.err = b.err;
+    r.epoch0 = (unsigned)((uint64_t)k * step_phases_max(c));
+    e = launch_step(c.dtype, c.head_dim, r, grid, s);
+    if (e != hipSuccess) return hip_fail(e, "persistent step launch");
+  }
+  for (int i = 0; i < st->B; ++i) st->host_pos[i] += T;
+  return ok();
+}
+
+rlt_status rlt_persistent_check(void *dev_workspace, void *stream) {
+  if (!dev_workspace) return fail(RLT_ERR_INVALID_ARG, "workspace is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  // the error word follows the barrier lines and the release word
+  const char *p = static_cast<const char *>(dev_workspace) +
+                  align256((size_t)kStepMaxGrid * kStepFlagWords * 4) + 256;
+  unsigned err = 0;
+  e = hipMemcpy(&err, p, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the error word");
+  if (err) return fail(RLT_ERR_DEVICE, "a grid barrier of the persistent step timed out");
   return ok();
 }
 

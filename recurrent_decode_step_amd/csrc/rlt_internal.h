@@ -81,7 +81,9 @@ struct GemmArgs {
   const float *sumsq; int n_parts; int part_ld; float eps;
   // epilogues
   void *out; int64_t ld_out;                // QKV (q part)/STORE/GELU: storage type; LOGITS: fp32
-  float *x;                                 // RESID/MERGE: fp32 residual stream [n][d]
+  float *x;                                 // RESID/MERGE: fp32 residual stream [n][d] (written)
+  const float *x_in;                        // RESID: the stream before this sublayer (read; == x
+                                            // in the launch chain)
   void *xg;                                 // RESID/MERGE: x * gamma_next, storage type, packed
   const float *gamma_next;
   float *sumsq_out;                         // RESID/MERGE: [N/16][part_ld]
@@ -141,6 +143,8 @@ hipError_t launch_pack_tiles(const void *src, int rows, int K, int64_t ld, int t
                              int tile_end, const PackedMat &dst, int dtype, hipStream_t s);
 hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const GemmArgs &a, int tiles,
                        int col_groups, int parts, hipStream_t s);
+// the grid of launch_gemm: tile groups, column groups and XCD placement (b->K set)
+void gemm_grid(int dtype, int ncb, int tpw, int tiles, int col_groups, GemmArgs *b);
 // Large batches (bf16, plain activations, more than 64 rows): persistent
 // GEMM with the same arithmetic as launch_gemm.  gemm_persistent_applies
 // says whether it takes a shape; launch_gemm_persistent reports real errors.
@@ -154,6 +158,40 @@ hipError_t launch_sample(const SampleArgs &a, int n_rows, hipStream_t s);
 // stand-in incremental encoder: e rows and memory entries of the sampled tokens
 hipError_t launch_encode(int dtype, const EncodeArgs &a, int n_rows, hipStream_t s);
 hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStream_t s);
+
+// ------------------------------------------------------ persistent step
+// One decoder step as a single cooperative launch: the phases of the launch
+// chain (merge, per layer QKV, window attention, O, Qc, cross-attention, Oc,
+// FFN-up, FFN-down, then the head) run one after the other inside the kernel,
+// separated by grid barriers.  Each phase runs the launch chain's own
+// per-workgroup code (same K parts and summation order, so the same bits);
+// its outputs go to buffers no other phase of the launch writes, with
+// write-through stores, so a reader on another XCD never holds a stale line.
+enum StepKind { STEP_GEMM = 0, STEP_ATTN = 1 };
+struct StepPhase {
+  int kind;            // StepKind
+  int act, epi;        // GEMM: activation source and epilogue
+  int nv;              // GEMM: workgroups of the launch chain's grid (NCB = TPW = 1);
+                       // ATTN: rows x heads
+  int parts;           // GEMM: wavefronts per workgroup (K parts: 1, 2, 4 or 8)
+  int n_rows;          // ATTN: rows
+  GemmArgs g;
+  AttnArgs at;
+};
+struct StepRun {
+  const StepPhase *ph; int n_phases;
+  const void *e; int64_t ld_e;          // this step's merge input (e rows)
+  float *logits; int64_t ld_logits;     // this step's head output (null: no head phase)
+  unsigned *flags;                      // [grid][64] arrival epochs, one line per workgroup
+  unsigned *rel;                        // release epoch
+  unsigned *err;                        // nonzero: a barrier wait timed out
+  unsigned epoch0;                      // barrier epochs of this launch: epoch0 + 1, ...
+};
+constexpr int kStepThreads = 512;
+constexpr int kStepFlagWords = 64;      // one 256-byte line per workgroup
+// workgroups of the cooperative launch (one per CU) or 0 when unsupported
+int step_grid(int dtype, int dh);
+hipError_t launch_step(int dtype, int dh, const StepRun &r, int grid, hipStream_t s);
 int attn_chunk_max(int dtype, int dh);
 hipError_t launch_state_init(float *s, int *pos, const float *s_star, int B, int d,
                              const int *slots, int n, hipStream_t st);

@@ -118,11 +118,54 @@ struct GemmRegs {
   static constexpr int AB = raw >= KSW ? KSW : (raw >= 16 ? 16 : (raw >= 8 ? 8 : (raw >= 4 ? 4 : 2)));
 };
 
+// Stores of values that other workgroups read later in the same launch (the
+// persistent step kernel, WT = true) go through to memory (agent-scope
+// stores, sc1), so a reader on another XCD that has never cached the line
+// sees them; the launch chain (WT = false) uses ordinary stores, made visible
+// by the kernel boundary.
+template <bool WT>
+__device__ __forceinline__ void st_b64(void *p, uint64_t v) {
+  if constexpr (WT) __hip_atomic_store(static_cast<uint64_t *>(p), v, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  else *static_cast<uint64_t *>(p) = v;
+}
+template <bool WT>
+__device__ __forceinline__ void st_f32(float *p, float v) {
+  if constexpr (WT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool WT>
+__device__ __forceinline__ void st_u32x4(void *p, const u32x4 &v) {
+  if constexpr (WT) {
+    st_b64<true>(p, (uint64_t)v.x | ((uint64_t)v.y << 32));
+    st_b64<true>(static_cast<char *>(p) + 8, (uint64_t)v.z | ((uint64_t)v.w << 32));
+  } else {
+    *static_cast<u32x4 *>(p) = v;
+  }
+}
+template <bool WT>
+__device__ __forceinline__ void st_f32x4(float *p, float a0, float a1, float a2, float a3) {
+  if constexpr (WT) st_u32x4<true>(p, u32x4{__float_as_uint(a0), __float_as_uint(a1),
+                                            __float_as_uint(a2), __float_as_uint(a3)});
+  else *reinterpret_cast<f32x4 *>(p) = f32x4{a0, a1, a2, a3};
+}
+// four values in the storage type (Num<T>::store4)
+template <typename T, bool WT>
+__device__ __forceinline__ void st4(T *p, const float *y) {
+  if constexpr (!WT) {
+    Num<T>::store4(p, y);
+  } else if constexpr (sizeof(T) == 2) {
+    st_b64<true>(p, (uint64_t)f2bf2(y[0], y[1]) | ((uint64_t)f2bf2(y[2], y[3]) << 32));
+  } else {
+    st_f32x4<true>(reinterpret_cast<float *>(p), y[0], y[1], y[2], y[3]);
+  }
+}
+
 // Epilogue of one 16-row weight tile and one 16-column batch block: yv is the
 // reduced tile; lane holds features rbase..rbase+3 of batch column c (within
 // the column group starting at col0).  Called by a whole wavefront.
 // have_pre: x_pre / g_pre hold x and gamma_next of this lane (RESID).
-template <typename T, int EPI>
+template <typename T, int EPI, bool WT>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x4 yv, int tile, int c, int col0,
                                               int ncols, float rinv, bool have_pre, f32x4 x_pre,
                                               f32x4 g_pre, int lane) {
@@ -142,7 +185,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x4 yv, int t
       float *xp = a.x + (size_t)i * a.d + rbase;
       float xv[4];
       if constexpr (EPI == EPI_RESID) {
-        const f32x4 old = have_pre ? x_pre : *reinterpret_cast<const f32x4 *>(xp);
+        const f32x4 old =
+            have_pre ? x_pre : *reinterpret_cast<const f32x4 *>(a.x_in + (size_t)i * a.d + rbase);
         xv[0] = old.x + y[0]; xv[1] = old.y + y[1]; xv[2] = old.z + y[2]; xv[3] = old.w + y[3];
       } else {
         // x = g * e + (1 - g) * s, g = sigmoid(W_g [e ; s] + b_g)
@@ -158,40 +202,38 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x4 yv, int t
           xv[u] = g * ev + (1.0f - g) * sp[u];
         }
       }
-      *reinterpret_cast<f32x4 *>(xp) = f32x4{xv[0], xv[1], xv[2], xv[3]};
-      if (a.s_out)
-        *reinterpret_cast<f32x4 *>(a.s_out + (size_t)sl * a.d + rbase) =
-            f32x4{xv[0], xv[1], xv[2], xv[3]};
+      st_f32x4<WT>(xp, xv[0], xv[1], xv[2], xv[3]);
+      if (a.s_out) st_f32x4<WT>(a.s_out + (size_t)sl * a.d + rbase, xv[0], xv[1], xv[2], xv[3]);
       // input of the next RMSNorm'd GEMM: x * gamma_next, storage type, packed
       const f32x4 gn = (EPI == EPI_RESID && have_pre)
                            ? g_pre : *reinterpret_cast<const f32x4 *>(a.gamma_next + rbase);
       const float xg[4] = {xv[0] * gn.x, xv[1] * gn.y, xv[2] * gn.z, xv[3] * gn.w};
-      Num<T>::store4(static_cast<T *>(a.xg) + packed_off<T>(i, rbase, a.kt_out), xg);
+      st4<T, WT>(static_cast<T *>(a.xg) + packed_off<T>(i, rbase, a.kt_out), xg);
       ss = ((xv[0] * xv[0] + xv[1] * xv[1]) + xv[2] * xv[2]) + xv[3] * xv[3];
     }
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    if (lane < 16 && c < ncols) a.sumsq_out[(size_t)tile * a.part_ld + i] = ss;
+    if (lane < 16 && c < ncols) st_f32<WT>(a.sumsq_out + (size_t)tile * a.part_ld + i, ss);
   } else if (live) {
     if constexpr (EPI == EPI_QKV) {
       const int d = a.d;
       const int which = rbase / d;
       const int f = rbase - which * d;
       if (which == 0) {
-        Num<T>::store4(static_cast<T *>(a.out) + (size_t)i * a.ld_out + f, y);
+        st4<T, WT>(static_cast<T *>(a.out) + (size_t)i * a.ld_out + f, y);
       } else {
         const int h = f / a.dh, cc = f - h * a.dh;
         const int sl = slot_of(a, i);
         const int w = a.pos[sl] % a.W;          // entry of position t = pos + 1
         T *ring = static_cast<T *>(which == 1 ? a.ring_k : a.ring_v);
-        Num<T>::store4(ring + (((size_t)sl * a.H + h) * a.W + w) * a.dh + cc, y);
+        st4<T, WT>(ring + (((size_t)sl * a.H + h) * a.W + w) * a.dh + cc, y);
       }
     } else if constexpr (EPI == EPI_STORE) {
-      Num<T>::store4(static_cast<T *>(a.out) + (size_t)i * a.ld_out + rbase, y);
+      st4<T, WT>(static_cast<T *>(a.out) + (size_t)i * a.ld_out + rbase, y);
     } else if constexpr (EPI == EPI_GELU) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) y[u] = gelu_erf(y[u]);
-      Num<T>::store4(static_cast<T *>(a.out) + packed_off<T>(i, rbase, a.kt_out), y);
+      st4<T, WT>(static_cast<T *>(a.out) + packed_off<T>(i, rbase, a.kt_out), y);
     } else if constexpr (EPI == EPI_LOGITS) {
       float *lp = static_cast<float *>(a.out) + (size_t)i * a.ld_out + rbase;
 #pragma unroll
@@ -201,18 +243,35 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x4 yv, int t
   }
 }
 
-template <typename T, int NCB, int ACT, int EPI, int KSW, int TPW>
-__global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
+// One workgroup's work of the GEMM (workgroup index L of the launch's grid),
+// run by a group of NW wavefronts (the K parts): `wave` and `tid` are indices
+// within the group, s_acc ([NW][TPW][NCB][64]), s_grp and s_rinv the group's
+// LDS.  k_gemm runs it as the whole workgroup; the persistent step kernel runs
+// several groups side by side.  Every group of a workgroup passes the same
+// workgroup barriers: a group with no work (valid = false) passes them too.
+template <typename T, int NCB, int ACT, int EPI, int KSW, int TPW, bool WT>
+__device__ __forceinline__ void gemm_vwg(const GemmArgs &a, int L, bool valid, int NW, int wave,
+                                         int tid, f32x4 *s_acc, float (*s_grp)[NCB * 16],
+                                         float *s_rinv) {
   constexpr int COLS = NCB * 16;
   constexpr int WB = KSW;                          // k-steps per batch of weight loads
   constexpr int AB = GemmRegs<KSW, TPW, NCB>::AB;  // activation k-steps in registers
   constexpr bool SCALED = EPI == EPI_QKV || EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_LOGITS;
-  extern __shared__ f32x4 s_acc[];                 // [parts][TPW][NCB][64] partial tiles
-  __shared__ float s_grp[8][COLS];
-  __shared__ float s_rinv[COLS];
-
-  const int NW = blockDim.x >> 6;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // The workgroup index, the group size and the wavefront index are the same
+  // on every lane of a wavefront: held in scalar registers, so every branch on
+  // them (the part bounds, the guarded MFMAs of a short batch) is a scalar
+  // branch.  An MFMA inside a lane-masked region would still run on all
+  // lanes (matrix instructions do not honour the execution mask).
+  L = __builtin_amdgcn_readfirstlane(L);
+  NW = __builtin_amdgcn_readfirstlane(NW);
+  wave = __builtin_amdgcn_readfirstlane(wave);
+  if (!__builtin_amdgcn_readfirstlane((int)valid)) {
+    if constexpr (SCALED) __syncthreads();
+    __syncthreads();
+    return;
+  }
+  const int lane = tid & 63;
+  const int NT = NW * 64;                          // threads of the group
   // Workgroup L runs on XCD L mod 8.  XCD-aware placement: the XCDs form
   // xcd_sets sets, set s serving column groups s*gx .. s*gx+gx-1 and each
   // XCD of a set a share of the tile groups; within an XCD the column groups
@@ -220,7 +279,6 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
   // once per set and the set's activations stay in that XCD's L2.
   int tg, cg;
   {
-    const int L = blockIdx.x;
     if (a.xcd_sets > 0) {
       const int NS = a.xcd_sets, xcd = L & 7, k = L >> 3;
       const int gx = a.col_groups / NS, tgx = (a.tile_groups * NS) >> 3;
@@ -277,7 +335,7 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
     if (wave < TPW * NCB) {
       const int rb = (tile0 + wave / NCB) * 16 + (lane >> 4) * 4;   // < N = d
       const int c = min((wave % NCB) * 16 + (lane & 15), ncols - 1);
-      x_pre = *reinterpret_cast<const f32x4 *>(a.x + (size_t)(col0 + c) * a.d + rb);
+      x_pre = *reinterpret_cast<const f32x4 *>(a.x_in + (size_t)(col0 + c) * a.d + rb);
       g_pre = *reinterpret_cast<const f32x4 *>(a.gamma_next + rb);
     }
   }
@@ -287,7 +345,7 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
   if constexpr (SCALED) {
     const int P = a.n_parts;
     const int per = (P + 7) / 8;
-    for (int q = tid; q < COLS * 8; q += blockDim.x) {
+    for (int q = tid; q < COLS * 8; q += NT) {
       const int c = q % COLS, g = q / COLS;
       const float *src = a.sumsq + col0 + min(c, ncols - 1);
       const int p0 = g * per, p1 = min(P, p0 + per);
@@ -302,7 +360,7 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
       s_grp[g][c] = ss;
     }
     __syncthreads();
-    for (int c = tid; c < COLS; c += blockDim.x) {
+    for (int c = tid; c < COLS; c += NT) {
       float ss = s_grp[0][c];
 #pragma unroll
       for (int g = 1; g < 8; ++g) ss += s_grp[g][c];
@@ -410,14 +468,24 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
     f32x4 yv = s_acc[(t * NCB + cb) * 64 + lane];
     for (int w = 1; w < NW; ++w) yv += s_acc[((w * TPW + t) * NCB + cb) * 64 + lane];
     const int c = cb * 16 + (lane & 15);
-    gemm_epilogue<T, EPI>(a, yv, tile0 + t, c, col0, ncols, SCALED ? s_rinv[c] : 1.f, q == wave,
-                          x_pre, g_pre, lane);
+    gemm_epilogue<T, EPI, WT>(a, yv, tile0 + t, c, col0, ncols, SCALED ? s_rinv[c] : 1.f,
+                              q == wave, x_pre, g_pre, lane);
   }
 
   // the last kernel of a step advances the positions (no reader of pos runs in it)
   if (a.advance_pos && tg == 0 && cg == 0) {
-    for (int i = tid; i < a.n_rows; i += blockDim.x) a.pos[slot_of(a, i)] += 1;
+    for (int i = tid; i < a.n_rows; i += NT) a.pos[slot_of(a, i)] += 1;
   }
+}
+
+template <typename T, int NCB, int ACT, int EPI, int KSW, int TPW>
+__global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
+  extern __shared__ f32x4 s_acc[];                 // [parts][TPW][NCB][64] partial tiles
+  __shared__ float s_grp[8][NCB * 16];
+  __shared__ float s_rinv[NCB * 16];
+  gemm_vwg<T, NCB, ACT, EPI, KSW, TPW, false>(a, (int)blockIdx.x, true, (int)(blockDim.x >> 6),
+                                              (int)(threadIdx.x >> 6), (int)threadIdx.x, s_acc,
+                                              s_grp, s_rinv);
 }
 
 // Large batches: a persistent form of k_gemm for 32-row column groups with
@@ -444,7 +512,9 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
   __shared__ float s_rinv[COLS];
 
   const int NW = blockDim.x >> 6;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // wavefront index in a scalar register: the guarded MFMAs of a short part
+  // are then scalar branches (an MFMA in a lane-masked region still runs)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int G = a.col_groups;
   const int wg = blockIdx.x, x = wg & 7, m = wg >> 3;
   const int cg = m % G, l = m / G, L8 = ((int)gridDim.x >> 3) / G;
@@ -530,7 +600,7 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
         f32x4 y = s_acc[buf][0][cb][lane];
         for (int w = 1; w < NW; ++w) y += s_acc[buf][w][cb][lane];
         const int c = cb * 16 + (lane & 15);
-        gemm_epilogue<T, EPI>(a, y, tile, c, col0, ncols, SCALED ? s_rinv[c] : 1.f,
+        gemm_epilogue<T, EPI, false>(a, y, tile, c, col0, ncols, SCALED ? s_rinv[c] : 1.f,
                               pre && cb == wave, xp, gp, lane);
       }
     }
@@ -540,7 +610,7 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
       // every wavefront loads (clamped column block), only cb < NCB uses it
       const int rb = tile * 16 + (lane >> 4) * 4;
       const int c = min(min(wave, NCB - 1) * 16 + (lane & 15), ncols - 1);
-      xp = *reinterpret_cast<const f32x4 *>(a.x + (size_t)(col0 + c) * a.d + rb);
+      xp = *reinterpret_cast<const f32x4 *>(a.x_in + (size_t)(col0 + c) * a.d + rb);
       gp = *reinterpret_cast<const f32x4 *>(a.gamma_next + rb);
     }
   };
@@ -735,22 +805,26 @@ __device__ __forceinline__ void attn_chunk(const float *qf, const u32x4 *kr, con
   m = mnew;
 }
 
-// KIND 0: sliding window over the decoder cache; 1: encoder memory (the same
-// code, two symbols so profiles keep them apart)
-template <typename T, int DH, int KIND, int UU = 0>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void k_attn(const AttnArgs a) {
+// The attention of batch row i (launch order) and head h, run by a group of 4
+// wavefronts (tid = 0..255 within the group) with the group's LDS.  k_attn
+// runs it as the whole workgroup; the persistent step kernel runs two groups
+// side by side.  A group with no work (valid = false) passes the workgroup
+// barrier too.
+template <typename T, int DH, int UU, bool WT>
+__device__ __forceinline__ void attn_item(const AttnArgs &a, int i, int h, bool valid, int tid,
+                                          float (*s_o)[DH], float (*s_ml)[2]) {
   using S = AttnShape<T, DH, UU>;
   constexpr int EPL = S::EPL, LPR = S::LPR, RPW = S::RPW, U = S::U;
-  __shared__ float s_o[4][DH];
-  __shared__ float s_ml[4][2];
-
-  const int i = a.order ? a.order[blockIdx.y] : (int)blockIdx.x;
-  const int h = a.order ? (int)blockIdx.x : (int)blockIdx.y;
+  i = __builtin_amdgcn_readfirstlane(i);        // the same on every lane (see gemm_vwg)
+  h = __builtin_amdgcn_readfirstlane(h);
+  if (!__builtin_amdgcn_readfirstlane((int)valid)) {
+    __syncthreads();
+    return;
+  }
   const int slot = a.slots ? a.slots[i] : i;
   const int t = a.pos[slot] + 1;
   const int len = min(t, a.len_cap);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave = tid >> 6, lane = tid & 63;
   const int sub = lane % LPR, row = lane / LPR;
   const int my = wave * RPW + row;                 // this lane's position within a load group
 
@@ -830,9 +904,21 @@ void k_attn(const AttnArgs a) {
       for (int w = 0; w < 4; ++w) acc += s_o[w][f * EPL + e] * sc[w];
       v[e] = acc / L;
     }
-    *reinterpret_cast<u32x4 *>(static_cast<T *>(a.out) + packed_off<T>(i, h * DH + f * EPL, a.kt_out)) =
-        Num<T>::pack(v);
+    st_u32x4<WT>(static_cast<T *>(a.out) + packed_off<T>(i, h * DH + f * EPL, a.kt_out),
+                 Num<T>::pack(v));
   }
+}
+
+// KIND 0: sliding window over the decoder cache; 1: encoder memory (the same
+// code, two symbols so profiles keep them apart)
+template <typename T, int DH, int KIND, int UU = 0>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void k_attn(const AttnArgs a) {
+  __shared__ float s_o[4][DH];
+  __shared__ float s_ml[4][2];
+  const int i = a.order ? a.order[blockIdx.y] : (int)blockIdx.x;
+  const int h = a.order ? (int)blockIdx.x : (int)blockIdx.y;
+  attn_item<T, DH, UU, false>(a, i, h, true, (int)threadIdx.x, s_o, s_ml);
 }
 
 // ---------------------------------------------------------------- scoring
@@ -1201,22 +1287,26 @@ int gemm_ksw(int dtype, int ks_per_part) {
   return ks_per_part >= 16 ? 16 : 8;
 }
 
+void gemm_grid(int dtype, int ncb, int tpw, int tiles, int col_groups, GemmArgs *b) {
+  b->tile_groups = tiles / tpw;
+  b->col_groups = col_groups;
+  // XCD sets: as few as keep each XCD's column groups' activations within
+  // half an L2 (2 MiB); used when the grid splits evenly over the 8 XCDs
+  const size_t act_group = (size_t)ncb * 16 * b->K * (dtype == RLT_DTYPE_BF16 ? 2 : 4);
+  int ns = 1;
+  while (ns < 8 && col_groups % (2 * ns) == 0 && (size_t)(col_groups / ns) * act_group > ((size_t)2 << 20))
+    ns *= 2;
+  const bool even = ((size_t)b->tile_groups * col_groups) % 8 == 0 && col_groups % ns == 0 &&
+                    (b->tile_groups * ns) % 8 == 0;
+  b->xcd_sets = even ? ns : 0;
+}
+
 hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const GemmArgs &a, int tiles,
                        int col_groups, int parts, hipStream_t s) {
   if (parts < 1 || parts > kMaxParts || (tpw != 1 && tpw != 2) || tiles % tpw || col_groups < 1)
     return hipErrorInvalidValue;
   GemmArgs b = a;
-  b.tile_groups = tiles / tpw;
-  b.col_groups = col_groups;
-  // XCD sets: as few as keep each XCD's column groups' activations within
-  // half an L2 (2 MiB); used when the grid splits evenly over the 8 XCDs
-  const size_t act_group = (size_t)ncb * 16 * a.K * (dtype == RLT_DTYPE_BF16 ? 2 : 4);
-  int ns = 1;
-  while (ns < 8 && col_groups % (2 * ns) == 0 && (size_t)(col_groups / ns) * act_group > ((size_t)2 << 20))
-    ns *= 2;
-  const bool even = ((size_t)b.tile_groups * col_groups) % 8 == 0 && col_groups % ns == 0 &&
-                    (b.tile_groups * ns) % 8 == 0;
-  b.xcd_sets = even ? ns : 0;
+  gemm_grid(dtype, ncb, tpw, tiles, col_groups, &b);
   const dim3 grid((unsigned)(b.tile_groups * col_groups));
   const int threads = parts * 64;
   const int ksw = gemm_ksw(dtype, a.KT / parts);
@@ -1337,6 +1427,191 @@ hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStre
   if (dtype == RLT_DTYPE_BF16)
     return mem ? attn_dispatch<bf16_t, 1>(dh, a, n_rows, s) : attn_dispatch<bf16_t, 0>(dh, a, n_rows, s);
   return mem ? attn_dispatch<float, 1>(dh, a, n_rows, s) : attn_dispatch<float, 0>(dh, a, n_rows, s);
+}
+
+// ---------------------------------------------------------- persistent step
+// Grid barrier of the persistent step: every workgroup publishes the epoch in
+// its own line once its stores are complete; workgroup 0 gathers the lines and
+// publishes the epoch in the release word, which the others wait for.  All
+// flag traffic is agent-scope (sc1), bypassing the non-coherent L2s.  Every
+// wait is bounded by the real-time clock (0.2 s): on timeout the kernel sets
+// the error word and every workgroup leaves (a later wait also times out or
+// sees the error word), so the launch always ends.
+constexpr uint64_t kStepWaitTicks = 20000000;   // s_memrealtime runs at 100 MHz
+
+__device__ __forceinline__ unsigned step_ld(const unsigned *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void step_st(unsigned *p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until *p >= target (wrap-free: epochs grow within one call) or timeout
+__device__ __forceinline__ bool step_wait(const unsigned *p, unsigned target, unsigned *err) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (step_ld(p) < target) {
+    if (step_ld(err) != 0u) return false;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kStepWaitTicks) {
+      step_st(err, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+__device__ __forceinline__ bool step_barrier(const StepRun &r, unsigned epoch, int *s_bad) {
+  __builtin_amdgcn_s_waitcnt(0);                 // this thread's stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    *s_bad = 0;
+    step_st(r.flags + (size_t)kStepFlagWords * blockIdx.x, epoch);
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (unsigned w = threadIdx.x; w < gridDim.x; w += blockDim.x)
+      if (!step_wait(r.flags + (size_t)kStepFlagWords * w, epoch, r.err)) *s_bad = 1;
+    __syncthreads();
+    if (threadIdx.x == 0 && !*s_bad) step_st(r.rel, epoch);
+  } else if (threadIdx.x == 0) {
+    if (!step_wait(r.rel, epoch, r.err)) *s_bad = 1;
+  }
+  __syncthreads();
+  return *s_bad == 0;
+}
+
+// One GEMM phase: the launch chain's workgroups v = 0..nv-1, spread over the
+// grid; a workgroup of 8 wavefronts runs 8 / parts of them side by side.
+// Workgroup v runs on a workgroup with the same index mod 8, so the XCD-aware
+// placement of the launch chain holds.
+template <typename T, int ACT, int EPI, int KSW>
+__device__ __forceinline__ void step_gemm(const GemmArgs &ga, int nv, int P, f32x4 *s_acc,
+                                          float (*s_grp)[8][16], float (*s_rinv)[16]) {
+  const int wave = threadIdx.x >> 6;
+  const int groups = 8 / P, grp = wave / P, gw = wave - grp * P;
+  const int gtid = threadIdx.x - grp * P * 64;
+  const int per_round = (int)gridDim.x * groups;
+  const int rounds = (nv + per_round - 1) / per_round;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int v = (int)blockIdx.x + (int)gridDim.x * (grp + groups * rd);
+    gemm_vwg<T, 1, ACT, EPI, KSW, 1, true>(ga, v, v < nv, P, gw, gtid, s_acc + grp * P * 64,
+                                           s_grp[grp], s_rinv[grp]);
+    if (rd + 1 < rounds) __syncthreads();        // LDS of this round read before the next fills it
+  }
+}
+
+// The phase's GemmArgs are read where they lie (the phase table); the merge
+// and head phases take this step's e rows and logits from the launch.
+template <typename T, int KSW>
+__device__ __forceinline__ void step_gemm_epi(const StepPhase &d, const StepRun &r,
+                                              f32x4 *s_acc, float (*s_grp)[8][16],
+                                              float (*s_rinv)[16]) {
+  switch (d.epi) {
+    case EPI_QKV: step_gemm<T, ACT_PLAIN, EPI_QKV, KSW>(d.g, d.nv, d.parts, s_acc, s_grp, s_rinv); break;
+    case EPI_STORE: step_gemm<T, ACT_PLAIN, EPI_STORE, KSW>(d.g, d.nv, d.parts, s_acc, s_grp, s_rinv); break;
+    case EPI_RESID: step_gemm<T, ACT_PLAIN, EPI_RESID, KSW>(d.g, d.nv, d.parts, s_acc, s_grp, s_rinv); break;
+    case EPI_GELU: step_gemm<T, ACT_PLAIN, EPI_GELU, KSW>(d.g, d.nv, d.parts, s_acc, s_grp, s_rinv); break;
+    case EPI_MERGE: {
+      GemmArgs ga = d.g;
+      ga.act = r.e;
+      ga.ld_act = r.ld_e;
+      step_gemm<T, ACT_MERGE, EPI_MERGE, KSW>(ga, d.nv, d.parts, s_acc, s_grp, s_rinv);
+      break;
+    }
+    case EPI_LOGITS: {
+      GemmArgs ga = d.g;
+      ga.out = r.logits;
+      ga.ld_out = r.ld_logits;
+      step_gemm<T, ACT_PLAIN, EPI_LOGITS, KSW>(ga, d.nv, d.parts, s_acc, s_grp, s_rinv);
+      break;
+    }
+  }
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(kStepThreads) void k_step(const StepRun r) {
+  __shared__ f32x4 s_acc[kMaxParts * 64];        // GEMM groups' partial tiles
+  __shared__ float s_grp[8][8][16];              // GEMM groups' 1/rms partial sums
+  __shared__ float s_rinv[8][16];
+  __shared__ float s_o[2][4][DH];                // attention groups' combine
+  __shared__ float s_ml[2][4][2];
+  __shared__ int s_bad;
+  if (threadIdx.x == 0) s_bad = step_ld(r.err) != 0u;
+  __syncthreads();
+  if (s_bad) return;                             // an earlier launch timed out
+  for (int p = 0; p < r.n_phases; ++p) {
+    const StepPhase &d = r.ph[p];
+    if (d.kind == STEP_GEMM) {
+      // batches of 8 k-steps: the load batch size changes no result
+      step_gemm_epi<T, 8>(d, r, s_acc, s_grp, s_rinv);
+    } else {
+      // attention items (row, head), two groups of 4 wavefronts per workgroup
+      const int grp = threadIdx.x >> 8, gtid = threadIdx.x & 255;
+      const int H = d.at.H;
+      const int per_round = (int)gridDim.x * 2;
+      const int rounds = (d.nv + per_round - 1) / per_round;
+      for (int rd = 0; rd < rounds; ++rd) {
+        const int v = (int)blockIdx.x + (int)gridDim.x * (grp + 2 * rd);
+        const bool valid = v < d.nv;
+        attn_item<T, DH, 0, true>(d.at, valid ? v / H : 0, valid ? v % H : 0, valid, gtid,
+                                  s_o[grp], s_ml[grp]);
+        if (rd + 1 < rounds) __syncthreads();    // LDS of this item read before the next fills it
+      }
+    }
+    if (p + 1 < r.n_phases && !step_barrier(r, r.epoch0 + (unsigned)p + 1, &s_bad)) return;
+  }
+}
+
+template <typename T, int DH>
+static hipError_t step_go(const StepRun &r, int grid, hipStream_t s) {
+  StepRun rr = r;
+  void *args[] = {&rr};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(k_step<T, DH>), dim3(grid),
+                                    dim3(kStepThreads), args, 0, s);
+}
+
+template <typename T, int DH>
+static int step_grid_of() {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_step<T, DH>, kStepThreads, 0) !=
+      hipSuccess || per < 1)
+    return 0;
+  return cus - cus % 8;            // a multiple of 8 keeps workgroup v on XCD v mod 8
+}
+
+int step_grid(int dtype, int dh) {
+  if (dtype == RLT_DTYPE_BF16) {
+    switch (dh) {
+      case 32: return step_grid_of<bf16_t, 32>();
+      case 64: return step_grid_of<bf16_t, 64>();
+      case 128: return step_grid_of<bf16_t, 128>();
+    }
+  } else {
+    switch (dh) {
+      case 16: return step_grid_of<float, 16>();
+      case 32: return step_grid_of<float, 32>();
+      case 64: return step_grid_of<float, 64>();
+    }
+  }
+  return 0;
+}
+
+hipError_t launch_step(int dtype, int dh, const StepRun &r, int grid, hipStream_t s) {
+  if (dtype == RLT_DTYPE_BF16) {
+    switch (dh) {
+      case 32: return step_go<bf16_t, 32>(r, grid, s);
+      case 64: return step_go<bf16_t, 64>(r, grid, s);
+      case 128: return step_go<bf16_t, 128>(r, grid, s);
+    }
+  } else {
+    switch (dh) {
+      case 16: return step_go<float, 16>(r, grid, s);
+      case 32: return step_go<float, 32>(r, grid, s);
+      case 64: return step_go<float, 64>(r, grid, s);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_state_init(float *s, int *pos, const float *s_star, int B, int d,

@@ -281,13 +281,16 @@ def test_batch_composition_is_bitwise_invisible(dtype):
 
 @pytest.mark.parametrize("shape", [dict(n_layers=2, mem_groups=2),
                                    dict(d_model=256, n_heads=2, d_ffn=4096, vocab=300, n_layers=2,
+                                        mem_groups=1),
+                                   dict(d_model=128, n_heads=2, d_ffn=512, vocab=60, n_layers=2,
                                         mem_groups=1)])
 def test_large_batch_kernels_match_small_batch_bitwise(shape):
     """Steps over more than 64 rows run the persistent GEMM (activations held
     in registers, many tiles per workgroup; d_ffn = 4096 also takes its
-    chunked long-K form); the same slots stepped in groups of at most 64 rows
-    run the per-tile GEMM.  The arithmetic is the same, so the logits are
-    bitwise equal."""
+    chunked long-K form; d_model = 128 gives parts of 4 k-steps, fewer than a
+    load batch, whose guarded MFMAs must be skipped, not run lane-masked);
+    the same slots stepped in groups of at most 64 rows run the per-tile
+    GEMM.  The arithmetic is the same, so the logits are bitwise equal."""
     cfg = BF16_SMALL.with_(**shape)
     B, T = 100, 4
     rig = Rig(cfg, B, T, attn_chunk=4)
