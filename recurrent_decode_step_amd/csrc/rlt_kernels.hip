@@ -295,8 +295,9 @@ __device__ __forceinline__ void gemm_vwg(const GemmArgs &a, int L, bool valid, i
   // (the host narrows the groups to fill the CUs): those share weight tiles
   constexpr bool WSH = NCB == 1;
   const int ncols = min(COLS, a.n_rows - col0);
-  const int ks0 = (wave * a.KT) / NW;
-  const int nks = ((wave + 1) * a.KT) / NW - ks0;
+  const int KT = __builtin_amdgcn_readfirstlane(a.KT);   // scalar: the part bounds guard MFMAs
+  const int ks0 = (wave * KT) / NW;
+  const int nks = ((wave + 1) * KT) / NW - ks0;
 
   // Every load below is unconditional and in bounds: batch columns past the
   // last row read the last row's data (their outputs are never stored), so no
@@ -523,8 +524,9 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
   auto tile_of = [&](int i) { return x + 8 * (l + L8 * i); };
   const int col0 = cg * COLS;
   const int ncols = min(COLS, a.n_rows - col0);
-  const int ks0 = (wave * a.KT) / NW;
-  const int nks = ((wave + 1) * a.KT) / NW - ks0;
+  const int KT = __builtin_amdgcn_readfirstlane(a.KT);   // scalar: the part bounds guard MFMAs
+  const int ks0 = (wave * KT) / NW;
+  const int nks = ((wave + 1) * KT) / NW - ks0;
 
   int cbg[NCB], irow[NCB];
 #pragma unroll
