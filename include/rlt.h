@@ -211,30 +211,35 @@ rlt_status rlt_run_sequence(const rlt_model *m, rlt_state *st, int32_t T,
 /* rlt_run_sequence with each decoder step as one persistent launch: the
  * step's phases (gated merge; per layer QKV, window attention, O, Qc,
  * cross-attention, Oc, FFN-up, FFN-down; the head) run inside one cooperative
- * kernel, one workgroup per compute unit, separated by grid barriers, instead
- * of 2 + 8L separate launches -- the kernel fusion the pages list among the
- * implementation targets [Princeton, design-principles paragraph; Article,
- * "Principle 2: Co-Design Between Model and Hardware"].  Each phase runs the
- * launch chain's own per-workgroup code with the same K split and summation
- * order, so logits and state are bitwise those of rlt_run_sequence.
+ * kernel, one workgroup per compute unit, instead of 2 + 8L separate launches
+ * -- the kernel fusion the pages list among the implementation targets
+ * [Princeton, design-principles paragraph; Article, "Principle 2: Co-Design
+ * Between Model and Hardware"].  There is no grid barrier: each work item of a
+ * phase (a GEMM tile of 16 rows, or an attention row and head) waits only for
+ * the items of the phase before it that it reads, through per-item ready
+ * flags, and issues its weights (or memory keys and values) before it waits.
+ * Each item runs the launch chain's own per-workgroup code with the same K
+ * split and summation order, so logits and state are bitwise those of
+ * rlt_run_sequence.
  *   dev_workspace  caller-owned device buffer of
  *                  rlt_persistent_workspace_bytes(cfg, B) bytes (256-byte
- *                  aligned): barrier words, the phase tables, and one output
- *                  buffer per phase of a step (no address is written twice
- *                  within a launch).  It must not be shared by calls that
- *                  overlap.
+ *                  aligned): the error word, one flag per item of a step,
+ *                  the phase tables, and one output buffer per phase of a
+ *                  step (no address is written twice within a launch).  It
+ *                  must not be shared by calls that overlap.
  * Supported: bf16 with head_dim 32, 64, 128; fp32 with head_dim 16, 32, 64
- * (RLT_ERR_UNSUPPORTED otherwise).  Every barrier wait is bounded (0.2 s): on
- * timeout the kernel sets an error word and all workgroups leave; results are
- * then undefined and rlt_persistent_check reports RLT_ERR_DEVICE.  Other
- * errors as rlt_run_sequence, plus RLT_ERR_SHAPE for a short workspace. */
+ * (RLT_ERR_UNSUPPORTED otherwise).  Every wait is bounded (0.2 s): on timeout
+ * the kernel sets an error word and every later wait returns at once, so the
+ * launch ends; results are then undefined and rlt_persistent_check reports
+ * RLT_ERR_DEVICE.  Other errors as rlt_run_sequence, plus RLT_ERR_SHAPE for a
+ * short workspace. */
 size_t rlt_persistent_workspace_bytes(const rlt_config *cfg, int32_t batch);
 rlt_status rlt_run_sequence_persistent(const rlt_model *m, rlt_state *st, int32_t T,
                                        const void *dev_e, const rlt_memory *mem,
                                        float *dev_logits, int32_t logits_mode,
                                        void *dev_workspace, size_t workspace_bytes,
                                        void *stream);
-/* Synchronize the stream and report whether a barrier of the last
+/* Synchronize the stream and report whether a wait of the last
  * rlt_run_sequence_persistent call on this workspace timed out
  * (RLT_ERR_DEVICE) or not (RLT_OK).  The word is cleared by the next call. */
 rlt_status rlt_persistent_check(void *dev_workspace, void *stream);

@@ -322,7 +322,7 @@ def rlt_run_sequence_persistent(model: Model, state: State, e: torch.Tensor, mem
 
 
 def rlt_persistent_check(workspace: StepWorkspace, stream=None):
-    """Raises RLTError(RLT_ERR_DEVICE) if a barrier wait of the last persistent call timed out."""
+    """Raises RLTError(RLT_ERR_DEVICE) if a wait of the last persistent call timed out."""
     _check(load_library().rlt_persistent_check(workspace.buf.data_ptr(), _stream(stream)))
 
 

@@ -750,15 +750,17 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, const StepScratch &w,
 }
 
 // ------------------------------------------------------- persistent step
-// Workspace of rlt_run_sequence_persistent for n rows: barrier lines, the two
-// phase tables (a step without and with the head), and one output buffer per
-// producing phase, so no address is written twice within one launch.
-// Producer k of the residual stream is the merge (k = 0) and, in layer l, the
-// O, Oc and FFN-down products (k = 3l+1, 3l+2, 3l+3).
+// Workspace of rlt_run_sequence_persistent for n rows: the error word, one
+// flag per item of a step (with the head), the two phase tables (a step
+// without and with the head), and one output buffer per producing phase, so
+// no address is written twice within one launch.  Producer k of the residual
+// stream is the merge (k = 0) and, in layer l, the O, Oc and FFN-down
+// products (k = 3l+1, 3l+2, 3l+3).
 constexpr int kStepMaxGrid = 1024;
 
 struct StepBufs {
-  unsigned *flags, *rel, *err;
+  unsigned *err, *items;
+  size_t n_items;
   StepPhase *tab[2];
   std::vector<float *> x, sumsq;     // [3L+1]
   std::vector<char *> xg;            // [3L+1]
@@ -768,14 +770,25 @@ struct StepBufs {
 
 int step_phases_max(const rlt_config &c) { return 2 + 8 * c.n_layers; }
 
+// items of a step with the head: GEMM phases tiles x 16-row column groups,
+// attention phases rows x heads
+size_t step_items(const rlt_config &c, int n) {
+  const int d = c.d_model, L = c.n_layers;
+  const size_t cg = (size_t)cdiv(n, 16), nh = (size_t)n * c.n_heads;
+  auto tiles = [](int N) { return (size_t)cdiv(N, 32) * 2; };
+  return tiles(d) * cg +
+         (size_t)L * ((tiles(3 * d) + 4 * tiles(d) + tiles(c.d_ffn)) * cg + 2 * nh) +
+         tiles(c.vocab) * cg;
+}
+
 size_t step_layout(const rlt_config &c, int n, void *base, StepBufs *b) {
   const int L = c.n_layers, d = c.d_model, F = c.d_ffn;
   const int es = esize_of(c.dtype);
   const size_t rows16 = (size_t)cdiv(n, 16) * 16;
   Arena ar(base);
-  b->flags = ar.take<unsigned>((size_t)kStepMaxGrid * kStepFlagWords * 4);
-  b->rel = ar.take<unsigned>(256);
   b->err = ar.take<unsigned>(256);
+  b->n_items = step_items(c, n);
+  b->items = ar.take<unsigned>(b->n_items * 4);
   for (int t = 0; t < 2; ++t) b->tab[t] = ar.take<StepPhase>((size_t)step_phases_max(c) * sizeof(StepPhase));
   b->x.resize(3 * L + 1);
   b->sumsq.resize(3 * L + 1);
@@ -801,6 +814,10 @@ size_t step_layout(const rlt_config &c, int n, void *base, StepBufs *b) {
 // uses 16-row tiles and 16-row column groups (a placement choice, invisible
 // in the results).  with_head: the head phase is the last and advances the
 // positions, otherwise the last FFN-down does.
+int fl_count_check(const std::vector<StepPhase> &tab) {
+  return tab.empty() ? 0 : tab.back().fl + tab.back().nv;
+}
+
 void build_step_phases(const rlt_model *m, rlt_state *st, const rlt_memory *mem,
                        const StepBufs &b, bool with_head, std::vector<StepPhase> &out) {
   const rlt_config &c = m->cfg;
@@ -975,6 +992,38 @@ void build_step_phases(const rlt_model *m, rlt_state *st, const rlt_memory *mem,
     a.sumsq = b.sumsq[3 * L];
     a.advance_pos = 1;
     gemm(m->p_head, m->wout, ACT_PLAIN, EPI_LOGITS, a);
+  }
+
+  // item flags and what each phase waits for: every phase reads the phase
+  // before it.  GEMM after GEMM: every tile of the column group (the
+  // normalised input needs the whole row); GEMM after attention: every head
+  // of the column group's rows; attention after QKV or Qc: the tiles of its
+  // head (q, k, v or q_c) of its row's column group.
+  int fl = 0;
+  for (size_t p = 0; p < out.size(); ++p) {
+    StepPhase &ph = out[p];
+    ph.n_rows = n;
+    ph.fl = fl;
+    fl += ph.nv;
+    if (p == 0) {
+      ph.dep_kind = DEP_NONE;
+      continue;
+    }
+    const StepPhase &pr = out[p - 1];
+    ph.dep = pr.fl;
+    if (ph.kind == STEP_GEMM && pr.kind == STEP_GEMM) {
+      ph.dep_kind = DEP_GEMM_CG;
+      ph.dep_n = pr.g.tile_groups;
+    } else if (ph.kind == STEP_GEMM) {
+      ph.dep_kind = DEP_ATTN_ROWS;
+      ph.dep_H = H;
+    } else {
+      ph.dep_kind = DEP_HEAD_TILES;
+      ph.dep_n = pr.g.tile_groups;
+      ph.dep_r = pr.epi == EPI_QKV ? 3 : 1;
+      ph.dep_rs = d / 16;
+      ph.dep_ht = dh / 16;
+    }
   }
 }
 
@@ -1299,8 +1348,6 @@ rlt_status rlt_run_sequence_persistent(const rlt_model *m, rlt_state *st, int32_
   if (grid < 8 || grid > kStepMaxGrid)
     return fail(RLT_ERR_UNSUPPORTED, "no persistent step for this dtype and head_dim %d",
                 c.head_dim);
-  const uint64_t epochs = (uint64_t)T * (uint64_t)step_phases_max(c);
-  if (epochs >= (1ull << 31)) return fail(RLT_ERR_RANGE, "T too large for one call");
   if ((rs = check_memory(m, mem, st->B - 1)) != RLT_OK) return rs;
   if ((rs = check_positions(st, mem, st->B, nullptr, T)) != RLT_OK) return rs;
   if ((rs = device_health()) != RLT_OK) return rs;
@@ -1314,9 +1361,12 @@ rlt_status rlt_run_sequence_persistent(const rlt_model *m, rlt_state *st, int32_
                                   hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "phase table upload");
   }
-  // barrier lines, release and error words start at zero in every call
-  hipError_t e = launch_zero(b.flags, (size_t)((char *)b.tab[0] - (char *)b.flags), s);
-  if (e != hipSuccess) return hip_fail(e, "barrier reset");
+  // the error word and the item flags start at zero in every call; step k
+  // of the call stores epoch k + 1
+  if ((size_t)fl_count_check(st->step_tab[1]) != b.n_items)
+    return fail(RLT_ERR_DEVICE, "item count mismatch in the persistent step tables");
+  hipError_t e = launch_zero(b.err, (size_t)((char *)b.tab[0] - (char *)b.err), s);
+  if (e != hipSuccess) return hip_fail(e, "item flag reset");
   const int d = c.d_model, V = c.vocab, es = m->esize;
   for (int k = 0; k < T; ++k) {
     StepRun r;
@@ -1333,10 +1383,9 @@ rlt_status rlt_run_sequence_persistent(const rlt_model *m, rlt_state *st, int32_
     const int t = r.logits ? 1 : 0;
     r.ph = b.tab[t];
     r.n_phases = (int)st->step_tab[t].size();
-    r.flags = b.flags;
-    r.rel = b.rel;
+    r.items = b.items;
     r.err = b.err;
-    r.epoch0 = (unsigned)((uint64_t)k * step_phases_max(c));
+    r.epoch = (unsigned)k + 1u;
     e = launch_step(c.dtype, c.head_dim, r, grid, s);
     if (e != hipSuccess) return hip_fail(e, "persistent step launch");
   }
@@ -1349,13 +1398,12 @@ rlt_status rlt_persistent_check(void *dev_workspace, void *stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "stream synchronize");
-  // the error word follows the barrier lines and the release word
-  const char *p = static_cast<const char *>(dev_workspace) +
-                  align256((size_t)kStepMaxGrid * kStepFlagWords * 4) + 256;
+  // the error word opens the workspace
+  const char *p = static_cast<const char *>(dev_workspace);
   unsigned err = 0;
   e = hipMemcpy(&err, p, 4, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "reading the error word");
-  if (err) return fail(RLT_ERR_DEVICE, "a grid barrier of the persistent step timed out");
+  if (err) return fail(RLT_ERR_DEVICE, "a wait of the persistent step timed out");
   return ok();
 }
 

@@ -168,13 +168,27 @@ hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStre
 // its outputs go to buffers no other phase of the launch writes, with
 // write-through stores, so a reader on another XCD never holds a stale line.
 enum StepKind { STEP_GEMM = 0, STEP_ATTN = 1 };
+// What the items of a phase wait for, among the items of the phase before it
+// (every phase reads the outputs of the one before it; older inputs are
+// reached through that chain).  A GEMM item is (tile tg, 16-row column group
+// cg), flag index cg * tiles + tg; an attention item is (row i, head h), flag
+// index i * H + h.
+enum StepDep {
+  DEP_NONE = 0,        // first phase of the step
+  DEP_GEMM_CG = 1,     // GEMM item: every tile of its column group (dep_n tiles)
+  DEP_ATTN_ROWS = 2,   // GEMM item: every head of the rows of its column group
+  DEP_HEAD_TILES = 3,  // attention item: the dep_ht tiles of its head in each of dep_r
+                       // ranges dep_rs tiles apart (q; or q, k, v), of its row's column group
+};
 struct StepPhase {
   int kind;            // StepKind
   int act, epi;        // GEMM: activation source and epilogue
-  int nv;              // GEMM: workgroups of the launch chain's grid (NCB = TPW = 1);
-                       // ATTN: rows x heads
+  int nv;              // items: GEMM (tiles x column groups, NCB = TPW = 1); ATTN rows x heads
   int parts;           // GEMM: wavefronts per workgroup (K parts: 1, 2, 4 or 8)
-  int n_rows;          // ATTN: rows
+  int n_rows;          // rows of the step
+  int fl;              // flag index of this phase's first item
+  int dep, dep_kind;   // flag index of the first item waited for, StepDep
+  int dep_n, dep_r, dep_rs, dep_ht, dep_H;
   GemmArgs g;
   AttnArgs at;
 };
@@ -182,13 +196,11 @@ struct StepRun {
   const StepPhase *ph; int n_phases;
   const void *e; int64_t ld_e;          // this step's merge input (e rows)
   float *logits; int64_t ld_logits;     // this step's head output (null: no head phase)
-  unsigned *flags;                      // [grid][64] arrival epochs, one line per workgroup
-  unsigned *rel;                        // release epoch
-  unsigned *err;                        // nonzero: a barrier wait timed out
-  unsigned epoch0;                      // barrier epochs of this launch: epoch0 + 1, ...
+  unsigned *items;                      // item flags: the epoch of the step that completed it
+  unsigned *err;                        // nonzero: a wait timed out
+  unsigned epoch;                       // this step's epoch (1, 2, ... within a call)
 };
 constexpr int kStepThreads = 512;
-constexpr int kStepFlagWords = 64;      // one 256-byte line per workgroup
 // workgroups of the cooperative launch (one per CU) or 0 when unsupported
 int step_grid(int dtype, int dh);
 hipError_t launch_step(int dtype, int dh, const StepRun &r, int grid, hipStream_t s);

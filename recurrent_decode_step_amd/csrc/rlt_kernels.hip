@@ -243,16 +243,83 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x4 yv, int t
   }
 }
 
+// ------------------------------------------------------- item dataflow
+// Waits of the persistent step kernel.  Every wait is bounded in real time:
+// past the bound it sets the error word and returns, and a wait that sees
+// the error word set returns at once, so a launch always ends.
+constexpr uint64_t kStepWaitTicks = 20000000;   // 0.2 s; s_memrealtime runs at 100 MHz
+
+__device__ __forceinline__ unsigned step_ld(const unsigned *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void step_st(unsigned *p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The launch chain's kernels: nothing to wait for (the kernel boundary
+// orders the phases).
+struct NoSync {
+  static constexpr bool active = false;
+  __device__ void gemm(int, int) const {}
+  __device__ void attn(int, int) const {}
+};
+
+// The persistent step: an item waits until every item of the phase before
+// it that it reads from has stored its epoch in the item flags.  Each
+// wavefront polls for itself (no workgroup barrier inside a wait); a flag is
+// stored only after its item's outputs are complete in memory (write-through
+// stores, waited for), and the outputs of a phase go to addresses nothing
+// read earlier in the launch, so the loads that follow see them.
+struct StepSync {
+  static constexpr bool active = true;
+  const unsigned *items;
+  unsigned *err;
+  unsigned epoch;
+  int dep, kind, n, r, rs, ht, H, n_rows;
+
+  // flags [first + q * rstride, + count) for q < ranges, all >= epoch
+  __device__ void wait_ranges(int first, int count, int ranges, int rstride) const {
+    const int lane = threadIdx.x & 63;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+      bool ok = true;
+      for (int q = 0; q < ranges; ++q)
+        for (int k = lane; k < count; k += 64) ok &= step_ld(items + first + q * rstride + k) >= epoch;
+      if (__all(ok)) return;
+      if (step_ld(err) != 0u) return;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kStepWaitTicks) {
+        step_st(err, 1u);
+        return;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  // GEMM item (tile group tg, 16-row column group cg)
+  __device__ void gemm(int tg, int cg) const {
+    (void)tg;
+    if (kind == DEP_GEMM_CG) {
+      wait_ranges(dep + cg * n, n, 1, 0);
+    } else if (kind == DEP_ATTN_ROWS) {
+      const int r0 = cg * 16, r1 = min(r0 + 16, n_rows);
+      wait_ranges(dep + r0 * H, (r1 - r0) * H, 1, 0);
+    }
+  }
+  // attention item (row i, head h)
+  __device__ void attn(int i, int h) const {
+    if (kind == DEP_HEAD_TILES) wait_ranges(dep + (i / 16) * n + h * ht, ht, r, rs);
+  }
+};
+
 // One workgroup's work of the GEMM (workgroup index L of the launch's grid),
 // run by a group of NW wavefronts (the K parts): `wave` and `tid` are indices
 // within the group, s_acc ([NW][TPW][NCB][64]), s_grp and s_rinv the group's
 // LDS.  k_gemm runs it as the whole workgroup; the persistent step kernel runs
 // several groups side by side.  Every group of a workgroup passes the same
 // workgroup barriers: a group with no work (valid = false) passes them too.
-template <typename T, int NCB, int ACT, int EPI, int KSW, int TPW, bool WT>
-__device__ __forceinline__ void gemm_vwg(const GemmArgs &a, int L, bool valid, int NW, int wave,
-                                         int tid, f32x4 *s_acc, float (*s_grp)[NCB * 16],
-                                         float *s_rinv) {
+template <typename T, int NCB, int ACT, int EPI, int KSW, int TPW, bool WT, class SY = NoSync>
+__device__ __forceinline__ int gemm_vwg(const GemmArgs &a, int L, bool valid, int NW, int wave,
+                                        int tid, f32x4 *s_acc, float (*s_grp)[NCB * 16],
+                                        float *s_rinv, const SY &sy = SY()) {
   constexpr int COLS = NCB * 16;
   constexpr int WB = KSW;                          // k-steps per batch of weight loads
   constexpr int AB = GemmRegs<KSW, TPW, NCB>::AB;  // activation k-steps in registers
@@ -268,7 +335,7 @@ __device__ __forceinline__ void gemm_vwg(const GemmArgs &a, int L, bool valid, i
   if (!__builtin_amdgcn_readfirstlane((int)valid)) {
     if constexpr (SCALED) __syncthreads();
     __syncthreads();
-    return;
+    return -1;
   }
   const int lane = tid & 63;
   const int NT = NW * 64;                          // threads of the group
@@ -327,7 +394,26 @@ __device__ __forceinline__ void gemm_vwg(const GemmArgs &a, int L, bool valid, i
 #pragma unroll
       for (int t = 0; t < TPW; ++t) wf[t][j] = wload_frag<WSH>(wp[t] + (size_t)(b0 + j) * 64);
   };
-  if (nks >= WB) issue_full(0);                    // first batch before anything else
+  if constexpr (SY::active) {
+    // the weights do not depend on the step: in flight before the wait for
+    // the producers of the activation
+    if (nks >= WB) {
+#pragma unroll
+      for (int j = 0; j < WB; ++j)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) wf[t][j] = wload_frag<WSH>(wp[t] + (size_t)j * 64);
+    }
+    sy.gemm(tg, cg);
+    if (nks >= WB) {
+#pragma unroll
+      for (int p = 0; p < AB; ++p)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          ab[p][cb] = load_b<T, ACT>(a, cbg[cb], irow[cb], slot[cb], ks0 + p, lane);
+    }
+  } else {
+    if (nks >= WB) issue_full(0);                  // first batch before anything else
+  }
 
   // residual epilogue operands of this wavefront's first (tile, column block),
   // loaded now so they are not waited for after the reduction
@@ -473,10 +559,20 @@ __device__ __forceinline__ void gemm_vwg(const GemmArgs &a, int L, bool valid, i
                               q == wave, x_pre, g_pre, lane);
   }
 
-  // the last kernel of a step advances the positions (no reader of pos runs in it)
-  if (a.advance_pos && tg == 0 && cg == 0) {
-    for (int i = tid; i < a.n_rows; i += NT) a.pos[slot_of(a, i)] += 1;
+  if constexpr (SY::active) {
+    // the last phase of a step advances the positions of its column group's
+    // rows: every reader of them (QKV and attention items of these rows) is a
+    // predecessor of this item
+    if (a.advance_pos && tg == 0) {
+      for (int i = col0 + tid; i < col0 + ncols; i += NT) a.pos[slot_of(a, i)] += 1;
+    }
+  } else {
+    // the last kernel of a step advances the positions (no reader of pos runs in it)
+    if (a.advance_pos && tg == 0 && cg == 0) {
+      for (int i = tid; i < a.n_rows; i += NT) a.pos[slot_of(a, i)] += 1;
+    }
   }
+  return cg * a.tile_groups + tg;
 }
 
 template <typename T, int NCB, int ACT, int EPI, int KSW, int TPW>
@@ -812,9 +908,10 @@ __device__ __forceinline__ void attn_chunk(const float *qf, const u32x4 *kr, con
 // runs it as the whole workgroup; the persistent step kernel runs two groups
 // side by side.  A group with no work (valid = false) passes the workgroup
 // barrier too.
-template <typename T, int DH, int UU, bool WT>
+template <typename T, int DH, int UU, bool WT, class SY = NoSync>
 __device__ __forceinline__ void attn_item(const AttnArgs &a, int i, int h, bool valid, int tid,
-                                          float (*s_o)[DH], float (*s_ml)[2]) {
+                                          float (*s_o)[DH], float (*s_ml)[2],
+                                          const SY &sy = SY(), bool pre = true) {
   using S = AttnShape<T, DH, UU>;
   constexpr int EPL = S::EPL, LPR = S::LPR, RPW = S::RPW, U = S::U;
   i = __builtin_amdgcn_readfirstlane(i);        // the same on every lane (see gemm_vwg)
@@ -840,7 +937,17 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int i, int h, bool 
   for (int u = 0; u < U; ++u) {
     ka[u] = u32x4{0u, 0u, 0u, 0u}; va[u] = ka[u]; kb2[u] = ka[u]; vb2[u] = ka[u];
   }
-  attn_load<T, DH, UU, false>(kp, vp, a.s_pos, 0, len, ch, my, ka, va);   // first chunk in flight first
+  if constexpr (SY::active) {
+    // keys and values the step does not write (the memory) are in flight
+    // before the wait for q; the window's newest entry is written by the
+    // step, so its first chunk is loaded after the wait
+    pre = __builtin_amdgcn_readfirstlane((int)pre) != 0;
+    if (pre) attn_load<T, DH, UU, false>(kp, vp, a.s_pos, 0, len, ch, my, ka, va);
+    sy.attn(i, h);
+    if (!pre) attn_load<T, DH, UU, false>(kp, vp, a.s_pos, 0, len, ch, my, ka, va);
+  } else {
+    attn_load<T, DH, UU, false>(kp, vp, a.s_pos, 0, len, ch, my, ka, va);   // first chunk in flight first
+  }
 
   float qf[EPL];
   Num<T>::unpack(*reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.q) + (size_t)i * a.d +
@@ -1432,62 +1539,31 @@ hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStre
 }
 
 // ---------------------------------------------------------- persistent step
-// Grid barrier of the persistent step: every workgroup publishes the epoch in
-// its own line once its stores are complete; workgroup 0 gathers the lines and
-// publishes the epoch in the release word, which the others wait for.  All
-// flag traffic is agent-scope (sc1), bypassing the non-coherent L2s.  Every
-// wait is bounded by the real-time clock (0.2 s): on timeout the kernel sets
-// the error word and every workgroup leaves (a later wait also times out or
-// sees the error word), so the launch always ends.
-constexpr uint64_t kStepWaitTicks = 20000000;   // s_memrealtime runs at 100 MHz
+// One decoder step as one cooperative launch: every workgroup walks the
+// step's phases in order, running its share of each phase's items, and an
+// item starts once the items of the phase before it that it reads from have
+// stored this step's epoch in their flags (StepSync).  There is no grid
+// barrier: workgroups drift apart by as much as the data allows.  Every item
+// of a phase waits only on items of the phase before it, and every workgroup
+// finishes a phase without waiting on a later one, so all items complete.
 
-__device__ __forceinline__ unsigned step_ld(const unsigned *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void step_st(unsigned *p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// wait until *p >= target (wrap-free: epochs grow within one call) or timeout
-__device__ __forceinline__ bool step_wait(const unsigned *p, unsigned target, unsigned *err) {
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (step_ld(p) < target) {
-    if (step_ld(err) != 0u) return false;
-    if (__builtin_amdgcn_s_memrealtime() - t0 > kStepWaitTicks) {
-      step_st(err, 1u);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  return true;
-}
-
-__device__ __forceinline__ bool step_barrier(const StepRun &r, unsigned epoch, int *s_bad) {
+// The item flag of this round's item, once every wavefront's stores of it
+// are complete.  The workgroup barrier also ends the round's use of the LDS.
+__device__ __forceinline__ void step_item_done(const StepRun &r, int flag, bool mine) {
   __builtin_amdgcn_s_waitcnt(0);                 // this thread's stores are complete
   __syncthreads();
-  if (threadIdx.x == 0) {
-    *s_bad = 0;
-    step_st(r.flags + (size_t)kStepFlagWords * blockIdx.x, epoch);
-  }
-  __syncthreads();
-  if (blockIdx.x == 0) {
-    for (unsigned w = threadIdx.x; w < gridDim.x; w += blockDim.x)
-      if (!step_wait(r.flags + (size_t)kStepFlagWords * w, epoch, r.err)) *s_bad = 1;
-    __syncthreads();
-    if (threadIdx.x == 0 && !*s_bad) step_st(r.rel, epoch);
-  } else if (threadIdx.x == 0) {
-    if (!step_wait(r.rel, epoch, r.err)) *s_bad = 1;
-  }
-  __syncthreads();
-  return *s_bad == 0;
+  if (mine && flag >= 0) step_st(r.items + flag, r.epoch);
 }
 
-// One GEMM phase: the launch chain's workgroups v = 0..nv-1, spread over the
-// grid; a workgroup of 8 wavefronts runs 8 / parts of them side by side.
-// Workgroup v runs on a workgroup with the same index mod 8, so the XCD-aware
-// placement of the launch chain holds.
+// One GEMM phase: the launch chain's workgroups v = 0..nv-1 (the items),
+// spread over the grid; a workgroup of 8 wavefronts runs 8 / parts of them
+// side by side.  Workgroup v runs on a workgroup with the same index mod 8,
+// so the XCD-aware placement of the launch chain holds.
 template <typename T, int ACT, int EPI, int KSW>
-__device__ __forceinline__ void step_gemm(const GemmArgs &ga, int nv, int P, f32x4 *s_acc,
+__device__ __forceinline__ void step_gemm(const GemmArgs &ga, const StepPhase &d, const StepRun &r,
+                                          const StepSync &sy, f32x4 *s_acc,
                                           float (*s_grp)[8][16], float (*s_rinv)[16]) {
+  const int nv = d.nv, P = d.parts;
   const int wave = threadIdx.x >> 6;
   const int groups = 8 / P, grp = wave / P, gw = wave - grp * P;
   const int gtid = threadIdx.x - grp * P * 64;
@@ -1495,9 +1571,9 @@ __device__ __forceinline__ void step_gemm(const GemmArgs &ga, int nv, int P, f32
   const int rounds = (nv + per_round - 1) / per_round;
   for (int rd = 0; rd < rounds; ++rd) {
     const int v = (int)blockIdx.x + (int)gridDim.x * (grp + groups * rd);
-    gemm_vwg<T, 1, ACT, EPI, KSW, 1, true>(ga, v, v < nv, P, gw, gtid, s_acc + grp * P * 64,
-                                           s_grp[grp], s_rinv[grp]);
-    if (rd + 1 < rounds) __syncthreads();        // LDS of this round read before the next fills it
+    const int item = gemm_vwg<T, 1, ACT, EPI, KSW, 1, true, StepSync>(
+        ga, v, v < nv, P, gw, gtid, s_acc + grp * P * 64, s_grp[grp], s_rinv[grp], sy);
+    step_item_done(r, item < 0 ? -1 : d.fl + item, gtid == 0);
   }
 }
 
@@ -1505,25 +1581,25 @@ __device__ __forceinline__ void step_gemm(const GemmArgs &ga, int nv, int P, f32
 // and head phases take this step's e rows and logits from the launch.
 template <typename T, int KSW>
 __device__ __forceinline__ void step_gemm_epi(const StepPhase &d, const StepRun &r,
-                                              f32x4 *s_acc, float (*s_grp)[8][16],
-                                              float (*s_rinv)[16]) {
+                                              const StepSync &sy, f32x4 *s_acc,
+                                              float (*s_grp)[8][16], float (*s_rinv)[16]) {
   switch (d.epi) {
-    case EPI_QKV: step_gemm<T, ACT_PLAIN, EPI_QKV, KSW>(d.g, d.nv, d.parts, s_acc, s_grp, s_rinv); break;
-    case EPI_STORE: step_gemm<T, ACT_PLAIN, EPI_STORE, KSW>(d.g, d.nv, d.parts, s_acc, s_grp, s_rinv); break;
-    case EPI_RESID: step_gemm<T, ACT_PLAIN, EPI_RESID, KSW>(d.g, d.nv, d.parts, s_acc, s_grp, s_rinv); break;
-    case EPI_GELU: step_gemm<T, ACT_PLAIN, EPI_GELU, KSW>(d.g, d.nv, d.parts, s_acc, s_grp, s_rinv); break;
+    case EPI_QKV: step_gemm<T, ACT_PLAIN, EPI_QKV, KSW>(d.g, d, r, sy, s_acc, s_grp, s_rinv); break;
+    case EPI_STORE: step_gemm<T, ACT_PLAIN, EPI_STORE, KSW>(d.g, d, r, sy, s_acc, s_grp, s_rinv); break;
+    case EPI_RESID: step_gemm<T, ACT_PLAIN, EPI_RESID, KSW>(d.g, d, r, sy, s_acc, s_grp, s_rinv); break;
+    case EPI_GELU: step_gemm<T, ACT_PLAIN, EPI_GELU, KSW>(d.g, d, r, sy, s_acc, s_grp, s_rinv); break;
     case EPI_MERGE: {
       GemmArgs ga = d.g;
       ga.act = r.e;
       ga.ld_act = r.ld_e;
-      step_gemm<T, ACT_MERGE, EPI_MERGE, KSW>(ga, d.nv, d.parts, s_acc, s_grp, s_rinv);
+      step_gemm<T, ACT_MERGE, EPI_MERGE, KSW>(ga, d, r, sy, s_acc, s_grp, s_rinv);
       break;
     }
     case EPI_LOGITS: {
       GemmArgs ga = d.g;
       ga.out = r.logits;
       ga.ld_out = r.ld_logits;
-      step_gemm<T, ACT_PLAIN, EPI_LOGITS, KSW>(ga, d.nv, d.parts, s_acc, s_grp, s_rinv);
+      step_gemm<T, ACT_PLAIN, EPI_LOGITS, KSW>(ga, d, r, sy, s_acc, s_grp, s_rinv);
       break;
     }
   }
@@ -1542,24 +1618,36 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepRun r) {
   if (s_bad) return;                             // an earlier launch timed out
   for (int p = 0; p < r.n_phases; ++p) {
     const StepPhase &d = r.ph[p];
+    StepSync sy;
+    sy.items = r.items;
+    sy.err = r.err;
+    sy.epoch = r.epoch;
+    sy.dep = d.dep;
+    sy.kind = d.dep_kind;
+    sy.n = d.dep_n;
+    sy.r = d.dep_r;
+    sy.rs = d.dep_rs;
+    sy.ht = d.dep_ht;
+    sy.H = d.dep_H;
+    sy.n_rows = d.n_rows;
     if (d.kind == STEP_GEMM) {
       // batches of 8 k-steps: the load batch size changes no result
-      step_gemm_epi<T, 8>(d, r, s_acc, s_grp, s_rinv);
+      step_gemm_epi<T, 8>(d, r, sy, s_acc, s_grp, s_rinv);
     } else {
       // attention items (row, head), two groups of 4 wavefronts per workgroup
       const int grp = threadIdx.x >> 8, gtid = threadIdx.x & 255;
       const int H = d.at.H;
+      const bool pre = d.at.len_cap == 0x7fffffff;   // the memory: not written by the step
       const int per_round = (int)gridDim.x * 2;
       const int rounds = (d.nv + per_round - 1) / per_round;
       for (int rd = 0; rd < rounds; ++rd) {
         const int v = (int)blockIdx.x + (int)gridDim.x * (grp + 2 * rd);
         const bool valid = v < d.nv;
-        attn_item<T, DH, 0, true>(d.at, valid ? v / H : 0, valid ? v % H : 0, valid, gtid,
-                                  s_o[grp], s_ml[grp]);
-        if (rd + 1 < rounds) __syncthreads();    // LDS of this item read before the next fills it
+        attn_item<T, DH, 0, true, StepSync>(d.at, valid ? v / H : 0, valid ? v % H : 0, valid,
+                                            gtid, s_o[grp], s_ml[grp], sy, pre);
+        step_item_done(r, valid ? d.fl + v : -1, gtid == 0);
       }
     }
-    if (p + 1 < r.n_phases && !step_barrier(r, r.epoch0 + (unsigned)p + 1, &s_bad)) return;
   }
 }
 

@@ -1,5 +1,6 @@
-"""The persistent step (one cooperative launch per decoder step, phases
-separated by grid barriers) against the launch chain, through the C ABI
+"""The persistent step (one cooperative launch per decoder step, each work
+item waiting on the ready flags of the items it reads) against the launch
+chain, through the C ABI
 (needs an MI355X).  Both run the same per-workgroup code with the same K
 split and summation order, so logits and the exported states must be equal
 bit for bit."""
