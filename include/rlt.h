@@ -243,6 +243,13 @@ rlt_status rlt_run_sequence_persistent(const rlt_model *m, rlt_state *st, int32_
  * rlt_run_sequence_persistent call on this workspace timed out
  * (RLT_ERR_DEVICE) or not (RLT_OK).  The word is cleared by the next call. */
 rlt_status rlt_persistent_check(void *dev_workspace, void *stream);
+/* For tests of the time-out path only: while on (nonzero, process-wide),
+ * the waits of later rlt_run_sequence_persistent calls look for an epoch
+ * that no item stores, so each such call's first wait times out after its
+ * bound (0.2 s), sets the error word, and the call's launches end at once;
+ * rlt_persistent_check then reports RLT_ERR_DEVICE and the state's contents
+ * and positions are undefined until it is reset. */
+void rlt_persistent_test_stall(int32_t on);
 
 /* Replay scoring [Tutorial, "Current-Policy Reinforcement Learning Replay":
  * rebuild the states from the sequence start under the current weights,

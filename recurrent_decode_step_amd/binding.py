@@ -28,7 +28,7 @@ EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_by
             "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",
             "rlt_state_destroy", "rlt_state_reset", "rlt_decoder_step", "rlt_decoder_step_noalloc",
             "rlt_run_sequence", "rlt_persistent_workspace_bytes", "rlt_run_sequence_persistent",
-            "rlt_persistent_check",
+            "rlt_persistent_check", "rlt_persistent_test_stall",
             "rlt_score_sequence", "rlt_generate",
             "rlt_state_position", "rlt_snapshot_bytes", "rlt_state_export", "rlt_state_import",
             "rlt_profile_begin", "rlt_profile_collect",
@@ -110,6 +110,7 @@ def load_library(path: str = LIB_PATH):
         "rlt_persistent_workspace_bytes": (sz, [P(rlt_config), i32]),
         "rlt_run_sequence_persistent": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, i32, vp, sz, vp]),
         "rlt_persistent_check": (i32, [vp, vp]),
+        "rlt_persistent_test_stall": (None, [i32]),
         "rlt_score_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, vp, vp]),
         "rlt_generate": (i32, [vp, vp, i32, vp, P(rlt_encoder_table), P(rlt_memory), P(rlt_sampling),
                                vp, vp, vp, vp, vp]),
@@ -324,6 +325,12 @@ def rlt_run_sequence_persistent(model: Model, state: State, e: torch.Tensor, mem
 def rlt_persistent_check(workspace: StepWorkspace, stream=None):
     """Raises RLTError(RLT_ERR_DEVICE) if a wait of the last persistent call timed out."""
     _check(load_library().rlt_persistent_check(workspace.buf.data_ptr(), _stream(stream)))
+
+
+def rlt_persistent_test_stall(on: bool):
+    """Tests of the time-out path only: while on, every wait of later
+    persistent calls looks for an epoch no item stores (see include/rlt.h)."""
+    load_library().rlt_persistent_test_stall(1 if on else 0)
 
 
 def rlt_score_sequence(model: Model, state: State, e: torch.Tensor, memory, tokens: torch.Tensor,

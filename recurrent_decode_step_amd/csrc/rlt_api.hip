@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <mutex>
 #include <string>
@@ -814,6 +815,9 @@ size_t step_layout(const rlt_config &c, int n, void *base, StepBufs *b) {
 // uses 16-row tiles and 16-row column groups (a placement choice, invisible
 // in the results).  with_head: the head phase is the last and advances the
 // positions, otherwise the last FFN-down does.
+// rlt_persistent_test_stall: waits look for an epoch no item stores
+std::atomic<int> g_test_stall{0};
+
 int fl_count_check(const std::vector<StepPhase> &tab) {
   return tab.empty() ? 0 : tab.back().fl + tab.back().nv;
 }
@@ -1386,12 +1390,15 @@ rlt_status rlt_run_sequence_persistent(const rlt_model *m, rlt_state *st, int32_
     r.items = b.items;
     r.err = b.err;
     r.epoch = (unsigned)k + 1u;
+    r.wait_epoch = r.epoch + (g_test_stall.load() ? 1u : 0u);
     e = launch_step(c.dtype, c.head_dim, r, grid, s);
     if (e != hipSuccess) return hip_fail(e, "persistent step launch");
   }
   for (int i = 0; i < st->B; ++i) st->host_pos[i] += T;
   return ok();
 }
+
+void rlt_persistent_test_stall(int32_t on) { g_test_stall.store(on ? 1 : 0); }
 
 rlt_status rlt_persistent_check(void *dev_workspace, void *stream) {
   if (!dev_workspace) return fail(RLT_ERR_INVALID_ARG, "workspace is NULL");

@@ -199,6 +199,8 @@ struct StepRun {
   unsigned *items;                      // item flags: the epoch of the step that completed it
   unsigned *err;                        // nonzero: a wait timed out
   unsigned epoch;                       // this step's epoch (1, 2, ... within a call)
+  unsigned wait_epoch;                  // the epoch the waits look for (== epoch, except
+                                        // under rlt_persistent_test_stall)
 };
 constexpr int kStepThreads = 512;
 // workgroups of the cooperative launch (one per CU) or 0 when unsupported

@@ -1621,7 +1621,7 @@ __global__ __launch_bounds__(kStepThreads) void k_step(const StepRun r) {
     StepSync sy;
     sy.items = r.items;
     sy.err = r.err;
-    sy.epoch = r.epoch;
+    sy.epoch = r.wait_epoch;
     sy.dep = d.dep;
     sy.kind = d.dep_kind;
     sy.n = d.dep_n;

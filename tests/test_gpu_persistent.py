@@ -127,3 +127,43 @@ def test_persistent_step_rejects_a_short_workspace():
         binding.rlt_run_sequence_persistent(model, st, e.to(DEV), (mk.to(DEV), mv.to(DEV)), short)
     assert ei.value.status == binding.RLT_ERR_SHAPE
     assert st.position(0) == 0
+
+
+def test_persistent_step_wait_time_out_is_reported_and_cleared():
+    """A wait that can never be satisfied, forced from the host (the waits look
+    for an epoch no item stores), times out after its 0.2 s bound: the call's
+    launches end, rlt_persistent_check reports RLT_ERR_DEVICE, and after a
+    reset the next call on the same workspace runs normally, bitwise equal to
+    the launch chain."""
+    import time
+    cfg = tiny_cfg()
+    B, T = 4, 6
+    e, mk, mv = inputs(cfg, B, T)
+    e, mem = e.to(DEV), (mk.to(DEV), mv.to(DEV))
+    params = {k: v.to(DEV) for k, v in synth.model_params(cfg, device="cpu").items()}
+    model = binding.Model(cfg, params, version=1)
+    st = binding.State(model, B, T)
+    ws = binding.StepWorkspace(model, B)
+    say("[persistent] forced time-out")
+    binding.rlt_persistent_test_stall(True)
+    try:
+        t0 = time.time()
+        binding.rlt_run_sequence_persistent(model, st, e, mem, ws)
+        with pytest.raises(binding.RLTError) as ei:
+            binding.rlt_persistent_check(ws)
+        elapsed = time.time() - t0
+    finally:
+        binding.rlt_persistent_test_stall(False)
+    assert ei.value.status == binding.RLT_ERR_DEVICE
+    say(f"  reported after {elapsed:.2f} s")
+    assert elapsed < 5.0                   # one bounded wait, then every later one returns at once
+    binding.rlt_state_reset(model, st, list(range(B)))
+    sa = binding.State(model, B, T)
+    la = binding.rlt_run_sequence(model, sa, e, mem)
+    lb = binding.rlt_run_sequence_persistent(model, st, e, mem, ws)
+    binding.rlt_persistent_check(ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(la).all()
+    assert torch.equal(la, lb)
+    for b in range(B):
+        assert st.position(b) == T
