@@ -38,6 +38,9 @@ Other measurements (each prints its own JSON line; not the default):
   --counters-sample       reference-depth model, all sequences at the run's
                           mean sampled position: a few steps for hardware
                           counter passes (with --calibrate-copy)
+  --peaks                 the device's achievable HBM read/copy and bf16 MFMA
+                          rates (also added to the reference-depth line as
+                          "achievable", measured after the timed region)
 """
 from __future__ import annotations
 
@@ -201,6 +204,42 @@ def cpu_baseline(cfg, params_gpu, e_gpu, mk_gpu, mv_gpu, t0, budget_s=15.0, max_
                       f"{prep:.1f} s state and input preparation untimed)"}
 
 
+def measure_peaks(dev):
+    """Achievable rates of this device, measured with the library's peak
+    kernels outside any timed region: a streaming read and a copy of 1 GiB
+    (16-byte non-temporal accesses, one contiguous 64 KiB span per workgroup)
+    and dense bf16 MFMA loops of both instruction shapes; the fastest of 5
+    launches each (events bound to the dispatch)."""
+    import torch
+    from recurrent_decode_step_amd import binding
+    n = 1 << 30
+    src = torch.zeros(n // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    read = binding.peak_bandwidth(src, dst, copy=False)
+    copy = binding.peak_bandwidth(src, dst, copy=True)
+    del src, dst
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(2 * cus * 256, dtype=torch.float32, device=dev)
+    m32 = binding.peak_mfma(0, 4096, sink)
+    m16 = binding.peak_mfma(1, 4096, sink)
+    del sink
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(read, 1), "hbm_copy_GBps": round(copy, 1),
+            "mfma_bf16_32x32x16_TFLOPs": round(m32, 1), "mfma_bf16_16x16x32_TFLOPs": round(m16, 1),
+            "method": "rlt_peak_bandwidth (1 GiB read; copy counts read + written bytes) and "
+                      "rlt_peak_mfma (dense loops), fastest of 5 launches"}
+
+
+def with_peaks(out, dev):
+    """Adds the measured achievable rates and the kernel's fraction of them."""
+    pk = measure_peaks(dev)
+    out["achievable"] = pk
+    rf = out.get("roofline")
+    if rf and rf.get("unit") == "GB/s" and rf.get("achieved"):
+        rf["frac_of_achievable_read"] = round(rf["achieved"] / pk["hbm_read_GBps"], 4)
+    return out
+
+
 def run_refdepth(args):
     import torch
     from recurrent_decode_step_amd import binding, synth
@@ -311,7 +350,7 @@ def run_refdepth(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, params, e, mk, mv, t0=(K + 1) // 2,
                                            budget_s=args.cpu_budget)
-    return out
+    return with_peaks(out, dev)
 
 
 def stratified_positions(T_total, K, n_states):
@@ -532,7 +571,7 @@ def run_refdepth_stratified(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_at(cfg, params, e, mk, mv, sorted(set(positions)),
                                               budget_s=args.cpu_budget)
-    return out
+    return with_peaks(out, dev)
 
 
 def run_counters_sample(args):
@@ -1235,6 +1274,8 @@ def main():
                     help="run one 256 MiB streaming kernel before warmup (counter scaling)")
     ap.add_argument("--persistent", action="store_true",
                     help="tiny/small/refdepth --steps K: one persistent launch per decoder step")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only the achievable HBM and MFMA rates of the device")
     ap.add_argument("--breakdown", action="store_true",
                     help="time every kernel class on the sampled steps (adds event records)")
     args = ap.parse_args()
@@ -1243,7 +1284,10 @@ def main():
               "communication, so N GPUs run N independent copies; run it with --gpus 1.",
               file=sys.stderr)
         raise SystemExit(2)
-    if args.counters_sample:
+    if args.peaks:
+        import torch
+        out = {"mode": "peaks", **measure_peaks(torch.device("cuda", 0))}
+    elif args.counters_sample:
         out = run_counters_sample(args)
     elif args.encode:
         out = run_encode(args)

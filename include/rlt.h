@@ -500,6 +500,29 @@ rlt_status rlt_profile_begin(rlt_state *st, int32_t class_mask, int32_t max_laun
 rlt_status rlt_profile_collect(rlt_state *st, int32_t kclass, double *total_ms,
                                int32_t *launches, double *bytes_moved);
 
+/* Achievable peaks of the device, measured on it (the survey's measurement
+ * contract asks for them beside the published figures; they price the
+ * path's kernels against what the part delivers).  Both return RLT_OK,
+ * RLT_ERR_INVALID_ARG for a null pointer or bad count, RLT_ERR_SHAPE for a
+ * bad size, RLT_ERR_DEVICE for a HIP error; they set no rlt_last_error text.
+ * Each runs `reps` launches on the stream and reports the fastest (HIP events
+ * bound to the launch's own dispatch); the call synchronises with them.
+ *   rlt_peak_bandwidth: read (copy = 0) or copy to dev_dst (copy = 1) `bytes`
+ *     bytes of dev_src (a multiple of 64 KiB, at least 64 MiB; both buffers
+ *     16-byte aligned, dev_dst at least `bytes` long for a copy and 4 KiB for
+ *     a read) with 16-byte non-temporal loads and stores, one contiguous
+ *     64 KiB span per workgroup; *gb_per_s = bytes moved (read, or read plus
+ *     written) / time, in 1e9 bytes per second.
+ *   rlt_peak_mfma: dense loops of v_mfma_f32_32x32x16_bf16 (shape 0, four
+ *     independent accumulator chains per wavefront) or v_mfma_f32_16x16x32_bf16
+ *     (shape 1, eight chains), `iters` rounds, two 256-thread workgroups per
+ *     compute unit; dev_sink receives one float per thread (2 * CUs * 256
+ *     floats, sink_bytes at least that); *tflops in 1e12 FLOP per second. */
+rlt_status rlt_peak_bandwidth(const void *dev_src, void *dev_dst, size_t bytes, int32_t copy,
+                              int32_t reps, double *gb_per_s, void *stream);
+rlt_status rlt_peak_mfma(int32_t shape, int32_t iters, int32_t reps, float *dev_sink,
+                         size_t sink_bytes, double *tflops, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_by
             "rlt_encoder_state_bytes", "rlt_encoder_state_init", "rlt_encoder_state_destroy",
             "rlt_encoder_state_reset", "rlt_encoder_position", "rlt_encode",
             "rlt_encoder_profile_begin", "rlt_encoder_profile_collect",
-            "rlt_bptt_workspace_bytes", "rlt_bptt")
+            "rlt_bptt_workspace_bytes", "rlt_bptt", "rlt_peak_bandwidth", "rlt_peak_mfma")
 
 
 class RLTError(RuntimeError):
@@ -133,6 +133,8 @@ def load_library(path: str = LIB_PATH):
         "rlt_encoder_profile_collect": (i32, [vp, i32, P(C.c_double), P(i32), P(C.c_double),
                                               P(C.c_double)]),
         "rlt_bptt_workspace_bytes": (sz, [P(rlt_config), i32, i32]),
+        "rlt_peak_bandwidth": (i32, [vp, vp, sz, i32, i32, P(C.c_double), vp]),
+        "rlt_peak_mfma": (i32, [i32, i32, i32, vp, sz, P(C.c_double), vp]),
         "rlt_bptt": (i32, [P(rlt_config), P(rlt_params), i32, i32, vp, P(rlt_memory), vp,
                            P(rlt_bptt_opts), P(rlt_params), vp, P(rlt_memory), vp, vp, sz, vp]),
     }
@@ -609,3 +611,22 @@ def rlt_bptt(cfg: ModelConfig, params: dict, e: torch.Tensor, memory, targets: t
                         C.byref(dmem) if dmem is not None else None, loss.data_ptr(),
                         workspace.data_ptr(), nbytes, _stream(stream)))
     return loss, grads, de, dm
+
+
+def peak_bandwidth(src: torch.Tensor, dst: torch.Tensor, copy: bool, reps: int = 5,
+                   stream=None) -> float:
+    """GB/s of a streaming read (copy False) or copy of src's bytes (rlt_peak_bandwidth)."""
+    out = C.c_double(0.0)
+    _check(load_library().rlt_peak_bandwidth(src.data_ptr(), dst.data_ptr(),
+                                             src.numel() * src.element_size(), 1 if copy else 0,
+                                             reps, C.byref(out), _stream(stream)))
+    return out.value
+
+
+def peak_mfma(shape: int, iters: int, sink: torch.Tensor, reps: int = 5, stream=None) -> float:
+    """TFLOP/s of a dense bf16 MFMA loop: shape 0 = 32x32x16, 1 = 16x16x32 (rlt_peak_mfma)."""
+    out = C.c_double(0.0)
+    _check(load_library().rlt_peak_mfma(shape, iters, reps, sink.data_ptr(),
+                                        sink.numel() * sink.element_size(), C.byref(out),
+                                        _stream(stream)))
+    return out.value

@@ -121,6 +121,28 @@ def test_null_handles():
     assert L.rlt_profile_collect(None, 0, None, None, None) == binding.RLT_ERR_INVALID_ARG
 
 
+def test_peak_measurement_argument_checks():
+    """The peak calls reject bad arguments on the host, before any device work."""
+    L = lib()
+    out = C.c_double(0.0)
+    big = 1 << 30
+    assert L.rlt_peak_bandwidth(None, C.c_void_p(0x1000), big, 0, 1, C.byref(out),
+                                None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_peak_bandwidth(C.c_void_p(0x1000), C.c_void_p(0x2000), big, 0, 0, C.byref(out),
+                                None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_peak_bandwidth(C.c_void_p(0x1000), C.c_void_p(0x2000), 1 << 20, 0, 1,
+                                C.byref(out), None) == binding.RLT_ERR_SHAPE      # under 64 MiB
+    assert L.rlt_peak_bandwidth(C.c_void_p(0x1000), C.c_void_p(0x2000), big + 16, 0, 1,
+                                C.byref(out), None) == binding.RLT_ERR_SHAPE      # not 64 KiB spans
+    assert L.rlt_peak_bandwidth(C.c_void_p(0x1008), C.c_void_p(0x2000), big, 1, 1,
+                                C.byref(out), None) == binding.RLT_ERR_SHAPE      # unaligned
+    assert L.rlt_peak_mfma(0, 16, 1, None, 1 << 20, C.byref(out), None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_peak_mfma(2, 16, 1, C.c_void_p(0x1000), 1 << 20, C.byref(out),
+                           None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_peak_mfma(0, 0, 1, C.c_void_p(0x1000), 1 << 20, C.byref(out),
+                           None) == binding.RLT_ERR_INVALID_ARG
+
+
 def test_encoder_null_handles_and_sizes():
     L = lib()
     out = C.c_void_p()
