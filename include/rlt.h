@@ -137,19 +137,30 @@ const char *rlt_status_str(rlt_status s);
 const char *rlt_last_error(void);          /* thread-local; "" if none */
 
 /* ------------------------------------------------------------------ model */
-/* Bytes of device memory a model needs (0 if the config is invalid). */
+/* Bytes of device memory a model needs (0 if the config is invalid): the
+ * decoder's parameters -- gate W_g, b_g and s*; per layer the three RMSNorm
+ * gains, W_Q, W_K, W_V, W_O, W_Qc, W_Oc, W_1, W_2; the output norm and head
+ * [Princeton, architecture; Tutorial, "How the Architecture Works"] -- in the
+ * packed tile layout the kernels read. */
 size_t rlt_model_bytes(const rlt_config *cfg);
 
 /* Validate cfg, repack `src` into dev_buf (>= rlt_model_bytes, 256-byte
  * aligned) with kernels on `stream`, and return a host handle in *out.
- * model_version tags every state made from this model. */
+ * model_version tags every state made from this model: a state is valid only
+ * under the weights that produced it, and a call with a state of another
+ * version fails with RLT_ERR_STALE [Tutorial, "Current-Policy Reinforcement
+ * Learning Replay": states are rebuilt under the current weights]. */
 rlt_status rlt_model_create(const rlt_config *cfg, const rlt_params *src,
                             uint64_t model_version, void *dev_buf, size_t bytes,
                             void *stream, rlt_model **out);
 void rlt_model_destroy(rlt_model *m);       /* frees the host handle only */
 
 /* ------------------------------------------------------------------ state */
-/* Bytes for a state of `batch` slots whose positions stay <= max_tokens
+/* The state of a sequence is H_t = (s_t, C_t): the decoder output carried to
+ * the next token's gate and the window cache of every layer [Tutorial, "How
+ * the Architecture Works": the state and its transition; Article, "The
+ * Recurrent Decoder State"].
+ * Bytes for a state of `batch` slots whose positions stay <= max_tokens
  * (max_tokens is checked by the calls, it does not change the size): s [B][d]
  * fp32, positions [B] int32, the window cache K,V [L][B][H][W][dh] in the
  * model dtype (a ring: position p lives in entry (p-1) mod W), and the
