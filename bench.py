@@ -1163,32 +1163,43 @@ def cpu_encoder_baseline(cfg, params_gpu, eparams_gpu, tokens, budget_s=15.0):
 
 
 def run_train(args):
-    """Backpropagation through time at the small configuration in fp32
-    (d = 512, H = 8, L = 12, F = 2048, W = 128, G = 12, V = 4096): B sequences
-    (default 128) x 128 steps from H_0, loss on every next token, the full gradient of every
-    parameter, e and the memory (one rlt_bptt call), repeated `steps` times."""
+    """Backpropagation through time in fp32: B sequences x T steps from H_0,
+    loss on every next token, the full gradient of every parameter, e and the
+    memory (one rlt_bptt call), repeated `steps` times.  Default: the small
+    configuration (d = 512, H = 8, L = 12, F = 2048, W = 128, G = 12, V = 4096),
+    B = 128, T = 128, every intermediate kept.  --train-workload refdepth: the
+    reference-depth model (d = 2048, L = 48, F = 8192, W = 512, G = 1,
+    V = 32768) in fp32, B = 8, T = 256, which fits only with activation
+    checkpointing (--train-segment, default 16 there)."""
     import torch
     from recurrent_decode_step_amd import binding, synth
-    from recurrent_decode_step_amd.configs import SMALL
-    cfg = SMALL.model.with_(dtype=0)
-    B, T = args.train_batch, 128
-    K = 3 if args.steps is None else args.steps
+    from recurrent_decode_step_amd.configs import SMALL, REFDEPTH
+    ref = args.train_workload == "refdepth"
+    cfg = (REFDEPTH if ref else SMALL).model.with_(dtype=0)
+    B = args.train_batch if args.train_batch else (8 if ref else 128)
+    T = args.train_steps if args.train_steps else (256 if ref else 128)
+    seg = args.train_segment if args.train_segment is not None else (16 if ref else 0)
+    K = (1 if ref else 3) if args.steps is None else args.steps
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     params = synth.model_params(cfg, device=dev)
     e = synth.encoder_e(cfg, B, T, device=dev)
     mk, mv = synth.encoder_memory(cfg, B, T, device=dev)
     tg = torch.from_numpy(synth.token_ids(B, T, cfg.vocab, index=0)).to(dev)
-    ws = None
-    for _ in range(max(args.warmup, 1)):
-        loss, g, de, dm = binding.rlt_bptt(cfg, params, e, (mk, mv), tg)
+    L_ = binding.load_library()
+    cc = binding.make_config(cfg)
+    ws_bytes = L_.rlt_bptt_workspace_bytes_segmented(binding.C.byref(cc), B, T, seg)
+    ws_full = L_.rlt_bptt_workspace_bytes(binding.C.byref(cc), B, T)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    for _ in range(1 if ref else max(args.warmup, 1)):
+        loss, g, de, dm = binding.rlt_bptt(cfg, params, e, (mk, mv), tg, workspace=ws, segment=seg)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(K):
-        loss, g, de, dm = binding.rlt_bptt(cfg, params, e, (mk, mv), tg)
+        loss, g, de, dm = binding.rlt_bptt(cfg, params, e, (mk, mv), tg, workspace=ws, segment=seg)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / K
@@ -1203,14 +1214,19 @@ def run_train(args):
     attn_flops = 3.0 * 4 * d * L * B * pos
     total = gemm_flops + attn_flops
     out = {
-        "metric": f"BPTT training tokens/sec at 1 GPU (fp32, 12-layer d=512, B={B} x 128 steps)",
+        "metric": f"BPTT training tokens/sec at 1 GPU (fp32, {L}-layer d={d}, B={B} x {T} steps)",
         "value": round(B * T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": max(args.warmup, 1), "ms_per_step": round(ms, 3), "higher_is_better": True,
-        "dtype": "f32", "data": "synthetic",
-        "config": {"workload": (f"small-f32 model (V={V},d={d},H={H},L={L},F={F},W={W},G={cfg.mem_groups}), "
-                                f"BPTT over B={B} sequences x T={T} steps"),
+        "warmup": 1 if ref else max(args.warmup, 1), "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": (f"{'refdepth' if ref else 'small'}-f32 model (V={V},d={d},H={H},L={L},F={F},"
+                                f"W={W},G={cfg.mem_groups}), BPTT over B={B} sequences x T={T} steps"),
                    "batch": B, "steps_per_sequence": T, "loss": "next-token cross-entropy, all targets",
-                   "gradients": "every parameter, e and memory; full BPTT"},
+                   "gradients": "every parameter, e and memory; full BPTT",
+                   "activation_checkpointing": (f"segments of {seg} steps (every step forward once, "
+                                                f"then each segment recomputed before its backward)"
+                                                if 0 < seg < T else "none: every intermediate kept"),
+                   "workspace_GB": round(ws_bytes / 1e9, 2),
+                   "workspace_GB_without_checkpointing": round(ws_full / 1e9, 2)},
         "roofline": {"bound": "mfma", "kernel": "whole rlt_bptt call (fp32 MFMA GEMMs, VALU attention)",
                      "achieved": round(total / (ms / 1e3) / 1e12, 2), "peak": 157.3,
                      "unit": "TFLOP/s", "frac": round(total / (ms / 1e3) / 157.3e12, 4),
@@ -1219,6 +1235,11 @@ def run_train(args):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_train_baseline(cfg, params, e, mk, mv, tg, args.cpu_budget)
+    if 0 < seg < T:
+        # forward FLOPs are spent twice for every segment but the last
+        nseg = (T + seg - 1) // seg
+        out["roofline"]["recomputed_forward_flops"] = round(
+            (gemm_flops + attn_flops) / 3.0 * (nseg - 1) * seg / T)
     return out
 
 
@@ -1257,8 +1278,14 @@ def main():
                     help="generation at the reference depth after the 2048-token prompt")
     ap.add_argument("--train", action="store_true",
                     help="backpropagation through time (fp32, small config, B x 128 steps)")
-    ap.add_argument("--train-batch", type=int, default=128,
-                    help="sequences per BPTT call for --train")
+    ap.add_argument("--train-batch", type=int, default=0,
+                    help="sequences per BPTT call for --train (default 128; refdepth 8)")
+    ap.add_argument("--train-steps", type=int, default=0,
+                    help="steps per sequence for --train (default 128; refdepth 256)")
+    ap.add_argument("--train-segment", type=int, default=None,
+                    help="activation checkpointing for --train: steps held at once (0 = all)")
+    ap.add_argument("--train-workload", default="small", choices=["small", "refdepth"],
+                    help="model for --train")
     ap.add_argument("--encode", action="store_true",
                     help="the causal encoder over the reference-depth prompt (B = 32 x 2048 tokens)")
     ap.add_argument("--score", action="store_true",

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define RLT_ABI_VERSION 1
+#define RLT_ABI_VERSION 2
 
 typedef enum {
   RLT_OK = 0,
@@ -465,17 +465,34 @@ rlt_status rlt_state_import(const rlt_model *m, rlt_state *st, int32_t n,
  * > 0, at each boundary between steps k*j and k*j + 1 the parts of H listed in
  * opts->detach are detached, RLT_DETACH_S (s) and/or RLT_DETACH_KV (every cache
  * entry carried across the boundary); the forward values never change.
- * opts NULL or chunk 0 = full BPTT. */
+ * opts NULL or chunk 0 = full BPTT.
+ * Activation checkpointing [Tutorial, "Key Design Principles": checkpointing
+ * around the recurrent decoder; Princeton, design-principles paragraph]:
+ * with opts->segment = S in [1, T), the intermediates of only S steps are
+ * held at once.  Every step runs forward once; then the segments go in
+ * reverse, each recomputed forward from its first state (the same kernels on
+ * the same inputs: the same bits) before its backward.  Kept for every step:
+ * the keys and values of every layer and their gradient rows, s_t and the
+ * per-row losses.  The loss, dev_de and the memory gradients are bitwise
+ * those of segment 0 (= T: everything kept); the parameter gradients are
+ * sums over the segments' rows in reverse segment order, so they differ from
+ * segment 0 only by the grouping of those sums. */
 enum { RLT_DETACH_S = 1, RLT_DETACH_KV = 2 };
 typedef struct {
   int32_t chunk;                /* truncation length in steps; 0 = none */
   int32_t detach;               /* RLT_DETACH_* bits cut at each chunk boundary */
+  int32_t segment;              /* steps whose intermediates are held at once; 0 = all T */
 } rlt_bptt_opts;
 
-/* Workspace bytes for rlt_bptt (every intermediate of the T steps is kept:
- * about (22 d + 3 F) * L + 7 d + V floats per sequence and step); 0 if the
+/* Workspace bytes for rlt_bptt with every intermediate of the T steps kept
+ * (about (22 d + 3 F) * L + 7 d + V floats per sequence and step); 0 if the
  * config is invalid, not fp32, or T exceeds 4096. */
 size_t rlt_bptt_workspace_bytes(const rlt_config *cfg, int32_t batch, int32_t T);
+/* The same for opts->segment = segment (0 = T): about 4 d L + d floats per
+ * sequence and step for all T steps plus (18 d + 3 F) * L + 6 d + V per
+ * sequence and step of one segment; 0 also for segment < 0. */
+size_t rlt_bptt_workspace_bytes_segmented(const rlt_config *cfg, int32_t batch, int32_t T,
+                                          int32_t segment);
 
 /* params: fp32 canonical device tensors as for rlt_model_create (read only).
  * grads:  buffers of the same shapes, OVERWRITTEN with d loss / d param.
@@ -483,7 +500,8 @@ size_t rlt_bptt_workspace_bytes(const rlt_config *cfg, int32_t batch, int32_t T)
  * dev_de [B][T][d] (written) or NULL; dmem: memory gradients with mem's
  * strides and 16-byte aligned pointers (RLT_ERR_SHAPE otherwise; ACCUMULATED
  * into: zero them first) or NULL; dev_loss [1] (written).
- * dev_workspace: >= rlt_bptt_workspace_bytes, 256-byte aligned, caller owned.
+ * dev_workspace: >= rlt_bptt_workspace_bytes_segmented(cfg, batch, T,
+ * opts->segment), 256-byte aligned, caller owned.
  * RLT_ERR_UNSUPPORTED for a bf16 config. */
 rlt_status rlt_bptt(const rlt_config *cfg, const rlt_params *params, int32_t batch, int32_t T,
                     const float *dev_e, const rlt_memory *mem, const int32_t *dev_targets,

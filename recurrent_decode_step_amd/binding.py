@@ -23,6 +23,7 @@ RLT_LOGITS_ALL, RLT_LOGITS_LAST, RLT_LOGITS_NONE = 0, 1, 2
 RLT_K_EXTRA, RLT_K_GEMM, RLT_K_SWA, RLT_K_CROSS = 0, 1, 2, 3
 RLT_E_GEMM, RLT_E_ATTN, RLT_E_OTHER = 0, 1, 2
 RLT_DETACH_S, RLT_DETACH_KV = 1, 2
+ABI_VERSION = 2                      # include/rlt.h RLT_ABI_VERSION
 
 EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_bytes",
             "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",
@@ -36,7 +37,8 @@ EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_by
             "rlt_encoder_state_bytes", "rlt_encoder_state_init", "rlt_encoder_state_destroy",
             "rlt_encoder_state_reset", "rlt_encoder_position", "rlt_encode",
             "rlt_encoder_profile_begin", "rlt_encoder_profile_collect",
-            "rlt_bptt_workspace_bytes", "rlt_bptt", "rlt_peak_bandwidth", "rlt_peak_mfma")
+            "rlt_bptt_workspace_bytes", "rlt_bptt_workspace_bytes_segmented", "rlt_bptt",
+            "rlt_peak_bandwidth", "rlt_peak_mfma")
 
 
 class RLTError(RuntimeError):
@@ -72,7 +74,7 @@ class rlt_sampling(C.Structure):
 
 
 class rlt_bptt_opts(C.Structure):
-    _fields_ = [("chunk", C.c_int32), ("detach", C.c_int32)]
+    _fields_ = [("chunk", C.c_int32), ("detach", C.c_int32), ("segment", C.c_int32)]
 
 
 class rlt_encoder_params(C.Structure):
@@ -133,6 +135,7 @@ def load_library(path: str = LIB_PATH):
         "rlt_encoder_profile_collect": (i32, [vp, i32, P(C.c_double), P(i32), P(C.c_double),
                                               P(C.c_double)]),
         "rlt_bptt_workspace_bytes": (sz, [P(rlt_config), i32, i32]),
+        "rlt_bptt_workspace_bytes_segmented": (sz, [P(rlt_config), i32, i32, i32]),
         "rlt_peak_bandwidth": (i32, [vp, vp, sz, i32, i32, P(C.c_double), vp]),
         "rlt_peak_mfma": (i32, [i32, i32, i32, vp, sz, P(C.c_double), vp]),
         "rlt_bptt": (i32, [P(rlt_config), P(rlt_params), i32, i32, vp, P(rlt_memory), vp,
@@ -142,6 +145,9 @@ def load_library(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.rlt_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.rlt_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild the library")
     _lib = lib
     return lib
 
@@ -573,7 +579,7 @@ PARAM_NAMES = tuple(n for n, _ in rlt_params._fields_)
 
 def rlt_bptt(cfg: ModelConfig, params: dict, e: torch.Tensor, memory, targets: torch.Tensor,
              chunk: int = 0, detach: int = 0, want_de: bool = True, want_dmem: bool = True,
-             workspace=None, stream=None):
+             workspace=None, stream=None, segment: int = 0):
     """Backpropagation through time over e [B][T][d] (fp32 model): returns
     (loss tensor [1], {name: gradient}, de [B][T][d] or None, (dmk, dmv) or None).
     params: canonical fp32 tensors; memory: (K, V) [G][B][H][cap][dh] fp32."""
@@ -600,12 +606,12 @@ def rlt_bptt(cfg: ModelConfig, params: dict, e: torch.Tensor, memory, targets: t
         dmem = memory_view(*dm)
     de = torch.empty_like(e) if want_de else None
     loss = torch.empty(1, dtype=torch.float32, device=dev)
-    nbytes = lib.rlt_bptt_workspace_bytes(C.byref(ccfg), B, T)
+    nbytes = lib.rlt_bptt_workspace_bytes_segmented(C.byref(ccfg), B, T, int(segment))
     if nbytes == 0:
         _check(RLT_ERR_INVALID_ARG)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    opts = rlt_bptt_opts(int(chunk), int(detach))
+    opts = rlt_bptt_opts(int(chunk), int(detach), int(segment))
     _check(lib.rlt_bptt(C.byref(ccfg), C.byref(cp), B, T, e.data_ptr(), C.byref(mem), tg.data_ptr(),
                         C.byref(opts), C.byref(cg), de.data_ptr() if de is not None else None,
                         C.byref(dmem) if dmem is not None else None, loss.data_ptr(),

@@ -2014,11 +2014,16 @@ rlt_status rlt_encoder_profile_collect(rlt_encoder_state *es, int32_t kclass, do
 // ================================================================== training
 extern "C" {
 
-size_t rlt_bptt_workspace_bytes(const rlt_config *cfg, int32_t batch, int32_t T) {
+size_t rlt_bptt_workspace_bytes_segmented(const rlt_config *cfg, int32_t batch, int32_t T,
+                                          int32_t segment) {
   if (check_config(cfg) != RLT_OK || cfg->dtype != RLT_DTYPE_F32 || batch < 1 || T < 1 ||
-      T > kTrainMaxPos)
+      T > kTrainMaxPos || segment < 0)
     return 0;
-  return train_workspace_bytes(*cfg, batch, T);
+  return train_workspace_bytes(*cfg, batch, T, segment);
+}
+
+size_t rlt_bptt_workspace_bytes(const rlt_config *cfg, int32_t batch, int32_t T) {
+  return rlt_bptt_workspace_bytes_segmented(cfg, batch, T, 0);
 }
 
 rlt_status rlt_bptt(const rlt_config *cfg, const rlt_params *params, int32_t batch, int32_t T,
@@ -2054,14 +2059,16 @@ rlt_status rlt_bptt(const rlt_config *cfg, const rlt_params *params, int32_t bat
     if (((uintptr_t)dmem->k | (uintptr_t)dmem->v) % 16)
       return fail(RLT_ERR_SHAPE, "memory gradient pointers must be 16-byte aligned");
   }
-  int chunk = 0, detach = 0;
+  int chunk = 0, detach = 0, segment = 0;
   if (opts) {
     chunk = opts->chunk;
     detach = opts->detach;
+    segment = opts->segment;
   }
   if (chunk < 0) return fail(RLT_ERR_INVALID_ARG, "chunk must be >= 0");
+  if (segment < 0) return fail(RLT_ERR_INVALID_ARG, "segment must be >= 0");
   if (detach & ~(RLT_DETACH_S | RLT_DETACH_KV)) return fail(RLT_ERR_INVALID_ARG, "unknown detach bits");
-  const size_t need_ws = rlt_bptt_workspace_bytes(cfg, batch, T);
+  const size_t need_ws = rlt_bptt_workspace_bytes_segmented(cfg, batch, T, segment);
   if (!dev_workspace) return fail(RLT_ERR_INVALID_ARG, "workspace is NULL");
   if ((uintptr_t)dev_workspace % 256) return fail(RLT_ERR_SHAPE, "workspace must be 256-byte aligned");
   if (workspace_bytes < need_ws)
@@ -2085,6 +2092,7 @@ rlt_status rlt_bptt(const rlt_config *cfg, const rlt_params *params, int32_t bat
   a.tg = dev_targets;
   a.chunk = chunk;
   a.detach = detach;
+  a.segment = segment;
   a.de = dev_de;
   a.loss = dev_loss;
   const hipError_t e = launch_bptt(a, dev_workspace, static_cast<hipStream_t>(stream));

@@ -283,10 +283,11 @@ struct TrainArgs {
   float *dmk, *dmv;          // memory gradients with the same strides (+=), or null
   const int32_t *tg;         // [B][T] targets
   int chunk, detach;         // truncation length (0: none) and RLT_DETACH_* bits
+  int segment;               // steps whose activations are kept at once (0: all T)
   float *de;                 // [B][T][d] or null
   float *loss;               // [1]
 };
-size_t train_workspace_bytes(const rlt_config &c, int B, int T);
+size_t train_workspace_bytes(const rlt_config &c, int B, int T, int segment);
 hipError_t launch_bptt(const TrainArgs &a, void *ws, hipStream_t s);
 
 }  // namespace rlt

@@ -963,23 +963,34 @@ void t_gemm_sum(const float *const *As, int64_t lda, const float *const *Bs, int
 
 // ---------------------------------------------------------------- driver
 namespace {
-// Workspace arrays (fp32 unless noted), carved in this order.
+// Workspace arrays (fp32 unless noted), carved in this order.  Activation
+// checkpointing: the arrays a later step or the end of the call reads keep
+// every step -- the keys and values of every layer (the window of later
+// steps reads them) with their gradient rows, s_t (the state at segment
+// boundaries) and the per-row losses; every other array holds one segment of
+// S steps, recomputed from the segment's first state before its backward.
 struct TrainWs {
-  // per layer [L][T][B][.]
-  float *xin, *r1, *a, *q, *kh, *vh, *m1, *l1, *o, *x1, *r2, *c, *qc, *m2, *l2, *oc, *x2, *r3, *f,
-      *hpre, *h;
-  float *dq, *dkh, *dvh, *dxo, *dqc, *dxoc, *dhp, *dxf, *da, *dc, *df;
-  // per step [T][B][.]
-  float *es, *g, *s, *ro, *sn, *dl, *lossr, *dz, *dsn;
+  // per layer, every step [L][T][B][d]
+  float *kh, *vh, *dkh, *dvh;
+  // per layer, one segment [L][S][B][.]
+  float *xin, *r1, *a, *q, *m1, *l1, *o, *x1, *r2, *c, *qc, *m2, *l2, *oc, *x2, *r3, *f, *hpre, *h;
+  float *dq, *dxo, *dqc, *dxoc, *dhp, *dxf, *da, *dc, *df;
+  // per step, every step [T][B][.]
+  float *s, *lossr;
+  // per step, one segment [S][B][.]
+  float *es, *g, *ro, *sn, *dl, *dz, *dsn;
   // scratch [B][.]
   float *logits, *dx, *dtmp, *des, *dscarry;
   int *lo_w, *lo_m, *hi;
   float *split;              // split-K partial sums
 };
 
-size_t train_layout(const rlt_config &c, int B, int T, TrainWs *w, void *base) {
+// steps whose activations are kept at once: S in [1, T]; 0 or more than T = T
+int segment_of(int T, int segment) { return segment <= 0 || segment > T ? T : segment; }
+
+size_t train_layout(const rlt_config &c, int B, int T, int S, TrainWs *w, void *base) {
   const size_t L = c.n_layers, d = c.d_model, F = c.d_ffn, H = c.n_heads, V = c.vocab;
-  const size_t TB = (size_t)T * B;
+  const size_t TB = (size_t)T * B, SB = (size_t)S * B;
   size_t off = 0;
   char *p = static_cast<char *>(base);
   auto take = [&](size_t elems) -> float * {
@@ -988,19 +999,20 @@ size_t train_layout(const rlt_config &c, int B, int T, TrainWs *w, void *base) {
     off += elems * 4;
     return r;
   };
-  const size_t LTB = L * TB;
-  w->xin = take(LTB * d); w->r1 = take(LTB); w->a = take(LTB * d); w->q = take(LTB * d);
-  w->kh = take(LTB * d); w->vh = take(LTB * d); w->m1 = take(LTB * H); w->l1 = take(LTB * H);
-  w->o = take(LTB * d); w->x1 = take(LTB * d); w->r2 = take(LTB); w->c = take(LTB * d);
-  w->qc = take(LTB * d); w->m2 = take(LTB * H); w->l2 = take(LTB * H); w->oc = take(LTB * d);
-  w->x2 = take(LTB * d); w->r3 = take(LTB); w->f = take(LTB * d); w->hpre = take(LTB * F);
-  w->h = take(LTB * F);
-  w->dq = take(LTB * d); w->dkh = take(LTB * d); w->dvh = take(LTB * d); w->dxo = take(LTB * d);
-  w->dqc = take(LTB * d); w->dxoc = take(LTB * d); w->dhp = take(LTB * F); w->dxf = take(LTB * d);
-  w->da = take(LTB * d); w->dc = take(LTB * d); w->df = take(LTB * d);
-  w->es = take(TB * 2 * d); w->g = take(TB * d); w->s = take(TB * d); w->ro = take(TB);
-  w->sn = take(TB * d); w->dl = take(TB * V); w->lossr = take(TB); w->dz = take(TB * d);
-  w->dsn = take(TB * d);
+  const size_t LTB = L * TB, LSB = L * SB;
+  w->kh = take(LTB * d); w->vh = take(LTB * d); w->dkh = take(LTB * d); w->dvh = take(LTB * d);
+  w->xin = take(LSB * d); w->r1 = take(LSB); w->a = take(LSB * d); w->q = take(LSB * d);
+  w->m1 = take(LSB * H); w->l1 = take(LSB * H);
+  w->o = take(LSB * d); w->x1 = take(LSB * d); w->r2 = take(LSB); w->c = take(LSB * d);
+  w->qc = take(LSB * d); w->m2 = take(LSB * H); w->l2 = take(LSB * H); w->oc = take(LSB * d);
+  w->x2 = take(LSB * d); w->r3 = take(LSB); w->f = take(LSB * d); w->hpre = take(LSB * F);
+  w->h = take(LSB * F);
+  w->dq = take(LSB * d); w->dxo = take(LSB * d); w->dqc = take(LSB * d); w->dxoc = take(LSB * d);
+  w->dhp = take(LSB * F); w->dxf = take(LSB * d); w->da = take(LSB * d); w->dc = take(LSB * d);
+  w->df = take(LSB * d);
+  w->s = take(TB * d); w->lossr = take(TB);
+  w->es = take(SB * 2 * d); w->g = take(SB * d); w->ro = take(SB); w->sn = take(SB * d);
+  w->dl = take(SB * V); w->dz = take(SB * d); w->dsn = take(SB * d);
   w->logits = take((size_t)B * V); w->dx = take((size_t)B * d); w->dtmp = take((size_t)B * d);
   w->des = take((size_t)B * 2 * d); w->dscarry = take((size_t)B * d);
   w->lo_w = reinterpret_cast<int *>(take(B)); w->lo_m = reinterpret_cast<int *>(take(B));
@@ -1009,7 +1021,7 @@ size_t train_layout(const rlt_config &c, int B, int T, TrainWs *w, void *base) {
   return (off + 255) & ~(size_t)255;
 }
 
-hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
+hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, int S, hipStream_t s) {
   // the attention kernels read 16-byte row pieces of the memory
   if (A.m_seq % 4 || A.m_head % 4 || A.m_pos % 4 || A.m_group % 4 || !aligned16(A.mk) ||
       !aligned16(A.mv) || (A.dmk && (!aligned16(A.dmk) || !aligned16(A.dmv))))
@@ -1030,9 +1042,15 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
   auto dwq = GL(A.gr->wq, (size_t)d * d), dwk = GL(A.gr->wk, (size_t)d * d), dwv = GL(A.gr->wv, (size_t)d * d),
        dwo = GL(A.gr->wo, (size_t)d * d), dwqc = GL(A.gr->wqc, (size_t)d * d), dwoc = GL(A.gr->woc, (size_t)d * d),
        dw1 = GL(A.gr->w1, (size_t)F * d), dw2 = GL(A.gr->w2, (size_t)d * F);
-  // per-layer saved rows: layer l, step t, row b
+  // rows of layer l at step t: every-step arrays (at, st) by t, segment arrays
+  // (sg, ss) by t - t0, the first step of the segment in hand
+  int t0 = 0;
   auto at = [&](float *base, int l, int t, size_t width) { return base + (((size_t)l * T + t) * B) * width; };
   auto st = [&](float *base, int t, size_t width) { return base + (size_t)t * B * width; };
+  auto sg = [&](float *base, int l, int t, size_t width) {
+    return base + (((size_t)l * S + (t - t0)) * B) * width;
+  };
+  auto ss = [&](float *base, int t, size_t width) { return base + (size_t)(t - t0) * B * width; };
   auto norm_fwd = [&](const float *x, const float *gm, float *y, float *r) {
     const dim3 g(B), t(64);                      // one wavefront (row) per workgroup
     switch (d) {
@@ -1064,15 +1082,20 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
   zero(A.gr->s_star, d); zero(A.gr->wg, (size_t)d * 2 * d); zero(A.gr->bg, d); zero(A.gr->go, d);
   zero(A.gr->wout, (size_t)V * d);
   zero(A.gr->g1, (size_t)L * d); zero(A.gr->g2, (size_t)L * d); zero(A.gr->g3, (size_t)L * d);
+  // the weight gradients are sums over the segments' rows
+  zero(A.gr->wq, (size_t)L * d * d); zero(A.gr->wk, (size_t)L * d * d); zero(A.gr->wv, (size_t)L * d * d);
+  zero(A.gr->wo, (size_t)L * d * d); zero(A.gr->wqc, (size_t)L * d * d); zero(A.gr->woc, (size_t)L * d * d);
+  zero(A.gr->w1, (size_t)L * F * d); zero(A.gr->w2, (size_t)L * d * F);
   zero(w.dkh, (size_t)L * TB * d); zero(w.dvh, (size_t)L * TB * d);
   zero(w.dscarry, (size_t)B * d);
   if (A.de) zero(A.de, TB * d);
 
-  // ---- forward
-  for (int t = 0; t < T; ++t) {
+  // ---- forward of step t (segment arrays at t - t0); the same kernels on the
+  // same inputs give the same bits, so a recomputed step equals its first pass
+  auto fwd_step = [&](int t) {
     hipLaunchKernelGGL(k_t_ranges, dim3(blocks_for(B, 64)), dim3(64), 0, s, w.lo_w, w.lo_m, w.hi, B, t, Wn);
     // es = [e_t ; s_{t-1}]
-    float *es = st(w.es, t, 2 * d);
+    float *es = ss(w.es, t, 2 * d);
     hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s,
                        A.e + (size_t)t * d, (int64_t)T * d, es, (int64_t)2 * d, B, d);
     if (t == 0) {
@@ -1084,16 +1107,16 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s,
                          st(w.s, t - 1, d), (int64_t)d, es + d, (int64_t)2 * d, B, d);
     }
-    float *gz = st(w.g, t, d);
+    float *gz = ss(w.g, t, d);
     t_gemm_go<false, true, false>(es, 2 * d, P_wg, 2 * d, gz, d, B, d, 2 * d, s, w.split);
     // u, written straight into layer 0's saved input
     hipLaunchKernelGGL(k_t_merge_fwd, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, es, gz, P_bg,
-                       at(w.xin, 0, t, d), B, d);
+                       sg(w.xin, 0, t, d), B, d);
     for (int l = 0; l < L; ++l) {
-      float *xin = at(w.xin, l, t, d);
-      float *a = at(w.a, l, t, d), *r1 = at(w.r1, l, t, 1);
+      float *xin = sg(w.xin, l, t, d);
+      float *a = sg(w.a, l, t, d), *r1 = sg(w.r1, l, t, 1);
       norm_fwd(xin, g1(l), a, r1);
-      float *q = at(w.q, l, t, d), *kh = at(w.kh, l, t, d), *vh = at(w.vh, l, t, d);
+      float *q = sg(w.q, l, t, d), *kh = at(w.kh, l, t, d), *vh = at(w.vh, l, t, d);
       {
         const float *wqkv[3] = {wq(l), wk(l), wv(l)};
         float *qkv[3] = {q, kh, vh};
@@ -1104,15 +1127,15 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       ta.kb = at(w.kh, l, 0, d); ta.vb = at(w.vh, l, 0, d);
       ta.s_seq = d; ta.s_head = dh; ta.s_pos = (int64_t)B * d;
       ta.lo = w.lo_w; ta.hi = w.hi;
-      ta.o = at(w.o, l, t, d); ta.ldo = d;
-      ta.m = at(w.m1, l, t, H); ta.l = at(w.l1, l, t, H);
+      ta.o = sg(w.o, l, t, d); ta.ldo = d;
+      ta.m = sg(w.m1, l, t, H); ta.l = sg(w.l1, l, t, H);
       ta.H = H; ta.dh = dh; ta.scale = scale;
       hipLaunchKernelGGL(k_t_attn_fwd, dim3(B * H), dim3(256), 0, s, ta);
-      float *x1 = at(w.x1, l, t, d);
+      float *x1 = sg(w.x1, l, t, d);
       t_gemm_res(ta.o, d, wo(l), d, xin, d, x1, d, B, d, d, s, w.split);
-      float *cc = at(w.c, l, t, d), *r2 = at(w.r2, l, t, 1);
+      float *cc = sg(w.c, l, t, d), *r2 = sg(w.r2, l, t, 1);
       norm_fwd(x1, g2(l), cc, r2);
-      float *qc = at(w.qc, l, t, d);
+      float *qc = sg(w.qc, l, t, d);
       t_gemm_go<false, true, false>(cc, d, wqc(l), d, qc, d, B, d, d, s, w.split);
       const int grp = G == 1 ? 0 : l;
       TAttn tc{};
@@ -1120,101 +1143,100 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       tc.kb = mem_base(A.mk, grp); tc.vb = mem_base(A.mv, grp);
       tc.s_seq = A.m_seq; tc.s_head = A.m_head; tc.s_pos = A.m_pos;
       tc.lo = w.lo_m; tc.hi = w.hi;
-      tc.o = at(w.oc, l, t, d); tc.ldo = d;
-      tc.m = at(w.m2, l, t, H); tc.l = at(w.l2, l, t, H);
+      tc.o = sg(w.oc, l, t, d); tc.ldo = d;
+      tc.m = sg(w.m2, l, t, H); tc.l = sg(w.l2, l, t, H);
       tc.H = H; tc.dh = dh; tc.scale = scale;
       hipLaunchKernelGGL(k_t_attn_fwd, dim3(B * H), dim3(256), 0, s, tc);
-      float *x2 = at(w.x2, l, t, d);
+      float *x2 = sg(w.x2, l, t, d);
       t_gemm_res(tc.o, d, woc(l), d, x1, d, x2, d, B, d, d, s, w.split);
-      float *ff = at(w.f, l, t, d), *r3 = at(w.r3, l, t, 1);
+      float *ff = sg(w.f, l, t, d), *r3 = sg(w.r3, l, t, 1);
       norm_fwd(x2, g3(l), ff, r3);
-      float *hpre = at(w.hpre, l, t, F), *hh = at(w.h, l, t, F);
+      float *hpre = sg(w.hpre, l, t, F), *hh = sg(w.h, l, t, F);
       t_gemm_gelu(ff, d, w1(l), d, hpre, hh, F, B, F, d, s, w.split);
       // x3 = x2 + W2 h: the next layer's saved input, after the last layer s_t
-      float *x3 = l + 1 < L ? at(w.xin, l + 1, t, d) : st(w.s, t, d);
+      float *x3 = l + 1 < L ? sg(w.xin, l + 1, t, d) : st(w.s, t, d);
       t_gemm_res(hh, F, w2(l), F, x2, d, x3, d, B, d, F, s, w.split);
     }
     float *sv = st(w.s, t, d);
-    float *sn = st(w.sn, t, d), *ro = st(w.ro, t, 1);
+    float *sn = ss(w.sn, t, d), *ro = ss(w.ro, t, 1);
     norm_fwd(sv, (const float *)A.p->go, sn, ro);
     t_gemm_go<false, true, false>(sn, d, (const float *)A.p->wout, d, w.logits, V, B, V, d, s, w.split);
     hipLaunchKernelGGL(k_t_ce, dim3(B), dim3(256), 0, s, w.logits, A.tg + t, (int64_t)T,
-                       st(w.dl, t, V), st(w.lossr, t, 1), B, V);
-  }
-  hipLaunchKernelGGL(k_t_sum, dim3(1), dim3(64), 0, s, w.lossr, TB, A.loss);
+                       ss(w.dl, t, V), st(w.lossr, t, 1), B, V);
+  };
 
-  // ---- backward, steps in reverse
+  // ---- backward of step t (its segment's activations in place)
   const bool det_s = (A.detach & RLT_DETACH_S) != 0, det_kv = (A.detach & RLT_DETACH_KV) != 0;
-  for (int t = T - 1; t >= 0; --t) {
+  auto bwd_step = [&](int t) {
     hipLaunchKernelGGL(k_t_ranges, dim3(blocks_for(B, 64)), dim3(64), 0, s, w.lo_w, w.lo_m, w.hi, B, t, Wn);
     const int chunk_start = A.chunk > 0 ? (t / A.chunk) * A.chunk : 0;
     // head: dsn = dlogits W_out; ds_t = carry + RMSNorm_o backward
-    float *dsn = st(w.dsn, t, d);
-    t_gemm_go<false, false, false>(st(w.dl, t, V), V, (const float *)A.p->wout, d, dsn, d, B, d, V, s, w.split);
+    float *dsn = ss(w.dsn, t, d);
+    t_gemm_go<false, false, false>(ss(w.dl, t, V), V, (const float *)A.p->wout, d, dsn, d, B, d, V, s, w.split);
     // dx = carry + RMSNorm_o backward, saved as the last layer's output gradient
-    norm_bwd(st(w.s, t, d), st(w.ro, t, 1), (const float *)A.p->go, dsn, w.dscarry, w.dx,
-             at(w.dxf, L - 1, t, d));
+    norm_bwd(st(w.s, t, d), ss(w.ro, t, 1), (const float *)A.p->go, dsn, w.dscarry, w.dx,
+             sg(w.dxf, L - 1, t, d));
     for (int l = L - 1; l >= 0; --l) {
       // FFN: x3 = x2 + W2 gelu(W1 f), f = norm3(x2)
       // w.dx (saved in dxf of this layer) is the gradient of the layer's output x3
-      float *dhp = at(w.dhp, l, t, F);
-      t_gemm_gelu_grad(w.dx, d, w2(l), F, at(w.hpre, l, t, F), dhp, F, B, F, d, s, w.split);
-      float *df = at(w.df, l, t, d);
+      float *dhp = sg(w.dhp, l, t, F);
+      t_gemm_gelu_grad(w.dx, d, w2(l), F, sg(w.hpre, l, t, F), dhp, F, B, F, d, s, w.split);
+      float *df = sg(w.df, l, t, d);
       t_gemm_go<false, false, false>(dhp, F, w1(l), d, df, d, B, d, F, s, w.split);
-      norm_bwd(at(w.x2, l, t, d), at(w.r3, l, t, 1), g3(l), df, w.dx, w.dx, at(w.dxoc, l, t, d));
+      norm_bwd(sg(w.x2, l, t, d), sg(w.r3, l, t, 1), g3(l), df, w.dx, w.dx, sg(w.dxoc, l, t, d));
       // cross: x2 = x1 + W_Oc attn(W_Qc c, memory), c = norm2(x1); w.dx = d x2 (saved in dxoc)
       t_gemm_go<false, false, false>(w.dx, d, woc(l), d, w.dtmp, d, B, d, d, s, w.split);   // d oc
       const int grp = G == 1 ? 0 : l;
       TAttn tc{};
-      tc.q = at(w.qc, l, t, d); tc.ldq = d;
+      tc.q = sg(w.qc, l, t, d); tc.ldq = d;
       tc.kb = mem_base(A.mk, grp); tc.vb = mem_base(A.mv, grp);
       tc.s_seq = A.m_seq; tc.s_head = A.m_head; tc.s_pos = A.m_pos;
       tc.lo = w.lo_m; tc.hi = w.hi;
-      tc.o = at(w.oc, l, t, d); tc.ldo = d;
-      tc.m = at(w.m2, l, t, H); tc.l = at(w.l2, l, t, H);
+      tc.o = sg(w.oc, l, t, d); tc.ldo = d;
+      tc.m = sg(w.m2, l, t, H); tc.l = sg(w.l2, l, t, H);
       tc.dout = w.dtmp;
-      float *dqc = at(w.dqc, l, t, d);
+      float *dqc = sg(w.dqc, l, t, d);
       tc.dq = dqc;
       tc.dkb = A.dmk ? A.dmk + (size_t)grp * A.m_group : nullptr;
       tc.dvb = A.dmv ? A.dmv + (size_t)grp * A.m_group : nullptr;
       tc.cut_lo = 0;
       tc.H = H; tc.dh = dh; tc.scale = scale;
       hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(256), 0, s, tc);
-      float *dcc = at(w.dc, l, t, d);
+      float *dcc = sg(w.dc, l, t, d);
       t_gemm_go<false, false, false>(dqc, d, wqc(l), d, dcc, d, B, d, d, s, w.split);
-      norm_bwd(at(w.x1, l, t, d), at(w.r2, l, t, 1), g2(l), dcc, w.dx, w.dx, at(w.dxo, l, t, d));
+      norm_bwd(sg(w.x1, l, t, d), sg(w.r2, l, t, 1), g2(l), dcc, w.dx, w.dx, sg(w.dxo, l, t, d));
       // window self-attention: x1 = xin + W_O attn(q, K, V), q,k,v = W a, a = norm1(xin);
       // w.dx = d x1 (saved in dxo)
       t_gemm_go<false, false, false>(w.dx, d, wo(l), d, w.dtmp, d, B, d, d, s, w.split);    // d o
       TAttn ta{};
-      ta.q = at(w.q, l, t, d); ta.ldq = d;
+      ta.q = sg(w.q, l, t, d); ta.ldq = d;
       ta.kb = at(w.kh, l, 0, d); ta.vb = at(w.vh, l, 0, d);
       ta.s_seq = d; ta.s_head = dh; ta.s_pos = (int64_t)B * d;
       ta.lo = w.lo_w; ta.hi = w.hi;
-      ta.o = at(w.o, l, t, d); ta.ldo = d;
-      ta.m = at(w.m1, l, t, H); ta.l = at(w.l1, l, t, H);
+      ta.o = sg(w.o, l, t, d); ta.ldo = d;
+      ta.m = sg(w.m1, l, t, H); ta.l = sg(w.l1, l, t, H);
       ta.dout = w.dtmp;
-      float *dq = at(w.dq, l, t, d);
+      float *dq = sg(w.dq, l, t, d);
       ta.dq = dq;
       ta.dkb = at(w.dkh, l, 0, d); ta.dvb = at(w.dvh, l, 0, d);
       ta.cut_lo = det_kv ? chunk_start : 0;
       ta.H = H; ta.dh = dh; ta.scale = scale;
       hipLaunchKernelGGL(k_t_attn_bwd, dim3(B * H), dim3(256), 0, s, ta);
       // da = dq Wq + dk_t Wk + dv_t Wv (dk_t, dv_t complete: every later reader is done)
-      float *daa = at(w.da, l, t, d);
+      float *daa = sg(w.da, l, t, d);
       {
         const float *dqkv[3] = {dq, at(w.dkh, l, t, d), at(w.dvh, l, t, d)};
         const float *wqkv[3] = {wq(l), wk(l), wv(l)};
         t_gemm_sum(dqkv, d, wqkv, d, 3, daa, d, B, d, d, s, w.split);
       }
       // w.dx = d xin, the previous layer's output gradient (saved in its dxf)
-      norm_bwd(at(w.xin, l, t, d), at(w.r1, l, t, 1), g1(l), daa, w.dx, w.dx,
-               l > 0 ? at(w.dxf, l - 1, t, d) : nullptr);
+      norm_bwd(sg(w.xin, l, t, d), sg(w.r1, l, t, 1), g1(l), daa, w.dx, w.dx,
+               l > 0 ? sg(w.dxf, l - 1, t, d) : nullptr);
     }
     // merge: u = g e + (1 - g) s_{t-1}, g = sigmoid(W_g [e ; s] + b_g)
-    float *dz = st(w.dz, t, d);
-    hipLaunchKernelGGL(k_t_merge_bwd, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, st(w.es, t, 2 * d),
-                       st(w.g, t, d), w.dx, dz, w.des, B, d);
+    float *dz = ss(w.dz, t, d);
+    hipLaunchKernelGGL(k_t_merge_bwd, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, ss(w.es, t, 2 * d),
+                       ss(w.g, t, d), w.dx, dz, w.des, B, d);
     t_gemm_go<false, false, true>(dz, d, P_wg, 2 * d, w.des, 2 * d, B, 2 * d, d, s, w.split);
     if (A.de)
       hipLaunchKernelGGL(k_t_copy2d, dim3(blocks_for((size_t)B * d)), dim3(256), 0, s, w.des,
@@ -1233,42 +1255,68 @@ hipError_t run_bptt(const TrainArgs &A, const TrainWs &w, hipStream_t s) {
       // s_0 = s* for every sequence
       t_colsum(w.des + d, nullptr, nullptr, (float *)A.gr->s_star, B, d, (int64_t)2 * d, s, w.split);
     }
-  }
+  };
 
-  // ---- parameter gradients over all T*B rows
-  const int R = (int)TB;
-  for (int l = 0; l < L; ++l) {
-    auto X = [&](float *base, size_t width) { return at(base, l, 0, width); };
-    t_gemm_go<true, false, false>(X(w.dq, d), d, X(w.a, d), d, dwq(l), d, d, d, R, s, w.split);
-    t_gemm_go<true, false, false>(X(w.dkh, d), d, X(w.a, d), d, dwk(l), d, d, d, R, s, w.split);
-    t_gemm_go<true, false, false>(X(w.dvh, d), d, X(w.a, d), d, dwv(l), d, d, d, R, s, w.split);
-    t_gemm_go<true, false, false>(X(w.dxo, d), d, X(w.o, d), d, dwo(l), d, d, d, R, s, w.split);
-    t_gemm_go<true, false, false>(X(w.dqc, d), d, X(w.c, d), d, dwqc(l), d, d, d, R, s, w.split);
-    t_gemm_go<true, false, false>(X(w.dxoc, d), d, X(w.oc, d), d, dwoc(l), d, d, d, R, s, w.split);
-    t_gemm_go<true, false, false>(X(w.dhp, F), F, X(w.f, d), d, dw1(l), d, F, d, R, s, w.split);
-    t_gemm_go<true, false, false>(X(w.dxf, d), d, X(w.h, F), F, dw2(l), F, d, F, R, s, w.split);
-    // gains: dgamma[n] = sum_rows dy[n] * x[n] * r
-    t_colsum(X(w.da, d), X(w.xin, d), at(w.r1, l, 0, 1), dg1(l), R, d, (int64_t)d, s, w.split);
-    t_colsum(X(w.dc, d), X(w.x1, d), at(w.r2, l, 0, 1), dg2(l), R, d, (int64_t)d, s, w.split);
-    t_colsum(X(w.df, d), X(w.x2, d), at(w.r3, l, 0, 1), dg3(l), R, d, (int64_t)d, s, w.split);
+  // ---- parameter gradients over the rows of steps t0 .. t0 + n - 1, added to
+  // the sums of the later segments (the keys' and values' gradient rows of
+  // these steps are complete once the segment's backward is done: every step
+  // that reads them is in it or in a later segment)
+  auto param_grads = [&](int n) {
+    const int R = n * B;
+    for (int l = 0; l < L; ++l) {
+      auto X = [&](float *base, size_t width) { return sg(base, l, t0, width); };
+      t_gemm_go<true, false, true>(X(w.dq, d), d, X(w.a, d), d, dwq(l), d, d, d, R, s, w.split);
+      t_gemm_go<true, false, true>(at(w.dkh, l, t0, d), d, X(w.a, d), d, dwk(l), d, d, d, R, s, w.split);
+      t_gemm_go<true, false, true>(at(w.dvh, l, t0, d), d, X(w.a, d), d, dwv(l), d, d, d, R, s, w.split);
+      t_gemm_go<true, false, true>(X(w.dxo, d), d, X(w.o, d), d, dwo(l), d, d, d, R, s, w.split);
+      t_gemm_go<true, false, true>(X(w.dqc, d), d, X(w.c, d), d, dwqc(l), d, d, d, R, s, w.split);
+      t_gemm_go<true, false, true>(X(w.dxoc, d), d, X(w.oc, d), d, dwoc(l), d, d, d, R, s, w.split);
+      t_gemm_go<true, false, true>(X(w.dhp, F), F, X(w.f, d), d, dw1(l), d, F, d, R, s, w.split);
+      t_gemm_go<true, false, true>(X(w.dxf, d), d, X(w.h, F), F, dw2(l), F, d, F, R, s, w.split);
+      // gains: dgamma[n] = sum_rows dy[n] * x[n] * r
+      t_colsum(X(w.da, d), X(w.xin, d), sg(w.r1, l, t0, 1), dg1(l), R, d, (int64_t)d, s, w.split);
+      t_colsum(X(w.dc, d), X(w.x1, d), sg(w.r2, l, t0, 1), dg2(l), R, d, (int64_t)d, s, w.split);
+      t_colsum(X(w.df, d), X(w.x2, d), sg(w.r3, l, t0, 1), dg3(l), R, d, (int64_t)d, s, w.split);
+    }
+    t_gemm_go<true, false, true>(ss(w.dl, t0, V), V, ss(w.sn, t0, d), d, (float *)A.gr->wout, d, V, d, R, s,
+                                 w.split);
+    t_gemm_go<true, false, true>(ss(w.dz, t0, d), d, ss(w.es, t0, 2 * d), 2 * d, (float *)A.gr->wg, 2 * d, d,
+                                 2 * d, R, s, w.split);
+    t_colsum(ss(w.dz, t0, d), nullptr, nullptr, (float *)A.gr->bg, R, d, (int64_t)d, s, w.split);
+    t_colsum(ss(w.dsn, t0, d), st(w.s, t0, d), ss(w.ro, t0, 1), (float *)A.gr->go, R, d, (int64_t)d, s,
+             w.split);
+  };
+
+  // ---- the call: every step forward once (the last segment's activations
+  // stay in place), then the segments in reverse: recompute, backward, sums
+  const int nseg = (T + S - 1) / S;
+  for (int k = 0; k < nseg; ++k) {
+    t0 = k * S;
+    for (int t = t0; t < std::min(T, t0 + S); ++t) fwd_step(t);
   }
-  t_gemm_go<true, false, false>(w.dl, V, w.sn, d, (float *)A.gr->wout, d, V, d, R, s, w.split);
-  t_gemm_go<true, false, false>(w.dz, d, w.es, 2 * d, (float *)A.gr->wg, 2 * d, d, 2 * d, R, s, w.split);
-  t_colsum(w.dz, nullptr, nullptr, (float *)A.gr->bg, R, d, (int64_t)d, s, w.split);
-  t_colsum(w.dsn, w.s, w.ro, (float *)A.gr->go, R, d, (int64_t)d, s, w.split);
+  hipLaunchKernelGGL(k_t_sum, dim3(1), dim3(64), 0, s, w.lossr, TB, A.loss);
+  for (int k = nseg - 1; k >= 0; --k) {
+    t0 = k * S;
+    const int t1 = std::min(T, t0 + S);
+    if (k < nseg - 1)
+      for (int t = t0; t < t1; ++t) fwd_step(t);
+    for (int t = t1 - 1; t >= t0; --t) bwd_step(t);
+    param_grads(t1 - t0);
+  }
   return hipGetLastError();
 }
 }  // namespace
 
-size_t train_workspace_bytes(const rlt_config &c, int B, int T) {
+size_t train_workspace_bytes(const rlt_config &c, int B, int T, int segment) {
   TrainWs w;
-  return train_layout(c, B, T, &w, nullptr);
+  return train_layout(c, B, T, segment_of(T, segment), &w, nullptr);
 }
 
 hipError_t launch_bptt(const TrainArgs &a, void *ws, hipStream_t s) {
   TrainWs w;
-  train_layout(a.c, a.B, a.T, &w, ws);
-  return run_bptt(a, w, s);
+  const int S = segment_of(a.T, a.segment);
+  train_layout(a.c, a.B, a.T, S, &w, ws);
+  return run_bptt(a, w, S, s);
 }
 
 }  // namespace rlt

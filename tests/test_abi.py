@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding.EXPORTED)
-    assert L.rlt_abi_version() == 1
+    assert L.rlt_abi_version() == 2
 
 
 def test_status_strings():

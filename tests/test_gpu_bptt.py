@@ -44,9 +44,9 @@ def case(cfg, B, T, scale=1.0, index=0, mask_first=0):
     return params, e, mk, mv, tg
 
 
-def compare(cfg, params, e, mk, mv, tg, chunk=0, detach=0, label=""):
+def compare(cfg, params, e, mk, mv, tg, chunk=0, detach=0, label="", segment=0):
     loss, g, de, (dmk, dmv) = binding.rlt_bptt(cfg, params, e, (mk, mv), tg, chunk=chunk,
-                                               detach=detach)
+                                               detach=detach, segment=segment)
     torch.cuda.synchronize()
     names = []
     if detach & binding.RLT_DETACH_S:
@@ -114,6 +114,62 @@ def test_truncated_bptt_matches_oracle(detach):
         assert torch.all(de[:, :3] == 0)
     else:
         assert float(de[:, :3].abs().max()) > 0
+
+
+@pytest.mark.parametrize("segment", [1, 4, 7, 19])
+def test_checkpointed_bptt_matches_full_bitwise_where_fixed(segment):
+    """Activation checkpointing (segment S < T): every step runs forward once,
+    then the segments in reverse are recomputed from their first state and run
+    backward.  The recomputed steps repeat the same kernels on the same inputs,
+    so the loss, the e gradients and the memory gradients are bitwise those of
+    the run that keeps everything; the parameter gradients only regroup their
+    sums over rows by segment (within 1e-5 of the full run's, relative to each
+    tensor's largest entry), and all of it passes the oracle gate.  S = 7 and
+    19 leave a ragged last segment (T = 20)."""
+    cfg = ModelConfig(vocab=200, d_model=128, n_heads=4, n_layers=2, d_ffn=256, window=5,
+                      mem_groups=1, dtype=0)
+    params, e, mk, mv, tg = case(cfg, 3, 20, mask_first=2)
+    full = binding.rlt_bptt(cfg, params, e, (mk, mv), tg)
+    seg = binding.rlt_bptt(cfg, params, e, (mk, mv), tg, segment=segment)
+    torch.cuda.synchronize()
+    assert torch.equal(seg[0], full[0])                       # loss
+    assert torch.equal(seg[2], full[2])                       # d e
+    assert torch.equal(seg[3][0], full[3][0]) and torch.equal(seg[3][1], full[3][1])   # d memory
+    worst = 0.0
+    for k in full[1]:
+        a, b = full[1][k].double(), seg[1][k].double()
+        scale = float(a.abs().max())
+        rel = float((a - b).abs().max()) / scale if scale > 0 else float((a - b).abs().max())
+        worst = max(worst, rel)
+        assert rel <= 1e-5, (k, rel)
+    say(f"[bptt] segment {segment}: parameter gradients within {worst:.2e} of the full run")
+    compare(cfg, params, e, mk, mv, tg, segment=segment, label=f"segment {segment}")
+
+
+def test_checkpointed_truncated_bptt():
+    """Segments that cut across truncation chunks (chunk 3, segment 2, s and
+    the cache detached): the same exact zeros and the oracle gate."""
+    cfg = ModelConfig(vocab=11, d_model=32, n_heads=2, n_layers=2, d_ffn=64, window=3,
+                      mem_groups=2, dtype=0)
+    params, e, mk, mv, tg = case(cfg, 2, 7, scale=10.0, mask_first=3)
+    de, _ = compare(cfg, params, e, mk, mv, tg, chunk=3, detach=3, segment=2,
+                    label="chunk 3, detach s and kv, segment 2")
+    assert torch.all(de[:, :3] == 0)
+
+
+def test_checkpointing_shrinks_the_workspace():
+    """The reference-depth model (fp32 for training) at 8 sequences x 256
+    steps: keeping every step needs about 28 GB, 16-step segments under 5 GB."""
+    from recurrent_decode_step_amd.configs import REFDEPTH
+    cfg = REFDEPTH.model.with_(dtype=0)
+    L = binding.load_library()
+    cc = binding.make_config(cfg)
+    full = L.rlt_bptt_workspace_bytes(binding.C.byref(cc), 8, 256)
+    seg = L.rlt_bptt_workspace_bytes_segmented(binding.C.byref(cc), 8, 256, 16)
+    assert full == L.rlt_bptt_workspace_bytes_segmented(binding.C.byref(cc), 8, 256, 0)
+    say(f"[bptt] workspace at reference depth, 8 x 256 steps: {full / 1e9:.1f} GB, "
+        f"16-step segments {seg / 1e9:.1f} GB")
+    assert seg < full / 3
 
 
 def test_memory_with_unaligned_rows_is_rejected():
