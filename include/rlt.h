@@ -408,6 +408,28 @@ rlt_status rlt_encode(const rlt_encoder *enc, rlt_encoder_state *es, int32_t n,
                       const int32_t *host_slots, int32_t T, const int32_t *dev_tokens,
                       void *dev_e, const rlt_memory *mem, void *stream);
 
+/* Autoregressive generation with the causal encoder in the loop [Tutorial,
+ * "Autoregressive generation": sample, encode the sampled token
+ * incrementally, consume it once]: rlt_generate with step 3 replaced by
+ * rlt_encode of each slot's new token (T = 1, slots 0..B-1 of es): the
+ * encoder attends to its cache of the slot's earlier tokens, writes e_t and
+ * memory entry pos of every group (pos = the slot's position before the
+ * step) into the caller's memory, and advances es.  Before the call every
+ * slot must have as many tokens encoded as consumed (es position == st
+ * position, e.g. after prefill: rlt_encode of the prompt, then
+ * rlt_run_sequence over its e rows); RLT_ERR_RANGE otherwise or when a
+ * position would pass either state's max_tokens or the memory capacity.
+ * enc must belong to m (RLT_ERR_INVALID_ARG), es to m's version
+ * (RLT_ERR_STALE), es->batch >= B and its max_rows >= B (RLT_ERR_SHAPE).
+ * The state, logits and memory entries are bitwise those of encoding the
+ * generated tokens in one rlt_encode call and running rlt_run_sequence over
+ * their e rows. */
+rlt_status rlt_generate_encoded(const rlt_model *m, rlt_state *st, int32_t n_steps,
+                                const float *dev_logits0, const rlt_encoder *enc,
+                                rlt_encoder_state *es, const rlt_memory *mem,
+                                const rlt_sampling *smp, const float *dev_u, int32_t *dev_tokens,
+                                float *dev_logprob, float *dev_logits_last, void *stream);
+
 /* Encoder kernel timing, as rlt_profile_begin with every call one step:
  * RLT_E_GEMM = the token-parallel GEMMs, RLT_E_ATTN = causal attention,
  * RLT_E_OTHER = embedding and RMSNorm.  Collect returns the recorded launch

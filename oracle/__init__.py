@@ -9,12 +9,12 @@ from .rlt_oracle import (Model, SeqState, round_bf16, initial_state, state_from_
                          copy_state, decoder_step, run_sequence, token_log_prob, score_sequence,
                          sampling_weights, sample_token, generate)
 from .brute import brute_force_run
-from .encoder import Encoder, encode, prefill
+from .encoder import Encoder, encode, prefill, generate_encoded
 from . import bptt
 from .parallel import parallel_swa_pass
 
 __all__ = ["Model", "SeqState", "round_bf16", "initial_state", "state_from_arrays",
            "copy_state", "decoder_step", "run_sequence", "token_log_prob", "score_sequence",
            "sampling_weights", "sample_token", "generate",
-           "brute_force_run", "Encoder", "encode", "prefill", "bptt",
+           "brute_force_run", "Encoder", "encode", "prefill", "generate_encoded", "bptt",
            "parallel_swa_pass"]

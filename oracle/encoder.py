@@ -125,3 +125,50 @@ def prefill(enc: Encoder, states, tokens, capacity=None):
         mem_v[:, i, :, :T] = r["mem_v"]
     logits = run_sequence(m, states, e, mem_k, mem_v)
     return logits, e, mem_k, mem_v
+
+
+def generate_encoded(enc: Encoder, states, prompts, logits0, mem_k, mem_v, temperature, top_k, u,
+                     follow=None):
+    """Autoregressive generation with the causal encoder in the loop
+    [Tutorial, "Autoregressive generation": sample from the preceding state's
+    distribution, encode the sampled token incrementally, consume it through
+    the decoder exactly once].  For every step and sequence: sample with
+    uniform u[i][j] (or take follow[i][j]) and record the token and its
+    log-probability; the token becomes the next position p of its sequence
+    (p = the decoder state's position before the step): e_p and memory entry
+    p of every group are the encoder's output at p given the sequence's
+    tokens 0..p (the encoder over the whole list; by causality the earlier
+    rows are those of the shorter list), written into mem_k/mem_v
+    [G][n][H][cap][dh]; then one decoder step consumes e_p.  prompts [n][P]:
+    the tokens already encoded and consumed (states at position P).  Returns
+    (tokens, log-probs, logits of the last step)."""
+    import math
+    from .rlt_oracle import decoder_step, sample_token, sampling_weights
+    m = enc.m
+    n = len(states)
+    steps = np.asarray(u).shape[1]
+    seqs = [list(int(t) for t in p) for p in np.asarray(prompts)]
+    toks = np.zeros((n, steps), dtype=np.int64)
+    lps = np.zeros((n, steps), dtype=np.float64)
+    logits = np.asarray(logits0, dtype=np.float64)
+    for j in range(steps):
+        for i in range(n):
+            tok, lp = sample_token(logits[i], temperature, top_k, float(u[i][j]))
+            if follow is not None:
+                tok = int(follow[i][j])
+                z = logits[i]
+                w, _ = sampling_weights(z, temperature, top_k)
+                lp = float((z[tok] - z.max()) / temperature - math.log(w.sum()))
+            toks[i, j], lps[i, j] = tok, lp
+        e_rows = np.empty((n, m.d), dtype=m.dt)
+        for i, st in enumerate(states):
+            seqs[i].append(int(toks[i, j]))
+            p = len(seqs[i]) - 1
+            if st.pos != p:
+                raise ValueError("the decoder state must have consumed every encoded token")
+            r = encode(enc, seqs[i])
+            e_rows[i] = r["e"][p]
+            mem_k[:, i, :, p] = r["mem_k"][:, :, p]
+            mem_v[:, i, :, p] = r["mem_v"][:, :, p]
+        logits = decoder_step(m, states, e_rows, mem_k, mem_v).astype(np.float64)
+    return toks, lps, logits

@@ -30,7 +30,7 @@ EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_by
             "rlt_state_destroy", "rlt_state_reset", "rlt_decoder_step", "rlt_decoder_step_noalloc",
             "rlt_run_sequence", "rlt_persistent_workspace_bytes", "rlt_run_sequence_persistent",
             "rlt_persistent_check", "rlt_persistent_test_stall",
-            "rlt_score_sequence", "rlt_generate",
+            "rlt_score_sequence", "rlt_generate", "rlt_generate_encoded",
             "rlt_state_position", "rlt_snapshot_bytes", "rlt_state_export", "rlt_state_import",
             "rlt_profile_begin", "rlt_profile_collect",
             "rlt_encoder_bytes", "rlt_encoder_create", "rlt_encoder_destroy",
@@ -114,6 +114,8 @@ def load_library(path: str = LIB_PATH):
         "rlt_persistent_check": (i32, [vp, vp]),
         "rlt_persistent_test_stall": (None, [i32]),
         "rlt_score_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, vp, vp]),
+        "rlt_generate_encoded": (i32, [vp, vp, i32, vp, vp, vp, P(rlt_memory), P(rlt_sampling),
+                                       vp, vp, vp, vp, vp]),
         "rlt_generate": (i32, [vp, vp, i32, vp, P(rlt_encoder_table), P(rlt_memory), P(rlt_sampling),
                                vp, vp, vp, vp, vp]),
         "rlt_state_position": (i32, [vp, i32]),
@@ -636,3 +638,28 @@ def peak_mfma(shape: int, iters: int, sink: torch.Tensor, reps: int = 5, stream=
                                         sink.numel() * sink.element_size(), C.byref(out),
                                         _stream(stream)))
     return out.value
+
+
+def rlt_generate_encoded(model: Model, state: State, logits0: torch.Tensor, encoder: "Encoder",
+                         enc_state: "EncoderState", memory, temperature: float, top_k: int,
+                         u: torch.Tensor, stream=None):
+    """Generate u.shape[1] tokens for all B slots with the causal encoder in
+    the loop (rlt_generate_encoded): each sampled token is encoded from the
+    encoder cache of its slot's earlier tokens.  The encoder state must have
+    as many tokens encoded per slot as the decoder state has consumed.
+    Returns (tokens [B][n] int32, log-probs [B][n] fp32, last logits [B][V])."""
+    lib = load_library()
+    B, n = u.shape
+    u = u.to(dtype=torch.float32).contiguous()
+    logits0 = logits0.to(dtype=torch.float32).contiguous()
+    dev = u.device
+    tokens = torch.empty((B, n), dtype=torch.int32, device=dev)
+    lp = torch.empty((B, n), dtype=torch.float32, device=dev)
+    last = torch.empty((B, model.cfg.vocab), dtype=torch.float32, device=dev)
+    mem = memory if isinstance(memory, rlt_memory) else memory_view(*memory)
+    smp = rlt_sampling(float(temperature), int(top_k))
+    _check(lib.rlt_generate_encoded(model.handle, state.handle, n, logits0.data_ptr(),
+                                    encoder.handle, enc_state.handle, C.byref(mem), C.byref(smp),
+                                    u.data_ptr(), tokens.data_ptr(), lp.data_ptr(), last.data_ptr(),
+                                    _stream(stream)))
+    return tokens, lp, last

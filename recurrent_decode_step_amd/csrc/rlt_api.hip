@@ -211,6 +211,7 @@ struct rlt_state {
   char *xg, *qbuf, *obuf, *hbuf;
   float *lscratch;           // [B][V] fp32 logits of a scored or generated step
   char *escratch;            // [B][d] e rows of generated tokens
+  int *tok_dev;              // [B] the tokens of a generated step, contiguous
   std::vector<int> host_pos;
   std::vector<int> staged;   // slot list currently in slots_dev (empty: none)
   std::vector<int> staged_order;   // row order currently in order_dev
@@ -295,6 +296,7 @@ size_t state_layout(const rlt_config &c, rlt_state *st, void *base, int B) {
   st->hbuf = ar.take<char>(rows16 * c.d_ffn * es);
   st->lscratch = ar.take<float>((size_t)B * c.vocab * 4);
   st->escratch = ar.take<char>((size_t)B * d * es);
+  st->tok_dev = ar.take<int>((size_t)B * 4);
   return align256(ar.off);
 }
 
@@ -1480,6 +1482,7 @@ rlt_status rlt_generate(const rlt_model *m, rlt_state *st, int32_t n_steps,
     sa.ld_u = n_steps;
     sa.tokens = dev_tokens + j;
     sa.ld_tok = n_steps;
+    sa.tokens2 = nullptr;
     sa.logprob = dev_logprob + j;
     sa.ld_lp = n_steps;
     sa.V = V;
@@ -1731,6 +1734,10 @@ PGemmArgs pgemm_args(const PackedMat &w, const void *act, int64_t lda, const Enc
   return a;
 }
 
+rlt_status enqueue_encode(const rlt_encoder *enc, rlt_encoder_state *es, const std::vector<int> &slots,
+                          int T, const int32_t *dev_tokens, void *dev_e, const rlt_memory *mem,
+                          hipStream_t s);
+
 }  // namespace
 
 extern "C" {
@@ -1882,8 +1889,22 @@ rlt_status rlt_encode(const rlt_encoder *enc, rlt_encoder_state *es, int32_t n,
   }
   if ((uintptr_t)dev_e % 16) return fail(RLT_ERR_SHAPE, "dev_e must be 16-byte aligned");
   if ((rs = device_health()) != RLT_OK) return rs;
+  return enqueue_encode(enc, es, slots, T, dev_tokens, dev_e, mem, static_cast<hipStream_t>(stream));
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+// The device work of rlt_encode for validated arguments: the listed slots'
+// next T tokens (dev_tokens [n][T]), e rows to dev_e (null: the state's
+// scratch), memory entries written, positions advanced.
+rlt_status enqueue_encode(const rlt_encoder *enc, rlt_encoder_state *es, const std::vector<int> &slots,
+                          int T, const int32_t *dev_tokens, void *dev_e, const rlt_memory *mem,
+                          hipStream_t s) {
+  rlt_status rs;
+  const rlt_model *m = enc->m;
+  const rlt_config &c = m->cfg;
+  const int n = (int)slots.size();
   const int L = c.n_layers, d = c.d_model, F = c.d_ffn, H = c.n_heads, dh = c.head_dim;
   const int esz = esize_of(c.dtype);
   const int R = n * T;
@@ -1996,6 +2017,10 @@ rlt_status rlt_encode(const rlt_encoder *enc, rlt_encoder_state *es, int32_t n,
   return ok();
 }
 
+}  // namespace
+
+extern "C" {
+
 rlt_status rlt_encoder_profile_begin(rlt_encoder_state *es, int32_t class_mask,
                                      int32_t max_launches) {
   if (!es) return fail(RLT_ERR_INVALID_ARG, "encoder state is NULL");
@@ -2007,6 +2032,74 @@ rlt_status rlt_encoder_profile_collect(rlt_encoder_state *es, int32_t kclass, do
   if (!es) return fail(RLT_ERR_INVALID_ARG, "encoder state is NULL");
   if (kclass < 0 || kclass >= RLT_E_NCLASSES) return fail(RLT_ERR_INVALID_ARG, "bad kernel class");
   return prof_collect(es->plog, kclass, total_ms, launches, bytes_moved, flops);
+}
+
+rlt_status rlt_generate_encoded(const rlt_model *m, rlt_state *st, int32_t n_steps,
+                                const float *dev_logits0, const rlt_encoder *enc,
+                                rlt_encoder_state *es, const rlt_memory *mem,
+                                const rlt_sampling *smp, const float *dev_u, int32_t *dev_tokens,
+                                float *dev_logprob, float *dev_logits_last, void *stream) {
+  rlt_status rs;
+  if ((rs = check_state(m, st)) != RLT_OK) return rs;
+  if (n_steps < 1) return fail(RLT_ERR_INVALID_ARG, "n_steps must be >= 1");
+  if (!dev_logits0 || !enc || !es || !smp || !dev_u || !dev_tokens || !dev_logprob)
+    return fail(RLT_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (enc->m != m) return fail(RLT_ERR_INVALID_ARG, "the encoder belongs to another model");
+  if (es->version != m->version)
+    return fail(RLT_ERR_STALE, "encoder state built for model version %llu, model is version %llu",
+                (unsigned long long)es->version, (unsigned long long)m->version);
+  if (!(smp->temperature > 0.f) || smp->top_k < 1)
+    return fail(RLT_ERR_INVALID_ARG, "temperature must be > 0 and top_k >= 1");
+  const int B = st->B;
+  if (es->B < B) return fail(RLT_ERR_SHAPE, "encoder state has %d slots < %d", es->B, B);
+  if (es->max_rows < B)
+    return fail(RLT_ERR_SHAPE, "encoder state max_rows %d < %d slots", es->max_rows, B);
+  for (int b = 0; b < B; ++b) {
+    // the token sampled after position p is encoded at encoder position p
+    if (es->host_pos[b] != st->host_pos[b])
+      return fail(RLT_ERR_RANGE, "slot %d: %d tokens encoded but %d consumed", b, es->host_pos[b],
+                  st->host_pos[b]);
+    if ((long long)es->host_pos[b] + n_steps > es->max_tokens)
+      return fail(RLT_ERR_RANGE, "slot %d would pass the encoder's max_tokens %d", b, es->max_tokens);
+  }
+  if ((rs = check_memory(m, mem, B - 1)) != RLT_OK) return rs;
+  if ((rs = check_positions(st, mem, B, nullptr, n_steps)) != RLT_OK) return rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const rlt_config &c = m->cfg;
+  const int V = c.vocab, d = c.d_model;
+  std::vector<int> slots(B);
+  for (int b = 0; b < B; ++b) slots[b] = b;
+  for (int j = 0; j < n_steps; ++j) {
+    // 1-2: sample from the preceding state's logits, record token and log-prob
+    SampleArgs sa;
+    sa.logits = j == 0 ? dev_logits0 : st->lscratch;
+    sa.ld = V;
+    sa.u = dev_u + j;
+    sa.ld_u = n_steps;
+    sa.tokens = dev_tokens + j;
+    sa.ld_tok = n_steps;
+    sa.tokens2 = st->tok_dev;
+    sa.logprob = dev_logprob + j;
+    sa.ld_lp = n_steps;
+    sa.V = V;
+    sa.top_k = std::min(smp->top_k, V);
+    sa.inv_temp = 1.0f / smp->temperature;
+    Prof ps(st->plog, RLT_K_EXTRA, s);
+    hipError_t e = launch_sample(sa, B, s);
+    if (e != hipSuccess) return hip_fail(e, "sample launch");
+    ps.done((double)B * V * 4 * 2);
+    // 3: the causal encoder over the new token of every slot (its cache holds
+    // the earlier ones): e row to the state's scratch, memory entries written
+    if ((rs = enqueue_encode(enc, es, slots, 1, st->tok_dev, st->escratch, mem, s)) != RLT_OK)
+      return rs;
+    // 4: consume it once
+    float *lg = (j == n_steps - 1 && dev_logits_last) ? dev_logits_last : st->lscratch;
+    if ((rs = enqueue_step(m, st, state_scratch(st), B, true, nullptr, st->escratch, d, mem, lg,
+                           V, s)) != RLT_OK)
+      return rs;
+  }
+  return ok();
 }
 
 }  // extern "C"

@@ -107,6 +107,7 @@ struct SampleArgs {
   const float *logits; int64_t ld;          // [n][ld] fp32 logits of the preceding state
   const float *u; int64_t ld_u;             // uniform in [0, 1) of row i at u[i * ld_u]
   int32_t *tokens; int64_t ld_tok;          // sampled token of row i at tokens[i * ld_tok]
+  int32_t *tokens2;                         // and at tokens2[i] (null: not written)
   float *logprob; int64_t ld_lp;            // its log-probability under the sampling distribution
   int V; int top_k; float inv_temp;
 };

@@ -1215,6 +1215,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(const SampleArgs a) {
         if (order_key(z[v]) >= kth) { tok = v; break; }
     }
     a.tokens[(size_t)i * a.ld_tok] = tok;
+    if (a.tokens2) a.tokens2[i] = tok;
     a.logprob[(size_t)i * a.ld_lp] = (z[tok] - mx) * a.inv_temp - logf(tot);
   }
 }

@@ -206,3 +206,61 @@ def test_prefill_runs_decoder_over_every_prompt_token():
     for i in range(2):
         r = oracle.encode(enc, tok[i])
         np.testing.assert_array_equal(r["mem_k"], mk[:, i])
+
+
+def _gen_case(cfg, n=2, P=3, steps=4):
+    enc, params, eparams = enc_model(cfg, precision="fp64")
+    prompts = synth.token_ids(n, P, cfg.vocab, index=11)
+    cap = P + steps
+    st = [oracle.initial_state(enc.m) for _ in range(n)]
+    logits, _, mk, mv = oracle.prefill(enc, st, prompts, capacity=cap)
+    u = synth.uniforms((n, steps), index=3).numpy()
+    return enc, prompts, st, logits[:, -1], mk, mv, u
+
+
+def test_encoded_generation_consumes_each_token_once():
+    """Generation with the encoder in the loop leaves the decoder where prompt
+    prefill over the prompt plus the generated tokens leaves it: the same last
+    logits and memory entries (each sampled token encoded as the next position
+    of its sequence and consumed exactly once) [Tutorial, "Autoregressive
+    generation" and "Prompt prefill"]."""
+    cfg = tiny_cfg(mem_groups=2, n_layers=2)
+    enc, prompts, st, logits0, mk, mv, u = _gen_case(cfg)
+    toks, lps, last = oracle.generate_encoded(enc, st, prompts, logits0, mk, mv, 0.8, 5, u)
+    full = np.concatenate([prompts, toks], axis=1)
+    st2 = [oracle.initial_state(enc.m) for _ in range(2)]
+    logits, _, mk2, mv2 = oracle.prefill(enc, st2, full)
+    np.testing.assert_allclose(last, logits[:, -1], rtol=0, atol=1e-10)
+    np.testing.assert_allclose(mk, mk2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(mv, mv2, rtol=0, atol=1e-12)
+    assert all(s.pos == full.shape[1] for s in st)
+
+
+def test_encoded_generation_records_the_behaviour_distribution():
+    """Every token is the inverse-CDF draw of its uniform under the preceding
+    state's distribution, and its recorded log-probability is that
+    distribution's at the token (the preceding logits rebuilt by prefill)."""
+    cfg = tiny_cfg()
+    enc, prompts, st, logits0, mk, mv, u = _gen_case(cfg, steps=5)
+    temp, k = 1.3, 4
+    toks, lps, _ = oracle.generate_encoded(enc, st, prompts, logits0, mk, mv, temp, k, u)
+    full = np.concatenate([prompts, toks], axis=1)
+    st2 = [oracle.initial_state(enc.m) for _ in range(2)]
+    logits, _, _, _ = oracle.prefill(enc, st2, full)
+    P = prompts.shape[1]
+    for i in range(2):
+        for j in range(toks.shape[1]):
+            z = logits[i, P - 1 + j]                      # the state before token j
+            tok, lp = oracle.sample_token(z, temp, k, float(u[i, j]))
+            assert tok == toks[i, j]
+            w, _ = oracle.sampling_weights(z, temp, k)
+            assert abs(lps[i, j] - np.log(w[tok] / w.sum())) < 1e-9
+            assert abs(lp - lps[i, j]) < 1e-9
+
+
+def test_encoded_generation_needs_the_states_at_the_prompt_end():
+    cfg = tiny_cfg()
+    enc, prompts, st, logits0, mk, mv, u = _gen_case(cfg)
+    st[1].pos += 1
+    with pytest.raises(ValueError):
+        oracle.generate_encoded(enc, st, prompts, logits0, mk, mv, 1.0, 5, u)

@@ -309,3 +309,107 @@ def test_refdepth_full_prompt_sampled_rows():
             rel = rel_l2(got, want)
             say(f"[encoder full] seq {bsel} {name}[:{P}] rel-L2 {rel:.2e}")
             assert rel <= 2e-2, (bsel, name, rel)
+
+
+def _valid_draw(z, temperature, top_k, u, tok, rel=1e-3):
+    """tok is a valid inverse-CDF draw for u under the float64 distribution:
+    its weight is positive and u * total lies in [cum(tok - 1), cum(tok)] up to
+    rel * total (the library accumulates in fp32)."""
+    w, _ = oracle.sampling_weights(z, temperature, top_k)
+    c = np.cumsum(w)
+    tot = c[-1]
+    lo = c[tok - 1] if tok > 0 else 0.0
+    return w[tok] > 0 and lo - rel * tot <= u * tot <= c[tok] + rel * tot
+
+
+def _prefilled(cfg, B, P, n, index=5):
+    params, eparams, model, enc, es, mk, mv = setup(cfg, B, P + n, B * (P + n))
+    prompts = synth.token_ids(B, P, cfg.vocab, index=index)
+    e = binding.rlt_encode(enc, es, torch.from_numpy(prompts).to(DEV), (mk, mv))
+    st = binding.State(model, B, P + n)
+    pre = binding.rlt_run_sequence(model, st, e, (mk, mv), logits_mode=binding.RLT_LOGITS_LAST)
+    return params, eparams, model, enc, es, mk, mv, prompts, st, pre
+
+
+def test_generate_encoded_matches_oracle_f32():
+    """Prefill, then 8 tokens generated with the causal encoder in the loop
+    [Tutorial, "Autoregressive generation": sample, encode the token
+    incrementally, consume it once]: every GPU token is a valid draw under the
+    oracle's logits (the oracle replays the GPU's tokens), log-probabilities
+    agree within 2e-4 / temperature, the last logits and the memory entries the
+    encoder wrote within 1e-4."""
+    cfg = ModelConfig(vocab=64, d_model=64, n_heads=2, n_layers=2, d_ffn=128, window=4,
+                      mem_groups=2, dtype=0)
+    B, P, n, temp, topk = 3, 5, 8, 0.9, 10
+    params, eparams, model, enc, es, mk, mv, prompts, st, pre = _prefilled(cfg, B, P, n)
+    u = synth.uniforms((B, n), index=6)
+    say("[generate encoded f32]")
+    tok, lp, last = binding.rlt_generate_encoded(model, st, pre, enc, es, (mk, mv), temp, topk,
+                                                 u.to(DEV))
+    torch.cuda.synchronize()
+    tok, lp, last = tok.cpu().numpy(), lp.cpu().numpy(), f64(last)
+    for b in range(B):
+        assert st.position(b) == P + n and es.position(b) == P + n
+    ref_enc = oracle_encoder(cfg, params, eparams, "fp32")
+    states = [oracle.initial_state(ref_enc.m) for _ in range(B)]
+    ologits, _, rmk, rmv = oracle.prefill(ref_enc, states, prompts, capacity=P + n)
+    logits = ologits[:, -1].astype(np.float64)
+    seqs = prompts.copy()
+    for j in range(n):
+        for b in range(B):
+            assert _valid_draw(logits[b], temp, topk, float(u[b, j]), int(tok[b, j])), (j, b)
+        _, olp, logits = oracle.generate_encoded(ref_enc, states, seqs, logits, rmk, rmv, temp,
+                                                 topk, u[:, j:j + 1].numpy(),
+                                                 follow=tok[:, j:j + 1])
+        seqs = np.concatenate([seqs, tok[:, j:j + 1]], axis=1)
+        assert np.max(np.abs(olp[:, 0] - lp[:, j])) <= 2e-4 / temp
+    err = float(np.abs(logits - last).max())
+    merr = max(float(np.abs(f64(mk) - rmk).max()), float(np.abs(f64(mv) - rmv).max()))
+    say(f"  last logits max |delta| {err:.2e}, memory entries {merr:.2e}")
+    assert err <= 1e-4 and merr <= 1e-4
+
+
+def test_generate_encoded_equals_encode_then_run_sequence_bitwise():
+    """bf16: generating n tokens with the encoder in the loop leaves the
+    decoder state, the last logits and the memory exactly where encoding those
+    n tokens in one rlt_encode call and running rlt_run_sequence over their e
+    rows leaves them (chunking never changes the encoder's values, and each
+    token is consumed once)."""
+    cfg = ModelConfig(vocab=96, d_model=128, n_heads=2, n_layers=2, d_ffn=256, window=4,
+                      mem_groups=1, dtype=1)
+    B, P, n = 4, 6, 5
+    params, eparams, model, enc, es, mk, mv, prompts, st, pre = _prefilled(cfg, B, P, n)
+    u = synth.uniforms((B, n), index=7).to(DEV)
+    say("[generate encoded bf16 bitwise]")
+    tok, lp, last = binding.rlt_generate_encoded(model, st, pre, enc, es, (mk, mv), 1.0, 40, u)
+    assert torch.isfinite(lp).all()
+    # the replay: a second encoder state and decoder state from the same prompt
+    es2 = binding.EncoderState(enc, B, P + n, B * (P + n))
+    mk2, mv2 = torch.zeros_like(mk), torch.zeros_like(mv)
+    e_pre = binding.rlt_encode(enc, es2, torch.from_numpy(prompts).to(DEV), (mk2, mv2))
+    st2 = binding.State(model, B, P + n)
+    binding.rlt_run_sequence(model, st2, e_pre, (mk2, mv2), logits_mode=binding.RLT_LOGITS_NONE)
+    e_gen = binding.rlt_encode(enc, es2, tok, (mk2, mv2))
+    rep = binding.rlt_run_sequence(model, st2, e_gen, (mk2, mv2))
+    torch.cuda.synchronize()
+    assert torch.equal(rep[:, -1], last)
+    assert torch.equal(mk, mk2) and torch.equal(mv, mv2)
+    snap_a = binding.rlt_state_export(model, st, list(range(B)))
+    snap_b = binding.rlt_state_export(model, st2, list(range(B)))
+    assert torch.equal(snap_a, snap_b)
+
+
+def test_generate_encoded_needs_matching_positions():
+    """The encoder must hold exactly the tokens the decoder consumed: a slot
+    whose decoder state is one token ahead is a range error, found before any
+    device work."""
+    cfg = ModelConfig(vocab=64, d_model=64, n_heads=2, n_layers=1, d_ffn=128, window=4,
+                      mem_groups=1, dtype=0)
+    B, P, n = 2, 3, 2
+    params, eparams, model, enc, es, mk, mv, prompts, st, pre = _prefilled(cfg, B, P, n + 1)
+    binding.rlt_decoder_step(model, st, torch.zeros((B, cfg.d_model), device=DEV), (mk, mv))
+    u = synth.uniforms((B, n), index=8).to(DEV)
+    with pytest.raises(binding.RLTError) as ex:
+        binding.rlt_generate_encoded(model, st, pre, enc, es, (mk, mv), 1.0, 5, u)
+    assert ex.value.status == binding.RLT_ERR_RANGE
+    assert es.position(0) == P and st.position(0) == P + 1
