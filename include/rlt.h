@@ -430,6 +430,33 @@ rlt_status rlt_generate_encoded(const rlt_model *m, rlt_state *st, int32_t n_ste
                                 const rlt_sampling *smp, const float *dev_u, int32_t *dev_tokens,
                                 float *dev_logprob, float *dev_logits_last, void *stream);
 
+/* Exact prefix snapshot of the encoder cache [Article, "Multi-Turn Serving":
+ * the snapshot of a prefix carries the encoder's cached state with the
+ * decoder's; Princeton, training/serving paragraph].  With the decoder's
+ * record (rlt_state_export) and the memory entries (caller buffers, copied by
+ * the caller), a conversation resumes in another slot or process bitwise.
+ * Per slot one record of rlt_encoder_snapshot_bytes(cfg, capacity, 1) bytes:
+ *   256-byte header: uint32 magic 0x454C5452, format 1, d_model, n_heads,
+ *         head_dim, n_layers, dtype, position p (tokens encoded), capacity,
+ *         0, then the model version as two uint32 (low, high); rest zero
+ *   then  K: [L][H][capacity][dh] model dtype, positions 0..p-1, later zero
+ *   then  V: same layout as K
+ * (each of K and V starts at a 256-byte boundary).  Export: RLT_ERR_RANGE if
+ * a listed slot holds more than `capacity` positions.  Import checks every
+ * header first and changes nothing on a mismatch (RLT_ERR_CONVENTION: not a
+ * record, another shape, dtype, capacity or model version, or a position past
+ * the state's max_tokens); it synchronises the stream once to read them.
+ * Both: RLT_ERR_STALE for an encoder state of another model version,
+ * RLT_ERR_INVALID_ARG for bad or repeated slots, RLT_ERR_SHAPE for a
+ * dev_snap that is not 256-byte aligned. */
+size_t rlt_encoder_snapshot_bytes(const rlt_config *cfg, int32_t capacity, int32_t n);
+rlt_status rlt_encoder_state_export(const rlt_encoder *enc, rlt_encoder_state *es, int32_t n,
+                                    const int32_t *host_slots, int32_t capacity, void *dev_snap,
+                                    void *stream);
+rlt_status rlt_encoder_state_import(const rlt_encoder *enc, rlt_encoder_state *es, int32_t n,
+                                    const int32_t *host_slots, int32_t capacity,
+                                    const void *dev_snap, void *stream);
+
 /* Encoder kernel timing, as rlt_profile_begin with every call one step:
  * RLT_E_GEMM = the token-parallel GEMMs, RLT_E_ATTN = causal attention,
  * RLT_E_OTHER = embedding and RMSNorm.  Collect returns the recorded launch

@@ -37,6 +37,7 @@ EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_by
             "rlt_encoder_state_bytes", "rlt_encoder_state_init", "rlt_encoder_state_destroy",
             "rlt_encoder_state_reset", "rlt_encoder_position", "rlt_encode",
             "rlt_encoder_profile_begin", "rlt_encoder_profile_collect",
+            "rlt_encoder_snapshot_bytes", "rlt_encoder_state_export", "rlt_encoder_state_import",
             "rlt_bptt_workspace_bytes", "rlt_bptt_workspace_bytes_segmented", "rlt_bptt",
             "rlt_peak_bandwidth", "rlt_peak_mfma")
 
@@ -134,6 +135,9 @@ def load_library(path: str = LIB_PATH):
         "rlt_encoder_position": (i32, [vp, i32]),
         "rlt_encode": (i32, [vp, vp, i32, P(i32), i32, vp, vp, P(rlt_memory), vp]),
         "rlt_encoder_profile_begin": (i32, [vp, i32, i32]),
+        "rlt_encoder_snapshot_bytes": (sz, [P(rlt_config), i32, i32]),
+        "rlt_encoder_state_export": (i32, [vp, vp, i32, P(i32), i32, vp, vp]),
+        "rlt_encoder_state_import": (i32, [vp, vp, i32, P(i32), i32, vp, vp]),
         "rlt_encoder_profile_collect": (i32, [vp, i32, P(C.c_double), P(i32), P(C.c_double),
                                               P(C.c_double)]),
         "rlt_bptt_workspace_bytes": (sz, [P(rlt_config), i32, i32]),
@@ -663,3 +667,29 @@ def rlt_generate_encoded(model: Model, state: State, logits0: torch.Tensor, enco
                                     u.data_ptr(), tokens.data_ptr(), lp.data_ptr(), last.data_ptr(),
                                     _stream(stream)))
     return tokens, lp, last
+
+
+def encoder_snapshot_bytes(cfg: ModelConfig, capacity: int, n: int) -> int:
+    return load_library().rlt_encoder_snapshot_bytes(C.byref(make_config(cfg)), capacity, n)
+
+
+def rlt_encoder_state_export(encoder: "Encoder", es: "EncoderState", slots, capacity: int,
+                             stream=None) -> torch.Tensor:
+    """Encoder-cache records of the listed slots (rlt_encoder_state_export),
+    `capacity` positions each; returns a uint8 device tensor."""
+    lib = load_library()
+    arr, n = _slots_arg(slots)
+    nbytes = encoder_snapshot_bytes(encoder.model.cfg, capacity, n)
+    snap = torch.empty(nbytes, dtype=torch.uint8, device=encoder.buf.device)
+    _check(lib.rlt_encoder_state_export(encoder.handle, es.handle, n, arr, capacity,
+                                        snap.data_ptr(), _stream(stream)))
+    return snap
+
+
+def rlt_encoder_state_import(encoder: "Encoder", es: "EncoderState", snap: torch.Tensor, slots,
+                             capacity: int, stream=None):
+    """Record i of snap into slot slots[i] (rlt_encoder_state_import)."""
+    lib = load_library()
+    arr, n = _slots_arg(slots)
+    _check(lib.rlt_encoder_state_import(encoder.handle, es.handle, n, arr, capacity,
+                                        snap.data_ptr(), _stream(stream)))

@@ -2034,6 +2034,155 @@ rlt_status rlt_encoder_profile_collect(rlt_encoder_state *es, int32_t kclass, do
   return prof_collect(es->plog, kclass, total_ms, launches, bytes_moved, flops);
 }
 
+size_t rlt_encoder_snapshot_bytes(const rlt_config *cfg, int32_t capacity, int32_t n) {
+  if (check_config(cfg) != RLT_OK || capacity < 0 || n < 1) return 0;
+  const size_t sec = align256((size_t)cfg->n_layers * cfg->n_heads * capacity * cfg->head_dim *
+                              esize_of(cfg->dtype));
+  return (256 + 2 * sec) * (size_t)n;
+}
+
+}  // extern "C"
+
+namespace {
+constexpr uint32_t kEncSnapMagic = 0x454C5452u;   // encoder-cache record
+
+// slot list checks shared by the encoder snapshot calls; the slots and the
+// given positions are staged in es's table
+rlt_status enc_snap_stage(rlt_encoder_state *es, int n, const int32_t *host_slots,
+                          const std::vector<int> &pos, hipStream_t s) {
+  if (n < 1 || n > es->B) return fail(RLT_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, es->B);
+  std::vector<char> seen(es->B, 0);
+  es->tbl.resize(2 * (size_t)n);
+  for (int i = 0; i < n; ++i) {
+    const int sl = host_slots[i];
+    if (sl < 0 || sl >= es->B) return fail(RLT_ERR_INVALID_ARG, "slot %d out of range", sl);
+    if (seen[sl]) return fail(RLT_ERR_INVALID_ARG, "slot %d listed twice", sl);
+    seen[sl] = 1;
+    es->tbl[i] = sl;
+    es->tbl[n + i] = pos[i];
+  }
+  hipError_t e = hipMemcpyAsync(es->slots_dev, es->tbl.data(), (size_t)n * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(es->p0_dev, es->tbl.data() + n, (size_t)n * 4, hipMemcpyHostToDevice, s);
+  return e == hipSuccess ? RLT_OK : hip_fail(e, "staging the snapshot table");
+}
+
+EncSnapArgs enc_snap_args(const rlt_encoder *enc, const rlt_encoder_state *es, int n, int cap) {
+  const rlt_config &c = enc->m->cfg;
+  EncSnapArgs a;
+  memset(&a, 0, sizeof a);
+  a.rec_bytes = rlt_encoder_snapshot_bytes(&c, cap, 1);
+  a.off_k = 256;
+  a.off_v = 256 + (a.rec_bytes - 256) / 2;
+  a.cache_k = es->cache_k;
+  a.cache_v = es->cache_v;
+  a.slots = es->slots_dev;
+  a.pos = es->p0_dev;
+  a.n = n;
+  a.B = es->B;
+  a.L = c.n_layers;
+  a.H = c.n_heads;
+  a.dh = c.head_dim;
+  a.max_tokens = es->max_tokens;
+  a.cap = cap;
+  a.esize = esize_of(c.dtype);
+  return a;
+}
+}  // namespace
+
+extern "C" {
+
+rlt_status rlt_encoder_state_export(const rlt_encoder *enc, rlt_encoder_state *es, int32_t n,
+                                    const int32_t *host_slots, int32_t capacity, void *dev_snap,
+                                    void *stream) {
+  if (!enc || !es) return fail(RLT_ERR_INVALID_ARG, "encoder or encoder state is NULL");
+  if (!host_slots || !dev_snap) return fail(RLT_ERR_INVALID_ARG, "host_slots or dev_snap is NULL");
+  if ((uintptr_t)dev_snap % 256) return fail(RLT_ERR_SHAPE, "dev_snap must be 256-byte aligned");
+  if (es->version != enc->m->version)
+    return fail(RLT_ERR_STALE, "encoder state built for model version %llu, model is version %llu",
+                (unsigned long long)es->version, (unsigned long long)enc->m->version);
+  if (capacity < 0) return fail(RLT_ERR_INVALID_ARG, "capacity must be >= 0");
+  if (n < 1 || n > es->B) return fail(RLT_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, es->B);
+  std::vector<int> pos(n);
+  for (int i = 0; i < n; ++i) {
+    if (host_slots[i] < 0 || host_slots[i] >= es->B)
+      return fail(RLT_ERR_INVALID_ARG, "slot %d out of range", host_slots[i]);
+    pos[i] = es->host_pos[host_slots[i]];
+    if (pos[i] > capacity)
+      return fail(RLT_ERR_RANGE, "slot %d holds %d positions > capacity %d", host_slots[i], pos[i],
+                  capacity);
+  }
+  rlt_status rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rs = enc_snap_stage(es, n, host_slots, pos, s)) != RLT_OK) return rs;
+  EncSnapArgs a = enc_snap_args(enc, es, n, capacity);
+  const rlt_config &c = enc->m->cfg;
+  a.snap = dev_snap;
+  const uint32_t hdr[12] = {kEncSnapMagic, 1u, (uint32_t)c.d_model, (uint32_t)c.n_heads,
+                            (uint32_t)c.head_dim, (uint32_t)c.n_layers, (uint32_t)c.dtype, 0u,
+                            (uint32_t)capacity, 0u, (uint32_t)(enc->m->version & 0xffffffffu),
+                            (uint32_t)(enc->m->version >> 32)};
+  memcpy(a.hdr, hdr, sizeof hdr);
+  const hipError_t e = launch_enc_snap(a, true, s);
+  if (e != hipSuccess) return hip_fail(e, "encoder snapshot export");
+  return ok();
+}
+
+rlt_status rlt_encoder_state_import(const rlt_encoder *enc, rlt_encoder_state *es, int32_t n,
+                                    const int32_t *host_slots, int32_t capacity,
+                                    const void *dev_snap, void *stream) {
+  if (!enc || !es) return fail(RLT_ERR_INVALID_ARG, "encoder or encoder state is NULL");
+  if (!host_slots || !dev_snap) return fail(RLT_ERR_INVALID_ARG, "host_slots or dev_snap is NULL");
+  if ((uintptr_t)dev_snap % 256) return fail(RLT_ERR_SHAPE, "dev_snap must be 256-byte aligned");
+  if (es->version != enc->m->version)
+    return fail(RLT_ERR_STALE, "encoder state built for model version %llu, model is version %llu",
+                (unsigned long long)es->version, (unsigned long long)enc->m->version);
+  if (capacity < 0) return fail(RLT_ERR_INVALID_ARG, "capacity must be >= 0");
+  if (n < 1 || n > es->B) return fail(RLT_ERR_INVALID_ARG, "n = %d outside [1, %d]", n, es->B);
+  rlt_status rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const rlt_config &c = enc->m->cfg;
+  const size_t rec = rlt_encoder_snapshot_bytes(&c, capacity, 1);
+  // read the headers back and check them before touching the state
+  std::vector<uint32_t> hd((size_t)n * 12);
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = hipMemcpyAsync(hd.data() + (size_t)i * 12,
+                                  static_cast<const char *>(dev_snap) + (size_t)i * rec, 48,
+                                  hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "reading encoder snapshot headers");
+  }
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading encoder snapshot headers");
+  std::vector<int> pos(n);
+  for (int i = 0; i < n; ++i) {
+    const uint32_t *f = hd.data() + (size_t)i * 12;
+    const uint64_t ver = (uint64_t)f[10] | ((uint64_t)f[11] << 32);
+    if (f[0] != kEncSnapMagic || f[1] != 1u)
+      return fail(RLT_ERR_CONVENTION, "record %d: not an encoder snapshot record", i);
+    if ((int)f[2] != c.d_model || (int)f[3] != c.n_heads || (int)f[4] != c.head_dim ||
+        (int)f[5] != c.n_layers || (int)f[6] != c.dtype)
+      return fail(RLT_ERR_CONVENTION, "record %d: shape or dtype differs from the model", i);
+    if ((int)f[8] != capacity)
+      return fail(RLT_ERR_CONVENTION, "record %d: capacity %u != %d", i, f[8], capacity);
+    if (ver != enc->m->version)
+      return fail(RLT_ERR_CONVENTION, "record %d: model version %llu != %llu", i,
+                  (unsigned long long)ver, (unsigned long long)enc->m->version);
+    pos[i] = (int)f[7];
+    if (pos[i] < 0 || pos[i] > capacity || pos[i] > es->max_tokens)
+      return fail(RLT_ERR_CONVENTION, "record %d: position %d outside [0, min(capacity, max_tokens)]",
+                  i, pos[i]);
+  }
+  if ((rs = enc_snap_stage(es, n, host_slots, pos, s)) != RLT_OK) return rs;
+  EncSnapArgs a = enc_snap_args(enc, es, n, capacity);
+  a.csnap = dev_snap;
+  e = launch_enc_snap(a, false, s);
+  if (e != hipSuccess) return hip_fail(e, "encoder snapshot import");
+  for (int i = 0; i < n; ++i) es->host_pos[host_slots[i]] = pos[i];
+  return ok();
+}
+
 rlt_status rlt_generate_encoded(const rlt_model *m, rlt_state *st, int32_t n_steps,
                                 const float *dev_logits0, const rlt_encoder *enc,
                                 rlt_encoder_state *es, const rlt_memory *mem,

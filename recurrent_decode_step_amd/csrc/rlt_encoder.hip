@@ -1197,4 +1197,48 @@ hipError_t launch_fattn(int dtype, int dh, const FAttnArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Encoder-cache snapshots: one workgroup per (record, layer, head) moves the
+// record's first pos positions (pos * dh contiguous elements on both sides,
+// 16-byte pieces); export clears the rest of the record's block and the
+// first workgroup of each record writes its header (the header words of the
+// call with this record's position in word 7).
+template <bool EXPORT>
+__global__ __launch_bounds__(256) void k_enc_snap(const EncSnapArgs a) {
+  const int i = blockIdx.x / (a.L * a.H), lh = blockIdx.x % (a.L * a.H);
+  const int l = lh / a.H, h = lh % a.H;
+  const int slot = a.slots[i], pos = a.pos[i];
+  const size_t blk = (size_t)a.dh * a.esize;                  // bytes per position
+  const size_t cache_off = ((((size_t)l * a.B + slot) * a.H + h) * a.max_tokens) * blk;
+  const size_t rec_off = (size_t)i * a.rec_bytes + ((size_t)l * a.H + h) * a.cap * blk;
+  const size_t used = (size_t)pos * blk / 16, all = (size_t)a.cap * blk / 16;
+  for (int kv = 0; kv < 2; ++kv) {
+    const size_t sec = kv ? a.off_v : a.off_k;
+    char *cache = kv ? a.cache_v : a.cache_k;
+    u32x4 *c16 = reinterpret_cast<u32x4 *>(cache + cache_off);
+    if constexpr (EXPORT) {
+      u32x4 *r16 = reinterpret_cast<u32x4 *>(static_cast<char *>(a.snap) + rec_off + sec);
+      for (size_t q = threadIdx.x; q < all; q += blockDim.x)
+        r16[q] = q < used ? c16[q] : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const u32x4 *r16 =
+          reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.csnap) + rec_off + sec);
+      for (size_t q = threadIdx.x; q < used; q += blockDim.x) c16[q] = r16[q];
+    }
+  }
+  if constexpr (EXPORT) {
+    if (lh == 0 && threadIdx.x < 64) {
+      uint32_t *hd = reinterpret_cast<uint32_t *>(static_cast<char *>(a.snap) + (size_t)i * a.rec_bytes);
+      const int w = threadIdx.x;
+      hd[w] = w < 12 ? (w == 7 ? (uint32_t)pos : a.hdr[w]) : 0u;
+    }
+  }
+}
+
+hipError_t launch_enc_snap(const EncSnapArgs &a, bool export_, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.n * a.L * a.H));
+  return export_ ? launch(k_enc_snap<true>, grid, dim3(256), 0, s, a)
+                 : launch(k_enc_snap<false>, grid, dim3(256), 0, s, a);
+}
+
 }  // namespace rlt

@@ -269,6 +269,18 @@ hipError_t launch_enc_norm(int dtype, const float *x, int64_t ldx, const float *
 hipError_t launch_pgemm(int dtype, int epi, const PGemmArgs &a, hipStream_t s);
 hipError_t launch_fattn(int dtype, int dh, const FAttnArgs &a, hipStream_t s);
 
+// Encoder-cache snapshot records (rlt_encoder_state_export / _import): per
+// record a 256-byte header, then K and V [L][H][cap][dh] in the model dtype.
+struct EncSnapArgs {
+  void *snap; const void *csnap;            // records, rec_bytes apart
+  size_t rec_bytes, off_k, off_v;
+  char *cache_k, *cache_v;                  // the state's cache [L][B][H][max_tokens][dh]
+  const int *slots, *pos;                   // device [n]: slot and position of record i
+  int n, B, L, H, dh, max_tokens, cap, esize;
+  uint32_t hdr[12];                         // export: header words (pos filled per record)
+};
+hipError_t launch_enc_snap(const EncSnapArgs &a, bool export_, hipStream_t s);
+
 // ---------------------------------------------------------------- training
 // Backpropagation through time, fp32 (rlt_train.hip).  Positions one row may
 // attend are limited to kTrainMaxPos (LDS score buffer of the attention kernels).

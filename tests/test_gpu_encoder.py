@@ -413,3 +413,84 @@ def test_generate_encoded_needs_matching_positions():
         binding.rlt_generate_encoded(model, st, pre, enc, es, (mk, mv), 1.0, 5, u)
     assert ex.value.status == binding.RLT_ERR_RANGE
     assert es.position(0) == P and st.position(0) == P + 1
+
+
+def test_encoder_snapshot_resumes_a_conversation_bitwise():
+    """Exact prefix snapshot of a conversation [Article, "Multi-Turn Serving"]:
+    the decoder records, the encoder-cache records and the memory entries of
+    three sequences after a 7-token prompt, imported into other slots (a
+    permutation) of fresh states, continue exactly like the originals: the
+    next 5 tokens' e rows, memory entries and logits are bitwise equal, row by
+    row.  (bf16, two memory groups.)"""
+    cfg = ModelConfig(vocab=96, d_model=128, n_heads=2, n_layers=2, d_ffn=256, window=4,
+                      mem_groups=2, dtype=1)
+    B, P, n, cap = 3, 7, 5, 12
+    params, eparams, model, enc, es, mk, mv = setup(cfg, B, cap, B * cap)
+    prompts = synth.token_ids(B, P, cfg.vocab, index=12)
+    nxt = torch.from_numpy(synth.token_ids(B, n, cfg.vocab, index=13)).to(DEV)
+    e = binding.rlt_encode(enc, es, torch.from_numpy(prompts).to(DEV), (mk, mv))
+    st = binding.State(model, B, cap)
+    binding.rlt_run_sequence(model, st, e, (mk, mv), logits_mode=binding.RLT_LOGITS_NONE)
+    dec = binding.rlt_state_export(model, st, list(range(B)))
+    encs = binding.rlt_encoder_state_export(enc, es, list(range(B)), P)
+    perm = [2, 0, 1]                                   # record i goes to slot perm[i]
+    es2 = binding.EncoderState(enc, B, cap, B * cap)
+    st2 = binding.State(model, B, cap)
+    binding.rlt_encoder_state_import(enc, es2, encs, perm, P)
+    binding.rlt_state_import(model, st2, dec, perm)
+    mk2, mv2 = torch.zeros_like(mk), torch.zeros_like(mv)
+    for i, j in enumerate(perm):
+        mk2[:, j], mv2[:, j] = mk[:, i], mv[:, i]
+    for i, j in enumerate(perm):
+        assert es2.position(j) == P and st2.position(j) == P
+    say("[encoder snapshot resume]")
+    e_a = binding.rlt_encode(enc, es, nxt, (mk, mv))
+    la = binding.rlt_run_sequence(model, st, e_a, (mk, mv))
+    nxt2 = torch.empty_like(nxt)
+    for i, j in enumerate(perm):
+        nxt2[j] = nxt[i]
+    e_b = binding.rlt_encode(enc, es2, nxt2, (mk2, mv2))
+    lb = binding.rlt_run_sequence(model, st2, e_b, (mk2, mv2))
+    torch.cuda.synchronize()
+    for i, j in enumerate(perm):
+        assert torch.equal(e_a[i], e_b[j])
+        assert torch.equal(la[i], lb[j])
+        assert torch.equal(mk[:, i], mk2[:, j]) and torch.equal(mv[:, i], mv2[:, j])
+
+
+def test_encoder_snapshot_checks_before_any_change():
+    """Export refuses a capacity below a slot's position (RLT_ERR_RANGE);
+    import refuses a record of another capacity, a decoder record and a
+    record of another model version (RLT_ERR_CONVENTION), each before it
+    changes the state."""
+    cfg = ModelConfig(vocab=64, d_model=64, n_heads=2, n_layers=1, d_ffn=128, window=4,
+                      mem_groups=1, dtype=0)
+    B, P, cap = 2, 5, 8
+    params, eparams, model, enc, es, mk, mv = setup(cfg, B, cap, B * cap)
+    binding.rlt_encode(enc, es, torch.from_numpy(synth.token_ids(B, P, cfg.vocab, index=14)).to(DEV),
+                       (mk, mv))
+    with pytest.raises(binding.RLTError) as ex:
+        binding.rlt_encoder_state_export(enc, es, [0, 1], P - 1)
+    assert ex.value.status == binding.RLT_ERR_RANGE
+    good = binding.rlt_encoder_state_export(enc, es, [0, 1], P)
+    es2 = binding.EncoderState(enc, B, cap, B * cap)
+    with pytest.raises(binding.RLTError) as ex:
+        binding.rlt_encoder_state_import(enc, es2, good, [0, 1], P + 1)
+    assert ex.value.status == binding.RLT_ERR_CONVENTION
+    st = binding.State(model, B, cap)
+    dec = binding.rlt_state_export(model, st, [0, 1])
+    need = binding.encoder_snapshot_bytes(cfg, P, 2)
+    fake = torch.zeros(max(need, dec.numel()), dtype=torch.uint8, device=DEV)
+    fake[:dec.numel()] = dec
+    with pytest.raises(binding.RLTError) as ex:
+        binding.rlt_encoder_state_import(enc, es2, fake, [0, 1], P)
+    assert ex.value.status == binding.RLT_ERR_CONVENTION
+    model2 = binding.Model(cfg, params, version=2)
+    enc2 = binding.Encoder(model2, eparams)
+    es3 = binding.EncoderState(enc2, B, cap, B * cap)
+    with pytest.raises(binding.RLTError) as ex:
+        binding.rlt_encoder_state_import(enc2, es3, good, [0, 1], P)
+    assert ex.value.status == binding.RLT_ERR_CONVENTION
+    assert es2.position(0) == 0 and es2.position(1) == 0 and es3.position(0) == 0
+    binding.rlt_encoder_state_import(enc, es2, good, [1, 0], P)
+    assert es2.position(0) == P and es2.position(1) == P
