@@ -33,6 +33,7 @@ Other measurements (each prints its own JSON line; not the default):
                           time fitted as a + b min(t, W) + c t and summed
   --generate              generation at the reference depth: 512 tokens sampled
                           (temperature 1, top-k 50) after the 2048-token prompt
+                          (--with-encoder: the causal encoder in the loop)
   --score                 replay scoring at the reference depth: every next
                           token's log-probability, read before it is consumed
   --counters-sample       reference-depth model, all sequences at the run's
@@ -771,6 +772,63 @@ def run_generate(args):
     }
 
 
+def run_generate_encoded(args):
+    """Generation at the reference depth with the causal encoder in the loop:
+    the 2048-token prompt of all 32 sequences encoded by rlt_encode and
+    consumed by rlt_run_sequence (untimed), then 512 tokens generated by
+    rlt_generate_encoded (temperature 1, top-k 50; each sampled token encoded
+    from the encoder cache of its sequence, T = 1), timed with HIP events
+    around the generation."""
+    import torch
+    from recurrent_decode_step_amd import binding, synth
+    from recurrent_decode_step_amd.configs import REFDEPTH
+    wl = REFDEPTH
+    cfg, B, T, P = wl.model, wl.batch, wl.steps, wl.prompt
+    n = T - P if args.steps is None else min(args.steps, T - P)
+    temperature, top_k = 1.0, 50
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    params = synth.model_params(cfg, device=dev)
+    model = binding.Model(cfg, params, version=1)
+    enc = binding.Encoder(model, synth.encoder_params(cfg, device=dev))
+    es = binding.EncoderState(enc, B, T, B * P)
+    sd = torch.bfloat16
+    shape = (cfg.mem_groups, B, cfg.n_heads, T, cfg.head_dim)
+    mk = torch.zeros(shape, dtype=sd, device=dev)
+    mv = torch.zeros(shape, dtype=sd, device=dev)
+    prompt = torch.from_numpy(synth.token_ids(B, P, cfg.vocab, index=0)).to(dev)
+    e = binding.rlt_encode(enc, es, prompt, (mk, mv))
+    u = synth.uniforms((B, n), device=dev)
+    state = binding.State(model, B, T)
+    logits0 = binding.rlt_run_sequence(model, state, e, (mk, mv), logits_mode=binding.RLT_LOGITS_LAST)
+    del e
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    tok, lp, _ = binding.rlt_generate_encoded(model, state, logits0, enc, es, (mk, mv), temperature,
+                                              top_k, u)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    if not torch.isfinite(lp).all():
+        raise RuntimeError("non-finite log-probabilities")
+    return {
+        "metric": "generated token-steps/sec at 1 GPU (48-layer, B=32, after a 2048-token prompt, "
+                  "causal encoder in the loop)",
+        "value": round(B * n / (ms / 1e3), 2), "unit": "token-steps/s", "n_gpus": 1, "steps": n,
+        "ms_per_step": round(ms / n, 4), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name + ", generation", "batch": B,
+                   "positions": f"{P + 1}..{P + n}",
+                   "sampling": f"temperature {temperature}, top-k {top_k}, uniforms seed 5",
+                   "encoder": "the causal encoder, one token per sequence per step from its cache"},
+        "mean_behaviour_logprob": round(float(lp.double().mean()), 4),
+        "distinct_tokens": int(torch.unique(tok).numel()),
+    }
+
+
 def run_longctx_full(args):
     """The long-context workload run whole: 8 sequences from H_0 through all
     32768 steps (rlt_run_sequence in chunks of 1024 steps, no reset, logits of
@@ -1276,6 +1334,8 @@ def main():
                     help="longctx: one full 32768-step run instead of the window fit")
     ap.add_argument("--generate", action="store_true",
                     help="generation at the reference depth after the 2048-token prompt")
+    ap.add_argument("--with-encoder", action="store_true",
+                    help="--generate with the causal encoder in the loop instead of the tables")
     ap.add_argument("--train", action="store_true",
                     help="backpropagation through time (fp32, small config, B x 128 steps)")
     ap.add_argument("--train-batch", type=int, default=0,
@@ -1323,7 +1383,7 @@ def main():
     elif args.score:
         out = run_score(args)
     elif args.generate:
-        out = run_generate(args)
+        out = run_generate_encoded(args) if args.with_encoder else run_generate(args)
     elif args.workload == "largebatch":
         out = run_largebatch(args)
     elif args.workload == "longctx":
