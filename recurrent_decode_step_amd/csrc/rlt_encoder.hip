@@ -13,14 +13,17 @@
 //   k_enc_embed  token embedding rows into the fp32 residual stream
 //   k_enc_norm   RMSNorm of rows into the storage type
 //   k_pgemm32d   token-parallel GEMM (bf16) on the 32x32x16 MFMA: 128 tokens x
-//                256 features per workgroup, both operands loaded straight
+//                256 features per workgroup (32 x 32 for calls of at most 64
+//                tokens), both operands loaded straight
 //                into LDS in fragment order (k_pgemm32: the register-staged
 //                form; k_pgemm: the fp32 form on 16x16x4),
 //                fused epilogues (q + encoder-cache append, residual add,
 //                GELU, memory K/V append)
 //   k_fattn32    causal flash attention over the encoder cache (bf16): 128
 //                queries of one (sequence, head) per workgroup, 32x32x16 MFMA
-//                for Q K^T and P V (k_fattn: the fp32 form, 64 queries, 16x16x4)
+//                for Q K^T and P V (k_fattn32_dec: calls of at most 32 tokens
+//                per sequence, deeper staging; k_fattn: the fp32 form, 64
+//                queries, 16x16x4)
 #include "rlt_device.h"
 
 #include <algorithm>
@@ -308,19 +311,34 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm(PGemmArgs a, int m
 // when written to LDS: piece (16-row tile t, lane r16 + 16 g) goes to 32-row
 // block t / 2, k-half g / 2, lane (t % 2) * 16 + r16 + 32 (g % 2).
 template <int RB_, int FB_, int WM_, int WN_, int NBUF_, int WPE_, int GROUP_ = 4, int PD_ = 1,
-          bool DIRECT_ = false>
+          bool DIRECT_ = false, int U_ = 1, int LW_ = 0>
 struct Pg32Cfg {
   static constexpr int RB = RB_, FB = FB_, WM = WM_, WN = WN_, NBUF = NBUF_, WPE = WPE_;
   static constexpr int GROUP = GROUP_;
   static constexpr int PD = PD_;       // stages in flight ahead of the one multiplied out
   static constexpr bool DIRECT = DIRECT_;   // direct-to-LDS loads (k_pgemm32d; NBUF - 1 stages in flight)
-  static constexpr int THREADS = 64 * WM * WN;
+  static constexpr int U = U_;         // stages per wait and barrier pair (k_pgemm32d)
+  static constexpr int LW = LW_;       // wavefronts that only stage (k_pgemm32d, U > 1)
+  static constexpr int THREADS = 64 * (WM * WN + LW);
   static constexpr int LDS = NBUF * (RB + FB) * 2 * 64 * 16;   // bytes
   static_assert(LDS >= WM * WN * 32 * 36 * 4, "epilogue scratch fits in the staging buffers");
 };
 // 128 tokens x 256 features, direct-to-LDS loads into three stages (two in
 // flight), two workgroups per CU
 using Pg32Default = Pg32Cfg<4, 8, 2, 2, 3, 2, 8, 2, true>;
+// Calls of at most 64 token rows (one token per sequence while generating):
+// 32 tokens x 32 features per workgroup, so that a launch has N / 32
+// workgroups, direct-to-LDS loads, stages in groups of four per wait (the LDS
+// reads of a group are issued ahead of its products).  One wavefront alone
+// keeps 15 stages (60 KiB) in flight, as a wavefront counts at most 63
+// outstanding loads; for long K (FFN-down: 8192) three more wavefronts that
+// only stage keep 32 stages (128 KiB) in flight, which pays for their barrier
+// waits.  The measured times per launch at 32 rows: 13 us for K = 2048, 37 us
+// for K = 8192 (against 41 us with the single wavefront).
+using Pg32Small = Pg32Cfg<1, 1, 1, 1, 19, 2, 1, 1, true, 4>;
+using Pg32SmallLong = Pg32Cfg<1, 1, 1, 1, 36, 1, 1, 1, true, 4, 3>;
+constexpr int kPgSmallRows = 64;
+constexpr int kPgLongKT = 128;        // packed k-steps (32 k each) from which K counts as long
 
 template <int EPI, class C>
 __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32(PGemmArgs a, int mt, int nt) {
@@ -330,6 +348,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32(PGemmArgs a, int
   constexpr int FPW = (FA + FW) / NW;
   constexpr int WRB = C::RB / C::WM, WFB = C::FB / C::WN;   // wavefront tile (32-blocks)
   static_assert((FA + FW) % NW == 0 && FA % NW == 0, "staging split");
+  static_assert(C::U == 1 && C::LW == 0, "grouped stages are a k_pgemm32d form");
   extern __shared__ u32x4 smem[];
   u32x4 *sA = smem;                      // [NBUF][FA * 64]
   u32x4 *sW = smem + C::NBUF * FA * 64;  // [NBUF][FW * 64]
@@ -518,15 +537,30 @@ __device__ __forceinline__ void wait_vmcnt() {
 #endif
 }
 
+// Wait until at most `after` stages of FPW loads each are still in flight
+// (the stages issued after the one about to be used; at most N of them).
+template <int FPW, int N>
+__device__ __forceinline__ void wait_stages(int after) {
+  static_assert(N * FPW < 64, "vmcnt counts at most 63 loads");
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (after >= N) wait_vmcnt<N * FPW>();
+    else wait_stages<FPW, N - 1>(after);
+  }
+}
+
 template <int EPI, class C>
 __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, int mt, int nt) {
   typedef float f32x16 __attribute__((ext_vector_type(16)));
-  constexpr int NW = C::WM * C::WN;
+  constexpr int NC = C::WM * C::WN;                         // wavefronts that multiply
+  constexpr int NW = NC + C::LW;                            // wavefronts that stage
   constexpr int FA = 2 * C::RB, FW = 2 * C::FB;
   constexpr int FS = FA + FW;                               // fragments per stage
   constexpr int FPW = FS / NW;
   constexpr int WRB = C::RB / C::WM, WFB = C::FB / C::WN;
-  static_assert(FS % NW == 0 && FA % NW == 0, "staging split");
+  static_assert(FS % NW == 0 && (FA % NW == 0 || C::LW > 0), "staging split");
+  static_assert(C::LW == 0 || C::U > 1, "staging-only wavefronts need grouped stages");
   extern __shared__ u32x4 smem[];                           // [3][FS * 64]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -557,7 +591,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, in
 #pragma unroll
   for (int u = 0; u < FPW; ++u) {
     const int f = wave + NW * u;
-    if (u < FA / NW) {
+    bool is_act;
+    if constexpr (FA % NW == 0) is_act = u < FA / NW;       // the same for every wavefront
+    else is_act = f < FA;
+    if (is_act) {
       const int row = min(row0 + (f >> 1) * 32 + (lane & 31), n_rows - 1);
       src[u] = reinterpret_cast<const u32x4 *>(ap + (size_t)row * a.lda + (f & 1) * 16 + (lane >> 5) * 8);
       step[u] = 32 * sizeof(bf16_t) / 16;                  // 32 k of bf16, in 16-byte units
@@ -612,29 +649,79 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, in
   // NBUF buffers, NBUF - 1 stages in flight: stage st + NBUF - 1 is loaded
   // into the buffer stage st - 1 used, which every wavefront has finished with
   // (the barrier that ends iteration st - 1)
-  constexpr int PD = C::NBUF - 1;
   const int S = a.KT;
-  for (int k = 0; k < PD && k < S; ++k) issue(k, k);
-  for (int st = 0; st < S; ++st) {
-    const int buf = st % C::NBUF;
-    if (st + PD < S) issue(st + PD, (st + PD) % C::NBUF);
-    // loads issued after this stage's: the stages st+1 .. st+PD that exist
-    const int after = min(S - 1, st + PD) - st;
-    if constexpr (PD >= 3) {
-      if (PD >= 4 && after >= 4) wait_vmcnt<(PD >= 4 ? 4 : 3) * FPW>();
-      else if (after >= 3) wait_vmcnt<3 * FPW>();
-      else if (after == 2) wait_vmcnt<2 * FPW>();
-      else if (after == 1) wait_vmcnt<FPW>();
-      else wait_vmcnt<0>();
-    } else {
-      if (after >= 2) wait_vmcnt<2 * FPW>();
-      else if (after == 1) wait_vmcnt<FPW>();
-      else wait_vmcnt<0>();
+  if constexpr (C::U == 1) {
+    constexpr int PD = C::NBUF - 1;
+    for (int k = 0; k < PD && k < S; ++k) issue(k, k);
+    for (int st = 0; st < S; ++st) {
+      const int buf = st % C::NBUF;
+      if (st + PD < S) issue(st + PD, (st + PD) % C::NBUF);
+      // loads issued after this stage's: the stages st+1 .. st+PD that exist
+      const int after = min(S - 1, st + PD) - st;
+      wait_stages<FPW, PD>(after);
+      __builtin_amdgcn_s_barrier();
+      mult(buf);
+      __builtin_amdgcn_s_barrier();
     }
-    __builtin_amdgcn_s_barrier();
-    mult(buf);
-    __builtin_amdgcn_s_barrier();
+  } else {
+    // groups of U stages: group st issues stages st + PD .. st + PD + U - 1
+    // into the buffers of group st - U (finished: the barrier that ended it),
+    // then waits for its own U stages, with the PD stages after them in flight
+    // (the products of a whole group are one branch-free block, so that the
+    // LDS reads of its later stages are issued under the earlier products);
+    // the last S % U stages, all issued by then, go one at a time
+    constexpr int U = C::U, PD = C::NBUF - U;
+    static_assert(PD >= 1, "stages in flight");
+    for (int k = 0; k < PD && k < S; ++k) issue(k, k);
+    int st = 0;
+    for (; st + U <= S; st += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (st + PD + u < S) issue(st + PD + u, (st + PD + u) % C::NBUF);
+      const int last = st + U - 1;
+      const int after = min(S - 1, st + PD + U - 1) - last;
+      wait_stages<FPW, PD>(after);
+      __builtin_amdgcn_s_barrier();
+      // all fragments of the group first, then its products in the order
+      // mult takes them (stage, k-half, tile)
+      if (C::LW == 0 || wave < NC) {
+      u32x4 gw[U][2][WFB], ga[U][2][WRB];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int buf = (st + u) % C::NBUF;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int f = 0; f < WFB; ++f)
+            gw[u][j][f] = smem[(buf * FS + FA + (wn * WFB + f) * 2 + j) * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < WRB; ++r) ga[u][j][r] = smem[(buf * FS + (wm * WRB + r) * 2 + j) * 64 + lane];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int f = 0; f < WFB; ++f)
+#pragma unroll
+            for (int r = 0; r < WRB; ++r)
+              acc[f][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8, gw[u][j][f]), __builtin_bit_cast(bf16x8, ga[u][j][r]),
+                  acc[f][r], 0, 0, 0);
+      }
+      __builtin_amdgcn_s_barrier();
+    }
+    if (st < S) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (C::LW == 0 || wave < NC)
+        for (; st < S; ++st) mult(st % C::NBUF);
+      __builtin_amdgcn_s_barrier();
+    }
   }
+  if (C::LW > 0 && wave >= NC) return;                      // staging only
 
   // epilogue through LDS, as in k_pgemm32 (every load has landed: the last wait was 0)
   constexpr int EROW = 36;
@@ -652,12 +739,36 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, in
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int tblk = row0 + (wm * WRB + r) * 32;
+      if constexpr (EPI == PEPI_RESID) {
+        // the four residual rows are read (from in-range addresses, also
+        // for outputs that are not stored) before any is written back, so
+        // that their loads are in flight together
+        f32x4 v[4], xo[4];
+        bool st[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(scr + tr * EROW + fc);
-        const int row = tblk + tr, n = fblk + fc;
-        if (row < n_rows && n < a.N) pgemm_store<bf16_t, EPI>(a, row, n, v);
+        for (int i = 0; i < 4; ++i) {
+          const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
+          v[i] = *reinterpret_cast<const f32x4 *>(scr + tr * EROW + fc);
+          const int row = tblk + tr, n = fblk + fc;
+          st[i] = row < n_rows && n < a.N;
+          xo[i] = *reinterpret_cast<const f32x4 *>(a.x + (size_t)min(row, n_rows - 1) * a.ld_x +
+                                                   min(n, a.N - 4));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
+          if (st[i])
+            *reinterpret_cast<f32x4 *>(a.x + (size_t)(tblk + tr) * a.ld_x + fblk + fc) =
+                f32x4{xo[i].x + v[i].x, xo[i].y + v[i].y, xo[i].z + v[i].z, xo[i].w + v[i].w};
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(scr + tr * EROW + fc);
+          const int row = tblk + tr, n = fblk + fc;
+          if (row < n_rows && n < a.N) pgemm_store<bf16_t, EPI>(a, row, n, v);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -871,29 +982,182 @@ __global__ __launch_bounds__(256, 2) void k_fattn(FAttnArgs a, int qblocks, int 
   }
 }
 
-// bf16 form on the 32x32x16 MFMA: 32 queries per wavefront, 128 per
-// workgroup, KV tiles of 64 positions.  S^T = K Q^T gives lane l query l % 32
-// and, in register r of position block pb, position pb*32 + 8 (r/4) + 4 (l/32)
-// + r % 4; P V takes its P^T fragment of k-step kk straight from registers
-// 8 (kk % 2) .. +7 of block kk / 2, and V^T reads the same positions from the
-// transposed tile.  A wavefront skips the products of tiles that lie wholly
-// after its last query (it still helps stage them).
+// bf16 form on the 32x32x16 MFMA: 32 queries per wavefront, KV tiles of 64
+// positions.  S^T = K Q^T gives lane l query l % 32 and, in register r of
+// position block pb, position pb*32 + 8 (r/4) + 4 (l/32) + r % 4; P V takes its
+// P^T fragment of k-step kk straight from registers 8 (kk % 2) .. +7 of block
+// kk / 2, and V^T reads the same positions from the transposed tile.  The
+// staging of a tile (each of the workgroup's 256 threads loads its share into
+// registers, then writes K in its row layout and V transposed to LDS) and the
+// products and softmax update of one tile are shared by both kernels below,
+// so a query's result does not depend on which of them ran it.
+template <int DH>
+struct FA32 {
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  static constexpr int KVT = 64;                  // positions per tile
+  static constexpr int KS = DH / 16;              // k-steps of Q K^T
+  static constexpr int CB = DH / 32;              // 32-channel blocks of O^T
+  static constexpr int VROW = KVT + 4;            // padded row of V^T (bf16)
+  static constexpr int NF = 2 * KS;               // K fragments per tile
+  static constexpr int KPT = NF / 4;              // K loads per thread (16 bytes each)
+  static constexpr int NVT = (KVT / 2) * (DH / 8);// V staging tasks (2 positions x 8 channels)
+  static constexpr int VPT = (NVT + 255) / 256;
+  static constexpr int CPR = DH / 8;              // 16-byte chunks per position row
+  static constexpr int KROW = CPR + 1;            // padded K row in LDS (u32x4)
+  static constexpr int SK = KVT * KROW;           // u32x4 of one K tile in LDS
+  static constexpr int SV = DH * VROW;            // bf16 of one V^T tile in LDS
+  static_assert(NF % 4 == 0, "head size");
+  struct Regs {
+    u32x4 k[KPT];
+    u32x4 v[VPT][2];
+  };
+
+  // this thread's share of tile `tile` (positions past kv_end - 1 read the
+  // last one): consecutive threads take consecutive 16-byte chunks of a
+  // position row, so a wavefront's load covers whole rows
+  static __device__ __forceinline__ void load(Regs &r, const bf16_t *kbase, const bf16_t *vbase,
+                                              int64_t s_pos, int tile, int kv_end, int tid) {
+    const int pbase = tile * KVT;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int t = u * 256 + tid;
+      const int p = min(pbase + t / CPR, kv_end - 1);
+      r.k[u] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)p * s_pos + (t % CPR) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int t = u * 256 + tid;
+      if (NVT % 256 == 0 || t < NVT) {
+        const int q = t / CPR, ch = t % CPR;     // positions 2q, 2q + 1; channels 8 ch .. + 7
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int p = min(pbase + q * 2 + e, kv_end - 1);
+          r.v[u][e] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)p * s_pos + ch * 8);
+        }
+      }
+    }
+  }
+
+  // K keeps its row layout (rows padded by 16 bytes, so that a fragment's
+  // 32 rows fall in distinct banks); V is written transposed
+  static __device__ __forceinline__ void store(const Regs &r, u32x4 *sK, bf16_t *sVt, int tid) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int t = u * 256 + tid;
+      sK[(t / CPR) * KROW + t % CPR] = r.k[u];
+    }
+    uint32_t *vt = reinterpret_cast<uint32_t *>(sVt);
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int t = u * 256 + tid;
+      if (NVT % 256 == 0 || t < NVT) {
+        const int q = t / CPR, ch = t % CPR;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = r.v[u][0][e], hi = r.v[u][1][e];
+          const int c = ch * 8 + 2 * e;
+          vt[(c * VROW + 2 * q) >> 1] = (lo & 0xffffu) | (hi << 16);
+          vt[((c + 1) * VROW + 2 * q) >> 1] = (lo >> 16) | (hi & 0xffff0000u);
+        }
+      }
+    }
+  }
+
+  // one tile's products and online-softmax update for the wavefront's 32
+  // queries, for NCB channel blocks cb0 .. cb0 + NCB - 1 of O (o[0 .. NCB-1]);
+  // each block's chain of P V products is the same whichever blocks a
+  // wavefront holds
+  template <int NCB = CB>
+  static __device__ __forceinline__ void tile(const u32x4 *sK, const bf16_t *sVt, const u32x4 *qf,
+                                              int tile, int qpos, float scale_log2, int lane,
+                                              int cb0, f32x16 *o, float &m, float &lsum) {
+    const int hh = lane >> 5;
+    f32x16 s[2];
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[pb][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, sK[(pb * 32 + (lane & 31)) * KROW + 2 * ks + hh]),
+            __builtin_bit_cast(bf16x8, qf[ks]), s[pb], 0, 0, 0);
+    }
+    const int pos0 = tile * KVT + 4 * hh;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = pos0 + pb * 32 + 8 * (r >> 2) + (r & 3);
+        const float sv = p <= qpos ? s[pb][r] * scale_log2 : -INFINITY;
+        s[pb][r] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2f(m - mn);
+    m = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) o[c] *= alpha;
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = exp2f(s[pb][r] - mn);
+        s[pb][r] = pv;
+        lsum += pv;
+      }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int pb = kk >> 1, r0 = 8 * (kk & 1);
+      const u32x4 pf = u32x4{f2bf2(s[pb][r0], s[pb][r0 + 1]), f2bf2(s[pb][r0 + 2], s[pb][r0 + 3]),
+                             f2bf2(s[pb][r0 + 4], s[pb][r0 + 5]), f2bf2(s[pb][r0 + 6], s[pb][r0 + 7])};
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const bf16_t *vp = sVt + ((cb0 + c) * 32 + (lane & 31)) * VROW + kk * 16 + 4 * hh;
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vp);
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vp + 8);
+        o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}),
+            __builtin_bit_cast(bf16x8, pf), o[c], 0, 0, 0);
+      }
+    }
+  }
+
+  // o / l of the wavefront's queries to their rows (lanes whose query
+  // exists), channel blocks cb0 .. cb0 + NCB - 1
+  template <int NCB = CB>
+  static __device__ __forceinline__ void finish(const FAttnArgs &a, const f32x16 *o, float lsum,
+                                                int rq, int h, int lane, int cb0, bool valid) {
+    lsum += __shfl_xor(lsum, 32);
+    if (!valid) return;
+    const float inv = 1.0f / lsum;
+    bf16_t *orow = static_cast<bf16_t *>(a.out) + (size_t)rq * a.ldo + h * DH + 4 * (lane >> 5);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float y[4] = {o[c][4 * q] * inv, o[c][4 * q + 1] * inv, o[c][4 * q + 2] * inv,
+                            o[c][4 * q + 3] * inv};
+        Num<bf16_t>::store4(orow + (cb0 + c) * 32 + 8 * q, y);
+      }
+  }
+};
+
+// 128 queries of one (sequence, head) per workgroup, 32 per wavefront.  The
+// next tile's loads are in flight while a tile is multiplied out; a wavefront
+// skips the products of tiles that lie wholly after its last query (it still
+// helps stage them).
 template <int DH>
 __global__ __launch_bounds__(256, 2) void k_fattn32(FAttnArgs a, int qblocks, int n_seq) {
-  typedef float f32x16 __attribute__((ext_vector_type(16)));
-  constexpr int KVT = 64;                  // positions per tile
-  constexpr int KS = DH / 16;              // k-steps of Q K^T
-  constexpr int CB = DH / 32;              // 32-channel blocks of O^T
-  constexpr int VROW = KVT + 4;            // padded row of V^T (bf16)
-  constexpr int NF = 2 * KS;               // K fragments per tile
-  constexpr int KPT = NF / 4;              // per wavefront
-  constexpr int NVT = (KVT / 2) * (DH / 8);// V staging tasks (2 positions x 8 channels)
-  constexpr int VPT = (NVT + 255) / 256;
-  static_assert(NF % 4 == 0, "head size");
-  __shared__ u32x4 sK[NF * 64];
-  __shared__ bf16_t sVt[DH * VROW];
+  using F = FA32<DH>;
+  typedef typename F::f32x16 f32x16;
+  __shared__ u32x4 sK[F::SK];
+  __shared__ bf16_t sVt[F::SV];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x % a.H;
   const int rest = blockIdx.x / a.H;
   const int i = rest % n_seq;
@@ -903,150 +1167,110 @@ __global__ __launch_bounds__(256, 2) void k_fattn32(FAttnArgs a, int qblocks, in
   const int j0 = qb * 128;
   const int jlast = min(j0 + 127, Tn - 1);
   const int kv_end = p0 + jlast + 1;
-  const int ntile = (kv_end + KVT - 1) / KVT;
+  const int ntile = (kv_end + F::KVT - 1) / F::KVT;
   const int jraw = j0 + wave * 32 + (lane & 31);
   const int jq = min(jraw, Tn - 1);
   const int qpos = p0 + jq;
   const int wave_last = p0 + min(j0 + wave * 32 + 31, Tn - 1);   // last query position of the wavefront
   const int rq = i * Tn + jq;
-  const int hh = lane >> 5;
   const bf16_t *kbase = static_cast<const bf16_t *>(a.kb) + (size_t)slot * a.s_seq + (size_t)h * a.s_head;
   const bf16_t *vbase = static_cast<const bf16_t *>(a.vb) + (size_t)slot * a.s_seq + (size_t)h * a.s_head;
 
-  u32x4 qf[KS];
-  const bf16_t *qrow = static_cast<const bf16_t *>(a.q) + (size_t)rq * a.ldq + h * DH + hh * 8;
+  u32x4 qf[F::KS];
+  const bf16_t *qrow = static_cast<const bf16_t *>(a.q) + (size_t)rq * a.ldq + h * DH + (lane >> 5) * 8;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const u32x4 *>(qrow + ks * 16);
+  for (int ks = 0; ks < F::KS; ++ks) qf[ks] = *reinterpret_cast<const u32x4 *>(qrow + ks * 16);
 
-  u32x4 kr[KPT], vr[VPT][2];
-  auto load = [&](int tile) {
-    const int pbase = tile * KVT;
+  f32x16 o[F::CB];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int f = u * 4 + wave;
-      const int pb = f / KS, ks = f - (f / KS) * KS;
-      const int p = min(pbase + pb * 32 + (lane & 31), kv_end - 1);
-      kr[u] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)p * a.s_pos + ks * 16 + hh * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int t = u * 256 + (int)threadIdx.x;
-      if (NVT % 256 == 0 || t < NVT) {
-        const int q = t % (KVT / 2), ch = t / (KVT / 2);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int p = min(pbase + q * 2 + e, kv_end - 1);
-          vr[u][e] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)p * a.s_pos + ch * 8);
-        }
-      }
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) sK[(u * 4 + wave) * 64 + lane] = kr[u];
-    uint32_t *vt = reinterpret_cast<uint32_t *>(sVt);
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int t = u * 256 + (int)threadIdx.x;
-      if (NVT % 256 == 0 || t < NVT) {
-        const int q = t % (KVT / 2), ch = t / (KVT / 2);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = vr[u][0][e], hi = vr[u][1][e];
-          const int c = ch * 8 + 2 * e;
-          vt[(c * VROW + 2 * q) >> 1] = (lo & 0xffffu) | (hi << 16);
-          vt[((c + 1) * VROW + 2 * q) >> 1] = (lo >> 16) | (hi & 0xffff0000u);
-        }
-      }
-    }
-  };
-
-  f32x16 o[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
+  for (int cb = 0; cb < F::CB; ++cb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
   float m = -INFINITY, lsum = 0.f;
 
-  load(0);
-  store();
+  typename F::Regs r;
+  F::load(r, kbase, vbase, a.s_pos, 0, kv_end, tid);
+  F::store(r, sK, sVt, tid);
   __syncthreads();
   for (int tile = 0; tile < ntile; ++tile) {
-    if (tile + 1 < ntile) load(tile + 1);
-    if (tile * KVT <= wave_last) {                 // uniform over the wavefront
-      f32x16 s[2];
-#pragma unroll
-      for (int pb = 0; pb < 2; ++pb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[pb][e] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, sK[(pb * KS + ks) * 64 + lane]),
-              __builtin_bit_cast(bf16x8, qf[ks]), s[pb], 0, 0, 0);
-      }
-      const int pos0 = tile * KVT + 4 * hh;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int p = pos0 + pb * 32 + 8 * (r >> 2) + (r & 3);
-          const float sv = p <= qpos ? s[pb][r] * a.scale_log2 : -INFINITY;
-          s[pb][r] = sv;
-          mx = fmaxf(mx, sv);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m, mx);
-      const float alpha = exp2f(m - mn);
-      m = mn;
-      lsum *= alpha;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
-#pragma unroll
-      for (int pb = 0; pb < 2; ++pb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = exp2f(s[pb][r] - mn);
-          s[pb][r] = pv;
-          lsum += pv;
-        }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int pb = kk >> 1, r0 = 8 * (kk & 1);
-        const u32x4 pf = u32x4{f2bf2(s[pb][r0], s[pb][r0 + 1]), f2bf2(s[pb][r0 + 2], s[pb][r0 + 3]),
-                               f2bf2(s[pb][r0 + 4], s[pb][r0 + 5]), f2bf2(s[pb][r0 + 6], s[pb][r0 + 7])};
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const bf16_t *vp = sVt + (cb * 32 + (lane & 31)) * VROW + kk * 16 + 4 * hh;
-          const u32x2 lo = *reinterpret_cast<const u32x2 *>(vp);
-          const u32x2 hi = *reinterpret_cast<const u32x2 *>(vp + 8);
-          o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}),
-              __builtin_bit_cast(bf16x8, pf), o[cb], 0, 0, 0);
-        }
-      }
-    }
+    if (tile + 1 < ntile) F::load(r, kbase, vbase, a.s_pos, tile + 1, kv_end, tid);
+    if (tile * F::KVT <= wave_last)                 // uniform over the wavefront
+      F::tile(sK, sVt, qf, tile, qpos, a.scale_log2, lane, 0, o, m, lsum);
     __syncthreads();
     if (tile + 1 < ntile) {
-      store();
+      F::store(r, sK, sVt, tid);
       __syncthreads();
     }
   }
+  F::finish(a, o, lsum, rq, h, lane, 0, jraw < Tn);
+}
 
-  lsum += __shfl_xor(lsum, 32);
-  if (jraw < Tn) {
-    const float inv = 1.0f / lsum;
-    bf16_t *orow = static_cast<bf16_t *>(a.out) + (size_t)rq * a.ldo + h * DH + 4 * hh;
+// Calls of at most 32 tokens per sequence (one token per sequence while
+// generating): one (sequence, head) per workgroup; its queries fit one
+// wavefront, so wavefront w computes the scores and softmax of all of them and
+// the P V products of channel block w of O only (head sizes below 128 leave
+// the wavefronts past the last block staging only).  Two LDS buffers and two
+// register sets: while tile t is multiplied out, tile t + 1 is written to the
+// other buffer and tiles t + 2 and t + 3 are in flight.
+template <int DH>
+__global__ __launch_bounds__(256, 2) void k_fattn32_dec(FAttnArgs a) {
+  using F = FA32<DH>;
+  typedef typename F::f32x16 f32x16;
+  extern __shared__ u32x4 dsm[];                    // K tiles [2][SK], then V^T tiles [2][SV]
+  u32x4 *const sK0 = dsm, *const sK1 = dsm + F::SK;
+  bf16_t *const sV0 = reinterpret_cast<bf16_t *>(dsm + 2 * F::SK), *const sV1 = sV0 + F::SV;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool active = wave < F::CB;                 // owns channel block `wave`
+  const int h = blockIdx.x % a.H;
+  const int i = blockIdx.x / a.H;
+  const int Tn = a.rows.T;
+  const int slot = a.rows.slots[i], p0 = a.rows.p0[i];
+  const int kv_end = p0 + Tn;
+  const int ntile = (kv_end + F::KVT - 1) / F::KVT;
+  const int jraw = lane & 31;
+  const int jq = min(jraw, Tn - 1);
+  const int qpos = p0 + jq;
+  const int rq = i * Tn + jq;
+  const bf16_t *kbase = static_cast<const bf16_t *>(a.kb) + (size_t)slot * a.s_seq + (size_t)h * a.s_head;
+  const bf16_t *vbase = static_cast<const bf16_t *>(a.vb) + (size_t)slot * a.s_seq + (size_t)h * a.s_head;
+
+  u32x4 qf[F::KS];
+  f32x16 o[1];
+  float m = -INFINITY, lsum = 0.f;
+  if (active) {
+    const bf16_t *qrow = static_cast<const bf16_t *>(a.q) + (size_t)rq * a.ldq + h * DH + (lane >> 5) * 8;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int ks = 0; ks < F::KS; ++ks) qf[ks] = *reinterpret_cast<const u32x4 *>(qrow + ks * 16);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float y[4] = {o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv, o[cb][4 * q + 2] * inv,
-                            o[cb][4 * q + 3] * inv};
-        Num<bf16_t>::store4(orow + cb * 32 + 8 * q, y);
-      }
+    for (int e = 0; e < 16; ++e) o[0][e] = 0.f;
   }
+
+  // Loads and stores are unconditional, so that every iteration leaves the
+  // same loads in flight and each wait lets the newer tile's loads stay
+  // outstanding: a tile past the last one reads position kv_end - 1 only (a
+  // few cache lines) and is written to a buffer that is not read again.
+  typename F::Regs r0, r1;
+  F::load(r0, kbase, vbase, a.s_pos, 0, kv_end, tid);
+  F::load(r1, kbase, vbase, a.s_pos, 1, kv_end, tid);
+  F::store(r0, sK0, sV0, tid);
+  F::load(r0, kbase, vbase, a.s_pos, 2, kv_end, tid);
+  __syncthreads();
+  for (int t = 0; t < ntile; t += 2) {
+    // tile t is in buffer 0, t + 1 in r1, t + 2 in r0
+    if (active) F::template tile<1>(sK0, sV0, qf, t, qpos, a.scale_log2, lane, wave, o, m, lsum);
+    F::store(r1, sK1, sV1, tid);
+    F::load(r1, kbase, vbase, a.s_pos, t + 3, kv_end, tid);
+    __syncthreads();
+    // tile t + 1 is in buffer 1, t + 2 in r0, t + 3 in r1 (the second half runs
+    // whole also after the last tile: one loop edge, the same waits each time)
+    if (active && t + 1 < ntile)
+      F::template tile<1>(sK1, sV1, qf, t + 1, qpos, a.scale_log2, lane, wave, o, m, lsum);
+    F::store(r0, sK0, sV0, tid);
+    F::load(r0, kbase, vbase, a.s_pos, t + 4, kv_end, tid);
+    __syncthreads();
+  }
+  if (active) F::template finish<1>(a, o, lsum, rq, h, lane, wave, jraw < Tn);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1155,8 +1379,9 @@ hipError_t launch_pgemm(int dtype, int epi, const PGemmArgs &a, hipStream_t s) {
   if (a.rows.n_rows < 1) return hipSuccess;
   // packed weights have whole 32-row pairs of tiles (Np % 32 == 0)
   if (a.Np % 32) return hipErrorInvalidValue;
-  return dtype == RLT_DTYPE_BF16 ? pgemm32_epi<Pg32Default>(epi, a, s)
-                                 : pgemm_epi<float, PgDefault>(epi, a, s);
+  if (dtype != RLT_DTYPE_BF16) return pgemm_epi<float, PgDefault>(epi, a, s);
+  if (a.rows.n_rows > kPgSmallRows) return pgemm32_epi<Pg32Default>(epi, a, s);
+  return a.KT >= kPgLongKT ? pgemm32_epi<Pg32SmallLong>(epi, a, s) : pgemm32_epi<Pg32Small>(epi, a, s);
 }
 
 template <typename T, int DH>
@@ -1176,8 +1401,29 @@ hipError_t fattn32_go(const FAttnArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int DH>
+hipError_t fattn32_dec_go(const FAttnArgs &a, hipStream_t s) {
+  constexpr int LDS = 2 * FA32<DH>::SK * 16 + 2 * FA32<DH>::SV * 2;
+  if constexpr (LDS > 65536) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_fattn32_dec<DH>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+    if (attr != hipSuccess) return attr;
+  }
+  const int n_seq = a.rows.n_rows / a.rows.T;
+  (void)launch((k_fattn32_dec<DH>), dim3(n_seq * a.H), dim3(256), LDS, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fattn(int dtype, int dh, const FAttnArgs &a, hipStream_t s) {
   if (a.rows.n_rows < 1) return hipSuccess;
+  if (dtype == RLT_DTYPE_BF16 && a.rows.T <= 32) {
+    switch (dh) {
+      case 32: return fattn32_dec_go<32>(a, s);
+      case 64: return fattn32_dec_go<64>(a, s);
+      case 128: return fattn32_dec_go<128>(a, s);
+    }
+  }
   if (dtype == RLT_DTYPE_BF16) {
     switch (dh) {
       case 32: return fattn32_go<32>(a, s);

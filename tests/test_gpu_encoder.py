@@ -134,6 +134,55 @@ def test_encode_chunks_and_batches_are_bitwise_invariant():
     assert torch.equal(mk3[:, 3, :, :T], mk[:, 3, :, :T])
 
 
+@pytest.mark.parametrize("d,H,F", [(256, 2, 4096), (128, 4, 256), (128, 2, 512)],
+                         ids=["dh128_longK", "dh32", "dh64"])
+def test_short_calls_are_bitwise_the_one_call_result(d, H, F):
+    """Calls of few rows take their own kernel forms (GEMM tiles of 32 tokens x
+    32 features, with staging-only wavefronts when K >= 4096; attention with
+    one query wavefront per (sequence, head) when a call has at most 32 tokens
+    per sequence).  Encoding 70 tokens, then 12, then 32, then 20 one token at
+    a time gives bitwise the e rows, memory and cache of one call over all
+    134 tokens; so does a batch of 64 sequences (two row tiles) stepped one
+    token at a time."""
+    cfg = ModelConfig(vocab=120, d_model=d, n_heads=H, n_layers=1, d_ffn=F, window=8,
+                      mem_groups=1, dtype=1)
+    B, chunks = 5, [70, 12, 32] + [1] * 20
+    T = sum(chunks)
+    say(f"[encoder short calls] d={d} H={H} F={F} B={B} chunks 70+12+32+20x1")
+    tok = torch.from_numpy(synth.token_ids(B, T, cfg.vocab, index=11)).to(DEV)
+    params, eparams, model, enc, es, mk, mv = setup(cfg, B, 160, B * T)
+    e_all = binding.rlt_encode(enc, es, tok, (mk, mv))
+    es2 = binding.EncoderState(enc, B, 160, B * 70)
+    mk2, mv2 = torch.zeros_like(mk), torch.zeros_like(mv)
+    parts, lo = [], 0
+    for n in chunks:
+        parts.append(binding.rlt_encode(enc, es2, tok[:, lo:lo + n].contiguous(), (mk2, mv2)))
+        lo += n
+    torch.cuda.synchronize()
+    assert torch.isfinite(e_all).all()
+    assert torch.equal(torch.cat(parts, dim=1), e_all)
+    assert torch.equal(mk, mk2) and torch.equal(mv, mv2)
+    k1, v1 = es.cache()
+    k2, v2 = es2.cache()
+    assert torch.equal(k1[:, :, :, :T], k2[:, :, :, :T]) and torch.equal(v1[:, :, :, :T], v2[:, :, :, :T])
+    # 64 sequences: a prompt of 9, then 3 single tokens (64 rows per call)
+    B2, P2 = 64, 9
+    tok2 = torch.from_numpy(synth.token_ids(B2, P2 + 3, cfg.vocab, index=12)).to(DEV)
+    es3 = binding.EncoderState(enc, B2, 16, B2 * (P2 + 3))
+    mk3 = torch.zeros((1, B2, H, 16, d // H), dtype=torch.bfloat16, device=DEV)
+    mv3 = torch.zeros_like(mk3)
+    e_ref = binding.rlt_encode(enc, es3, tok2, (mk3, mv3))
+    es4 = binding.EncoderState(enc, B2, 16, B2 * P2)
+    mk4, mv4 = torch.zeros_like(mk3), torch.zeros_like(mv3)
+    got = [binding.rlt_encode(enc, es4, tok2[:, :P2].contiguous(), (mk4, mv4))]
+    for j in range(P2, P2 + 3):
+        got.append(binding.rlt_encode(enc, es4, tok2[:, j:j + 1].contiguous(), (mk4, mv4)))
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(got, dim=1), e_ref)
+    assert torch.equal(mk3, mk4) and torch.equal(mv3, mv4)
+    say("[encoder short calls] bitwise ok")
+
+
 def test_large_call_matches_per_sequence_calls_bitwise():
     """17100 token rows in one call (134 row tiles, the last one ragged; 384
     QKV features, so a ragged feature tile too) against the same prompts
