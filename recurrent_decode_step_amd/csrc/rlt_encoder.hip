@@ -328,15 +328,15 @@ struct Pg32Cfg {
 using Pg32Default = Pg32Cfg<4, 8, 2, 2, 3, 2, 8, 2, true>;
 // Calls of at most 64 token rows (one token per sequence while generating):
 // 32 tokens x 32 features per workgroup, so that a launch has N / 32
-// workgroups, direct-to-LDS loads, stages in groups of four per wait (the LDS
+// workgroups, direct-to-LDS loads, stages in groups of eight per wait (the LDS
 // reads of a group are issued ahead of its products).  One wavefront alone
 // keeps 15 stages (60 KiB) in flight, as a wavefront counts at most 63
 // outstanding loads; for long K (FFN-down: 8192) three more wavefronts that
-// only stage keep 32 stages (128 KiB) in flight, which pays for their barrier
-// waits.  The measured times per launch at 32 rows: 13 us for K = 2048, 37 us
-// for K = 8192 (against 41 us with the single wavefront).
-using Pg32Small = Pg32Cfg<1, 1, 1, 1, 19, 2, 1, 1, true, 4>;
-using Pg32SmallLong = Pg32Cfg<1, 1, 1, 1, 36, 1, 1, 1, true, 4, 3>;
+// only stage keep 30 stages (120 KiB) in flight, which pays for their barrier
+// waits.  The measured times per launch at 32 rows: 11.3-12.3 us for K = 2048,
+// 34 us for K = 8192 (41 us with the single wavefront and groups of one).
+using Pg32Small = Pg32Cfg<1, 1, 1, 1, 23, 2, 1, 1, true, 8>;
+using Pg32SmallLong = Pg32Cfg<1, 1, 1, 1, 38, 1, 1, 1, true, 8, 3>;
 constexpr int kPgSmallRows = 64;
 constexpr int kPgLongKT = 128;        // packed k-steps (32 k each) from which K counts as long
 

@@ -134,13 +134,14 @@ def test_encode_chunks_and_batches_are_bitwise_invariant():
     assert torch.equal(mk3[:, 3, :, :T], mk[:, 3, :, :T])
 
 
-@pytest.mark.parametrize("d,H,F", [(256, 2, 4096), (128, 4, 256), (128, 2, 512)],
-                         ids=["dh128_longK", "dh32", "dh64"])
+@pytest.mark.parametrize("d,H,F", [(256, 2, 4096), (128, 4, 256), (128, 2, 320)],
+                         ids=["dh128_longK", "dh32", "dh64_Kgroups_and_rest"])
 def test_short_calls_are_bitwise_the_one_call_result(d, H, F):
     """Calls of few rows take their own kernel forms (GEMM tiles of 32 tokens x
-    32 features, with staging-only wavefronts when K >= 4096; attention with
-    one query wavefront per (sequence, head) when a call has at most 32 tokens
-    per sequence).  Encoding 70 tokens, then 12, then 32, then 20 one token at
+    32 features, stages in groups of eight, with staging-only wavefronts when
+    K >= 4096; attention with one query wavefront per (sequence, head) when a
+    call has at most 32 tokens per sequence).  K = 128 runs only the stages
+    after the last whole group, 320 one group and the rest, 4096 whole groups.  Encoding 70 tokens, then 12, then 32, then 20 one token at
     a time gives bitwise the e rows, memory and cache of one call over all
     134 tokens; so does a batch of 64 sequences (two row tiles) stepped one
     token at a time."""
