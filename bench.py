@@ -33,7 +33,8 @@ Other measurements (each prints its own JSON line; not the default):
                           time fitted as a + b min(t, W) + c t and summed
   --generate              generation at the reference depth: 512 tokens sampled
                           (temperature 1, top-k 50) after the 2048-token prompt
-                          (--with-encoder: the causal encoder in the loop)
+                          (--with-encoder: the causal encoder in the loop;
+                          --fast-encoder: its short calls on the decoder's forms)
   --score                 replay scoring at the reference depth: every next
                           token's log-probability, read before it is consumed
   --counters-sample       reference-depth model, all sequences at the run's
@@ -802,6 +803,8 @@ def run_generate_encoded(args):
     state = binding.State(model, B, T)
     logits0 = binding.rlt_run_sequence(model, state, e, (mk, mv), logits_mode=binding.RLT_LOGITS_LAST)
     del e
+    if args.fast_encoder:
+        binding.rlt_encoder_state_set_mode(es, binding.RLT_ENC_FAST)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -823,7 +826,9 @@ def run_generate_encoded(args):
         "config": {"workload": wl.name + ", generation", "batch": B,
                    "positions": f"{P + 1}..{P + n}",
                    "sampling": f"temperature {temperature}, top-k {top_k}, uniforms seed 5",
-                   "encoder": "the causal encoder, one token per sequence per step from its cache"},
+                   "encoder": "the causal encoder, one token per sequence per step from its cache",
+                   "encoder_mode": "fast (decoder kernel forms)" if args.fast_encoder
+                                   else "exact (the prompt kernels' arithmetic)"},
         "mean_behaviour_logprob": round(float(lp.double().mean()), 4),
         "distinct_tokens": int(torch.unique(tok).numel()),
     }
@@ -1336,6 +1341,8 @@ def main():
                     help="generation at the reference depth after the 2048-token prompt")
     ap.add_argument("--with-encoder", action="store_true",
                     help="--generate with the causal encoder in the loop instead of the tables")
+    ap.add_argument("--fast-encoder", action="store_true",
+                    help="--with-encoder: the encoder state in RLT_ENC_FAST mode")
     ap.add_argument("--train", action="store_true",
                     help="backpropagation through time (fp32, small config, B x 128 steps)")
     ap.add_argument("--train-batch", type=int, default=0,

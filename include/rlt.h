@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define RLT_ABI_VERSION 2
+#define RLT_ABI_VERSION 3
 
 typedef enum {
   RLT_OK = 0,
@@ -383,6 +383,23 @@ void rlt_encoder_state_destroy(rlt_encoder_state *es);
 
 /* Set the listed slots back to position 0 (a new document).  Host only. */
 rlt_status rlt_encoder_state_reset(rlt_encoder_state *es, int32_t n, const int32_t *host_slots);
+
+/* Kernel forms of the state's short calls [Tutorial, "Autoregressive
+ * generation": each sampled token is encoded incrementally, and kernels that
+ * share the execution semantics need not agree numerically].
+ *   RLT_ENC_EXACT (the default): every call runs the prompt kernels'
+ *     arithmetic, so a prompt gives bitwise the same values however it is
+ *     split into calls.
+ *   RLT_ENC_FAST: calls of at most 64 token rows with K >= 4096 split K over
+ *     four workgroups (parts added in a fixed order), and calls of one token
+ *     per sequence take the decoder's attention form (independent wavefront
+ *     streams); values agree with the exact mode up to rounding, do not
+ *     depend on the other rows of a call and are the same on every run.
+ * Applies to the calls made after it, rlt_generate_encoded's included.
+ * RLT_ERR_INVALID_ARG for another mode.  Host only. */
+#define RLT_ENC_EXACT 0
+#define RLT_ENC_FAST 1
+rlt_status rlt_encoder_state_set_mode(rlt_encoder_state *es, int32_t mode);
 
 /* Tokens encoded so far in a slot; -1 on a bad argument. */
 int32_t rlt_encoder_position(const rlt_encoder_state *es, int32_t slot);

@@ -23,7 +23,7 @@ RLT_LOGITS_ALL, RLT_LOGITS_LAST, RLT_LOGITS_NONE = 0, 1, 2
 RLT_K_EXTRA, RLT_K_GEMM, RLT_K_SWA, RLT_K_CROSS = 0, 1, 2, 3
 RLT_E_GEMM, RLT_E_ATTN, RLT_E_OTHER = 0, 1, 2
 RLT_DETACH_S, RLT_DETACH_KV = 1, 2
-ABI_VERSION = 2                      # include/rlt.h RLT_ABI_VERSION
+ABI_VERSION = 3                      # include/rlt.h RLT_ABI_VERSION
 
 EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_bytes",
             "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",
@@ -35,7 +35,7 @@ EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_by
             "rlt_profile_begin", "rlt_profile_collect",
             "rlt_encoder_bytes", "rlt_encoder_create", "rlt_encoder_destroy",
             "rlt_encoder_state_bytes", "rlt_encoder_state_init", "rlt_encoder_state_destroy",
-            "rlt_encoder_state_reset", "rlt_encoder_position", "rlt_encode",
+            "rlt_encoder_state_reset", "rlt_encoder_state_set_mode", "rlt_encoder_position", "rlt_encode",
             "rlt_encoder_profile_begin", "rlt_encoder_profile_collect",
             "rlt_encoder_snapshot_bytes", "rlt_encoder_state_export", "rlt_encoder_state_import",
             "rlt_bptt_workspace_bytes", "rlt_bptt_workspace_bytes_segmented", "rlt_bptt",
@@ -132,6 +132,7 @@ def load_library(path: str = LIB_PATH):
         "rlt_encoder_state_init": (i32, [vp, i32, i32, i32, vp, sz, P(vp)]),
         "rlt_encoder_state_destroy": (None, [vp]),
         "rlt_encoder_state_reset": (i32, [vp, i32, P(i32)]),
+        "rlt_encoder_state_set_mode": (i32, [vp, i32]),
         "rlt_encoder_position": (i32, [vp, i32]),
         "rlt_encode": (i32, [vp, vp, i32, P(i32), i32, vp, vp, P(rlt_memory), vp]),
         "rlt_encoder_profile_begin": (i32, [vp, i32, i32]),
@@ -539,6 +540,15 @@ class EncoderState:
 def _align_elems(n: int, dtype) -> int:
     es = 2 if dtype == torch.bfloat16 else 4
     return ((n * es + 255) // 256 * 256) // es
+
+
+RLT_ENC_EXACT, RLT_ENC_FAST = 0, 1
+
+
+def rlt_encoder_state_set_mode(es: EncoderState, mode: int):
+    """Kernel forms of the state's short calls: RLT_ENC_EXACT (bitwise the
+    prompt kernels' arithmetic) or RLT_ENC_FAST (the decoder's forms)."""
+    _check(load_library().rlt_encoder_state_set_mode(es.handle, int(mode)))
 
 
 def rlt_encoder_state_reset(es: EncoderState, slots):

@@ -1673,10 +1673,14 @@ struct rlt_encoder_state {
   int B, max_tokens, max_rows;
   char *cache_k, *cache_v;         // [L][B][H][max_tokens][dh] model dtype
   int *slots_dev, *p0_dev;         // [B] slot and first position of each listed sequence
+  int *pos_dev;                    // [B] position of every slot (fast one-token calls)
   float *x;                        // [R][d] residual stream
   char *abuf, *qbuf, *obuf, *hbuf, *ebuf;   // [R][d] / [R][F] model dtype
+  float *split;                    // K-split partial tiles of the fast short-call GEMMs
   std::vector<int> host_pos;
   std::vector<int> tbl;            // host copy of the staged slot / position table
+  std::vector<int> pos_tbl;        // host copy of the staged positions (fast calls)
+  bool fast = false;               // RLT_ENC_FAST: short calls on the decoder's kernel forms
   ProfLog plog;
 };
 
@@ -1712,12 +1716,14 @@ size_t encoder_state_layout(const rlt_config &c, rlt_encoder_state *es, void *ba
   es->cache_v = ar.take<char>((size_t)L * B * H * cap * dh * e);
   es->slots_dev = ar.take<int>((size_t)B * 4);
   es->p0_dev = ar.take<int>((size_t)B * 4);
+  es->pos_dev = ar.take<int>((size_t)B * 4);
   es->x = ar.take<float>((size_t)R * d * 4);
   es->abuf = ar.take<char>((size_t)R * d * e);
   es->qbuf = ar.take<char>((size_t)R * d * e);
   es->obuf = ar.take<char>((size_t)R * d * e);
   es->hbuf = ar.take<char>((size_t)R * c.d_ffn * e);
   es->ebuf = ar.take<char>((size_t)R * d * e);
+  es->split = ar.take<float>(pgemm_split_bytes(std::max(3 * d, c.d_ffn)));
   return align256(ar.off);
 }
 
@@ -1845,6 +1851,14 @@ rlt_status rlt_encoder_state_reset(rlt_encoder_state *es, int32_t n, const int32
   return ok();
 }
 
+rlt_status rlt_encoder_state_set_mode(rlt_encoder_state *es, int32_t mode) {
+  if (!es) return fail(RLT_ERR_INVALID_ARG, "encoder state is NULL");
+  if (mode != RLT_ENC_EXACT && mode != RLT_ENC_FAST)
+    return fail(RLT_ERR_INVALID_ARG, "mode must be RLT_ENC_EXACT or RLT_ENC_FAST (got %d)", mode);
+  es->fast = mode == RLT_ENC_FAST;
+  return ok();
+}
+
 int32_t rlt_encoder_position(const rlt_encoder_state *es, int32_t slot) {
   if (!es || slot < 0 || slot >= es->B) return -1;
   return es->host_pos[slot];
@@ -1921,12 +1935,20 @@ rlt_status enqueue_encode(const rlt_encoder *enc, rlt_encoder_state *es, const s
   hipError_t e = hipMemcpyAsync(es->slots_dev, es->tbl.data(), (size_t)n * 4, hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(es->p0_dev, es->tbl.data() + n, (size_t)n * 4, hipMemcpyHostToDevice, s);
+  // fast one-token calls: the positions of all slots, indexed by slot
+  const bool fast_attn = es->fast && T == 1;
+  if (e == hipSuccess && fast_attn) {
+    es->pos_tbl = es->host_pos;
+    e = hipMemcpyAsync(es->pos_dev, es->pos_tbl.data(), (size_t)es->B * 4, hipMemcpyHostToDevice, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "staging the slot table");
   const EncRows rows{es->slots_dev, es->p0_dev, T, R};
 
   auto gemm = [&](const PGemmArgs &a, int epi, const char *what) -> rlt_status {
     Prof p(es->plog, RLT_E_GEMM, s);
-    const hipError_t err = launch_pgemm(c.dtype, epi, a, s);
+    PGemmArgs b = a;
+    b.split = es->split;
+    const hipError_t err = es->fast ? launch_pgemm_fast(c.dtype, epi, b, s) : launch_pgemm(c.dtype, epi, a, s);
     const double flops = 2.0 * R * a.N * a.K;
     const double out_bytes = epi == PEPI_RESID ? (double)R * a.N * 8 : (double)R * a.N * esz;
     p.done((double)a.N * a.K * esz + (double)R * a.K * esz + out_bytes, flops);
@@ -1965,7 +1987,29 @@ rlt_status enqueue_encode(const rlt_encoder *enc, rlt_encoder_state *es, const s
     a.H = H;
     a.dh = dh;
     if ((rs = gemm(a, PEPI_QKV, "qkv gemm")) != RLT_OK) return rs;
-    {
+    if (fast_attn) {
+      // the decoder's attention over the encoder cache as memory: position
+      // p of a slot attends to cache positions 0..p (entry p written above)
+      AttnArgs at{};
+      at.q = es->qbuf;
+      at.out = es->obuf;
+      at.kb = ck;
+      at.vb = cv;
+      at.s_seq = s_seq;
+      at.s_head = s_head;
+      at.s_pos = dh;
+      at.len_cap = 0x7fffffff;
+      at.ch = m->chunk;
+      at.slots = es->slots_dev;
+      at.pos = es->pos_dev;
+      at.H = H;
+      at.d = d;
+      at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)dh));
+      Prof p(es->plog, RLT_E_ATTN, s);
+      e = launch_attn_rows(c.dtype, dh, at, n, s);
+      p.done(2.0 * R * d * esz + 2.0 * kv_positions * d * esz, 4.0 * attn_pairs * d);
+      if ((rs = other(e, "attention (fast one-token form)")) != RLT_OK) return rs;
+    } else {
       FAttnArgs fa{};
       fa.q = es->qbuf;
       fa.ldq = d;

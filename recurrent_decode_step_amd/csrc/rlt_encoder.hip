@@ -550,7 +550,83 @@ __device__ __forceinline__ void wait_stages(int after) {
   }
 }
 
-template <int EPI, class C>
+// Row tile tm and feature tile tn of launch tile id (the launch order of
+// k_pgemm32d: with GROUP > 0 each XCD takes a contiguous run of groups of
+// GROUP row tiles x all feature tiles).
+template <int GROUP>
+__device__ __forceinline__ void pg32_tile(int id, int mt, int nt, int &tm, int &tn) {
+  const int total = mt * nt;
+  if constexpr (GROUP > 0) {
+    const int v = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;
+    const int grp = v / (GROUP * nt);
+    const int m0 = grp * GROUP;
+    const int gm = min(GROUP, mt - m0);
+    const int w = v - grp * GROUP * nt;
+    tm = m0 + w % gm;
+    tn = w / gm;
+  } else {
+    tm = id / nt;
+    tn = id - tm * nt;
+  }
+}
+
+// Epilogue of one 32 x 32 product block (token rows tblk.., features fblk..)
+// through the wavefront's padded LDS scratch [token][feature], read back by
+// rows so a store instruction covers 8 token rows x 32 consecutive features.
+template <int EPI>
+__device__ __forceinline__ void pg32_store_block(const PGemmArgs &a, const float *acc16, int tblk,
+                                                 int fblk, int lane, float *scr) {
+  typedef f32x4 v4;
+  constexpr int EROW = 36;                           // padded row, floats
+  const int n_rows = a.rows.n_rows;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<v4 *>(scr + (lane & 31) * EROW + 8 * q + 4 * (lane >> 5)) =
+        v4{acc16[4 * q], acc16[4 * q + 1], acc16[4 * q + 2], acc16[4 * q + 3]};
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if constexpr (EPI == PEPI_RESID) {
+    // the four residual rows are read (from in-range addresses, also for
+    // outputs that are not stored) before any is written back, so that their
+    // loads are in flight together
+    v4 v[4], xo[4];
+    bool st[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
+      v[i] = *reinterpret_cast<const v4 *>(scr + tr * EROW + fc);
+      const int row = tblk + tr, n = fblk + fc;
+      st[i] = row < n_rows && n < a.N;
+      xo[i] = *reinterpret_cast<const v4 *>(a.x + (size_t)min(row, n_rows - 1) * a.ld_x +
+                                            min(n, a.N - 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
+      if (st[i])
+        *reinterpret_cast<v4 *>(a.x + (size_t)(tblk + tr) * a.ld_x + fblk + fc) =
+            v4{xo[i].x + v[i].x, xo[i].y + v[i].y, xo[i].z + v[i].z, xo[i].w + v[i].w};
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
+      const v4 v = *reinterpret_cast<const v4 *>(scr + tr * EROW + fc);
+      const int row = tblk + tr, n = fblk + fc;
+      if (row < n_rows && n < a.N) pgemm_store<bf16_t, EPI>(a, row, n, v);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// SPLIT > 1 (the fast short-call form, U > 1 configurations): launch tile
+// id + total * part multiplies packed k-steps [part S / SPLIT, (part + 1) S /
+// SPLIT) only and writes its raw accumulators to a.split (tile-major, part,
+// lane, 16 floats); k_pgemm32_reduce adds the parts and runs the epilogue.
+template <int EPI, class C, int SPLIT = 1>
 __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, int mt, int nt) {
   typedef float f32x16 __attribute__((ext_vector_type(16)));
   constexpr int NC = C::WM * C::WN;                         // wavefronts that multiply
@@ -563,22 +639,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, in
   static_assert(C::LW == 0 || C::U > 1, "staging-only wavefronts need grouped stages");
   extern __shared__ u32x4 smem[];                           // [3][FS * 64]
 
+  static_assert(SPLIT == 1 || (C::U > 1 && C::WM * C::WN == 1 && C::LW == 0), "split form");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int total = mt * nt;
-  const int id = blockIdx.x;
+  const int id = SPLIT > 1 ? (int)blockIdx.x % total : (int)blockIdx.x;
+  const int part = SPLIT > 1 ? (int)blockIdx.x / total : 0;
   int tm, tn;
-  if constexpr (C::GROUP > 0) {
-    const int v = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;
-    const int grp = v / (C::GROUP * nt);
-    const int m0 = grp * C::GROUP;
-    const int gm = min(C::GROUP, mt - m0);
-    const int w = v - grp * C::GROUP * nt;
-    tm = m0 + w % gm;
-    tn = w / gm;
-  } else {
-    tm = id / nt;
-    tn = id - tm * nt;
-  }
+  pg32_tile<C::GROUP>(id, mt, nt, tm, tn);
   const int row0 = tm * C::RB * 32, tile0 = tn * C::FB * 2;
   const int ntiles = a.Np >> 4;
   const int n_rows = a.rows.n_rows;
@@ -670,16 +737,21 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, in
     // (the products of a whole group are one branch-free block, so that the
     // LDS reads of its later stages are issued under the earlier products);
     // the last S % U stages, all issued by then, go one at a time
+    // (with SPLIT > 1 over this launch tile's share of the k-steps: stage j
+    // here is packed k-step s0 + j)
     constexpr int U = C::U, PD = C::NBUF - U;
     static_assert(PD >= 1, "stages in flight");
-    for (int k = 0; k < PD && k < S; ++k) issue(k, k);
+    const int s0 = part * S / SPLIT;
+    const int SL = (part + 1) * S / SPLIT - s0;
+    auto issue_l = [&](int j) { issue(s0 + j, j % C::NBUF); };
+    for (int k = 0; k < PD && k < SL; ++k) issue_l(k);
     int st = 0;
-    for (; st + U <= S; st += U) {
+    for (; st + U <= SL; st += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (st + PD + u < S) issue(st + PD + u, (st + PD + u) % C::NBUF);
+        if (st + PD + u < SL) issue_l(st + PD + u);
       const int last = st + U - 1;
-      const int after = min(S - 1, st + PD + U - 1) - last;
+      const int after = min(SL - 1, st + PD + U - 1) - last;
       wait_stages<FPW, PD>(after);
       __builtin_amdgcn_s_barrier();
       // all fragments of the group first, then its products in the order
@@ -713,68 +785,63 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, in
       }
       __builtin_amdgcn_s_barrier();
     }
-    if (st < S) {
+    if (st < SL) {
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
       if (C::LW == 0 || wave < NC)
-        for (; st < S; ++st) mult(st % C::NBUF);
+        for (; st < SL; ++st) mult(st % C::NBUF);
       __builtin_amdgcn_s_barrier();
     }
   }
   if (C::LW > 0 && wave >= NC) return;                      // staging only
+  if constexpr (SPLIT > 1) {
+    // this part's raw accumulators (one wavefront, one 32 x 32 block)
+    f32x4 *dst = reinterpret_cast<f32x4 *>(a.split) + (((size_t)id * SPLIT + part) * 64 + lane) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dst[q] = f32x4{acc[0][0][4 * q], acc[0][0][4 * q + 1], acc[0][0][4 * q + 2], acc[0][0][4 * q + 3]};
+    return;
+  }
 
   // epilogue through LDS, as in k_pgemm32 (every load has landed: the last wait was 0)
-  constexpr int EROW = 36;
-  float *scr = reinterpret_cast<float *>(smem) + wave * 32 * EROW;
+  float *scr = reinterpret_cast<float *>(smem) + wave * 32 * 36;
 #pragma unroll
   for (int f = 0; f < WFB; ++f) {
     const int fblk = (tile0 / 2 + wn * WFB + f) * 32;
 #pragma unroll
     for (int r = 0; r < WRB; ++r) {
+      float a16[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4 *>(scr + (lane & 31) * EROW + 8 * q + 4 * (lane >> 5)) =
-            f32x4{acc[f][r][4 * q], acc[f][r][4 * q + 1], acc[f][r][4 * q + 2], acc[f][r][4 * q + 3]};
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int tblk = row0 + (wm * WRB + r) * 32;
-      if constexpr (EPI == PEPI_RESID) {
-        // the four residual rows are read (from in-range addresses, also
-        // for outputs that are not stored) before any is written back, so
-        // that their loads are in flight together
-        f32x4 v[4], xo[4];
-        bool st[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
-          v[i] = *reinterpret_cast<const f32x4 *>(scr + tr * EROW + fc);
-          const int row = tblk + tr, n = fblk + fc;
-          st[i] = row < n_rows && n < a.N;
-          xo[i] = *reinterpret_cast<const f32x4 *>(a.x + (size_t)min(row, n_rows - 1) * a.ld_x +
-                                                   min(n, a.N - 4));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
-          if (st[i])
-            *reinterpret_cast<f32x4 *>(a.x + (size_t)(tblk + tr) * a.ld_x + fblk + fc) =
-                f32x4{xo[i].x + v[i].x, xo[i].y + v[i].y, xo[i].z + v[i].z, xo[i].w + v[i].w};
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tr = (lane >> 3) + 8 * i, fc = (lane & 7) * 4;
-          const f32x4 v = *reinterpret_cast<const f32x4 *>(scr + tr * EROW + fc);
-          const int row = tblk + tr, n = fblk + fc;
-          if (row < n_rows && n < a.N) pgemm_store<bf16_t, EPI>(a, row, n, v);
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int e = 0; e < 16; ++e) a16[e] = acc[f][r][e];
+      pg32_store_block<EPI>(a, a16, row0 + (wm * WRB + r) * 32, fblk, lane, scr);
     }
   }
+}
+
+// The parts of the fast short-call form added in part order (a fixed order:
+// the result depends on K and the part count only), then the epilogue.  One
+// wavefront per launch tile, tiles in the order k_pgemm32d placed them.
+template <int EPI, int SPLIT, int GROUP>
+__global__ __launch_bounds__(64) void k_pgemm32_reduce(PGemmArgs a, int mt, int nt) {
+  __shared__ float scr[32 * 36];
+  const int lane = threadIdx.x, id = blockIdx.x;
+  int tm, tn;
+  pg32_tile<GROUP>(id, mt, nt, tm, tn);
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(a.split) + ((size_t)id * SPLIT * 64 + lane) * 4;
+  float a16[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 v = src[q];
+    a16[4 * q] = v.x; a16[4 * q + 1] = v.y; a16[4 * q + 2] = v.z; a16[4 * q + 3] = v.w;
+  }
+#pragma unroll
+  for (int p = 1; p < SPLIT; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = src[(size_t)p * 64 * 4 + q];
+      a16[4 * q] += v.x; a16[4 * q + 1] += v.y; a16[4 * q + 2] += v.z; a16[4 * q + 3] += v.w;
+    }
+  pg32_store_block<EPI>(a, a16, tm * 32, tn * 32, lane, scr);
 }
 
 // ---------------------------------------------------------------- attention
@@ -1364,6 +1431,24 @@ hipError_t pgemm32_go(const PGemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The fast short-call form: SPLIT launch tiles per output block, then the
+// ordered reduction with the epilogue (the kernel boundary orders the two).
+template <int EPI, class C>
+hipError_t pgemm32_split_go(const PGemmArgs &a, hipStream_t s) {
+  constexpr int P = kPgSplitParts;
+  const int mt = (a.rows.n_rows + C::RB * 32 - 1) / (C::RB * 32);
+  const int nt = ((a.Np >> 5) + C::FB - 1) / C::FB;
+  if constexpr (C::LDS > 65536) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_pgemm32d<EPI, C, P>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (attr != hipSuccess) return attr;
+  }
+  (void)launch((k_pgemm32d<EPI, C, P>), dim3(mt * nt * P), dim3(C::THREADS), C::LDS, s, a, mt, nt);
+  (void)launch((k_pgemm32_reduce<EPI, P, C::GROUP>), dim3(mt * nt), dim3(64), 0, s, a, mt, nt);
+  return hipGetLastError();
+}
+
 template <class C>
 hipError_t pgemm32_epi(int epi, const PGemmArgs &a, hipStream_t s) {
   switch (epi) {
@@ -1382,6 +1467,19 @@ hipError_t launch_pgemm(int dtype, int epi, const PGemmArgs &a, hipStream_t s) {
   if (dtype != RLT_DTYPE_BF16) return pgemm_epi<float, PgDefault>(epi, a, s);
   if (a.rows.n_rows > kPgSmallRows) return pgemm32_epi<Pg32Default>(epi, a, s);
   return a.KT >= kPgLongKT ? pgemm32_epi<Pg32SmallLong>(epi, a, s) : pgemm32_epi<Pg32Small>(epi, a, s);
+}
+
+hipError_t launch_pgemm_fast(int dtype, int epi, const PGemmArgs &a, hipStream_t s) {
+  if (dtype != RLT_DTYPE_BF16 || a.rows.n_rows < 1 || a.rows.n_rows > kPgSmallRows ||
+      a.KT < kPgSplitMinKT || !a.split || a.Np % 32)
+    return launch_pgemm(dtype, epi, a, s);
+  switch (epi) {
+    case PEPI_QKV: return pgemm32_split_go<PEPI_QKV, Pg32Small>(a, s);
+    case PEPI_RESID: return pgemm32_split_go<PEPI_RESID, Pg32Small>(a, s);
+    case PEPI_GELU: return pgemm32_split_go<PEPI_GELU, Pg32Small>(a, s);
+    case PEPI_MEM: return pgemm32_split_go<PEPI_MEM, Pg32Small>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int DH>

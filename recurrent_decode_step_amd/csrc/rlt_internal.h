@@ -159,6 +159,9 @@ hipError_t launch_sample(const SampleArgs &a, int n_rows, hipStream_t s);
 // stand-in incremental encoder: e rows and memory entries of the sampled tokens
 hipError_t launch_encode(int dtype, const EncodeArgs &a, int n_rows, hipStream_t s);
 hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStream_t s);
+// the same attention over a memory-like cache with row-major output (q and out
+// [n][d]); rows by a.slots, positions by a.pos indexed by slot
+hipError_t launch_attn_rows(int dtype, int dh, const AttnArgs &a, int n_rows, hipStream_t s);
 
 // ------------------------------------------------------ persistent step
 // One decoder step as a single cooperative launch: the phases of the launch
@@ -249,6 +252,7 @@ struct PGemmArgs {
   void *kb, *vb;                            // QKV: this layer's encoder cache; MEM: this group's memory
   int64_t s_seq, s_head, s_pos;             // elements
   int d, H, dh;                             // QKV: N = 3d (q, k, v); MEM: N = 2d (k, v)
+  float *split;                             // fast short calls: K-split partial tiles
 };
 
 struct FAttnArgs {
@@ -267,6 +271,18 @@ hipError_t launch_enc_embed(int dtype, const int32_t *tokens, int n_rows, const 
 hipError_t launch_enc_norm(int dtype, const float *x, int64_t ldx, const float *gamma, float eps,
                            void *out, int64_t ldo, int n_rows, int d, hipStream_t s);
 hipError_t launch_pgemm(int dtype, int epi, const PGemmArgs &a, hipStream_t s);
+// The fast short-call form (bf16, at most 64 rows): K split over kPgSplitParts
+// workgroups, partial tiles to a.split, added in part order by a second
+// kernel that runs the epilogue.  Falls back to launch_pgemm where it does
+// not apply (fp32, more rows, K under kPgSplitMinKT packed k-steps).
+hipError_t launch_pgemm_fast(int dtype, int epi, const PGemmArgs &a, hipStream_t s);
+constexpr int kPgSplitParts = 4;
+constexpr int kPgSplitMinKT = 128;
+// bytes of a.split that the fast form needs for GEMMs of at most n_max outputs
+// (two 32-row tiles of 32 x 32 fp32 partials per part)
+inline size_t pgemm_split_bytes(int n_max) {
+  return (size_t)2 * ((n_max + 31) / 32) * kPgSplitParts * 64 * 16 * sizeof(float);
+}
 hipError_t launch_fattn(int dtype, int dh, const FAttnArgs &a, hipStream_t s);
 
 // Encoder-cache snapshot records (rlt_encoder_state_export / _import): per

@@ -908,7 +908,7 @@ __device__ __forceinline__ void attn_chunk(const float *qf, const u32x4 *kr, con
 // runs it as the whole workgroup; the persistent step kernel runs two groups
 // side by side.  A group with no work (valid = false) passes the workgroup
 // barrier too.
-template <typename T, int DH, int UU, bool WT, class SY = NoSync>
+template <typename T, int DH, int UU, bool WT, class SY = NoSync, bool ROW = false>
 __device__ __forceinline__ void attn_item(const AttnArgs &a, int i, int h, bool valid, int tid,
                                           float (*s_o)[DH], float (*s_ml)[2],
                                           const SY &sy = SY(), bool pre = true) {
@@ -1002,8 +1002,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int i, int h, bool 
     sc[w] = exp2f(s_ml[w][0] - M);               // a wavefront with no positions has m = -inf
     L += s_ml[w][1] * sc[w];
   }
-  // output fragment-packed (the input layout of the next GEMM): one 16-byte
-  // fragment of EPL consecutive values per thread
+  // output fragment-packed (the input layout of the next GEMM; ROW: rows of
+  // d values, the encoder's layout): one 16-byte piece of EPL consecutive
+  // values per thread
   for (int f = tid; f < DH / EPL; f += kAttnThreads) {
     float v[EPL];
 #pragma unroll
@@ -1013,13 +1014,15 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int i, int h, bool 
       for (int w = 0; w < 4; ++w) acc += s_o[w][f * EPL + e] * sc[w];
       v[e] = acc / L;
     }
-    st_u32x4<WT>(static_cast<T *>(a.out) + packed_off<T>(i, h * DH + f * EPL, a.kt_out),
-                 Num<T>::pack(v));
+    T *dst = static_cast<T *>(a.out) +
+             (ROW ? (size_t)i * a.d + h * DH + f * EPL : packed_off<T>(i, h * DH + f * EPL, a.kt_out));
+    st_u32x4<WT>(dst, Num<T>::pack(v));
   }
 }
 
 // KIND 0: sliding window over the decoder cache; 1: encoder memory (the same
-// code, two symbols so profiles keep them apart)
+// code, two symbols so profiles keep them apart); 2: the encoder's own cache
+// in its one-token calls of the fast short-call mode, output in rows
 template <typename T, int DH, int KIND, int UU = 0>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void k_attn(const AttnArgs a) {
@@ -1027,7 +1030,7 @@ void k_attn(const AttnArgs a) {
   __shared__ float s_ml[4][2];
   const int i = a.order ? a.order[blockIdx.y] : (int)blockIdx.x;
   const int h = a.order ? (int)blockIdx.x : (int)blockIdx.y;
-  attn_item<T, DH, UU, false>(a, i, h, true, (int)threadIdx.x, s_o, s_ml);
+  attn_item<T, DH, UU, false, NoSync, KIND == 2>(a, i, h, true, (int)threadIdx.x, s_o, s_ml);
 }
 
 // ---------------------------------------------------------------- scoring
@@ -1537,6 +1540,12 @@ hipError_t launch_attn(int dtype, int dh, const AttnArgs &a, int n_rows, hipStre
   if (dtype == RLT_DTYPE_BF16)
     return mem ? attn_dispatch<bf16_t, 1>(dh, a, n_rows, s) : attn_dispatch<bf16_t, 0>(dh, a, n_rows, s);
   return mem ? attn_dispatch<float, 1>(dh, a, n_rows, s) : attn_dispatch<float, 0>(dh, a, n_rows, s);
+}
+
+hipError_t launch_attn_rows(int dtype, int dh, const AttnArgs &a, int n_rows, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  return dtype == RLT_DTYPE_BF16 ? attn_dispatch<bf16_t, 2>(dh, a, n_rows, s)
+                                 : attn_dispatch<float, 2>(dh, a, n_rows, s);
 }
 
 // ---------------------------------------------------------- persistent step

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding.EXPORTED)
-    assert L.rlt_abi_version() == 2
+    assert L.rlt_abi_version() == 3
 
 
 def test_status_strings():
@@ -152,18 +152,22 @@ def test_encoder_null_handles_and_sizes():
     assert L.rlt_encoder_state_init(None, 2, 16, 8, None, 0, C.byref(out)) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_encode(None, None, 1, None, 1, None, None, None, None) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_encoder_state_reset(None, 1, None) == binding.RLT_ERR_INVALID_ARG
+    assert L.rlt_encoder_state_set_mode(None, binding.RLT_ENC_FAST) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_encoder_position(None, 0) == -1
     assert L.rlt_encoder_profile_begin(None, 1, 1) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_encoder_profile_collect(None, 0, None, None, None, None) == binding.RLT_ERR_INVALID_ARG
-    # the encoder state holds the cache [L][B][H][cap][dh] twice plus per-row scratch
+    # the encoder state holds the cache [L][B][H][cap][dh] twice, per-row scratch
+    # and the partial tiles of the fast short-call GEMMs (two 32-row tiles x
+    # max(3d, F) / 32 feature tiles x 4 parts x 4 KiB)
     for w in (TINY, SMALL, REFDEPTH):
         m = w.model
         es = 2 if m.dtype == 1 else 4
         B, cap, R = 4, 96, 40
         cache = 2 * m.n_layers * B * m.d_model * cap * es
         scratch = R * m.d_model * (4 + 4 * es) + R * m.d_ffn * es
+        split = 2 * ((max(3 * m.d_model, m.d_ffn) + 31) // 32) * 4 * 4096
         got = L.rlt_encoder_state_bytes(C.byref(cfg_of(w)), B, cap, R)
-        assert cache + scratch <= got <= cache + scratch + 16 * 256
+        assert cache + scratch + split <= got <= cache + scratch + split + 16 * 256
     assert L.rlt_encoder_state_bytes(C.byref(cfg_of(TINY)), 0, 16, 8) == 0
     assert L.rlt_encoder_state_bytes(C.byref(cfg_of(TINY)), 2, 16, 0) == 0
     # bf16 with head_dim 16 is outside the encoder kernels

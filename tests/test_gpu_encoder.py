@@ -449,6 +449,95 @@ def test_generate_encoded_equals_encode_then_run_sequence_bitwise():
     assert torch.equal(snap_a, snap_b)
 
 
+@pytest.mark.parametrize("d,H,F,dtype", [(256, 2, 4096, 1), (128, 2, 256, 1), (128, 4, 256, 1),
+                                         (128, 2, 4096, 0)],
+                         ids=["bf16_dh128_splitK", "bf16_dh64", "bf16_dh32", "fp32_dh64"])
+def test_fast_short_calls_match_exact_and_oracle(d, H, F, dtype):
+    """RLT_ENC_FAST: one-token calls take the decoder's attention form and,
+    when K >= 4096 (bf16), a K split over four workgroups added in part order.
+    After a 70-token prompt (one exact call), 20 one-token calls per sequence:
+    e rows and memory within rounding of the exact mode (bf16 rel-L2 <= 1e-2,
+    fp32 max |delta| <= 1e-4) and of the oracle (bf16 2e-2, fp32 1e-4); the
+    same bits on a second run; and a sequence stepped alone gets the same bits
+    as inside the batch."""
+    cfg = ModelConfig(vocab=120, d_model=d, n_heads=H, n_layers=2, d_ffn=F, window=8,
+                      mem_groups=1, dtype=dtype)
+    B, P, n = 5, 70, 20
+    T = P + n
+    say(f"[encoder fast] d={d} H={H} F={F} dtype={dtype}")
+    tok = torch.from_numpy(synth.token_ids(B, T, cfg.vocab, index=13)).to(DEV)
+    params, eparams, model, enc, es, mk, mv = setup(cfg, B, 96, B * P)
+
+    def run(slots, mode):
+        st_ = binding.EncoderState(enc, B, 96, B * P)
+        mk_, mv_ = torch.zeros_like(mk), torch.zeros_like(mv)
+        binding.rlt_encode(enc, st_, tok[slots, :P].contiguous(), (mk_, mv_), slots=slots)
+        binding.rlt_encoder_state_set_mode(st_, mode)
+        rows = [binding.rlt_encode(enc, st_, tok[slots, j:j + 1].contiguous(), (mk_, mv_), slots=slots)
+                for j in range(P, T)]
+        torch.cuda.synchronize()
+        return torch.cat(rows, dim=1), mk_, mv_
+
+    slots = list(range(B))
+    e_x, mk_x, mv_x = run(slots, binding.RLT_ENC_EXACT)
+    e_f, mk_f, mv_f = run(slots, binding.RLT_ENC_FAST)
+    e_f2, mk_f2, mv_f2 = run(slots, binding.RLT_ENC_FAST)
+    assert torch.isfinite(e_f).all()
+    assert torch.equal(e_f, e_f2) and torch.equal(mk_f, mk_f2) and torch.equal(mv_f, mv_f2)
+    e_one, mk_one, _ = run([3], binding.RLT_ENC_FAST)
+    assert torch.equal(e_one[0], e_f[3])
+    assert torch.equal(mk_one[:, 3, :, :T], mk_f[:, 3, :, :T])
+    if dtype == 1:
+        rel = rel_l2(f64(e_f), f64(e_x))
+        relm = rel_l2(f64(mk_f[:, :, :, P:T]), f64(mk_x[:, :, :, P:T]))
+        say(f"[encoder fast] fast vs exact: e rel-L2 {rel:.2e}, memory k rel-L2 {relm:.2e}")
+        assert rel <= 1e-2 and relm <= 1e-2
+    else:
+        worst = float((e_f - e_x).abs().max())
+        say(f"[encoder fast] fast vs exact: e max |delta| {worst:.2e}")
+        assert worst <= 1e-4
+    oe = oracle_encoder(cfg, params, eparams, "bf16" if dtype == 1 else "fp32")
+    r = oracle.encode(oe, tok.cpu().numpy()[1, :T])
+    if dtype == 1:
+        rel = rel_l2(f64(e_f[1]), r["e"][P:T])
+        say(f"[encoder fast] seq 1 against the oracle: rel-L2 {rel:.2e}")
+        assert rel <= 2e-2
+    else:
+        worst = float(np.abs(f64(e_f[1]) - r["e"][P:T]).max())
+        say(f"[encoder fast] seq 1 against the oracle: max |delta| {worst:.2e}")
+        assert worst <= 1e-4
+
+
+def test_generate_encoded_fast_equals_token_calls_then_run_sequence_bitwise():
+    """With RLT_ENC_FAST set, generation leaves the decoder state, last logits
+    and memory exactly where encoding the generated tokens one call per token
+    (fast) and running rlt_run_sequence over their e rows leaves them."""
+    cfg = ModelConfig(vocab=96, d_model=256, n_heads=2, n_layers=2, d_ffn=4096, window=4,
+                      mem_groups=1, dtype=1)
+    B, P, n = 4, 6, 5
+    params, eparams, model, enc, es, mk, mv, prompts, st, pre = _prefilled(cfg, B, P, n)
+    binding.rlt_encoder_state_set_mode(es, binding.RLT_ENC_FAST)
+    u = synth.uniforms((B, n), index=9).to(DEV)
+    say("[generate encoded fast bitwise]")
+    tok, lp, last = binding.rlt_generate_encoded(model, st, pre, enc, es, (mk, mv), 1.0, 40, u)
+    assert torch.isfinite(lp).all()
+    es2 = binding.EncoderState(enc, B, P + n, B * (P + n))
+    mk2, mv2 = torch.zeros_like(mk), torch.zeros_like(mv)
+    e_pre = binding.rlt_encode(enc, es2, torch.from_numpy(prompts).to(DEV), (mk2, mv2))
+    st2 = binding.State(model, B, P + n)
+    binding.rlt_run_sequence(model, st2, e_pre, (mk2, mv2), logits_mode=binding.RLT_LOGITS_NONE)
+    binding.rlt_encoder_state_set_mode(es2, binding.RLT_ENC_FAST)
+    e_gen = torch.cat([binding.rlt_encode(enc, es2, tok[:, j:j + 1].contiguous(), (mk2, mv2))
+                       for j in range(n)], dim=1)
+    rep = binding.rlt_run_sequence(model, st2, e_gen, (mk2, mv2))
+    torch.cuda.synchronize()
+    assert torch.equal(rep[:, -1], last)
+    assert torch.equal(mk, mk2) and torch.equal(mv, mv2)
+    with pytest.raises(binding.RLTError) as ex:
+        binding.rlt_encoder_state_set_mode(es2, 2)
+    assert ex.value.status == binding.RLT_ERR_INVALID_ARG
+
+
 def test_generate_encoded_needs_matching_positions():
     """The encoder must hold exactly the tokens the decoder consumed: a slot
     whose decoder state is one token ahead is a range error, found before any
