@@ -1677,6 +1677,7 @@ struct rlt_encoder_state {
   float *x;                        // [R][d] residual stream
   char *abuf, *qbuf, *obuf, *hbuf, *ebuf;   // [R][d] / [R][F] model dtype
   float *split;                    // K-split partial tiles of the fast short-call GEMMs
+  unsigned *split_cnt;             // parts finished per output tile (0 between launches)
   std::vector<int> host_pos;
   std::vector<int> tbl;            // host copy of the staged slot / position table
   std::vector<int> pos_tbl;        // host copy of the staged positions (fast calls)
@@ -1724,6 +1725,7 @@ size_t encoder_state_layout(const rlt_config &c, rlt_encoder_state *es, void *ba
   es->hbuf = ar.take<char>((size_t)R * c.d_ffn * e);
   es->ebuf = ar.take<char>((size_t)R * d * e);
   es->split = ar.take<float>(pgemm_split_bytes(std::max(3 * d, c.d_ffn)));
+  es->split_cnt = ar.take<unsigned>(pgemm_split_counters(std::max(3 * d, c.d_ffn)) * 4);
   return align256(ar.off);
 }
 
@@ -1830,6 +1832,14 @@ rlt_status rlt_encoder_state_init(const rlt_encoder *enc, int32_t batch, int32_t
   es->max_rows = max_rows;
   encoder_state_layout(c, es, dev_buf, batch, max_tokens, max_rows);
   es->host_pos.assign(batch, 0);
+  // the fast short-call GEMMs' tile counters start at zero (and every launch
+  // leaves them at zero)
+  const hipError_t e = hipMemset(es->split_cnt, 0,
+                                 pgemm_split_counters(std::max(3 * c.d_model, c.d_ffn)) * 4);
+  if (e != hipSuccess) {
+    delete es;
+    return hip_fail(e, "clearing the encoder state's tile counters");
+  }
   *out = es;
   return ok();
 }
@@ -1948,6 +1958,7 @@ rlt_status enqueue_encode(const rlt_encoder *enc, rlt_encoder_state *es, const s
     Prof p(es->plog, RLT_E_GEMM, s);
     PGemmArgs b = a;
     b.split = es->split;
+    b.split_cnt = es->split_cnt;
     const hipError_t err = es->fast ? launch_pgemm_fast(c.dtype, epi, b, s) : launch_pgemm(c.dtype, epi, a, s);
     const double flops = 2.0 * R * a.N * a.K;
     const double out_bytes = epi == PEPI_RESID ? (double)R * a.N * 8 : (double)R * a.N * esz;

@@ -625,7 +625,8 @@ __device__ __forceinline__ void pg32_store_block(const PGemmArgs &a, const float
 // SPLIT > 1 (the fast short-call form, U > 1 configurations): launch tile
 // id + total * part multiplies packed k-steps [part S / SPLIT, (part + 1) S /
 // SPLIT) only and writes its raw accumulators to a.split (tile-major, part,
-// lane, 16 floats); k_pgemm32_reduce adds the parts and runs the epilogue.
+// lane, 16 floats); the last part of a tile to finish adds them in part order
+// (a fixed order: the result depends on K and SPLIT only) and stores.
 template <int EPI, class C, int SPLIT = 1>
 __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, int mt, int nt) {
   typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -795,11 +796,40 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, in
   }
   if (C::LW > 0 && wave >= NC) return;                      // staging only
   if constexpr (SPLIT > 1) {
-    // this part's raw accumulators (one wavefront, one 32 x 32 block)
-    f32x4 *dst = reinterpret_cast<f32x4 *>(a.split) + (((size_t)id * SPLIT + part) * 64 + lane) * 4;
+    // This part's raw accumulators (one wavefront, one 32 x 32 block),
+    // written through and waited for, then counted: the part that counts
+    // last adds all parts in part order (addresses nothing read earlier in
+    // the launch, so its loads see the other parts' stores), resets the
+    // counter for the next launch and runs the epilogue.  No part waits.
+    uint64_t *dst = reinterpret_cast<uint64_t *>(a.split) + (((size_t)id * SPLIT + part) * 64 + lane) * 8;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      dst[q] = f32x4{acc[0][0][4 * q], acc[0][0][4 * q + 1], acc[0][0][4 * q + 2], acc[0][0][4 * q + 3]};
+    for (int q = 0; q < 8; ++q)
+      __hip_atomic_store(dst + q,
+                         (uint64_t)__float_as_uint(acc[0][0][2 * q]) |
+                             ((uint64_t)__float_as_uint(acc[0][0][2 * q + 1]) << 32),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    unsigned done = 0;
+    if (lane == 0)
+      done = __hip_atomic_fetch_add(a.split_cnt + id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    done = __builtin_amdgcn_readfirstlane(done);
+    if (done != SPLIT - 1) return;
+    if (lane == 0) __hip_atomic_store(a.split_cnt + id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(a.split) + ((size_t)id * SPLIT * 64 + lane) * 4;
+    float a16[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = src[q];
+      a16[4 * q] = v.x; a16[4 * q + 1] = v.y; a16[4 * q + 2] = v.z; a16[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int p = 1; p < SPLIT; ++p)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = src[(size_t)p * 64 * 4 + q];
+        a16[4 * q] += v.x; a16[4 * q + 1] += v.y; a16[4 * q + 2] += v.z; a16[4 * q + 3] += v.w;
+      }
+    pg32_store_block<EPI>(a, a16, row0, tile0 / 2 * 32, lane, reinterpret_cast<float *>(smem));
     return;
   }
 
@@ -816,32 +846,6 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void k_pgemm32d(PGemmArgs a, in
       pg32_store_block<EPI>(a, a16, row0 + (wm * WRB + r) * 32, fblk, lane, scr);
     }
   }
-}
-
-// The parts of the fast short-call form added in part order (a fixed order:
-// the result depends on K and the part count only), then the epilogue.  One
-// wavefront per launch tile, tiles in the order k_pgemm32d placed them.
-template <int EPI, int SPLIT, int GROUP>
-__global__ __launch_bounds__(64) void k_pgemm32_reduce(PGemmArgs a, int mt, int nt) {
-  __shared__ float scr[32 * 36];
-  const int lane = threadIdx.x, id = blockIdx.x;
-  int tm, tn;
-  pg32_tile<GROUP>(id, mt, nt, tm, tn);
-  const f32x4 *src = reinterpret_cast<const f32x4 *>(a.split) + ((size_t)id * SPLIT * 64 + lane) * 4;
-  float a16[16];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x4 v = src[q];
-    a16[4 * q] = v.x; a16[4 * q + 1] = v.y; a16[4 * q + 2] = v.z; a16[4 * q + 3] = v.w;
-  }
-#pragma unroll
-  for (int p = 1; p < SPLIT; ++p)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 v = src[(size_t)p * 64 * 4 + q];
-      a16[4 * q] += v.x; a16[4 * q + 1] += v.y; a16[4 * q + 2] += v.z; a16[4 * q + 3] += v.w;
-    }
-  pg32_store_block<EPI>(a, a16, tm * 32, tn * 32, lane, scr);
 }
 
 // ---------------------------------------------------------------- attention
@@ -1431,13 +1435,10 @@ hipError_t pgemm32_go(const PGemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The fast short-call form: SPLIT launch tiles per output block, then the
-// ordered reduction with the epilogue (the kernel boundary orders the two).
-template <int EPI, class C>
-hipError_t pgemm32_split_go(const PGemmArgs &a, hipStream_t s) {
-  constexpr int P = kPgSplitParts;
-  const int mt = (a.rows.n_rows + C::RB * 32 - 1) / (C::RB * 32);
-  const int nt = ((a.Np >> 5) + C::FB - 1) / C::FB;
+// The fast short-call form: P launch tiles per output block, the last of
+// which adds the parts and stores.
+template <int EPI, class C, int P>
+hipError_t pgemm32_split_go(const PGemmArgs &a, int mt, int nt, hipStream_t s) {
   if constexpr (C::LDS > 65536) {
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&k_pgemm32d<EPI, C, P>),
@@ -1445,8 +1446,13 @@ hipError_t pgemm32_split_go(const PGemmArgs &a, hipStream_t s) {
     if (attr != hipSuccess) return attr;
   }
   (void)launch((k_pgemm32d<EPI, C, P>), dim3(mt * nt * P), dim3(C::THREADS), C::LDS, s, a, mt, nt);
-  (void)launch((k_pgemm32_reduce<EPI, P, C::GROUP>), dim3(mt * nt), dim3(64), 0, s, a, mt, nt);
   return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t pgemm32_split_parts(int parts, const PGemmArgs &a, int mt, int nt, hipStream_t s) {
+  return parts == 4 ? pgemm32_split_go<EPI, Pg32Small, 4>(a, mt, nt, s)
+                    : pgemm32_split_go<EPI, Pg32Small, 2>(a, mt, nt, s);
 }
 
 template <class C>
@@ -1470,14 +1476,20 @@ hipError_t launch_pgemm(int dtype, int epi, const PGemmArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_pgemm_fast(int dtype, int epi, const PGemmArgs &a, hipStream_t s) {
-  if (dtype != RLT_DTYPE_BF16 || a.rows.n_rows < 1 || a.rows.n_rows > kPgSmallRows ||
-      a.KT < kPgSplitMinKT || !a.split || a.Np % 32)
+  if (dtype != RLT_DTYPE_BF16 || a.rows.n_rows < 1 || a.rows.n_rows > kPgSmallRows || !a.split ||
+      !a.split_cnt || a.Np % 32)
     return launch_pgemm(dtype, epi, a, s);
+  const int mt = (a.rows.n_rows + 31) / 32, nt = a.Np >> 5;
+  // as many parts as keep a 32-row launch at about 256 workgroups (one per
+  // CU); a function of N and K only, so that a row's result does not depend
+  // on how many rows share the call
+  const int parts = nt * 4 <= 256 ? 4 : nt * 2 <= 256 ? 2 : 1;
+  if (parts == 1 || a.KT < kPgSplitMinKT * parts) return launch_pgemm(dtype, epi, a, s);
   switch (epi) {
-    case PEPI_QKV: return pgemm32_split_go<PEPI_QKV, Pg32Small>(a, s);
-    case PEPI_RESID: return pgemm32_split_go<PEPI_RESID, Pg32Small>(a, s);
-    case PEPI_GELU: return pgemm32_split_go<PEPI_GELU, Pg32Small>(a, s);
-    case PEPI_MEM: return pgemm32_split_go<PEPI_MEM, Pg32Small>(a, s);
+    case PEPI_QKV: return pgemm32_split_parts<PEPI_QKV>(parts, a, mt, nt, s);
+    case PEPI_RESID: return pgemm32_split_parts<PEPI_RESID>(parts, a, mt, nt, s);
+    case PEPI_GELU: return pgemm32_split_parts<PEPI_GELU>(parts, a, mt, nt, s);
+    case PEPI_MEM: return pgemm32_split_parts<PEPI_MEM>(parts, a, mt, nt, s);
   }
   return hipErrorInvalidValue;
 }

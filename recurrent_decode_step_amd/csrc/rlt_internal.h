@@ -253,6 +253,7 @@ struct PGemmArgs {
   int64_t s_seq, s_head, s_pos;             // elements
   int d, H, dh;                             // QKV: N = 3d (q, k, v); MEM: N = 2d (k, v)
   float *split;                             // fast short calls: K-split partial tiles
+  unsigned *split_cnt;                      // and the parts finished per output tile (0 between launches)
 };
 
 struct FAttnArgs {
@@ -271,18 +272,22 @@ hipError_t launch_enc_embed(int dtype, const int32_t *tokens, int n_rows, const 
 hipError_t launch_enc_norm(int dtype, const float *x, int64_t ldx, const float *gamma, float eps,
                            void *out, int64_t ldo, int n_rows, int d, hipStream_t s);
 hipError_t launch_pgemm(int dtype, int epi, const PGemmArgs &a, hipStream_t s);
-// The fast short-call form (bf16, at most 64 rows): K split over kPgSplitParts
-// workgroups, partial tiles to a.split, added in part order by a second
-// kernel that runs the epilogue.  Falls back to launch_pgemm where it does
-// not apply (fp32, more rows, K under kPgSplitMinKT packed k-steps).
+// The fast short-call form (bf16, at most 64 rows): K split over 2 or 4
+// workgroups per output tile (as many as keep a 32-row launch near 256
+// workgroups: a function of N and K only),
+// each writing its partial tile to a.split; the last to finish, found by the
+// tile's counter in a.split_cnt, adds the parts in part order and runs the
+// epilogue.  Falls back to launch_pgemm where it does not apply (fp32, more
+// rows, no split worth it, K under kPgSplitMinKT packed k-steps per part).
 hipError_t launch_pgemm_fast(int dtype, int epi, const PGemmArgs &a, hipStream_t s);
-constexpr int kPgSplitParts = 4;
-constexpr int kPgSplitMinKT = 128;
-// bytes of a.split that the fast form needs for GEMMs of at most n_max outputs
-// (two 32-row tiles of 32 x 32 fp32 partials per part)
+constexpr int kPgSplitParts = 4;          // at most
+constexpr int kPgSplitMinKT = 16;         // packed k-steps per part, at least
+// bytes of a.split, and counters in a.split_cnt, for GEMMs of at most n_max
+// outputs (two 32-row tiles of 32 x 32 fp32 partials per part)
 inline size_t pgemm_split_bytes(int n_max) {
   return (size_t)2 * ((n_max + 31) / 32) * kPgSplitParts * 64 * 16 * sizeof(float);
 }
+inline size_t pgemm_split_counters(int n_max) { return (size_t)2 * ((n_max + 31) / 32); }
 hipError_t launch_fattn(int dtype, int dh, const FAttnArgs &a, hipStream_t s);
 
 // Encoder-cache snapshot records (rlt_encoder_state_export / _import): per

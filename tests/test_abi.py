@@ -158,14 +158,14 @@ def test_encoder_null_handles_and_sizes():
     assert L.rlt_encoder_profile_collect(None, 0, None, None, None, None) == binding.RLT_ERR_INVALID_ARG
     # the encoder state holds the cache [L][B][H][cap][dh] twice, per-row scratch
     # and the partial tiles of the fast short-call GEMMs (two 32-row tiles x
-    # max(3d, F) / 32 feature tiles x 4 parts x 4 KiB)
+    # max(3d, F) / 32 feature tiles x 4 parts x 4 KiB, one counter per tile)
     for w in (TINY, SMALL, REFDEPTH):
         m = w.model
         es = 2 if m.dtype == 1 else 4
         B, cap, R = 4, 96, 40
         cache = 2 * m.n_layers * B * m.d_model * cap * es
         scratch = R * m.d_model * (4 + 4 * es) + R * m.d_ffn * es
-        split = 2 * ((max(3 * m.d_model, m.d_ffn) + 31) // 32) * 4 * 4096
+        split = 2 * ((max(3 * m.d_model, m.d_ffn) + 31) // 32) * (4 * 4096 + 4)   # tiles, counters
         got = L.rlt_encoder_state_bytes(C.byref(cfg_of(w)), B, cap, R)
         assert cache + scratch + split <= got <= cache + scratch + split + 16 * 256
     assert L.rlt_encoder_state_bytes(C.byref(cfg_of(TINY)), 0, 16, 8) == 0

@@ -449,22 +449,28 @@ def test_generate_encoded_equals_encode_then_run_sequence_bitwise():
     assert torch.equal(snap_a, snap_b)
 
 
-@pytest.mark.parametrize("d,H,F,dtype", [(256, 2, 4096, 1), (128, 2, 256, 1), (128, 4, 256, 1),
-                                         (128, 2, 4096, 0)],
-                         ids=["bf16_dh128_splitK", "bf16_dh64", "bf16_dh32", "fp32_dh64"])
-def test_fast_short_calls_match_exact_and_oracle(d, H, F, dtype):
-    """RLT_ENC_FAST: one-token calls take the decoder's attention form and,
-    when K >= 4096 (bf16), a K split over four workgroups added in part order.
-    After a 70-token prompt (one exact call), 20 one-token calls per sequence:
+@pytest.mark.parametrize("d,H,F,dtype,B", [(256, 2, 4096, 1, 5), (1024, 8, 4096, 1, 5),
+                                           (1024, 8, 4096, 1, 40), (128, 2, 256, 1, 5),
+                                           (128, 4, 256, 1, 5), (128, 2, 4096, 0, 5)],
+                         ids=["bf16_dh128_split4", "bf16_split2_and_4", "bf16_split_two_row_tiles",
+                              "bf16_dh64", "bf16_dh32", "fp32_dh64"])
+def test_fast_short_calls_match_exact_and_oracle(d, H, F, dtype, B):
+    """RLT_ENC_FAST: one-token calls take the decoder's attention form, and
+    bf16 GEMMs of at most 64 rows split K over 2 or 4 workgroups (as many as
+    keep a launch near 256 workgroups, at least 16 packed k-steps each), the
+    last of which adds the parts in part order; the split depends on N and K
+    only.  At d = 1024 QKV and FFN-up split in two and FFN-down in four, with
+    5 rows (one row tile) or 40 (two).  After a 70-token prompt (one exact
+    call), 20 one-token calls per sequence:
     e rows and memory within rounding of the exact mode (bf16 rel-L2 <= 1e-2,
     fp32 max |delta| <= 1e-4) and of the oracle (bf16 2e-2, fp32 1e-4); the
     same bits on a second run; and a sequence stepped alone gets the same bits
     as inside the batch."""
     cfg = ModelConfig(vocab=120, d_model=d, n_heads=H, n_layers=2, d_ffn=F, window=8,
                       mem_groups=1, dtype=dtype)
-    B, P, n = 5, 70, 20
+    P, n = 70, 20
     T = P + n
-    say(f"[encoder fast] d={d} H={H} F={F} dtype={dtype}")
+    say(f"[encoder fast] d={d} H={H} F={F} dtype={dtype} B={B}")
     tok = torch.from_numpy(synth.token_ids(B, T, cfg.vocab, index=13)).to(DEV)
     params, eparams, model, enc, es, mk, mv = setup(cfg, B, 96, B * P)
 
