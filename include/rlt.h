@@ -375,7 +375,9 @@ size_t rlt_encoder_state_bytes(const rlt_config *cfg, int32_t batch, int32_t max
                                int32_t max_rows);
 
 /* Lay out an encoder state in dev_buf with every slot at position 0 (no
- * tokens encoded).  No device work. */
+ * tokens encoded).  The only device work is clearing the small array of tile
+ * counters the fast short-call mode uses (a synchronous memset of
+ * 8 * ceil(max(3 d_model, d_ffn) / 32) bytes); RLT_ERR_DEVICE if it fails. */
 rlt_status rlt_encoder_state_init(const rlt_encoder *enc, int32_t batch, int32_t max_tokens,
                                   int32_t max_rows, void *dev_buf, size_t bytes,
                                   rlt_encoder_state **out);
@@ -390,11 +392,13 @@ rlt_status rlt_encoder_state_reset(rlt_encoder_state *es, int32_t n, const int32
  *   RLT_ENC_EXACT (the default): every call runs the prompt kernels'
  *     arithmetic, so a prompt gives bitwise the same values however it is
  *     split into calls.
- *   RLT_ENC_FAST: calls of at most 64 token rows with K >= 4096 split K over
- *     four workgroups (parts added in a fixed order), and calls of one token
- *     per sequence take the decoder's attention form (independent wavefront
- *     streams); values agree with the exact mode up to rounding, do not
- *     depend on the other rows of a call and are the same on every run.
+ *   RLT_ENC_FAST: the bf16 GEMMs of calls of at most 64 token rows split K
+ *     over 2 or 4 workgroups where N leaves room (a function of N and K only;
+ *     the parts added in a fixed order), and calls of one token per sequence
+ *     take the decoder's attention form (independent wavefront streams);
+ *     values agree with the exact mode up to rounding, do not depend on the
+ *     other rows of a call and are the same on every run.  Calls in fast mode
+ *     on one state must not overlap (the split's tile counters live in it).
  * Applies to the calls made after it, rlt_generate_encoded's included.
  * RLT_ERR_INVALID_ARG for another mode.  Host only. */
 #define RLT_ENC_EXACT 0
