@@ -400,7 +400,10 @@ rlt_status rlt_encoder_state_reset(rlt_encoder_state *es, int32_t n, const int32
  *     other rows of a call and are the same on every run.  Calls in fast mode
  *     on one state must not overlap (the split's tile counters live in it).
  * Applies to the calls made after it, rlt_generate_encoded's included.
- * RLT_ERR_INVALID_ARG for another mode.  Host only. */
+ * Selecting RLT_ENC_FAST also clears the tile counters (a synchronous memset;
+ * every complete launch leaves them clear, so this only matters after a
+ * device error).  RLT_ERR_INVALID_ARG for another mode, RLT_ERR_DEVICE if the
+ * memset fails. */
 #define RLT_ENC_EXACT 0
 #define RLT_ENC_FAST 1
 rlt_status rlt_encoder_state_set_mode(rlt_encoder_state *es, int32_t mode);

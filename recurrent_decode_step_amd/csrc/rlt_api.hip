@@ -1865,6 +1865,13 @@ rlt_status rlt_encoder_state_set_mode(rlt_encoder_state *es, int32_t mode) {
   if (!es) return fail(RLT_ERR_INVALID_ARG, "encoder state is NULL");
   if (mode != RLT_ENC_EXACT && mode != RLT_ENC_FAST)
     return fail(RLT_ERR_INVALID_ARG, "mode must be RLT_ENC_EXACT or RLT_ENC_FAST (got %d)", mode);
+  if (mode == RLT_ENC_FAST) {
+    // tile counters at zero (they are after every complete launch; this
+    // re-arms them after a launch that did not complete)
+    const hipError_t e = hipMemset(es->split_cnt, 0,
+                                   pgemm_split_counters(std::max(3 * es->cfg.d_model, es->cfg.d_ffn)) * 4);
+    if (e != hipSuccess) return hip_fail(e, "clearing the encoder state's tile counters");
+  }
   es->fast = mode == RLT_ENC_FAST;
   return ok();
 }
