@@ -43,6 +43,10 @@ Other measurements (each prints its own JSON line; not the default):
   --peaks                 the device's achievable HBM read/copy and bf16 MFMA
                           rates (also added to the reference-depth line as
                           "achievable", measured after the timed region)
+  --vendor-gemms          the step's GEMM sequence (reference-depth shapes,
+                          weights per layer) through the vendor GEMM library
+                          at --vendor-rows rows, for comparison with the
+                          decoder's own GEMM kernels (kernel time by rocprofv3)
 """
 from __future__ import annotations
 
@@ -1328,6 +1332,58 @@ def cpu_train_baseline(cfg, params, e, mk, mv, tg, budget_s=15.0):
                       f"12 layers; {el:.1f} s timed, {spent:.1f} s over the doubling lengths)"}
 
 
+def run_vendor_gemms(args):
+    """The decoder step's GEMM sequence (merge, then per layer QKV, O, Qc, Oc,
+    FFN-up, FFN-down, then the head) at the reference-depth model with its own
+    weights per layer, run through torch.nn.functional.linear in bf16 (the
+    vendor GEMM library) at 32 or 256 rows: the library's rate on the same
+    shapes and weight streams, beside the decoder's own GEMM kernels.  No
+    norms, epilogues or attention: plain products only.  The wall time here
+    includes the host's per-call cost; the kernel time comes from a
+    rocprofv3 kernel trace of the same command."""
+    import torch
+    import torch.nn.functional as Fn
+    from recurrent_decode_step_amd.configs import REFDEPTH
+    cfg = REFDEPTH.model
+    L, d, F, V = cfg.n_layers, cfg.d_model, cfg.d_ffn, cfg.vocab
+    M = args.vendor_rows
+    K = args.steps or 10
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev).manual_seed(0)
+
+    def w(n, k):
+        return (torch.randn(n, k, device=dev, generator=g) * 0.02).to(torch.bfloat16).contiguous()
+    layers = [(w(3 * d, d), w(d, d), w(d, d), w(d, d), w(F, d), w(d, F)) for _ in range(L)]
+    wg, wout = w(d, 2 * d), w(V, d)
+    xs = {k: torch.randn(M, k, device=dev, generator=g).to(torch.bfloat16) for k in (d, 2 * d, F)}
+
+    def step():
+        Fn.linear(xs[2 * d], wg)
+        for qkv, o, qc, oc, up, down in layers:
+            for wm in (qkv, o, qc, oc, up):
+                Fn.linear(xs[d], wm)
+            Fn.linear(xs[F], down)
+        Fn.linear(xs[d], wout)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    flops = gemm_flops_per_step(cfg, M)
+    return {"mode": "vendor GEMM sequence (torch.nn.functional.linear, bf16)", "rows": M,
+            "steps": K, "warmup": args.warmup, "gemm_flops_per_step": flops,
+            "wall_ms_per_step": round(ms, 4),
+            "wall_TFLOPs": round(flops / (ms / 1e3) / 1e12, 1),
+            "note": "wall time includes the host's per-call cost; take the kernel time from "
+                    "rocprofv3 --kernel-trace --stats of this command"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1370,6 +1426,9 @@ def main():
                     help="tiny/small/refdepth --steps K: one persistent launch per decoder step")
     ap.add_argument("--peaks", action="store_true",
                     help="only the achievable HBM and MFMA rates of the device")
+    ap.add_argument("--vendor-gemms", action="store_true",
+                    help="the step's GEMM sequence through the vendor GEMM library (comparison)")
+    ap.add_argument("--vendor-rows", type=int, default=256, help="rows for --vendor-gemms")
     ap.add_argument("--breakdown", action="store_true",
                     help="time every kernel class on the sampled steps (adds event records)")
     args = ap.parse_args()
@@ -1381,6 +1440,8 @@ def main():
     if args.peaks:
         import torch
         out = {"mode": "peaks", **measure_peaks(torch.device("cuda", 0))}
+    elif args.vendor_gemms:
+        out = run_vendor_gemms(args)
     elif args.counters_sample:
         out = run_counters_sample(args)
     elif args.encode:

@@ -288,27 +288,29 @@ def test_large_batch_kernels_match_small_batch_bitwise(shape):
     """Steps over more than 64 rows run the persistent GEMM (activations held
     in registers, many tiles per workgroup; d_ffn = 4096 also takes its
     chunked long-K form; d_model = 128 gives parts of 4 k-steps, fewer than a
-    load batch, whose guarded MFMAs must be skipped, not run lane-masked);
-    the same slots stepped in groups of at most 64 rows run the per-tile
-    GEMM.  The arithmetic is the same, so the logits are bitwise equal."""
+    load batch, whose guarded MFMAs must be skipped, not run lane-masked;
+    vocab 60 and 300 leave a ragged last tile); the same slots stepped in
+    groups of at most 64 rows run the per-tile GEMM.  200, 150 and 100 rows
+    give 4, 3 and 2 column groups, the last one ragged.  The arithmetic is
+    the same, so the logits are bitwise equal."""
     cfg = BF16_SMALL.with_(**shape)
-    B, T = 100, 4
+    B, T = 200, 4
     rig = Rig(cfg, B, T, attn_chunk=4)
     say(f"[large batch] shape={shape} B={B}")
     full = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, rig.mem).cpu()
     assert torch.isfinite(full).all()
     st = rig.state()
-    groups = [list(range(0, 64)), list(range(64, 100))]
+    groups = [list(range(0, 64)), list(range(64, 164)), list(range(164, 200))]
     out = torch.empty_like(full)
     for j in range(T):
         for g in groups:
             out[g, j] = binding.rlt_decoder_step(rig.model, st, rig.ed[g, j], rig.mem, slots=g).cpu()
     assert torch.equal(out, full)
-    # more than 64 rows through an explicit, permuted slot list (persistent GEMM
-    # with slots), the remaining rows in a second call
+    # 150 rows through an explicit, permuted slot list (persistent GEMM with
+    # slots and a ragged last column group), the remaining rows in a second call
     st2 = rig.state()
     perm = [int(x) for x in np.random.default_rng(9).permutation(B)]
-    big, rest = perm[:80], perm[80:]
+    big, rest = perm[:150], perm[150:]
     out2 = torch.empty_like(full)
     for j in range(T):
         for g in (big, rest):
