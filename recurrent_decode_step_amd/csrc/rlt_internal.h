@@ -146,8 +146,8 @@ hipError_t launch_gemm(int dtype, int ncb, int tpw, int act, int epi, const Gemm
                        int col_groups, int parts, hipStream_t s);
 // the grid of launch_gemm: tile groups, column groups and XCD placement (b->K set)
 void gemm_grid(int dtype, int ncb, int tpw, int tiles, int col_groups, GemmArgs *b);
-// Large batches (bf16, plain activations, more than 64 rows): persistent
-// GEMM with the same arithmetic as launch_gemm.  gemm_persistent_applies
+// Large batches (bf16, more than 64 rows; plain activations, or the gate's
+// rows for the merge): persistent GEMM with the same arithmetic as launch_gemm.  gemm_persistent_applies
 // says whether it takes a shape; launch_gemm_persistent reports real errors.
 bool gemm_persistent_applies(int dtype, int act, int epi, int n_rows, int KT, int parts);
 hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int tiles, int n_rows,

@@ -602,6 +602,9 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm(const GemmArgs a) {
 template <typename T, int NCB, int EPI, bool SHORT>
 __global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
   constexpr int SC = 8;
+  // the gate's input [e_t ; s_{t-1}] is read from its rows (and the slots'
+  // states), every other input from the packed activations
+  constexpr int ACT = EPI == EPI_MERGE ? ACT_MERGE : ACT_PLAIN;
   constexpr int COLS = NCB * 16;
   constexpr bool SCALED = EPI == EPI_QKV || EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_LOGITS;
   __shared__ f32x4 s_acc[2][kMaxParts][NCB][64];
@@ -624,11 +627,12 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
   const int ks0 = (wave * KT) / NW;
   const int nks = ((wave + 1) * KT) / NW - ks0;
 
-  int cbg[NCB], irow[NCB];
+  int cbg[NCB], irow[NCB], slot[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     cbg[cb] = min(cg * NCB + cb, (a.n_rows - 1) >> 4);
     irow[cb] = col0 + min(cb * 16 + (lane & 15), ncols - 1);
+    slot[cb] = ACT == ACT_MERGE ? slot_of(a, irow[cb]) : 0;
   }
   auto wload = [&](u32x4 *dst, int tile, int c0, int nc) {
     const u32x4 *wp = static_cast<const u32x4 *>(a.wp) + ((size_t)tile * a.KT + ks0 + c0) * 64 + lane;
@@ -641,7 +645,7 @@ __global__ __launch_bounds__(kMaxParts * 64) void k_gemm_p(const GemmArgs a) {
     for (int j = 0; j < SC; ++j)
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
-        av[j][cb] = load_b<T, ACT_PLAIN>(a, cbg[cb], irow[cb], 0, ks0 + c0 + min(j, nc - 1), lane);
+        av[j][cb] = load_b<T, ACT>(a, cbg[cb], irow[cb], slot[cb], ks0 + c0 + min(j, nc - 1), lane);
   };
   auto chain = [&](f32x4 *acc, const u32x4 *w, int nc) {
 #pragma unroll
@@ -1455,12 +1459,12 @@ constexpr int kPersistentWorkgroups = 256;   // one per CU
 // longer parts stream them in chunks, 32-row groups
 static bool persistent_short(int KT, int parts) { return (KT + parts - 1) / parts <= 8; }
 static int persistent_ncb(int epi, int KT, int parts) {
-  return persistent_short(KT, parts) && epi != EPI_RESID ? 4 : 2;
+  return persistent_short(KT, parts) && epi != EPI_RESID && epi != EPI_MERGE ? 4 : 2;
 }
 
 bool gemm_persistent_applies(int dtype, int act, int epi, int n_rows, int KT, int parts) {
-  if (dtype != RLT_DTYPE_BF16 || act != ACT_PLAIN || n_rows <= 64 || parts < 1 || parts > kMaxParts)
-    return false;
+  if (dtype != RLT_DTYPE_BF16 || n_rows <= 64 || parts < 1 || parts > kMaxParts) return false;
+  if (act != (epi == EPI_MERGE ? ACT_MERGE : ACT_PLAIN)) return false;
   const int ncb = persistent_ncb(epi, KT, parts);
   return 8 * ((n_rows + 16 * ncb - 1) / (16 * ncb)) <= kPersistentWorkgroups;
 }
@@ -1468,7 +1472,8 @@ bool gemm_persistent_applies(int dtype, int act, int epi, int n_rows, int KT, in
 hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int tiles, int n_rows,
                                   int parts, hipStream_t s) {
   constexpr int kWorkgroups = kPersistentWorkgroups;
-  if (!gemm_persistent_applies(dtype, ACT_PLAIN, epi, n_rows, a.KT, parts) || tiles < 1)
+  if (!gemm_persistent_applies(dtype, epi == EPI_MERGE ? ACT_MERGE : ACT_PLAIN, epi, n_rows, a.KT,
+                               parts) || tiles < 1)
     return hipErrorInvalidValue;
   const bool short_k = persistent_short(a.KT, parts);
   const int ncb = persistent_ncb(epi, a.KT, parts);
@@ -1491,6 +1496,7 @@ hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int til
     RLT_GP(EPI_RESID, 2)
     RLT_GP(EPI_GELU, 4)
     RLT_GP(EPI_LOGITS, 4)
+    RLT_GP(EPI_MERGE, 2)
     default: return hipErrorInvalidValue;
   }
 #undef RLT_GP
