@@ -376,8 +376,9 @@ size_t rlt_encoder_state_bytes(const rlt_config *cfg, int32_t batch, int32_t max
 
 /* Lay out an encoder state in dev_buf with every slot at position 0 (no
  * tokens encoded).  The only device work is clearing the small array of tile
- * counters the fast short-call mode uses (a synchronous memset of
- * 8 * ceil(max(3 d_model, d_ffn) / 32) bytes); RLT_ERR_DEVICE if it fails. */
+ * counters the fast short-call mode uses (a memset of
+ * 8 * ceil(max(3 d_model, d_ffn) / 32) bytes on the null stream, waited for
+ * before the call returns); RLT_ERR_DEVICE if it fails. */
 rlt_status rlt_encoder_state_init(const rlt_encoder *enc, int32_t batch, int32_t max_tokens,
                                   int32_t max_rows, void *dev_buf, size_t bytes,
                                   rlt_encoder_state **out);
@@ -400,9 +401,9 @@ rlt_status rlt_encoder_state_reset(rlt_encoder_state *es, int32_t n, const int32
  *     other rows of a call and are the same on every run.  Calls in fast mode
  *     on one state must not overlap (the split's tile counters live in it).
  * Applies to the calls made after it, rlt_generate_encoded's included.
- * Selecting RLT_ENC_FAST also clears the tile counters (a synchronous memset;
- * every complete launch leaves them clear, so this only matters after a
- * device error).  RLT_ERR_INVALID_ARG for another mode, RLT_ERR_DEVICE if the
+ * Selecting RLT_ENC_FAST also clears the tile counters (a memset on the null
+ * stream, waited for before the call returns; every complete launch leaves
+ * them clear, so this only matters after a device error).  RLT_ERR_INVALID_ARG for another mode, RLT_ERR_DEVICE if the
  * memset fails. */
 #define RLT_ENC_EXACT 0
 #define RLT_ENC_FAST 1

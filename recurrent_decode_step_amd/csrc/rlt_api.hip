@@ -1048,6 +1048,15 @@ rlt_status check_positions(const rlt_state *st, const rlt_memory *mem, int n,
   return RLT_OK;
 }
 
+// Zero device memory for calls that take no stream: the memset goes to the
+// null stream and is waited for, so work later enqueued on any stream
+// (blocking or not) finds the memory cleared.
+hipError_t clear_now(void *p, size_t bytes) {
+  hipError_t e = hipMemset(p, 0, bytes);
+  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  return e;
+}
+
 rlt_status device_health() {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "earlier device error");
@@ -1834,7 +1843,7 @@ rlt_status rlt_encoder_state_init(const rlt_encoder *enc, int32_t batch, int32_t
   es->host_pos.assign(batch, 0);
   // the fast short-call GEMMs' tile counters start at zero (and every launch
   // leaves them at zero)
-  const hipError_t e = hipMemset(es->split_cnt, 0,
+  const hipError_t e = clear_now(es->split_cnt,
                                  pgemm_split_counters(std::max(3 * c.d_model, c.d_ffn)) * 4);
   if (e != hipSuccess) {
     delete es;
@@ -1868,7 +1877,7 @@ rlt_status rlt_encoder_state_set_mode(rlt_encoder_state *es, int32_t mode) {
   if (mode == RLT_ENC_FAST) {
     // tile counters at zero (they are after every complete launch; this
     // re-arms them after a launch that did not complete)
-    const hipError_t e = hipMemset(es->split_cnt, 0,
+    const hipError_t e = clear_now(es->split_cnt,
                                    pgemm_split_counters(std::max(3 * es->cfg.d_model, es->cfg.d_ffn)) * 4);
     if (e != hipSuccess) return hip_fail(e, "clearing the encoder state's tile counters");
   }
