@@ -436,7 +436,7 @@ def run_refdepth_stratified(args):
     cfg = wl.model
     B, T_total = wl.batch, wl.steps
     K = args.steps
-    n_states = min(K, 20)
+    n_states = min(K, args.strata)
     starts, counts = stratified_positions(T_total, K, n_states)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -1416,6 +1416,8 @@ def main():
     ap.add_argument("--counters-sample", action="store_true",
                     help="a few reference-depth steps at the sampled mean position (counter passes)")
     ap.add_argument("--sample-steps", type=int, default=4)
+    ap.add_argument("--strata", type=int, default=20,
+                    help="reference depth --steps K: position strata (resident states), at most K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--progress", action="store_true",
