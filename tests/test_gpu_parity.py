@@ -203,13 +203,18 @@ BF16_TINY_CASES = {
     "d64-F256": (dict(d_model=64, d_ffn=256), 0, 5, 12),
     "d128-F512-B20": (dict(d_model=128, n_heads=2, d_ffn=512), 3, 20, 12),
     "d256-G2-W3": (dict(d_model=256, n_heads=4, mem_groups=2, window=3), 0, 4, 10),
+    # attention at dh 128 and 256 (16 and 32 lanes per position), the window
+    # wrapping and the memory longer than one chunk of positions
+    "dh128-W6": (dict(d_model=256, n_heads=2, d_ffn=256, vocab=45, window=6), 16, 3, 40),
+    "dh256-W5": (dict(d_model=256, n_heads=1, d_ffn=128, vocab=33, window=5), 0, 2, 40),
 }
 
 
 @pytest.mark.parametrize("name", list(BF16_TINY_CASES))
 def test_bf16_small_dims_match_oracle_per_step(name):
-    """bf16 models with short K: every step checked from the library's own
-    exported state (rel-L2 of the logits <= 2e-2), and logits finite."""
+    """bf16 models with short K and every head size the attention kernels
+    take: every step checked from the library's own exported state (rel-L2
+    of the logits <= 2e-2), and logits finite."""
     kw, chunk, B, T = BF16_TINY_CASES[name]
     cfg = tiny_cfg(dtype=DTYPE_BF16, **kw)
     say(f"[bf16 small dims] case={name} cfg={kw} chunk={chunk} B={B} T={T}")
