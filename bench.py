@@ -1434,6 +1434,8 @@ def main():
     ap.add_argument("--breakdown", action="store_true",
                     help="time every kernel class on the sampled steps (adds event records)")
     args = ap.parse_args()
+    if args.strata < 1:
+        ap.error("--strata must be >= 1")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decoder step shards by sequence with no "
               "communication, so N GPUs run N independent copies; run it with --gpus 1.",
