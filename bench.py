@@ -27,7 +27,8 @@ Other measurements (each prints its own JSON line; not the default):
                           W = 1024: K consecutive batched steps from imported
                           states, MFMA utilisation of the GEMM kernels
   --workload tiny|small   the tiny fp32 and small bf16 configs, whole runs
-                          (launch-bound; reported, not targeted)
+                          (launch-bound; reported, not targeted); --fused:
+                          the tiny run as one launch, one workgroup per sequence
   --workload longctx      d = 4096, 8 sequences, T = 32768: 64-step windows
                           from imported states at six start positions, per-step
                           time fitted as a + b min(t, W) + c t and summed
@@ -687,9 +688,14 @@ def run_full_sequence(args, wl):
     logits = torch.empty((B, T, cfg.vocab), dtype=torch.float32, device=dev)
     ws = binding.StepWorkspace(model, B) if args.persistent else None
 
+    if args.fused and not binding.fused_supported(cfg):
+        raise SystemExit(f"--fused: {wl.name} does not fit one workgroup's LDS")
+
     def run(ee, lg=None):
         if ws is not None:
             return binding.rlt_run_sequence_persistent(model, state, ee, mem, ws, logits=lg)
+        if args.fused:
+            return binding.rlt_run_sequence_fused(model, state, ee, mem, logits=lg)
         return binding.rlt_run_sequence(model, state, ee, mem, logits=lg)
 
     run(e[:, :min(4, T)])                                               # warm-up
@@ -715,7 +721,8 @@ def run_full_sequence(args, wl):
         "config": {"workload": wl.name, "batch": B, "positions": f"1..{T}",
                    "repeats": "median of 5 full runs", "logits": "every step, fp32",
                    "step": "persistent (one cooperative launch per step)" if ws is not None
-                           else "launch chain (2 + 8L launches per step)"},
+                           else ("fused (the whole run in one launch, one workgroup per sequence)"
+                                 if args.fused else "launch chain (2 + 8L launches per step)")},
         "step_roofline": {"bound": "hbm", "algorithmic_GB_per_step": round(bytes_run / T / 1e9, 5),
                           "achieved": round(bytes_run / (ms / 1e3) / 1e9, 1), "peak": HBM_PEAK_GBS,
                           "unit": "GB/s",
@@ -1426,6 +1433,8 @@ def main():
                     help="run one 256 MiB streaming kernel before warmup (counter scaling)")
     ap.add_argument("--persistent", action="store_true",
                     help="tiny/small/refdepth --steps K: one persistent launch per decoder step")
+    ap.add_argument("--fused", action="store_true",
+                    help="tiny: the whole run in one launch (rlt_run_sequence_fused)")
     ap.add_argument("--peaks", action="store_true",
                     help="only the achievable HBM and MFMA rates of the device")
     ap.add_argument("--vendor-gemms", action="store_true",

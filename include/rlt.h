@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define RLT_ABI_VERSION 3
+#define RLT_ABI_VERSION 4
 
 typedef enum {
   RLT_OK = 0,
@@ -261,6 +261,28 @@ rlt_status rlt_persistent_check(void *dev_workspace, void *stream);
  * rlt_persistent_check then reports RLT_ERR_DEVICE and the state's contents
  * and positions are undefined until it is reset. */
 void rlt_persistent_test_stall(int32_t on);
+
+/* rlt_run_sequence for small fp32 models, as one launch for the whole call:
+ * workgroup b runs all T steps of slot b (the recurrence is sequential
+ * within a sequence and sequences never interact [Princeton, architecture
+ * and design-principles paragraphs]), with the model's weights unpacked once
+ * into its LDS and the slot's window cache mirrored there, so the phases of
+ * a step are separated by workgroup barriers only -- the kernel fusion the
+ * pages list among the implementation targets, for models where the launch
+ * chain would pay a kernel boundary for a few hundred multiply-adds.
+ * Arguments, semantics and errors as rlt_run_sequence (the state, window
+ * cache and positions it leaves are those the launch chain would leave, up
+ * to rounding), plus RLT_ERR_UNSUPPORTED unless rlt_fused_supported(cfg).
+ * Results: fp32 sums in a fixed order per output (not the chain's MFMA
+ * order), so they match the chain and the CPU oracle up to rounding, and
+ * splitting a run into calls changes no bit. */
+int32_t rlt_fused_supported(const rlt_config *cfg);   /* 1: fp32, at most 16 layers,
+                                                          heads * window <= 256, and
+                                                          weights, gains, one slot's window
+                                                          cache and activations in 160 KiB */
+rlt_status rlt_run_sequence_fused(const rlt_model *m, rlt_state *st, int32_t T, const void *dev_e,
+                                  const rlt_memory *mem, float *dev_logits, int32_t logits_mode,
+                                  void *stream);
 
 /* Replay scoring [Tutorial, "Current-Policy Reinforcement Learning Replay":
  * rebuild the states from the sequence start under the current weights,

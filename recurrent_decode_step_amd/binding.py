@@ -23,12 +23,13 @@ RLT_LOGITS_ALL, RLT_LOGITS_LAST, RLT_LOGITS_NONE = 0, 1, 2
 RLT_K_EXTRA, RLT_K_GEMM, RLT_K_SWA, RLT_K_CROSS = 0, 1, 2, 3
 RLT_E_GEMM, RLT_E_ATTN, RLT_E_OTHER = 0, 1, 2
 RLT_DETACH_S, RLT_DETACH_KV = 1, 2
-ABI_VERSION = 3                      # include/rlt.h RLT_ABI_VERSION
+ABI_VERSION = 4                      # include/rlt.h RLT_ABI_VERSION
 
 EXPORTED = ("rlt_abi_version", "rlt_status_str", "rlt_last_error", "rlt_model_bytes",
             "rlt_model_create", "rlt_model_destroy", "rlt_state_bytes", "rlt_state_init",
             "rlt_state_destroy", "rlt_state_reset", "rlt_decoder_step", "rlt_decoder_step_noalloc",
-            "rlt_run_sequence", "rlt_persistent_workspace_bytes", "rlt_run_sequence_persistent",
+            "rlt_run_sequence", "rlt_fused_supported", "rlt_run_sequence_fused",
+            "rlt_persistent_workspace_bytes", "rlt_run_sequence_persistent",
             "rlt_persistent_check", "rlt_persistent_test_stall",
             "rlt_score_sequence", "rlt_generate", "rlt_generate_encoded",
             "rlt_state_position", "rlt_snapshot_bytes", "rlt_state_export", "rlt_state_import",
@@ -110,6 +111,8 @@ def load_library(path: str = LIB_PATH):
         "rlt_decoder_step": (i32, [vp, vp, i32, P(i32), vp, P(rlt_memory), vp, vp]),
         "rlt_decoder_step_noalloc": (i32, [vp, vp, i32, P(i32), vp, P(rlt_memory), vp, vp]),
         "rlt_run_sequence": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, i32, vp]),
+        "rlt_fused_supported": (i32, [P(rlt_config)]),
+        "rlt_run_sequence_fused": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, i32, vp]),
         "rlt_persistent_workspace_bytes": (sz, [P(rlt_config), i32]),
         "rlt_run_sequence_persistent": (i32, [vp, vp, i32, vp, P(rlt_memory), vp, i32, vp, sz, vp]),
         "rlt_persistent_check": (i32, [vp, vp]),
@@ -305,6 +308,28 @@ def rlt_run_sequence(model: Model, state: State, e: torch.Tensor, memory,
     _check(lib.rlt_run_sequence(model.handle, state.handle, T, e.data_ptr(), C.byref(mem),
                                 logits.data_ptr() if logits is not None else None, logits_mode,
                                 _stream(stream)))
+    return logits
+
+
+def fused_supported(cfg) -> bool:
+    """Whether rlt_run_sequence_fused takes models of this configuration."""
+    return bool(load_library().rlt_fused_supported(C.byref(make_config(cfg, 0))))
+
+
+def rlt_run_sequence_fused(model: Model, state: State, e: torch.Tensor, memory,
+                           logits_mode: int = RLT_LOGITS_ALL, logits=None, stream=None):
+    """rlt_run_sequence as one launch (one workgroup per slot, weights in LDS;
+    small fp32 models); same arguments and logits."""
+    lib = load_library()
+    B, T = e.shape[0], e.shape[1]
+    e = e.contiguous()
+    if logits is None and logits_mode != RLT_LOGITS_NONE:
+        shape = (B, T, model.cfg.vocab) if logits_mode == RLT_LOGITS_ALL else (B, model.cfg.vocab)
+        logits = torch.empty(shape, dtype=torch.float32, device=e.device)
+    mem = memory if isinstance(memory, rlt_memory) else memory_view(*memory)
+    _check(lib.rlt_run_sequence_fused(model.handle, state.handle, T, e.data_ptr(), C.byref(mem),
+                                      logits.data_ptr() if logits is not None else None,
+                                      logits_mode, _stream(stream)))
     return logits
 
 

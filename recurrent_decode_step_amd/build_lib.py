@@ -16,7 +16,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["csrc/rlt_api.hip", "csrc/rlt_kernels.hip", "csrc/rlt_encoder.hip", "csrc/rlt_train.hip",
-           "csrc/rlt_peaks.hip"]
+           "csrc/rlt_peaks.hip", "csrc/rlt_fused.hip"]
 OUT = os.path.join(HERE, "librlt.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 

@@ -1332,6 +1332,81 @@ rlt_status rlt_run_sequence(const rlt_model *m, rlt_state *st, int32_t T, const 
   return ok();
 }
 
+int32_t rlt_fused_supported(const rlt_config *cfg) {
+  if (!cfg || check_config(cfg) != RLT_OK || cfg->dtype != RLT_DTYPE_F32) return 0;
+  if (cfg->n_layers > kFusedMaxLayers || cfg->n_heads * cfg->window > 256) return 0;
+  return fused_lds_bytes(cfg->d_model, cfg->n_heads, cfg->head_dim, cfg->n_layers, cfg->d_ffn,
+                         cfg->vocab, cfg->window) <= kFusedMaxLds;
+}
+
+rlt_status rlt_run_sequence_fused(const rlt_model *m, rlt_state *st, int32_t T, const void *dev_e,
+                                  const rlt_memory *mem, float *dev_logits, int32_t logits_mode,
+                                  void *stream) {
+  rlt_status rs;
+  if ((rs = check_state(m, st)) != RLT_OK) return rs;
+  if (!rlt_fused_supported(&m->cfg))
+    return fail(RLT_ERR_UNSUPPORTED,
+                "the fused run takes fp32 models of at most %d layers with heads x window <= 256 "
+                "whose weights fit in %zu bytes of LDS", kFusedMaxLayers, kFusedMaxLds);
+  if (T < 1) return fail(RLT_ERR_INVALID_ARG, "T must be >= 1");
+  if (!dev_e) return fail(RLT_ERR_INVALID_ARG, "dev_e is NULL");
+  if (logits_mode != RLT_LOGITS_ALL && logits_mode != RLT_LOGITS_LAST &&
+      logits_mode != RLT_LOGITS_NONE)
+    return fail(RLT_ERR_INVALID_ARG, "bad logits_mode");
+  if (logits_mode != RLT_LOGITS_NONE && !dev_logits)
+    return fail(RLT_ERR_INVALID_ARG, "dev_logits is NULL");
+  if ((rs = check_memory(m, mem, st->B - 1)) != RLT_OK) return rs;
+  if ((rs = check_positions(st, mem, st->B, nullptr, T)) != RLT_OK) return rs;
+  if ((rs = device_health()) != RLT_OK) return rs;
+  const rlt_config &c = m->cfg;
+  FusedArgs a;
+  memset(&a, 0, sizeof a);
+  a.d = c.d_model;
+  a.H = c.n_heads;
+  a.dh = c.head_dim;
+  a.L = c.n_layers;
+  a.F = c.d_ffn;
+  a.V = c.vocab;
+  a.W = c.window;
+  a.G = c.mem_groups;
+  a.T = T;
+  a.B = st->B;
+  a.eps = c.rms_eps;
+  a.scale = (float)(1.0 / sqrt((double)c.head_dim));
+  a.wg = static_cast<const float *>(m->wg.p);
+  a.bg = m->bg;
+  a.wout = static_cast<const float *>(m->wout.p);
+  a.go = m->go;
+  for (int l = 0; l < c.n_layers; ++l) {
+    a.wqkv[l] = static_cast<const float *>(m->wqkv[l].p);
+    a.wo[l] = static_cast<const float *>(m->wo[l].p);
+    a.wqc[l] = static_cast<const float *>(m->wqc[l].p);
+    a.woc[l] = static_cast<const float *>(m->woc[l].p);
+    a.w1[l] = static_cast<const float *>(m->w1[l].p);
+    a.w2[l] = static_cast<const float *>(m->w2[l].p);
+  }
+  a.g1 = m->g1;
+  a.g2 = m->g2;
+  a.g3 = m->g3;
+  a.s = st->s;
+  a.pos = st->pos;
+  a.ring_k = reinterpret_cast<float *>(st->ring_k);
+  a.ring_v = reinterpret_cast<float *>(st->ring_v);
+  a.e = static_cast<const float *>(dev_e);
+  a.mk = static_cast<const float *>(mem->k);
+  a.mv = static_cast<const float *>(mem->v);
+  a.sg = mem->stride_group;
+  a.ss = mem->stride_seq;
+  a.sh = mem->stride_head;
+  a.sp = mem->stride_pos;
+  a.logits = dev_logits;
+  a.logits_mode = logits_mode;
+  const hipError_t e = launch_fused_run(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fused run launch");
+  for (int i = 0; i < st->B; ++i) st->host_pos[i] += T;
+  return ok();
+}
+
 size_t rlt_persistent_workspace_bytes(const rlt_config *cfg, int32_t n) {
   if (check_config(cfg) != RLT_OK || n < 1) return 0;
   StepBufs b;

@@ -152,6 +152,25 @@ void gemm_grid(int dtype, int ncb, int tpw, int tiles, int col_groups, GemmArgs 
 bool gemm_persistent_applies(int dtype, int act, int epi, int n_rows, int KT, int parts);
 hipError_t launch_gemm_persistent(int dtype, int epi, const GemmArgs &a, int tiles, int n_rows,
                                   int parts, hipStream_t s);
+// The whole run of every slot in one workgroup per slot (fp32 models whose
+// weights, gains, window cache of one slot and activations fit in LDS).
+constexpr int kFusedMaxLayers = 16;
+constexpr size_t kFusedMaxLds = (size_t)160 << 10;
+struct FusedArgs {
+  int d, H, dh, L, F, V, W, G, T, B;
+  float eps, scale;                         // RMSNorm epsilon, 1 / sqrt(dh)
+  const float *wg, *bg, *wout, *go;         // packed [d][2d], [V][d]; b_g, gamma_o
+  const float *wqkv[kFusedMaxLayers], *wo[kFusedMaxLayers], *wqc[kFusedMaxLayers],
+      *woc[kFusedMaxLayers], *w1[kFusedMaxLayers], *w2[kFusedMaxLayers];
+  const float *g1, *g2, *g3;                // [L][d]
+  float *s; int *pos;                       // state [B][d], [B]
+  float *ring_k, *ring_v;                   // state window cache [L][B][H][W][dh]
+  const float *e;                           // [B][T][d]
+  const float *mk, *mv; int64_t sg, ss, sh, sp;   // memory and its strides (elements)
+  float *logits; int logits_mode;           // ALL: [B][T][V]; LAST: [B][V]; NONE
+};
+size_t fused_lds_bytes(int d, int H, int dh, int L, int F, int V, int W);
+hipError_t launch_fused_run(const FusedArgs &a, hipStream_t s);
 // log softmax of each row's logits at its realized token (one workgroup per row)
 hipError_t launch_score(const ScoreArgs &a, int n_rows, hipStream_t s);
 // sampling from each row's logits (temperature, top-k truncation, inverse CDF in token order)

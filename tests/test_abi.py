@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(binding.EXPORTED)
-    assert L.rlt_abi_version() == 3
+    assert L.rlt_abi_version() == binding.ABI_VERSION == 4
 
 
 def test_status_strings():
@@ -187,3 +187,18 @@ def test_bptt_host_checks():
                       None, None, 0, None) == binding.RLT_ERR_INVALID_ARG
     assert L.rlt_bptt(C.byref(cfg_of(SMALL)), C.byref(p), 2, 4, None, None, None, None, C.byref(p),
                       None, None, None, None, 0, None) == binding.RLT_ERR_UNSUPPORTED
+
+
+def test_fused_run_support_rule():
+    """rlt_fused_supported (host only): fp32 models whose weights, gains, one
+    slot's window cache and activations fit in 160 KiB of LDS."""
+    from _tiny import tiny_cfg
+    from recurrent_decode_step_amd.configs import DTYPE_BF16, SMALL
+    ok = [tiny_cfg(), tiny_cfg(window=1), tiny_cfg(window=32), tiny_cfg(n_heads=1),
+          tiny_cfg(n_layers=3, mem_groups=3, d_ffn=64)]
+    for cfg in ok:
+        assert binding.fused_supported(cfg), cfg
+    no = [tiny_cfg(dtype=DTYPE_BF16), tiny_cfg(window=64), tiny_cfg(n_layers=3, mem_groups=3),
+          tiny_cfg(d_model=64, n_heads=2), SMALL.model]
+    for cfg in no:
+        assert not binding.fused_supported(cfg), cfg
