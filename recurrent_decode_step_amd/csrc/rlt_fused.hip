@@ -11,10 +11,12 @@
 // interact.  For a model this small every phase of a step is a few hundred
 // multiply-adds, so the launch chain pays a kernel boundary for almost no
 // work.  Here workgroup b runs all T steps of slot b: the packed weights are
-// unpacked once into LDS (k-major, so consecutive threads read consecutive
-// banks), the slot's window cache is mirrored in LDS (every entry the run
+// unpacked once into LDS (k-major with an odd row stride; each output of a
+// product is summed by a group of lanes that split K and meet in a
+// butterfly), the slot's window cache is mirrored in LDS (every entry the run
 // reads comes from the mirror; each new entry is also stored to the state),
-// and the phases of a step are separated by workgroup barriers only.  No
+// the memory is read in chunks staged into LDS with all loads in flight, and
+// the phases of a step are separated by workgroup barriers only.  No
 // workgroup waits for another.
 //
 // Arithmetic: fp32 throughout, sums in a fixed order per output, so a run is
