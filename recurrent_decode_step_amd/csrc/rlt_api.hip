@@ -589,6 +589,9 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, const StepScratch &w,
       gc.groups = cdiv(n, gc.ncb * 16);
       tpw = gc.ncb <= 2 ? g.tpw : 1;
     }
+    // one 16-row column group whose tile pairs leave CUs without a workgroup
+    // (N = 4096 at 16 rows or fewer): one tile per wavefront
+    if (gc.ncb == 1 && tpw > 1 && (g.tiles / tpw) * gc.groups < kFillWorkgroups) tpw = 1;
     // large batches: the persistent kernel (same arithmetic, activations in
     // registers, many tiles per workgroup)
     const hipError_t e2 =

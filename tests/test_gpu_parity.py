@@ -295,9 +295,11 @@ def test_large_batch_kernels_match_small_batch_bitwise(shape):
     chunked long-K form; d_model = 128 gives parts of 4 k-steps, fewer than a
     load batch, whose guarded MFMAs must be skipped, not run lane-masked;
     vocab 60 and 300 leave a ragged last tile); the same slots stepped in
-    groups of at most 64 rows run the per-tile GEMM.  200, 150 and 100 rows
-    give 4, 3 and 2 column groups, the last one ragged.  The arithmetic is
-    the same, so the logits are bitwise equal."""
+    groups of at most 64 rows run the per-tile GEMM (8 rows: one 16-row
+    column group, and with d_ffn = 4096 the FFN-up's 256 tiles one per
+    wavefront).  200, 150 and 100 rows give 4, 3 and 2 column groups, the
+    last one ragged.  The arithmetic is the same, so the logits are bitwise
+    equal."""
     cfg = BF16_SMALL.with_(**shape)
     B, T = 200, 4
     rig = Rig(cfg, B, T, attn_chunk=4)
@@ -305,7 +307,7 @@ def test_large_batch_kernels_match_small_batch_bitwise(shape):
     full = binding.rlt_run_sequence(rig.model, rig.state(), rig.ed, rig.mem).cpu()
     assert torch.isfinite(full).all()
     st = rig.state()
-    groups = [list(range(0, 64)), list(range(64, 164)), list(range(164, 200))]
+    groups = [list(range(0, 8)), list(range(8, 64)), list(range(64, 164)), list(range(164, 200))]
     out = torch.empty_like(full)
     for j in range(T):
         for g in groups:
