@@ -53,6 +53,7 @@ CASES = {
     "window-over-T": (dict(window=32), 2, 30),
     "L3-G3-F64": (dict(n_layers=3, mem_groups=3, d_ffn=64), 3, 24),
     "H1-dh32": (dict(n_heads=1), 2, 20),
+    "B64": (dict(), 64, 12),                        # one workgroup per slot, 64 of them
 }
 
 
