@@ -81,24 +81,22 @@ __device__ __forceinline__ int fused_group(int N) {
   return G;
 }
 
-// y[n] (+)= scale * sum_k WT[k][n] a[k]: G consecutive lanes per output, lane
-// j of a group summing k = j, j + G, ... in order, then the G partial sums
-// added by a butterfly over the group.  y may be in LDS or global memory.
-template <bool ADD>
-__device__ __forceinline__ void matvec(float *y, const float *WT, const float *a, int N, int K,
-                                       float scale) {
+// out(n, sum_k WT[k][n] in(k)) for n < N: G consecutive lanes per output,
+// lane j of a group summing k = j, j + G, ... in order, then the G partial
+// sums added by a butterfly over the group; out runs on the group's first
+// lane.  in and out fold the elementwise steps around a product (the RMSNorm
+// gain, the attention's normalisation, the bias and gate, GELU) into it.
+template <class In, class Out>
+__device__ __forceinline__ void matvec(const float *WT, int N, int K, In in, Out out) {
   const int G = fused_group(N), ld = fused_ld(N);
   const int j = threadIdx.x & (G - 1), per = kFT / G;
   for (int n0 = 0; n0 < N; n0 += per) {
     const int n = n0 + (int)threadIdx.x / G;
     float acc = 0.f;
     if (n < N)
-      for (int k = j; k < K; k += G) acc = fmaf(WT[(size_t)k * ld + n], a[k], acc);
+      for (int k = j; k < K; k += G) acc = fmaf(WT[(size_t)k * ld + n], in(k), acc);
     for (int off = G >> 1; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (j == 0 && n < N) {
-      if constexpr (ADD) y[n] += scale * acc;
-      else y[n] = scale * acc;
-    }
+    if (j == 0 && n < N) out(n, acc);
   }
 }
 
@@ -129,7 +127,7 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
   const size_t ring_n = (size_t)H * W * dh;        // one layer of this slot's window cache
   float *rk = take((size_t)L * ring_n), *rv = take((size_t)L * ring_n);
   float *ev = take((size_t)2 * d), *x = ev + d;   // [e ; s], the gate's input
-  float *av = take(d), *qkv = take((size_t)3 * d), *ov = take(d), *hv = take(F);
+  float *qkv = take((size_t)3 * d), *ov = take(d), *hv = take(F);
   float *sc = take(kFT), *hm = take(kFT), *hs = take(kFT), *hal = take(kFT), *red = take(8);
   const int P = fused_chunk(H, dh);                // memory positions of a head per chunk
   float *ck = take((size_t)H * P * dh), *cv = take((size_t)H * P * dh);
@@ -164,15 +162,18 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
   int pos = a.pos[b];
   __syncthreads();
 
-  // RMSNorm'd input of a GEMM: av = x * gamma, returns 1/rms(x)
-  auto norm_in = [&](const float *gamma) {
+  // 1/rms(x) (the RMSNorm'd input of a product is x * gamma * 1/rms(x): the
+  // gain is applied to the input and 1/rms to the sums)
+  auto rms_inv = [&]() {
     float ss = 0.f;
     for (int i = tid; i < d; i += kFT) ss += x[i] * x[i];
     ss = block_sum(ss, red);
-    for (int i = tid; i < d; i += kFT) av[i] = x[i] * gamma[i];
-    __syncthreads();
     return 1.0f / sqrtf(ss / (float)d + a.eps);
   };
+  auto normed = [&](const float *gamma) { return [=](int k) { return x[k] * gamma[k]; }; };
+  auto store = [](float *y, float scale) { return [=](int n, float acc) { y[n] = scale * acc; }; };
+  auto accumulate = [](float *y) { return [=](int n, float acc) { y[n] += 1.f * acc; }; };
+  auto from = [](const float *v) { return [=](int k) { return v[k]; }; };
 
   // e rows: the next step's row is in flight while a step runs (d <= 256)
   const bool ahead = d <= kFT;
@@ -188,12 +189,10 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
     }
     __syncthreads();
     if (ahead && tid < d && step + 1 < a.T) e_next = a.e[((size_t)b * a.T + step + 1) * d + tid];
-    matvec<false>(ov, WgT, ev, d, 2 * d, 1.f);     // W_g [e ; s]
-    __syncthreads();
-    for (int n = tid; n < d; n += kFT) {
-      const float g = 1.0f / (1.0f + __expf(-(ov[n] + bg[n])));
+    matvec(WgT, d, 2 * d, from(ev), [=](int n, float acc) {   // W_g [e ; s], the gate, the mix
+      const float g = 1.0f / (1.0f + __expf(-(1.f * acc + bg[n])));
       ov[n] = g * ev[n] + (1.0f - g) * x[n];
-    }
+    });
     __syncthreads();
     for (int i = tid; i < d; i += kFT) x[i] = ov[i];
     __syncthreads();
@@ -201,8 +200,8 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
     for (int l = 0; l < L; ++l) {
       float *lrk = rk + l * ring_n, *lrv = rv + l * ring_n;
       // ---- q, k, v of RMSNorm(x; g1); k, v to window entry (t - 1) mod W
-      float r = norm_in(g1 + (size_t)l * d);
-      matvec<false>(qkv, WqkvT(l), av, 3 * d, d, r);
+      float r = rms_inv();
+      matvec(WqkvT(l), 3 * d, d, normed(g1 + (size_t)l * d), store(qkv, r));
       __syncthreads();
       const int we = (t - 1) % W;
       for (int i = tid; i < d; i += kFT) {
@@ -248,11 +247,11 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
       }
       __syncthreads();
       // ---- x += W_O o
-      matvec<true>(x, WoT(l), ov, d, d, 1.f);
+      matvec(WoT(l), d, d, from(ov), accumulate(x));
       __syncthreads();
       // ---- q_c of RMSNorm(x; g2); cross-attention to memory positions 1..t
-      r = norm_in(g2 + (size_t)l * d);
-      matvec<false>(qkv, WqcT(l), av, d, d, r);
+      r = rms_inv();
+      matvec(WqcT(l), d, d, normed(g2 + (size_t)l * d), store(qkv, r));
       __syncthreads();
       const int grp = a.G == 1 ? 0 : l;
       const float *mk = a.mk + (size_t)grp * a.sg + (size_t)b * a.ss;
@@ -333,18 +332,15 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
         }
         __syncthreads();
       }
-      for (int i = tid; i < d; i += kFT) ov[i] /= hs[i / dh];
-      __syncthreads();
-      // ---- x += W_Oc o_c
-      matvec<true>(x, WocT(l), ov, d, d, 1.f);
+      // ---- x += W_Oc o_c (o_c normalised by each head's softmax sum on the way in)
+      matvec(WocT(l), d, d, [=](int k) { return ov[k] / hs[k / dh]; }, accumulate(x));
       __syncthreads();
       // ---- x += W_2 GELU(W_1 RMSNorm(x; g3))
-      r = norm_in(g3 + (size_t)l * d);
-      matvec<false>(hv, W1T(l), av, F, d, r);
+      r = rms_inv();
+      matvec(W1T(l), F, d, normed(g3 + (size_t)l * d),
+             [=](int n, float acc) { hv[n] = gelu_erf(r * acc); });
       __syncthreads();
-      for (int n = tid; n < F; n += kFT) hv[n] = gelu_erf(hv[n]);
-      __syncthreads();
-      matvec<true>(x, W2T(l), hv, d, F, 1.f);
+      matvec(W2T(l), d, F, from(hv), accumulate(x));
       __syncthreads();
     }
 
@@ -353,8 +349,8 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
     if (a.logits_mode == RLT_LOGITS_ALL) lrow = a.logits + ((size_t)b * a.T + step) * V;
     else if (a.logits_mode == RLT_LOGITS_LAST && step == a.T - 1) lrow = a.logits + (size_t)b * V;
     if (lrow) {
-      const float r = norm_in(go);
-      matvec<false>(lrow, WoutT, av, V, d, r);
+      const float r = rms_inv();
+      matvec(WoutT, V, d, normed(go), store(lrow, r));
       __syncthreads();
     }
     pos += 1;
@@ -371,7 +367,7 @@ size_t fused_lds_bytes(int d, int H, int dh, int L, int F, int V, int W) {
                                 (size_t)d * fused_ld(F) + (size_t)F * ldd);
   const size_t vec = (size_t)2 * d + (size_t)3 * L * d;
   const size_t ring = (size_t)2 * L * H * W * dh;
-  const size_t act = (size_t)7 * d + F + 4 * kFT + 8;
+  const size_t act = (size_t)6 * d + F + 4 * kFT + 8;
   const size_t chunk = (size_t)2 * H * fused_chunk(H, dh) * dh;
   return (w + vec + ring + act + chunk) * 4;
 }
