@@ -273,6 +273,9 @@ void rlt_persistent_test_stall(int32_t on);
  * Arguments, semantics and errors as rlt_run_sequence (the state, window
  * cache and positions it leaves are those the launch chain would leave, up
  * to rounding), plus RLT_ERR_UNSUPPORTED unless rlt_fused_supported(cfg).
+ * With one memory group, the memory positions the call reads are held in
+ * LDS for the whole call when they fit beside the rest; otherwise they are
+ * read from the memory in chunks in every layer (the same values either way).
  * Results: fp32 sums in a fixed order per output (not the chain's MFMA
  * order), so they match the chain and the CPU oracle up to rounding, and
  * splitting a run into calls changes no bit. */

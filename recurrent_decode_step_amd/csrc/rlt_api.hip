@@ -1339,7 +1339,7 @@ int32_t rlt_fused_supported(const rlt_config *cfg) {
   if (!cfg || check_config(cfg) != RLT_OK || cfg->dtype != RLT_DTYPE_F32) return 0;
   if (cfg->n_layers > kFusedMaxLayers || cfg->n_heads * cfg->window > 256) return 0;
   return fused_lds_bytes(cfg->d_model, cfg->n_heads, cfg->head_dim, cfg->n_layers, cfg->d_ffn,
-                         cfg->vocab, cfg->window) <= kFusedMaxLds;
+                         cfg->vocab, cfg->window, 0) <= kFusedMaxLds;
 }
 
 rlt_status rlt_run_sequence_fused(const rlt_model *m, rlt_state *st, int32_t T, const void *dev_e,
@@ -1404,6 +1404,15 @@ rlt_status rlt_run_sequence_fused(const rlt_model *m, rlt_state *st, int32_t T, 
   a.sp = mem->stride_pos;
   a.logits = dev_logits;
   a.logits_mode = logits_mode;
+  // one shared memory group: the positions the call reads (through the
+  // furthest slot's last one) stay in LDS for the whole call when they fit
+  if (c.mem_groups == 1) {
+    int last = 0;
+    for (int i = 0; i < st->B; ++i) last = std::max(last, st->host_pos[i] + T);
+    if (fused_lds_bytes(c.d_model, c.n_heads, c.head_dim, c.n_layers, c.d_ffn, c.vocab, c.window,
+                        last) <= kFusedMaxLds)
+      a.mres = last;
+  }
   const hipError_t e = launch_fused_run(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fused run launch");
   for (int i = 0; i < st->B; ++i) st->host_pos[i] += T;

@@ -130,7 +130,11 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
   float *qkv = take((size_t)3 * d), *ov = take(d), *hv = take(F);
   float *sc = take(kFT), *hm = take(kFT), *hs = take(kFT), *hal = take(kFT), *red = take(8);
   const int P = fused_chunk(H, dh);                // memory positions of a head per chunk
-  float *ck = take((size_t)H * P * dh), *cv = take((size_t)H * P * dh);
+  // the memory: resident (one shared group: positions 0 .. mres-1 of the
+  // slot, loaded once) or staged chunk by chunk
+  const bool resident = a.mres > 0;
+  const int rs = resident ? a.mres : P;            // positions per head in the LDS copy
+  float *ck = take((size_t)H * rs * dh), *cv = take((size_t)H * rs * dh);
 
   stage_t(WgT, a.wg, d, 2 * d);
   stage_t(WoutT, a.wout, V, d);
@@ -157,6 +161,16 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
     for (size_t i = tid; i < ring_n; i += kFT) {
       rk[l * ring_n + i] = a.ring_k[src + i];
       rv[l * ring_n + i] = a.ring_v[src + i];
+    }
+  }
+  if (resident) {
+    const float *mk = a.mk + (size_t)b * a.ss, *mv = a.mv + (size_t)b * a.ss;
+    const int n = H * rs * dh;
+    for (int i = tid; i < n; i += kFT) {
+      const int h = i / (rs * dh), rem = i - h * rs * dh, p = rem / dh, c = rem - p * dh;
+      const size_t g = (size_t)h * a.sh + (size_t)p * a.sp + c;
+      ck[i] = mk[g];
+      cv[i] = mv[g];
     }
   }
   int pos = a.pos[b];
@@ -264,27 +278,30 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
       __syncthreads();
       for (int c0 = 0; c0 < t; c0 += P) {
         const int np = min(P, t - c0);
-        // the chunk's keys and values of every head into LDS, all loads in flight together
-        const int nel = H * np * dh;
-        float kr[kFusedStage], vr[kFusedStage];
+        const int cb = resident ? c0 : 0;          // the chunk's first position in the LDS copy
+        if (!resident) {
+          // the chunk's keys and values of every head into LDS, all loads in flight together
+          const int nel = H * np * dh;
+          float kr[kFusedStage], vr[kFusedStage];
 #pragma unroll
-        for (int u = 0; u < kFusedStage; ++u) {
-          const int q = min(tid + u * kFT, nel - 1);
-          const int h = q / (np * dh), rem = q - h * np * dh, jj = rem / dh, c = rem - jj * dh;
-          const size_t g = (size_t)h * a.sh + (size_t)(c0 + jj) * a.sp + c;
-          kr[u] = mk[g];
-          vr[u] = mv[g];
-        }
-#pragma unroll
-        for (int u = 0; u < kFusedStage; ++u) {
-          const int q = tid + u * kFT;
-          if (q < nel) {
+          for (int u = 0; u < kFusedStage; ++u) {
+            const int q = min(tid + u * kFT, nel - 1);
             const int h = q / (np * dh), rem = q - h * np * dh, jj = rem / dh, c = rem - jj * dh;
-            ck[((size_t)h * P + jj) * dh + c] = kr[u];
-            cv[((size_t)h * P + jj) * dh + c] = vr[u];
+            const size_t g = (size_t)h * a.sh + (size_t)(c0 + jj) * a.sp + c;
+            kr[u] = mk[g];
+            vr[u] = mv[g];
           }
+#pragma unroll
+          for (int u = 0; u < kFusedStage; ++u) {
+            const int q = tid + u * kFT;
+            if (q < nel) {
+              const int h = q / (np * dh), rem = q - h * np * dh, jj = rem / dh, c = rem - jj * dh;
+              ck[((size_t)h * P + jj) * dh + c] = kr[u];
+              cv[((size_t)h * P + jj) * dh + c] = vr[u];
+            }
+          }
+          __syncthreads();
         }
-        __syncthreads();
         // one score per thread; each head's P scores are P consecutive lanes
         // of one wavefront (P a power of two), reduced by butterflies
         {
@@ -293,7 +310,8 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
           float sv = -INFINITY;
           if (live && jj < np) {
             sv = 0.f;
-            for (int c = 0; c < dh; ++c) sv = fmaf(qkv[h * dh + c], ck[((size_t)h * P + jj) * dh + c], sv);
+            for (int c = 0; c < dh; ++c)
+              sv = fmaf(qkv[h * dh + c], ck[((size_t)h * rs + cb + jj) * dh + c], sv);
             sv *= a.scale;
           }
           float m = sv;
@@ -324,7 +342,7 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
               h = i / dh;
               const int c = i - h * dh;
               for (int jj = j; jj < np; jj += G)
-                o = fmaf(sc[h * P + jj], cv[((size_t)h * P + jj) * dh + c], o);
+                o = fmaf(sc[h * P + jj], cv[((size_t)h * rs + cb + jj) * dh + c], o);
             }
             for (int off = G >> 1; off >= 1; off >>= 1) o += __shfl_xor(o, off);
             if (j == 0 && i < d) ov[i] = ov[i] * hal[h] + o;
@@ -360,7 +378,7 @@ __global__ __launch_bounds__(kFT) void k_fused_run(const FusedArgs a) {
   if (tid == 0) a.pos[b] = pos;
 }
 
-size_t fused_lds_bytes(int d, int H, int dh, int L, int F, int V, int W) {
+size_t fused_lds_bytes(int d, int H, int dh, int L, int F, int V, int W, int mres) {
   const size_t ldd = fused_ld(d);
   const size_t w = (size_t)2 * d * ldd + (size_t)d * fused_ld(V) +
                    (size_t)L * ((size_t)d * fused_ld(3 * d) + 3 * (size_t)d * ldd +
@@ -368,12 +386,12 @@ size_t fused_lds_bytes(int d, int H, int dh, int L, int F, int V, int W) {
   const size_t vec = (size_t)2 * d + (size_t)3 * L * d;
   const size_t ring = (size_t)2 * L * H * W * dh;
   const size_t act = (size_t)6 * d + F + 4 * kFT + 8;
-  const size_t chunk = (size_t)2 * H * fused_chunk(H, dh) * dh;
+  const size_t chunk = (size_t)2 * H * (mres > 0 ? mres : fused_chunk(H, dh)) * dh;
   return (w + vec + ring + act + chunk) * 4;
 }
 
 hipError_t launch_fused_run(const FusedArgs &a, hipStream_t s) {
-  const size_t lds = fused_lds_bytes(a.d, a.H, a.dh, a.L, a.F, a.V, a.W);
+  const size_t lds = fused_lds_bytes(a.d, a.H, a.dh, a.L, a.F, a.V, a.W, a.mres);
   if (lds > kFusedMaxLds || a.L > kFusedMaxLayers || a.B < 1) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(k_fused_run),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,

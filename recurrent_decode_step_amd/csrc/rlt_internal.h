@@ -168,8 +168,11 @@ struct FusedArgs {
   const float *e;                           // [B][T][d]
   const float *mk, *mv; int64_t sg, ss, sh, sp;   // memory and its strides (elements)
   float *logits; int logits_mode;           // ALL: [B][T][V]; LAST: [B][V]; NONE
+  int mres;                                 // > 0 (G = 1): memory positions 0 .. mres-1 held in
+                                            // LDS for the whole call; 0: staged in chunks
 };
-size_t fused_lds_bytes(int d, int H, int dh, int L, int F, int V, int W);
+// LDS of the fused run; mres > 0 holds that many memory positions resident
+size_t fused_lds_bytes(int d, int H, int dh, int L, int F, int V, int W, int mres);
 hipError_t launch_fused_run(const FusedArgs &a, hipStream_t s);
 // log softmax of each row's logits at its realized token (one workgroup per row)
 hipError_t launch_score(const ScoreArgs &a, int n_rows, hipStream_t s);

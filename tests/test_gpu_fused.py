@@ -1,5 +1,6 @@
 """rlt_run_sequence_fused: the whole run of each slot in one workgroup (small
-fp32 models).  Checked against the CPU oracle (max |d logit| <= 1e-4, the
+fp32 models), its memory held in LDS for the call or staged in chunks.
+Checked against the CPU oracle (max |d logit| <= 1e-4, the
 fp32 gate), for bitwise invariance to splitting a run into calls, for
 continuing states the launch chain left (ragged positions included), for
 its logits modes, and for its refusal of models it does not take."""
@@ -54,6 +55,8 @@ CASES = {
     "L3-G3-F64": (dict(n_layers=3, mem_groups=3, d_ffn=64), 3, 24),
     "H1-dh32": (dict(n_heads=1), 2, 20),
     "B64": (dict(), 64, 12),                        # one workgroup per slot, 64 of them
+    # one memory group but too many positions to hold in LDS: staged in chunks
+    "G1-staged": (dict(), 2, 120),
 }
 
 
