@@ -469,21 +469,18 @@ __device__ __forceinline__ int gemm_vwg(const GemmArgs &a, int L, bool valid, in
       u32x4 wf2[WB];
 #pragma unroll
       for (int j = 0; j < WB; ++j) wf2[j] = wload_frag<WSH>(wp[0] + (size_t)(WB + j) * 64);
+      static_assert(WB % AB == 0, "k-step g sits in register g % AB in both batches");
+      // the activation registers roll over both batches: once k-step g is
+      // multiplied, its register takes k-step g + AB (the second batch's
+      // first activations are in flight while the first batch is multiplied)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        if (h2 == 1) {
-#pragma unroll
-          for (int p = 0; p < AB; ++p)
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-              ab[p][cb] = load_b<T, ACT>(a, cbg[cb], irow[cb], slot[cb], ks0 + WB + p, lane);
-        }
 #pragma unroll
         for (int j = 0; j < WB; ++j) {
           const u32x4 w = h2 == 0 ? wf[0][j] : wf2[j];
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) acc[0][cb] = mma_step(w, ab[j % AB][cb], acc[0][cb], T());
-          if (AB < WB && j + AB < WB) {
+          if (h2 * WB + j + AB < 2 * WB) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
               ab[j % AB][cb] =
