@@ -290,6 +290,8 @@ def test_batch_composition_is_bitwise_invisible(dtype):
                                    dict(d_model=128, n_heads=2, d_ffn=512, vocab=60, n_layers=2,
                                         mem_groups=1),
                                    dict(d_model=256, n_heads=2, d_ffn=8192, vocab=300, n_layers=1,
+                                        mem_groups=1),
+                                   dict(d_model=256, n_heads=2, d_ffn=16384, vocab=300, n_layers=1,
                                         mem_groups=1)])
 def test_large_batch_kernels_match_small_batch_bitwise(shape):
     """Steps over more than 64 rows run the persistent GEMM (activations held
@@ -300,7 +302,8 @@ def test_large_batch_kernels_match_small_batch_bitwise(shape):
     groups of at most 64 rows run the per-tile GEMM (8 rows: one 16-row
     column group, and with d_ffn = 4096 the FFN-up's 256 tiles one per
     wavefront; with d_ffn = 8192 the FFN-down's parts of 32 k-steps take two
-    load batches with the activation registers rolling over both).  200, 150 and 100 rows give 4, 3 and 2 column groups, the
+    load batches with the activation registers rolling over both, with
+    d_ffn = 16384 its parts of 64 k-steps four batches one after another).  200, 150 and 100 rows give 4, 3 and 2 column groups, the
     last one ragged.  The arithmetic is the same, so the logits are bitwise
     equal."""
     cfg = BF16_SMALL.with_(**shape)
