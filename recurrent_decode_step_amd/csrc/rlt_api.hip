@@ -592,6 +592,12 @@ rlt_status enqueue_step(const rlt_model *m, rlt_state *st, const StepScratch &w,
     // one 16-row column group whose tile pairs leave CUs without a workgroup
     // (N = 4096 at 16 rows or fewer): one tile per wavefront
     if (gc.ncb == 1 && tpw > 1 && (g.tiles / tpw) * gc.groups < kFillWorkgroups) tpw = 1;
+    // ... and tile pairs whose last round of workgroups would leave CUs idle
+    // where single tiles fill whole rounds (N = 12288 at 16 rows or fewer:
+    // 384 workgroups against 768)
+    if (gc.ncb == 1 && tpw > 1 && ((g.tiles / tpw) * gc.groups) % kFillWorkgroups != 0 &&
+        (g.tiles * gc.groups) % kFillWorkgroups == 0)
+      tpw = 1;
     // large batches: the persistent kernel (same arithmetic, activations in
     // registers, many tiles per workgroup)
     const hipError_t e2 =
