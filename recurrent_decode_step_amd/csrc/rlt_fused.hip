@@ -32,13 +32,13 @@ namespace rlt {
 namespace {
 
 constexpr int kFT = 256;                         // threads per workgroup
-constexpr int kFusedStage = 4;                   // memory elements per thread and tensor per chunk
+constexpr int kFusedStage = 8;                   // memory elements per thread and tensor per chunk
 
 // memory positions per head in one chunk of the cross-attention (a power of
-// two, at most 32): one score per thread (H * P <= 256), the chunk's keys and
+// two, at most one wavefront's 64 lanes): one score per thread (H * P <= 256), the chunk's keys and
 // values of all heads staged by kFusedStage loads per thread and tensor
 __host__ __device__ inline int fused_chunk(int H, int dh) {
-  int p = 32;                                    // a power of two: the scores' butterflies
+  int p = 64;                                    // a power of two within one wavefront: the scores' butterflies
   while (p > 1 && (H * p > kFT || H * p * dh > kFusedStage * kFT)) p /= 2;
   return p;
 }

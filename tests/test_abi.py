@@ -194,11 +194,13 @@ def test_fused_run_support_rule():
     slot's window cache and activations fit in 160 KiB of LDS."""
     from _tiny import tiny_cfg
     from recurrent_decode_step_amd.configs import DTYPE_BF16, SMALL
-    ok = [tiny_cfg(), tiny_cfg(window=1), tiny_cfg(window=32), tiny_cfg(n_heads=1),
-          tiny_cfg(n_layers=3, mem_groups=3, d_ffn=64)]
+    ok = [tiny_cfg(), tiny_cfg(window=1), tiny_cfg(window=24), tiny_cfg(n_heads=1),
+          tiny_cfg(n_layers=3, mem_groups=3, d_ffn=32)]
     for cfg in ok:
         assert binding.fused_supported(cfg), cfg
-    no = [tiny_cfg(dtype=DTYPE_BF16), tiny_cfg(window=64), tiny_cfg(n_layers=3, mem_groups=3),
+    # W = 32, or three layers at d_ffn = 64: 163 and 161 KiB with a chunk of 64 memory positions
+    no = [tiny_cfg(dtype=DTYPE_BF16), tiny_cfg(window=32), tiny_cfg(window=64),
+          tiny_cfg(n_layers=3, mem_groups=3, d_ffn=64), tiny_cfg(n_layers=3, mem_groups=3),
           tiny_cfg(d_model=64, n_heads=2), SMALL.model]
     for cfg in no:
         assert not binding.fused_supported(cfg), cfg

@@ -51,8 +51,8 @@ CASES = {
     "tiny": (dict(), 4, 64),                        # the tiny fp32 workload: B = 4, T = 64
     "window1": (dict(window=1), 3, 20),
     "window2": (dict(window=2), 3, 20),
-    "window-over-T": (dict(window=32), 2, 30),
-    "L3-G3-F64": (dict(n_layers=3, mem_groups=3, d_ffn=64), 3, 24),
+    "window-over-T": (dict(window=24), 2, 20),
+    "L3-G3-F32": (dict(n_layers=3, mem_groups=3, d_ffn=32), 3, 24),
     "H1-dh32": (dict(n_heads=1), 2, 20),
     "B64": (dict(), 64, 12),                        # one workgroup per slot, 64 of them
     # one memory group but too many positions to hold in LDS: staged in chunks
